@@ -1,0 +1,397 @@
+/*
+ * oracle.c -- plain CPU reference for 2:4 compression and sparse x dense
+ * matrix multiply.  TEST INFRASTRUCTURE ONLY (see oracle.h): the product
+ * path never includes, links or calls this file.
+ *
+ * Every function is the plain definition written out: per-group top-2
+ * selection by magnitude ([P3] "2:4 Fine-Grained Structured Sparsity" and the
+ * first listing of "Python: Build a 2:4 Mask, Compress It ..."), bit-copied
+ * values with 2-bit positions ([P3] worked example; [P2] "How Tensor Cores
+ * Leverage This Pattern"), a residual that keeps what the selection dropped
+ * ([P4] "How the three-layer format makes moderate sparsity fast"), and a
+ * product computed by expanding to dense and summing over k in ascending
+ * order in fp64 (int64 for int8).  No blocking, no reordering.
+ */
+#include "oracle.h"
+
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* ---- element decoding, from the IEEE-754 binary16 and bfloat16 definitions ---- */
+
+double orc_f16_to_f64(uint16_t bits) {
+    /* binary16: 1 sign bit, 5 exponent bits (bias 15), 10 fraction bits. */
+    int sign = bits >> 15, e = (bits >> 10) & 0x1F, f = bits & 0x3FF;
+    double v;
+    if (e == 0)
+        v = ldexp((double)f, -24);                 /* subnormal: f * 2^-14 * 2^-10 */
+    else if (e == 31)
+        v = f ? NAN : INFINITY;
+    else
+        v = ldexp((double)(1024 + f), e - 25);     /* (1 + f/2^10) * 2^(e-15) */
+    return sign ? -v : v;
+}
+
+double orc_bf16_to_f64(uint16_t bits) {
+    /* bfloat16: 1 sign bit, 8 exponent bits (bias 127), 7 fraction bits. */
+    int sign = bits >> 15, e = (bits >> 7) & 0xFF, f = bits & 0x7F;
+    double v;
+    if (e == 0)
+        v = ldexp((double)f, -133);                /* subnormal: f * 2^-126 * 2^-7 */
+    else if (e == 255)
+        v = f ? NAN : INFINITY;
+    else
+        v = ldexp((double)(128 + f), e - 134);     /* (1 + f/2^7) * 2^(e-127) */
+    return sign ? -v : v;
+}
+
+static int valid_dtype(int dt) { return dt == ORC_F16 || dt == ORC_BF16 || dt == ORC_I8; }
+static size_t esize(int dt) { return dt == ORC_I8 ? 1 : 2; }
+
+static double elem_f64(int dt, const void* base, int64_t i) {
+    if (dt == ORC_I8) return (double)((const int8_t*)base)[i];
+    uint16_t u = ((const uint16_t*)base)[i];
+    return dt == ORC_F16 ? orc_f16_to_f64(u) : orc_bf16_to_f64(u);
+}
+
+static int64_t elem_i64(const void* base, int64_t i) { return (int64_t)((const int8_t*)base)[i]; }
+
+static void elem_copy(int dt, void* dst, int64_t di, const void* src, int64_t si) {
+    size_t s = esize(dt);
+    memcpy((char*)dst + (size_t)di * s, (const char*)src + (size_t)si * s, s);
+}
+
+static void elem_zero(int dt, void* dst, int64_t di) {
+    memset((char*)dst + (size_t)di * esize(dt), 0, esize(dt));
+}
+
+/* ---- selection ---- */
+
+void orc_select_group(const double mag[4], int keep[4]) {
+    for (int p = 0; p < 4; ++p) {
+        int rank = 0;
+        for (int q = 0; q < 4; ++q) {
+            if (q == p) continue;
+            if (mag[q] > mag[p] || (mag[q] == mag[p] && q < p)) ++rank;
+        }
+        keep[p] = rank < 2;
+    }
+}
+
+/* Selection for group g of row m of A.  Returns 0, or ORC_ENONFINITE. */
+static int group_keep(int dt, const void* A, int64_t lda, int64_t m, int64_t g, int keep[4]) {
+    double mag[4];
+    for (int p = 0; p < 4; ++p) {
+        double x = elem_f64(dt, A, m * lda + 4 * g + p);
+        if (!isfinite(x)) return ORC_ENONFINITE;
+        mag[p] = fabs(x);                          /* int8: |-128| = 128 */
+    }
+    orc_select_group(mag, keep);
+    return ORC_OK;
+}
+
+static int64_t meta_cols(int64_t K) { return (K + 7) / 8; }
+
+static int check_a(int dt, int64_t M, int64_t K, const void* A, int64_t lda) {
+    if (!valid_dtype(dt)) return ORC_EDTYPE;
+    if (M < 0 || K < 0 || K % 4 != 0) return ORC_ESHAPE;
+    if (M > 0 && K > 0 && !A) return ORC_ENULL;
+    if (lda < K) return ORC_ESTRIDE;
+    return ORC_OK;
+}
+
+/* Writes the 2:4 layer of row m. */
+static int compress_row(int dt, int64_t K, const void* A, int64_t lda, int64_t m,
+                        void* vals, int64_t ldv, uint8_t* meta, int64_t ldm) {
+    for (int64_t j = 0; j < meta_cols(K); ++j) meta[m * ldm + j] = 0;
+    for (int64_t g = 0; g < K / 4; ++g) {
+        int keep[4], t = 0, pos[2] = {0, 0};
+        int rc = group_keep(dt, A, lda, m, g, keep);
+        if (rc) return rc;
+        for (int p = 0; p < 4; ++p)
+            if (keep[p]) pos[t++] = p;             /* ascending: pos[0] < pos[1] */
+        elem_copy(dt, vals, m * ldv + 2 * g, A, m * lda + 4 * g + pos[0]);
+        elem_copy(dt, vals, m * ldv + 2 * g + 1, A, m * lda + 4 * g + pos[1]);
+        uint8_t nib = (uint8_t)(pos[0] | (pos[1] << 2));
+        meta[m * ldm + g / 2] |= (uint8_t)(nib << (4 * (g % 2)));
+    }
+    return ORC_OK;
+}
+
+int orc_compress(int dt, int64_t M, int64_t K, const void* A, int64_t lda,
+                 void* vals, int64_t ldv, uint8_t* meta, int64_t ldm) {
+    int rc = check_a(dt, M, K, A, lda);
+    if (rc) return rc;
+    if (M > 0 && K > 0 && (!vals || !meta)) return ORC_ENULL;
+    if (ldv < K / 2 || ldm < meta_cols(K)) return ORC_ESTRIDE;
+    for (int64_t m = 0; m < M; ++m) {
+        rc = compress_row(dt, K, A, lda, m, vals, ldv, meta, ldm);
+        if (rc) return rc;
+    }
+    return ORC_OK;
+}
+
+int orc_prune(int dt, int64_t M, int64_t K, const void* A, int64_t lda, void* P, int64_t ldp) {
+    int rc = check_a(dt, M, K, A, lda);
+    if (rc) return rc;
+    if (M > 0 && K > 0 && !P) return ORC_ENULL;
+    if (ldp < K) return ORC_ESTRIDE;
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t g = 0; g < K / 4; ++g) {
+            int keep[4];
+            rc = group_keep(dt, A, lda, m, g, keep);
+            if (rc) return rc;
+            for (int p = 0; p < 4; ++p) {
+                if (keep[p]) elem_copy(dt, P, m * ldp + 4 * g + p, A, m * lda + 4 * g + p);
+                else elem_zero(dt, P, m * ldp + 4 * g + p);
+            }
+        }
+    return ORC_OK;
+}
+
+/* Nibble of group g of row m; positions decoded into i0, i1.  Returns 1 if
+ * the nibble names two distinct positions in ascending order. */
+static int decode_nibble(const uint8_t* meta, int64_t ldm, int64_t m, int64_t g, int* i0, int* i1) {
+    int nib = (meta[m * ldm + g / 2] >> (4 * (g % 2))) & 0xF;
+    *i0 = nib & 3;
+    *i1 = nib >> 2;
+    return *i0 < *i1;
+}
+
+int64_t orc_decompress(int dt, int64_t M, int64_t K, const void* vals, int64_t ldv,
+                       const uint8_t* meta, int64_t ldm, void* D, int64_t ldd) {
+    if (!valid_dtype(dt)) return ORC_EDTYPE;
+    if (M < 0 || K < 0 || K % 4 != 0) return ORC_ESHAPE;
+    if (M > 0 && K > 0 && (!vals || !meta || !D)) return ORC_ENULL;
+    if (ldv < K / 2 || ldm < meta_cols(K) || ldd < K) return ORC_ESTRIDE;
+    int64_t bad = 0;
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t g = 0; g < K / 4; ++g) {
+            int i0, i1;
+            for (int p = 0; p < 4; ++p) elem_zero(dt, D, m * ldd + 4 * g + p);
+            if (!decode_nibble(meta, ldm, m, g, &i0, &i1)) { ++bad; continue; }
+            elem_copy(dt, D, m * ldd + 4 * g + i0, vals, m * ldv + 2 * g);
+            elem_copy(dt, D, m * ldd + 4 * g + i1, vals, m * ldv + 2 * g + 1);
+        }
+    return bad;
+}
+
+/* ---- residual split ---- */
+
+/* Count (and optionally emit) the dropped non-zeros of row m, k ascending. */
+static int row_overflow(int dt, int64_t K, const void* A, int64_t lda, int64_t m,
+                        int64_t* count, int32_t* col, void* rvals, int64_t base) {
+    int64_t c = 0;
+    for (int64_t g = 0; g < K / 4; ++g) {
+        int keep[4];
+        int rc = group_keep(dt, A, lda, m, g, keep);
+        if (rc) return rc;
+        for (int p = 0; p < 4; ++p) {
+            int64_t k = 4 * g + p;
+            if (keep[p] || elem_f64(dt, A, m * lda + k) == 0.0) continue;   /* -0 counts as zero */
+            if (col) {
+                col[base + c] = (int32_t)k;
+                elem_copy(dt, rvals, base + c, A, m * lda + k);
+            }
+            ++c;
+        }
+    }
+    *count = c;
+    return ORC_OK;
+}
+
+int orc_split_count(int dt, int64_t M, int64_t K, const void* A, int64_t lda, int32_t* row_ptr) {
+    int rc = check_a(dt, M, K, A, lda);
+    if (rc) return rc;
+    if (!row_ptr) return ORC_ENULL;
+    int64_t total = 0;
+    row_ptr[0] = 0;
+    for (int64_t m = 0; m < M; ++m) {
+        int64_t c;
+        rc = row_overflow(dt, K, A, lda, m, &c, NULL, NULL, 0);
+        if (rc) return rc;
+        total += c;
+        if (total > INT32_MAX) return ORC_ERANGE;
+        row_ptr[m + 1] = (int32_t)total;
+    }
+    return ORC_OK;
+}
+
+int orc_split_fill(int dt, int64_t M, int64_t K, const void* A, int64_t lda,
+                   void* vals, int64_t ldv, uint8_t* meta, int64_t ldm,
+                   const int32_t* row_ptr, int32_t* col, void* rvals) {
+    int rc = orc_compress(dt, M, K, A, lda, vals, ldv, meta, ldm);
+    if (rc) return rc;
+    if (!row_ptr) return ORC_ENULL;
+    if (M > 0 && row_ptr[M] > 0 && (!col || !rvals)) return ORC_ENULL;
+    for (int64_t m = 0; m < M; ++m) {
+        int64_t c;
+        rc = row_overflow(dt, K, A, lda, m, &c, col, rvals, row_ptr[m]);
+        if (rc) return rc;
+        if (c != (int64_t)row_ptr[m + 1] - row_ptr[m]) return ORC_EFORMAT;
+    }
+    return ORC_OK;
+}
+
+/* ---- sparse x dense product ---- */
+
+static int check_mm(int dt, int64_t M, int64_t N, int64_t K, const void* vals, int64_t ldv,
+                    const uint8_t* meta, int64_t ldm, const void* B, int64_t ldb, int64_t ldc,
+                    const double* Cf, const int64_t* Ci) {
+    if (!valid_dtype(dt)) return ORC_EDTYPE;
+    if (M < 0 || N < 0 || K < 0 || K % 4 != 0) return ORC_ESHAPE;
+    if (M > 0 && K > 0 && (!vals || !meta)) return ORC_ENULL;
+    if (K > 0 && N > 0 && !B) return ORC_ENULL;
+    if (M > 0 && N > 0 && (dt == ORC_I8 ? !Ci : !Cf)) return ORC_ENULL;
+    if (ldv < K / 2 || ldm < meta_cols(K) || ldb < N || ldc < N) return ORC_ESTRIDE;
+    return ORC_OK;
+}
+
+/* Dense row m of decompress(vals, meta) [+ residual], as fp64 and int64.
+ * Returns ORC_EFORMAT on a bad nibble. */
+static int dense_row(int dt, int64_t K, const void* vals, int64_t ldv, const uint8_t* meta, int64_t ldm,
+                     const int32_t* row_ptr, const int32_t* col, const void* rvals, int64_t m,
+                     double* rowf, int64_t* rowi) {
+    for (int64_t k = 0; k < K; ++k) { rowf[k] = 0.0; rowi[k] = 0; }
+    for (int64_t g = 0; g < K / 4; ++g) {
+        int i0, i1;
+        if (!decode_nibble(meta, ldm, m, g, &i0, &i1)) return ORC_EFORMAT;
+        int64_t v0 = m * ldv + 2 * g, v1 = v0 + 1;
+        rowf[4 * g + i0] = elem_f64(dt, vals, v0);
+        rowf[4 * g + i1] = elem_f64(dt, vals, v1);
+        if (dt == ORC_I8) { rowi[4 * g + i0] = elem_i64(vals, v0); rowi[4 * g + i1] = elem_i64(vals, v1); }
+    }
+    if (row_ptr) {
+        for (int64_t j = row_ptr[m]; j < row_ptr[m + 1]; ++j) {
+            int64_t k = col[j];
+            if (k < 0 || k >= K) return ORC_EFORMAT;
+            rowf[k] += elem_f64(dt, rvals, j);
+            if (dt == ORC_I8) rowi[k] += elem_i64(rvals, j);
+        }
+    }
+    return ORC_OK;
+}
+
+static int spmm_impl(int dt, int64_t M, int64_t N, int64_t K, const void* vals, int64_t ldv,
+                     const uint8_t* meta, int64_t ldm, const int32_t* row_ptr, const int32_t* col,
+                     const void* rvals, const void* B, int64_t ldb, double* Cf, int64_t* Ci,
+                     double* S, int64_t ldc) {
+    int rc = check_mm(dt, M, N, K, vals, ldv, meta, ldm, B, ldb, ldc, Cf, Ci);
+    if (rc) return rc;
+    if (row_ptr && M > 0 && row_ptr[M] > 0 && (!col || !rvals)) return ORC_ENULL;
+    if (M == 0 || N == 0) return ORC_OK;
+    /* B converted once, stored column by column so each output walks one
+     * contiguous column; the sum order over k is unchanged. */
+    double* bt = (double*)malloc(sizeof(double) * (size_t)(K > 0 ? K : 1) * (size_t)N);
+    int64_t* bti = (int64_t*)malloc(sizeof(int64_t) * (size_t)(K > 0 ? K : 1) * (size_t)N);
+    if (!bt || !bti) { free(bt); free(bti); return ORC_ENOMEM; }
+    for (int64_t k = 0; k < K; ++k)
+        for (int64_t n = 0; n < N; ++n) {
+            bt[n * K + k] = elem_f64(dt, B, k * ldb + n);
+            bti[n * K + k] = dt == ORC_I8 ? elem_i64(B, k * ldb + n) : 0;
+        }
+    int err = ORC_OK;
+#pragma omp parallel
+    {
+        double* rowf = (double*)malloc(sizeof(double) * (size_t)(K > 0 ? K : 1));
+        int64_t* rowi = (int64_t*)malloc(sizeof(int64_t) * (size_t)(K > 0 ? K : 1));
+        if (!rowf || !rowi) {
+#pragma omp critical
+            err = ORC_ENOMEM;
+        }
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t m = 0; m < M; ++m) {
+            if (!rowf || !rowi) continue;
+            int r = dense_row(dt, K, vals, ldv, meta, ldm, row_ptr, col, rvals, m, rowf, rowi);
+            if (r) {
+#pragma omp critical
+                err = r;
+                continue;
+            }
+            for (int64_t n = 0; n < N; ++n) {
+                if (dt == ORC_I8) {
+                    int64_t acc = 0;
+                    for (int64_t k = 0; k < K; ++k) acc += rowi[k] * bti[n * K + k];
+                    Ci[m * ldc + n] = acc;
+                } else {
+                    double acc = 0.0, s = 0.0;
+                    for (int64_t k = 0; k < K; ++k) {
+                        double t = rowf[k] * bt[n * K + k];
+                        acc += t;
+                        s += fabs(t);
+                    }
+                    Cf[m * ldc + n] = acc;
+                    if (S) S[m * ldc + n] = s;
+                }
+            }
+        }
+        free(rowf);
+        free(rowi);
+    }
+    free(bt);
+    free(bti);
+    return err;
+}
+
+int orc_spmm(int dt, int64_t M, int64_t N, int64_t K,
+             const void* vals, int64_t ldv, const uint8_t* meta, int64_t ldm,
+             const void* B, int64_t ldb, double* Cf, int64_t* Ci, double* S, int64_t ldc) {
+    return spmm_impl(dt, M, N, K, vals, ldv, meta, ldm, NULL, NULL, NULL, B, ldb, Cf, Ci, S, ldc);
+}
+
+int orc_spmm_residual(int dt, int64_t M, int64_t N, int64_t K,
+                      const void* vals, int64_t ldv, const uint8_t* meta, int64_t ldm,
+                      const int32_t* row_ptr, const int32_t* col, const void* rvals,
+                      const void* B, int64_t ldb, double* Cf, int64_t* Ci, double* S, int64_t ldc) {
+    if (!row_ptr) return ORC_ENULL;
+    return spmm_impl(dt, M, N, K, vals, ldv, meta, ldm, row_ptr, col, rvals, B, ldb, Cf, Ci, S, ldc);
+}
+
+int orc_spmm_entries(int dt, int64_t M, int64_t N, int64_t K,
+                     const void* vals, int64_t ldv, const uint8_t* meta, int64_t ldm,
+                     const int32_t* row_ptr, const int32_t* col, const void* rvals,
+                     const void* B, int64_t ldb, int64_t n_entries,
+                     const int64_t* ms, const int64_t* ns, double* Cf, int64_t* Ci, double* S) {
+    int rc = check_mm(dt, M, N, K, vals, ldv, meta, ldm, B, ldb, N, Cf, Ci);
+    if (rc) return rc;
+    if (n_entries < 0) return ORC_ESHAPE;
+    if (n_entries > 0 && (!ms || !ns || (dt == ORC_I8 ? !Ci : !Cf))) return ORC_ENULL;
+    double* rowf = (double*)malloc(sizeof(double) * (size_t)(K > 0 ? K : 1));
+    int64_t* rowi = (int64_t*)malloc(sizeof(int64_t) * (size_t)(K > 0 ? K : 1));
+    if (!rowf || !rowi) { free(rowf); free(rowi); return ORC_ENOMEM; }
+    for (int64_t e = 0; e < n_entries && rc == ORC_OK; ++e) {
+        int64_t m = ms[e], n = ns[e];
+        if (m < 0 || m >= M || n < 0 || n >= N) { rc = ORC_ERANGE; break; }
+        rc = dense_row(dt, K, vals, ldv, meta, ldm, row_ptr, col, rvals, m, rowf, rowi);
+        if (rc) break;
+        if (dt == ORC_I8) {
+            int64_t acc = 0;
+            for (int64_t k = 0; k < K; ++k) acc += rowi[k] * elem_i64(B, k * ldb + n);
+            Ci[e] = acc;
+        } else {
+            double acc = 0.0, s = 0.0;
+            for (int64_t k = 0; k < K; ++k) {
+                double t = rowf[k] * elem_f64(dt, B, k * ldb + n);
+                acc += t;
+                s += fabs(t);
+            }
+            Cf[e] = acc;
+            if (S) S[e] = s;
+        }
+    }
+    free(rowf);
+    free(rowi);
+    return rc;
+}
+
+int orc_num_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}

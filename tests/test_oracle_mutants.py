@@ -1,0 +1,72 @@
+"""Planted mistakes in a copy of the oracle must be caught by its pins.
+
+Each mutant is one plausible slip (a tie broken the wrong way, a swapped
+bit field, a dropped term, a wrong exponent bias ...) applied to a temporary
+copy of oracle.c.  The copy is built with gcc and the pin suite is run
+against it in a subprocess; the suite must fail.  CPU only."""
+import concurrent.futures as cf
+import os
+import shutil
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "oracle", "oracle.c")
+HDR = os.path.join(ROOT, "oracle", "oracle.h")
+PINS = os.path.join(ROOT, "tests", "test_oracle_pins.py")
+
+MUTANTS = [
+    ("ties to the higher position", "(mag[q] == mag[p] && q < p)", "(mag[q] == mag[p] && q > p)"),
+    ("keeps the two smallest", "keep[p] = rank < 2;", "keep[p] = rank > 1;"),
+    ("signed magnitude", "mag[p] = fabs(x);", "mag[p] = x;"),
+    ("index fields swapped", "(uint8_t)(pos[0] | (pos[1] << 2))", "(uint8_t)(pos[1] | (pos[0] << 2))"),
+    ("group nibbles swapped", "meta[m * ldm + g / 2] |= (uint8_t)(nib << (4 * (g % 2)));",
+     "meta[m * ldm + g / 2] |= (uint8_t)(nib << (4 * ((g + 1) % 2)));"),
+    ("decode reads the wrong nibble", "int nib = (meta[m * ldm + g / 2] >> (4 * (g % 2))) & 0xF;",
+     "int nib = (meta[m * ldm + g / 2] >> (4 * ((g + 1) % 2))) & 0xF;"),
+    ("last k term dropped", "for (int64_t k = 0; k < K; ++k) {\n                        double t = rowf[k] * bt[n * K + k];",
+     "for (int64_t k = 0; k + 1 < K; ++k) {\n                        double t = rowf[k] * bt[n * K + k];"),
+    ("int8 product reads the wrong B column",
+     "for (int64_t k = 0; k < K; ++k) acc += rowi[k] * bti[n * K + k];",
+     "for (int64_t k = 0; k < K; ++k) acc += rowi[k] * bti[(N - 1 - n) * K + k];"),
+    ("fp16 subnormal scale", "v = ldexp((double)f, -24);", "v = ldexp((double)f, -25);"),
+    ("bf16 exponent bias", "v = ldexp((double)(128 + f), e - 134);", "v = ldexp((double)(128 + f), e - 133);"),
+    ("-0 counted as a residual non-zero", "if (keep[p] || elem_f64(dt, A, m * lda + k) == 0.0) continue;",
+     "if (keep[p] || (dt == ORC_I8 ? elem_f64(dt, A, m * lda + k) == 0.0 : ((const uint16_t*)A)[m * lda + k] == 0)) continue;"),
+    ("last residual entry of a row dropped", "for (int64_t j = row_ptr[m]; j < row_ptr[m + 1]; ++j) {",
+     "for (int64_t j = row_ptr[m]; j + 1 < row_ptr[m + 1]; ++j) {"),
+    ("bound accumulates signed terms", "s += fabs(t);\n                    }\n                    Cf[m * ldc + n] = acc;",
+     "s += t;\n                    }\n                    Cf[m * ldc + n] = acc;"),
+]
+
+
+def _run_mutant(tmp, name, old, new):
+    src = open(SRC).read()
+    assert src.count(old) == 1, "mutation anchor not unique: %s" % name
+    d = os.path.join(tmp, "m%d" % abs(hash(name)))
+    os.makedirs(d)
+    with open(os.path.join(d, "oracle.c"), "w") as f:
+        f.write(src.replace(old, new))
+    shutil.copy(HDR, d)
+    lib = os.path.join(d, "liboracle.so")
+    subprocess.run(["gcc", "-O1", "-std=c11", "-fopenmp", "-fPIC", "-shared", os.path.join(d, "oracle.c"),
+                    "-o", lib, "-lm"], check=True)
+    env = dict(os.environ, SSG_ORACLE_LIB=lib, OMP_NUM_THREADS="1")
+    r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider", PINS],
+                       cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
+    return name, r.returncode
+
+
+def test_pins_catch_every_planted_mistake(tmp_path):
+    with cf.ThreadPoolExecutor(max_workers=4) as ex:
+        results = list(ex.map(lambda m: _run_mutant(str(tmp_path), *m), MUTANTS))
+    survivors = [name for name, rc in results if rc == 0]
+    assert not survivors, "pins did not catch: %s" % survivors
+
+
+def test_unmutated_copy_passes(tmp_path):
+    # the harness itself must not fail a correct oracle
+    name, rc = _run_mutant(str(tmp_path), "identity", "int orc_num_threads(void) {", "int orc_num_threads(void) {")
+    assert rc == 0

@@ -1,0 +1,353 @@
+"""Pins of the CPU oracle against facts fixed outside it: values the pages
+print, closed forms, invariants, brute force on tiny inputs and independent
+library routines (numpy / torch).  CPU only."""
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from tests import _util as U
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+DTS = ["f16", "bf16", "i8"]
+FAMILIES = ["normal", "ties", "sparse", "extreme"]
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+# ---------------------------------------------------------------- decoders
+
+def test_f16_decoder_matches_numpy_on_every_bit_pattern():
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    ref = bits.view(np.float16).astype(np.float64)
+    got = np.array([oracle.f16_to_f64(b) for b in bits])
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+    # sign of zero survives
+    assert np.signbit(got[0x8000]) and not np.signbit(got[0])
+
+
+def test_bf16_decoder_matches_torch_on_every_bit_pattern():
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    ref = torch.from_numpy(bits.view(np.int16).copy()).view(torch.bfloat16).to(torch.float64).numpy()
+    got = np.array([oracle.bf16_to_f64(b) for b in bits])
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+
+
+# ---------------------------------------------------------------- selection
+
+@pytest.mark.parametrize("mags", [
+    [5, 3, 3, 1], [3, 3, 3, 3], [2, 5, 5, 5], [5, 3, 5, 3], [0, 0, 0, 5], [1, 2, 3, 4], [4, 3, 2, 1],
+    [0, 0, 0, 0], [1, 0, 0, 1], [0, 7, 0, 7],
+])
+def test_select_group_equals_pair_enumeration(mags):
+    keep = oracle.select_group(mags)
+    p, q = U.brute_pair(mags)
+    assert keep == [int(i in (p, q)) for i in range(4)]
+
+
+def test_worked_example_from_the_pages():
+    g = _golden("worked_example.json")
+    for dt, case in g["cases"].items():
+        row = U.encode(dt, case["row"]).reshape(1, -1)
+        vals, meta = oracle.compress(dt, row)
+        assert np.array_equal(U.to_f64(dt, vals)[0], case["vals"])
+        assert list(meta[0]) == case["meta"]
+        nibs = [meta[0, 0] & 0xF, meta[0, 0] >> 4]
+        assert [[n & 3, n >> 2] for n in nibs] == case["indices"]
+        P = oracle.prune(dt, row)
+        assert np.array_equal(U.to_f64(dt, P)[0], case["pruned"])
+
+
+def test_hand_cases():
+    # all equal -> the two lowest positions
+    v, m = oracle.compress("f16", U.encode("f16", [1, 1, 1, 1]).reshape(1, 4))
+    assert m[0, 0] == 0x4 and list(U.to_f64("f16", v)[0]) == [1, 1]
+    # one non-zero: a zero is stored beside it, positions ascending
+    v, m = oracle.compress("f16", U.encode("f16", [0, 0, 0, 5]).reshape(1, 4))
+    assert m[0, 0] == 0xC and list(U.to_f64("f16", v)[0]) == [0, 5]
+    # -0 and +0 tie; kept bits are copied (the -0 stays -0)
+    a = np.array([[0x8000, 0x0000, 0x0000, 0x0000]], dtype=np.uint16)
+    v, m = oracle.compress("f16", a)
+    assert m[0, 0] == 0x4 and list(v[0]) == [0x8000, 0x0000]
+    # int8: |-128| = 128 outranks 127
+    v, m = oracle.compress("i8", np.array([[127, 3, -128, 5]], dtype=np.int8))
+    assert m[0, 0] == (0 | (2 << 2)) and list(v[0]) == [127, -128]
+    # bf16: magnitude, not sign, decides
+    v, m = oracle.compress("bf16", U.encode("bf16", [-8, 1, 7, -2]).reshape(1, 4))
+    assert m[0, 0] == (0 | (2 << 2)) and list(U.to_f64("bf16", v)[0]) == [-8, 7]
+
+
+@pytest.mark.parametrize("dt", DTS)
+def test_selection_matches_pair_enumeration_on_8x8(dt):
+    for seed in range(40):
+        for fam in FAMILIES:
+            A = U.random_matrix(dt, 8, 8, fam, seed)
+            keep = U.brute_keep_mask(dt, A)
+            vals, meta = oracle.compress(dt, A)
+            for m in range(8):
+                for g in range(2):
+                    kept = [p for p in range(4) if keep[m, 4 * g + p]]
+                    nib = (meta[m, g // 2] >> (4 * (g % 2))) & 0xF
+                    assert [nib & 3, nib >> 2] == kept
+                    assert list(vals[m, 2 * g:2 * g + 2]) == [A[m, 4 * g + kept[0]], A[m, 4 * g + kept[1]]]
+
+
+# ---------------------------------------------------------------- the pages' printed numbers
+
+def test_printed_byte_accounting_of_the_listing():
+    g = _golden("byte_accounting.json")
+    torch.manual_seed(0)
+    W = torch.randn(g["M"], g["K"])                    # the listing's own input
+    A = W.to(torch.float16).view(torch.int16).numpy().view(np.uint16)
+    vals, meta = oracle.compress("f16", A)
+    P = oracle.prune("f16", A)
+    zero = U.is_zero("f16", P)
+    assert "%.1f%%" % (100 * zero.mean()) == g["printed"]["sparsity"]
+    per_group = (~zero).reshape(g["M"], g["K"] // 4, 4).sum(-1)
+    assert bool((per_group == 2).all()) is g["printed"]["all_groups_have_exactly_2_nonzeros"]
+    dense = A.size * g["bytes_per_value"]
+    sparse = vals.nbytes + meta.nbytes                 # values + 2 bits per kept value
+    assert "%.1f" % (dense / 1024) == g["printed"]["dense_KB"]
+    assert "%.1f" % (sparse / 1024) == g["printed"]["sparse_KB"]
+    assert "%.1f%%" % (100 * sparse / dense) == g["printed"]["sparse_fraction_of_dense"]
+
+
+def test_storage_closed_form():
+    g = _golden("storage_closed_form.json")
+    M, K = 16, 64
+    for dt, b in (("f16", 16), ("i8", 8)):
+        A = U.random_matrix(dt, M, K, "normal", 7)
+        vals, meta = oracle.compress(dt, A)
+        assert vals.size * 2 == A.size                  # half of the values are stored
+        assert meta.size * 8 == A.size                  # one metadata bit per dense element
+        frac = (vals.nbytes + meta.nbytes) / A.nbytes
+        assert frac == pytest.approx(0.5 + 1.0 / b)
+    p = g["printed"]
+    assert "%d%%" % round(100 * (0.5 + 1 / 16)) == p["fp16_fraction_of_dense"]
+    assert "%d%%" % round(100 * (1 / 16)) == p["metadata_overhead_16bit"]
+    assert "%d%%" % round(100 * (1 / 4)) == p["metadata_overhead_4bit"]
+    assert "%.1fx" % (1 / (0.5 + 1 / 16)) == p["decode_bandwidth_gain_fp16"]
+
+
+# ---------------------------------------------------------------- invariants and round trips
+
+@pytest.mark.parametrize("dt", DTS)
+@pytest.mark.parametrize("fam", FAMILIES)
+def test_invariants(dt, fam):
+    A = U.random_matrix(dt, 24, 64, fam, 11)
+    P = oracle.prune(dt, A)
+    mag_a = np.abs(U.to_f64(dt, A)).reshape(24, 16, 4)
+    keep = U.brute_keep_mask(dt, A).reshape(24, 16, 4)
+    # (i) every kept magnitude >= every dropped magnitude in its group
+    kept_min = np.where(keep, mag_a, np.inf).min(-1)
+    drop_max = np.where(~keep, mag_a, -np.inf).max(-1)
+    assert (kept_min >= drop_max).all()
+    # (ii)/(iii) at most two non-zeros per group, exactly min(nnz_g(A), 2)
+    nz_a = (~U.is_zero(dt, A)).reshape(24, 16, 4).sum(-1)
+    nz_p = (~U.is_zero(dt, P)).reshape(24, 16, 4).sum(-1)
+    assert (nz_p <= 2).all()
+    assert np.array_equal(nz_p, np.minimum(nz_a, 2))
+    # dropped positions are +0 bits; kept positions are bit copies
+    Pg = P.reshape(24, 16, 4)
+    Ag = A.reshape(24, 16, 4)
+    assert np.array_equal(Pg[keep], Ag[keep])
+    assert (Pg[~keep] == 0).all()
+
+
+@pytest.mark.parametrize("dt", DTS)
+@pytest.mark.parametrize("fam", FAMILIES)
+def test_roundtrip_and_idempotence(dt, fam):
+    A = U.random_matrix(dt, 16, 72, fam, 3)           # K=72: odd number of groups per meta byte
+    vals, meta = oracle.compress(dt, A)
+    D, bad = oracle.decompress(dt, vals, meta, 72)
+    assert bad == 0
+    assert np.array_equal(D, oracle.prune(dt, A))
+    v2, m2 = oracle.compress(dt, oracle.prune(dt, A))
+    assert np.array_equal(v2, vals) and np.array_equal(m2, meta)
+    groups = np.stack([meta & 0xF, meta >> 4], axis=-1).reshape(16, -1)[:, :18]
+    assert set(np.unique(groups)) <= U.VALID_NIBBLES
+    # the unused high nibble of the last byte (18 groups -> 9 bytes exactly) is absent;
+    # K=20 leaves one: it must be 0
+    A5 = U.random_matrix(dt, 3, 20, fam, 4)
+    _, m5 = oracle.compress(dt, A5)
+    assert m5.shape == (3, 3) and (m5[:, 2] >> 4 == 0).all()
+
+
+@pytest.mark.parametrize("dt", DTS)
+def test_decompress_counts_invalid_nibbles_and_zero_fills(dt):
+    A = U.random_matrix(dt, 4, 16, "normal", 5)
+    vals, meta = oracle.compress(dt, A)
+    meta = meta.copy()
+    meta[1, 0] = (meta[1, 0] & 0xF0) | 0x5            # (1,1): repeated position
+    meta[2, 1] = (meta[2, 1] & 0x0F) | (0x7 << 4)     # (3,1): descending
+    D, bad = oracle.decompress(dt, vals, meta, 16)
+    assert bad == 2
+    assert (D[1, 0:4] == 0).all() and (D[2, 12:16] == 0).all()
+    ref = oracle.prune(dt, A)
+    assert np.array_equal(D[0], ref[0]) and np.array_equal(D[3], ref[3])
+    with pytest.raises(oracle.OracleError):
+        oracle.spmm(dt, vals, meta, U.random_matrix(dt, 16, 4, "normal", 6), 16)
+
+
+# ---------------------------------------------------------------- residual split
+
+@pytest.mark.parametrize("dt", DTS)
+@pytest.mark.parametrize("fam", ["normal", "ties", "sparse"])
+def test_split(dt, fam):
+    M, K = 20, 48
+    A = U.random_matrix(dt, M, K, fam, 9)
+    vals, meta, row_ptr, col, rvals = oracle.split(dt, A)
+    v0, m0 = oracle.compress(dt, A)
+    assert np.array_equal(vals, v0) and np.array_equal(meta, m0)
+    keep = U.brute_keep_mask(dt, A)
+    nz = ~U.is_zero(dt, A)
+    want = nz & ~keep                                  # dropped non-zeros
+    assert row_ptr[0] == 0 and np.array_equal(np.diff(row_ptr), want.sum(1))
+    for m in range(M):
+        cols = col[row_ptr[m]:row_ptr[m + 1]]
+        assert list(cols) == list(np.nonzero(want[m])[0])            # ascending
+        assert np.array_equal(rvals[row_ptr[m]:row_ptr[m + 1]], A[m, cols])
+    # nnz(L) + nnz(R) = nnz(A); residual only in groups with > 2 non-zeros, at most 2 per group
+    P = oracle.prune(dt, A)
+    assert (~U.is_zero(dt, P)).sum() + len(col) == nz.sum()
+    per_group_r = want.reshape(M, K // 4, 4).sum(-1)
+    per_group_a = nz.reshape(M, K // 4, 4).sum(-1)
+    assert (per_group_r <= 2).all() and (per_group_r[per_group_a <= 2] == 0).all()
+    # decompress(L) + scatter(R) reproduces A's values
+    D, _ = oracle.decompress(dt, vals, meta, K)
+    Dv = U.to_f64(dt, D)
+    Dv[np.repeat(np.arange(M), np.diff(row_ptr)), col] += U.to_f64(dt, rvals)
+    assert np.array_equal(Dv, U.to_f64(dt, A))
+
+
+# ---------------------------------------------------------------- products
+
+def _exact_small(dt, shape, seed, lo=-3, hi=3):
+    rng = np.random.default_rng(seed)
+    return U.encode(dt, rng.integers(lo, hi + 1, size=shape))
+
+
+@pytest.mark.parametrize("dt", DTS)
+def test_spmm_bruteforce_exact_8x8(dt):
+    for seed in range(30):
+        A = _exact_small(dt, (8, 8), seed)
+        B = _exact_small(dt, (8, 8), seed + 1000)
+        keep = U.brute_keep_mask(dt, A)
+        a = [[int(x) for x in row] for row in U.to_f64(dt, A)]
+        b = [[int(x) for x in row] for row in U.to_f64(dt, B)]
+        want = [[sum(a[m][k] * b[k][n] for k in range(8) if keep[m, k]) for n in range(8)] for m in range(8)]
+        vals, meta = oracle.compress(dt, A)
+        C, S = oracle.spmm(dt, vals, meta, B, 8)
+        assert np.array_equal(np.asarray(C, dtype=np.float64), np.array(want, dtype=np.float64))
+        if S is not None:
+            sw = [[sum(abs(a[m][k] * b[k][n]) for k in range(8) if keep[m, k]) for n in range(8)] for m in range(8)]
+            assert np.array_equal(S, np.array(sw, dtype=np.float64))
+
+
+@pytest.mark.parametrize("dt", DTS)
+@pytest.mark.parametrize("shape", [(37, 64, 9), (16, 256, 33), (1, 4, 1), (5, 12, 64)])
+def test_spmm_matches_numpy_matmul(dt, shape):
+    M, K, N = shape
+    A = U.random_matrix(dt, M, K, "normal", M + K)
+    B = U.random_matrix(dt, K, N, "normal", N + 17)
+    vals, meta = oracle.compress(dt, A)
+    C, S = oracle.spmm(dt, vals, meta, B, K)
+    P = np.where(U.brute_keep_mask(dt, A), U.to_f64(dt, A), 0.0)   # independent pruned dense
+    if dt == "i8":
+        ref = P.astype(np.int64) @ U.to_i64(B)
+        assert np.array_equal(C, ref)
+    else:
+        Bf = U.to_f64(dt, B)
+        ref = P @ Bf
+        assert np.allclose(C, ref, rtol=1e-12, atol=1e-12 * np.abs(ref).max())
+        assert np.allclose(S, np.abs(P) @ np.abs(Bf), rtol=1e-12, atol=0)
+        assert (S >= np.abs(C) - 1e-12).all()
+
+
+@pytest.mark.parametrize("dt", DTS)
+def test_spmm_identity_B_returns_the_pruned_matrix(dt):
+    K = 32
+    A = U.random_matrix(dt, 12, K, "normal", 21)
+    I = U.encode(dt, np.eye(K))
+    vals, meta = oracle.compress(dt, A)
+    C, _ = oracle.spmm(dt, vals, meta, I, K)
+    assert np.array_equal(np.asarray(C, dtype=np.float64), U.to_f64(dt, oracle.prune(dt, A)))
+
+
+@pytest.mark.parametrize("dt", DTS)
+def test_spmm_residual_equals_dense_product(dt):
+    M, K, N = 24, 64, 10
+    A = U.random_matrix(dt, M, K, "sparse", 31)
+    B = U.random_matrix(dt, K, N, "normal", 32)
+    vals, meta, row_ptr, col, rvals = oracle.split(dt, A)
+    C, S = oracle.spmm_residual(dt, vals, meta, row_ptr, col, rvals, B, K)
+    if dt == "i8":
+        assert np.array_equal(C, U.to_i64(A) @ U.to_i64(B))
+    else:
+        ref = U.to_f64(dt, A) @ U.to_f64(dt, B)
+        assert np.allclose(C, ref, rtol=1e-12, atol=1e-12 * np.abs(ref).max())
+        assert np.allclose(S, np.abs(U.to_f64(dt, A)) @ np.abs(U.to_f64(dt, B)), rtol=1e-12)
+
+
+@pytest.mark.parametrize("dt", DTS)
+def test_spmm_entries_match_the_full_product(dt):
+    M, K, N = 20, 40, 12
+    A = U.random_matrix(dt, M, K, "sparse", 41)
+    B = U.random_matrix(dt, K, N, "normal", 42)
+    vals, meta, row_ptr, col, rvals = oracle.split(dt, A)
+    rng = np.random.default_rng(0)
+    ms, ns = rng.integers(0, M, 50), rng.integers(0, N, 50)
+    for residual in (None, (row_ptr, col, rvals)):
+        full, fs = (oracle.spmm(dt, vals, meta, B, K) if residual is None
+                    else oracle.spmm_residual(dt, vals, meta, row_ptr, col, rvals, B, K))
+        e, es = oracle.spmm_entries(dt, vals, meta, B, K, ms, ns, residual=residual)
+        assert np.array_equal(e, full[ms, ns])
+        if fs is not None:
+            assert np.array_equal(es, fs[ms, ns])
+
+
+def test_int8_linearity_in_B():
+    A = U.random_matrix("i8", 9, 32, "normal", 51)
+    B1 = U.encode("i8", np.random.default_rng(1).integers(-60, 61, size=(32, 7)))
+    B2 = U.encode("i8", np.random.default_rng(2).integers(-60, 61, size=(32, 7)))
+    vals, meta = oracle.compress("i8", A)
+    c1, _ = oracle.spmm("i8", vals, meta, B1, 32)
+    c2, _ = oracle.spmm("i8", vals, meta, B2, 32)
+    c12, _ = oracle.spmm("i8", vals, meta, (B1.astype(np.int16) + B2).astype(np.int8), 32)
+    assert np.array_equal(c12, c1 + c2)
+
+
+# ---------------------------------------------------------------- argument errors
+
+def test_errors():
+    A = U.random_matrix("f16", 2, 6, "normal", 0)
+    with pytest.raises(oracle.OracleError, match="bad shape"):
+        oracle.compress("f16", A)                      # K % 4 != 0
+    nan = U.encode("f16", [1.0, np.nan, 0.0, 2.0]).reshape(1, 4)
+    with pytest.raises(oracle.OracleError, match="non-finite"):
+        oracle.compress("f16", nan)
+    inf = U.encode("bf16", [1.0, np.inf, 0.0, 2.0]).reshape(1, 4)
+    with pytest.raises(oracle.OracleError, match="non-finite"):
+        oracle.prune("bf16", inf)
+    with pytest.raises(oracle.OracleError):
+        oracle.compress("f32", A)
+
+
+def test_empty_inputs():
+    for dt in DTS:
+        A = np.zeros((0, 8), dtype=U.store_dtype(dt))
+        v, m = oracle.compress(dt, A)
+        assert v.shape == (0, 4) and m.shape == (0, 1)
+        A = np.zeros((3, 0), dtype=U.store_dtype(dt))
+        v, m = oracle.compress(dt, A)
+        assert v.shape == (3, 0) and m.shape == (3, 0)

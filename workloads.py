@@ -1,0 +1,114 @@
+"""Seeded synthetic inputs for the 2:4 SpMM workloads.
+
+This module generates dense inputs only: it holds none of the method's
+arithmetic (no selection, compression or product).  Both the GPU path's
+callers (tests, bench) and the CPU oracle's callers draw their inputs here,
+so the two sides see bit-identical data.
+
+Recipe, per workload:
+* a torch CPU generator per operand, seeded ``1000 + i`` for A, ``2000 + i``
+  for B and ``3000 + i`` for the mask of workload ``i``;
+* floating-point values are drawn in fp32 (``randn`` times the stated sigma)
+  and rounded to nearest-even into fp16 / bf16;
+* int8 values are drawn with ``randint`` over the stated closed range;
+* the moderately-unstructured workload keeps each A element independently
+  with probability 0.5 (``rand < 0.5``); dropped elements are set to +0 with
+  ``torch.where`` so a negative value never turns into -0.
+
+The shapes follow LLM projection layers: 11008 x 4096 is a 7B-class FFN
+weight and 28672 x 8192 a 70B-class FFN weight; 16 columns of B is a decode
+batch, 2048 a prefill chunk.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, replace
+from typing import Optional
+
+import numpy as np
+import torch
+
+TORCH_DTYPE = {"f16": torch.float16, "bf16": torch.bfloat16, "i8": torch.int8}
+
+
+@dataclass(frozen=True)
+class Workload:
+    key: str
+    title: str
+    dtype: str            # "f16" | "bf16" | "i8"
+    M: int
+    K: int
+    N: int
+    index: int            # seeds are 1000+index, 2000+index, 3000+index
+    a_sigma: float = 1.0  # fp: A ~ N(0, a_sigma^2)
+    a_range: tuple = (-127, 127)   # int8: A uniform over this closed range
+    b_range: tuple = (-128, 127)   # int8: B uniform over this closed range
+    keep_prob: Optional[float] = None   # moderately-unstructured mask
+    klass: str = "latency"              # "latency" | "large_n" | "small_n"
+
+    def with_shape(self, M=None, K=None, N=None) -> "Workload":
+        """Same distribution and seeds at another shape (for reduced-size tests)."""
+        return replace(self, M=self.M if M is None else M, K=self.K if K is None else K,
+                       N=self.N if N is None else N)
+
+    @property
+    def residual(self) -> bool:
+        return self.keep_prob is not None
+
+
+WORKLOADS = {
+    "c1": Workload("c1", "fp16 2:4 SpMM M=256 K=256 N=64", "f16", 256, 256, 64, 1, a_sigma=1.0),
+    "c2": Workload("c2", "int8 2:4 SpMM M=K=N=4096", "i8", 4096, 4096, 4096, 2, klass="large_n"),
+    "c3": Workload("c3", "fp16 decode-shape SpMM M=11008 K=4096 N=16", "f16", 11008, 4096, 16, 3,
+                   a_sigma=0.02, klass="small_n"),
+    "c4": Workload("c4", "bf16 prefill-shape SpMM M=28672 K=8192 N=2048", "bf16", 28672, 8192, 2048, 4,
+                   a_sigma=0.02, klass="large_n"),
+    "c5": Workload("c5", "fp16 moderately-unstructured SpMM M=K=8192 N=16 (50% mask, 2:4 + residual)",
+                   "f16", 8192, 8192, 16, 5, a_sigma=0.02, keep_prob=0.5, klass="small_n"),
+}
+
+
+def _gen(seed: int) -> torch.Generator:
+    g = torch.Generator(device="cpu")
+    g.manual_seed(seed)
+    return g
+
+
+def gen_a(w: Workload) -> torch.Tensor:
+    """Dense A [M, K] on the CPU (before any pruning)."""
+    g = _gen(1000 + w.index)
+    if w.dtype == "i8":
+        lo, hi = w.a_range
+        a = torch.randint(lo, hi + 1, (w.M, w.K), generator=g, dtype=torch.int8)
+    else:
+        a = (torch.randn((w.M, w.K), generator=g, dtype=torch.float32) * w.a_sigma).to(TORCH_DTYPE[w.dtype])
+    if w.keep_prob is not None:
+        keep = torch.rand((w.M, w.K), generator=_gen(3000 + w.index)) < w.keep_prob
+        a = torch.where(keep, a, torch.zeros((), dtype=a.dtype))
+    return a
+
+
+def gen_b(w: Workload) -> torch.Tensor:
+    """Dense B [K, N] on the CPU."""
+    g = _gen(2000 + w.index)
+    if w.dtype == "i8":
+        lo, hi = w.b_range
+        return torch.randint(lo, hi + 1, (w.K, w.N), generator=g, dtype=torch.int8)
+    return torch.randn((w.K, w.N), generator=g, dtype=torch.float32).to(TORCH_DTYPE[w.dtype])
+
+
+def bits(t: torch.Tensor) -> np.ndarray:
+    """Raw storage of a CPU tensor as numpy: uint16 bit patterns for fp16/bf16, int8 as is."""
+    t = t.contiguous()
+    if t.dtype in (torch.float16, torch.bfloat16):
+        return t.view(torch.int16).numpy().view(np.uint16)
+    if t.dtype == torch.int8:
+        return t.numpy()
+    raise TypeError("unsupported dtype %s" % (t.dtype,))
+
+
+def from_bits(a: np.ndarray, dtype: str) -> torch.Tensor:
+    """Inverse of bits(): a CPU tensor of the named dtype sharing nothing with a."""
+    a = np.ascontiguousarray(a)
+    if dtype == "i8":
+        return torch.from_numpy(a.astype(np.int8, copy=True))
+    return torch.from_numpy(a.astype(np.uint16, copy=True).view(np.int16)).view(TORCH_DTYPE[dtype])
