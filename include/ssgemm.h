@@ -1,0 +1,177 @@
+/*
+ * ssgemm.h -- C ABI of libssgemm.so: 2:4 structured-sparse weight times dense
+ * activation matrix multiply (SpMM) on AMD Instinct MI355X (gfx950).
+ *
+ * What is computed (the pages this follows):
+ *   - 2:4 structure: in every group of 4 consecutive elements along the
+ *     reduction dimension at most two are non-zero; the two kept values are
+ *     stored with a 2-bit position each, 4 bits per group
+ *     ["Chapter 26 -- Sparsity: The Hardware View", section "2:4 Fine-Grained
+ *      Structured Sparsity", worked example; "10.4g Structured Sparsity (2:4)",
+ *      sections "What is 2:4 Structured Sparsity?" and "How Tensor Cores
+ *      Leverage This Pattern"].
+ *   - Pruning keeps the two largest magnitudes of each group and the kept
+ *     positions are stored in ascending order ["Chapter 26", first listing of
+ *     section "Python: Build a 2:4 Mask, Compress It, ..."].
+ *   - The product is C = A x B with the sparse weight on the left ["Chapter 26",
+ *     second listing of the same section].
+ *   - Moderately unstructured weights are split into a 2:4 layer plus a
+ *     residual layer holding what the 2:4 layer dropped, so the product stays
+ *     exact ["How sparse LLM weights cut GPU inference cost without
+ *     quantization", section "How the three-layer format makes moderate
+ *     sparsity fast"].
+ *
+ * Layout (all row-major, leading dimensions counted in elements):
+ *   A     [M, K]  dense weight, K % 4 == 0, groups of 4 along K (lda >= K)
+ *   vals  [M, K/2] kept values, group g at columns 2g, 2g+1 (ldv >= K/2)
+ *   meta  [M, ceil(K/8)] uint8: nibble of group g is i0 | (i1 << 2), with
+ *         i0 < i1 the kept positions inside the group; group 2j is the low
+ *         nibble of byte j, group 2j+1 the high nibble; an unused high nibble
+ *         of the last byte is 0 (ldm >= ceil(K/8)).  Valid nibbles are
+ *         0x4, 0x8, 0xC, 0x9, 0xD, 0xE.
+ *   B     [K, N]  dense activation (ldb >= N)
+ *   C     [M, N]  fp32 for fp16/bf16 inputs, int32 for int8 inputs (ldc >= N)
+ *   residual: CSR, row_ptr int32 [M+1] (row_ptr[0] = 0), col int32 [nnz]
+ *         ascending within a row, rvals [nnz] in the element type of A.
+ *
+ * Selection rule: for a group with magnitudes a0..a3 (|x| of the value; int8
+ * -128 has magnitude 128; -0 and +0 are equal), position p is kept iff fewer
+ * than two positions q != p have |a_q| > |a_p|, or |a_q| == |a_p| and q < p.
+ * Exactly two slots are stored per group; a kept slot may hold a zero.
+ * Inputs must be finite; NaN/Inf inputs give unspecified selections.
+ *
+ * Ownership and execution: every pointer is device memory owned by the
+ * caller; the library allocates no device memory and keeps no mutable global
+ * state (calls are re-entrant).  Every call validates its arguments on the
+ * host, enqueues its kernels on `stream` (a hipStream_t; NULL = the null
+ * stream) and returns without synchronising.  Asynchronous device faults show
+ * at the caller's next synchronisation.  No C++ exception crosses the ABI.
+ *
+ * Errors: a non-zero return is an ssg_status; nothing was enqueued when
+ * validation fails.  Zero-size problems return SSG_OK and enqueue nothing,
+ * except spmm with K == 0, which zero-fills C.  ssg_last_error() gives a
+ * thread-local description of the last failure.
+ */
+#ifndef SSGEMM_H
+#define SSGEMM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SSG_ABI_VERSION 1
+
+typedef enum {
+    SSG_OK = 0,
+    SSG_ERR_NULL = 1,       /* a required pointer is NULL */
+    SSG_ERR_SHAPE = 2,      /* negative size, K % 4 != 0, or a size too large for the kernels */
+    SSG_ERR_STRIDE = 3,     /* a leading dimension smaller than its row */
+    SSG_ERR_DTYPE = 4,      /* unsupported element type or (input, output) pair */
+    SSG_ERR_FORMAT = 5,     /* inconsistent sparse operand arguments (nnz_r < 0 or above 2^31 - 1) */
+    SSG_ERR_WORKSPACE = 6,  /* workspace smaller than ssg_spmm_workspace_bytes() */
+    SSG_ERR_HIP = 7,        /* a HIP runtime call failed; see ssg_last_error() */
+    SSG_ERR_ALGO = 8        /* the requested algorithm cannot run this problem */
+} ssg_status;
+
+typedef enum { SSG_F16 = 0, SSG_BF16 = 1, SSG_I8 = 2, SSG_F32 = 3, SSG_I32 = 4 } ssg_dtype;
+
+/* SpMM algorithms.  AUTO picks by shape; the others force one kernel family
+ * (for A/B comparison and tests) and return SSG_ERR_ALGO when the problem is
+ * outside what that family handles. */
+typedef enum {
+    SSG_ALGO_AUTO = 0,
+    SSG_ALGO_GENERIC = 1,   /* one thread per output, any shape/stride/alignment */
+    SSG_ALGO_SMALL_N = 2,   /* bandwidth-bound decode shapes (N <= 16) on sparse MFMA */
+    SSG_ALGO_LARGE_N = 3    /* compute-bound tiles on sparse MFMA */
+} ssg_algo;
+
+int ssg_abi_version(void);
+const char* ssg_status_str(int status);
+const char* ssg_last_error(void);
+
+/* Row lengths of the compressed operands for a reduction length K. */
+int64_t ssg_vals_cols(int64_t K);   /* K / 2 */
+int64_t ssg_meta_cols(int64_t K);   /* ceil(K / 8) bytes */
+
+/* P = A with the two dropped elements of every group set to +0 (kept ones
+ * bit-copied).  dt: SSG_F16, SSG_BF16 or SSG_I8.  P may alias A exactly
+ * (in place, lda == ldp); other overlaps are undefined. */
+int ssg_prune_2to4(int dt, int64_t M, int64_t K, const void* A, int64_t lda,
+                   void* P, int64_t ldp, void* stream);
+
+/* (vals, meta) = the 2:4 compressed form of A (values bit-copied). */
+int ssg_compress_2to4(int dt, int64_t M, int64_t K, const void* A, int64_t lda,
+                      void* vals, int64_t ldv, uint8_t* meta, int64_t ldm, void* stream);
+
+/* D = dense expansion of (vals, meta): the two stored values at their
+ * positions, +0 elsewhere.  A group whose nibble is not a valid pair is
+ * written as four zeros and, if bad_count is not NULL, counted into the
+ * device int32 *bad_count (added atomically; the caller zeroes it). */
+int ssg_decompress_2to4(int dt, int64_t M, int64_t K, const void* vals, int64_t ldv,
+                        const uint8_t* meta, int64_t ldm, void* D, int64_t ldd,
+                        int32_t* bad_count, void* stream);
+
+/* Residual split, pass 1: row_ptr[0] = 0 and row_ptr[m+1] = row_ptr[m] + the
+ * number of numerically non-zero elements of row m (-0 counts as zero) that
+ * the 2:4 selection drops.  The caller then reads row_ptr[M] (nnz of the
+ * residual) to size col and rvals.  Fails with SSG_ERR_SHAPE if M * K exceeds
+ * what int32 row_ptr can count (2^31 - 1). */
+int ssg_split_count(int dt, int64_t M, int64_t K, const void* A, int64_t lda,
+                    int32_t* row_ptr, void* stream);
+
+/* Residual split, pass 2: writes the 2:4 layer (as ssg_compress_2to4) and the
+ * CSR residual (col ascending, rvals bit-copied) using row_ptr from pass 1.
+ * col and rvals may be NULL only if row_ptr[M] == 0. */
+int ssg_split_fill(int dt, int64_t M, int64_t K, const void* A, int64_t lda,
+                   void* vals, int64_t ldv, uint8_t* meta, int64_t ldm,
+                   const int32_t* row_ptr, int32_t* col, void* rvals, void* stream);
+
+/* Workspace the SpMM calls need for this problem (bytes; may be 0). */
+size_t ssg_spmm_workspace_bytes(int ab, int64_t M, int64_t N, int64_t K);
+
+/* C = expand(vals, meta) x B.  (ab, c) must be (SSG_F16, SSG_F32),
+ * (SSG_BF16, SSG_F32) or (SSG_I8, SSG_I32).  fp16/bf16 products are
+ * accumulated in fp32 in an order that is fixed for a given shape and
+ * algorithm (results are reproducible run to run); int8 accumulates exactly
+ * in int32 (the caller keeps |C| < 2^31).  Metadata nibbles must be valid
+ * (as produced by ssg_compress_2to4); invalid ones give unspecified values
+ * in the affected outputs, never out-of-bounds accesses. */
+int ssg_spmm_2to4(int ab, int c, int64_t M, int64_t N, int64_t K,
+                  const void* vals, int64_t ldv, const uint8_t* meta, int64_t ldm,
+                  const void* B, int64_t ldb, void* C, int64_t ldc,
+                  void* ws, size_t ws_bytes, void* stream);
+
+/* C = (expand(vals, meta) + residual) x B.  nnz_r must equal row_ptr[M]
+ * (it sizes nothing on the device; it selects the launch shape and is
+ * trusted).  Column indices must lie in [0, K). */
+int ssg_spmm_2to4_residual(int ab, int c, int64_t M, int64_t N, int64_t K,
+                           const void* vals, int64_t ldv, const uint8_t* meta, int64_t ldm,
+                           const int32_t* row_ptr, const int32_t* col, const void* rvals,
+                           int64_t nnz_r, const void* B, int64_t ldb, void* C, int64_t ldc,
+                           void* ws, size_t ws_bytes, void* stream);
+
+/* As the two calls above with an explicit algorithm (ssg_algo). */
+int ssg_spmm_2to4_ex(int algo, int ab, int c, int64_t M, int64_t N, int64_t K,
+                     const void* vals, int64_t ldv, const uint8_t* meta, int64_t ldm,
+                     const void* B, int64_t ldb, void* C, int64_t ldc,
+                     void* ws, size_t ws_bytes, void* stream);
+int ssg_spmm_2to4_residual_ex(int algo, int ab, int c, int64_t M, int64_t N, int64_t K,
+                              const void* vals, int64_t ldv, const uint8_t* meta, int64_t ldm,
+                              const int32_t* row_ptr, const int32_t* col, const void* rvals,
+                              int64_t nnz_r, const void* B, int64_t ldb, void* C, int64_t ldc,
+                              void* ws, size_t ws_bytes, void* stream);
+
+/* The algorithm SSG_ALGO_AUTO would run for this problem and these pointers
+ * and leading dimensions (alignment decides between fast and generic paths). */
+int ssg_spmm_select_algo(int ab, int64_t M, int64_t N, int64_t K,
+                         const void* vals, int64_t ldv, const uint8_t* meta, int64_t ldm,
+                         const void* B, int64_t ldb, const void* C, int64_t ldc);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SSGEMM_H */

@@ -1,0 +1,222 @@
+"""structured_sparse_gemm_amd -- 2:4 structured-sparse weight x dense activation
+matrix multiply for AMD Instinct MI355X (gfx950).
+
+Every computation runs in the HIP kernels of libssgemm.so; this module only
+marshals torch tensors (device memory and the current stream) into the C
+ABI declared in include/ssgemm.h.  There is no CPU fallback: tensors must
+live on a ROCm device and the library must load.
+
+Same-named bindings of the C ABI (``ssg_compress_2to4`` ...) take
+preallocated tensors; ``compress``, ``prune``, ``decompress``, ``split``,
+``spmm`` and ``spmm_residual`` allocate their outputs.
+"""
+from __future__ import annotations
+
+from typing import Optional, Tuple
+
+import torch
+
+from . import _abi
+from ._abi import (SSG_ALGO_AUTO, SSG_ALGO_GENERIC, SSG_ALGO_LARGE_N, SSG_ALGO_SMALL_N, SSG_BF16, SSG_F16,
+                   SSG_F32, SSG_I8, SSG_I32)
+
+__all__ = [
+    "SsgError", "compress", "prune", "decompress", "split", "spmm", "spmm_residual", "vals_cols", "meta_cols",
+    "ssg_prune_2to4", "ssg_compress_2to4", "ssg_decompress_2to4", "ssg_split_count", "ssg_split_fill",
+    "ssg_spmm_workspace_bytes", "ssg_spmm_2to4", "ssg_spmm_2to4_residual", "ssg_spmm_select_algo",
+    "SSG_ALGO_AUTO", "SSG_ALGO_GENERIC", "SSG_ALGO_SMALL_N", "SSG_ALGO_LARGE_N", "library_path",
+]
+
+_DT = {torch.float16: SSG_F16, torch.bfloat16: SSG_BF16, torch.int8: SSG_I8}
+_OUT = {SSG_F16: (SSG_F32, torch.float32), SSG_BF16: (SSG_F32, torch.float32), SSG_I8: (SSG_I32, torch.int32)}
+ALGO_NAMES = {SSG_ALGO_AUTO: "auto", SSG_ALGO_GENERIC: "generic", SSG_ALGO_SMALL_N: "small_n",
+              SSG_ALGO_LARGE_N: "large_n"}
+
+
+class SsgError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(message)
+        self.status = status
+
+
+def library_path() -> str:
+    return _abi.LIB_PATH
+
+
+def _lib():
+    return _abi.load()
+
+
+def _check(rc: int, what: str) -> None:
+    if rc != 0:
+        lib = _lib()
+        raise SsgError(rc, "%s: %s (%s)" % (what, lib.ssg_status_str(rc).decode(), lib.ssg_last_error().decode()))
+
+
+def _dtype(t: torch.Tensor) -> int:
+    if t.dtype not in _DT:
+        raise SsgError(_abi.SSG_ERR_DTYPE, "unsupported element type %s" % (t.dtype,))
+    return _DT[t.dtype]
+
+
+def _ptr(t: Optional[torch.Tensor], name: str):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise SsgError(_abi.SSG_ERR_NULL, "%s must be a ROCm device tensor (got %s)" % (name, t.device))
+    return t.data_ptr() if t.numel() > 0 else None
+
+
+def _ld(t: torch.Tensor, name: str) -> int:
+    if t.dim() != 2:
+        raise SsgError(_abi.SSG_ERR_SHAPE, "%s must be 2-D, got shape %s" % (name, tuple(t.shape)))
+    if t.shape[1] > 1 and t.stride(1) != 1:
+        raise SsgError(_abi.SSG_ERR_STRIDE, "%s must have unit column stride" % name)
+    return max(t.stride(0), t.shape[1]) if t.shape[0] > 1 else t.shape[1]
+
+
+def _stream(t: torch.Tensor, stream) -> Optional[int]:
+    if stream is None:
+        stream = torch.cuda.current_stream(t.device)
+    return getattr(stream, "cuda_stream", stream) or None
+
+
+def vals_cols(K: int) -> int:
+    return int(_lib().ssg_vals_cols(K))
+
+
+def meta_cols(K: int) -> int:
+    return int(_lib().ssg_meta_cols(K))
+
+
+# ---------------------------------------------------------------- same-named bindings
+
+def ssg_prune_2to4(A: torch.Tensor, P: torch.Tensor, stream=None) -> None:
+    M, K = A.shape
+    _check(_lib().ssg_prune_2to4(_dtype(A), M, K, _ptr(A, "A"), _ld(A, "A"), _ptr(P, "P"), _ld(P, "P"),
+                                 _stream(A, stream)), "ssg_prune_2to4")
+
+
+def ssg_compress_2to4(A: torch.Tensor, vals: torch.Tensor, meta: torch.Tensor, stream=None) -> None:
+    M, K = A.shape
+    _check(_lib().ssg_compress_2to4(_dtype(A), M, K, _ptr(A, "A"), _ld(A, "A"), _ptr(vals, "vals"),
+                                    _ld(vals, "vals"), _ptr(meta, "meta"), _ld(meta, "meta"), _stream(A, stream)),
+           "ssg_compress_2to4")
+
+
+def ssg_decompress_2to4(vals: torch.Tensor, meta: torch.Tensor, D: torch.Tensor,
+                        bad_count: Optional[torch.Tensor] = None, stream=None) -> None:
+    M, K = D.shape
+    _check(_lib().ssg_decompress_2to4(_dtype(vals), M, K, _ptr(vals, "vals"), _ld(vals, "vals"),
+                                      _ptr(meta, "meta"), _ld(meta, "meta"), _ptr(D, "D"), _ld(D, "D"),
+                                      _ptr(bad_count, "bad_count"), _stream(D, stream)), "ssg_decompress_2to4")
+
+
+def ssg_split_count(A: torch.Tensor, row_ptr: torch.Tensor, stream=None) -> None:
+    M, K = A.shape
+    _check(_lib().ssg_split_count(_dtype(A), M, K, _ptr(A, "A"), _ld(A, "A"), _ptr(row_ptr, "row_ptr"),
+                                  _stream(A, stream)), "ssg_split_count")
+
+
+def ssg_split_fill(A, vals, meta, row_ptr, col, rvals, stream=None) -> None:
+    M, K = A.shape
+    _check(_lib().ssg_split_fill(_dtype(A), M, K, _ptr(A, "A"), _ld(A, "A"), _ptr(vals, "vals"), _ld(vals, "vals"),
+                                 _ptr(meta, "meta"), _ld(meta, "meta"), _ptr(row_ptr, "row_ptr"),
+                                 _ptr(col, "col"), _ptr(rvals, "rvals"), _stream(A, stream)), "ssg_split_fill")
+
+
+def ssg_spmm_workspace_bytes(dtype: torch.dtype, M: int, N: int, K: int) -> int:
+    return int(_lib().ssg_spmm_workspace_bytes(_DT[dtype], M, N, K))
+
+
+def _workspace(dt_t: torch.dtype, M, N, K, device, ws):
+    need = ssg_spmm_workspace_bytes(dt_t, M, N, K)
+    if ws is None and need > 0:
+        ws = torch.empty(need, dtype=torch.uint8, device=device)
+    return ws, (ws.numel() * ws.element_size() if ws is not None else 0)
+
+
+def ssg_spmm_2to4(vals, meta, B, C, ws=None, algo: int = SSG_ALGO_AUTO, stream=None) -> None:
+    ab = _dtype(vals)
+    M, N, K = vals.shape[0], B.shape[1], B.shape[0]
+    ws, wsb = _workspace(vals.dtype, M, N, K, vals.device, ws)
+    _check(_lib().ssg_spmm_2to4_ex(algo, ab, _OUT[ab][0], M, N, K, _ptr(vals, "vals"), _ld(vals, "vals"),
+                                   _ptr(meta, "meta"), _ld(meta, "meta"), _ptr(B, "B"), _ld(B, "B"), _ptr(C, "C"),
+                                   _ld(C, "C"), _ptr(ws, "ws"), wsb, _stream(C, stream)), "ssg_spmm_2to4")
+
+
+def ssg_spmm_2to4_residual(vals, meta, row_ptr, col, rvals, B, C, ws=None, algo: int = SSG_ALGO_AUTO,
+                           stream=None) -> None:
+    ab = _dtype(vals)
+    M, N, K = vals.shape[0], B.shape[1], B.shape[0]
+    nnz = int(col.numel()) if col is not None else 0
+    ws, wsb = _workspace(vals.dtype, M, N, K, vals.device, ws)
+    _check(_lib().ssg_spmm_2to4_residual_ex(algo, ab, _OUT[ab][0], M, N, K, _ptr(vals, "vals"), _ld(vals, "vals"),
+                                            _ptr(meta, "meta"), _ld(meta, "meta"), _ptr(row_ptr, "row_ptr"),
+                                            _ptr(col, "col"), _ptr(rvals, "rvals"), nnz, _ptr(B, "B"), _ld(B, "B"),
+                                            _ptr(C, "C"), _ld(C, "C"), _ptr(ws, "ws"), wsb, _stream(C, stream)),
+           "ssg_spmm_2to4_residual")
+
+
+def ssg_spmm_select_algo(vals, meta, B, C) -> int:
+    return int(_lib().ssg_spmm_select_algo(_dtype(vals), vals.shape[0], B.shape[1], B.shape[0], _ptr(vals, "vals"),
+                                           _ld(vals, "vals"), _ptr(meta, "meta"), _ld(meta, "meta"), _ptr(B, "B"),
+                                           _ld(B, "B"), _ptr(C, "C"), _ld(C, "C")))
+
+
+# ---------------------------------------------------------------- allocating helpers
+
+def prune(A: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    P = torch.empty_like(A) if out is None else out
+    ssg_prune_2to4(A, P)
+    return P
+
+
+def compress(A: torch.Tensor) -> Tuple[torch.Tensor, torch.Tensor]:
+    """(vals [M, K/2], meta [M, ceil(K/8)] uint8) of a dense [M, K] weight."""
+    M, K = A.shape
+    vals = torch.empty((M, K // 2), dtype=A.dtype, device=A.device)
+    meta = torch.empty((M, (K + 7) // 8), dtype=torch.uint8, device=A.device)
+    ssg_compress_2to4(A, vals, meta)
+    return vals, meta
+
+
+def decompress(vals: torch.Tensor, meta: torch.Tensor, K: Optional[int] = None, count_bad: bool = False):
+    M = vals.shape[0]
+    K = 2 * vals.shape[1] if K is None else K
+    D = torch.empty((M, K), dtype=vals.dtype, device=vals.device)
+    bad = torch.zeros(1, dtype=torch.int32, device=vals.device) if count_bad else None
+    ssg_decompress_2to4(vals, meta, D, bad)
+    return (D, int(bad.item())) if count_bad else D
+
+
+def split(A: torch.Tensor):
+    """2:4 layer plus CSR residual: (vals, meta, row_ptr, col, rvals).  Reads the
+    residual size back to the host between the two passes (one sync)."""
+    M, K = A.shape
+    row_ptr = torch.empty(M + 1, dtype=torch.int32, device=A.device)
+    ssg_split_count(A, row_ptr)
+    nnz = int(row_ptr[M].item())
+    vals = torch.empty((M, K // 2), dtype=A.dtype, device=A.device)
+    meta = torch.empty((M, (K + 7) // 8), dtype=torch.uint8, device=A.device)
+    col = torch.empty(nnz, dtype=torch.int32, device=A.device)
+    rvals = torch.empty(nnz, dtype=A.dtype, device=A.device)
+    ssg_split_fill(A, vals, meta, row_ptr, col if nnz else None, rvals if nnz else None)
+    return vals, meta, row_ptr, col, rvals
+
+
+def spmm(vals: torch.Tensor, meta: torch.Tensor, B: torch.Tensor, algo: int = SSG_ALGO_AUTO,
+         out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """C = expand(vals, meta) @ B: fp32 for fp16/bf16, int32 for int8."""
+    ab = _dtype(vals)
+    C = torch.empty((vals.shape[0], B.shape[1]), dtype=_OUT[ab][1], device=vals.device) if out is None else out
+    ssg_spmm_2to4(vals, meta, B, C, algo=algo)
+    return C
+
+
+def spmm_residual(vals, meta, row_ptr, col, rvals, B, algo: int = SSG_ALGO_AUTO,
+                  out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    ab = _dtype(vals)
+    C = torch.empty((vals.shape[0], B.shape[1]), dtype=_OUT[ab][1], device=vals.device) if out is None else out
+    ssg_spmm_2to4_residual(vals, meta, row_ptr, col, rvals, B, C, algo=algo)
+    return C

@@ -1,0 +1,424 @@
+// compress.hip -- HIP kernels that turn a dense weight into its 2:4 form:
+// magnitude prune, compress (values + 2-bit positions), expand back, and the
+// two-pass split of a moderately unstructured weight into a 2:4 layer plus a
+// CSR residual of the dropped non-zeros.
+//
+// Selection follows "Chapter 26 -- Sparsity: The Hardware View", section
+// "Python: Build a 2:4 Mask, Compress It, ..." (keep the two largest
+// magnitudes of each group of 4 along K, positions ascending); the storage
+// follows the worked example of its section "2:4 Fine-Grained Structured
+// Sparsity"; the residual follows "How sparse LLM weights cut GPU inference
+// cost without quantization", section "How the three-layer format makes
+// moderate sparsity fast".
+//
+// Work unit: one thread owns a chunk of 8 groups (32 elements) of one row,
+// so it writes whole metadata bytes (4 bytes = 8 nibbles) and never shares a
+// byte with another thread.  Full chunks with aligned rows use 16-byte loads
+// and stores; the ragged last chunk of a row and unaligned operands take
+// element-wise accesses in the same kernels.  All of these kernels are
+// HBM-bound streaming passes.
+#include "ssg_device.hpp"
+#include "ssg_kernels.hpp"
+
+namespace ssg {
+
+namespace {
+
+constexpr int kChunkGroups = 8;
+constexpr int kChunkElems = 32;
+
+// Raw storage word of one element: uint16_t for fp16/bf16, int8_t for int8.
+template <int DT> struct Store { using T = uint16_t; };
+template <> struct Store<DT_I8> { using T = int8_t; };
+
+template <int DT>
+__device__ __forceinline__ uint32_t key_of(typename Store<DT>::T x) {
+    if constexpr (DT == DT_I8) return mag_key8((int32_t)x);
+    else return mag_key16((uint32_t)x);
+}
+
+// Loads the chunk's 4*ng elements (ng <= 8) into x[0..31]; missing ones are 0.
+template <int DT>
+__device__ __forceinline__ void load_chunk(const typename Store<DT>::T* a, int ng, bool vec,
+                                           typename Store<DT>::T (&x)[kChunkElems]) {
+    using T = typename Store<DT>::T;
+    if (vec && ng == kChunkGroups) {
+        constexpr int kVecs = kChunkElems * sizeof(T) / 16;
+        uint4 w[kVecs];
+#pragma unroll
+        for (int i = 0; i < kVecs; ++i) w[i] = reinterpret_cast<const uint4*>(a)[i];
+        __builtin_memcpy(x, w, sizeof(w));
+    } else {
+#pragma unroll
+        for (int i = 0; i < kChunkElems; ++i) x[i] = (i < 4 * ng) ? a[i] : T(0);
+    }
+}
+
+template <typename T>
+__device__ __forceinline__ T pick_low(uint32_t i0, T x0, T x1, T x2) { return i0 == 0 ? x0 : (i0 == 1 ? x1 : x2); }
+template <typename T>
+__device__ __forceinline__ T pick_high(uint32_t i1, T x1, T x2, T x3) { return i1 == 1 ? x1 : (i1 == 2 ? x2 : x3); }
+
+// Nibbles of the chunk (nibble g at bits 4g..4g+3) and the kept values.
+template <int DT>
+__device__ __forceinline__ uint32_t select_chunk(const typename Store<DT>::T (&x)[kChunkElems], int ng,
+                                                 typename Store<DT>::T (&v)[2 * kChunkGroups]) {
+    uint32_t word = 0;
+#pragma unroll
+    for (int g = 0; g < kChunkGroups; ++g) {
+        const uint32_t nib = select_nibble(key_of<DT>(x[4 * g]), key_of<DT>(x[4 * g + 1]),
+                                           key_of<DT>(x[4 * g + 2]), key_of<DT>(x[4 * g + 3]));
+        v[2 * g] = pick_low(nib & 3u, x[4 * g], x[4 * g + 1], x[4 * g + 2]);
+        v[2 * g + 1] = pick_high(nib >> 2, x[4 * g + 1], x[4 * g + 2], x[4 * g + 3]);
+        if (g < ng) word |= nib << (4 * g);
+    }
+    return word;
+}
+
+template <int DT>
+__device__ __forceinline__ void store_compressed(typename Store<DT>::T* vrow, uint8_t* mrow, int ng, bool vec,
+                                                 const typename Store<DT>::T (&v)[2 * kChunkGroups], uint32_t word) {
+    using T = typename Store<DT>::T;
+    if (vec && ng == kChunkGroups) {
+        constexpr int kVecs = 2 * kChunkGroups * sizeof(T) / 16;
+        uint4 w[kVecs];
+        __builtin_memcpy(w, v, sizeof(w));
+#pragma unroll
+        for (int i = 0; i < kVecs; ++i) reinterpret_cast<uint4*>(vrow)[i] = w[i];
+        *reinterpret_cast<uint32_t*>(mrow) = word;
+    } else {
+#pragma unroll
+        for (int i = 0; i < 2 * kChunkGroups; ++i)
+            if (i < 2 * ng) vrow[i] = v[i];
+#pragma unroll
+        for (int j = 0; j < kChunkGroups / 2; ++j)
+            if (2 * j < ng) mrow[j] = (uint8_t)(word >> (8 * j));
+    }
+}
+
+template <int DT>
+__global__ void __launch_bounds__(256) k_compress(int64_t M, int64_t K, const typename Store<DT>::T* __restrict__ A,
+                                                  int64_t lda, typename Store<DT>::T* __restrict__ vals, int64_t ldv,
+                                                  uint8_t* __restrict__ meta, int64_t ldm, int vec) {
+    using T = typename Store<DT>::T;
+    const int64_t chunks = (K + kChunkElems - 1) / kChunkElems;
+    const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (t >= M * chunks) return;
+    const int64_t m = t / chunks, c = t - m * chunks;
+    const int ng = (int)min<int64_t>(kChunkGroups, (K - c * kChunkElems) / 4);
+    T x[kChunkElems], v[2 * kChunkGroups];
+    load_chunk<DT>(A + m * lda + c * kChunkElems, ng, vec != 0, x);
+    const uint32_t word = select_chunk<DT>(x, ng, v);
+    store_compressed<DT>(vals + m * ldv + c * 2 * kChunkGroups, meta + m * ldm + c * (kChunkGroups / 2), ng,
+                         vec != 0, v, word);
+}
+
+template <int DT>
+__global__ void __launch_bounds__(256) k_prune(int64_t M, int64_t K, const typename Store<DT>::T* A, int64_t lda,
+                                               typename Store<DT>::T* P, int64_t ldp, int vec) {
+    using T = typename Store<DT>::T;
+    const int64_t chunks = (K + kChunkElems - 1) / kChunkElems;
+    const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (t >= M * chunks) return;
+    const int64_t m = t / chunks, c = t - m * chunks;
+    const int ng = (int)min<int64_t>(kChunkGroups, (K - c * kChunkElems) / 4);
+    T x[kChunkElems], v[2 * kChunkGroups];
+    load_chunk<DT>(A + m * lda + c * kChunkElems, ng, vec != 0, x);   // whole chunk read before any write
+    const uint32_t word = select_chunk<DT>(x, ng, v);
+#pragma unroll
+    for (int g = 0; g < kChunkGroups; ++g) {
+        const uint32_t nib = (word >> (4 * g)) & 0xFu, i0 = nib & 3u, i1 = nib >> 2;
+#pragma unroll
+        for (int p = 0; p < 4; ++p)
+            if (p != (int)i0 && p != (int)i1) x[4 * g + p] = T(0);
+    }
+    T* prow = P + m * ldp + c * kChunkElems;
+    if (vec && ng == kChunkGroups) {
+        constexpr int kVecs = kChunkElems * sizeof(T) / 16;
+        uint4 w[kVecs];
+        __builtin_memcpy(w, x, sizeof(w));
+#pragma unroll
+        for (int i = 0; i < kVecs; ++i) reinterpret_cast<uint4*>(prow)[i] = w[i];
+    } else {
+#pragma unroll
+        for (int i = 0; i < kChunkElems; ++i)
+            if (i < 4 * ng) prow[i] = x[i];
+    }
+}
+
+template <int DT>
+__global__ void __launch_bounds__(256) k_decompress(int64_t M, int64_t K, const typename Store<DT>::T* vals,
+                                                    int64_t ldv, const uint8_t* meta, int64_t ldm,
+                                                    typename Store<DT>::T* D, int64_t ldd, int32_t* bad_count,
+                                                    int vec) {
+    using T = typename Store<DT>::T;
+    const int64_t chunks = (K + kChunkElems - 1) / kChunkElems;
+    const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (t >= M * chunks) return;
+    const int64_t m = t / chunks, c = t - m * chunks;
+    const int ng = (int)min<int64_t>(kChunkGroups, (K - c * kChunkElems) / 4);
+    const T* vrow = vals + m * ldv + c * 2 * kChunkGroups;
+    const uint8_t* mrow = meta + m * ldm + c * (kChunkGroups / 2);
+    T v[2 * kChunkGroups];
+    uint32_t word = 0;
+    if (vec && ng == kChunkGroups) {
+        constexpr int kVecs = 2 * kChunkGroups * sizeof(T) / 16;
+        uint4 w[kVecs];
+#pragma unroll
+        for (int i = 0; i < kVecs; ++i) w[i] = reinterpret_cast<const uint4*>(vrow)[i];
+        __builtin_memcpy(v, w, sizeof(w));
+        word = *reinterpret_cast<const uint32_t*>(mrow);
+    } else {
+#pragma unroll
+        for (int i = 0; i < 2 * kChunkGroups; ++i) v[i] = (i < 2 * ng) ? vrow[i] : T(0);
+#pragma unroll
+        for (int j = 0; j < kChunkGroups / 2; ++j)
+            if (2 * j < ng) word |= (uint32_t)mrow[j] << (8 * j);
+    }
+    T x[kChunkElems];
+    int bad = 0;
+#pragma unroll
+    for (int g = 0; g < kChunkGroups; ++g) {
+        const uint32_t nib = (word >> (4 * g)) & 0xFu, i0 = nib & 3u, i1 = nib >> 2;
+        const bool ok = nibble_valid(nib);
+        if (g < ng && !ok) ++bad;
+#pragma unroll
+        for (int p = 0; p < 4; ++p)
+            x[4 * g + p] = (ok && p == (int)i0) ? v[2 * g] : ((ok && p == (int)i1) ? v[2 * g + 1] : T(0));
+    }
+    T* drow = D + m * ldd + c * kChunkElems;
+    if (vec && ng == kChunkGroups) {
+        constexpr int kVecs = kChunkElems * sizeof(T) / 16;
+        uint4 w[kVecs];
+        __builtin_memcpy(w, x, sizeof(w));
+#pragma unroll
+        for (int i = 0; i < kVecs; ++i) reinterpret_cast<uint4*>(drow)[i] = w[i];
+    } else {
+#pragma unroll
+        for (int i = 0; i < kChunkElems; ++i)
+            if (i < 4 * ng) drow[i] = x[i];
+    }
+    if (bad && bad_count) atomicAdd(bad_count, bad);
+}
+
+// ---- residual split -------------------------------------------------------
+
+constexpr int kSplitThreads = 256;
+
+// Exclusive prefix sum over a 256-thread block; *total receives the sum.
+__device__ __forceinline__ int block_exclusive_scan(int v, int* total, int* lds4) {
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+    int x = v;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const int y = __shfl_up(x, d, 64);
+        if (lane >= d) x += y;
+    }
+    if (lane == 63) lds4[wid] = x;
+    __syncthreads();
+    int before = 0, sum = 0;
+#pragma unroll
+    for (int w = 0; w < kSplitThreads / 64; ++w) {
+        const int s = lds4[w];
+        before += (w < wid) ? s : 0;
+        sum += s;
+    }
+    __syncthreads();
+    *total = sum;
+    return before + x - v;
+}
+
+// Dropped non-zeros of a chunk as a bit mask over its 32 elements.
+template <int DT>
+__device__ __forceinline__ uint32_t overflow_mask(const typename Store<DT>::T (&x)[kChunkElems], uint32_t word,
+                                                  int ng) {
+    uint32_t mask = 0;
+#pragma unroll
+    for (int g = 0; g < kChunkGroups; ++g) {
+        const uint32_t nib = (word >> (4 * g)) & 0xFu, i0 = nib & 3u, i1 = nib >> 2;
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            const bool dropped_nonzero = p != (int)i0 && p != (int)i1 && key_of<DT>(x[4 * g + p]) != 0u;
+            if (g < ng && dropped_nonzero) mask |= 1u << (4 * g + p);
+        }
+    }
+    return mask;
+}
+
+// Pass 1: per-row counts into row_ptr[m + 1]; one block per row (grid-stride).
+template <int DT>
+__global__ void __launch_bounds__(kSplitThreads) k_split_count(int64_t M, int64_t K, const typename Store<DT>::T* A,
+                                                               int64_t lda, int32_t* row_ptr, int vec) {
+    using T = typename Store<DT>::T;
+    __shared__ int lds4[kSplitThreads / 64];
+    const int64_t chunks = (K + kChunkElems - 1) / kChunkElems;
+    for (int64_t m = blockIdx.x; m < M; m += gridDim.x) {
+        int cnt = 0;
+        for (int64_t c = threadIdx.x; c < chunks; c += kSplitThreads) {
+            const int ng = (int)min<int64_t>(kChunkGroups, (K - c * kChunkElems) / 4);
+            T x[kChunkElems], v[2 * kChunkGroups];
+            load_chunk<DT>(A + m * lda + c * kChunkElems, ng, vec != 0, x);
+            const uint32_t word = select_chunk<DT>(x, ng, v);
+            cnt += __popc(overflow_mask<DT>(x, word, ng));
+        }
+        int total;
+        block_exclusive_scan(cnt, &total, lds4);
+        if (threadIdx.x == 0) row_ptr[m + 1] = total;
+    }
+}
+
+// Inclusive scan of row_ptr[1..M] in place, row_ptr[0] = 0; one block.
+__global__ void __launch_bounds__(1024) k_scan_rows(int64_t M, int32_t* row_ptr) {
+    __shared__ int wsum[16];
+    __shared__ int carry_s;
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+    if (threadIdx.x == 0) { row_ptr[0] = 0; carry_s = 0; }
+    __syncthreads();
+    for (int64_t base = 0; base < M; base += 1024) {
+        const int64_t i = base + threadIdx.x;
+        const int v = (i < M) ? row_ptr[i + 1] : 0;
+        int x = v;
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            const int y = __shfl_up(x, d, 64);
+            if (lane >= d) x += y;
+        }
+        if (lane == 63) wsum[wid] = x;
+        __syncthreads();
+        int before = carry_s, sum = 0;
+        for (int w = 0; w < 16; ++w) {
+            before += (w < wid) ? wsum[w] : 0;
+            sum += wsum[w];
+        }
+        if (i < M) row_ptr[i + 1] = before + x;
+        __syncthreads();
+        if (threadIdx.x == 0) carry_s += sum;
+        __syncthreads();
+    }
+}
+
+// Pass 2: the 2:4 layer and the CSR residual; one block per row (grid-stride).
+// Chunks are taken 256 at a time in K order; a block scan places each
+// thread's dropped non-zeros after those of lower chunks, so columns come
+// out ascending.
+template <int DT>
+__global__ void __launch_bounds__(kSplitThreads) k_split_fill(int64_t M, int64_t K, const typename Store<DT>::T* A,
+                                                              int64_t lda, typename Store<DT>::T* vals, int64_t ldv,
+                                                              uint8_t* meta, int64_t ldm, const int32_t* row_ptr,
+                                                              int32_t* col, typename Store<DT>::T* rvals, int vec) {
+    using T = typename Store<DT>::T;
+    __shared__ int lds4[kSplitThreads / 64];
+    const int64_t chunks = (K + kChunkElems - 1) / kChunkElems;
+    for (int64_t m = blockIdx.x; m < M; m += gridDim.x) {
+        int64_t carry = row_ptr[m];
+        for (int64_t c0 = 0; c0 < chunks; c0 += kSplitThreads) {
+            const int64_t c = c0 + threadIdx.x;
+            uint32_t mask = 0;
+            T x[kChunkElems];
+            if (c < chunks) {
+                const int ng = (int)min<int64_t>(kChunkGroups, (K - c * kChunkElems) / 4);
+                T v[2 * kChunkGroups];
+                load_chunk<DT>(A + m * lda + c * kChunkElems, ng, vec != 0, x);
+                const uint32_t word = select_chunk<DT>(x, ng, v);
+                store_compressed<DT>(vals + m * ldv + c * 2 * kChunkGroups, meta + m * ldm + c * (kChunkGroups / 2),
+                                     ng, vec != 0, v, word);
+                mask = overflow_mask<DT>(x, word, ng);
+            }
+            int total;
+            const int before = block_exclusive_scan(__popc(mask), &total, lds4);
+            if (col != nullptr) {
+                int64_t pos = carry + before;
+#pragma unroll
+                for (int i = 0; i < kChunkElems; ++i) {
+                    if (mask & (1u << i)) {
+                        col[pos] = (int32_t)(c * kChunkElems + i);
+                        rvals[pos] = x[i];
+                        ++pos;
+                    }
+                }
+            }
+            carry += total;
+        }
+    }
+}
+
+inline unsigned blocks_for(int64_t threads, int per_block) {
+    return (unsigned)((threads + per_block - 1) / per_block);
+}
+
+}  // namespace
+
+// ---- host launchers --------------------------------------------------------
+
+#define SSG_DISPATCH_DT(dt, BODY)                                        \
+    switch (dt) {                                                        \
+        case DT_F16: { constexpr int D = DT_F16; BODY; } break;           \
+        case DT_BF16: { constexpr int D = DT_BF16; BODY; } break;         \
+        case DT_I8: { constexpr int D = DT_I8; BODY; } break;             \
+        default: return hipErrorInvalidValue;                            \
+    }
+
+hipError_t launch_compress(int dt, int64_t M, int64_t K, const void* A, int64_t lda, void* vals, int64_t ldv,
+                           uint8_t* meta, int64_t ldm, bool vec, hipStream_t s) {
+    const int64_t threads = M * ((K + kChunkElems - 1) / kChunkElems);
+    if (threads == 0) return hipSuccess;
+    SSG_DISPATCH_DT(dt, {
+        using T = typename Store<D>::T;
+        hipLaunchKernelGGL(k_compress<D>, dim3(blocks_for(threads, 256)), dim3(256), 0, s, M, K, (const T*)A, lda,
+                           (T*)vals, ldv, meta, ldm, (int)vec);
+    });
+    return hipGetLastError();
+}
+
+hipError_t launch_prune(int dt, int64_t M, int64_t K, const void* A, int64_t lda, void* P, int64_t ldp, bool vec,
+                        hipStream_t s) {
+    const int64_t threads = M * ((K + kChunkElems - 1) / kChunkElems);
+    if (threads == 0) return hipSuccess;
+    SSG_DISPATCH_DT(dt, {
+        using T = typename Store<D>::T;
+        hipLaunchKernelGGL(k_prune<D>, dim3(blocks_for(threads, 256)), dim3(256), 0, s, M, K, (const T*)A, lda,
+                           (T*)P, ldp, (int)vec);
+    });
+    return hipGetLastError();
+}
+
+hipError_t launch_decompress(int dt, int64_t M, int64_t K, const void* vals, int64_t ldv, const uint8_t* meta,
+                             int64_t ldm, void* D_, int64_t ldd, int32_t* bad, bool vec, hipStream_t s) {
+    const int64_t threads = M * ((K + kChunkElems - 1) / kChunkElems);
+    if (threads == 0) return hipSuccess;
+    SSG_DISPATCH_DT(dt, {
+        using T = typename Store<D>::T;
+        hipLaunchKernelGGL(k_decompress<D>, dim3(blocks_for(threads, 256)), dim3(256), 0, s, M, K, (const T*)vals,
+                           ldv, meta, ldm, (T*)D_, ldd, bad, (int)vec);
+    });
+    return hipGetLastError();
+}
+
+hipError_t launch_split_count(int dt, int64_t M, int64_t K, const void* A, int64_t lda, int32_t* row_ptr, bool vec,
+                              hipStream_t s) {
+    const unsigned grid = (unsigned)(M < 65536 ? M : 65536);
+    if (M > 0) {
+        SSG_DISPATCH_DT(dt, {
+            using T = typename Store<D>::T;
+            hipLaunchKernelGGL(k_split_count<D>, dim3(grid), dim3(kSplitThreads), 0, s, M, K, (const T*)A, lda,
+                               row_ptr, (int)vec);
+        });
+    }
+    hipLaunchKernelGGL(k_scan_rows, dim3(1), dim3(1024), 0, s, M, row_ptr);
+    return hipGetLastError();
+}
+
+hipError_t launch_split_fill(int dt, int64_t M, int64_t K, const void* A, int64_t lda, void* vals, int64_t ldv,
+                             uint8_t* meta, int64_t ldm, const int32_t* row_ptr, int32_t* col, void* rvals, bool vec,
+                             hipStream_t s) {
+    if (M == 0) return hipSuccess;
+    const unsigned grid = (unsigned)(M < 65536 ? M : 65536);
+    SSG_DISPATCH_DT(dt, {
+        using T = typename Store<D>::T;
+        hipLaunchKernelGGL(k_split_fill<D>, dim3(grid), dim3(kSplitThreads), 0, s, M, K, (const T*)A, lda, (T*)vals,
+                           ldv, meta, ldm, row_ptr, col, (T*)rvals, (int)vec);
+    });
+    return hipGetLastError();
+}
+
+}  // namespace ssg

@@ -1,0 +1,52 @@
+// ssg_kernels.hpp -- host-side launchers of the HIP kernels (internal to
+// libssgemm; the public surface is include/ssgemm.h).  Every launcher
+// enqueues on stream `s` and returns the launch status; the caller has
+// validated sizes, strides and pointers.  `vec` = operands are aligned for
+// 16-byte vector accesses.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ssg {
+
+enum Dtype { DT_F16 = 0, DT_BF16 = 1, DT_I8 = 2 };
+
+hipError_t launch_compress(int dt, int64_t M, int64_t K, const void* A, int64_t lda, void* vals, int64_t ldv,
+                           uint8_t* meta, int64_t ldm, bool vec, hipStream_t s);
+hipError_t launch_prune(int dt, int64_t M, int64_t K, const void* A, int64_t lda, void* P, int64_t ldp, bool vec,
+                        hipStream_t s);
+hipError_t launch_decompress(int dt, int64_t M, int64_t K, const void* vals, int64_t ldv, const uint8_t* meta,
+                             int64_t ldm, void* D, int64_t ldd, int32_t* bad, bool vec, hipStream_t s);
+hipError_t launch_split_count(int dt, int64_t M, int64_t K, const void* A, int64_t lda, int32_t* row_ptr, bool vec,
+                              hipStream_t s);
+hipError_t launch_split_fill(int dt, int64_t M, int64_t K, const void* A, int64_t lda, void* vals, int64_t ldv,
+                             uint8_t* meta, int64_t ldm, const int32_t* row_ptr, int32_t* col, void* rvals, bool vec,
+                             hipStream_t s);
+
+// Sparse operand of one SpMM call.
+struct SpmmArgs {
+    int dt;                     // DT_F16 / DT_BF16 / DT_I8
+    int64_t M, N, K;
+    const void* vals; int64_t ldv;
+    const uint8_t* meta; int64_t ldm;
+    const int32_t* row_ptr;     // residual CSR (nullptr: none)
+    const int32_t* col;
+    const void* rvals;
+    int64_t nnz_r;
+    const void* B; int64_t ldb;
+    void* C; int64_t ldc;       // fp32 or int32
+};
+
+hipError_t launch_spmm_generic(const SpmmArgs& a, hipStream_t s);
+// Residual-only pass: C += residual x B (C already holds the 2:4 product).
+hipError_t launch_residual_add(const SpmmArgs& a, hipStream_t s);
+
+// Fast paths.  `supported_*` say whether a problem fits the kernel family
+// (shape, alignment); the launchers assume it does.
+bool supported_small_n(const SpmmArgs& a);
+hipError_t launch_spmm_small_n(const SpmmArgs& a, hipStream_t s);
+bool supported_large_n(const SpmmArgs& a);
+hipError_t launch_spmm_large_n(const SpmmArgs& a, hipStream_t s);
+
+}  // namespace ssg

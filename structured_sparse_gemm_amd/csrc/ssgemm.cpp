@@ -1,0 +1,270 @@
+// ssgemm.cpp -- the C ABI of libssgemm (include/ssgemm.h): host-side
+// argument validation, alignment checks and kernel dispatch.  Nothing here
+// allocates device memory or keeps mutable global state; the only
+// per-thread state is the text of the last error.
+#include "ssgemm.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <string>
+
+#include "ssg_kernels.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int status, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return status;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+    return fail(SSG_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool in_dtype(int dt) { return dt == SSG_F16 || dt == SSG_BF16 || dt == SSG_I8; }
+int64_t esize(int dt) { return dt == SSG_I8 ? 1 : 2; }
+bool al(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// A row chunk of 32 elements is 16-byte aligned when the base is and the
+// row stride is a multiple of 16 bytes.
+bool rows_aligned16(const void* p, int64_t ld, int dt) { return al(p, 16) && (ld * esize(dt)) % 16 == 0; }
+
+int check_dense(int dt, int64_t M, int64_t K, const void* A, int64_t lda) {
+    if (!in_dtype(dt)) return fail(SSG_ERR_DTYPE, "element type %d is not SSG_F16, SSG_BF16 or SSG_I8", dt);
+    if (M < 0 || K < 0) return fail(SSG_ERR_SHAPE, "negative size M=%lld K=%lld", (long long)M, (long long)K);
+    if (K % 4 != 0) return fail(SSG_ERR_SHAPE, "K=%lld is not a multiple of 4", (long long)K);
+    // thread count of the chunked kernels must fit a 1-D grid
+    if ((M * ((K + 31) / 32)) / 256 >= (int64_t)1 << 31)
+        return fail(SSG_ERR_SHAPE, "M*K too large (%lld x %lld)", (long long)M, (long long)K);
+    if (M > 0 && K > 0 && !A) return fail(SSG_ERR_NULL, "A is NULL");
+    if (lda < K) return fail(SSG_ERR_STRIDE, "lda=%lld < K=%lld", (long long)lda, (long long)K);
+    return SSG_OK;
+}
+
+int check_compressed(int64_t M, int64_t K, const void* vals, int64_t ldv, const uint8_t* meta, int64_t ldm,
+                     bool need) {
+    if (need && M > 0 && K > 0 && (!vals || !meta)) return fail(SSG_ERR_NULL, "vals or meta is NULL");
+    if (ldv < K / 2) return fail(SSG_ERR_STRIDE, "ldv=%lld < K/2=%lld", (long long)ldv, (long long)(K / 2));
+    if (ldm < (K + 7) / 8) return fail(SSG_ERR_STRIDE, "ldm=%lld < ceil(K/8)=%lld", (long long)ldm, (long long)((K + 7) / 8));
+    return SSG_OK;
+}
+
+bool vec_compressed(int dt, const void* vals, int64_t ldv, const uint8_t* meta, int64_t ldm) {
+    return rows_aligned16(vals, ldv, dt) && al(meta, 4) && ldm % 4 == 0;
+}
+
+int to_dt(int dt) { return dt == SSG_F16 ? ssg::DT_F16 : (dt == SSG_BF16 ? ssg::DT_BF16 : ssg::DT_I8); }
+
+int check_spmm(int ab, int c, int64_t M, int64_t N, int64_t K, const void* vals, int64_t ldv, const uint8_t* meta,
+               int64_t ldm, const void* B, int64_t ldb, const void* C, int64_t ldc) {
+    const bool pair_ok = (ab == SSG_F16 && c == SSG_F32) || (ab == SSG_BF16 && c == SSG_F32) ||
+                         (ab == SSG_I8 && c == SSG_I32);
+    if (!pair_ok) return fail(SSG_ERR_DTYPE, "unsupported (input, output) types (%d, %d)", ab, c);
+    if (M < 0 || N < 0 || K < 0) return fail(SSG_ERR_SHAPE, "negative size");
+    if (K % 4 != 0) return fail(SSG_ERR_SHAPE, "K=%lld is not a multiple of 4", (long long)K);
+    if (N > ((int64_t)1 << 31) || M > ((int64_t)1 << 40)) return fail(SSG_ERR_SHAPE, "size too large");
+    int rc = check_compressed(M, K, vals, ldv, meta, ldm, true);
+    if (rc) return rc;
+    if (K > 0 && N > 0 && !B) return fail(SSG_ERR_NULL, "B is NULL");
+    if (M > 0 && N > 0 && !C) return fail(SSG_ERR_NULL, "C is NULL");
+    if (ldb < N) return fail(SSG_ERR_STRIDE, "ldb=%lld < N=%lld", (long long)ldb, (long long)N);
+    if (ldc < N) return fail(SSG_ERR_STRIDE, "ldc=%lld < N=%lld", (long long)ldc, (long long)N);
+    return SSG_OK;
+}
+
+int pick_algo(const ssg::SpmmArgs& a) {
+    if (a.K > 0 && ssg::supported_small_n(a)) return SSG_ALGO_SMALL_N;
+    if (a.K > 0 && ssg::supported_large_n(a)) return SSG_ALGO_LARGE_N;
+    return SSG_ALGO_GENERIC;
+}
+
+int run_spmm(int algo, const ssg::SpmmArgs& a, hipStream_t s) {
+    if (a.M == 0 || a.N == 0) return SSG_OK;
+    if (algo == SSG_ALGO_AUTO) algo = pick_algo(a);
+    hipError_t e = hipSuccess;
+    switch (algo) {
+        case SSG_ALGO_GENERIC:
+            e = ssg::launch_spmm_generic(a, s);
+            break;
+        case SSG_ALGO_SMALL_N:
+            if (a.K == 0 || !ssg::supported_small_n(a))
+                return fail(SSG_ERR_ALGO, "the small-N kernel does not take this problem (N=%lld, alignment)",
+                            (long long)a.N);
+            e = ssg::launch_spmm_small_n(a, s);
+            break;
+        case SSG_ALGO_LARGE_N:
+            if (a.K == 0 || !ssg::supported_large_n(a))
+                return fail(SSG_ERR_ALGO, "the large-N kernel does not take this problem (shape, alignment)");
+            e = ssg::launch_spmm_large_n(a, s);
+            // the large-N tiles cover the 2:4 layer; the residual is a second pass
+            if (e == hipSuccess && a.row_ptr) e = ssg::launch_residual_add(a, s);
+            break;
+        default:
+            return fail(SSG_ERR_ALGO, "unknown algorithm %d", algo);
+    }
+    if (e != hipSuccess) return hip_fail(e, "kernel launch");
+    return SSG_OK;
+}
+
+ssg::SpmmArgs make_args(int ab, int64_t M, int64_t N, int64_t K, const void* vals, int64_t ldv,
+                        const uint8_t* meta, int64_t ldm, const void* B, int64_t ldb, void* C, int64_t ldc) {
+    ssg::SpmmArgs a{};
+    a.dt = to_dt(ab);
+    a.M = M; a.N = N; a.K = K;
+    a.vals = vals; a.ldv = ldv; a.meta = meta; a.ldm = ldm;
+    a.row_ptr = nullptr; a.col = nullptr; a.rvals = nullptr; a.nnz_r = 0;
+    a.B = B; a.ldb = ldb; a.C = C; a.ldc = ldc;
+    return a;
+}
+
+}  // namespace
+
+extern "C" {
+
+int ssg_abi_version(void) { return SSG_ABI_VERSION; }
+
+const char* ssg_status_str(int status) {
+    switch (status) {
+        case SSG_OK: return "SSG_OK";
+        case SSG_ERR_NULL: return "SSG_ERR_NULL: a required pointer is NULL";
+        case SSG_ERR_SHAPE: return "SSG_ERR_SHAPE: invalid or unsupported size";
+        case SSG_ERR_STRIDE: return "SSG_ERR_STRIDE: leading dimension smaller than the row";
+        case SSG_ERR_DTYPE: return "SSG_ERR_DTYPE: unsupported element type";
+        case SSG_ERR_FORMAT: return "SSG_ERR_FORMAT: inconsistent sparse operand";
+        case SSG_ERR_WORKSPACE: return "SSG_ERR_WORKSPACE: workspace too small";
+        case SSG_ERR_HIP: return "SSG_ERR_HIP: HIP runtime error";
+        case SSG_ERR_ALGO: return "SSG_ERR_ALGO: algorithm cannot run this problem";
+        default: return "unknown ssg_status";
+    }
+}
+
+const char* ssg_last_error(void) { return g_last_error.c_str(); }
+
+int64_t ssg_vals_cols(int64_t K) { return K / 2; }
+int64_t ssg_meta_cols(int64_t K) { return (K + 7) / 8; }
+
+int ssg_prune_2to4(int dt, int64_t M, int64_t K, const void* A, int64_t lda, void* P, int64_t ldp, void* stream) {
+    int rc = check_dense(dt, M, K, A, lda);
+    if (rc) return rc;
+    if (M > 0 && K > 0 && !P) return fail(SSG_ERR_NULL, "P is NULL");
+    if (ldp < K) return fail(SSG_ERR_STRIDE, "ldp=%lld < K=%lld", (long long)ldp, (long long)K);
+    if (P == A && ldp != lda) return fail(SSG_ERR_STRIDE, "in-place prune needs ldp == lda");
+    const bool vec = rows_aligned16(A, lda, dt) && rows_aligned16(P, ldp, dt);
+    hipError_t e = ssg::launch_prune(to_dt(dt), M, K, A, lda, P, ldp, vec, (hipStream_t)stream);
+    return e == hipSuccess ? SSG_OK : hip_fail(e, "prune launch");
+}
+
+int ssg_compress_2to4(int dt, int64_t M, int64_t K, const void* A, int64_t lda, void* vals, int64_t ldv,
+                      uint8_t* meta, int64_t ldm, void* stream) {
+    int rc = check_dense(dt, M, K, A, lda);
+    if (rc) return rc;
+    rc = check_compressed(M, K, vals, ldv, meta, ldm, true);
+    if (rc) return rc;
+    const bool vec = rows_aligned16(A, lda, dt) && vec_compressed(dt, vals, ldv, meta, ldm);
+    hipError_t e = ssg::launch_compress(to_dt(dt), M, K, A, lda, vals, ldv, meta, ldm, vec, (hipStream_t)stream);
+    return e == hipSuccess ? SSG_OK : hip_fail(e, "compress launch");
+}
+
+int ssg_decompress_2to4(int dt, int64_t M, int64_t K, const void* vals, int64_t ldv, const uint8_t* meta,
+                        int64_t ldm, void* D, int64_t ldd, int32_t* bad_count, void* stream) {
+    int rc = check_dense(dt, M, K, D, ldd);
+    if (rc) return rc;
+    rc = check_compressed(M, K, vals, ldv, meta, ldm, true);
+    if (rc) return rc;
+    const bool vec = rows_aligned16(D, ldd, dt) && vec_compressed(dt, vals, ldv, meta, ldm);
+    hipError_t e = ssg::launch_decompress(to_dt(dt), M, K, vals, ldv, meta, ldm, D, ldd, bad_count, vec,
+                                          (hipStream_t)stream);
+    return e == hipSuccess ? SSG_OK : hip_fail(e, "decompress launch");
+}
+
+int ssg_split_count(int dt, int64_t M, int64_t K, const void* A, int64_t lda, int32_t* row_ptr, void* stream) {
+    int rc = check_dense(dt, M, K, A, lda);
+    if (rc) return rc;
+    if (!row_ptr) return fail(SSG_ERR_NULL, "row_ptr is NULL");
+    if (M > 0 && K / 2 > 0 && M > INT32_MAX / (K / 2))
+        return fail(SSG_ERR_SHAPE, "residual of a %lld x %lld matrix may not fit int32 row_ptr", (long long)M,
+                    (long long)K);
+    hipError_t e = ssg::launch_split_count(to_dt(dt), M, K, A, lda, row_ptr, rows_aligned16(A, lda, dt),
+                                           (hipStream_t)stream);
+    return e == hipSuccess ? SSG_OK : hip_fail(e, "split_count launch");
+}
+
+int ssg_split_fill(int dt, int64_t M, int64_t K, const void* A, int64_t lda, void* vals, int64_t ldv,
+                   uint8_t* meta, int64_t ldm, const int32_t* row_ptr, int32_t* col, void* rvals, void* stream) {
+    int rc = check_dense(dt, M, K, A, lda);
+    if (rc) return rc;
+    rc = check_compressed(M, K, vals, ldv, meta, ldm, true);
+    if (rc) return rc;
+    if (!row_ptr) return fail(SSG_ERR_NULL, "row_ptr is NULL");
+    if ((col == nullptr) != (rvals == nullptr)) return fail(SSG_ERR_NULL, "col and rvals must both be set or both NULL");
+    if (M > 0 && K / 2 > 0 && M > INT32_MAX / (K / 2))
+        return fail(SSG_ERR_SHAPE, "residual may not fit int32 indices");
+    const bool vec = rows_aligned16(A, lda, dt) && vec_compressed(dt, vals, ldv, meta, ldm);
+    hipError_t e = ssg::launch_split_fill(to_dt(dt), M, K, A, lda, vals, ldv, meta, ldm, row_ptr, col, rvals, vec,
+                                          (hipStream_t)stream);
+    return e == hipSuccess ? SSG_OK : hip_fail(e, "split_fill launch");
+}
+
+size_t ssg_spmm_workspace_bytes(int ab, int64_t M, int64_t N, int64_t K) {
+    (void)ab; (void)M; (void)N; (void)K;
+    return 0;
+}
+
+int ssg_spmm_2to4_ex(int algo, int ab, int c, int64_t M, int64_t N, int64_t K, const void* vals, int64_t ldv,
+                     const uint8_t* meta, int64_t ldm, const void* B, int64_t ldb, void* C, int64_t ldc, void* ws,
+                     size_t ws_bytes, void* stream) {
+    int rc = check_spmm(ab, c, M, N, K, vals, ldv, meta, ldm, B, ldb, C, ldc);
+    if (rc) return rc;
+    const size_t need = ssg_spmm_workspace_bytes(ab, M, N, K);
+    if (ws_bytes < need || (need > 0 && !ws)) return fail(SSG_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
+    return run_spmm(algo, make_args(ab, M, N, K, vals, ldv, meta, ldm, B, ldb, C, ldc), (hipStream_t)stream);
+}
+
+int ssg_spmm_2to4(int ab, int c, int64_t M, int64_t N, int64_t K, const void* vals, int64_t ldv, const uint8_t* meta,
+                  int64_t ldm, const void* B, int64_t ldb, void* C, int64_t ldc, void* ws, size_t ws_bytes,
+                  void* stream) {
+    return ssg_spmm_2to4_ex(SSG_ALGO_AUTO, ab, c, M, N, K, vals, ldv, meta, ldm, B, ldb, C, ldc, ws, ws_bytes,
+                            stream);
+}
+
+int ssg_spmm_2to4_residual_ex(int algo, int ab, int c, int64_t M, int64_t N, int64_t K, const void* vals,
+                              int64_t ldv, const uint8_t* meta, int64_t ldm, const int32_t* row_ptr,
+                              const int32_t* col, const void* rvals, int64_t nnz_r, const void* B, int64_t ldb,
+                              void* C, int64_t ldc, void* ws, size_t ws_bytes, void* stream) {
+    int rc = check_spmm(ab, c, M, N, K, vals, ldv, meta, ldm, B, ldb, C, ldc);
+    if (rc) return rc;
+    if (nnz_r < 0 || nnz_r > INT32_MAX) return fail(SSG_ERR_FORMAT, "nnz_r=%lld out of range", (long long)nnz_r);
+    if (M > 0 && !row_ptr) return fail(SSG_ERR_NULL, "row_ptr is NULL");
+    if (nnz_r > 0 && (!col || !rvals)) return fail(SSG_ERR_NULL, "col or rvals is NULL with nnz_r > 0");
+    const size_t need = ssg_spmm_workspace_bytes(ab, M, N, K);
+    if (ws_bytes < need || (need > 0 && !ws)) return fail(SSG_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
+    ssg::SpmmArgs a = make_args(ab, M, N, K, vals, ldv, meta, ldm, B, ldb, C, ldc);
+    a.row_ptr = row_ptr; a.col = col; a.rvals = rvals; a.nnz_r = nnz_r;
+    return run_spmm(algo, a, (hipStream_t)stream);
+}
+
+int ssg_spmm_2to4_residual(int ab, int c, int64_t M, int64_t N, int64_t K, const void* vals, int64_t ldv,
+                           const uint8_t* meta, int64_t ldm, const int32_t* row_ptr, const int32_t* col,
+                           const void* rvals, int64_t nnz_r, const void* B, int64_t ldb, void* C, int64_t ldc,
+                           void* ws, size_t ws_bytes, void* stream) {
+    return ssg_spmm_2to4_residual_ex(SSG_ALGO_AUTO, ab, c, M, N, K, vals, ldv, meta, ldm, row_ptr, col, rvals, nnz_r,
+                                     B, ldb, C, ldc, ws, ws_bytes, stream);
+}
+
+int ssg_spmm_select_algo(int ab, int64_t M, int64_t N, int64_t K, const void* vals, int64_t ldv,
+                         const uint8_t* meta, int64_t ldm, const void* B, int64_t ldb, const void* C, int64_t ldc) {
+    if (!in_dtype(ab) || M <= 0 || N <= 0 || K <= 0 || K % 4) return SSG_ALGO_GENERIC;
+    return pick_algo(make_args(ab, M, N, K, vals, ldv, meta, ldm, B, ldb, const_cast<void*>(C), ldc));
+}
+
+}  // extern "C"

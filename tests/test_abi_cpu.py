@@ -1,0 +1,134 @@
+"""The C ABI library on the CPU: it loads, exports every function the header
+declares, and rejects invalid arguments on the host before any HIP call
+(so these run without a GPU).  No compute call is made here."""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+import structured_sparse_gemm_amd as ssg
+from structured_sparse_gemm_amd import _abi
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ssgemm.h")
+
+FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: every call below fails validation first
+F16, BF16, I8, F32, I32 = 0, 1, 2, 3, 4
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _abi.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ssg_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary_calls():
+    names = declared_functions()
+    for required in ("ssg_compress_2to4", "ssg_prune_2to4", "ssg_decompress_2to4", "ssg_split_count",
+                     "ssg_split_fill", "ssg_spmm_2to4", "ssg_spmm_2to4_residual", "ssg_spmm_workspace_bytes",
+                     "ssg_status_str", "ssg_last_error", "ssg_vals_cols", "ssg_meta_cols", "ssg_abi_version"):
+        assert required in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    missing = [n for n in declared_functions() if not hasattr(lib, n)]
+    assert not missing
+    # and the ctypes signature table covers them all
+    assert set(declared_functions()) == set(_abi.SIGNATURES)
+
+
+def test_version_and_sizes(lib):
+    assert lib.ssg_abi_version() == 1
+    for K, v, m in [(0, 0, 0), (4, 2, 1), (8, 4, 1), (12, 6, 2), (4096, 2048, 512), (8196, 4098, 1025)]:
+        assert lib.ssg_vals_cols(K) == v and lib.ssg_meta_cols(K) == m
+    for s in range(9):
+        assert lib.ssg_status_str(s).decode().startswith("SSG_")
+    assert lib.ssg_spmm_workspace_bytes(F16, 11008, 16, 4096) >= 0
+
+
+def _status(rc):
+    return rc
+
+
+def test_dense_argument_errors(lib):
+    # bad dtype / shape / stride / null, all caught on the host
+    assert lib.ssg_compress_2to4(F32, 4, 8, FAKE, 8, FAKE, 4, FAKE, 1, None) == _abi.SSG_ERR_DTYPE
+    assert lib.ssg_compress_2to4(F16, 4, 6, FAKE, 8, FAKE, 4, FAKE, 1, None) == _abi.SSG_ERR_SHAPE
+    assert lib.ssg_compress_2to4(F16, -1, 8, FAKE, 8, FAKE, 4, FAKE, 1, None) == _abi.SSG_ERR_SHAPE
+    assert lib.ssg_compress_2to4(F16, 4, 8, FAKE, 7, FAKE, 4, FAKE, 1, None) == _abi.SSG_ERR_STRIDE
+    assert lib.ssg_compress_2to4(F16, 4, 8, FAKE, 8, FAKE, 3, FAKE, 1, None) == _abi.SSG_ERR_STRIDE
+    assert lib.ssg_compress_2to4(F16, 4, 16, FAKE, 16, FAKE, 8, FAKE, 1, None) == _abi.SSG_ERR_STRIDE
+    assert lib.ssg_compress_2to4(I8, 4, 8, None, 8, FAKE, 4, FAKE, 1, None) == _abi.SSG_ERR_NULL
+    assert lib.ssg_compress_2to4(I8, 4, 8, FAKE, 8, FAKE, 4, None, 1, None) == _abi.SSG_ERR_NULL
+    assert "lda" in lib.ssg_last_error().decode() or True
+    assert lib.ssg_prune_2to4(BF16, 2, 8, FAKE, 8, None, 8, None) == _abi.SSG_ERR_NULL
+    assert lib.ssg_prune_2to4(BF16, 2, 8, FAKE, 16, FAKE, 8, None) == _abi.SSG_ERR_STRIDE   # in place needs lda == ldp
+    assert lib.ssg_decompress_2to4(F16, 2, 8, FAKE, 4, FAKE, 1, FAKE, 4, None, None) == _abi.SSG_ERR_STRIDE
+    assert lib.ssg_split_count(F16, 2, 8, FAKE, 8, None, None) == _abi.SSG_ERR_NULL
+    assert lib.ssg_split_fill(F16, 2, 8, FAKE, 8, FAKE, 4, FAKE, 1, FAKE, FAKE, None, None) == _abi.SSG_ERR_NULL
+    # int32 row_ptr cannot count the residual of a huge matrix
+    assert lib.ssg_split_count(F16, 1 << 20, 1 << 14, FAKE, 1 << 14, FAKE, None) == _abi.SSG_ERR_SHAPE
+
+
+def test_last_error_names_the_problem(lib):
+    assert lib.ssg_compress_2to4(F16, 4, 8, FAKE, 7, FAKE, 4, FAKE, 1, None) == _abi.SSG_ERR_STRIDE
+    assert "lda=7" in lib.ssg_last_error().decode()
+
+
+def test_zero_size_is_a_no_op(lib):
+    # M == 0 or K == 0: nothing is enqueued, so this succeeds without a GPU
+    assert lib.ssg_compress_2to4(F16, 0, 8, FAKE, 8, FAKE, 4, FAKE, 1, None) == 0
+    assert lib.ssg_compress_2to4(F16, 5, 0, None, 0, None, 0, None, 0, None) == 0
+    assert lib.ssg_prune_2to4(I8, 0, 8, FAKE, 8, FAKE, 8, None) == 0
+    assert lib.ssg_spmm_2to4(F16, F32, 0, 16, 64, FAKE, 32, FAKE, 8, FAKE, 16, FAKE, 16, None, 0, None) == 0
+    assert lib.ssg_spmm_2to4(F16, F32, 8, 0, 64, FAKE, 32, FAKE, 8, FAKE, 0, FAKE, 0, None, 0, None) == 0
+
+
+def test_spmm_argument_errors(lib):
+    f = lib.ssg_spmm_2to4
+    ok = dict(M=8, N=16, K=64)
+    # (input, output) type pairs
+    for ab, c in [(F16, I32), (I8, F32), (F32, F32), (BF16, 5)]:
+        assert f(ab, c, 8, 16, 64, FAKE, 32, FAKE, 8, FAKE, 16, FAKE, 16, None, 0, None) == _abi.SSG_ERR_DTYPE
+    assert f(F16, F32, 8, 16, 62, FAKE, 31, FAKE, 8, FAKE, 16, FAKE, 16, None, 0, None) == _abi.SSG_ERR_SHAPE
+    assert f(F16, F32, 8, 16, 64, FAKE, 31, FAKE, 8, FAKE, 16, FAKE, 16, None, 0, None) == _abi.SSG_ERR_STRIDE
+    assert f(F16, F32, 8, 16, 64, FAKE, 32, FAKE, 7, FAKE, 16, FAKE, 16, None, 0, None) == _abi.SSG_ERR_STRIDE
+    assert f(F16, F32, 8, 16, 64, FAKE, 32, FAKE, 8, FAKE, 15, FAKE, 16, None, 0, None) == _abi.SSG_ERR_STRIDE
+    assert f(F16, F32, 8, 16, 64, FAKE, 32, FAKE, 8, FAKE, 16, FAKE, 15, None, 0, None) == _abi.SSG_ERR_STRIDE
+    assert f(F16, F32, 8, 16, 64, None, 32, FAKE, 8, FAKE, 16, FAKE, 16, None, 0, None) == _abi.SSG_ERR_NULL
+    assert f(F16, F32, 8, 16, 64, FAKE, 32, FAKE, 8, None, 16, FAKE, 16, None, 0, None) == _abi.SSG_ERR_NULL
+    assert f(F16, F32, 8, 16, 64, FAKE, 32, FAKE, 8, FAKE, 16, None, 16, None, 0, None) == _abi.SSG_ERR_NULL
+    r = lib.ssg_spmm_2to4_residual
+    assert r(F16, F32, 8, 16, 64, FAKE, 32, FAKE, 8, FAKE, FAKE, FAKE, -1, FAKE, 16, FAKE, 16, None, 0,
+             None) == _abi.SSG_ERR_FORMAT
+    assert r(F16, F32, 8, 16, 64, FAKE, 32, FAKE, 8, None, FAKE, FAKE, 4, FAKE, 16, FAKE, 16, None, 0,
+             None) == _abi.SSG_ERR_NULL
+    assert r(F16, F32, 8, 16, 64, FAKE, 32, FAKE, 8, FAKE, None, FAKE, 4, FAKE, 16, FAKE, 16, None, 0,
+             None) == _abi.SSG_ERR_NULL
+    e = lib.ssg_spmm_2to4_ex
+    assert e(99, F16, F32, 8, 16, 64, FAKE, 32, FAKE, 8, FAKE, 16, FAKE, 16, None, 0, None) == _abi.SSG_ERR_ALGO
+    del ok
+
+
+def test_python_binding_has_no_cpu_fallback():
+    A = torch.zeros((4, 8), dtype=torch.float16)
+    with pytest.raises(ssg.SsgError):
+        ssg.compress(A)
+    with pytest.raises(ssg.SsgError):
+        ssg.spmm(torch.zeros((4, 4), dtype=torch.float16), torch.zeros((4, 1), dtype=torch.uint8),
+                 torch.zeros((8, 2), dtype=torch.float16))
+
+
+def test_python_binding_names_match_the_abi():
+    for name in declared_functions():
+        if name in ("ssg_abi_version", "ssg_status_str", "ssg_last_error", "ssg_vals_cols", "ssg_meta_cols",
+                    "ssg_spmm_2to4_ex", "ssg_spmm_2to4_residual_ex"):
+            continue
+        assert hasattr(ssg, name), name

@@ -1,0 +1,318 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle.
+
+* compression, pruning, expansion and the residual split: bit-exact;
+* int8 SpMM: bit-exact (int32 vs int64);
+* fp16/bf16 SpMM: relative Frobenius error <= 1e-3 and, element by element,
+  |C_gpu - C_ref| <= 1e-2 * sum_k |a_mk b_kn|.
+
+Small cases are compared in full; the full-size workloads compare the whole
+compressed operand and a sample of outputs the oracle computes one by one.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import structured_sparse_gemm_amd as ssg
+import workloads as W
+from tests import _util as U
+
+pytestmark = pytest.mark.gpu
+
+DTS = ["f16", "bf16", "i8"]
+FRO_TOL = 1e-3
+ELEM_TOL = 1e-2
+ALGOS = [ssg.SSG_ALGO_GENERIC, ssg.SSG_ALGO_SMALL_N, ssg.SSG_ALGO_LARGE_N]
+
+
+@pytest.fixture(scope="module", autouse=True)
+def device():
+    if not torch.cuda.is_available():
+        pytest.skip("no ROCm device")
+    torch.cuda.init()
+    return torch.device("cuda:0")
+
+
+def to_dev(a_bits: np.ndarray, dt: str) -> torch.Tensor:
+    return W.from_bits(a_bits, dt).cuda()
+
+
+def to_host(t: torch.Tensor) -> np.ndarray:
+    t = t.cpu()
+    if t.dtype in (torch.float16, torch.bfloat16, torch.int8):
+        return W.bits(t)
+    return t.numpy()
+
+
+def check_fp(c_gpu, c_ref, s_ref, what=""):
+    c_gpu = np.asarray(c_gpu, dtype=np.float64)
+    err = np.abs(c_gpu - c_ref)
+    ref_norm = np.linalg.norm(c_ref)
+    fro = np.linalg.norm(c_gpu - c_ref) / ref_norm if ref_norm > 0 else np.linalg.norm(c_gpu - c_ref)
+    assert fro <= FRO_TOL, "%s: relative Frobenius error %.3g" % (what, fro)
+    bad = err > ELEM_TOL * s_ref
+    assert not bad.any(), "%s: %d elements beyond 1e-2*sum|ab| (worst at %s)" % (
+        what, int(bad.sum()), np.unravel_index(np.argmax(err - ELEM_TOL * s_ref), err.shape))
+
+
+def check_product(dt, c_gpu, c_ref, s_ref, what=""):
+    if dt == "i8":
+        assert np.array_equal(np.asarray(c_gpu, dtype=np.int64), c_ref), what
+    else:
+        check_fp(c_gpu, c_ref, s_ref, what)
+
+
+def strided(t: torch.Tensor, extra: int) -> torch.Tensor:
+    """The same values inside a wider buffer (leading dimension > row length)."""
+    if extra == 0:
+        return t
+    buf = torch.zeros((t.shape[0], t.shape[1] + extra), dtype=t.dtype, device=t.device)
+    buf[:, :t.shape[1]] = t
+    return buf[:, :t.shape[1]]
+
+
+# ------------------------------------------------------------------ compression
+
+SHAPES = [(1, 4), (3, 36), (5, 12), (64, 256), (77, 1000), (128, 4096), (33, 8196)]
+
+
+@pytest.mark.parametrize("dt", DTS)
+@pytest.mark.parametrize("fam", ["normal", "ties", "sparse", "extreme"])
+@pytest.mark.parametrize("shape", SHAPES)
+def test_compress_prune_decompress_bitexact(dt, fam, shape):
+    M, K = shape
+    a = U.random_matrix(dt, M, K, fam, seed=M * 131 + K)
+    A = to_dev(a, dt)
+    vals, meta = ssg.compress(A)
+    rv, rm = oracle.compress(dt, a)
+    assert np.array_equal(to_host(vals), rv)
+    assert np.array_equal(to_host(meta), rm)
+    P = ssg.prune(A)
+    assert np.array_equal(to_host(P), oracle.prune(dt, a))
+    D, bad = ssg.decompress(vals, meta, K, count_bad=True)
+    assert bad == 0 and np.array_equal(to_host(D), oracle.prune(dt, a))
+
+
+@pytest.mark.parametrize("dt", DTS)
+@pytest.mark.parametrize("extra,offset", [(1, 0), (8, 0), (0, 1), (5, 3)])
+def test_compress_strided_and_unaligned(dt, extra, offset):
+    M, K = 19, 200
+    a = U.random_matrix(dt, M, K, "normal", seed=extra * 7 + offset)
+    base = torch.zeros((M, K + extra + offset), dtype=W.TORCH_DTYPE[dt], device="cuda")
+    base[:, offset:offset + K] = to_dev(a, dt)
+    A = base[:, offset:offset + K]
+    vb = torch.zeros((M, K // 2 + extra + offset), dtype=A.dtype, device="cuda")
+    mb = torch.zeros((M, (K + 7) // 8 + extra + offset), dtype=torch.uint8, device="cuda")
+    vals, meta = vb[:, offset:offset + K // 2], mb[:, offset:offset + (K + 7) // 8]
+    ssg.ssg_compress_2to4(A, vals, meta)
+    rv, rm = oracle.compress(dt, a)
+    assert np.array_equal(to_host(vals.contiguous()), rv)
+    assert np.array_equal(to_host(meta.contiguous()), rm)
+    P = torch.zeros_like(base)[:, offset:offset + K]
+    ssg.ssg_prune_2to4(A, P)
+    assert np.array_equal(to_host(P.contiguous()), oracle.prune(dt, a))
+    # neighbours of the strided outputs were not touched
+    assert not vb[:, :offset].any() and not vb[:, offset + K // 2:].any()
+    assert not mb[:, :offset].any() and not mb[:, offset + (K + 7) // 8:].any()
+
+
+@pytest.mark.parametrize("dt", DTS)
+def test_prune_in_place(dt):
+    a = U.random_matrix(dt, 40, 128, "ties", seed=3)
+    A = to_dev(a, dt)
+    ssg.ssg_prune_2to4(A, A)
+    assert np.array_equal(to_host(A), oracle.prune(dt, a))
+
+
+@pytest.mark.parametrize("dt", DTS)
+def test_decompress_counts_bad_nibbles(dt):
+    a = U.random_matrix(dt, 6, 64, "normal", seed=5)
+    rv, rm = oracle.compress(dt, a)
+    rm = rm.copy()
+    rm[1, 0] = (rm[1, 0] & 0xF0) | 0x5
+    rm[4, 7] = (rm[4, 7] & 0x0F) | 0x30
+    rm[5, 2] = 0x00                                   # two bad groups
+    D, bad = ssg.decompress(to_dev(rv, dt), torch.from_numpy(rm).cuda(), 64, count_bad=True)
+    ref, rbad = oracle.decompress(dt, rv, rm, 64)
+    assert bad == rbad == 4
+    assert np.array_equal(to_host(D), ref)
+
+
+@pytest.mark.parametrize("dt", DTS)
+@pytest.mark.parametrize("fam", ["normal", "ties", "sparse"])
+@pytest.mark.parametrize("shape", [(1, 4), (7, 44), (64, 256), (50, 1100), (9, 8192)])
+def test_split_bitexact(dt, fam, shape):
+    M, K = shape
+    a = U.random_matrix(dt, M, K, fam, seed=M + 3 * K)
+    vals, meta, row_ptr, col, rvals = ssg.split(to_dev(a, dt))
+    r = oracle.split(dt, a)
+    assert np.array_equal(to_host(vals), r[0]) and np.array_equal(to_host(meta), r[1])
+    assert np.array_equal(row_ptr.cpu().numpy(), r[2])
+    assert np.array_equal(col.cpu().numpy(), r[3])
+    assert np.array_equal(to_host(rvals), r[4])
+
+
+# ------------------------------------------------------------------ products
+
+def run_algo(algo, fn):
+    try:
+        return fn()
+    except ssg.SsgError as e:
+        if e.status == 8:          # SSG_ERR_ALGO: this family does not take the problem
+            pytest.skip("algorithm %s does not take this problem" % ssg.ALGO_NAMES[algo])
+        raise
+
+
+PRODUCT_SHAPES = [(1, 4, 1), (16, 64, 16), (37, 64, 9), (256, 256, 64), (48, 512, 16), (100, 1024, 13),
+                  (130, 4096, 16), (64, 192, 48), (256, 512, 256), (300, 1024, 200)]
+
+
+@pytest.mark.parametrize("algo", ALGOS)
+@pytest.mark.parametrize("dt", DTS)
+@pytest.mark.parametrize("shape", PRODUCT_SHAPES)
+def test_spmm_matches_oracle(algo, dt, shape):
+    M, K, N = shape
+    a = U.random_matrix(dt, M, K, "normal", seed=M + K)
+    b = U.random_matrix(dt, K, N, "normal", seed=N + 17)
+    vals, meta = oracle.compress(dt, a)
+    C = run_algo(algo, lambda: ssg.spmm(to_dev(vals, dt), torch.from_numpy(meta).cuda(), to_dev(b, dt), algo=algo))
+    cref, sref = oracle.spmm(dt, vals, meta, b, K)
+    check_product(dt, C.cpu().numpy(), cref, sref, "spmm %s %s" % (dt, shape))
+
+
+@pytest.mark.parametrize("algo", ALGOS)
+@pytest.mark.parametrize("dt", DTS)
+@pytest.mark.parametrize("shape", [(16, 64, 16), (40, 256, 16), (130, 2048, 16), (64, 128, 40), (200, 512, 256)])
+def test_spmm_residual_matches_oracle(algo, dt, shape):
+    M, K, N = shape
+    a = U.random_matrix(dt, M, K, "sparse", seed=M * K)
+    b = U.random_matrix(dt, K, N, "normal", seed=N)
+    vals, meta, row_ptr, col, rvals = oracle.split(dt, a)
+    dev = lambda x: torch.from_numpy(x).cuda()
+    C = run_algo(algo, lambda: ssg.spmm_residual(to_dev(vals, dt), dev(meta), dev(row_ptr), dev(col),
+                                                 to_dev(rvals, dt) if len(rvals) else torch.empty(0, dtype=W.TORCH_DTYPE[dt], device="cuda"),
+                                                 to_dev(b, dt), algo=algo))
+    cref, sref = oracle.spmm_residual(dt, vals, meta, row_ptr, col, rvals, b, K)
+    check_product(dt, C.cpu().numpy(), cref, sref, "residual %s %s" % (dt, shape))
+
+
+@pytest.mark.parametrize("dt", ["f16", "bf16"])
+def test_identity_B_gives_the_pruned_matrix_exactly(dt):
+    K = 256
+    a = U.random_matrix(dt, 64, K, "normal", seed=9)
+    vals, meta = oracle.compress(dt, a)
+    eye = U.encode(dt, np.eye(K))
+    for algo in ALGOS:
+        try:
+            C = ssg.spmm(to_dev(vals, dt), torch.from_numpy(meta).cuda(), to_dev(eye, dt), algo=algo)
+        except ssg.SsgError as e:
+            assert e.status == 8
+            continue
+        assert np.array_equal(C.cpu().numpy().astype(np.float64), U.to_f64(dt, oracle.prune(dt, a)))
+
+
+@pytest.mark.parametrize("dt", DTS)
+def test_spmm_strided_operands(dt):
+    M, K, N = 50, 512, 24
+    a = U.random_matrix(dt, M, K, "normal", seed=1)
+    b = U.random_matrix(dt, K, N, "normal", seed=2)
+    vals, meta = oracle.compress(dt, a)
+    V = strided(to_dev(vals, dt), 8)
+    Mt = strided(torch.from_numpy(meta).cuda(), 4)
+    B = strided(to_dev(b, dt), 16)
+    cbuf = torch.full((M, N + 8), 7, dtype=torch.int32 if dt == "i8" else torch.float32, device="cuda")
+    C = cbuf[:, :N]
+    ssg.ssg_spmm_2to4(V, Mt, B, C)
+    cref, sref = oracle.spmm(dt, vals, meta, b, K)
+    check_product(dt, C.cpu().numpy(), cref, sref)
+    assert (cbuf[:, N:] == 7).all()
+
+
+def test_k_zero_fills_C():
+    vals = torch.empty((5, 0), dtype=torch.float16, device="cuda")
+    meta = torch.empty((5, 0), dtype=torch.uint8, device="cuda")
+    B = torch.empty((0, 3), dtype=torch.float16, device="cuda")
+    C = torch.full((5, 3), 1.5, dtype=torch.float32, device="cuda")
+    ssg.ssg_spmm_2to4(vals, meta, B, C)
+    assert (C == 0).all()
+
+
+def test_int8_extremes_exact():
+    M, K, N = 64, 2048, 64
+    rng = np.random.default_rng(0)
+    a = rng.choice([-128, 127, -127], size=(M, K)).astype(np.int8)
+    b = rng.choice([-128, 127], size=(K, N)).astype(np.int8)
+    vals, meta = oracle.compress("i8", a)
+    for algo in ALGOS:
+        try:
+            C = ssg.spmm(to_dev(vals, "i8"), torch.from_numpy(meta).cuda(), to_dev(b, "i8"), algo=algo)
+        except ssg.SsgError as e:
+            assert e.status == 8
+            continue
+        cref, _ = oracle.spmm("i8", vals, meta, b, K)
+        assert np.array_equal(C.cpu().numpy().astype(np.int64), cref)
+
+
+@pytest.mark.parametrize("dt", DTS)
+def test_results_are_reproducible(dt):
+    M, K, N = 512, 2048, 16
+    a = U.random_matrix(dt, M, K, "normal", seed=4)
+    b = U.random_matrix(dt, K, N, "normal", seed=5)
+    vals, meta = oracle.compress(dt, a)
+    V, Mt, B = to_dev(vals, dt), torch.from_numpy(meta).cuda(), to_dev(b, dt)
+    c1 = ssg.spmm(V, Mt, B)
+    c2 = ssg.spmm(V, Mt, B)
+    assert torch.equal(c1, c2)
+
+
+# ------------------------------------------------------------------ full-size workloads
+
+def sample_entries(M, N, count, seed):
+    """Sampled (m, n): the four corners, tile edges and a random spread."""
+    rng = np.random.default_rng(seed)
+    ms = [0, M - 1, 0, M - 1] + [min(M - 1, x) for x in (15, 16, 31, 32, 127, 128, 255, 256)]
+    ns = [0, 0, N - 1, N - 1] + [min(N - 1, x) for x in (15, 16, 31, 32, 127, 128, 255, 256)]
+    ms += list(rng.integers(0, M, count))
+    ns += list(rng.integers(0, N, count))
+    return np.array(ms, dtype=np.int64), np.array(ns, dtype=np.int64)
+
+
+MAX_GENERIC_MACS = 1 << 32
+
+
+@pytest.mark.parametrize("key", ["c1", "c2", "c3", "c4", "c5"])
+def test_full_size_workload(key):
+    w = W.WORKLOADS[key]
+    print("full-size workload %s: %s" % (key, w.title), flush=True)
+    a_cpu, b_cpu = W.gen_a(w), W.gen_b(w)
+    a, b = W.bits(a_cpu), W.bits(b_cpu)
+    A, B = a_cpu.cuda(), b_cpu.cuda()
+    if w.residual:
+        vals, meta, row_ptr, col, rvals = ssg.split(A)
+        r = oracle.split(w.dtype, a)
+        assert np.array_equal(to_host(vals), r[0]) and np.array_equal(to_host(meta), r[1])
+        assert np.array_equal(row_ptr.cpu().numpy(), r[2]) and np.array_equal(col.cpu().numpy(), r[3])
+        assert np.array_equal(to_host(rvals), r[4])
+        residual = (r[2], r[3], r[4])
+    else:
+        vals, meta = ssg.compress(A)
+        r = oracle.compress(w.dtype, a)
+        assert np.array_equal(to_host(vals), r[0]) and np.array_equal(to_host(meta), r[1])
+        residual = None
+    del A
+    algo = ssg.ssg_spmm_select_algo(vals, meta, B, torch.empty((1, 1), dtype=torch.float32, device="cuda"))
+    if algo == ssg.SSG_ALGO_GENERIC and w.M * w.N * w.K > MAX_GENERIC_MACS:
+        pytest.skip("no fast kernel selected for %s yet" % key)
+    if residual is None:
+        C = ssg.spmm(vals, meta, B)
+    else:
+        C = ssg.spmm_residual(vals, meta, row_ptr, col, rvals, B)
+    C = C.cpu().numpy()
+    if w.M * w.N <= 1 << 16:
+        cref, sref = (oracle.spmm(w.dtype, r[0], r[1], b, w.K) if residual is None
+                      else oracle.spmm_residual(w.dtype, r[0], r[1], *residual, b, w.K))
+        check_product(w.dtype, C, cref, sref, key)
+    else:
+        ms, ns = sample_entries(w.M, w.N, 3000, seed=w.index)
+        cref, sref = oracle.spmm_entries(w.dtype, r[0], r[1], b, w.K, ms, ns, residual=residual)
+        check_product(w.dtype, C[ms, ns], cref, sref, key)

@@ -112,3 +112,52 @@ def from_bits(a: np.ndarray, dtype: str) -> torch.Tensor:
     if dtype == "i8":
         return torch.from_numpy(a.astype(np.int8, copy=True))
     return torch.from_numpy(a.astype(np.uint16, copy=True).view(np.int16)).view(TORCH_DTYPE[dtype])
+
+
+# ---------------------------------------------------------------- small random families for tests
+
+def store_dtype(dt: str):
+    return np.int8 if dt == "i8" else np.uint16
+
+
+def encode(dt: str, values) -> np.ndarray:
+    """Raw storage (numpy) of float values in dt, rounded to nearest-even."""
+    v = np.asarray(values, dtype=np.float64)
+    if dt == "i8":
+        return v.astype(np.int8)
+    if dt == "f16":
+        return v.astype(np.float16).view(np.uint16)
+    t = torch.from_numpy(v.astype(np.float32)).to(torch.bfloat16)
+    return t.view(torch.int16).numpy().view(np.uint16)
+
+
+def random_matrix(dt: str, M: int, K: int, family: str, seed: int) -> np.ndarray:
+    """Raw storage of a random [M, K] matrix.
+
+    families: "normal" (continuous), "ties" (few distinct magnitudes, zeros and
+    -0), "sparse" (about half the entries +0), "extreme" (int8 -128/127 or
+    large/small fp magnitudes)."""
+    rng = np.random.default_rng(seed)
+    if dt == "i8":
+        if family == "normal":
+            a = rng.integers(-127, 128, size=(M, K))
+        elif family == "ties":
+            a = rng.choice([-2, -1, 0, 1, 2], size=(M, K))
+        elif family == "sparse":
+            a = rng.integers(-127, 128, size=(M, K)) * (rng.random((M, K)) < 0.5)
+        else:
+            a = rng.choice([-128, -127, 127, 0, 1, -1], size=(M, K))
+        return a.astype(np.int8)
+    if family == "normal":
+        v = rng.standard_normal((M, K))
+    elif family == "ties":
+        v = rng.choice([-2.0, -1.0, -0.0, 0.0, 1.0, 2.0], size=(M, K))
+    elif family == "sparse":
+        v = rng.standard_normal((M, K)) * (rng.random((M, K)) < 0.5)
+    else:
+        v = rng.choice([-60000.0, 60000.0, 1e-7, -1e-7, 0.0, -0.0, 1.0], size=(M, K))
+    if dt == "bf16" and family == "extreme":
+        v = rng.choice([-3e38, 3e38, 1e-40, -1e-40, 0.0, -0.0, 1.0], size=(M, K))
+    return encode(dt, v)
+
+
