@@ -1,0 +1,269 @@
+"""Benchmark of the 2:4 SpMM hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+Headline workload: int8 2:4 SpMM with M = K = N = 4096 (A uniform in
+[-127, 127] pruned 2:4 by magnitude, B uniform int8, int32 accumulate).  One
+step is the whole hot path over one batch: prune + compress A on the GPU,
+then C = expand(vals, meta) x B.  `value` is dense-equivalent throughput
+2*M*N*K / step time, inputs resident in HBM before the timed region.
+
+Also printed, in the same JSON line:
+* roofline: the SpMM kernel's own launch duration from HIP events recorded on
+  the stream it runs on; achieved = algorithmic ops (M*N*K: two ops per
+  stored non-zero product) / duration, against the dense int8 MFMA peak;
+  traffic from the committed rocprofv3 counter summary if it was taken on the
+  current kernel source, else null;
+* cpu_baseline: the CPU oracle (plain C, fp64/int64) timed on this host on a
+  bounded sample of rows of the same workload;
+* workloads: kernel time and roofline fraction of the other four shapes
+  (small-N ones rotate >= 1 GiB of operand copies so the 256 MB Infinity Cache
+  cannot serve repeated reads).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK = {  # MI355X published peaks
+    "hbm_GBps": 8000.0,
+    "f16": 2516.6, "bf16": 2516.6, "i8": 5033.2,      # dense MFMA, TFLOP/s or TOPS
+}
+METRIC = "2:4 SpMM dense-equiv TFLOP/s (large N) and compressed-weight HBM GB/s (small N)"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def kernel_source_sha() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "structured_sparse_gemm_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".hip", ".hpp", ".cpp")):
+            with open(os.path.join(csrc, name), "rb") as f:
+                h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_for(workload: str, kernel: str):
+    """HBM bytes per launch from the committed counter summary, or None when
+    the summary is missing or was taken on other kernel sources."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    e = t.get("entries", {}).get("%s/%s" % (workload, kernel))
+    if not e or e.get("kernel_source_sha") != kernel_source_sha():
+        return None
+    return e.get("bytes_per_launch")
+
+
+def cpu_baseline(w, a_cpu, b_cpu, target_s: float):
+    """The oracle on the first R rows of the workload, R sized to about target_s."""
+    import numpy as np
+
+    import oracle
+    import workloads as W
+    a, b = W.bits(a_cpu), W.bits(b_cpu)
+
+    def run(rows):
+        t0 = time.perf_counter()
+        if w.residual:
+            v, m, rp, col, rv = oracle.split(w.dtype, a[:rows])
+            c, _ = oracle.spmm_residual(w.dtype, v, m, rp, col, rv, b, w.K)
+        else:
+            v, m = oracle.compress(w.dtype, a[:rows])
+            c, _ = oracle.spmm(w.dtype, v, m, b, w.K)
+        return time.perf_counter() - t0, c
+
+    rows = 8
+    t, _ = run(rows)
+    rows = int(max(8, min(w.M, rows * target_s / max(t, 1e-6))))
+    t, c = run(rows)
+    return {
+        "value": 2.0 * rows * w.N * w.K / t / 1e12,
+        "unit": "TFLOP/s",
+        "cores": oracle.num_threads(),
+        "kind": "oracle",
+        "sample": "first %d of %d rows of A with all of B (%s + product), %.1f s" % (
+            rows, w.M, "split" if w.residual else "prune/compress", t),
+        "seconds": t,
+        "rows": rows,
+    }, (rows, c)
+
+
+def time_kernel(fn, iters: int, stream) -> float:
+    """Average duration (s) of fn() launches, HIP events on `stream`."""
+    import torch
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(iters):
+        fn(i)
+    e1.record(stream)
+    e1.synchronize()
+    return e0.elapsed_time(e1) * 1e-3 / iters
+
+
+def bench_workload(key: str, iters: int):
+    """Kernel-level numbers for one workload (compression outside the timing)."""
+    import numpy as np
+    import torch
+
+    import structured_sparse_gemm_amd as ssg
+    import workloads as W
+    w = W.WORKLOADS[key]
+    a = W.gen_a(w).cuda()
+    b = W.gen_b(w).cuda()
+    ops = ssg.split(a) if w.residual else ssg.compress(a)
+    del a
+    wbytes = sum(t.numel() * t.element_size() for t in ops)
+    copies = 1
+    if w.klass == "small_n":
+        copies = max(1, int(np.ceil((1 << 30) / wbytes)))
+    sets = [ops] + [tuple(t.clone() for t in ops) for _ in range(copies - 1)]
+    out = torch.empty((w.M, w.N), dtype=torch.int32 if w.dtype == "i8" else torch.float32, device="cuda")
+    algo = ssg.ssg_spmm_select_algo(ops[0], ops[1], b, out)
+
+    def launch(i):
+        o = sets[i % copies]
+        if w.residual:
+            ssg.ssg_spmm_2to4_residual(*o, b, out)
+        else:
+            ssg.ssg_spmm_2to4(o[0], o[1], b, out)
+
+    stream = torch.cuda.current_stream()
+    for i in range(max(3, copies)):
+        launch(i)
+    torch.cuda.synchronize()
+    s = time_kernel(launch, iters, stream)
+    flops = 2.0 * w.M * w.N * w.K
+    bbytes = b.numel() * b.element_size()
+    cbytes = out.numel() * out.element_size()
+    r = {"title": w.title, "algo": ssg.ALGO_NAMES[algo], "us_per_launch": s * 1e6,
+         "dense_equiv_TFLOPs": flops / s / 1e12, "compressed_weight_bytes": wbytes,
+         "compressed_weight_GBps": wbytes / s / 1e9, "operand_copies_rotated": copies}
+    if w.klass == "large_n":
+        r["frac_dense_peak"] = flops / s / 1e12 / PEAK[w.dtype]
+        r["frac_sparse_peak"] = r["frac_dense_peak"] / 2
+    else:
+        r["frac_hbm_weights"] = wbytes / s / 1e9 / PEAK["hbm_GBps"]
+        r["frac_hbm_all_bytes"] = (wbytes + bbytes + cbytes) / s / 1e9 / PEAK["hbm_GBps"]
+    del sets, ops, out, b
+    torch.cuda.empty_cache()
+    return r
+
+
+def main() -> int:
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--cpu-seconds", type=float, default=10.0, help="oracle sample size, in seconds of CPU work")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-workloads", action="store_true", help="skip the per-workload table")
+    args = p.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus %d)" % args.gpus,
+              file=sys.stderr)
+        return 2
+
+    import torch
+
+    import structured_sparse_gemm_amd as ssg
+    import workloads as W
+    if not torch.cuda.is_available():
+        print("bench.py needs a ROCm device", file=sys.stderr)
+        return 1
+
+    key = "c2"
+    w = W.WORKLOADS[key]
+    print("bench: %s" % w.title, file=sys.stderr, flush=True)
+    a_cpu, b_cpu = W.gen_a(w), W.gen_b(w)
+    A, B = a_cpu.cuda(), b_cpu.cuda()
+    vals = torch.empty((w.M, w.K // 2), dtype=A.dtype, device="cuda")
+    meta = torch.empty((w.M, (w.K + 7) // 8), dtype=torch.uint8, device="cuda")
+    C = torch.empty((w.M, w.N), dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+
+    def step(e=None):
+        if e: e[0].record(stream)
+        ssg.ssg_compress_2to4(A, vals, meta)
+        if e: e[1].record(stream)
+        ssg.ssg_spmm_2to4(vals, meta, B, C)
+        if e: e[2].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(ev[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms = (t1 - t0) * 1e3 / args.steps
+    spmm_s = sum(e[1].elapsed_time(e[2]) for e in ev) * 1e-3 / args.steps
+    comp_s = sum(e[0].elapsed_time(e[1]) for e in ev) * 1e-3 / args.steps
+    flops = 2.0 * w.M * w.N * w.K
+    algo_ops = float(w.M) * w.N * w.K          # two ops per stored product, half the positions stored
+    print("bench: step %.3f ms (compress %.1f us, spmm %.1f us)" % (ms, comp_s * 1e6, spmm_s * 1e6),
+          file=sys.stderr, flush=True)
+
+    roofline = {
+        "kernel": "spmm_large_n (int8 sparse MFMA 32x32x64)",
+        "bound": "mfma",
+        "achieved": algo_ops / spmm_s / 1e12,
+        "peak": PEAK["i8"],
+        "unit": "TFLOP/s",
+        "frac": algo_ops / spmm_s / 1e12 / PEAK["i8"],
+        "traffic": traffic_for(key, "spmm"),
+        "launch_us": spmm_s * 1e6,
+        "dense_equiv_frac_of_dense_peak": flops / spmm_s / 1e12 / PEAK["i8"],
+        "algorithmic_ops_per_launch": algo_ops,
+    }
+    out = {
+        "metric": METRIC,
+        "value": flops / (ms * 1e-3) / 1e12,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "i8",
+        "data": "synthetic",
+        "config": {"workload": "int8 2:4 SpMM M=K=N=4096; step = prune+compress A, then SpMM (int32 out)",
+                   "M": w.M, "K": w.K, "N": w.N, "seeds": [1000 + w.index, 2000 + w.index]},
+        "spmm_only_dense_equiv_TFLOPs": flops / spmm_s / 1e12,
+        "compress_us": comp_s * 1e6,
+        "roofline": roofline,
+    }
+    if not args.no_cpu_baseline:
+        print("bench: cpu baseline (oracle) ...", file=sys.stderr, flush=True)
+        cb, (rows, cref) = cpu_baseline(w, a_cpu, b_cpu, args.cpu_seconds)
+        import numpy as np
+        cb["sample_matches_gpu"] = bool(np.array_equal(C[:rows].cpu().numpy().astype(np.int64), cref))
+        out["cpu_baseline"] = cb
+    del A, B, vals, meta, C
+    torch.cuda.empty_cache()
+    if not args.no_workloads:
+        table = {}
+        for k in ("c1", "c3", "c4", "c5"):
+            print("bench: workload %s ..." % k, file=sys.stderr, flush=True)
+            table[k] = bench_workload(k, iters=200 if W.WORKLOADS[k].klass != "large_n" else 20)
+        out["workloads"] = table
+    print(json.dumps(out))
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -23,6 +23,7 @@ DTS = ["f16", "bf16", "i8"]
 FRO_TOL = 1e-3
 ELEM_TOL = 1e-2
 ALGOS = [ssg.SSG_ALGO_GENERIC, ssg.SSG_ALGO_SMALL_N, ssg.SSG_ALGO_LARGE_N]
+ALGO_IDS = ["generic", "small_n", "large_n"]
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -167,7 +168,7 @@ PRODUCT_SHAPES = [(1, 4, 1), (16, 64, 16), (37, 64, 9), (256, 256, 64), (48, 512
                   (130, 4096, 16), (64, 192, 48), (256, 512, 256), (300, 1024, 200)]
 
 
-@pytest.mark.parametrize("algo", ALGOS)
+@pytest.mark.parametrize("algo", ALGOS, ids=ALGO_IDS)
 @pytest.mark.parametrize("dt", DTS)
 @pytest.mark.parametrize("shape", PRODUCT_SHAPES)
 def test_spmm_matches_oracle(algo, dt, shape):
@@ -180,7 +181,7 @@ def test_spmm_matches_oracle(algo, dt, shape):
     check_product(dt, C.cpu().numpy(), cref, sref, "spmm %s %s" % (dt, shape))
 
 
-@pytest.mark.parametrize("algo", ALGOS)
+@pytest.mark.parametrize("algo", ALGOS, ids=ALGO_IDS)
 @pytest.mark.parametrize("dt", DTS)
 @pytest.mark.parametrize("shape", [(16, 64, 16), (40, 256, 16), (130, 2048, 16), (64, 128, 40), (200, 512, 256)])
 def test_spmm_residual_matches_oracle(algo, dt, shape):
