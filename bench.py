@@ -83,9 +83,12 @@ def cpu_baseline(w, a_cpu, b_cpu, target_s: float):
         return time.perf_counter() - t0, c
 
     rows = 8
-    t, _ = run(rows)
-    rows = int(max(8, min(w.M, rows * target_s / max(t, 1e-6))))
     t, c = run(rows)
+    # grow the sample until it takes about target_s (the first calls are
+    # dominated by fixed costs such as converting B, so scale in steps)
+    while t < 0.5 * target_s and rows < w.M:
+        rows = int(max(rows + 1, min(w.M, rows * min(8.0, 0.9 * target_s / max(t, 1e-6)))))
+        t, c = run(rows)
     return {
         "value": 2.0 * rows * w.N * w.K / t / 1e12,
         "unit": "TFLOP/s",
