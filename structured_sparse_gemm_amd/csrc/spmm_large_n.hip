@@ -1,28 +1,36 @@
-// spmm_large_n.hip -- 2:4 SpMM for compute-bound shapes (prefill, large N)
-// on gfx950's sparse MFMA.
+// spmm_large_n.hip -- pipelined 2:4 SpMM for compute-bound shapes (prefill,
+// large N) on gfx950's sparse MFMA.
 //
-// What it computes: C = expand(vals, meta) x B, where each stored pair of a
-// group meets the two rows of B its 2-bit positions select ("Chapter 26 --
+// What it computes: C = expand(vals, meta) x B, each stored pair of a group
+// meeting the two rows of B its 2-bit positions select ("Chapter 26 --
 // Sparsity: The Hardware View", section "2:4 Fine-Grained Structured
-// Sparsity"); in the compute-bound regime the sparse matrix units' doubled
-// rate is what pays ("Chapter 26", sections "2:4: ~2x on the Matmul, Less
-// End-to-End" and "2:4 in the Memory-Bound Regime").
+// Sparsity"); in the compute-bound regime the doubled rate of the sparse
+// matrix units is what pays (same chapter, sections "2:4: ~2x on the Matmul,
+// Less End-to-End" and "2:4 in the Memory-Bound Regime").
 //
 // Mapping:
-// * Workgroup tile BM x BN (256 x 256 by default), 4 waves in a 2 x 2
-//   layout, each wave a (BM/2) x (BN/2) block of 32 x 32 sparse MFMA tiles
-//   (v_smfmac_f32_32x32x32_{f16,bf16}: 32 dense k per step;
-//   v_smfmac_i32_32x32x64_i8: 64 dense k per step).
-// * Sparse operand straight from global memory into registers: lane l holds
-//   row l%32's stored values for dense k in [q*EB, (q+1)*EB), q = l/32, which
-//   is one 16-byte load of `vals` plus 2 (16-bit) / 4 (int8) bytes of `meta`
-//   in the stored nibble order.  Prefetched one k-step ahead.
-// * B tile (one k-step x BN) staged through LDS, double-buffered, rows padded
-//   so the transposing reads (ds_read_b64_tr_b16 / _b8) that build the MFMA
-//   operand (consecutive k of one column per lane) hit distinct banks:
-//   pitch = 2*BN + 64 bytes (16-bit), BN + 32 bytes (int8).
-// * One barrier per k-step.  Edges in M and N are masked (zero operands,
-//   masked stores); K must be a multiple of the k-step.
+// * Workgroup tile 256 x 256, 4 waves (one per SIMD) in 2 x 2, each wave a
+//   4 x 4 grid of 32 x 32 sparse MFMA tiles: v_smfmac_f32_32x32x32_{f16,bf16}
+//   (32 dense k) or v_smfmac_i32_32x32x64_i8 (64 dense k); two of them per
+//   k-block (BK = 64 dense k for 16-bit, 128 for int8).
+// * Every operand reaches LDS through direct-to-LDS buffer loads
+//   (buffer_load ... lds): no register staging, and a row or column beyond
+//   the matrix is an out-of-range buffer offset that reads as zero, so edge
+//   tiles need no branches.  Three LDS stages; the loads of k-block i+2 are
+//   issued right after the barrier that opens k-block i, and the wait before
+//   that barrier counts only k-block i's loads.
+// * Sparse values are laid out in MFMA operand order (1 KiB per 32-row x
+//   sub-step fragment: lane l's 16 bytes are row l%32's stored values for
+//   dense k [q*EB, (q+1)*EB), q = l/32 -- one contiguous slice of `vals`);
+//   metadata rows are copied as they are stored and each lane reads its 2
+//   (16-bit) or 4 (int8) bytes.
+// * B rows are stored unpadded with the 16-byte chunks of row r XOR-swizzled
+//   (chunk c at slot c ^ 4*(r%4) for 16-bit, c ^ 2*(r%8) for int8); the
+//   transposing reads (ds_read_b64_tr_b16 / _b8) that build the B operand
+//   then hit 16 distinct 16-byte bank groups per 256 bytes.
+// * Tiles are ordered so each XCD (workgroups are dealt round-robin to the 8
+//   XCDs) gets a contiguous range of tiles, walked 4 row tiles at a time, so
+//   the 32 tiles in flight on an XCD share their A and B panels in its L2.
 #include "ssg_device.hpp"
 #include "ssg_kernels.hpp"
 
@@ -30,32 +38,64 @@ namespace ssg {
 
 namespace {
 
-template <int DT> struct LN;
-template <> struct LN<DT_F16> {
-    static constexpr int KSTEP = 32;       // dense k per MFMA
-    static constexpr int ES = 2;
-    static constexpr int VALS = 16;        // stored values per row per k-step
-    static constexpr int META = 4;         // metadata bytes per row per k-step
-    static constexpr int IDXB = 2;         // metadata bytes per lane
-    static constexpr int PAD = 64;         // LDS row padding (bytes)
+constexpr int kBM = 256, kBN = 256, kStages = 3, kThreads = 256;
+constexpr int kGroupM = 4;             // row tiles walked together per XCD
+constexpr uint32_t kOob = 0x80000000u; // buffer offset that reads as zero
+
+template <int DT> struct PT;
+template <> struct PT<DT_F16> {
+    static constexpr int ES = 2;       // element bytes
+    static constexpr int KSUB = 32;    // dense k per MFMA
+    static constexpr int BK = 64;      // dense k per stage
+    static constexpr int VSUB = 16;    // stored values per row per MFMA k-step
+    static constexpr int MSTAGE = 8;   // metadata bytes per row per stage
+    static constexpr int IDXB = 2;     // metadata bytes per lane per MFMA
+    static constexpr int EPC = 8;      // elements per 16-byte chunk
+    static constexpr int MLOADS = 2;   // metadata load instructions per wave per stage (dword)
+    static constexpr int MSIZE = 4;
 };
-template <> struct LN<DT_BF16> : LN<DT_F16> {};
-template <> struct LN<DT_I8> {
-    static constexpr int KSTEP = 64;
+template <> struct PT<DT_BF16> : PT<DT_F16> {};
+template <> struct PT<DT_I8> {
     static constexpr int ES = 1;
-    static constexpr int VALS = 32;
-    static constexpr int META = 8;
+    static constexpr int KSUB = 64;
+    static constexpr int BK = 128;
+    static constexpr int VSUB = 32;
+    static constexpr int MSTAGE = 16;
     static constexpr int IDXB = 4;
-    static constexpr int PAD = 32;
+    static constexpr int EPC = 16;
+    static constexpr int MLOADS = 1;   // dwordx4
+    static constexpr int MSIZE = 16;
 };
 
-template <int DT> using Acc16 = typename std::conditional<DT == DT_I8, i32x16, f32x16>::type;
+template <int DT>
+struct Lay {
+    using T = PT<DT>;
+    static constexpr int ROWB = kBN * T::ES;               // B tile row bytes
+    static constexpr int CPR = ROWB / 16;                  // 16-byte chunks per row
+    static constexpr int B_BYTES = T::BK * ROWB;           // 32 KiB
+    static constexpr int A_FRAGS = (kBM / 32) * 2;         // 32-row tiles x 2 k-steps
+    static constexpr int A_BYTES = A_FRAGS * 1024;         // 16 KiB
+    static constexpr int M_BYTES = kBM * T::MSTAGE;        // 2 / 4 KiB
+    static constexpr int STAGE = B_BYTES + A_BYTES + M_BYTES;
+    static constexpr int B_LOADS = B_BYTES / 1024 / 4;     // per wave per stage
+    static constexpr int A_LOADS = A_FRAGS / 4;
+    static constexpr int VM_PER_STAGE = B_LOADS + A_LOADS + T::MLOADS;
+    static_assert(kStages * STAGE <= 160 * 1024, "LDS");
+};
 
+template <int DT> __device__ __forceinline__ int swz(int r) {
+    if constexpr (DT == DT_I8) return 2 * (r & 7);
+    else return 4 * (r & 3);
+}
+
+typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
 
+template <int DT> using Acc16 = typename std::conditional<DT == DT_I8, i32x16, f32x16>::type;
+
 template <int DT>
-__device__ __forceinline__ Acc16<DT> smfmac32(uint4 a, const uint4 (&b)[2], Acc16<DT> c, uint32_t idx) {
+__device__ __forceinline__ Acc16<DT> mma(uint4 a, const uint4 (&b)[2], Acc16<DT> c, uint32_t idx) {
     if constexpr (DT == DT_I8) {
         i32x4 av;
         i32x8 bv;
@@ -77,187 +117,215 @@ __device__ __forceinline__ Acc16<DT> smfmac32(uint4 a, const uint4 (&b)[2], Acc1
     }
 }
 
-// MFMA B operand of the 32-column block starting at tile column `cb`
-// (an element index; byte offsets are formed here).
-// Lane l: column cb + l%32, block bb = l/32; element e is dense
-// k = (e / H) * (KSTEP / 2) + H * bb + e % H, H = 8 (16-bit) / 16 (int8).
-// Transposing reads work on 16-lane groups: source lane 4q+r (tr16) or 2q+r
-// (tr8) names a row and 4 / 8 consecutive columns; output lane i receives
-// column i of 4 / 8 consecutive rows.
-template <int DT, int PITCH>
-__device__ __forceinline__ void b_operand(const uint8_t* buf, int cb, int lane, uint4 (&b)[2]) {
+// B operand (32 columns from tile column `cb`, MFMA k-step `s` of the stage)
+// from the swizzled LDS tile.  Lane l: column cb + l%32, block bb = l/32;
+// element e is dense k = (e / H) * (KSUB / 2) + H * bb + e % H within the
+// k-step, H = 8 (16-bit) / 16 (int8).  Transposing reads act on 16-lane
+// groups: source lane 4q+r (tr16) / 2q+r (tr8) names a row and 4 / 8
+// consecutive columns; output lane i gets column i of 4 / 8 consecutive rows.
+template <int DT>
+__device__ __forceinline__ void b_frag(const uint8_t* bt, int s, int cb, int lane, uint4 (&b)[2]) {
+    using L = Lay<DT>;
     const int bb = lane >> 5, h = (lane >> 4) & 1, i = lane & 15;
     if constexpr (DT == DT_I8) {
         const int q = i >> 1, r = i & 1;
-        const uint8_t* p = buf + (16 * bb + q) * PITCH + cb + 16 * h + 8 * r;
-        i32x2 v0 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(p));
-        i32x2 v1 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(p + 8 * PITCH));
-        i32x2 v2 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(p + 32 * PITCH));
-        i32x2 v3 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(p + 40 * PITCH));
-        b[0] = make_uint4(v0[0], v0[1], v1[0], v1[1]);
-        b[1] = make_uint4(v2[0], v2[1], v3[0], v3[1]);
+        const int c = (cb >> 4) + h;                       // 16-byte chunk of the 16 columns
+        i32x2 v[4];
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            const int row = s * 64 + (p >> 1) * 32 + 16 * bb + (p & 1) * 8 + q;
+            v[p] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                (lds_i32x2*)(bt + row * L::ROWB + ((c ^ swz<DT>(row)) << 4) + 8 * r));
+        }
+        b[0] = make_uint4(v[0][0], v[0][1], v[1][0], v[1][1]);
+        b[1] = make_uint4(v[2][0], v[2][1], v[3][0], v[3][1]);
     } else {
         const int q = i >> 2, r = i & 3;
-        const uint8_t* p = buf + (8 * bb + q) * PITCH + 2 * (cb + 16 * h + 4 * r);
-        i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
-        i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p + 4 * PITCH));
-        i16x4 v2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p + 16 * PITCH));
-        i16x4 v3 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p + 20 * PITCH));
-        uint2 w0, w1, w2, w3;
-        __builtin_memcpy(&w0, &v0, 8);
-        __builtin_memcpy(&w1, &v1, 8);
-        __builtin_memcpy(&w2, &v2, 8);
-        __builtin_memcpy(&w3, &v3, 8);
-        b[0] = make_uint4(w0.x, w0.y, w1.x, w1.y);
-        b[1] = make_uint4(w2.x, w2.y, w3.x, w3.y);
+        const int c = (cb >> 3) + 2 * h + (r >> 1);          // 16-byte chunk of the 4 columns
+        uint2 w[4];
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            const int row = s * 32 + (p >> 1) * 16 + 8 * bb + (p & 1) * 4 + q;
+            i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_i16x4*)(bt + row * L::ROWB + ((c ^ swz<DT>(row)) << 4) + 8 * (r & 1)));
+            __builtin_memcpy(&w[p], &v, 8);
+        }
+        b[0] = make_uint4(w[0].x, w[0].y, w[1].x, w[1].y);
+        b[1] = make_uint4(w[2].x, w[2].y, w[3].x, w[3].y);
     }
 }
 
-template <int DT, int BM, int BN>
-struct Cfg {
-    using T = LN<DT>;
-    static constexpr int THREADS = 256;
-    static constexpr int TM = BM / 64, TN = BN / 64;          // 32x32 tiles per wave (2x2 waves)
-    static constexpr int ROWB = BN * T::ES;                   // B tile row bytes
-    static constexpr int PITCH = ROWB + T::PAD;
-    static constexpr int BUF = T::KSTEP * PITCH;              // one LDS buffer
-    static constexpr int CHUNKS = T::KSTEP * ROWB / 16;       // 16-byte pieces per B tile
-    static constexpr int CPT = CHUNKS / THREADS;              // per thread
-    static_assert(CHUNKS % THREADS == 0, "B tile must split evenly");
+struct Ctx {
+    const uint8_t* vbase;   // vals row m0
+    const uint8_t* mbase;   // meta row m0
+    const uint8_t* bbase;   // B column n0
+    int64_t vbytes, mbytes, bbytes;   // bytes from each base to the end of its buffer
+    int64_t vstage, mstage, bstage;   // bytes per stage along K
+    uint32_t boff[8], aoff[4], moff[2];
 };
 
-// Global -> registers: this thread's pieces of the B tile of k-step ks.
-template <int DT, int BM, int BN>
-__device__ __forceinline__ void load_b_tile(const SpmmArgs& a, int64_t n0, int64_t ks, bool vecb,
-                                            uint4 (&r)[Cfg<DT, BM, BN>::CPT]) {
-    using C = Cfg<DT, BM, BN>;
-    using T = LN<DT>;
-    constexpr int PER_ROW = C::ROWB / 16, EPV = 16 / T::ES;
-#pragma unroll
-    for (int j = 0; j < C::CPT; ++j) {
-        const int c = threadIdx.x + j * C::THREADS;
-        const int row = c / PER_ROW, col = (c % PER_ROW) * EPV;
-        const int64_t k = ks * T::KSTEP + row, n = n0 + col;
-        const uint8_t* src = reinterpret_cast<const uint8_t*>(a.B) + (k * a.ldb + n) * T::ES;
-        if (vecb && n + EPV <= a.N) {
-            r[j] = *reinterpret_cast<const uint4*>(src);
-        } else {
-            uint8_t tmp[16];
-#pragma unroll
-            for (int e = 0; e < EPV; ++e) {
-                if constexpr (T::ES == 2) {
-                    const uint16_t v = (n + e < a.N) ? reinterpret_cast<const uint16_t*>(src)[e] : (uint16_t)0;
-                    __builtin_memcpy(tmp + 2 * e, &v, 2);
-                } else {
-                    tmp[e] = (n + e < a.N) ? src[e] : (uint8_t)0;
-                }
-            }
-            __builtin_memcpy(&r[j], tmp, 16);
-        }
-    }
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const uint8_t* base, int64_t remaining) {
+    const int64_t n = remaining < 0 ? 0 : (remaining > 0x7fffffff ? 0x7fffffff : remaining);
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), 0, (int)n, 0x00020000);
 }
 
-template <int DT, int BM, int BN>
-__device__ __forceinline__ void store_b_tile(uint8_t* buf, const uint4 (&r)[Cfg<DT, BM, BN>::CPT]) {
-    using C = Cfg<DT, BM, BN>;
-    constexpr int PER_ROW = C::ROWB / 16;
-#pragma unroll
-    for (int j = 0; j < C::CPT; ++j) {
-        const int c = threadIdx.x + j * C::THREADS;
-        const int row = c / PER_ROW, colb = (c % PER_ROW) * 16;
-        *reinterpret_cast<uint4*>(buf + row * C::PITCH + colb) = r[j];
-    }
+// One direct-to-LDS load: each lane's `BYTES` (4 or 16) from the buffer at
+// byte offset `voff` land at LDS address m0 + lane * BYTES.  Issued as inline
+// assembly so the compiler neither tracks these loads nor inserts its own
+// conservative waits for them; the kernel counts them itself (wait_vm).
+template <int BYTES>
+__device__ __forceinline__ void dma(__amdgpu_buffer_rsrc_t r, const uint8_t* lds_dst, uint32_t voff) {
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(const lds_void*)lds_dst);
+    if constexpr (BYTES == 16)
+        asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(m0), "v"(voff), "s"(r)
+                     : "memory");
+    else
+        asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds" ::"s"(m0), "v"(voff), "s"(r)
+                     : "memory");
 }
 
-// Sparse operand of this wave's TM row tiles for k-step ks.
-template <int DT, int TM>
-__device__ __forceinline__ void load_a(const SpmmArgs& a, int64_t row0, int64_t ks, int lane, uint4 (&av)[TM],
-                                       uint32_t (&ix)[TM]) {
-    using T = LN<DT>;
-    const int q = lane >> 5, rl = lane & 31;
-#pragma unroll
-    for (int i = 0; i < TM; ++i) {
-        const int64_t row = row0 + 32 * i + rl;
-        if (row < a.M) {
-            const uint8_t* vp = reinterpret_cast<const uint8_t*>(a.vals) +
-                                (row * a.ldv + ks * T::VALS + q * (T::VALS / 2)) * T::ES;
-            const uint8_t* mp = a.meta + row * a.ldm + ks * T::META + q * T::IDXB;
-            av[i] = *reinterpret_cast<const uint4*>(vp);
-            if constexpr (T::IDXB == 4) ix[i] = *reinterpret_cast<const uint32_t*>(mp);
-            else ix[i] = *reinterpret_cast<const uint16_t*>(mp);
-        } else {
-            av[i] = make_uint4(0, 0, 0, 0);
-            ix[i] = 0x44444444u;
-        }
-    }
+// s_waitcnt vmcnt(N): at most N of this wave's vector-memory operations are
+// still outstanding (they complete in issue order).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    static_assert(N >= 0 && N < 64, "vmcnt");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-template <int DT, int BM, int BN>
-__global__ void __launch_bounds__(256) k_spmm_large_n(SpmmArgs a, int vecb) {
-    using C = Cfg<DT, BM, BN>;
-    using T = LN<DT>;
+// Workgroup barrier that is also a compiler memory barrier; unlike
+// __syncthreads it does not make the compiler drain the direct-to-LDS loads.
+__device__ __forceinline__ void barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+// Issue the direct-to-LDS loads of stage `it` into `st` (this wave's share).
+template <int DT>
+__device__ __forceinline__ void issue(const Ctx& x, uint8_t* st, int64_t it, int wave) {
+    using L = Lay<DT>;
+    using T = PT<DT>;
+    const __amdgpu_buffer_rsrc_t rb = rsrc(x.bbase + it * x.bstage, x.bbytes - it * x.bstage);
+    const __amdgpu_buffer_rsrc_t ra = rsrc(x.vbase + it * x.vstage, x.vbytes - it * x.vstage);
+    const __amdgpu_buffer_rsrc_t rm = rsrc(x.mbase + it * x.mstage, x.mbytes - it * x.mstage);
+#pragma unroll
+    for (int j = 0; j < L::B_LOADS; ++j) dma<16>(rb, st + (wave * L::B_LOADS + j) * 1024, x.boff[j]);
+#pragma unroll
+    for (int j = 0; j < L::A_LOADS; ++j) dma<16>(ra, st + L::B_BYTES + (wave * L::A_LOADS + j) * 1024, x.aoff[j]);
+#pragma unroll
+    for (int j = 0; j < T::MLOADS; ++j)
+        dma<T::MSIZE>(rm, st + L::B_BYTES + L::A_BYTES + (wave * T::MLOADS + j) * 64 * T::MSIZE, x.moff[j]);
+}
+
+template <int DT>
+__global__ void __launch_bounds__(kThreads) k_spmm_pipe(SpmmArgs a, int tiles_m, int tiles_n) {
+    using T = PT<DT>;
+    using L = Lay<DT>;
     using Acc = Acc16<DT>;
     using S = typename std::conditional<DT == DT_I8, int32_t, float>::type;
-    constexpr int TM = C::TM, TN = C::TN;
-    __shared__ __attribute__((aligned(16))) uint8_t lds[2 * C::BUF];
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[kStages * L::STAGE];
 
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wm = wave >> 1, wn = wave & 1;
-    const int64_t m0 = (int64_t)blockIdx.y * BM, n0 = (int64_t)blockIdx.x * BN;
-    const int64_t wrow0 = m0 + wm * (BM / 2);
-    const int wcol0 = wn * (BN / 2);            // column offset inside the tile
-    const int64_t nk = a.K / T::KSTEP;
 
-    Acc acc[TM][TN];
+    // XCD-aware tile order
+    const int tiles = tiles_m * tiles_n;
+    int bid = blockIdx.x;
+    const int per_xcd = tiles / 8;
+    if (bid < per_xcd * 8) bid = (bid & 7) * per_xcd + (bid >> 3);
+    const int group = bid / (kGroupM * tiles_n);
+    const int first_m = group * kGroupM;
+    const int gm = min(kGroupM, tiles_m - first_m);
+    const int in_group = bid - group * kGroupM * tiles_n;
+    const int tm = first_m + in_group % gm, tn = in_group / gm;
+    const int64_t m0 = (int64_t)tm * kBM, n0 = (int64_t)tn * kBN;
+
+    // per-lane load offsets (constant across stages)
+    Ctx x;
+    x.vbase = reinterpret_cast<const uint8_t*>(a.vals) + m0 * a.ldv * T::ES;
+    x.mbase = a.meta + m0 * a.ldm;
+    x.bbase = reinterpret_cast<const uint8_t*>(a.B) + n0 * T::ES;
+    x.vbytes = ((a.M - 1) * a.ldv + a.K / 2 - m0 * a.ldv) * T::ES;
+    x.mbytes = (a.M - 1) * a.ldm + (a.K + 7) / 8 - m0 * a.ldm;
+    x.bbytes = ((a.K - 1) * a.ldb + a.N - n0) * T::ES;
+    x.vstage = (int64_t)(T::BK / 2) * T::ES;
+    x.mstage = T::MSTAGE;
+    x.bstage = (int64_t)T::BK * a.ldb * T::ES;
 #pragma unroll
-    for (int i = 0; i < TM; ++i)
+    for (int j = 0; j < L::B_LOADS; ++j) {
+        const int slot = (wave * L::B_LOADS + j) * 64 + lane;
+        const int r = slot / L::CPR, c = (slot % L::CPR) ^ swz<DT>(r);
+        x.boff[j] = (n0 + (int64_t)c * T::EPC < a.N) ? (uint32_t)((r * a.ldb + c * T::EPC) * T::ES) : kOob;
+    }
 #pragma unroll
-        for (int j = 0; j < TN; ++j)
+    for (int j = 0; j < L::A_LOADS; ++j) {
+        const int f = wave * L::A_LOADS + j, tile = f >> 1, s = f & 1;
+        const int row = 32 * tile + (lane & 31);
+        x.aoff[j] = (m0 + row < a.M)
+                        ? (uint32_t)((row * a.ldv + s * T::VSUB + (lane >> 5) * (T::VSUB / 2)) * T::ES)
+                        : kOob;
+    }
+#pragma unroll
+    for (int j = 0; j < T::MLOADS; ++j) {
+        // 16-bit: dword loads, lane -> row 32*ins + lane/2, dword lane%2
+        // int8:   dwordx4 loads, lane -> row 64*ins + lane
+        const int ins = wave * T::MLOADS + j;
+        const int row = T::MSIZE == 4 ? 32 * ins + (lane >> 1) : 64 * ins + lane;
+        const int col = T::MSIZE == 4 ? 4 * (lane & 1) : 0;
+        x.moff[j] = (m0 + row < a.M) ? (uint32_t)(row * a.ldm + col) : kOob;
+    }
+
+    Acc acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[i][j][e] = S(0);
 
-    uint4 av[TM], av_next[TM];
-    uint32_t ix[TM], ix_next[TM];
-    uint4 breg[C::CPT];
+    const int64_t nit = a.K / T::BK;
+    issue<DT>(x, lds, 0, wave);
+    if (nit > 1) issue<DT>(x, lds + L::STAGE, 1, wave);
 
-    load_a<DT, TM>(a, wrow0, 0, lane, av, ix);
-    load_b_tile<DT, BM, BN>(a, n0, 0, vecb != 0, breg);
-    store_b_tile<DT, BM, BN>(lds, breg);
-    __syncthreads();
-
-    for (int64_t ks = 0; ks < nk; ++ks) {
-        const uint8_t* cur = lds + (ks & 1) * C::BUF;
-        uint8_t* nxt = lds + ((ks + 1) & 1) * C::BUF;
-        const bool more = ks + 1 < nk;
-        if (more) {
-            load_a<DT, TM>(a, wrow0, ks + 1, lane, av_next, ix_next);
-            load_b_tile<DT, BM, BN>(a, n0, ks + 1, vecb != 0, breg);
-        }
+    const int q = lane >> 5, rl = lane & 31;
+    for (int64_t it = 0; it < nit; ++it) {
+        // this stage's loads are done once only the next stage's remain
+        if (it + 1 < nit) wait_vm<L::VM_PER_STAGE>();
+        else wait_vm<0>();
+        barrier();
+        if (it + 2 < nit) issue<DT>(x, lds + ((it + 2) % kStages) * L::STAGE, it + 2, wave);
+        const uint8_t* st = lds + (it % kStages) * L::STAGE;
+        const uint8_t* bt = st;
+        const uint8_t* at = st + L::B_BYTES;
+        const uint8_t* mt = st + L::B_BYTES + L::A_BYTES;
 #pragma unroll
-        for (int j = 0; j < TN; ++j) {
-            uint4 b[2];
-            b_operand<DT, C::PITCH>(cur, wcol0 + 32 * j, lane, b);   // column index (elements)
+        for (int s = 0; s < 2; ++s) {
+            uint4 av[4];
+            uint32_t ix[4];
 #pragma unroll
-            for (int i = 0; i < TM; ++i) acc[i][j] = smfmac32<DT>(av[i], b, acc[i][j], ix[i]);
-        }
-        if (more) store_b_tile<DT, BM, BN>(nxt, breg);
-        __syncthreads();
+            for (int i = 0; i < 4; ++i) {
+                const int tile = wm * 4 + i;
+                av[i] = *reinterpret_cast<const uint4*>(at + (tile * 2 + s) * 1024 + lane * 16);
+                const uint8_t* mp = mt + (32 * tile + rl) * T::MSTAGE + s * (T::MSTAGE / 2) + q * T::IDXB;
+                if constexpr (T::IDXB == 4) ix[i] = *reinterpret_cast<const uint32_t*>(mp);
+                else ix[i] = *reinterpret_cast<const uint16_t*>(mp);
+            }
+            uint4 b[4][2];
 #pragma unroll
-        for (int i = 0; i < TM; ++i) {
-            av[i] = av_next[i];
-            ix[i] = ix_next[i];
+            for (int j = 0; j < 4; ++j) b_frag<DT>(bt, s, wn * 128 + 32 * j, lane, b[j]);
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) acc[i][j] = mma<DT>(av[i], b[j], acc[i][j], ix[i]);
         }
     }
 
     // epilogue: D element e of lane l is row 8*(e/4) + 4*(l/32) + e%4, column l%32
 #pragma unroll
-    for (int i = 0; i < TM; ++i) {
+    for (int i = 0; i < 4; ++i) {
 #pragma unroll
-        for (int j = 0; j < TN; ++j) {
-            const int64_t col = n0 + wcol0 + 32 * j + (lane & 31);
+        for (int j = 0; j < 4; ++j) {
+            const int64_t col = n0 + wn * 128 + 32 * j + rl;
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
-                const int64_t row = wrow0 + 32 * i + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+                const int64_t row = m0 + wm * 128 + 32 * i + 8 * (e >> 2) + 4 * q + (e & 3);
                 if (row < a.M && col < a.N) reinterpret_cast<S*>(a.C)[row * a.ldc + col] = acc[i][j][e];
             }
         }
@@ -265,40 +333,45 @@ __global__ void __launch_bounds__(256) k_spmm_large_n(SpmmArgs a, int vecb) {
 }
 
 template <int DT>
-bool supported_t(const SpmmArgs& a) {
-    using T = LN<DT>;
-    const uintptr_t v = reinterpret_cast<uintptr_t>(a.vals), m = reinterpret_cast<uintptr_t>(a.meta);
-    return a.M > 0 && a.N > 0 && a.K > 0 && a.K % T::KSTEP == 0 && v % 16 == 0 && (a.ldv * T::ES) % 16 == 0 &&
-           m % T::IDXB == 0 && a.ldm % T::IDXB == 0 && (a.M + 255) / 256 <= 65535;
+bool pipe_supported(const SpmmArgs& a) {
+    using T = PT<DT>;
+    const uintptr_t v = reinterpret_cast<uintptr_t>(a.vals), m = reinterpret_cast<uintptr_t>(a.meta),
+                    b = reinterpret_cast<uintptr_t>(a.B);
+    const int64_t tiles = ((a.M + kBM - 1) / kBM) * ((a.N + kBN - 1) / kBN);
+    return a.M > 0 && a.N > 0 && a.K > 0 && a.K % T::BK == 0 && a.N % T::EPC == 0 &&
+           v % 16 == 0 && (a.ldv * T::ES) % 16 == 0 && b % 16 == 0 && (a.ldb * T::ES) % 16 == 0 &&
+           m % T::MSIZE == 0 && a.ldm % T::MSIZE == 0 &&
+           // every buffer addressed with 31-bit offsets
+           ((a.M - 1) * a.ldv + a.K / 2) * T::ES < 0x7fffffff && (a.M - 1) * a.ldm + a.K / 8 < 0x7fffffff &&
+           ((a.K - 1) * a.ldb + a.N) * T::ES < 0x7fffffff && tiles < 0x7fffffff;
 }
 
 template <int DT>
-hipError_t launch_t(const SpmmArgs& a, hipStream_t s) {
-    using T = LN<DT>;
-    constexpr int BM = 256, BN = 256;
-    const uintptr_t bp = reinterpret_cast<uintptr_t>(a.B);
-    const bool vecb = bp % 16 == 0 && (a.ldb * T::ES) % 16 == 0;
-    const dim3 grid((unsigned)((a.N + BN - 1) / BN), (unsigned)((a.M + BM - 1) / BM));
-    hipLaunchKernelGGL((k_spmm_large_n<DT, BM, BN>), grid, dim3(256), 0, s, a, (int)vecb);
+hipError_t pipe_launch(const SpmmArgs& a, hipStream_t s) {
+    const int tm = (int)((a.M + kBM - 1) / kBM), tn = (int)((a.N + kBN - 1) / kBN);
+    hipLaunchKernelGGL(k_spmm_pipe<DT>, dim3((unsigned)(tm * tn)), dim3(kThreads), 0, s, a, tm, tn);
     return hipGetLastError();
 }
 
-}  // namespace
-
-bool supported_large_n(const SpmmArgs& a) {
+bool pipe_ok(const SpmmArgs& a) {
     switch (a.dt) {
-        case DT_F16: return supported_t<DT_F16>(a);
-        case DT_BF16: return supported_t<DT_BF16>(a);
-        case DT_I8: return supported_t<DT_I8>(a);
+        case DT_F16: return pipe_supported<DT_F16>(a);
+        case DT_BF16: return pipe_supported<DT_BF16>(a);
+        case DT_I8: return pipe_supported<DT_I8>(a);
         default: return false;
     }
 }
 
+}  // namespace
+
+bool supported_large_n(const SpmmArgs& a) { return pipe_ok(a) || supported_large_n_basic(a); }
+
 hipError_t launch_spmm_large_n(const SpmmArgs& a, hipStream_t s) {
+    if (!pipe_ok(a)) return launch_spmm_large_n_basic(a, s);
     switch (a.dt) {
-        case DT_F16: return launch_t<DT_F16>(a, s);
-        case DT_BF16: return launch_t<DT_BF16>(a, s);
-        case DT_I8: return launch_t<DT_I8>(a, s);
+        case DT_F16: return pipe_launch<DT_F16>(a, s);
+        case DT_BF16: return pipe_launch<DT_BF16>(a, s);
+        case DT_I8: return pipe_launch<DT_I8>(a, s);
         default: return hipErrorInvalidValue;
     }
 }

@@ -46,7 +46,9 @@ hipError_t launch_residual_add(const SpmmArgs& a, hipStream_t s);
 // (shape, alignment); the launchers assume it does.
 bool supported_small_n(const SpmmArgs& a);
 hipError_t launch_spmm_small_n(const SpmmArgs& a, hipStream_t s);
-bool supported_large_n(const SpmmArgs& a);
+bool supported_large_n(const SpmmArgs& a);          // pipelined kernel or the basic one
 hipError_t launch_spmm_large_n(const SpmmArgs& a, hipStream_t s);
+bool supported_large_n_basic(const SpmmArgs& a);
+hipError_t launch_spmm_large_n_basic(const SpmmArgs& a, hipStream_t s);
 
 }  // namespace ssg
