@@ -39,10 +39,11 @@ namespace ssg {
 
 namespace {
 
-constexpr int kBatch = 4;                 // k-steps per wave per batch
+constexpr int kUnits = 12;                // (tile, k-step) weight fragments per wave per batch
 constexpr int kTMax = 4;                  // 16-row tiles per workgroup
 constexpr int kMaxWaves = 16;
 constexpr int kLdsB = 128 * 1024;         // B chunk
+constexpr int kLdsM = 24 * 1024;         // the slab's metadata rows for one chunk
 constexpr int kLdsRes = kTMax * 16 * 16 * 4;   // residual row sums (fp32/int32)
 
 template <int DT> struct SN;
@@ -153,160 +154,219 @@ __device__ __forceinline__ float res_value(const void* rvals, int64_t j) {
     return elem_to_f32<DT>(reinterpret_cast<const uint16_t*>(rvals)[j]);
 }
 
-// First index in [lo, hi) whose column is >= k (columns ascending).
-__device__ __forceinline__ int64_t lower_bound_col(const int32_t* col, int64_t lo, int64_t hi, int64_t k) {
-    while (lo < hi) {
-        const int64_t mid = (lo + hi) >> 1;
-        if (col[mid] < k) lo = mid + 1;
-        else hi = mid;
-    }
-    return lo;
+typedef __attribute__((address_space(3))) void lds_void;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, int64_t bytes) {
+    const int64_t n = bytes < 0 ? 0 : (bytes > 0x7fffffff ? 0x7fffffff : bytes);
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)n, 0x00020000);
 }
 
-// Residual rows of the slab owned by this wave, for the columns of the
-// current B chunk [kc0, kc1); row sums accumulate into res[row][16].
+// Direct-to-LDS load of BYTES (4 or 16) per lane: lane l's bytes from buffer
+// offset `voff` land at the LDS address of `dst` + l * BYTES; an offset past
+// the buffer reads as zero.  Inline assembly, so the compiler does not track
+// it: the kernel waits for these loads itself (vmcnt) before its barrier.
+template <int BYTES>
+__device__ __forceinline__ void dma(__amdgpu_buffer_rsrc_t r, const uint8_t* dst, uint32_t voff) {
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(const lds_void*)dst);
+    if constexpr (BYTES == 16)
+        asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(m0), "v"(voff), "s"(r)
+                     : "memory");
+    else
+        asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds" ::"s"(m0), "v"(voff), "s"(r)
+                     : "memory");
+}
+
+constexpr uint32_t kOob = 0x80000000u;   // buffer offset that reads as zero
+
+// Residual rows of the slab owned by this wave, restricted to columns of the
+// current B chunk [kc0, kc1).  Columns ascend within a row, so each row keeps
+// a cursor (first entry not yet consumed) across chunks.  Entries are taken
+// 128 at a time (2 per lane, loads in flight together); row sums accumulate
+// into res[row][16] in chunk order.
 template <int DT>
-__device__ __forceinline__ void residual_chunk(const SpmmArgs& a, const uint8_t* ldsb, void* res, int64_t r0,
-                                               int nrows, int64_t kc0, int64_t kc1, bool multi_chunk, int wave,
-                                               int waves, int lane) {
+__device__ __forceinline__ void residual_chunk(const SpmmArgs& a, const uint8_t* ldsb, void* res, int32_t* cursor,
+                                               int64_t r0, int nrows, int64_t kc0, int64_t kc1, bool first_chunk,
+                                               int wave, int waves, int lane) {
     constexpr int ES = SN<DT>::ES;
     using S = typename std::conditional<DT == DT_I8, int32_t, float>::type;
     for (int rl = wave; rl < nrows; rl += waves) {
         const int64_t m = r0 + rl;
-        int64_t lo = max<int64_t>(a.row_ptr[m], 0), hi = min<int64_t>(a.row_ptr[m + 1], a.nnz_r);
-        if (multi_chunk && lo < hi) {
-            const int64_t l2 = lower_bound_col(a.col, lo, hi, kc0);
-            hi = lower_bound_col(a.col, l2, hi, kc1);
-            lo = l2;
-        }
+        const int64_t hi = min<int64_t>(a.row_ptr[m + 1], a.nnz_r);
+        int64_t lo = first_chunk ? max<int64_t>(a.row_ptr[m], 0) : (int64_t)cursor[rl];
         S acc[16];
 #pragma unroll
         for (int n = 0; n < 16; ++n) acc[n] = S(0);
-        for (int64_t j = lo + lane; j < hi; j += 64) {
-            const int64_t c = a.col[j];
-            if (c < kc0 || c >= kc1) continue;
-            const uint8_t* brow = ldsb + (c - kc0) * 16 * ES;
-            if constexpr (DT == DT_I8) {
-                const int32_t rv = reinterpret_cast<const int8_t*>(a.rvals)[j];
-                const uint4 w = *reinterpret_cast<const uint4*>(brow);
-                int8_t bv[16];
-                __builtin_memcpy(bv, &w, 16);
+        while (lo < hi) {
+            int32_t c[2];
+            S v[2];
 #pragma unroll
-                for (int n = 0; n < 16; ++n) acc[n] += rv * (int32_t)bv[n];
-            } else {
-                const float rv = res_value<DT>(a.rvals, j);
-                const uint4 w0 = *reinterpret_cast<const uint4*>(brow);
-                const uint4 w1 = *reinterpret_cast<const uint4*>(brow + 16);
-                uint16_t bv[16];
-                __builtin_memcpy(bv, &w0, 16);
-                __builtin_memcpy(bv + 8, &w1, 16);
-#pragma unroll
-                for (int n = 0; n < 16; ++n) acc[n] = fmaf(rv, elem_to_f32<DT>(bv[n]), acc[n]);
+            for (int u = 0; u < 2; ++u) {
+                const int64_t j = lo + 64 * u + lane;
+                c[u] = j < hi ? a.col[j] : (int32_t)kc1;
+                if constexpr (DT == DT_I8) v[u] = j < hi ? (int32_t)reinterpret_cast<const int8_t*>(a.rvals)[j] : 0;
+                else v[u] = j < hi ? res_value<DT>(a.rvals, j) : 0.0f;
             }
+            int taken = 0;
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const bool in = c[u] >= kc0 && c[u] < kc1;
+                taken += __popcll(__ballot(c[u] < kc1 && lo + 64 * u + lane < hi));
+                if (in) {
+                    const uint8_t* brow = ldsb + (c[u] - kc0) * 16 * ES;
+                    if constexpr (DT == DT_I8) {
+                        const uint4 w = *reinterpret_cast<const uint4*>(brow);
+                        int8_t bv[16];
+                        __builtin_memcpy(bv, &w, 16);
+#pragma unroll
+                        for (int n = 0; n < 16; ++n) acc[n] += v[u] * (int32_t)bv[n];
+                    } else {
+                        const uint4 w0 = *reinterpret_cast<const uint4*>(brow);
+                        const uint4 w1 = *reinterpret_cast<const uint4*>(brow + 16);
+                        uint16_t bv[16];
+                        __builtin_memcpy(bv, &w0, 16);
+                        __builtin_memcpy(bv + 8, &w1, 16);
+#pragma unroll
+                        for (int n = 0; n < 16; ++n) acc[n] = fmaf(v[u], elem_to_f32<DT>(bv[n]), acc[n]);
+                    }
+                }
+            }
+            lo += taken;
+            if (taken < 128) break;     // reached an entry of a later chunk, or the row's end
         }
+        if (lane == 0) cursor[rl] = (int32_t)lo;
         S mine = S(0);
 #pragma unroll
         for (int n = 0; n < 16; ++n) {
-            S v = acc[n];
+            S x = acc[n];
 #pragma unroll
-            for (int d = 32; d >= 1; d >>= 1) v += __shfl_xor(v, d, 64);
-            if (lane == n) mine = v;
+            for (int d = 32; d >= 1; d >>= 1) x += __shfl_xor(x, d, 64);
+            if (lane == n) mine = x;
         }
         if (lane < 16) reinterpret_cast<S*>(res)[rl * 16 + lane] += mine;
     }
 }
 
-template <int DT>
+// TM = 16-row tiles of the slab; each wave takes batches of KB = 12/TM
+// k-steps for all TM tiles (12 fragments in flight per wave).
+template <int DT, int TM>
 __global__ void __launch_bounds__(kMaxWaves * 64) k_spmm_small_n(SpmmArgs a, int rows_per_wg, int chunk_steps,
-                                                                 int vecb) {
+                                                                 int dma_b) {
+    constexpr int kBatch = kUnits / TM;
     using T = SN<DT>;
     using Acc = AccT<DT>;
     using S = typename std::conditional<DT == DT_I8, int32_t, float>::type;
-    __shared__ __attribute__((aligned(16))) uint8_t lds[kLdsB + kLdsRes];
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[kLdsB + kLdsM + kLdsRes + 256];
     uint8_t* ldsb = lds;
-    void* res = lds + kLdsB;
+    uint8_t* ldsm = lds + kLdsB;
+    void* res = lds + kLdsB + kLdsM;
+    int32_t* cursor = reinterpret_cast<int32_t*>(lds + kLdsB + kLdsM + kLdsRes);
 
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, waves = blockDim.x >> 6;
+    const int lane = threadIdx.x & 63, waves = blockDim.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int64_t r0 = (int64_t)blockIdx.x * rows_per_wg;
     const int nrows = (int)min<int64_t>(rows_per_wg, a.M - r0);
     const int tiles = (nrows + 15) >> 4;
     const int64_t ksteps = a.K / T::KS;
     const bool residual = a.row_ptr != nullptr;
-    const bool multi_chunk = ksteps > chunk_steps;
 
     if (residual)
         for (int i = threadIdx.x; i < kTMax * 16 * 16; i += blockDim.x) reinterpret_cast<S*>(res)[i] = S(0);
 
-    Acc acc[kTMax];
+    Acc acc[TM];
 #pragma unroll
-    for (int t = 0; t < kTMax; ++t) acc[t] = Acc{0, 0, 0, 0};
+    for (int t = 0; t < TM; ++t) acc[t] = Acc{0, 0, 0, 0};
 
-    // per-lane operand addresses: row r0 + 16t + lane%16, stored values
-    // [q*VALS/4, (q+1)*VALS/4) of each k-step, q = lane/16
+    // sparse operand of lane l: row r0 + 16t + l%16, stored values
+    // [q*VALS/4, (q+1)*VALS/4) of each k-step, q = l/16
     const int q = lane >> 4, rl = lane & 15;
     const uint8_t* vbase = reinterpret_cast<const uint8_t*>(a.vals) + (r0 + rl) * a.ldv * T::ES + q * 16;
-    const uint8_t* mbase = a.meta + (r0 + rl) * a.ldm + q * (T::META / 4);
-    const int64_t vstep = (int64_t)T::VALS * T::ES;     // bytes of vals per row per k-step
-    const int64_t vtile = 16 * a.ldv * T::ES, mtile = 16 * a.ldm;
+    const int64_t vstep = (int64_t)T::VALS * T::ES;
+    const int64_t vtile = 16 * a.ldv * T::ES;
 
     for (int64_t c0 = 0; c0 < ksteps; c0 += chunk_steps) {
         const int csteps = (int)min<int64_t>(chunk_steps, ksteps - c0);
+        const int mpitch = csteps * T::META;             // metadata bytes per row in this chunk
+        if (c0 > 0) __syncthreads();                      // previous chunk consumed
+
+        // 1. direct-to-LDS: this chunk of B (when it copies in 16-byte
+        //    pieces) and the slab's metadata rows for the chunk
+        if (dma_b) {
+            constexpr int ROWB = 16 * T::ES, PIECES = ROWB / 16;
+            const int rows = csteps * T::KS;
+            const __amdgpu_buffer_rsrc_t rb =
+                rsrc(reinterpret_cast<const uint8_t*>(a.B) + c0 * T::KS * a.ldb * T::ES,
+                     ((a.K - c0 * T::KS - 1) * a.ldb + a.N) * T::ES);
+            for (int ins = wave; ins * 64 < rows * PIECES; ins += waves) {
+                const int p = ins * 64 + lane, row = p / PIECES, piece = p - row * PIECES;
+                const uint32_t off = row < rows ? (uint32_t)(row * a.ldb * T::ES + 16 * piece) : kOob;
+                dma<16>(rb, ldsb + ins * 1024, off);
+            }
+        }
+        {
+            const int words = mpitch / 4;                 // dwords per metadata row
+            const __amdgpu_buffer_rsrc_t rm =
+                rsrc(a.meta + r0 * a.ldm + c0 * T::META, (a.M - r0 - 1) * a.ldm + (a.K + 7) / 8 - c0 * T::META);
+            for (int ins = wave; ins * 64 < nrows * words; ins += waves) {
+                const int p = ins * 64 + lane, row = p / words, w = p - row * words;
+                const uint32_t off = row < nrows ? (uint32_t)(row * a.ldm + 4 * w) : kOob;
+                dma<4>(rm, ldsm + ins * 256, off);
+            }
+        }
+        // 2. B chunks that are not 16 full columns: element-wise staging
+        if (!dma_b) stage_b<DT>(a, ldsb, c0 * T::KS, csteps * T::KS, false);
+
+        // 3. weight batches; the first batch's loads are issued before the
+        //    wait so they stream while B and the metadata land
         bool first = true;
-        for (int kb = wave * kBatch; kb < csteps; kb += waves * kBatch) {
-            uint4 av[kBatch][kTMax];
-            uint32_t ix[kBatch][kTMax];
+        for (int kb = wave * kBatch;; kb += waves * kBatch) {
+            const bool have = kb < csteps;
+            uint4 av[kBatch][TM];
+            if (have) {
 #pragma unroll
-            for (int s = 0; s < kBatch; ++s) {
+                for (int s = 0; s < kBatch; ++s) {
 #pragma unroll
-                for (int t = 0; t < kTMax; ++t) {
-                    const bool ok = t < tiles && 16 * t + rl < nrows && kb + s < csteps;
-                    const int64_t ks = c0 + kb + s;
-                    if (ok) {
-                        av[s][t] = *reinterpret_cast<const uint4*>(vbase + t * vtile + ks * vstep);
-                        if constexpr (DT == DT_I8)
-                            ix[s][t] = *reinterpret_cast<const uint32_t*>(mbase + t * mtile + ks * T::META);
-                        else
-                            ix[s][t] = *reinterpret_cast<const uint16_t*>(mbase + t * mtile + ks * T::META);
-                    } else {
-                        av[s][t] = make_uint4(0, 0, 0, 0);
-                        ix[s][t] = 0x44444444u;     // any valid pairs: the values are zero
+                    for (int t = 0; t < TM; ++t) {
+                        const bool ok = 16 * t + rl < nrows && kb + s < csteps;
+                        av[s][t] = ok ? *reinterpret_cast<const uint4*>(vbase + t * vtile + (c0 + kb + s) * vstep)
+                                      : make_uint4(0, 0, 0, 0);
                     }
                 }
             }
             if (first) {
-                // the first batch's loads are in flight; now stage this chunk of B
-                __syncthreads();
-                stage_b<DT>(a, ldsb, c0 * T::KS, csteps * T::KS, vecb != 0);
+                // this wave's direct-to-LDS loads are done once its vector
+                // memory counter drains; the barrier covers the other waves'
+                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
                 __syncthreads();
                 first = false;
             }
+            if (!have) break;
 #pragma unroll
             for (int s = 0; s < kBatch; ++s) {
                 if (kb + s >= csteps) break;
                 uint4 b[2];
                 load_b_operand<DT>(ldsb, kb + s, lane, b);
 #pragma unroll
-                for (int t = 0; t < kTMax; ++t)
-                    if (t < tiles) acc[t] = smfmac<DT>(av[s][t], b, acc[t], ix[s][t]);
+                for (int t = 0; t < TM; ++t) {
+                    {
+                        const uint8_t* mp = ldsm + (16 * t + rl) * mpitch + (kb + s) * T::META + q * (T::META / 4);
+                        uint32_t ix;
+                        if constexpr (DT == DT_I8) ix = *reinterpret_cast<const uint32_t*>(mp);
+                        else ix = *reinterpret_cast<const uint16_t*>(mp);
+                        acc[t] = smfmac<DT>(av[s][t], b, acc[t], ix);
+                    }
+                }
             }
         }
-        if (first) {
-            // this wave had no k-steps in the chunk: it still joins the barriers
-            __syncthreads();
-            stage_b<DT>(a, ldsb, c0 * T::KS, csteps * T::KS, vecb != 0);
-            __syncthreads();
-        }
         if (residual)
-            residual_chunk<DT>(a, ldsb, res, r0, nrows, c0 * T::KS, (c0 + csteps) * T::KS, multi_chunk, wave, waves,
-                               lane);
-        __syncthreads();   // the chunk is consumed before the next one is staged
+            residual_chunk<DT>(a, ldsb, res, cursor, r0, nrows, c0 * T::KS, (c0 + csteps) * T::KS, c0 == 0, wave,
+                               waves, lane);
     }
+    __syncthreads();
 
     // fixed-order reduction of the waves' partial tiles
     Acc* red = reinterpret_cast<Acc*>(ldsb);
 #pragma unroll
-    for (int t = 0; t < kTMax; ++t)
-        if (t < tiles) red[(wave * kTMax + t) * 64 + lane] = acc[t];
+    for (int t = 0; t < TM; ++t) red[(wave * kTMax + t) * 64 + lane] = acc[t];
     __syncthreads();
     for (int i = threadIdx.x; i < tiles * 256; i += blockDim.x) {
         const int t = i >> 8, ln = (i >> 2) & 63, r = i & 3;
@@ -324,9 +384,11 @@ template <int DT>
 bool supported_t(const SpmmArgs& a) {
     using T = SN<DT>;
     const uintptr_t v = reinterpret_cast<uintptr_t>(a.vals), m = reinterpret_cast<uintptr_t>(a.meta);
-    const int malign = T::META / 4;   // 2 or 4 bytes per lane
+    // vals rows 16-byte aligned; metadata rows 4-byte aligned (dword copies);
+    // every buffer addressed with 31-bit offsets
     return a.N >= 1 && a.N <= 16 && a.K > 0 && a.K % T::KS == 0 && v % 16 == 0 && (a.ldv * T::ES) % 16 == 0 &&
-           m % malign == 0 && a.ldm % malign == 0 && a.M > 0;
+           m % 4 == 0 && a.ldm % 4 == 0 && a.M > 0 && (a.M - 1) * a.ldm + a.K / 8 < 0x7fffffff &&
+           ((a.K - 1) * a.ldb + a.N) * T::ES < 0x7fffffff;
 }
 
 template <int DT>
@@ -339,14 +401,26 @@ hipError_t launch_t(const SpmmArgs& a, hipStream_t s) {
     const int64_t rows_per_wg = (a.M + G - 1) / G;
     G = (a.M + rows_per_wg - 1) / rows_per_wg;
     const int64_t ksteps = a.K / T::KS;
-    const int64_t max_chunk = kLdsB / (16 * T::ES) / T::KS;
-    const int chunk_steps = (int)(ksteps < max_chunk ? ksteps : max_chunk);
-    int waves = (chunk_steps + kBatch - 1) / kBatch;
+    // chunks of K: B rows (16 columns) and the slab's metadata rows must fit
+    // their LDS regions; chunks are made equal
+    int64_t max_steps = kLdsB / (16 * T::ES * T::KS);
+    const int64_t msteps = kLdsM / (rows_per_wg * T::META);
+    if (msteps < max_steps) max_steps = msteps;
+    const int64_t nchunks = (ksteps + max_steps - 1) / max_steps;
+    const int chunk_steps = (int)((ksteps + nchunks - 1) / nchunks);
+    const int tm = (int)((rows_per_wg + 15) / 16);
+    const int kbatch = kUnits / tm;
+    int waves = (chunk_steps + kbatch - 1) / kbatch;
     if (waves > kMaxWaves) waves = kMaxWaves;
     const uintptr_t bp = reinterpret_cast<uintptr_t>(a.B);
-    const bool vecb = a.N == 16 && bp % 16 == 0 && (a.ldb * T::ES) % 16 == 0;
-    hipLaunchKernelGGL(k_spmm_small_n<DT>, dim3((unsigned)G), dim3(64 * waves), 0, s, a, (int)rows_per_wg,
-                       chunk_steps, (int)vecb);
+    const bool dma_b = a.N == 16 && bp % 16 == 0 && (a.ldb * T::ES) % 16 == 0;
+    const dim3 grid((unsigned)G), block(64 * waves);
+    switch (tm) {
+        case 1: hipLaunchKernelGGL((k_spmm_small_n<DT, 1>), grid, block, 0, s, a, (int)rows_per_wg, chunk_steps, (int)dma_b); break;
+        case 2: hipLaunchKernelGGL((k_spmm_small_n<DT, 2>), grid, block, 0, s, a, (int)rows_per_wg, chunk_steps, (int)dma_b); break;
+        case 3: hipLaunchKernelGGL((k_spmm_small_n<DT, 3>), grid, block, 0, s, a, (int)rows_per_wg, chunk_steps, (int)dma_b); break;
+        default: hipLaunchKernelGGL((k_spmm_small_n<DT, 4>), grid, block, 0, s, a, (int)rows_per_wg, chunk_steps, (int)dma_b); break;
+    }
     return hipGetLastError();
 }
 
