@@ -196,6 +196,31 @@ __device__ __forceinline__ void wait_vm() {
 // __syncthreads it does not make the compiler drain the direct-to-LDS loads.
 __device__ __forceinline__ void barrier() { asm volatile("s_barrier" ::: "memory"); }
 
+// Scheduling pattern for a block of NM MFMAs and ND LDS reads: one MFMA,
+// then one or two reads (two for the first ND - NM MFMAs), so the reads of
+// the next k-step are spread over the current one's MFMAs instead of
+// clustering in front of the first use.
+template <int NM, int ND>
+__device__ __forceinline__ void interleave() {
+    if constexpr (NM > 0) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if constexpr (ND > NM) {
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+            interleave<NM - 1, ND - 2>();
+        } else if constexpr (ND > 0) {
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            interleave<NM - 1, ND - 1>();
+        } else {
+            interleave<NM - 1, 0>();
+        }
+    }
+}
+
+// LDS reads of one k-step's operands: 4 sparse fragments + 4 x 4 transposing reads
+constexpr int kOpsReads = 4 + 16;
+// LDS reads of a stage's index words (per row tile: two u16 / one read2)
+template <int DT> constexpr int kIdxReads = DT == DT_I8 ? 4 : 8;
+
 // Issue the direct-to-LDS loads of stage `it` into `st` (this wave's share).
 template <int DT>
 __device__ __forceinline__ void issue(const Ctx& x, uint8_t* st, int64_t it, int wave) {
@@ -281,41 +306,88 @@ __global__ void __launch_bounds__(kThreads) k_spmm_pipe(SpmmArgs a, int tiles_m,
             for (int e = 0; e < 16; ++e) acc[i][j][e] = S(0);
 
     const int64_t nit = a.K / T::BK;
-    issue<DT>(x, lds, 0, wave);
-    if (nit > 1) issue<DT>(x, lds + L::STAGE, 1, wave);
-
     const int q = lane >> 5, rl = lane & 31;
-    for (int64_t it = 0; it < nit; ++it) {
-        // this stage's loads are done once only the next stage's remain
-        if (it + 1 < nit) wait_vm<L::VM_PER_STAGE>();
-        else wait_vm<0>();
-        barrier();
-        if (it + 2 < nit) issue<DT>(x, lds + ((it + 2) % kStages) * L::STAGE, it + 2, wave);
-        const uint8_t* st = lds + (it % kStages) * L::STAGE;
-        const uint8_t* bt = st;
-        const uint8_t* at = st + L::B_BYTES;
+
+    // Operands of one MFMA k-step (sub-step) from an LDS stage: 4 sparse
+    // fragments of this wave's row tiles and 4 B fragments of its columns.
+    struct Ops {
+        uint4 av[4];
+        uint4 b[4][2];
+    };
+    auto read_ops = [&](const uint8_t* st, int s, Ops& o) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            o.av[i] = *reinterpret_cast<const uint4*>(st + L::B_BYTES + ((wm * 4 + i) * 2 + s) * 1024 + lane * 16);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) b_frag<DT>(st, s, wn * 128 + 32 * j, lane, o.b[j]);
+    };
+    // Index words of both sub-steps of a stage, read so that no per-lane
+    // selection follows the read: 16-bit -- sub-step s, lane half q is the
+    // 16 bits at byte 4s + 2q of the row's 8 (two zero-extending u16 reads);
+    // int8 -- dword 2s + q of the row's 16 bytes (one two-dword read).
+    auto read_idx = [&](const uint8_t* st, uint32_t (&ix)[2][4]) {
         const uint8_t* mt = st + L::B_BYTES + L::A_BYTES;
 #pragma unroll
-        for (int s = 0; s < 2; ++s) {
-            uint4 av[4];
-            uint32_t ix[4];
+        for (int i = 0; i < 4; ++i) {
+            const uint8_t* mp = mt + (32 * (wm * 4 + i) + rl) * T::MSTAGE + q * T::IDXB;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int tile = wm * 4 + i;
-                av[i] = *reinterpret_cast<const uint4*>(at + (tile * 2 + s) * 1024 + lane * 16);
-                const uint8_t* mp = mt + (32 * tile + rl) * T::MSTAGE + s * (T::MSTAGE / 2) + q * T::IDXB;
-                if constexpr (T::IDXB == 4) ix[i] = *reinterpret_cast<const uint32_t*>(mp);
-                else ix[i] = *reinterpret_cast<const uint16_t*>(mp);
+            for (int s = 0; s < 2; ++s) {
+                if constexpr (T::IDXB == 4) ix[s][i] = *reinterpret_cast<const uint32_t*>(mp + 8 * s);
+                else ix[s][i] = *reinterpret_cast<const uint16_t*>(mp + 4 * s);
             }
-            uint4 b[4][2];
+        }
+    };
+    auto mmas = [&](const Ops& o, const uint32_t (&ix)[4]) {
 #pragma unroll
-            for (int j = 0; j < 4; ++j) b_frag<DT>(bt, s, wn * 128 + 32 * j, lane, b[j]);
+        for (int j = 0; j < 4; ++j)
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
+            for (int i = 0; i < 4; ++i) acc[i][j] = mma<DT>(o.av[i], o.b[j], acc[i][j], ix[i]);
+    };
+
+    // Pipeline: DMA stages run two ahead of the stage being multiplied; the
+    // LDS reads of the next sub-step are in flight while the current one's
+    // MFMAs execute.  The loop has no branches: a stage past the end of K is
+    // a load with an empty buffer range, which writes zeros to a slot that is
+    // never multiplied.
+    issue<DT>(x, lds, 0, wave);
+    issue<DT>(x, lds + L::STAGE, 1, wave);
+    wait_vm<L::VM_PER_STAGE>();
+    barrier();
+    issue<DT>(x, lds + 2 * L::STAGE, 2, wave);
+
+    Ops o0, o1;
+    uint32_t ix[2][4];
+    read_idx(lds, ix);
+    read_ops(lds, 0, o0);
+    int slot = 0;
+    for (int64_t it = 0; it < nit; ++it) {
+        const uint8_t* st = lds + slot * L::STAGE;
+        read_ops(st, 1, o1);
+        mmas(o0, ix[0]);
+        interleave<16, kOpsReads>();
+        // stage it+1 has landed once only stage it+2's loads remain; this
+        // wave's reads of stage it are done (s_waitcnt lgkmcnt(0), through the
+        // builtin so the compiler knows they have landed) before the barrier
+        // lets stage it+3's loads overwrite its slot
+        wait_vm<L::VM_PER_STAGE>();
+        __builtin_amdgcn_s_waitcnt(0xC07F);
+        barrier();
+        issue<DT>(x, lds + slot * L::STAGE, it + 3, wave);
+        slot = slot == kStages - 1 ? 0 : slot + 1;
+        const uint8_t* nx = lds + slot * L::STAGE;
+        uint32_t ixn[2][4];
+        read_idx(nx, ixn);
+        read_ops(nx, 0, o0);
+        mmas(o1, ix[1]);
+        interleave<16, kOpsReads + kIdxReads<DT>>();
 #pragma unroll
-                for (int i = 0; i < 4; ++i) acc[i][j] = mma<DT>(av[i], b[j], acc[i][j], ix[i]);
+        for (int i = 0; i < 4; ++i) {
+            ix[0][i] = ixn[0][i];
+            ix[1][i] = ixn[1][i];
         }
     }
+    // the zero-filling loads of the stages past K land before the LDS is released
+    wait_vm<0>();
 
     // epilogue: D element e of lane l is row 8*(e/4) + 4*(l/32) + e%4, column l%32
 #pragma unroll
