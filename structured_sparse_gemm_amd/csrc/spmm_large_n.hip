@@ -19,11 +19,13 @@
 //   tiles need no branches.  Three LDS stages; the loads of k-block i+2 are
 //   issued right after the barrier that opens k-block i, and the wait before
 //   that barrier counts only k-block i's loads.
-// * Sparse values are laid out in MFMA operand order (1 KiB per 32-row x
-//   sub-step fragment: lane l's 16 bytes are row l%32's stored values for
-//   dense k [q*EB, (q+1)*EB), q = l/32 -- one contiguous slice of `vals`);
-//   metadata rows are copied as they are stored and each lane reads its 2
-//   (16-bit) or 4 (int8) bytes.
+// * Loads are shaped for the texture path, whose cost grows with the number
+//   of distinct rows a quarter-wave touches: sparse values arrive 16 rows x
+//   64 bytes per load (each row's stored values of the stage, 16-byte chunks
+//   XOR-swizzled by row so the ds_read_b128 that builds a lane's operand --
+//   row l%32, chunk 2s + l/32 -- is bank-conflict free); metadata arrives in
+//   blocks of 32 bytes per row covering 4 (16-bit) or 2 (int8) stages, two
+//   blocks resident, 8 rows per load.
 // * B rows are stored unpadded with the 16-byte chunks of row r XOR-swizzled
 //   (chunk c at slot c ^ 4*(r%4) for 16-bit, c ^ 2*(r%8) for int8); the
 //   transposing reads (ds_read_b64_tr_b16 / _b8) that build the B operand
@@ -47,24 +49,20 @@ template <> struct PT<DT_F16> {
     static constexpr int ES = 2;       // element bytes
     static constexpr int KSUB = 32;    // dense k per MFMA
     static constexpr int BK = 64;      // dense k per stage
-    static constexpr int VSUB = 16;    // stored values per row per MFMA k-step
     static constexpr int MSTAGE = 8;   // metadata bytes per row per stage
     static constexpr int IDXB = 2;     // metadata bytes per lane per MFMA
     static constexpr int EPC = 8;      // elements per 16-byte chunk
-    static constexpr int MLOADS = 2;   // metadata load instructions per wave per stage (dword)
-    static constexpr int MSIZE = 4;
+    static constexpr int MB = 4;       // stages per 32-byte metadata block
 };
 template <> struct PT<DT_BF16> : PT<DT_F16> {};
 template <> struct PT<DT_I8> {
     static constexpr int ES = 1;
     static constexpr int KSUB = 64;
     static constexpr int BK = 128;
-    static constexpr int VSUB = 32;
     static constexpr int MSTAGE = 16;
     static constexpr int IDXB = 4;
     static constexpr int EPC = 16;
-    static constexpr int MLOADS = 1;   // dwordx4
-    static constexpr int MSIZE = 16;
+    static constexpr int MB = 2;
 };
 
 template <int DT>
@@ -73,15 +71,25 @@ struct Lay {
     static constexpr int ROWB = kBN * T::ES;               // B tile row bytes
     static constexpr int CPR = ROWB / 16;                  // 16-byte chunks per row
     static constexpr int B_BYTES = T::BK * ROWB;           // 32 KiB
-    static constexpr int A_FRAGS = (kBM / 32) * 2;         // 32-row tiles x 2 k-steps
-    static constexpr int A_BYTES = A_FRAGS * 1024;         // 16 KiB
-    static constexpr int M_BYTES = kBM * T::MSTAGE;        // 2 / 4 KiB
-    static constexpr int STAGE = B_BYTES + A_BYTES + M_BYTES;
-    static constexpr int B_LOADS = B_BYTES / 1024 / 4;     // per wave per stage
-    static constexpr int A_LOADS = A_FRAGS / 4;
-    static constexpr int VM_PER_STAGE = B_LOADS + A_LOADS + T::MLOADS;
-    static_assert(kStages * STAGE <= 160 * 1024, "LDS");
+    static constexpr int A_ROWB = T::BK / 2 * T::ES;      // stored bytes per row per stage (64)
+    static constexpr int A_BYTES = kBM * A_ROWB;           // 16 KiB
+    static constexpr int STAGE = B_BYTES + A_BYTES;
+    static constexpr int MBLK_ROWB = T::MB * T::MSTAGE;    // metadata bytes per row per block (32)
+    static constexpr int MBLK = kBM * MBLK_ROWB;           // 8 KiB, two blocks resident
+    static constexpr int LDS = kStages * STAGE + 2 * MBLK;
+    static constexpr int B_LOADS = B_BYTES / 1024 / 4;     // per wave per stage (1 KiB each)
+    static constexpr int A_LOADS = A_BYTES / 1024 / 4;
+    static constexpr int M_LOADS = MBLK / 256 / 4;         // per wave per block (256 B each)
+    static constexpr int VM_PER_STAGE = B_LOADS + A_LOADS;
+    static_assert(A_ROWB == 64 && MBLK_ROWB == 32, "layout");
+    static_assert(LDS <= 160 * 1024, "LDS");
 };
+
+// 16-byte chunk c of row r of the sparse-value tile sits at chunk
+// c ^ swz_a(r) of the row's 64 bytes: the 8 or 16 lanes that a
+// ds_read_b128 serves together (consecutive rows, one chunk) then land on
+// distinct 16-byte bank groups.
+__device__ __forceinline__ int swz_a(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
 
 template <int DT> __device__ __forceinline__ int swz(int r) {
     if constexpr (DT == DT_I8) return 2 * (r & 7);
@@ -160,8 +168,8 @@ struct Ctx {
     const uint8_t* mbase;   // meta row m0
     const uint8_t* bbase;   // B column n0
     int64_t vbytes, mbytes, bbytes;   // bytes from each base to the end of its buffer
-    int64_t vstage, mstage, bstage;   // bytes per stage along K
-    uint32_t boff[8], aoff[4], moff[2];
+    int64_t vstage, bstage;           // bytes per stage along K
+    uint32_t boff[8], aoff[4], moff[8];
 };
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const uint8_t* base, int64_t remaining) {
@@ -216,10 +224,9 @@ __device__ __forceinline__ void interleave() {
     }
 }
 
-// LDS reads of one k-step's operands: 4 sparse fragments + 4 x 4 transposing reads
-constexpr int kOpsReads = 4 + 16;
-// LDS reads of a stage's index words (per row tile: two u16 / one read2)
-template <int DT> constexpr int kIdxReads = DT == DT_I8 ? 4 : 8;
+// LDS reads of one k-step's operands: 4 sparse fragments, 4 x 4 transposing
+// reads of B and 4 index words
+constexpr int kOpsReads = 4 + 16 + 4;
 
 // Issue the direct-to-LDS loads of stage `it` into `st` (this wave's share).
 template <int DT>
@@ -228,14 +235,20 @@ __device__ __forceinline__ void issue(const Ctx& x, uint8_t* st, int64_t it, int
     using T = PT<DT>;
     const __amdgpu_buffer_rsrc_t rb = rsrc(x.bbase + it * x.bstage, x.bbytes - it * x.bstage);
     const __amdgpu_buffer_rsrc_t ra = rsrc(x.vbase + it * x.vstage, x.vbytes - it * x.vstage);
-    const __amdgpu_buffer_rsrc_t rm = rsrc(x.mbase + it * x.mstage, x.mbytes - it * x.mstage);
 #pragma unroll
     for (int j = 0; j < L::B_LOADS; ++j) dma<16>(rb, st + (wave * L::B_LOADS + j) * 1024, x.boff[j]);
 #pragma unroll
     for (int j = 0; j < L::A_LOADS; ++j) dma<16>(ra, st + L::B_BYTES + (wave * L::A_LOADS + j) * 1024, x.aoff[j]);
+}
+
+// Issue the direct-to-LDS loads of metadata block `g` (the 32 bytes of each
+// of the tile's rows that cover stages [g * MB, (g + 1) * MB)) into `mt`.
+template <int DT>
+__device__ __forceinline__ void issue_meta(const Ctx& x, uint8_t* mt, int64_t g, int wave) {
+    using L = Lay<DT>;
+    const __amdgpu_buffer_rsrc_t rm = rsrc(x.mbase + g * L::MBLK_ROWB, x.mbytes - g * L::MBLK_ROWB);
 #pragma unroll
-    for (int j = 0; j < T::MLOADS; ++j)
-        dma<T::MSIZE>(rm, st + L::B_BYTES + L::A_BYTES + (wave * T::MLOADS + j) * 64 * T::MSIZE, x.moff[j]);
+    for (int j = 0; j < L::M_LOADS; ++j) dma<4>(rm, mt + (wave * L::M_LOADS + j) * 256, x.moff[j]);
 }
 
 template <int DT>
@@ -244,7 +257,8 @@ __global__ void __launch_bounds__(kThreads) k_spmm_pipe(SpmmArgs a, int tiles_m,
     using L = Lay<DT>;
     using Acc = Acc16<DT>;
     using S = typename std::conditional<DT == DT_I8, int32_t, float>::type;
-    __shared__ __attribute__((aligned(1024))) uint8_t lds[kStages * L::STAGE];
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[L::LDS];
+    uint8_t* const mlds = lds + kStages * L::STAGE;   // two metadata blocks
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -270,8 +284,7 @@ __global__ void __launch_bounds__(kThreads) k_spmm_pipe(SpmmArgs a, int tiles_m,
     x.vbytes = ((a.M - 1) * a.ldv + a.K / 2 - m0 * a.ldv) * T::ES;
     x.mbytes = (a.M - 1) * a.ldm + (a.K + 7) / 8 - m0 * a.ldm;
     x.bbytes = ((a.K - 1) * a.ldb + a.N - n0) * T::ES;
-    x.vstage = (int64_t)(T::BK / 2) * T::ES;
-    x.mstage = T::MSTAGE;
+    x.vstage = L::A_ROWB;
     x.bstage = (int64_t)T::BK * a.ldb * T::ES;
 #pragma unroll
     for (int j = 0; j < L::B_LOADS; ++j) {
@@ -281,20 +294,16 @@ __global__ void __launch_bounds__(kThreads) k_spmm_pipe(SpmmArgs a, int tiles_m,
     }
 #pragma unroll
     for (int j = 0; j < L::A_LOADS; ++j) {
-        const int f = wave * L::A_LOADS + j, tile = f >> 1, s = f & 1;
-        const int row = 32 * tile + (lane & 31);
-        x.aoff[j] = (m0 + row < a.M)
-                        ? (uint32_t)((row * a.ldv + s * T::VSUB + (lane >> 5) * (T::VSUB / 2)) * T::ES)
-                        : kOob;
+        // 16 rows x 64 bytes per load: lane -> row 16*ins + lane/4, LDS chunk lane%4
+        const int row = 16 * (wave * L::A_LOADS + j) + (lane >> 2);
+        const int c = (lane & 3) ^ swz_a(row);
+        x.aoff[j] = (m0 + row < a.M) ? (uint32_t)(row * a.ldv * T::ES + 16 * c) : kOob;
     }
 #pragma unroll
-    for (int j = 0; j < T::MLOADS; ++j) {
-        // 16-bit: dword loads, lane -> row 32*ins + lane/2, dword lane%2
-        // int8:   dwordx4 loads, lane -> row 64*ins + lane
-        const int ins = wave * T::MLOADS + j;
-        const int row = T::MSIZE == 4 ? 32 * ins + (lane >> 1) : 64 * ins + lane;
-        const int col = T::MSIZE == 4 ? 4 * (lane & 1) : 0;
-        x.moff[j] = (m0 + row < a.M) ? (uint32_t)(row * a.ldm + col) : kOob;
+    for (int j = 0; j < L::M_LOADS; ++j) {
+        // 8 rows x 32 bytes per load: lane -> row 8*ins + lane/8, dword lane%8
+        const int row = 8 * (wave * L::M_LOADS + j) + (lane >> 3);
+        x.moff[j] = (m0 + row < a.M) ? (uint32_t)(row * a.ldm + 4 * (lane & 7)) : kOob;
     }
 
     Acc acc[4][4];
@@ -316,25 +325,26 @@ __global__ void __launch_bounds__(kThreads) k_spmm_pipe(SpmmArgs a, int tiles_m,
     };
     auto read_ops = [&](const uint8_t* st, int s, Ops& o) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            o.av[i] = *reinterpret_cast<const uint4*>(st + L::B_BYTES + ((wm * 4 + i) * 2 + s) * 1024 + lane * 16);
+        for (int i = 0; i < 4; ++i) {
+            const int row = 32 * (wm * 4 + i) + rl;
+            o.av[i] = *reinterpret_cast<const uint4*>(st + L::B_BYTES + row * L::A_ROWB +
+                                                      (((2 * s + q) ^ swz_a(row)) << 4));
+        }
 #pragma unroll
         for (int j = 0; j < 4; ++j) b_frag<DT>(st, s, wn * 128 + 32 * j, lane, o.b[j]);
     };
-    // Index words of both sub-steps of a stage, read so that no per-lane
-    // selection follows the read: 16-bit -- sub-step s, lane half q is the
-    // 16 bits at byte 4s + 2q of the row's 8 (two zero-extending u16 reads);
-    // int8 -- dword 2s + q of the row's 16 bytes (one two-dword read).
-    auto read_idx = [&](const uint8_t* st, uint32_t (&ix)[2][4]) {
-        const uint8_t* mt = st + L::B_BYTES + L::A_BYTES;
+    // Index word of sub-step s of stage t for this lane, read so that no
+    // per-lane selection follows the read: 16-bit -- the 16 bits at byte
+    // 4s + 2q of the row's 8 (a zero-extending u16 read); int8 -- dword
+    // 2s + q of the row's 16.  Stage t's bytes are at (t % MB) * MSTAGE of
+    // each row of metadata block t / MB.
+    auto read_idx = [&](int64_t t, int s, uint32_t (&ix)[4]) {
+        const uint8_t* mt = mlds + ((t / T::MB) & 1) * L::MBLK + (t % T::MB) * T::MSTAGE + s * (T::MSTAGE / 2);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const uint8_t* mp = mt + (32 * (wm * 4 + i) + rl) * T::MSTAGE + q * T::IDXB;
-#pragma unroll
-            for (int s = 0; s < 2; ++s) {
-                if constexpr (T::IDXB == 4) ix[s][i] = *reinterpret_cast<const uint32_t*>(mp + 8 * s);
-                else ix[s][i] = *reinterpret_cast<const uint16_t*>(mp + 4 * s);
-            }
+            const uint8_t* mp = mt + (32 * (wm * 4 + i) + rl) * L::MBLK_ROWB + q * T::IDXB;
+            if constexpr (T::IDXB == 4) ix[i] = *reinterpret_cast<const uint32_t*>(mp);
+            else ix[i] = *reinterpret_cast<const uint16_t*>(mp);
         }
     };
     auto mmas = [&](const Ops& o, const uint32_t (&ix)[4]) {
@@ -349,42 +359,47 @@ __global__ void __launch_bounds__(kThreads) k_spmm_pipe(SpmmArgs a, int tiles_m,
     // MFMAs execute.  The loop has no branches: a stage past the end of K is
     // a load with an empty buffer range, which writes zeros to a slot that is
     // never multiplied.
+    //
+    // Metadata comes in blocks of MB stages, two resident: block g is issued
+    // right after the A/B loads of stage (g - 1) * MB + 2 (the iteration
+    // after every wave's last read of block g - 2, whose buffer it takes) and
+    // is first read MB - 1 iterations later.  The wait of an iteration that
+    // follows such an issue leaves the block's loads outstanding too.
+    issue_meta<DT>(x, mlds, 0, wave);
     issue<DT>(x, lds, 0, wave);
     issue<DT>(x, lds + L::STAGE, 1, wave);
     wait_vm<L::VM_PER_STAGE>();
     barrier();
     issue<DT>(x, lds + 2 * L::STAGE, 2, wave);
+    issue_meta<DT>(x, mlds + L::MBLK, 1, wave);
 
     Ops o0, o1;
-    uint32_t ix[2][4];
-    read_idx(lds, ix);
+    uint32_t ix0[4], ix1[4];
+    read_idx(0, 0, ix0);
     read_ops(lds, 0, o0);
     int slot = 0;
     for (int64_t it = 0; it < nit; ++it) {
         const uint8_t* st = lds + slot * L::STAGE;
         read_ops(st, 1, o1);
-        mmas(o0, ix[0]);
+        read_idx(it, 1, ix1);
+        mmas(o0, ix0);
         interleave<16, kOpsReads>();
         // stage it+1 has landed once only stage it+2's loads remain; this
         // wave's reads of stage it are done (s_waitcnt lgkmcnt(0), through the
         // builtin so the compiler knows they have landed) before the barrier
         // lets stage it+3's loads overwrite its slot
-        wait_vm<L::VM_PER_STAGE>();
+        if (it % T::MB == 0) wait_vm<L::VM_PER_STAGE + L::M_LOADS>();
+        else wait_vm<L::VM_PER_STAGE>();
         __builtin_amdgcn_s_waitcnt(0xC07F);
         barrier();
         issue<DT>(x, lds + slot * L::STAGE, it + 3, wave);
+        if ((it + 1) % T::MB == 0) issue_meta<DT>(x, mlds + (((it + 1) / T::MB + 1) & 1) * L::MBLK, (it + 1) / T::MB + 1, wave);
         slot = slot == kStages - 1 ? 0 : slot + 1;
         const uint8_t* nx = lds + slot * L::STAGE;
-        uint32_t ixn[2][4];
-        read_idx(nx, ixn);
         read_ops(nx, 0, o0);
-        mmas(o1, ix[1]);
-        interleave<16, kOpsReads + kIdxReads<DT>>();
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            ix[0][i] = ixn[0][i];
-            ix[1][i] = ixn[1][i];
-        }
+        read_idx(it + 1, 0, ix0);
+        mmas(o1, ix1);
+        interleave<16, kOpsReads>();
     }
     // the zero-filling loads of the stages past K land before the LDS is released
     wait_vm<0>();
@@ -412,7 +427,7 @@ bool pipe_supported(const SpmmArgs& a) {
     const int64_t tiles = ((a.M + kBM - 1) / kBM) * ((a.N + kBN - 1) / kBN);
     return a.M > 0 && a.N > 0 && a.K > 0 && a.K % T::BK == 0 && a.N % T::EPC == 0 &&
            v % 16 == 0 && (a.ldv * T::ES) % 16 == 0 && b % 16 == 0 && (a.ldb * T::ES) % 16 == 0 &&
-           m % T::MSIZE == 0 && a.ldm % T::MSIZE == 0 &&
+           m % 4 == 0 && a.ldm % 4 == 0 &&
            // every buffer addressed with 31-bit offsets
            ((a.M - 1) * a.ldv + a.K / 2) * T::ES < 0x7fffffff && (a.M - 1) * a.ldm + a.K / 8 < 0x7fffffff &&
            ((a.K - 1) * a.ldb + a.N) * T::ES < 0x7fffffff && tiles < 0x7fffffff;
