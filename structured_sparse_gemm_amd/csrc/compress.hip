@@ -26,6 +26,10 @@ namespace {
 
 constexpr int kChunkGroups = 8;
 constexpr int kChunkElems = 32;
+#ifndef SSG_COMPRESS_BLOCKS
+#define SSG_COMPRESS_BLOCKS 2048
+#endif
+constexpr int64_t kCompressBlocks = SSG_COMPRESS_BLOCKS;   // grid cap of the compress pass
 
 // Raw storage word of one element: uint16_t for fp16/bf16, int8_t for int8.
 template <int DT> struct Store { using T = uint16_t; };
@@ -96,21 +100,47 @@ __device__ __forceinline__ void store_compressed(typename Store<DT>::T* vrow, ui
     }
 }
 
+// Grid-stride loop over chunks with the next chunk's loads in flight while
+// the current one is selected and stored, so reads and writes of the pass
+// overlap instead of running as one load phase followed by one store phase.
 template <int DT>
 __global__ void __launch_bounds__(256) k_compress(int64_t M, int64_t K, const typename Store<DT>::T* __restrict__ A,
                                                   int64_t lda, typename Store<DT>::T* __restrict__ vals, int64_t ldv,
                                                   uint8_t* __restrict__ meta, int64_t ldm, int vec) {
     using T = typename Store<DT>::T;
     const int64_t chunks = (K + kChunkElems - 1) / kChunkElems;
-    const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (t >= M * chunks) return;
-    const int64_t m = t / chunks, c = t - m * chunks;
-    const int ng = (int)min<int64_t>(kChunkGroups, (K - c * kChunkElems) / 4);
-    T x[kChunkElems], v[2 * kChunkGroups];
+    const int64_t total = M * chunks;
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (t >= total) return;
+    int64_t m = t / chunks, c = t - m * chunks;
+    int ng = (int)min<int64_t>(kChunkGroups, (K - c * kChunkElems) / 4);
+    T x[kChunkElems];
     load_chunk<DT>(A + m * lda + c * kChunkElems, ng, vec != 0, x);
-    const uint32_t word = select_chunk<DT>(x, ng, v);
-    store_compressed<DT>(vals + m * ldv + c * 2 * kChunkGroups, meta + m * ldm + c * (kChunkGroups / 2), ng,
-                         vec != 0, v, word);
+    for (;;) {
+        const int64_t tn = t + stride;
+        const bool more = tn < total;
+        int64_t mn = 0, cn = 0;
+        int ngn = 0;
+        T xn[kChunkElems];
+        if (more) {
+            mn = tn / chunks;
+            cn = tn - mn * chunks;
+            ngn = (int)min<int64_t>(kChunkGroups, (K - cn * kChunkElems) / 4);
+            load_chunk<DT>(A + mn * lda + cn * kChunkElems, ngn, vec != 0, xn);
+        }
+        T v[2 * kChunkGroups];
+        const uint32_t word = select_chunk<DT>(x, ng, v);
+        store_compressed<DT>(vals + m * ldv + c * 2 * kChunkGroups, meta + m * ldm + c * (kChunkGroups / 2), ng,
+                             vec != 0, v, word);
+        if (!more) break;
+#pragma unroll
+        for (int i = 0; i < kChunkElems; ++i) x[i] = xn[i];
+        t = tn;
+        m = mn;
+        c = cn;
+        ng = ngn;
+    }
 }
 
 template <int DT>
@@ -362,9 +392,13 @@ hipError_t launch_compress(int dt, int64_t M, int64_t K, const void* A, int64_t 
                            uint8_t* meta, int64_t ldm, bool vec, hipStream_t s) {
     const int64_t threads = M * ((K + kChunkElems - 1) / kChunkElems);
     if (threads == 0) return hipSuccess;
+    // a few chunks per thread: enough waves to cover latency, few enough that
+    // each thread's loop overlaps its next loads with its stores
+    int64_t blocks = blocks_for(threads, 256);
+    if (blocks > kCompressBlocks) blocks = kCompressBlocks;
     SSG_DISPATCH_DT(dt, {
         using T = typename Store<D>::T;
-        hipLaunchKernelGGL(k_compress<D>, dim3(blocks_for(threads, 256)), dim3(256), 0, s, M, K, (const T*)A, lda,
+        hipLaunchKernelGGL(k_compress<D>, dim3((unsigned)blocks), dim3(256), 0, s, M, K, (const T*)A, lda,
                            (T*)vals, ldv, meta, ldm, (int)vec);
     });
     return hipGetLastError();
