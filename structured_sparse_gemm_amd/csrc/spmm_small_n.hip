@@ -39,12 +39,12 @@ namespace ssg {
 
 namespace {
 
-constexpr int kUnits = 12;                // (tile, k-step) weight fragments per wave per batch
 constexpr int kTMax = 4;                  // 16-row tiles per workgroup
-constexpr int kMaxWaves = 16;
-constexpr int kLdsB = 128 * 1024;         // B chunk
-constexpr int kLdsM = 24 * 1024;         // the slab's metadata rows for one chunk
+constexpr int kWaves = 8;
 constexpr int kLdsRes = kTMax * 16 * 16 * 4;   // residual row sums (fp32/int32)
+constexpr int kLdsCursor = 256;                // residual row cursors
+// B chunk followed by the slab's padded metadata rows for the chunk
+constexpr int kLdsData = 160 * 1024 - kLdsRes - kLdsCursor;
 
 template <int DT> struct SN;
 template <> struct SN<DT_F16> {
@@ -154,6 +154,170 @@ __device__ __forceinline__ float res_value(const void* rvals, int64_t j) {
     return elem_to_f32<DT>(reinterpret_cast<const uint16_t*>(rvals)[j]);
 }
 
+template <int CTRL, typename S>
+__device__ __forceinline__ S dpp_xor(S x) {
+    int v;
+    __builtin_memcpy(&v, &x, 4);
+    const int r = __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
+    S y;
+    __builtin_memcpy(&y, &r, 4);
+    return y;
+}
+
+// ds_swizzle in bit-mask mode: lane i reads lane i ^ X within its 32 lanes
+template <int X, typename S>
+__device__ __forceinline__ S swz_xor(S x) {
+    int v;
+    __builtin_memcpy(&v, &x, 4);
+    const int r = __builtin_amdgcn_ds_swizzle(v, 0x1F | (X << 10));
+    S y;
+    __builtin_memcpy(&y, &r, 4);
+    return y;
+}
+
+// Transposing reduction of 16 per-lane column sums over the 64 lanes: at
+// each exchange a lane keeps half of its columns and adds its partner's
+// copy of them, so after 4 exchanges within a row of 16 lanes lane i holds
+// one column, bitrev4(i % 16), and two more fold the four rows.  About 60
+// instructions instead of 16 full-wave reductions; the order of the adds is
+// fixed, so the sum is the same on every run.
+template <typename S>
+__device__ __forceinline__ S transpose_sum16(S (&x)[16], int lane) {
+    const bool b0 = lane & 1, b1 = lane & 2, b2 = lane & 4, b3 = lane & 8;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const S send = b0 ? x[i] : x[i + 8], keep = b0 ? x[i + 8] : x[i];
+        x[i] = keep + dpp_xor<0xB1>(send);   // quad_perm [1,0,3,2]
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const S send = b1 ? x[i] : x[i + 4], keep = b1 ? x[i + 4] : x[i];
+        x[i] = keep + dpp_xor<0x4E>(send);   // quad_perm [2,3,0,1]
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const S send = b2 ? x[i] : x[i + 2], keep = b2 ? x[i + 2] : x[i];
+        x[i] = keep + swz_xor<4>(send);
+    }
+    {
+        const S send = b3 ? x[0] : x[1], keep = b3 ? x[1] : x[0];
+        x[0] = keep + swz_xor<8>(send);
+    }
+    S t = x[0];
+    t += swz_xor<16>(t);
+    t += __shfl_xor(t, 32, 64);
+    return t;
+}
+
+__device__ __forceinline__ int transpose_col(int lane) {
+    return ((lane & 1) << 3) | ((lane & 2) << 1) | ((lane & 4) >> 1) | ((lane & 8) >> 3);
+}
+
+// Residual rows of the slab owned by this wave (rl = wave + W*j), restricted
+// to columns of the current B chunk [kc0, kc1).  Columns ascend within a
+// row, so each row keeps a cursor (first entry not yet consumed) across
+// chunks.  A pass loads the next 64*E entries of every one of the wave's
+// rows at once (one memory round-trip for all of them), then takes each row
+// in turn: the entries of the chunk meet their B row in LDS, the 16 column
+// sums are reduced across the wave and added to res[row][16] in pass order.
+template <int DT, int NRW, int E>
+__device__ __forceinline__ void residual_chunk(const SpmmArgs& a, const uint8_t* ldsb, void* res, int32_t* cursor,
+                                               int64_t r0, int nrows, int64_t kc0, int64_t kc1, bool first_chunk,
+                                               int wave, int waves, int lane) {
+    constexpr int ES = SN<DT>::ES;
+    using S = typename std::conditional<DT == DT_I8, int32_t, float>::type;
+    int64_t lo[NRW], hi[NRW];
+#pragma unroll
+    for (int j = 0; j < NRW; ++j) {
+        const int rl = wave + waves * j;
+        const int64_t m = r0 + rl;
+        lo[j] = hi[j] = 0;
+        if (rl < nrows) {
+            hi[j] = min<int64_t>(a.row_ptr[m + 1], a.nnz_r);
+            lo[j] = first_chunk ? max<int64_t>(a.row_ptr[m], 0) : (int64_t)cursor[rl];
+        }
+    }
+    bool open[NRW];
+#pragma unroll
+    for (int j = 0; j < NRW; ++j) open[j] = lo[j] < hi[j];
+    using Raw = typename std::conditional<DT == DT_I8, int32_t, uint32_t>::type;
+    for (;;) {
+        bool any = false;
+#pragma unroll
+        for (int j = 0; j < NRW; ++j) any |= open[j];
+        if (!any) break;
+        // every load of the pass is issued before any is used; lanes past a
+        // row's end read entry 0 (the CSR is non-empty while a row is open)
+        // and are masked afterwards, so no load sits in a branch
+        int32_t c[NRW][E];
+        Raw vr[NRW][E];
+#pragma unroll
+        for (int j = 0; j < NRW; ++j)
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                const int64_t idx = lo[j] + 64 * e + lane;
+                const bool in = open[j] && idx < hi[j];
+                const int64_t li = in ? idx : 0;
+                const int32_t cc = a.col[li];
+                Raw raw;
+                if constexpr (DT == DT_I8) raw = (int32_t)reinterpret_cast<const int8_t*>(a.rvals)[li];
+                else raw = reinterpret_cast<const uint16_t*>(a.rvals)[li];
+                c[j][e] = in ? cc : (int32_t)kc1;
+                vr[j][e] = in ? raw : Raw(0);
+            }
+#pragma unroll
+        for (int j = 0; j < NRW; ++j) {
+            if (!open[j]) continue;
+            // B rows of the row's entries in this chunk (row 0 for the others,
+            // whose value is zeroed), all reads in flight before the products
+            uint4 w[E][2];
+            S vv[E];
+            int taken = 0;
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                const int64_t idx = lo[j] + 64 * e + lane;
+                taken += __popcll(__ballot(c[j][e] < kc1 && idx < hi[j]));
+                const bool inch = c[j][e] >= kc0 && c[j][e] < kc1;
+                const uint8_t* brow = ldsb + (inch ? (int)(c[j][e] - kc0) : 0) * 16 * ES;
+                w[e][0] = *reinterpret_cast<const uint4*>(brow);
+                if constexpr (ES == 2) w[e][1] = *reinterpret_cast<const uint4*>(brow + 16);
+                if constexpr (DT == DT_I8) vv[e] = inch ? vr[j][e] : 0;
+                else vv[e] = inch ? elem_to_f32<DT>((uint16_t)vr[j][e]) : 0.0f;
+            }
+            S acc[16];
+#pragma unroll
+            for (int n = 0; n < 16; ++n) acc[n] = S(0);
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                if constexpr (DT == DT_I8) {
+                    int8_t bv[16];
+                    __builtin_memcpy(bv, &w[e][0], 16);
+#pragma unroll
+                    for (int n = 0; n < 16; ++n) acc[n] += vv[e] * (int32_t)bv[n];
+                } else {
+                    uint16_t bv[16];
+                    __builtin_memcpy(bv, &w[e][0], 16);
+                    __builtin_memcpy(bv + 8, &w[e][1], 16);
+#pragma unroll
+                    for (int n = 0; n < 16; ++n) acc[n] = fmaf(vv[e], elem_to_f32<DT>(bv[n]), acc[n]);
+                }
+            }
+            const S tot = transpose_sum16<S>(acc, lane);
+            const int rl = wave + waves * j;
+            if (lane < 16) reinterpret_cast<S*>(res)[rl * 16 + transpose_col(lane)] += tot;
+            lo[j] += taken;
+            // a pass that stopped short of 64*E reached a column of a later
+            // chunk or the row's end
+            open[j] = taken == 64 * E && lo[j] < hi[j];
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < NRW; ++j) {
+        const int rl = wave + waves * j;
+        if (rl < nrows && lane == 0) cursor[rl] = (int32_t)lo[j];
+    }
+}
+
 typedef __attribute__((address_space(3))) void lds_void;
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, int64_t bytes) {
@@ -161,13 +325,16 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, int64_t
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)n, 0x00020000);
 }
 
-// Direct-to-LDS load of BYTES (4 or 16) per lane: lane l's bytes from buffer
-// offset `voff` land at the LDS address of `dst` + l * BYTES; an offset past
-// the buffer reads as zero.  Inline assembly, so the compiler does not track
-// it: the kernel waits for these loads itself (vmcnt) before its barrier.
+// Direct-to-LDS load of BYTES (4 or 16) per active lane: lane l's bytes from
+// buffer offset `voff` land at LDS byte address `dst` + l * BYTES (`dst`
+// wave-uniform); an offset past the buffer
+// reads as zero.  Inline assembly, so the compiler does not count it: the
+// kernel waits for these loads itself (vmcnt), and issues them before the
+// weight loads the compiler does count, so the compiler's own waits for
+// those (loads complete in order) also cover them.
 template <int BYTES>
-__device__ __forceinline__ void dma(__amdgpu_buffer_rsrc_t r, const uint8_t* dst, uint32_t voff) {
-    const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(const lds_void*)dst);
+__device__ __forceinline__ void dma(__amdgpu_buffer_rsrc_t r, uint32_t dst, uint32_t voff) {
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane(dst);
     if constexpr (BYTES == 16)
         asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(m0), "v"(voff), "s"(r)
                      : "memory");
@@ -176,98 +343,150 @@ __device__ __forceinline__ void dma(__amdgpu_buffer_rsrc_t r, const uint8_t* dst
                      : "memory");
 }
 
-constexpr uint32_t kOob = 0x80000000u;   // buffer offset that reads as zero
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    static_assert(N >= 0 && N < 64, "vmcnt");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
 
-// Residual rows of the slab owned by this wave, restricted to columns of the
-// current B chunk [kc0, kc1).  Columns ascend within a row, so each row keeps
-// a cursor (first entry not yet consumed) across chunks.  Entries are taken
-// 128 at a time (2 per lane, loads in flight together); row sums accumulate
-// into res[row][16] in chunk order.
+// The chunk's B rows (16 columns, contiguous in memory when ldb == 16) as
+// 1 KiB direct-to-LDS loads, dealt round-robin to the waves.
 template <int DT>
-__device__ __forceinline__ void residual_chunk(const SpmmArgs& a, const uint8_t* ldsb, void* res, int32_t* cursor,
-                                               int64_t r0, int nrows, int64_t kc0, int64_t kc1, bool first_chunk,
-                                               int wave, int waves, int lane) {
+__device__ __forceinline__ void dma_b(const SpmmArgs& a, uint32_t ldsb, int64_t k0, int rows, int wave) {
     constexpr int ES = SN<DT>::ES;
-    using S = typename std::conditional<DT == DT_I8, int32_t, float>::type;
-    for (int rl = wave; rl < nrows; rl += waves) {
-        const int64_t m = r0 + rl;
-        const int64_t hi = min<int64_t>(a.row_ptr[m + 1], a.nnz_r);
-        int64_t lo = first_chunk ? max<int64_t>(a.row_ptr[m], 0) : (int64_t)cursor[rl];
-        S acc[16];
-#pragma unroll
-        for (int n = 0; n < 16; ++n) acc[n] = S(0);
-        while (lo < hi) {
-            int32_t c[2];
-            S v[2];
-#pragma unroll
-            for (int u = 0; u < 2; ++u) {
-                const int64_t j = lo + 64 * u + lane;
-                c[u] = j < hi ? a.col[j] : (int32_t)kc1;
-                if constexpr (DT == DT_I8) v[u] = j < hi ? (int32_t)reinterpret_cast<const int8_t*>(a.rvals)[j] : 0;
-                else v[u] = j < hi ? res_value<DT>(a.rvals, j) : 0.0f;
-            }
-            int taken = 0;
-#pragma unroll
-            for (int u = 0; u < 2; ++u) {
-                const bool in = c[u] >= kc0 && c[u] < kc1;
-                taken += __popcll(__ballot(c[u] < kc1 && lo + 64 * u + lane < hi));
-                if (in) {
-                    const uint8_t* brow = ldsb + (c[u] - kc0) * 16 * ES;
-                    if constexpr (DT == DT_I8) {
-                        const uint4 w = *reinterpret_cast<const uint4*>(brow);
-                        int8_t bv[16];
-                        __builtin_memcpy(bv, &w, 16);
-#pragma unroll
-                        for (int n = 0; n < 16; ++n) acc[n] += v[u] * (int32_t)bv[n];
-                    } else {
-                        const uint4 w0 = *reinterpret_cast<const uint4*>(brow);
-                        const uint4 w1 = *reinterpret_cast<const uint4*>(brow + 16);
-                        uint16_t bv[16];
-                        __builtin_memcpy(bv, &w0, 16);
-                        __builtin_memcpy(bv + 8, &w1, 16);
-#pragma unroll
-                        for (int n = 0; n < 16; ++n) acc[n] = fmaf(v[u], elem_to_f32<DT>(bv[n]), acc[n]);
-                    }
-                }
-            }
-            lo += taken;
-            if (taken < 128) break;     // reached an entry of a later chunk, or the row's end
-        }
-        if (lane == 0) cursor[rl] = (int32_t)lo;
-        S mine = S(0);
-#pragma unroll
-        for (int n = 0; n < 16; ++n) {
-            S x = acc[n];
-#pragma unroll
-            for (int d = 32; d >= 1; d >>= 1) x += __shfl_xor(x, d, 64);
-            if (lane == n) mine = x;
-        }
-        if (lane < 16) reinterpret_cast<S*>(res)[rl * 16 + lane] += mine;
+    const int bytes = rows * 16 * ES;
+    const int64_t avail = (a.K - k0) * 16 * ES;
+    const __amdgpu_buffer_rsrc_t r = rsrc(reinterpret_cast<const uint8_t*>(a.B) + k0 * 16 * ES, avail);
+    const int lane = threadIdx.x & 63;
+    for (int ins = wave; ins * 1024 < bytes; ins += kWaves) dma<16>(r, ldsb + ins * 1024, (uint32_t)(ins * 1024 + lane * 16));
+}
+
+// The slab's metadata for the chunk as 256-byte direct-to-LDS loads, one row
+// segment each (rows padded to `pitch` in LDS); lanes past a row's end are
+// masked off so they write nothing.
+template <int DT>
+__device__ __forceinline__ void dma_meta(const SpmmArgs& a, uint32_t ldsm, int64_t r0, int nrows, int64_t c0,
+                                         int csteps, int pitch, int wave) {
+    constexpr int META = SN<DT>::META;
+    const int rowb = csteps * META, segs = (rowb + 255) / 256;
+    const __amdgpu_buffer_rsrc_t r = rsrc(a.meta + r0 * a.ldm, (a.M - r0 - 1) * a.ldm + (a.K + 7) / 8);
+    const int lane = threadIdx.x & 63;
+    for (int ins = wave; ins < nrows * segs; ins += kWaves) {
+        const int row = ins / segs, seg = ins - row * segs;
+        const int off = 256 * seg + 4 * lane;
+        if (off < rowb) dma<4>(r, ldsm + row * pitch + 256 * seg, (uint32_t)(row * a.ldm + c0 * META + off));
     }
 }
 
-// TM = 16-row tiles of the slab; each wave takes batches of KB = 12/TM
-// k-steps for all TM tiles (12 fragments in flight per wave).
-template <int DT, int TM>
-__global__ void __launch_bounds__(kMaxWaves * 64) k_spmm_small_n(SpmmArgs a, int rows_per_wg, int chunk_steps,
-                                                                 int dma_b) {
-    constexpr int kBatch = kUnits / TM;
+// LDS barrier without the release fence of __syncthreads (which would also
+// wait for this wave's outstanding weight loads): the wave's own LDS
+// accesses are made complete first (lgkmcnt(0)), then the workgroup meets.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    asm volatile("s_barrier" ::: "memory");
+}
+
+// Stage B rows [k0, k0 + rows) as 16-column rows into LDS.  The 16-byte
+// path issues all of a thread's loads before its first LDS write, so the
+// staging costs one memory latency, not one per piece.
+template <int DT>
+__device__ __forceinline__ void stage_b_batched(const SpmmArgs& a, uint8_t* ldsb, int64_t k0, int rows, bool vecb) {
+    constexpr int ES = SN<DT>::ES, ROWB = 16 * ES, PIECES = ROWB / 16, J = 16;
+    if (!vecb) {
+        stage_b<DT>(a, ldsb, k0, rows, false);
+        return;
+    }
+    const uint8_t* src = reinterpret_cast<const uint8_t*>(a.B) + k0 * a.ldb * ES;
+    const int n = rows * PIECES;
+    for (int base = threadIdx.x; base < n; base += J * blockDim.x) {
+        uint4 v[J];
+#pragma unroll
+        for (int j = 0; j < J; ++j) {
+            const int i = base + j * blockDim.x;
+            const int r = i / PIECES, p = i - r * PIECES;
+            v[j] = i < n ? *reinterpret_cast<const uint4*>(src + (int64_t)r * a.ldb * ES + 16 * p) : make_uint4(0, 0, 0, 0);
+        }
+#pragma unroll
+        for (int j = 0; j < J; ++j) {
+            const int i = base + j * blockDim.x;
+            if (i < n) *reinterpret_cast<uint4*>(ldsb + 16 * i) = v[j];
+        }
+    }
+}
+
+// Stage the slab's metadata for k-steps [c0, c0 + csteps) into LDS rows of
+// `pitch` bytes (the chunk's bytes plus 4 of padding, so the 16 lanes that
+// read one column of 16 rows hit different banks).  Batched like B.
+template <int DT>
+__device__ __forceinline__ void stage_meta(const SpmmArgs& a, uint8_t* ldsm, int64_t r0, int nrows, int64_t c0,
+                                           int csteps, int pitch, bool vec) {
+    constexpr int META = SN<DT>::META, J = 16;
+    const int rowb = csteps * META;
+    if (vec) {
+        const int pieces = rowb / 4, n = nrows * pieces;
+        for (int base = threadIdx.x; base < n; base += J * blockDim.x) {
+            uint32_t v[J];
+#pragma unroll
+            for (int j = 0; j < J; ++j) {
+                const int i = base + j * blockDim.x;
+                const int r = i / pieces, p = i - r * pieces;
+                v[j] = i < n ? *reinterpret_cast<const uint32_t*>(a.meta + (r0 + r) * a.ldm + c0 * META + 4 * p) : 0u;
+            }
+#pragma unroll
+            for (int j = 0; j < J; ++j) {
+                const int i = base + j * blockDim.x;
+                const int r = i / pieces, p = i - r * pieces;
+                if (i < n) *reinterpret_cast<uint32_t*>(ldsm + r * pitch + 4 * p) = v[j];
+            }
+        }
+    } else {
+        for (int i = threadIdx.x; i < nrows * rowb; i += blockDim.x) {
+            const int r = i / rowb, p = i - r * rowb;
+            ldsm[r * pitch + p] = a.meta[(r0 + r) * a.ldm + c0 * META + p];
+        }
+    }
+}
+
+// One workgroup owns a slab of <= 16*TM rows and all of K.  Wave w takes the
+// k-steps w, w + W, w + 2W, ... (W waves), so the waves walk K together and
+// share each B chunk.  A wave keeps the sparse fragments of its next P
+// k-steps in flight in a register ring and refills a slot as soon as the
+// slot's k-step has been multiplied: the weight stream of every CU stays
+// P x TM KiB per wave deep from the first cycle to the last.
+template <int DT, int TM, int P>
+__global__ void __launch_bounds__(kWaves * 64) k_spmm_small_n(SpmmArgs a, int rows_per_wg, int chunk_steps,
+                                                              int vec_b, int vec_m) {
+    constexpr int W = kWaves;
+    constexpr int kResRows = (16 * TM + W - 1) / W;   // residual rows per wave (dealt round-robin)
     using T = SN<DT>;
     using Acc = AccT<DT>;
     using S = typename std::conditional<DT == DT_I8, int32_t, float>::type;
-    __shared__ __attribute__((aligned(1024))) uint8_t lds[kLdsB + kLdsM + kLdsRes + 256];
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[kLdsData + kLdsRes + kLdsCursor];
     uint8_t* ldsb = lds;
-    uint8_t* ldsm = lds + kLdsB;
-    void* res = lds + kLdsB + kLdsM;
-    int32_t* cursor = reinterpret_cast<int32_t*>(lds + kLdsB + kLdsM + kLdsRes);
+    uint8_t* ldsm = lds + chunk_steps * 16 * T::ES * T::KS;
+    void* res = lds + kLdsData;
+    int32_t* cursor = reinterpret_cast<int32_t*>(lds + kLdsData + kLdsRes);
+    const uint32_t lds_addr = (uint32_t)(uintptr_t)(const lds_void*)lds;   // LDS byte address of `lds`
 
-    const int lane = threadIdx.x & 63, waves = blockDim.x >> 6;
+    const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int64_t r0 = (int64_t)blockIdx.x * rows_per_wg;
     const int nrows = (int)min<int64_t>(rows_per_wg, a.M - r0);
-    const int tiles = (nrows + 15) >> 4;
     const int64_t ksteps = a.K / T::KS;
     const bool residual = a.row_ptr != nullptr;
+    const int q = lane >> 4, rl = lane & 15;
+
+    // sparse operand of lane l for k-step g, tile t: row r0 + 16t + l%16,
+    // stored values [q*VALS/4, (q+1)*VALS/4) of the k-step, q = l/16
+    const uint8_t* vbase = reinterpret_cast<const uint8_t*>(a.vals) + (r0 + rl) * a.ldv * T::ES + q * 16;
+    const int64_t vstep = (int64_t)T::VALS * T::ES;
+    const int64_t vtile = 16 * a.ldv * T::ES;
+    auto load_a = [&](int64_t g, uint4 (&f)[TM]) {
+#pragma unroll
+        for (int t = 0; t < TM; ++t)
+            f[t] = (16 * t + rl < nrows && g < ksteps) ? *reinterpret_cast<const uint4*>(vbase + t * vtile + g * vstep)
+                                                      : make_uint4(0, 0, 0, 0);
+    };
 
     if (residual)
         for (int i = threadIdx.x; i < kTMax * 16 * 16; i += blockDim.x) reinterpret_cast<S*>(res)[i] = S(0);
@@ -276,102 +495,70 @@ __global__ void __launch_bounds__(kMaxWaves * 64) k_spmm_small_n(SpmmArgs a, int
 #pragma unroll
     for (int t = 0; t < TM; ++t) acc[t] = Acc{0, 0, 0, 0};
 
-    // sparse operand of lane l: row r0 + 16t + l%16, stored values
-    // [q*VALS/4, (q+1)*VALS/4) of each k-step, q = l/16
-    const int q = lane >> 4, rl = lane & 15;
-    const uint8_t* vbase = reinterpret_cast<const uint8_t*>(a.vals) + (r0 + rl) * a.ldv * T::ES + q * 16;
-    const int64_t vstep = (int64_t)T::VALS * T::ES;
-    const int64_t vtile = 16 * a.ldv * T::ES;
-
-    for (int64_t c0 = 0; c0 < ksteps; c0 += chunk_steps) {
+    uint4 ring[P][TM];
+    const int64_t nchunks = (ksteps + chunk_steps - 1) / chunk_steps;
+    for (int64_t c = 0; c < nchunks; ++c) {
+        const int64_t c0 = c * chunk_steps;
         const int csteps = (int)min<int64_t>(chunk_steps, ksteps - c0);
-        const int mpitch = csteps * T::META;             // metadata bytes per row in this chunk
-        if (c0 > 0) __syncthreads();                      // previous chunk consumed
-
-        // 1. direct-to-LDS: this chunk of B (when it copies in 16-byte
-        //    pieces) and the slab's metadata rows for the chunk
-        if (dma_b) {
-            constexpr int ROWB = 16 * T::ES, PIECES = ROWB / 16;
-            const int rows = csteps * T::KS;
-            const __amdgpu_buffer_rsrc_t rb =
-                rsrc(reinterpret_cast<const uint8_t*>(a.B) + c0 * T::KS * a.ldb * T::ES,
-                     ((a.K - c0 * T::KS - 1) * a.ldb + a.N) * T::ES);
-            for (int ins = wave; ins * 64 < rows * PIECES; ins += waves) {
-                const int p = ins * 64 + lane, row = p / PIECES, piece = p - row * PIECES;
-                const uint32_t off = row < rows ? (uint32_t)(row * a.ldb * T::ES + 16 * piece) : kOob;
-                dma<16>(rb, ldsb + ins * 1024, off);
-            }
-        }
-        {
-            const int words = mpitch / 4;                 // dwords per metadata row
-            const __amdgpu_buffer_rsrc_t rm =
-                rsrc(a.meta + r0 * a.ldm + c0 * T::META, (a.M - r0 - 1) * a.ldm + (a.K + 7) / 8 - c0 * T::META);
-            for (int ins = wave; ins * 64 < nrows * words; ins += waves) {
-                const int p = ins * 64 + lane, row = p / words, w = p - row * words;
-                const uint32_t off = row < nrows ? (uint32_t)(row * a.ldm + 4 * w) : kOob;
-                dma<4>(rm, ldsm + ins * 256, off);
-            }
-        }
-        // 2. B chunks that are not 16 full columns: element-wise staging
-        if (!dma_b) stage_b<DT>(a, ldsb, c0 * T::KS, csteps * T::KS, false);
-
-        // 3. weight batches; the first batch's loads are issued before the
-        //    wait so they stream while B and the metadata land
-        bool first = true;
-        for (int kb = wave * kBatch;; kb += waves * kBatch) {
-            const bool have = kb < csteps;
-            uint4 av[kBatch][TM];
-            if (have) {
+        const int pitch = csteps * T::META + 4;
+        if (c > 0) lds_barrier();                         // previous chunk's B and metadata consumed
+        // The ring's first loads go out before the chunk's B rows and
+        // metadata: waiting for the staging loads then also waits for them
+        // (loads complete in order), but the weight stream is already running.
+        if (vec_b) dma_b<DT>(a, lds_addr, c0 * T::KS, csteps * T::KS, wave);
+        if (vec_m) dma_meta<DT>(a, lds_addr + (uint32_t)(ldsm - lds), r0, nrows, c0, csteps, pitch, wave);
+        if (c == 0) {
 #pragma unroll
-                for (int s = 0; s < kBatch; ++s) {
+            for (int u = 0; u < P; ++u) load_a(wave + (int64_t)W * u, ring[u]);
+        }
+        // this wave's B and metadata loads have landed (with the ring's first
+        // loads, which the first multiply waits for anyway)
+        wait_vm<0>();
+        if (!vec_b) stage_b<DT>(a, ldsb, c0 * T::KS, csteps * T::KS, false);
+        if (!vec_m) stage_meta<DT>(a, ldsm, r0, nrows, c0, csteps, pitch, false);
+        lds_barrier();
+
+        // this wave's k-steps of the chunk: local kk = wave + W*i; a full
+        // chunk holds a multiple of W*P k-steps, so ring slot i % P belongs
+        // to the wave's global k-step sequence across chunks
+        const int nw = csteps > wave ? (csteps - wave + W - 1) / W : 0;
+        for (int i0 = 0; i0 < nw; i0 += P) {
+#pragma unroll
+            for (int u = 0; u < P; ++u) {
+                const int i = i0 + u;
+                if (i < nw) {
+                    const int kk = wave + W * i;
+                    uint4 b[2];
+                    load_b_operand<DT>(ldsb, kk, lane, b);
 #pragma unroll
                     for (int t = 0; t < TM; ++t) {
-                        const bool ok = 16 * t + rl < nrows && kb + s < csteps;
-                        av[s][t] = ok ? *reinterpret_cast<const uint4*>(vbase + t * vtile + (c0 + kb + s) * vstep)
-                                      : make_uint4(0, 0, 0, 0);
-                    }
-                }
-            }
-            if (first) {
-                // this wave's direct-to-LDS loads are done once its vector
-                // memory counter drains; the barrier covers the other waves'
-                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-                __syncthreads();
-                first = false;
-            }
-            if (!have) break;
-#pragma unroll
-            for (int s = 0; s < kBatch; ++s) {
-                if (kb + s >= csteps) break;
-                uint4 b[2];
-                load_b_operand<DT>(ldsb, kb + s, lane, b);
-#pragma unroll
-                for (int t = 0; t < TM; ++t) {
-                    {
-                        const uint8_t* mp = ldsm + (16 * t + rl) * mpitch + (kb + s) * T::META + q * (T::META / 4);
+                        const uint8_t* mp = ldsm + (16 * t + rl) * pitch + kk * T::META + q * (T::META / 4);
                         uint32_t ix;
                         if constexpr (DT == DT_I8) ix = *reinterpret_cast<const uint32_t*>(mp);
                         else ix = *reinterpret_cast<const uint16_t*>(mp);
-                        acc[t] = smfmac<DT>(av[s][t], b, acc[t], ix);
+                        acc[t] = smfmac<DT>(ring[u][t], b, acc[t], ix);
                     }
+                    load_a(c0 + kk + (int64_t)W * P, ring[u]);
                 }
             }
         }
         if (residual)
-            residual_chunk<DT>(a, ldsb, res, cursor, r0, nrows, c0 * T::KS, (c0 + csteps) * T::KS, c0 == 0, wave,
-                               waves, lane);
+            residual_chunk<DT, kResRows, (kResRows > 4 ? 2 : 4)>(a, ldsb, res, cursor, r0, nrows, c0 * T::KS,
+                                                                 (c0 + csteps) * T::KS, c == 0, wave, W, lane);
     }
-    __syncthreads();
+    lds_barrier();
 
     // fixed-order reduction of the waves' partial tiles
     Acc* red = reinterpret_cast<Acc*>(ldsb);
 #pragma unroll
     for (int t = 0; t < TM; ++t) red[(wave * kTMax + t) * 64 + lane] = acc[t];
-    __syncthreads();
+    lds_barrier();
+    const int tiles = (nrows + 15) >> 4;
     for (int i = threadIdx.x; i < tiles * 256; i += blockDim.x) {
         const int t = i >> 8, ln = (i >> 2) & 63, r = i & 3;
         S sum = S(0);
-        for (int w = 0; w < waves; ++w) sum += reinterpret_cast<const S*>(red)[((w * kTMax + t) * 64 + ln) * 4 + r];
+#pragma unroll
+        for (int w = 0; w < W; ++w) sum += reinterpret_cast<const S*>(red)[((w * kTMax + t) * 64 + ln) * 4 + r];
         const int row = 16 * t + 4 * (ln >> 4) + r, col = ln & 15;
         if (row < nrows && col < a.N) {
             if (residual) sum += reinterpret_cast<const S*>(res)[row * 16 + col];
@@ -383,45 +570,50 @@ __global__ void __launch_bounds__(kMaxWaves * 64) k_spmm_small_n(SpmmArgs a, int
 template <int DT>
 bool supported_t(const SpmmArgs& a) {
     using T = SN<DT>;
-    const uintptr_t v = reinterpret_cast<uintptr_t>(a.vals), m = reinterpret_cast<uintptr_t>(a.meta);
-    // vals rows 16-byte aligned; metadata rows 4-byte aligned (dword copies);
-    // every buffer addressed with 31-bit offsets
+    const uintptr_t v = reinterpret_cast<uintptr_t>(a.vals);
+    // vals rows 16-byte aligned; every index fits the kernel's 32-bit LDS math
     return a.N >= 1 && a.N <= 16 && a.K > 0 && a.K % T::KS == 0 && v % 16 == 0 && (a.ldv * T::ES) % 16 == 0 &&
-           m % 4 == 0 && a.ldm % 4 == 0 && a.M > 0 && (a.M - 1) * a.ldm + a.K / 8 < 0x7fffffff &&
-           ((a.K - 1) * a.ldb + a.N) * T::ES < 0x7fffffff;
+           a.M > 0;
+}
+
+// Ring depth by tiles per slab: about 16 fragments (KiB) in flight per wave.
+template <int TM> constexpr int kRing = TM == 1 ? 16 : TM == 2 ? 8 : 4;
+
+template <int DT, int TM>
+hipError_t launch_tm(const SpmmArgs& a, int64_t G, int64_t rows_per_wg, hipStream_t s) {
+    using T = SN<DT>;
+    constexpr int P = kRing<TM>;
+    const int64_t ksteps = a.K / T::KS;
+    // chunks of K: the chunk's B rows (16 columns) and the padded metadata
+    // rows of the slab's 16*TM rows share the LDS data region; a chunk that
+    // is not the last holds a multiple of W*P k-steps
+    const int64_t max_steps = (kLdsData - 16 * TM * 4) / (16 * T::ES * T::KS + 16 * TM * T::META);
+    int64_t chunk = ksteps;
+    if (chunk > max_steps) chunk = max_steps / (kWaves * P) * (kWaves * P);
+    if (chunk <= 0) return hipErrorInvalidConfiguration;   // excluded by the caller's choice of TM
+    const uintptr_t bp = reinterpret_cast<uintptr_t>(a.B), mp = reinterpret_cast<uintptr_t>(a.meta);
+    const bool vec_b = a.N == 16 && a.ldb == 16 && bp % 16 == 0 &&
+                       a.K * 16 * T::ES < 0x7fffffff;                // one contiguous block of B
+    const bool vec_m = mp % 4 == 0 && a.ldm % 4 == 0 && (a.M - 1) * a.ldm + (a.K + 7) / 8 < 0x7fffffff;
+    hipLaunchKernelGGL((k_spmm_small_n<DT, TM, P>), dim3((unsigned)G), dim3(64 * kWaves), 0, s, a, (int)rows_per_wg,
+                       (int)chunk, (int)vec_b, (int)vec_m);
+    return hipGetLastError();
 }
 
 template <int DT>
 hipError_t launch_t(const SpmmArgs& a, hipStream_t s) {
-    using T = SN<DT>;
     const int64_t tiles = (a.M + 15) / 16;
     int64_t G = tiles < 256 ? tiles : 256;
     const int64_t min_g = (tiles + kTMax - 1) / kTMax;
     if (G < min_g) G = min_g;
     const int64_t rows_per_wg = (a.M + G - 1) / G;
     G = (a.M + rows_per_wg - 1) / rows_per_wg;
-    const int64_t ksteps = a.K / T::KS;
-    // chunks of K: B rows (16 columns) and the slab's metadata rows must fit
-    // their LDS regions; chunks are made equal
-    int64_t max_steps = kLdsB / (16 * T::ES * T::KS);
-    const int64_t msteps = kLdsM / (rows_per_wg * T::META);
-    if (msteps < max_steps) max_steps = msteps;
-    const int64_t nchunks = (ksteps + max_steps - 1) / max_steps;
-    const int chunk_steps = (int)((ksteps + nchunks - 1) / nchunks);
-    const int tm = (int)((rows_per_wg + 15) / 16);
-    const int kbatch = kUnits / tm;
-    int waves = (chunk_steps + kbatch - 1) / kbatch;
-    if (waves > kMaxWaves) waves = kMaxWaves;
-    const uintptr_t bp = reinterpret_cast<uintptr_t>(a.B);
-    const bool dma_b = a.N == 16 && bp % 16 == 0 && (a.ldb * T::ES) % 16 == 0;
-    const dim3 grid((unsigned)G), block(64 * waves);
-    switch (tm) {
-        case 1: hipLaunchKernelGGL((k_spmm_small_n<DT, 1>), grid, block, 0, s, a, (int)rows_per_wg, chunk_steps, (int)dma_b); break;
-        case 2: hipLaunchKernelGGL((k_spmm_small_n<DT, 2>), grid, block, 0, s, a, (int)rows_per_wg, chunk_steps, (int)dma_b); break;
-        case 3: hipLaunchKernelGGL((k_spmm_small_n<DT, 3>), grid, block, 0, s, a, (int)rows_per_wg, chunk_steps, (int)dma_b); break;
-        default: hipLaunchKernelGGL((k_spmm_small_n<DT, 4>), grid, block, 0, s, a, (int)rows_per_wg, chunk_steps, (int)dma_b); break;
+    switch ((rows_per_wg + 15) / 16) {
+        case 1: return launch_tm<DT, 1>(a, G, rows_per_wg, s);
+        case 2: return launch_tm<DT, 2>(a, G, rows_per_wg, s);
+        case 3: return launch_tm<DT, 3>(a, G, rows_per_wg, s);
+        default: return launch_tm<DT, 4>(a, G, rows_per_wg, s);
     }
-    return hipGetLastError();
 }
 
 }  // namespace
