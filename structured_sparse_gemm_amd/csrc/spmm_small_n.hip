@@ -320,6 +320,8 @@ __device__ __forceinline__ void residual_chunk(const SpmmArgs& a, const uint8_t*
 
 typedef __attribute__((address_space(3))) void lds_void;
 
+constexpr uint32_t kOob = 0x80000000u;   // buffer offset that reads as zero
+
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, int64_t bytes) {
     const int64_t n = bytes < 0 ? 0 : (bytes > 0x7fffffff ? 0x7fffffff : bytes);
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)n, 0x00020000);
@@ -567,6 +569,150 @@ __global__ void __launch_bounds__(kWaves * 64) k_spmm_small_n(SpmmArgs a, int ro
     }
 }
 
+// Variant for products without a residual whose B is one contiguous K x 16
+// block.  The slab's metadata rows (all of K) are staged once, in 256-byte
+// row segments, behind the only barrier before the final reduction.  After
+// that every wave fetches what its k-steps need on its own -- the two 1 KiB
+// pieces of B rows (direct to a private LDS slot) and the sparse fragments
+// (to registers) -- as buffer loads from inline assembly.  A k-step beyond
+// K or a row beyond the slab uses an offset past its buffer, which reads
+// zero, so every wave issues the same GOPS loads per k-step and one
+// hand-counted wait per k-step is exact.
+template <int DT, int TM, int P>
+__global__ void __launch_bounds__(kWaves * 64) k_spmm_small_n_ring(SpmmArgs a, int rows_per_wg) {
+    constexpr int W = kWaves;
+    using T = SN<DT>;
+    using Acc = AccT<DT>;
+    using S = typename std::conditional<DT == DT_I8, int32_t, float>::type;
+    constexpr int BSTEP = 16 * T::ES * T::KS;           // B bytes per k-step (2 KiB)
+    constexpr int GOPS = 2 + TM;                        // loads per k-step per wave
+    static_assert(P * GOPS < 64, "vmcnt");
+    static_assert(W * kTMax * 1024 <= W * P * BSTEP, "LDS");
+    extern __shared__ __attribute__((aligned(1024))) uint8_t lds[];   // B slots, then the metadata rows
+    const uint32_t lds_addr = (uint32_t)(uintptr_t)(const lds_void*)lds;
+    uint8_t* ldsm = lds + W * P * BSTEP;
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t r0 = (int64_t)blockIdx.x * rows_per_wg;
+    const int nrows = (int)min<int64_t>(rows_per_wg, a.M - r0);
+    const int64_t ksteps = a.K / T::KS;
+    const int q = lane >> 4, rl = lane & 15;
+    const int pitch = (int)(ksteps * T::META) + 4;      // metadata row pitch in LDS (padded against conflicts)
+
+    const __amdgpu_buffer_rsrc_t rv = rsrc(reinterpret_cast<const uint8_t*>(a.vals) + r0 * a.ldv * T::ES,
+                                           ((a.M - r0 - 1) * a.ldv + a.K / 2) * T::ES);
+    const __amdgpu_buffer_rsrc_t rb = rsrc(a.B, a.K * 16 * T::ES);
+    uint32_t voff[TM];
+#pragma unroll
+    for (int t = 0; t < TM; ++t)
+        voff[t] = 16 * t + rl < nrows ? (uint32_t)((16 * t + rl) * a.ldv * T::ES + q * 16) : kOob;
+
+    i32x4 av[P][TM];   // native vector registers, so they can be tied to the wait below
+    // k-step g of this wave into ring slot u
+    auto issue = [&](int64_t g, int u) {
+        const bool in = g < ksteps;
+        const uint32_t slot = lds_addr + (uint32_t)((wave * P + u) * BSTEP);
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+            dma<16>(rb, slot + j * 1024, in ? (uint32_t)(g * BSTEP + j * 1024 + lane * 16) : kOob);
+#pragma unroll
+        for (int t = 0; t < TM; ++t) {
+            const uint32_t o = in ? voff[t] + (uint32_t)(g * T::VALS * T::ES) : kOob;
+            asm volatile("buffer_load_dwordx4 %0, %1, %2, 0 offen" : "=v"(av[u][t]) : "v"(o), "s"(rv) : "memory");
+        }
+    };
+
+    Acc acc[TM];
+#pragma unroll
+    for (int t = 0; t < TM; ++t) acc[t] = Acc{0, 0, 0, 0};
+    dma_meta<DT>(a, lds_addr + (uint32_t)(W * P * BSTEP), r0, nrows, 0, (int)ksteps, pitch, wave);
+#pragma unroll
+    for (int u = 0; u < P; ++u) issue(wave + (int64_t)W * u, u);
+    wait_vm<P * GOPS>();                                // this wave's metadata segments have landed
+    lds_barrier();                                      // and every other wave's
+    const int nw = ksteps > wave ? (int)((ksteps - wave + W - 1) / W) : 0;
+    for (int i0 = 0; i0 < nw; i0 += P) {
+#pragma unroll
+        for (int u = 0; u < P; ++u) {
+            const int i = i0 + u;
+            if (i < nw) {
+                // the oldest k-step in flight has landed once only the P-1
+                // younger ones remain; its registers are tied to the wait so
+                // no use moves above it
+                wait_vm<(P - 1) * GOPS>();
+#pragma unroll
+                for (int t = 0; t < TM; ++t) asm volatile("" : "+v"(av[u][t]));
+                uint4 b[2];
+                load_b_operand<DT>(lds + (wave * P + u) * BSTEP, 0, lane, b);
+                const int64_t g = wave + (int64_t)W * i;
+#pragma unroll
+                for (int t = 0; t < TM; ++t) {
+                    const uint8_t* mp = ldsm + (16 * t + rl) * pitch + g * T::META + q * (T::META / 4);
+                    uint32_t ix;
+                    if constexpr (DT == DT_I8) ix = *reinterpret_cast<const uint32_t*>(mp);
+                    else ix = *reinterpret_cast<const uint16_t*>(mp);
+                    uint4 f;
+                    __builtin_memcpy(&f, &av[u][t], 16);
+                    acc[t] = smfmac<DT>(f, b, acc[t], ix);
+                }
+                // the slot's LDS reads are done before its next B rows land
+                __builtin_amdgcn_s_waitcnt(0xC07F);
+                issue(wave + (int64_t)W * (i + P), u);
+            }
+        }
+    }
+    // the loads past the wave's last k-step land before the LDS is reused
+    wait_vm<0>();
+    lds_barrier();
+
+    // fixed-order reduction of the waves' partial tiles
+    Acc* red = reinterpret_cast<Acc*>(lds);
+#pragma unroll
+    for (int t = 0; t < TM; ++t) red[(wave * kTMax + t) * 64 + lane] = acc[t];
+    lds_barrier();
+    const int tiles = (nrows + 15) >> 4;
+    for (int i = threadIdx.x; i < tiles * 256; i += blockDim.x) {
+        const int t = i >> 8, ln = (i >> 2) & 63, r = i & 3;
+        S sum = S(0);
+#pragma unroll
+        for (int w = 0; w < W; ++w) sum += reinterpret_cast<const S*>(red)[((w * kTMax + t) * 64 + ln) * 4 + r];
+        const int row = 16 * t + 4 * (ln >> 4) + r, col = ln & 15;
+        if (row < nrows && col < a.N) reinterpret_cast<S*>(a.C)[(r0 + row) * a.ldc + col] = sum;
+    }
+}
+
+template <int TM> constexpr int kRingP = TM == 4 ? 6 : 8;
+
+// LDS of the ring variant: the waves' B slots and the slab's metadata rows
+template <int DT, int TM>
+int64_t ring_lds(const SpmmArgs& a) {
+    using T = SN<DT>;
+    return (int64_t)kWaves * kRingP<TM> * 16 * T::ES * T::KS + 16 * TM * ((a.K / T::KS) * T::META + 4);
+}
+
+template <int DT, int TM>
+hipError_t launch_ring(const SpmmArgs& a, int64_t G, int64_t rows_per_wg, hipStream_t s) {
+    constexpr int P = kRingP<TM>;
+    const unsigned shm = (unsigned)ring_lds<DT, TM>(a);
+    hipLaunchKernelGGL((k_spmm_small_n_ring<DT, TM, P>), dim3((unsigned)G), dim3(64 * kWaves), shm, s, a,
+                       (int)rows_per_wg);
+    return hipGetLastError();
+}
+
+// The barrier-free variant takes products without a residual whose B is one
+// contiguous K x 16 block and whose buffers are addressed with 31-bit offsets.
+template <int DT>
+bool ring_ok(const SpmmArgs& a, int tm) {
+    using T = SN<DT>;
+    const uintptr_t bp = reinterpret_cast<uintptr_t>(a.B), mp = reinterpret_cast<uintptr_t>(a.meta);
+    const int64_t lds = tm == 1 ? ring_lds<DT, 1>(a) : tm == 2 ? ring_lds<DT, 2>(a) : tm == 3 ? ring_lds<DT, 3>(a)
+                                                                                            : ring_lds<DT, 4>(a);
+    return a.row_ptr == nullptr && a.N == 16 && a.ldb == 16 && bp % 16 == 0 && mp % 4 == 0 && a.ldm % 4 == 0 &&
+           lds <= 160 * 1024 && a.K * 16 * T::ES < 0x7fffffff && a.M * a.ldv * T::ES < 0x7fffffff &&
+           a.M * a.ldm < 0x7fffffff;
+}
+
 template <int DT>
 bool supported_t(const SpmmArgs& a) {
     using T = SN<DT>;
@@ -608,6 +754,14 @@ hipError_t launch_t(const SpmmArgs& a, hipStream_t s) {
     if (G < min_g) G = min_g;
     const int64_t rows_per_wg = (a.M + G - 1) / G;
     G = (a.M + rows_per_wg - 1) / rows_per_wg;
+    if (ring_ok<DT>(a, (int)((rows_per_wg + 15) / 16))) {
+        switch ((rows_per_wg + 15) / 16) {
+            case 1: return launch_ring<DT, 1>(a, G, rows_per_wg, s);
+            case 2: return launch_ring<DT, 2>(a, G, rows_per_wg, s);
+            case 3: return launch_ring<DT, 3>(a, G, rows_per_wg, s);
+            default: return launch_ring<DT, 4>(a, G, rows_per_wg, s);
+        }
+    }
     switch ((rows_per_wg + 15) / 16) {
         case 1: return launch_tm<DT, 1>(a, G, rows_per_wg, s);
         case 2: return launch_tm<DT, 2>(a, G, rows_per_wg, s);
