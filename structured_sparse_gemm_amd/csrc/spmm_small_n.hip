@@ -213,108 +213,128 @@ __device__ __forceinline__ int transpose_col(int lane) {
     return ((lane & 1) << 3) | ((lane & 2) << 1) | ((lane & 4) >> 1) | ((lane & 8) >> 3);
 }
 
-// Residual rows of the slab owned by this wave (rl = wave + W*j), restricted
-// to columns of the current B chunk [kc0, kc1).  Columns ascend within a
-// row, so each row keeps a cursor (first entry not yet consumed) across
-// chunks.  A pass loads the next 64*E entries of every one of the wave's
-// rows at once (one memory round-trip for all of them), then takes each row
-// in turn: the entries of the chunk meet their B row in LDS, the 16 column
-// sums are reduced across the wave and added to res[row][16] in pass order.
+// Residual rows of the slab owned by this wave (rl = wave + W*j), taken
+// chunk by chunk of K (the columns whose B rows are in LDS).  Columns ascend
+// within a row, so each row keeps a cursor (first entry not yet consumed)
+// across chunks.  A pass loads the next 64*E entries of every one of the
+// wave's rows at once -- one memory round-trip for all of them, issued
+// before the chunk's 2:4 work so it lands meanwhile -- and is then consumed
+// row by row: the entries of the chunk meet their B row in LDS, the 16
+// column sums are reduced across the wave and added to res[row][16].
 template <int DT, int NRW, int E>
-__device__ __forceinline__ void residual_chunk(const SpmmArgs& a, const uint8_t* ldsb, void* res, int32_t* cursor,
-                                               int64_t r0, int nrows, int64_t kc0, int64_t kc1, bool first_chunk,
-                                               int wave, int waves, int lane) {
+struct ResPass {
+    using Raw = typename std::conditional<DT == DT_I8, int8_t, uint16_t>::type;   // stored width: no widening at load
+    int64_t lo[NRW], hi[NRW];
+    bool open[NRW];
+    int32_t c[NRW][E];
+    Raw vr[NRW][E];
+};
+
+template <int DT, int NRW, int E>
+__device__ __forceinline__ void residual_begin(ResPass<DT, NRW, E>& st, const SpmmArgs& a, const int32_t* cursor,
+                                               int64_t r0, int nrows, bool first_chunk, int wave, int waves) {
+    // all row bounds are read before any is used (rows past the slab read
+    // its last row and are masked)
+    int32_t p0[NRW], p1[NRW];
+#pragma unroll
+    for (int j = 0; j < NRW; ++j) {
+        const int64_t m = r0 + min(wave + waves * j, nrows - 1);
+        p0[j] = a.row_ptr[m];
+        p1[j] = a.row_ptr[m + 1];
+    }
+#pragma unroll
+    for (int j = 0; j < NRW; ++j) {
+        const int rl = wave + waves * j;
+        const bool valid = rl < nrows;
+        st.hi[j] = valid ? min<int64_t>(p1[j], a.nnz_r) : 0;
+        st.lo[j] = valid ? (first_chunk ? max<int64_t>(p0[j], 0) : (int64_t)cursor[rl]) : 0;
+        st.open[j] = st.lo[j] < st.hi[j];
+    }
+}
+
+// Issue one pass of loads.  Lanes past a row's end read entry 0 (the CSR is
+// non-empty while a row is open), so no load sits in a branch; the loaded
+// words are kept as they are and masked only when consumed, so nothing
+// waits for them here.
+template <int DT, int NRW, int E>
+__device__ __forceinline__ void residual_load(ResPass<DT, NRW, E>& st, const SpmmArgs& a, int lane) {
+#pragma unroll
+    for (int j = 0; j < NRW; ++j)
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            const int64_t idx = st.lo[j] + 64 * e + lane;
+            const int64_t li = st.open[j] && idx < st.hi[j] ? idx : 0;
+            st.c[j][e] = a.col[li];
+            if constexpr (DT == DT_I8) st.vr[j][e] = reinterpret_cast<const int8_t*>(a.rvals)[li];
+            else st.vr[j][e] = reinterpret_cast<const uint16_t*>(a.rvals)[li];
+        }
+}
+
+// Consume the loaded pass; returns whether any row still has entries of
+// this chunk left (a pass that stopped short of 64*E reached a column of a
+// later chunk or the row's end).
+template <int DT, int NRW, int E>
+__device__ __forceinline__ bool residual_consume(ResPass<DT, NRW, E>& st, const uint8_t* ldsb, void* res,
+                                                 int64_t kc0, int64_t kc1, int wave, int waves, int lane) {
     constexpr int ES = SN<DT>::ES;
     using S = typename std::conditional<DT == DT_I8, int32_t, float>::type;
-    int64_t lo[NRW], hi[NRW];
+    bool any = false;
+#pragma unroll
+    for (int j = 0; j < NRW; ++j) {
+        if (!st.open[j]) continue;
+        // B rows of the row's entries in this chunk (row 0 for the others,
+        // whose value is zeroed), all reads in flight before the products
+        uint4 w[E][2];
+        S vv[E];
+        int taken = 0;
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            const int64_t idx = st.lo[j] + 64 * e + lane;
+            const bool in = idx < st.hi[j];
+            const int32_t cc = in ? st.c[j][e] : (int32_t)kc1;
+            taken += __popcll(__ballot(cc < kc1));
+            const bool inch = cc >= kc0 && cc < kc1;
+            const uint8_t* brow = ldsb + (inch ? (int)(cc - kc0) : 0) * 16 * ES;
+            w[e][0] = *reinterpret_cast<const uint4*>(brow);
+            if constexpr (ES == 2) w[e][1] = *reinterpret_cast<const uint4*>(brow + 16);
+            if constexpr (DT == DT_I8) vv[e] = inch ? (int32_t)st.vr[j][e] : 0;
+            else vv[e] = inch ? elem_to_f32<DT>(st.vr[j][e]) : 0.0f;
+        }
+        S acc[16];
+#pragma unroll
+        for (int n = 0; n < 16; ++n) acc[n] = S(0);
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            if constexpr (DT == DT_I8) {
+                int8_t bv[16];
+                __builtin_memcpy(bv, &w[e][0], 16);
+#pragma unroll
+                for (int n = 0; n < 16; ++n) acc[n] += vv[e] * (int32_t)bv[n];
+            } else {
+                uint16_t bv[16];
+                __builtin_memcpy(bv, &w[e][0], 16);
+                __builtin_memcpy(bv + 8, &w[e][1], 16);
+#pragma unroll
+                for (int n = 0; n < 16; ++n) acc[n] = fmaf(vv[e], elem_to_f32<DT>(bv[n]), acc[n]);
+            }
+        }
+        const S tot = transpose_sum16<S>(acc, lane);
+        const int rl = wave + waves * j;
+        if (lane < 16) reinterpret_cast<S*>(res)[rl * 16 + transpose_col(lane)] += tot;
+        st.lo[j] += taken;
+        st.open[j] = taken == 64 * E && st.lo[j] < st.hi[j];
+        any |= st.open[j];
+    }
+    return any;
+}
+
+template <int DT, int NRW, int E>
+__device__ __forceinline__ void residual_end(const ResPass<DT, NRW, E>& st, int32_t* cursor, int nrows, int wave,
+                                             int waves, int lane) {
 #pragma unroll
     for (int j = 0; j < NRW; ++j) {
         const int rl = wave + waves * j;
-        const int64_t m = r0 + rl;
-        lo[j] = hi[j] = 0;
-        if (rl < nrows) {
-            hi[j] = min<int64_t>(a.row_ptr[m + 1], a.nnz_r);
-            lo[j] = first_chunk ? max<int64_t>(a.row_ptr[m], 0) : (int64_t)cursor[rl];
-        }
-    }
-    bool open[NRW];
-#pragma unroll
-    for (int j = 0; j < NRW; ++j) open[j] = lo[j] < hi[j];
-    using Raw = typename std::conditional<DT == DT_I8, int32_t, uint32_t>::type;
-    for (;;) {
-        bool any = false;
-#pragma unroll
-        for (int j = 0; j < NRW; ++j) any |= open[j];
-        if (!any) break;
-        // every load of the pass is issued before any is used; lanes past a
-        // row's end read entry 0 (the CSR is non-empty while a row is open)
-        // and are masked afterwards, so no load sits in a branch
-        int32_t c[NRW][E];
-        Raw vr[NRW][E];
-#pragma unroll
-        for (int j = 0; j < NRW; ++j)
-#pragma unroll
-            for (int e = 0; e < E; ++e) {
-                const int64_t idx = lo[j] + 64 * e + lane;
-                const bool in = open[j] && idx < hi[j];
-                const int64_t li = in ? idx : 0;
-                const int32_t cc = a.col[li];
-                Raw raw;
-                if constexpr (DT == DT_I8) raw = (int32_t)reinterpret_cast<const int8_t*>(a.rvals)[li];
-                else raw = reinterpret_cast<const uint16_t*>(a.rvals)[li];
-                c[j][e] = in ? cc : (int32_t)kc1;
-                vr[j][e] = in ? raw : Raw(0);
-            }
-#pragma unroll
-        for (int j = 0; j < NRW; ++j) {
-            if (!open[j]) continue;
-            // B rows of the row's entries in this chunk (row 0 for the others,
-            // whose value is zeroed), all reads in flight before the products
-            uint4 w[E][2];
-            S vv[E];
-            int taken = 0;
-#pragma unroll
-            for (int e = 0; e < E; ++e) {
-                const int64_t idx = lo[j] + 64 * e + lane;
-                taken += __popcll(__ballot(c[j][e] < kc1 && idx < hi[j]));
-                const bool inch = c[j][e] >= kc0 && c[j][e] < kc1;
-                const uint8_t* brow = ldsb + (inch ? (int)(c[j][e] - kc0) : 0) * 16 * ES;
-                w[e][0] = *reinterpret_cast<const uint4*>(brow);
-                if constexpr (ES == 2) w[e][1] = *reinterpret_cast<const uint4*>(brow + 16);
-                if constexpr (DT == DT_I8) vv[e] = inch ? vr[j][e] : 0;
-                else vv[e] = inch ? elem_to_f32<DT>((uint16_t)vr[j][e]) : 0.0f;
-            }
-            S acc[16];
-#pragma unroll
-            for (int n = 0; n < 16; ++n) acc[n] = S(0);
-#pragma unroll
-            for (int e = 0; e < E; ++e) {
-                if constexpr (DT == DT_I8) {
-                    int8_t bv[16];
-                    __builtin_memcpy(bv, &w[e][0], 16);
-#pragma unroll
-                    for (int n = 0; n < 16; ++n) acc[n] += vv[e] * (int32_t)bv[n];
-                } else {
-                    uint16_t bv[16];
-                    __builtin_memcpy(bv, &w[e][0], 16);
-                    __builtin_memcpy(bv + 8, &w[e][1], 16);
-#pragma unroll
-                    for (int n = 0; n < 16; ++n) acc[n] = fmaf(vv[e], elem_to_f32<DT>(bv[n]), acc[n]);
-                }
-            }
-            const S tot = transpose_sum16<S>(acc, lane);
-            const int rl = wave + waves * j;
-            if (lane < 16) reinterpret_cast<S*>(res)[rl * 16 + transpose_col(lane)] += tot;
-            lo[j] += taken;
-            // a pass that stopped short of 64*E reached a column of a later
-            // chunk or the row's end
-            open[j] = taken == 64 * E && lo[j] < hi[j];
-        }
-    }
-#pragma unroll
-    for (int j = 0; j < NRW; ++j) {
-        const int rl = wave + waves * j;
-        if (rl < nrows && lane == 0) cursor[rl] = (int32_t)lo[j];
+        if (rl < nrows && lane == 0) cursor[rl] = (int32_t)st.lo[j];
     }
 }
 
@@ -460,6 +480,7 @@ __global__ void __launch_bounds__(kWaves * 64) k_spmm_small_n(SpmmArgs a, int ro
                                                               int vec_b, int vec_m) {
     constexpr int W = kWaves;
     constexpr int kResRows = (16 * TM + W - 1) / W;   // residual rows per wave (dealt round-robin)
+    constexpr int kResE = kResRows > 4 ? 2 : 4;          // residual entries per lane per row per pass
     using T = SN<DT>;
     using Acc = AccT<DT>;
     using S = typename std::conditional<DT == DT_I8, int32_t, float>::type;
@@ -516,6 +537,12 @@ __global__ void __launch_bounds__(kWaves * 64) k_spmm_small_n(SpmmArgs a, int ro
         // this wave's B and metadata loads have landed (with the ring's first
         // loads, which the first multiply waits for anyway)
         wait_vm<0>();
+        // the chunk's first residual pass is in flight during its 2:4 work
+        ResPass<DT, kResRows, kResE> rp;
+        if (residual) {
+            residual_begin(rp, a, cursor, r0, nrows, c == 0, wave, W);
+            residual_load(rp, a, lane);
+        }
         if (!vec_b) stage_b<DT>(a, ldsb, c0 * T::KS, csteps * T::KS, false);
         if (!vec_m) stage_meta<DT>(a, ldsm, r0, nrows, c0, csteps, pitch, false);
         lds_barrier();
@@ -544,9 +571,11 @@ __global__ void __launch_bounds__(kWaves * 64) k_spmm_small_n(SpmmArgs a, int ro
                 }
             }
         }
-        if (residual)
-            residual_chunk<DT, kResRows, (kResRows > 4 ? 2 : 4)>(a, ldsb, res, cursor, r0, nrows, c0 * T::KS,
-                                                                 (c0 + csteps) * T::KS, c == 0, wave, W, lane);
+        if (residual) {
+            while (residual_consume(rp, ldsb, res, c0 * T::KS, (c0 + csteps) * T::KS, wave, W, lane))
+                residual_load(rp, a, lane);
+            residual_end(rp, cursor, nrows, wave, W, lane);
+        }
     }
     lds_barrier();
 
