@@ -121,8 +121,51 @@ def time_kernel(fn, iters: int, stream) -> float:
     return e0.elapsed_time(e1) * 1e-3 / iters
 
 
-def bench_workload(key: str, iters: int):
-    """Kernel-level numbers for one workload (compression outside the timing)."""
+def graph_time(launches, reps: int, stream) -> float:
+    """Average duration (s) of one launch: `launches` (a list of callables) is
+    captured once into a HIP graph and replayed `reps` times between two HIP
+    events on `stream`."""
+    import torch
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for f in launches:
+            f()
+    g.replay()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        g.replay()
+    e1.record(stream)
+    e1.synchronize()
+    return e0.elapsed_time(e1) * 1e-3 / (reps * len(launches))
+
+
+def read_bandwidth_GBps() -> float:
+    """Achievable HBM read rate on this device: a 2 GiB read-only reduction."""
+    import torch
+    x = torch.ones(512 << 20, dtype=torch.float32, device="cuda")
+    for _ in range(2):
+        x.sum()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(5):
+        x.sum()
+    e1.record()
+    e1.synchronize()
+    s = e0.elapsed_time(e1) * 1e-3 / 5
+    n = x.numel() * 4
+    del x
+    torch.cuda.empty_cache()
+    return n / s / 1e9
+
+
+def bench_workload(key: str, iters: int, read_GBps: float):
+    """Kernel-level numbers for one workload (compression outside the timing),
+    next to a dense GEMM of the same shape from the vendor library."""
     import numpy as np
     import torch
 
@@ -132,7 +175,6 @@ def bench_workload(key: str, iters: int):
     a = W.gen_a(w).cuda()
     b = W.gen_b(w).cuda()
     ops = ssg.split(a) if w.residual else ssg.compress(a)
-    del a
     wbytes = sum(t.numel() * t.element_size() for t in ops)
     copies = 1
     if w.klass == "small_n":
@@ -149,14 +191,18 @@ def bench_workload(key: str, iters: int):
             ssg.ssg_spmm_2to4(o[0], o[1], b, out)
 
     stream = torch.cuda.current_stream()
-    for i in range(max(3, copies)):
+    n = max(iters, copies)
+    for i in range(n):
         launch(i)
     torch.cuda.synchronize()
-    s = time_kernel(launch, iters, stream)
+    ref = out.clone()                                   # eager result of the last launch
+    s = graph_time([lambda i=i: launch(i) for i in range(n)], 2, stream)
+    graph_ok = bool(torch.equal(out, ref))
     flops = 2.0 * w.M * w.N * w.K
     bbytes = b.numel() * b.element_size()
     cbytes = out.numel() * out.element_size()
     r = {"title": w.title, "algo": ssg.ALGO_NAMES[algo], "us_per_launch": s * 1e6,
+         "timing": "HIP graph of %d launches, replayed twice; replay output matches eager: %s" % (n, graph_ok),
          "dense_equiv_TFLOPs": flops / s / 1e12, "compressed_weight_bytes": wbytes,
          "compressed_weight_GBps": wbytes / s / 1e9, "operand_copies_rotated": copies}
     if w.klass == "large_n":
@@ -165,7 +211,34 @@ def bench_workload(key: str, iters: int):
     else:
         r["frac_hbm_weights"] = wbytes / s / 1e9 / PEAK["hbm_GBps"]
         r["frac_hbm_all_bytes"] = (wbytes + bbytes + cbytes) / s / 1e9 / PEAK["hbm_GBps"]
-    del sets, ops, out, b
+        r["frac_measured_read_bw_weights"] = wbytes / s / 1e9 / read_GBps
+    del sets, ops, out
+    torch.cuda.empty_cache()
+
+    # dense comparator: the same product as a dense GEMM (vendor library via
+    # torch), weights as a dense matrix, copies rotated like the sparse ones
+    dense = a
+    dbytes = dense.numel() * dense.element_size()
+    dcopies = max(1, int(np.ceil((1 << 30) / dbytes))) if w.klass == "small_n" else 1
+    dsets = [dense] + [dense.clone() for _ in range(dcopies - 1)]
+    del a
+    if w.dtype == "i8":
+        dfn = lambda x: torch._int_mm(x, b)
+    else:
+        dfn = lambda x: torch.matmul(x, b)
+    nd = max(iters, dcopies)
+    try:
+        for i in range(nd):
+            dfn(dsets[i % dcopies])
+        torch.cuda.synchronize()
+        sd = time_kernel(lambda i: dfn(dsets[i % dcopies]), nd, stream)
+        r["dense_gemm_us"] = sd * 1e6
+        r["dense_gemm"] = "torch %s on dense weights of the same shape (%s output), back-to-back launches" % (
+            "_int_mm" if w.dtype == "i8" else "matmul", "int32" if w.dtype == "i8" else w.dtype)
+        r["speedup_vs_dense"] = sd / s
+    except RuntimeError as e:
+        r["dense_gemm"] = "unavailable: %s" % str(e).splitlines()[0][:120]
+    del dsets, dense, b
     torch.cuda.empty_cache()
     return r
 
@@ -178,6 +251,8 @@ def main() -> int:
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="oracle sample size, in seconds of CPU work")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-workloads", action="store_true", help="skip the per-workload table")
+    p.add_argument("--workload-iters", type=int, default=0,
+                   help="launches per workload in the table (default 200 for small N, 20 for large N)")
     p.add_argument("--calib-copy", action="store_true",
                    help="first run a plain elementwise copy of 256 MiB (read 256 MiB, write 256 MiB) three times, "
                         "outside the timed region: the reference for scaling HBM byte counters")
@@ -262,6 +337,16 @@ def main() -> int:
     print("bench: step %.3f ms (graph replay; compress %.1f us, spmm %.1f us)" % (ms, comp_s * 1e6, spmm_s * 1e6),
           file=sys.stderr, flush=True)
 
+    dense_note = None
+    try:
+        torch._int_mm(A, B)
+        torch.cuda.synchronize()
+        dense_s = time_kernel(lambda i: torch._int_mm(A, B), reps, stream)
+        dense_note = {"dense_gemm_us": dense_s * 1e6, "speedup_spmm_vs_dense": dense_s / spmm_s,
+                      "dense_gemm": "torch _int_mm (int8 x int8 -> int32) on the dense weights, back-to-back launches"}
+    except RuntimeError as e:
+        dense_note = {"dense_gemm": "unavailable: %s" % str(e).splitlines()[0][:120]}
+
     roofline = {
         "kernel": "spmm_large_n (int8 sparse MFMA 32x32x64)",
         "bound": "mfma",
@@ -292,7 +377,9 @@ def main() -> int:
         "spmm_only_dense_equiv_TFLOPs": flops / spmm_s / 1e12,
         "compress_us": comp_s * 1e6,
         "launch": "HIP graph of the step (compress + SpMM), replayed; replays match eager outputs: %s" % graph_ok,
+        "device": "%s, HIP %s" % (torch.cuda.get_device_name(0), torch.version.hip),
         "roofline": roofline,
+        "dense_comparator": dense_note,
     }
     if not args.no_cpu_baseline:
         print("bench: cpu baseline (oracle) ...", file=sys.stderr, flush=True)
@@ -303,10 +390,13 @@ def main() -> int:
     del A, B, vals, meta, C
     torch.cuda.empty_cache()
     if not args.no_workloads:
+        rbw = read_bandwidth_GBps()
+        out["measured_read_GBps"] = rbw
         table = {}
         for k in ("c1", "c3", "c4", "c5"):
             print("bench: workload %s ..." % k, file=sys.stderr, flush=True)
-            table[k] = bench_workload(k, iters=200 if W.WORKLOADS[k].klass != "large_n" else 20)
+            it = args.workload_iters or (200 if W.WORKLOADS[k].klass != "large_n" else 20)
+            table[k] = bench_workload(k, it, rbw)
         out["workloads"] = table
     print(json.dumps(out))
     return 0
