@@ -83,6 +83,10 @@ def _load():
                                               _vp, _vp, _vp, _vp, _i64, _vp, _vp, _vp, _i64]
             lib.orc_spmm_entries.argtypes = [ctypes.c_int, _i64, _i64, _i64, _vp, _i64, _vp, _i64,
                                              _vp, _vp, _vp, _vp, _i64, _i64, _vp, _vp, _vp, _vp, _vp]
+            lib.orc_delta_count.argtypes = [_i64, _i64, _vp, _vp, _vp]
+            lib.orc_delta_fill.argtypes = [ctypes.c_int, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp]
+            lib.orc_spmm_residual_delta.argtypes = lib.orc_spmm_residual.argtypes
+            lib.orc_spmm_entries_delta.argtypes = lib.orc_spmm_entries.argtypes
             lib.orc_num_threads.restype = ctypes.c_int
             _lib = lib
     return _lib
@@ -189,7 +193,27 @@ def split(dt: str, A):
     return vals, meta, row_ptr, col[:nnz], rvals[:nnz]
 
 
-def _mm(dt, vals, meta, B, K, residual):
+def delta_encode(dt: str, row_ptr, col, rvals, K: int):
+    """Delta-coded residual of a CSR (columns strictly ascending in [0, K)):
+    (drow_ptr int32 [M+1], dcol uint8, dvals).  Entry j of a row stores its
+    column as the byte col_j - col_(j-1), col_(-1) = -1; a gap above 255 is
+    bridged by fillers (255, +0) in front of the entry."""
+    row_ptr = np.ascontiguousarray(row_ptr, dtype=np.int32)
+    col = np.ascontiguousarray(col, dtype=np.int32)
+    rvals = np.ascontiguousarray(rvals, dtype=_store_dtype(dt))
+    M = row_ptr.shape[0] - 1
+    lib = _load()
+    drow_ptr = np.zeros(M + 1, dtype=np.int32)
+    _check(lib.orc_delta_count(M, K, _p(row_ptr), _p(col) if col.size else None, _p(drow_ptr)), "delta_count")
+    n = int(drow_ptr[M])
+    dcol = np.zeros(max(n, 1), dtype=np.uint8)
+    dvals = np.zeros(max(n, 1), dtype=_store_dtype(dt))
+    _check(lib.orc_delta_fill(DTYPES[dt], M, K, _p(row_ptr), _p(col) if col.size else None,
+                              _p(rvals) if rvals.size else None, _p(drow_ptr), _p(dcol), _p(dvals)), "delta_fill")
+    return drow_ptr, dcol[:n], dvals[:n]
+
+
+def _mm(dt, vals, meta, B, K, residual, delta=False):
     vals = _mat(vals, dt)
     B = _mat(B, dt)
     meta = np.ascontiguousarray(np.asarray(meta, dtype=np.uint8))
@@ -211,10 +235,11 @@ def _mm(dt, vals, meta, B, K, residual):
     else:
         row_ptr, col, rvals = residual
         row_ptr = np.ascontiguousarray(row_ptr, dtype=np.int32)
-        col = np.ascontiguousarray(col, dtype=np.int32)
+        col = np.ascontiguousarray(col, dtype=np.uint8 if delta else np.int32)
         rvals = np.ascontiguousarray(rvals, dtype=_store_dtype(dt))
-        rc = lib.orc_spmm_residual(DTYPES[dt], M, N, K, _p(vals), ldv, _p(meta), ldm, _p(row_ptr),
-                                   _p(col), _p(rvals), _p(B), ldb, _p(Cf), _p(Ci), _p(S), max(N, 1))
+        fn = lib.orc_spmm_residual_delta if delta else lib.orc_spmm_residual
+        rc = fn(DTYPES[dt], M, N, K, _p(vals), ldv, _p(meta), ldm, _p(row_ptr), _p(col), _p(rvals), _p(B), ldb,
+                _p(Cf), _p(Ci), _p(S), max(N, 1))
     _check(rc, "spmm")
     return C, S
 
@@ -228,8 +253,15 @@ def spmm_residual(dt: str, vals, meta, row_ptr, col, rvals, B, K: int):
     return _mm(dt, vals, meta, B, K, (row_ptr, col, rvals))
 
 
-def spmm_entries(dt: str, vals, meta, B, K: int, ms, ns, residual=None):
-    """Outputs C[ms[e], ns[e]] (and their bounds) one by one."""
+def spmm_residual_delta(dt: str, vals, meta, drow_ptr, dcol, dvals, B, K: int):
+    """As spmm_residual with a delta-coded residual (see delta_encode)."""
+    return _mm(dt, vals, meta, B, K, (drow_ptr, dcol, dvals), delta=True)
+
+
+def spmm_entries(dt: str, vals, meta, B, K: int, ms, ns, residual=None, delta: bool = False):
+    """Outputs C[ms[e], ns[e]] (and their bounds) one by one.  `residual` is a
+    CSR (row_ptr, col, rvals), or with delta=True a delta-coded
+    (drow_ptr, dcol, dvals)."""
     vals = _mat(vals, dt)
     B = _mat(B, dt)
     meta = np.ascontiguousarray(np.asarray(meta, dtype=np.uint8))
@@ -245,9 +277,10 @@ def spmm_entries(dt: str, vals, meta, B, K: int, ms, ns, residual=None):
     rp = col = rv = None
     if residual is not None:
         rp = np.ascontiguousarray(residual[0], dtype=np.int32)
-        col = np.ascontiguousarray(residual[1], dtype=np.int32)
+        col = np.ascontiguousarray(residual[1], dtype=np.uint8 if delta else np.int32)
         rv = np.ascontiguousarray(residual[2], dtype=_store_dtype(dt))
-    rc = _load().orc_spmm_entries(DTYPES[dt], M, N, K, _p(vals), max(vals.shape[1], 1), _p(meta),
+    fn = _load().orc_spmm_entries_delta if delta else _load().orc_spmm_entries
+    rc = fn(DTYPES[dt], M, N, K, _p(vals), max(vals.shape[1], 1), _p(meta),
                                   max(meta.shape[1], 1), _p(rp), _p(col), _p(rv), _p(B),
                                   _ld(B) if K > 0 else max(N, 1), E, _p(ms), _p(ns), _p(Cf), _p(Ci), _p(S))
     _check(rc, "spmm_entries")

@@ -237,6 +237,90 @@ int orc_split_fill(int dt, int64_t M, int64_t K, const void* A, int64_t lda,
     return ORC_OK;
 }
 
+/* ---- delta-coded residual ----
+ * [P4] section "How the three-layer format makes moderate sparsity fast"
+ * names a compact differential position code for the sparse layers, decoded
+ * in parallel on chip, and gives no layout.  The layout here is this
+ * library's own.  Per row, in CSR order, entry j stores its column as the
+ * gap d_j = col_j - col_(j-1) in one byte, with col_(-1) = -1 (so the first
+ * entry stores col_0 + 1).  A gap above 255 is bridged by filler entries,
+ * d = 255 and value +0, placed before the entry, as many as leave its own d
+ * in [1, 255].  Decoding is a running sum; a filler adds zero. */
+
+/* Fillers in front of an entry whose gap from the previous column is gap >= 1. */
+static int64_t fillers_for_gap(int64_t gap) { return (gap - 1) / 255; }
+
+/* Columns of a CSR row must ascend strictly within [0, K). */
+static int check_csr_row(int64_t K, const int32_t* col, int64_t lo, int64_t hi) {
+    int64_t prev = -1;
+    for (int64_t j = lo; j < hi; ++j) {
+        if (col[j] <= prev || col[j] >= K) return ORC_EFORMAT;
+        prev = col[j];
+    }
+    return ORC_OK;
+}
+
+static int check_csr(int64_t M, int64_t K, const int32_t* row_ptr, const int32_t* col) {
+    if (M < 0 || K < 0) return ORC_ESHAPE;
+    if (!row_ptr) return ORC_ENULL;
+    if (row_ptr[0] != 0) return ORC_EFORMAT;
+    for (int64_t m = 0; m < M; ++m)
+        if (row_ptr[m + 1] < row_ptr[m]) return ORC_EFORMAT;
+    if (M > 0 && row_ptr[M] > 0 && !col) return ORC_ENULL;
+    for (int64_t m = 0; m < M; ++m) {
+        int rc = check_csr_row(K, col, row_ptr[m], row_ptr[m + 1]);
+        if (rc) return rc;
+    }
+    return ORC_OK;
+}
+
+int orc_delta_count(int64_t M, int64_t K, const int32_t* row_ptr, const int32_t* col, int32_t* drow_ptr) {
+    int rc = check_csr(M, K, row_ptr, col);
+    if (rc) return rc;
+    if (!drow_ptr) return ORC_ENULL;
+    int64_t total = 0;
+    drow_ptr[0] = 0;
+    for (int64_t m = 0; m < M; ++m) {
+        int64_t prev = -1;
+        for (int64_t j = row_ptr[m]; j < row_ptr[m + 1]; ++j) {
+            total += 1 + fillers_for_gap((int64_t)col[j] - prev);
+            prev = col[j];
+        }
+        if (total > INT32_MAX) return ORC_ERANGE;
+        drow_ptr[m + 1] = (int32_t)total;
+    }
+    return ORC_OK;
+}
+
+int orc_delta_fill(int dt, int64_t M, int64_t K, const int32_t* row_ptr, const int32_t* col, const void* rvals,
+                   const int32_t* drow_ptr, uint8_t* dcol, void* dvals) {
+    if (!valid_dtype(dt)) return ORC_EDTYPE;
+    int rc = check_csr(M, K, row_ptr, col);
+    if (rc) return rc;
+    if (!drow_ptr) return ORC_ENULL;
+    if (M > 0 && row_ptr[M] > 0 && !rvals) return ORC_ENULL;
+    if (M > 0 && drow_ptr[M] > 0 && (!dcol || !dvals)) return ORC_ENULL;
+    for (int64_t m = 0; m < M; ++m) {
+        int64_t pos = drow_ptr[m], prev = -1;
+        for (int64_t j = row_ptr[m]; j < row_ptr[m + 1]; ++j) {
+            int64_t gap = (int64_t)col[j] - prev;
+            for (; gap > 255; gap -= 255) {
+                if (pos >= drow_ptr[m + 1]) return ORC_EFORMAT;
+                dcol[pos] = 255;
+                elem_zero(dt, dvals, pos);
+                ++pos;
+            }
+            if (pos >= drow_ptr[m + 1]) return ORC_EFORMAT;
+            dcol[pos] = (uint8_t)gap;
+            elem_copy(dt, dvals, pos, rvals, j);
+            ++pos;
+            prev = col[j];
+        }
+        if (pos != drow_ptr[m + 1]) return ORC_EFORMAT;
+    }
+    return ORC_OK;
+}
+
 /* ---- sparse x dense product ---- */
 
 static int check_mm(int dt, int64_t M, int64_t N, int64_t K, const void* vals, int64_t ldv,
@@ -254,8 +338,8 @@ static int check_mm(int dt, int64_t M, int64_t N, int64_t K, const void* vals, i
 /* Dense row m of decompress(vals, meta) [+ residual], as fp64 and int64.
  * Returns ORC_EFORMAT on a bad nibble. */
 static int dense_row(int dt, int64_t K, const void* vals, int64_t ldv, const uint8_t* meta, int64_t ldm,
-                     const int32_t* row_ptr, const int32_t* col, const void* rvals, int64_t m,
-                     double* rowf, int64_t* rowi) {
+                     const int32_t* row_ptr, const int32_t* col, const uint8_t* dcol, const void* rvals,
+                     int64_t m, double* rowf, int64_t* rowi) {
     for (int64_t k = 0; k < K; ++k) { rowf[k] = 0.0; rowi[k] = 0; }
     for (int64_t g = 0; g < K / 4; ++g) {
         int i0, i1;
@@ -266,8 +350,10 @@ static int dense_row(int dt, int64_t K, const void* vals, int64_t ldv, const uin
         if (dt == ORC_I8) { rowi[4 * g + i0] = elem_i64(vals, v0); rowi[4 * g + i1] = elem_i64(vals, v1); }
     }
     if (row_ptr) {
+        int64_t k = -1;                            /* delta-coded: column before the row's first entry */
         for (int64_t j = row_ptr[m]; j < row_ptr[m + 1]; ++j) {
-            int64_t k = col[j];
+            if (dcol) k += dcol[j];
+            else k = col[j];
             if (k < 0 || k >= K) return ORC_EFORMAT;
             rowf[k] += elem_f64(dt, rvals, j);
             if (dt == ORC_I8) rowi[k] += elem_i64(rvals, j);
@@ -278,11 +364,11 @@ static int dense_row(int dt, int64_t K, const void* vals, int64_t ldv, const uin
 
 static int spmm_impl(int dt, int64_t M, int64_t N, int64_t K, const void* vals, int64_t ldv,
                      const uint8_t* meta, int64_t ldm, const int32_t* row_ptr, const int32_t* col,
-                     const void* rvals, const void* B, int64_t ldb, double* Cf, int64_t* Ci,
-                     double* S, int64_t ldc) {
+                     const uint8_t* dcol, const void* rvals, const void* B, int64_t ldb, double* Cf,
+                     int64_t* Ci, double* S, int64_t ldc) {
     int rc = check_mm(dt, M, N, K, vals, ldv, meta, ldm, B, ldb, ldc, Cf, Ci);
     if (rc) return rc;
-    if (row_ptr && M > 0 && row_ptr[M] > 0 && (!col || !rvals)) return ORC_ENULL;
+    if (row_ptr && M > 0 && row_ptr[M] > 0 && ((!col && !dcol) || !rvals)) return ORC_ENULL;
     if (M == 0 || N == 0) return ORC_OK;
     /* B converted once, stored column by column so each output walks one
      * contiguous column; the sum order over k is unchanged. */
@@ -306,7 +392,7 @@ static int spmm_impl(int dt, int64_t M, int64_t N, int64_t K, const void* vals, 
 #pragma omp for schedule(dynamic, 1)
         for (int64_t m = 0; m < M; ++m) {
             if (!rowf || !rowi) continue;
-            int r = dense_row(dt, K, vals, ldv, meta, ldm, row_ptr, col, rvals, m, rowf, rowi);
+            int r = dense_row(dt, K, vals, ldv, meta, ldm, row_ptr, col, dcol, rvals, m, rowf, rowi);
             if (r) {
 #pragma omp critical
                 err = r;
@@ -340,7 +426,7 @@ static int spmm_impl(int dt, int64_t M, int64_t N, int64_t K, const void* vals, 
 int orc_spmm(int dt, int64_t M, int64_t N, int64_t K,
              const void* vals, int64_t ldv, const uint8_t* meta, int64_t ldm,
              const void* B, int64_t ldb, double* Cf, int64_t* Ci, double* S, int64_t ldc) {
-    return spmm_impl(dt, M, N, K, vals, ldv, meta, ldm, NULL, NULL, NULL, B, ldb, Cf, Ci, S, ldc);
+    return spmm_impl(dt, M, N, K, vals, ldv, meta, ldm, NULL, NULL, NULL, NULL, B, ldb, Cf, Ci, S, ldc);
 }
 
 int orc_spmm_residual(int dt, int64_t M, int64_t N, int64_t K,
@@ -348,14 +434,22 @@ int orc_spmm_residual(int dt, int64_t M, int64_t N, int64_t K,
                       const int32_t* row_ptr, const int32_t* col, const void* rvals,
                       const void* B, int64_t ldb, double* Cf, int64_t* Ci, double* S, int64_t ldc) {
     if (!row_ptr) return ORC_ENULL;
-    return spmm_impl(dt, M, N, K, vals, ldv, meta, ldm, row_ptr, col, rvals, B, ldb, Cf, Ci, S, ldc);
+    return spmm_impl(dt, M, N, K, vals, ldv, meta, ldm, row_ptr, col, NULL, rvals, B, ldb, Cf, Ci, S, ldc);
 }
 
-int orc_spmm_entries(int dt, int64_t M, int64_t N, int64_t K,
-                     const void* vals, int64_t ldv, const uint8_t* meta, int64_t ldm,
-                     const int32_t* row_ptr, const int32_t* col, const void* rvals,
-                     const void* B, int64_t ldb, int64_t n_entries,
-                     const int64_t* ms, const int64_t* ns, double* Cf, int64_t* Ci, double* S) {
+int orc_spmm_residual_delta(int dt, int64_t M, int64_t N, int64_t K,
+                            const void* vals, int64_t ldv, const uint8_t* meta, int64_t ldm,
+                            const int32_t* drow_ptr, const uint8_t* dcol, const void* dvals,
+                            const void* B, int64_t ldb, double* Cf, int64_t* Ci, double* S, int64_t ldc) {
+    if (!drow_ptr) return ORC_ENULL;
+    return spmm_impl(dt, M, N, K, vals, ldv, meta, ldm, drow_ptr, NULL, dcol, dvals, B, ldb, Cf, Ci, S, ldc);
+}
+
+static int entries_impl(int dt, int64_t M, int64_t N, int64_t K,
+                        const void* vals, int64_t ldv, const uint8_t* meta, int64_t ldm,
+                        const int32_t* row_ptr, const int32_t* col, const uint8_t* dcol, const void* rvals,
+                        const void* B, int64_t ldb, int64_t n_entries,
+                        const int64_t* ms, const int64_t* ns, double* Cf, int64_t* Ci, double* S) {
     int rc = check_mm(dt, M, N, K, vals, ldv, meta, ldm, B, ldb, N, Cf, Ci);
     if (rc) return rc;
     if (n_entries < 0) return ORC_ESHAPE;
@@ -366,7 +460,7 @@ int orc_spmm_entries(int dt, int64_t M, int64_t N, int64_t K,
     for (int64_t e = 0; e < n_entries && rc == ORC_OK; ++e) {
         int64_t m = ms[e], n = ns[e];
         if (m < 0 || m >= M || n < 0 || n >= N) { rc = ORC_ERANGE; break; }
-        rc = dense_row(dt, K, vals, ldv, meta, ldm, row_ptr, col, rvals, m, rowf, rowi);
+        rc = dense_row(dt, K, vals, ldv, meta, ldm, row_ptr, col, dcol, rvals, m, rowf, rowi);
         if (rc) break;
         if (dt == ORC_I8) {
             int64_t acc = 0;
@@ -386,6 +480,24 @@ int orc_spmm_entries(int dt, int64_t M, int64_t N, int64_t K,
     free(rowf);
     free(rowi);
     return rc;
+}
+
+int orc_spmm_entries(int dt, int64_t M, int64_t N, int64_t K,
+                     const void* vals, int64_t ldv, const uint8_t* meta, int64_t ldm,
+                     const int32_t* row_ptr, const int32_t* col, const void* rvals,
+                     const void* B, int64_t ldb, int64_t n_entries,
+                     const int64_t* ms, const int64_t* ns, double* Cf, int64_t* Ci, double* S) {
+    return entries_impl(dt, M, N, K, vals, ldv, meta, ldm, row_ptr, col, NULL, rvals, B, ldb, n_entries, ms, ns,
+                        Cf, Ci, S);
+}
+
+int orc_spmm_entries_delta(int dt, int64_t M, int64_t N, int64_t K,
+                           const void* vals, int64_t ldv, const uint8_t* meta, int64_t ldm,
+                           const int32_t* drow_ptr, const uint8_t* dcol, const void* dvals,
+                           const void* B, int64_t ldb, int64_t n_entries,
+                           const int64_t* ms, const int64_t* ns, double* Cf, int64_t* Ci, double* S) {
+    return entries_impl(dt, M, N, K, vals, ldv, meta, ldm, drow_ptr, NULL, dcol, dvals, B, ldb, n_entries, ms, ns,
+                        Cf, Ci, S);
 }
 
 int orc_num_threads(void) {

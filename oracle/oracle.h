@@ -30,7 +30,10 @@
  *     low nibble of metadata byte j; a row has ceil(K/8) metadata bytes;
  *   - the residual is the set of numerically non-zero elements the top-2
  *     selection dropped, stored as CSR (int32 row_ptr/col, col ascending);
- *   - fp16/bf16 products are accumulated in fp64, int8 in int64.
+ *   - fp16/bf16 products are accumulated in fp64, int8 in int64;
+ *   - the compact residual position code ([P4], same section, names one and
+ *     gives no layout) is this library's own delta code, defined at
+ *     orc_delta_count below.
  *
  * Element types: ORC_F16 (IEEE-754 binary16), ORC_BF16 (bfloat16),
  * ORC_I8 (two's-complement int8).  All matrices are row-major with an
@@ -82,6 +85,20 @@ int orc_split_fill(int dt, int64_t M, int64_t K, const void* A, int64_t lda,
                    void* vals, int64_t ldv, uint8_t* meta, int64_t ldm,
                    const int32_t* row_ptr, int32_t* col, void* rvals);
 
+/* Delta-coded residual, pass 1.  Input: a CSR with columns strictly
+ * ascending within [0, K) in every row (else ORC_EFORMAT).  Per row, in CSR
+ * order, entry j is stored as the byte d_j = col_j - col_(j-1), col_(-1) = -1;
+ * a gap above 255 is bridged by filler entries (d = 255, value +0) placed
+ * before the entry, floor((gap - 1) / 255) of them, which leaves d_j in
+ * [1, 255].  drow_ptr[0] = 0, drow_ptr[m+1] = drow_ptr[m] + entries of row m
+ * including fillers. */
+int orc_delta_count(int64_t M, int64_t K, const int32_t* row_ptr, const int32_t* col, int32_t* drow_ptr);
+
+/* Delta-coded residual, pass 2: dcol[] (bytes) and dvals[] (bit copies of
+ * rvals, +0 for fillers) at the positions drow_ptr gives. */
+int orc_delta_fill(int dt, int64_t M, int64_t K, const int32_t* row_ptr, const int32_t* col, const void* rvals,
+                   const int32_t* drow_ptr, uint8_t* dcol, void* dvals);
+
 /* C[m,n] = sum_k D[m,k] * B[k,n] over k ascending, D = decompress(vals, meta),
  * B[K,N] row-major.  fp16/bf16: Cf (fp64) and the bound S[m,n] = sum_k
  * |D[m,k] B[k,n]| (S may be NULL).  int8: Ci (int64).  Rows run in parallel
@@ -96,6 +113,13 @@ int orc_spmm_residual(int dt, int64_t M, int64_t N, int64_t K,
                       const int32_t* row_ptr, const int32_t* col, const void* rvals,
                       const void* B, int64_t ldb, double* Cf, int64_t* Ci, double* S, int64_t ldc);
 
+/* As orc_spmm_residual with the residual delta-coded: entry j of row m adds
+ * dvals[j] at column -1 + the sum of dcol over the row's entries up to j. */
+int orc_spmm_residual_delta(int dt, int64_t M, int64_t N, int64_t K,
+                            const void* vals, int64_t ldv, const uint8_t* meta, int64_t ldm,
+                            const int32_t* drow_ptr, const uint8_t* dcol, const void* dvals,
+                            const void* B, int64_t ldb, double* Cf, int64_t* Ci, double* S, int64_t ldc);
+
 /* Selected outputs only: for e < n_entries, (m, n) = (ms[e], ns[e]); writes
  * Cf[e]/Ci[e] and S[e].  row_ptr may be NULL (no residual). */
 int orc_spmm_entries(int dt, int64_t M, int64_t N, int64_t K,
@@ -103,6 +127,13 @@ int orc_spmm_entries(int dt, int64_t M, int64_t N, int64_t K,
                      const int32_t* row_ptr, const int32_t* col, const void* rvals,
                      const void* B, int64_t ldb, int64_t n_entries,
                      const int64_t* ms, const int64_t* ns, double* Cf, int64_t* Ci, double* S);
+
+/* As orc_spmm_entries with a delta-coded residual (drow_ptr not NULL). */
+int orc_spmm_entries_delta(int dt, int64_t M, int64_t N, int64_t K,
+                           const void* vals, int64_t ldv, const uint8_t* meta, int64_t ldm,
+                           const int32_t* drow_ptr, const uint8_t* dcol, const void* dvals,
+                           const void* B, int64_t ldb, int64_t n_entries,
+                           const int64_t* ms, const int64_t* ns, double* Cf, int64_t* Ci, double* S);
 
 /* Number of threads an OpenMP parallel region would use (1 without OpenMP). */
 int orc_num_threads(void);

@@ -35,8 +35,16 @@ MUTANTS = [
     ("bf16 exponent bias", "v = ldexp((double)(128 + f), e - 134);", "v = ldexp((double)(128 + f), e - 133);"),
     ("-0 counted as a residual non-zero", "if (keep[p] || elem_f64(dt, A, m * lda + k) == 0.0) continue;",
      "if (keep[p] || (dt == ORC_I8 ? elem_f64(dt, A, m * lda + k) == 0.0 : ((const uint16_t*)A)[m * lda + k] == 0)) continue;"),
-    ("last residual entry of a row dropped", "for (int64_t j = row_ptr[m]; j < row_ptr[m + 1]; ++j) {",
-     "for (int64_t j = row_ptr[m]; j + 1 < row_ptr[m + 1]; ++j) {"),
+    ("last residual entry of a row dropped",
+     "first entry */\n        for (int64_t j = row_ptr[m]; j < row_ptr[m + 1]; ++j) {",
+     "first entry */\n        for (int64_t j = row_ptr[m]; j + 1 < row_ptr[m + 1]; ++j) {"),
+    ("a gap of exactly 255 gets a filler", "static int64_t fillers_for_gap(int64_t gap) { return (gap - 1) / 255; }",
+     "static int64_t fillers_for_gap(int64_t gap) { return gap / 255; }"),
+    ("delta fill bridges gaps of 255", "for (; gap > 255; gap -= 255) {", "for (; gap >= 255; gap -= 255) {"),
+    ("delta gaps counted from column 0", "int64_t pos = drow_ptr[m], prev = -1;", "int64_t pos = drow_ptr[m], prev = 0;"),
+    ("filler carries the entry's value", "elem_zero(dt, dvals, pos);", "elem_copy(dt, dvals, pos, rvals, j);"),
+    ("delta decode starts at column 0", "int64_t k = -1;                            /* delta-coded",
+     "int64_t k = 0;                            /* delta-coded"),
     ("bound accumulates signed terms", "s += fabs(t);\n                    }\n                    Cf[m * ldc + n] = acc;",
      "s += t;\n                    }\n                    Cf[m * ldc + n] = acc;"),
 ]

@@ -230,6 +230,121 @@ def test_split(dt, fam):
     assert np.array_equal(Dv, U.to_f64(dt, A))
 
 
+# ---------------------------------------------------------------- delta-coded residual
+
+def _golden_delta(dt):
+    g = _golden("delta_code.json")
+    rows = g["rows"]
+    row_ptr = np.concatenate([[0], np.cumsum([len(r["col"]) for r in rows])]).astype(np.int32)
+    col = np.array([c for r in rows for c in r["col"]], dtype=np.int32)
+    rvals = U.encode(dt, np.array([v for r in rows for v in r["val"]], dtype=np.float64))
+    return g, row_ptr, col, rvals
+
+
+@pytest.mark.parametrize("dt", DTS)
+def test_delta_code_hand_worked_rows(dt):
+    g, row_ptr, col, rvals = _golden_delta(dt)
+    drow_ptr, dcol, dvals = oracle.delta_encode(dt, row_ptr, col, rvals, g["K"])
+    assert list(drow_ptr) == g["drow_ptr"]
+    assert list(dcol) == [d for r in g["rows"] for d in r["dcol"]]
+    want = U.encode(dt, np.array([v for r in g["rows"] for v in r["dval"]], dtype=np.float64))
+    assert np.array_equal(dvals, want)                  # fillers are +0 (all bits clear)
+
+
+def _random_csr(M, K, density, seed, far=False):
+    """Random CSR rows (ascending columns); `far` spreads a few entries over
+    long gaps so that fillers appear."""
+    rng = np.random.default_rng(seed)
+    cols = []
+    for m in range(M):
+        if far:
+            c = np.sort(rng.choice(K, size=rng.integers(0, 6), replace=False))
+        else:
+            c = np.nonzero(rng.random(K) < density)[0]
+        cols.append(c)
+    row_ptr = np.concatenate([[0], np.cumsum([len(c) for c in cols])]).astype(np.int32)
+    col = np.concatenate(cols).astype(np.int32) if row_ptr[-1] else np.zeros(0, np.int32)
+    return row_ptr, col
+
+
+@pytest.mark.parametrize("dt", DTS)
+@pytest.mark.parametrize("far", [False, True])
+def test_delta_code_invariants(dt, far):
+    M, K = 40, 3000
+    row_ptr, col = _random_csr(M, K, 0.09, 7 + far, far)
+    rvals = U.random_matrix(dt, 1, max(len(col), 1), "normal", 8)[0, :len(col)]
+    rvals = np.where(U.is_zero(dt, rvals), U.encode(dt, np.ones(len(col))), rvals)   # no explicit zeros
+    drow_ptr, dcol, dvals = oracle.delta_encode(dt, row_ptr, col, rvals, K)
+    assert drow_ptr[0] == 0 and (np.diff(drow_ptr) >= 0).all()
+    assert ((dcol >= 1) & (dcol <= 255)).all()
+    nz = ~U.is_zero(dt, dvals)
+    for m in range(M):
+        lo, hi, dlo, dhi = row_ptr[m], row_ptr[m + 1], drow_ptr[m], drow_ptr[m + 1]
+        c = col[lo:hi].astype(np.int64)
+        gaps = np.diff(np.concatenate([[-1], c]))
+        assert dhi - dlo == len(c) + ((gaps - 1) // 255).sum()          # closed-form length
+        dec = np.cumsum(dcol[dlo:dhi].astype(np.int64)) - 1             # running sum decodes the columns
+        real = nz[dlo:dhi]
+        assert np.array_equal(dec[real], c)
+        assert np.array_equal(dvals[dlo:dhi][real], rvals[lo:hi])
+        assert (dcol[dlo:dhi][~real] == 255).all()                      # fillers: full steps, value +0
+        if len(c):
+            assert dec[-1] == c[-1] and real[-1]
+    if far:
+        assert (~nz).sum() > 0                                           # the case exercises fillers
+
+
+@pytest.mark.parametrize("dt", DTS)
+def test_spmm_residual_delta_equals_csr_product(dt):
+    M, K, N = 24, 1024, 10
+    A = U.random_matrix(dt, M, K, "sparse", 61)
+    B = U.random_matrix(dt, K, N, "normal", 62)
+    vals, meta, row_ptr, col, rvals = oracle.split(dt, A)
+    drow_ptr, dcol, dvals = oracle.delta_encode(dt, row_ptr, col, rvals, K)
+    C0, S0 = oracle.spmm_residual(dt, vals, meta, row_ptr, col, rvals, B, K)
+    C1, S1 = oracle.spmm_residual_delta(dt, vals, meta, drow_ptr, dcol, dvals, B, K)
+    assert np.array_equal(C0, C1)
+    if S0 is not None:
+        assert np.array_equal(S0, S1)
+    # against the dense product of A itself
+    if dt == "i8":
+        assert np.array_equal(C1, U.to_i64(A) @ U.to_i64(B))
+    else:
+        ref = U.to_f64(dt, A) @ U.to_f64(dt, B)
+        assert np.allclose(C1, ref, rtol=1e-12, atol=1e-12 * np.abs(ref).max())
+    rng = np.random.default_rng(3)
+    ms, ns = rng.integers(0, M, 40), rng.integers(0, N, 40)
+    e, _ = oracle.spmm_entries(dt, vals, meta, B, K, ms, ns, residual=(drow_ptr, dcol, dvals), delta=True)
+    assert np.array_equal(e, C1[ms, ns])
+
+
+def test_spmm_residual_delta_with_fillers_bruteforce():
+    # residual entries far apart (fillers), int8 so every sum is exact
+    M, K, N = 6, 1200, 3
+    row_ptr, col = _random_csr(M, K, 0.0, 5, far=True)
+    rng = np.random.default_rng(4)
+    rv = rng.integers(1, 9, size=len(col)) * rng.choice([-1, 1], size=len(col))
+    rvals = U.encode("i8", rv)
+    B = U.encode("i8", rng.integers(-5, 6, size=(K, N)))
+    vals = np.zeros((M, K // 2), dtype=np.int8)
+    meta = np.full((M, K // 8), 0x44, dtype=np.uint8)                     # keep positions 0, 1 (values 0)
+    drow_ptr, dcol, dvals = oracle.delta_encode("i8", row_ptr, col, rvals, K)
+    C, _ = oracle.spmm_residual_delta("i8", vals, meta, drow_ptr, dcol, dvals, B, K)
+    want = np.zeros((M, N), dtype=np.int64)
+    for m in range(M):
+        for j in range(row_ptr[m], row_ptr[m + 1]):
+            for n in range(N):
+                want[m, n] += int(rv[j]) * int(B[col[j], n])
+    assert np.array_equal(C, want)
+
+
+def test_delta_code_rejects_bad_csr():
+    K = 100
+    for row_ptr, col in [([0, 2], [5, 5]), ([0, 2], [7, 3]), ([0, 1], [100]), ([0, 1], [-1]), ([0, 2, 1], [1, 2])]:
+        with pytest.raises(oracle.OracleError, match="bad format"):
+            oracle.delta_encode("i8", np.array(row_ptr), np.array(col), np.ones(len(col), np.int8), K)
+
+
 # ---------------------------------------------------------------- products
 
 def _exact_small(dt, shape, seed, lo=-3, hi=3):
