@@ -163,9 +163,10 @@ def read_bandwidth_GBps() -> float:
     return n / s / 1e9
 
 
-def bench_workload(key: str, iters: int, read_GBps: float):
+def bench_workload(key: str, iters: int, read_GBps: float, delta: bool = False, dense_cmp: bool = True):
     """Kernel-level numbers for one workload (compression outside the timing),
-    next to a dense GEMM of the same shape from the vendor library."""
+    next to a dense GEMM of the same shape from the vendor library.  With
+    delta=True the residual is delta-coded (one-byte column gaps)."""
     import numpy as np
     import torch
 
@@ -175,6 +176,8 @@ def bench_workload(key: str, iters: int, read_GBps: float):
     a = W.gen_a(w).cuda()
     b = W.gen_b(w).cuda()
     ops = ssg.split(a) if w.residual else ssg.compress(a)
+    if delta:
+        ops = ops[:2] + ssg.delta_encode(ops[2], ops[3], ops[4], w.K)
     wbytes = sum(t.numel() * t.element_size() for t in ops)
     copies = 1
     if w.klass == "small_n":
@@ -185,7 +188,9 @@ def bench_workload(key: str, iters: int, read_GBps: float):
 
     def launch(i):
         o = sets[i % copies]
-        if w.residual:
+        if delta:
+            ssg.ssg_spmm_2to4_residual_delta(*o, b, out)
+        elif w.residual:
             ssg.ssg_spmm_2to4_residual(*o, b, out)
         else:
             ssg.ssg_spmm_2to4(o[0], o[1], b, out)
@@ -201,7 +206,8 @@ def bench_workload(key: str, iters: int, read_GBps: float):
     flops = 2.0 * w.M * w.N * w.K
     bbytes = b.numel() * b.element_size()
     cbytes = out.numel() * out.element_size()
-    r = {"title": w.title, "algo": ssg.ALGO_NAMES[algo], "us_per_launch": s * 1e6,
+    r = {"title": w.title + (", residual delta-coded" if delta else ""), "algo": ssg.ALGO_NAMES[algo],
+         "us_per_launch": s * 1e6,
          "timing": "HIP graph of %d launches, replayed twice; replay output matches eager: %s" % (n, graph_ok),
          "dense_equiv_TFLOPs": flops / s / 1e12, "compressed_weight_bytes": wbytes,
          "compressed_weight_GBps": wbytes / s / 1e9, "operand_copies_rotated": copies}
@@ -214,6 +220,8 @@ def bench_workload(key: str, iters: int, read_GBps: float):
         r["frac_measured_read_bw_weights"] = wbytes / s / 1e9 / read_GBps
     del sets, ops, out
     torch.cuda.empty_cache()
+    if not dense_cmp:
+        return r
 
     # dense comparator: the same product as a dense GEMM (vendor library via
     # torch), weights as a dense matrix, copies rotated like the sparse ones
@@ -397,6 +405,9 @@ def main() -> int:
             print("bench: workload %s ..." % k, file=sys.stderr, flush=True)
             it = args.workload_iters or (200 if W.WORKLOADS[k].klass != "large_n" else 20)
             table[k] = bench_workload(k, it, rbw)
+            if W.WORKLOADS[k].residual:
+                print("bench: workload %s, delta-coded residual ..." % k, file=sys.stderr, flush=True)
+                table[k + "_delta"] = bench_workload(k, it, rbw, delta=True, dense_cmp=False)
         out["workloads"] = table
     print(json.dumps(out))
     return 0

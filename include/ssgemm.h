@@ -32,7 +32,9 @@
  *   B     [K, N]  dense activation (ldb >= N)
  *   C     [M, N]  fp32 for fp16/bf16 inputs, int32 for int8 inputs (ldc >= N)
  *   residual: CSR, row_ptr int32 [M+1] (row_ptr[0] = 0), col int32 [nnz]
- *         ascending within a row, rvals [nnz] in the element type of A.
+ *         ascending within a row, rvals [nnz] in the element type of A; or
+ *         delta-coded (one-byte column gaps, described before
+ *         ssg_residual_delta_count).
  *
  * Selection rule: for a group with magnitudes a0..a3 (|x| of the value; int8
  * -128 has magnitude 128; -0 and +0 are equal), position p is kept iff fewer
@@ -153,7 +155,49 @@ int ssg_spmm_2to4_residual(int ab, int c, int64_t M, int64_t N, int64_t K,
                            int64_t nnz_r, const void* B, int64_t ldb, void* C, int64_t ldc,
                            void* ws, size_t ws_bytes, void* stream);
 
-/* As the two calls above with an explicit algorithm (ssg_algo). */
+/* Delta-coded residual: the residual CSR with each column index replaced by
+ * a one-byte gap, decoded on the GPU by a running sum.  "How sparse LLM
+ * weights cut GPU inference cost without quantization", section "How the
+ * three-layer format makes moderate sparsity fast", names a differential
+ * position code for the sparse layers that is decoded in parallel on chip;
+ * it gives no layout, and this one is the library's own:
+ *   drow_ptr int32 [M+1], drow_ptr[0] = 0, row m = entries
+ *            [drow_ptr[m], drow_ptr[m+1]);
+ *   dcol     uint8 [n]: entry j of a row stores col_j - col_(j-1), with
+ *            col_(-1) = -1, a value in [1, 255];
+ *   dvals    [n] in the element type of A.
+ * A gap above 255 is bridged by filler entries (dcol 255, dvals +0) placed in
+ * front of the entry, floor((gap - 1) / 255) of them.  An entry costs 1 + s
+ * bytes (s = element size) instead of the CSR's 4 + s; fillers appear only
+ * where a row's residual columns lie more than 255 apart.
+ *
+ * Encoding, pass 1: drow_ptr from a CSR whose columns ascend strictly
+ * within [0, K) in every row; nnz_r = row_ptr[M] (trusted, as for the
+ * products).  A CSR outside that contract gives an unspecified code but no
+ * out-of-bounds access: entries are clamped to [0, nnz_r), columns to
+ * [0, K - 1], and a gap below 1 counts as 1.  The caller reads drow_ptr[M]
+ * to size dcol and dvals.  Fails with SSG_ERR_SHAPE when the worst case,
+ * nnz_r + M * (K / 255 + 1) entries, exceeds 2^31 - 1. */
+int ssg_residual_delta_count(int64_t M, int64_t K, const int32_t* row_ptr, const int32_t* col, int64_t nnz_r,
+                             int32_t* drow_ptr, void* stream);
+
+/* Encoding, pass 2: dcol and dvals (values bit-copied, fillers +0) at the
+ * positions drow_ptr (from pass 1 on the same CSR) gives.  Writes stay
+ * inside each row's [drow_ptr[m], drow_ptr[m+1]). */
+int ssg_residual_delta_fill(int dt, int64_t M, int64_t K, const int32_t* row_ptr, const int32_t* col,
+                            const void* rvals, int64_t nnz_r, const int32_t* drow_ptr, uint8_t* dcol, void* dvals,
+                            void* stream);
+
+/* C = (expand(vals, meta) + delta-coded residual) x B, as
+ * ssg_spmm_2to4_residual.  nnz_d must equal drow_ptr[M] (trusted; it selects
+ * the launch shape).  Decoded columns at or beyond K are skipped. */
+int ssg_spmm_2to4_residual_delta(int ab, int c, int64_t M, int64_t N, int64_t K,
+                                 const void* vals, int64_t ldv, const uint8_t* meta, int64_t ldm,
+                                 const int32_t* drow_ptr, const uint8_t* dcol, const void* dvals,
+                                 int64_t nnz_d, const void* B, int64_t ldb, void* C, int64_t ldc,
+                                 void* ws, size_t ws_bytes, void* stream);
+
+/* As the SpMM calls above with an explicit algorithm (ssg_algo). */
 int ssg_spmm_2to4_ex(int algo, int ab, int c, int64_t M, int64_t N, int64_t K,
                      const void* vals, int64_t ldv, const uint8_t* meta, int64_t ldm,
                      const void* B, int64_t ldb, void* C, int64_t ldc,
@@ -163,6 +207,11 @@ int ssg_spmm_2to4_residual_ex(int algo, int ab, int c, int64_t M, int64_t N, int
                               const int32_t* row_ptr, const int32_t* col, const void* rvals,
                               int64_t nnz_r, const void* B, int64_t ldb, void* C, int64_t ldc,
                               void* ws, size_t ws_bytes, void* stream);
+int ssg_spmm_2to4_residual_delta_ex(int algo, int ab, int c, int64_t M, int64_t N, int64_t K,
+                                    const void* vals, int64_t ldv, const uint8_t* meta, int64_t ldm,
+                                    const int32_t* drow_ptr, const uint8_t* dcol, const void* dvals,
+                                    int64_t nnz_d, const void* B, int64_t ldb, void* C, int64_t ldc,
+                                    void* ws, size_t ws_bytes, void* stream);
 
 /* The algorithm SSG_ALGO_AUTO would run for this problem and these pointers
  * and leading dimensions (alignment decides between fast and generic paths). */

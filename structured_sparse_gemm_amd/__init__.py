@@ -8,7 +8,8 @@ live on a ROCm device and the library must load.
 
 Same-named bindings of the C ABI (``ssg_compress_2to4`` ...) take
 preallocated tensors; ``compress``, ``prune``, ``decompress``, ``split``,
-``spmm`` and ``spmm_residual`` allocate their outputs.
+``delta_encode``, ``spmm``, ``spmm_residual`` and ``spmm_residual_delta``
+allocate their outputs.
 """
 from __future__ import annotations
 
@@ -21,9 +22,11 @@ from ._abi import (SSG_ALGO_AUTO, SSG_ALGO_GENERIC, SSG_ALGO_LARGE_N, SSG_ALGO_S
                    SSG_F32, SSG_I8, SSG_I32)
 
 __all__ = [
-    "SsgError", "compress", "prune", "decompress", "split", "spmm", "spmm_residual", "vals_cols", "meta_cols",
+    "SsgError", "compress", "prune", "decompress", "split", "delta_encode", "spmm", "spmm_residual",
+    "spmm_residual_delta", "vals_cols", "meta_cols",
     "ssg_prune_2to4", "ssg_compress_2to4", "ssg_decompress_2to4", "ssg_split_count", "ssg_split_fill",
-    "ssg_spmm_workspace_bytes", "ssg_spmm_2to4", "ssg_spmm_2to4_residual", "ssg_spmm_select_algo",
+    "ssg_residual_delta_count", "ssg_residual_delta_fill", "ssg_spmm_workspace_bytes", "ssg_spmm_2to4",
+    "ssg_spmm_2to4_residual", "ssg_spmm_2to4_residual_delta", "ssg_spmm_select_algo",
     "SSG_ALGO_AUTO", "SSG_ALGO_GENERIC", "SSG_ALGO_SMALL_N", "SSG_ALGO_LARGE_N", "library_path",
 ]
 
@@ -125,6 +128,22 @@ def ssg_split_fill(A, vals, meta, row_ptr, col, rvals, stream=None) -> None:
                                  _ptr(col, "col"), _ptr(rvals, "rvals"), _stream(A, stream)), "ssg_split_fill")
 
 
+def ssg_residual_delta_count(row_ptr, col, K: int, drow_ptr, stream=None) -> None:
+    M = row_ptr.numel() - 1
+    nnz = int(col.numel()) if col is not None else 0
+    _check(_lib().ssg_residual_delta_count(M, K, _ptr(row_ptr, "row_ptr"), _ptr(col, "col"), nnz,
+                                           _ptr(drow_ptr, "drow_ptr"), _stream(row_ptr, stream)),
+           "ssg_residual_delta_count")
+
+
+def ssg_residual_delta_fill(row_ptr, col, rvals, K: int, drow_ptr, dcol, dvals, stream=None) -> None:
+    M = row_ptr.numel() - 1
+    nnz = int(col.numel()) if col is not None else 0
+    _check(_lib().ssg_residual_delta_fill(_dtype(rvals), M, K, _ptr(row_ptr, "row_ptr"), _ptr(col, "col"),
+                                          _ptr(rvals, "rvals"), nnz, _ptr(drow_ptr, "drow_ptr"), _ptr(dcol, "dcol"),
+                                          _ptr(dvals, "dvals"), _stream(row_ptr, stream)), "ssg_residual_delta_fill")
+
+
 def ssg_spmm_workspace_bytes(dtype: torch.dtype, M: int, N: int, K: int) -> int:
     return int(_lib().ssg_spmm_workspace_bytes(_DT[dtype], M, N, K))
 
@@ -156,6 +175,20 @@ def ssg_spmm_2to4_residual(vals, meta, row_ptr, col, rvals, B, C, ws=None, algo:
                                             _ptr(col, "col"), _ptr(rvals, "rvals"), nnz, _ptr(B, "B"), _ld(B, "B"),
                                             _ptr(C, "C"), _ld(C, "C"), _ptr(ws, "ws"), wsb, _stream(C, stream)),
            "ssg_spmm_2to4_residual")
+
+
+def ssg_spmm_2to4_residual_delta(vals, meta, drow_ptr, dcol, dvals, B, C, ws=None, algo: int = SSG_ALGO_AUTO,
+                                 stream=None) -> None:
+    ab = _dtype(vals)
+    M, N, K = vals.shape[0], B.shape[1], B.shape[0]
+    nnz = int(dcol.numel()) if dcol is not None else 0
+    ws, wsb = _workspace(vals.dtype, M, N, K, vals.device, ws)
+    _check(_lib().ssg_spmm_2to4_residual_delta_ex(algo, ab, _OUT[ab][0], M, N, K, _ptr(vals, "vals"),
+                                                  _ld(vals, "vals"), _ptr(meta, "meta"), _ld(meta, "meta"),
+                                                  _ptr(drow_ptr, "drow_ptr"), _ptr(dcol, "dcol"),
+                                                  _ptr(dvals, "dvals"), nnz, _ptr(B, "B"), _ld(B, "B"),
+                                                  _ptr(C, "C"), _ld(C, "C"), _ptr(ws, "ws"), wsb,
+                                                  _stream(C, stream)), "ssg_spmm_2to4_residual_delta")
 
 
 def ssg_spmm_select_algo(vals, meta, B, C) -> int:
@@ -219,4 +252,26 @@ def spmm_residual(vals, meta, row_ptr, col, rvals, B, algo: int = SSG_ALGO_AUTO,
     ab = _dtype(vals)
     C = torch.empty((vals.shape[0], B.shape[1]), dtype=_OUT[ab][1], device=vals.device) if out is None else out
     ssg_spmm_2to4_residual(vals, meta, row_ptr, col, rvals, B, C, algo=algo)
+    return C
+
+
+def delta_encode(row_ptr: torch.Tensor, col: torch.Tensor, rvals: torch.Tensor, K: int):
+    """Delta-coded form (drow_ptr, dcol uint8, dvals) of a CSR residual (columns
+    ascending in every row).  Reads the coded size back to the host between
+    the two passes (one sync)."""
+    M = row_ptr.numel() - 1
+    drow_ptr = torch.empty(M + 1, dtype=torch.int32, device=row_ptr.device)
+    ssg_residual_delta_count(row_ptr, col, K, drow_ptr)
+    n = int(drow_ptr[M].item())
+    dcol = torch.empty(n, dtype=torch.uint8, device=row_ptr.device)
+    dvals = torch.empty(n, dtype=rvals.dtype, device=row_ptr.device)
+    ssg_residual_delta_fill(row_ptr, col, rvals, K, drow_ptr, dcol, dvals)
+    return drow_ptr, dcol, dvals
+
+
+def spmm_residual_delta(vals, meta, drow_ptr, dcol, dvals, B, algo: int = SSG_ALGO_AUTO,
+                        out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    ab = _dtype(vals)
+    C = torch.empty((vals.shape[0], B.shape[1]), dtype=_OUT[ab][1], device=vals.device) if out is None else out
+    ssg_spmm_2to4_residual_delta(vals, meta, drow_ptr, dcol, dvals, B, C, algo=algo)
     return C

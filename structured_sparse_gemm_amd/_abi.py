@@ -40,6 +40,12 @@ SIGNATURES = {
                               _vp, _sz, _vp]),
     "ssg_spmm_2to4_residual_ex": (_i, [_i, _i, _i, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _vp, _vp,
                                        _i64, _vp, _i64, _vp, _i64, _vp, _sz, _vp]),
+    "ssg_residual_delta_count": (_i, [_i64, _i64, _vp, _vp, _i64, _vp, _vp]),
+    "ssg_residual_delta_fill": (_i, [_i, _i64, _i64, _vp, _vp, _vp, _i64, _vp, _vp, _vp, _vp]),
+    "ssg_spmm_2to4_residual_delta": (_i, [_i, _i, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _vp, _vp, _i64,
+                                          _vp, _i64, _vp, _i64, _vp, _sz, _vp]),
+    "ssg_spmm_2to4_residual_delta_ex": (_i, [_i, _i, _i, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _vp, _vp,
+                                             _i64, _vp, _i64, _vp, _i64, _vp, _sz, _vp]),
     "ssg_spmm_select_algo": (_i, [_i, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64]),
 }
 

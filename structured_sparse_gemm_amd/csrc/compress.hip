@@ -372,6 +372,91 @@ __global__ void __launch_bounds__(kSplitThreads) k_split_fill(int64_t M, int64_t
     }
 }
 
+// ---- delta-coded residual --------------------------------------------------
+//
+// Compact residual: entry j of a row stores its column as the one-byte gap
+// d = col_j - col_(j-1) (col_(-1) = -1), and a gap above 255 is bridged by
+// filler entries (d = 255, value +0) in front of it, floor((gap - 1) / 255)
+// of them.  "How sparse LLM weights cut GPU inference cost without
+// quantization", section "How the three-layer format makes moderate sparsity
+// fast", names such a differential position code decoded on chip; the byte
+// layout is this library's own.  Both passes read the CSR through the same
+// clamps (entries to [0, nnz), columns to [0, K - 1], a gap below 1 taken as
+// 1), so the fill writes exactly the entries the count gave each row, even
+// for a malformed CSR.
+
+struct DeltaEntry {
+    int fillers;   // filler entries in front of the entry
+    int d;         // the entry's own gap byte, in [1, 255]
+};
+
+__device__ __forceinline__ DeltaEntry delta_entry(const int32_t* col, int64_t j, int64_t lo, int64_t K) {
+    const int64_t c = min<int64_t>(max<int64_t>(col[j], 0), K - 1);
+    const int64_t p = j > lo ? min<int64_t>(max<int64_t>(col[j - 1], 0), K - 1) : -1;
+    const int64_t gap = max<int64_t>(c - p, 1);
+    const int f = (int)((gap - 1) / 255);
+    return DeltaEntry{f, (int)(gap - 255 * (int64_t)f)};
+}
+
+__device__ __forceinline__ void csr_row_range(const int32_t* row_ptr, int64_t m, int64_t nnz, int64_t* lo,
+                                              int64_t* hi) {
+    *lo = min<int64_t>(max<int64_t>(row_ptr[m], 0), nnz);
+    *hi = min<int64_t>(max<int64_t>(row_ptr[m + 1], *lo), nnz);
+}
+
+// Pass 1: entries of row m (fillers included) into drow_ptr[m + 1]; one block
+// per row (grid-stride).
+__global__ void __launch_bounds__(kSplitThreads) k_delta_count(int64_t M, int64_t K, const int32_t* row_ptr,
+                                                               const int32_t* col, int64_t nnz, int32_t* drow_ptr) {
+    __shared__ int lds4[kSplitThreads / 64];
+    for (int64_t m = blockIdx.x; m < M; m += gridDim.x) {
+        int64_t lo, hi;
+        csr_row_range(row_ptr, m, nnz, &lo, &hi);
+        int cnt = 0;
+        for (int64_t j = lo + threadIdx.x; j < hi; j += kSplitThreads) cnt += 1 + delta_entry(col, j, lo, K).fillers;
+        int total;
+        block_exclusive_scan(cnt, &total, lds4);
+        if (threadIdx.x == 0) drow_ptr[m + 1] = total;
+    }
+}
+
+// Pass 2: the gap bytes and values; 256 entries of a row at a time, a block
+// scan placing each entry (and its fillers) after those of lower threads.
+template <int DT>
+__global__ void __launch_bounds__(kSplitThreads) k_delta_fill(int64_t M, int64_t K, const int32_t* row_ptr,
+                                                              const int32_t* col, const typename Store<DT>::T* rvals,
+                                                              int64_t nnz, const int32_t* drow_ptr, uint8_t* dcol,
+                                                              typename Store<DT>::T* dvals) {
+    using T = typename Store<DT>::T;
+    __shared__ int lds4[kSplitThreads / 64];
+    for (int64_t m = blockIdx.x; m < M; m += gridDim.x) {
+        int64_t lo, hi;
+        csr_row_range(row_ptr, m, nnz, &lo, &hi);
+        const int64_t end = drow_ptr[m + 1];
+        int64_t carry = drow_ptr[m];
+        for (int64_t j0 = lo; j0 < hi; j0 += kSplitThreads) {
+            const int64_t j = j0 + threadIdx.x;
+            const bool have = j < hi;
+            DeltaEntry e{0, 0};
+            if (have) e = delta_entry(col, j, lo, K);
+            int total;
+            const int before = block_exclusive_scan(have ? 1 + e.fillers : 0, &total, lds4);
+            int64_t pos = carry + before;
+            for (int i = 0; i < e.fillers; ++i, ++pos) {
+                if (pos < end) {
+                    dcol[pos] = 255;
+                    dvals[pos] = T(0);
+                }
+            }
+            if (have && pos < end) {
+                dcol[pos] = (uint8_t)e.d;
+                dvals[pos] = rvals[j];
+            }
+            carry += total;
+        }
+    }
+}
+
 inline unsigned blocks_for(int64_t threads, int per_block) {
     return (unsigned)((threads + per_block - 1) / per_block);
 }
@@ -451,6 +536,33 @@ hipError_t launch_split_fill(int dt, int64_t M, int64_t K, const void* A, int64_
         using T = typename Store<D>::T;
         hipLaunchKernelGGL(k_split_fill<D>, dim3(grid), dim3(kSplitThreads), 0, s, M, K, (const T*)A, lda, (T*)vals,
                            ldv, meta, ldm, row_ptr, col, (T*)rvals, (int)vec);
+    });
+    return hipGetLastError();
+}
+
+hipError_t launch_delta_count(int64_t M, int64_t K, const int32_t* row_ptr, const int32_t* col, int64_t nnz,
+                              int32_t* drow_ptr, hipStream_t s) {
+    if (M > 0 && K > 0) {
+        const unsigned grid = (unsigned)(M < 65536 ? M : 65536);
+        hipLaunchKernelGGL(k_delta_count, dim3(grid), dim3(kSplitThreads), 0, s, M, K, row_ptr, col, nnz, drow_ptr);
+    } else if (M > 0) {
+        // no columns: every row is empty
+        hipLaunchKernelGGL(k_delta_count, dim3(1), dim3(kSplitThreads), 0, s, M, K, row_ptr, col, (int64_t)0,
+                           drow_ptr);
+    }
+    hipLaunchKernelGGL(k_scan_rows, dim3(1), dim3(1024), 0, s, M, drow_ptr);
+    return hipGetLastError();
+}
+
+hipError_t launch_delta_fill(int dt, int64_t M, int64_t K, const int32_t* row_ptr, const int32_t* col,
+                             const void* rvals, int64_t nnz, const int32_t* drow_ptr, uint8_t* dcol, void* dvals,
+                             hipStream_t s) {
+    if (M == 0 || K == 0 || nnz == 0) return hipSuccess;
+    const unsigned grid = (unsigned)(M < 65536 ? M : 65536);
+    SSG_DISPATCH_DT(dt, {
+        using T = typename Store<D>::T;
+        hipLaunchKernelGGL(k_delta_fill<D>, dim3(grid), dim3(kSplitThreads), 0, s, M, K, row_ptr, col,
+                           (const T*)rvals, nnz, drow_ptr, dcol, (T*)dvals);
     });
     return hipGetLastError();
 }

@@ -1,11 +1,11 @@
 // spmm_generic.hip -- the plain-layout SpMM kernels: one thread per output
 // element walking its row's groups (decode nibble -> the two kept positions
-// -> two multiply-adds, the "index picks which two of the four activations
-// pair with the two stored weights" scheme of "Chapter 26 -- Sparsity: The
+// -> two multiply-adds: the 2-bit positions choose the two activations of
+// the four that meet the stored weights, as in "Chapter 26 -- Sparsity: The
 // Hardware View", section "2:4 Fine-Grained Structured Sparsity"), plus the
-// residual CSR term of "How sparse LLM weights cut GPU inference cost without
-// quantization", section "How the three-layer format makes moderate sparsity
-// fast".
+// residual term (CSR or delta-coded) of "How sparse LLM weights cut GPU
+// inference cost without quantization", section "How the three-layer format
+// makes moderate sparsity fast".
 //
 // These kernels take any shape, leading dimension and alignment.  They are
 // the fallback for operands the tiled kernels do not take, and the residual
@@ -30,12 +30,22 @@ __device__ __forceinline__ void mac(typename Acc<DT>::T& acc, const void* a, int
     }
 }
 
-// Residual CSR contribution to C[m, n]; the entry range is clamped to
-// [0, nnz_r) and columns outside [0, K) are skipped, so a corrupt CSR cannot
-// cause an out-of-bounds access.
+// Residual contribution to C[m, n]; the entry range is clamped to
+// [0, nnz_r) and columns outside [0, K) are skipped, so a corrupt residual
+// cannot cause an out-of-bounds access.  A delta-coded residual (dcol set)
+// gives each entry's column as the running sum of the row's gap bytes from
+// column -1; its filler entries hold +0.
 template <int DT>
 __device__ __forceinline__ void residual_row(typename Acc<DT>::T& acc, const SpmmArgs& a, int64_t m, int64_t n) {
     const int64_t lo = max<int64_t>(a.row_ptr[m], 0), hi = min<int64_t>(a.row_ptr[m + 1], a.nnz_r);
+    if (a.dcol) {
+        int64_t k = -1;
+        for (int64_t j = lo; j < hi; ++j) {
+            k += a.dcol[j];
+            if (k >= 0 && k < a.K) mac<DT>(acc, a.rvals, j, a.B, k * a.ldb + n);
+        }
+        return;
+    }
     for (int64_t j = lo; j < hi; ++j) {
         const int64_t k = a.col[j];
         if (k >= 0 && k < a.K) mac<DT>(acc, a.rvals, j, a.B, k * a.ldb + n);

@@ -180,16 +180,18 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const uint8_t* base, int6
 // One direct-to-LDS load: each lane's `BYTES` (4 or 16) from the buffer at
 // byte offset `voff` land at LDS address m0 + lane * BYTES.  Issued as inline
 // assembly so the compiler neither tracks these loads nor inserts its own
-// conservative waits for them; the kernel counts them itself (wait_vm).
+// conservative waits for them; the kernel counts them itself (wait_vm).  The
+// s_nop is the wait state GFX9 needs between an SALU write of M0 and an
+// LDS-DMA load that reads it.
 template <int BYTES>
 __device__ __forceinline__ void dma(__amdgpu_buffer_rsrc_t r, const uint8_t* lds_dst, uint32_t voff) {
     const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(const lds_void*)lds_dst);
     if constexpr (BYTES == 16)
-        asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(m0), "v"(voff), "s"(r)
-                     : "memory");
+        asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(m0), "v"(voff), "s"(r)
+                     : "memory", "m0");
     else
-        asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds" ::"s"(m0), "v"(voff), "s"(r)
-                     : "memory");
+        asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, 0 offen lds" ::"s"(m0), "v"(voff), "s"(r)
+                     : "memory", "m0");
 }
 
 // s_waitcnt vmcnt(N): at most N of this wave's vector-memory operations are

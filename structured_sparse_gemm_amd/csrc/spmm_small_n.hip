@@ -27,9 +27,10 @@
 //   of up to 128 KiB, row-major; the MFMA operand (16 consecutive k of one
 //   column per lane) comes from transposing LDS reads (ds_read_b64_tr_b16 /
 //   _b8), 4 per k-step, shared by the slab's tiles.
-// * The residual CSR rows of the slab are processed by the same workgroup
-//   while the matching B chunk is in LDS: one entry per lane, 16 columns per
-//   lane, a wave reduction per row.
+// * The residual rows of the slab (CSR, or delta-coded gap bytes decoded by
+//   a wave prefix sum) are processed by the same workgroup while the
+//   matching B chunk is in LDS: one entry per lane, 16 columns per lane, a
+//   wave reduction per row.
 // * Partial tiles of the waves are summed through LDS in wave order, so the
 //   fp32 result is the same on every run.
 #include "ssg_device.hpp"
@@ -42,9 +43,10 @@ namespace {
 constexpr int kTMax = 4;                  // 16-row tiles per workgroup
 constexpr int kWaves = 8;
 constexpr int kLdsRes = kTMax * 16 * 16 * 4;   // residual row sums (fp32/int32)
-constexpr int kLdsCursor = 256;                // residual row cursors
+constexpr int kLdsCursor = 512;                // residual row cursors (entry, column before it)
 // B chunk followed by the slab's padded metadata rows for the chunk
 constexpr int kLdsData = 160 * 1024 - kLdsRes - kLdsCursor;
+constexpr int kRingResOff = 160 * 1024 - kLdsRes;       // ring kernel: residual row sums at the top of LDS
 
 template <int DT> struct SN;
 template <> struct SN<DT_F16> {
@@ -149,11 +151,6 @@ __device__ __forceinline__ void stage_b(const SpmmArgs& a, uint8_t* ldsb, int64_
     }
 }
 
-template <int DT>
-__device__ __forceinline__ float res_value(const void* rvals, int64_t j) {
-    return elem_to_f32<DT>(reinterpret_cast<const uint16_t*>(rvals)[j]);
-}
-
 template <int CTRL, typename S>
 __device__ __forceinline__ S dpp_xor(S x) {
     int v;
@@ -213,129 +210,16 @@ __device__ __forceinline__ int transpose_col(int lane) {
     return ((lane & 1) << 3) | ((lane & 2) << 1) | ((lane & 4) >> 1) | ((lane & 8) >> 3);
 }
 
-// Residual rows of the slab owned by this wave (rl = wave + W*j), taken
-// chunk by chunk of K (the columns whose B rows are in LDS).  Columns ascend
-// within a row, so each row keeps a cursor (first entry not yet consumed)
-// across chunks.  A pass loads the next 64*E entries of every one of the
-// wave's rows at once -- one memory round-trip for all of them, issued
-// before the chunk's 2:4 work so it lands meanwhile -- and is then consumed
-// row by row: the entries of the chunk meet their B row in LDS, the 16
-// column sums are reduced across the wave and added to res[row][16].
-template <int DT, int NRW, int E>
-struct ResPass {
-    using Raw = typename std::conditional<DT == DT_I8, int8_t, uint16_t>::type;   // stored width: no widening at load
-    int64_t lo[NRW], hi[NRW];
-    bool open[NRW];
-    int32_t c[NRW][E];
-    Raw vr[NRW][E];
-};
-
-template <int DT, int NRW, int E>
-__device__ __forceinline__ void residual_begin(ResPass<DT, NRW, E>& st, const SpmmArgs& a, const int32_t* cursor,
-                                               int64_t r0, int nrows, bool first_chunk, int wave, int waves) {
-    // all row bounds are read before any is used (rows past the slab read
-    // its last row and are masked)
-    int32_t p0[NRW], p1[NRW];
-#pragma unroll
-    for (int j = 0; j < NRW; ++j) {
-        const int64_t m = r0 + min(wave + waves * j, nrows - 1);
-        p0[j] = a.row_ptr[m];
-        p1[j] = a.row_ptr[m + 1];
-    }
-#pragma unroll
-    for (int j = 0; j < NRW; ++j) {
-        const int rl = wave + waves * j;
-        const bool valid = rl < nrows;
-        st.hi[j] = valid ? min<int64_t>(p1[j], a.nnz_r) : 0;
-        st.lo[j] = valid ? (first_chunk ? max<int64_t>(p0[j], 0) : (int64_t)cursor[rl]) : 0;
-        st.open[j] = st.lo[j] < st.hi[j];
-    }
-}
-
-// Issue one pass of loads.  Lanes past a row's end read entry 0 (the CSR is
-// non-empty while a row is open), so no load sits in a branch; the loaded
-// words are kept as they are and masked only when consumed, so nothing
-// waits for them here.
-template <int DT, int NRW, int E>
-__device__ __forceinline__ void residual_load(ResPass<DT, NRW, E>& st, const SpmmArgs& a, int lane) {
-#pragma unroll
-    for (int j = 0; j < NRW; ++j)
-#pragma unroll
-        for (int e = 0; e < E; ++e) {
-            const int64_t idx = st.lo[j] + 64 * e + lane;
-            const int64_t li = st.open[j] && idx < st.hi[j] ? idx : 0;
-            st.c[j][e] = a.col[li];
-            if constexpr (DT == DT_I8) st.vr[j][e] = reinterpret_cast<const int8_t*>(a.rvals)[li];
-            else st.vr[j][e] = reinterpret_cast<const uint16_t*>(a.rvals)[li];
-        }
-}
-
-// Consume the loaded pass; returns whether any row still has entries of
-// this chunk left (a pass that stopped short of 64*E reached a column of a
-// later chunk or the row's end).
-template <int DT, int NRW, int E>
-__device__ __forceinline__ bool residual_consume(ResPass<DT, NRW, E>& st, const uint8_t* ldsb, void* res,
-                                                 int64_t kc0, int64_t kc1, int wave, int waves, int lane) {
-    constexpr int ES = SN<DT>::ES;
-    using S = typename std::conditional<DT == DT_I8, int32_t, float>::type;
-    bool any = false;
-#pragma unroll
-    for (int j = 0; j < NRW; ++j) {
-        if (!st.open[j]) continue;
-        // B rows of the row's entries in this chunk (row 0 for the others,
-        // whose value is zeroed), all reads in flight before the products
-        uint4 w[E][2];
-        S vv[E];
-        int taken = 0;
-#pragma unroll
-        for (int e = 0; e < E; ++e) {
-            const int64_t idx = st.lo[j] + 64 * e + lane;
-            const bool in = idx < st.hi[j];
-            const int32_t cc = in ? st.c[j][e] : (int32_t)kc1;
-            taken += __popcll(__ballot(cc < kc1));
-            const bool inch = cc >= kc0 && cc < kc1;
-            const uint8_t* brow = ldsb + (inch ? (int)(cc - kc0) : 0) * 16 * ES;
-            w[e][0] = *reinterpret_cast<const uint4*>(brow);
-            if constexpr (ES == 2) w[e][1] = *reinterpret_cast<const uint4*>(brow + 16);
-            if constexpr (DT == DT_I8) vv[e] = inch ? (int32_t)st.vr[j][e] : 0;
-            else vv[e] = inch ? elem_to_f32<DT>(st.vr[j][e]) : 0.0f;
-        }
-        S acc[16];
-#pragma unroll
-        for (int n = 0; n < 16; ++n) acc[n] = S(0);
-#pragma unroll
-        for (int e = 0; e < E; ++e) {
-            if constexpr (DT == DT_I8) {
-                int8_t bv[16];
-                __builtin_memcpy(bv, &w[e][0], 16);
-#pragma unroll
-                for (int n = 0; n < 16; ++n) acc[n] += vv[e] * (int32_t)bv[n];
-            } else {
-                uint16_t bv[16];
-                __builtin_memcpy(bv, &w[e][0], 16);
-                __builtin_memcpy(bv + 8, &w[e][1], 16);
-#pragma unroll
-                for (int n = 0; n < 16; ++n) acc[n] = fmaf(vv[e], elem_to_f32<DT>(bv[n]), acc[n]);
-            }
-        }
-        const S tot = transpose_sum16<S>(acc, lane);
-        const int rl = wave + waves * j;
-        if (lane < 16) reinterpret_cast<S*>(res)[rl * 16 + transpose_col(lane)] += tot;
-        st.lo[j] += taken;
-        st.open[j] = taken == 64 * E && st.lo[j] < st.hi[j];
-        any |= st.open[j];
-    }
-    return any;
-}
-
-template <int DT, int NRW, int E>
-__device__ __forceinline__ void residual_end(const ResPass<DT, NRW, E>& st, int32_t* cursor, int nrows, int wave,
-                                             int waves, int lane) {
-#pragma unroll
-    for (int j = 0; j < NRW; ++j) {
-        const int rl = wave + waves * j;
-        if (rl < nrows && lane == 0) cursor[rl] = (int32_t)st.lo[j];
-    }
+// Inclusive prefix sum over the wave's 64 lanes: four row_shr steps inside
+// each row of 16 lanes, then every lane adds the totals of the rows below.
+__device__ __forceinline__ int wave_incl_sum(int x, int lane) {
+    x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, true);   // row_shr:1
+    x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, true);   // row_shr:2
+    x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, true);   // row_shr:4
+    x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, true);   // row_shr:8
+    const int r0 = __builtin_amdgcn_readlane(x, 15), r1 = __builtin_amdgcn_readlane(x, 31),
+              r2 = __builtin_amdgcn_readlane(x, 47);
+    return x + (lane >= 16 ? r0 : 0) + (lane >= 32 ? r1 : 0) + (lane >= 48 ? r2 : 0);
 }
 
 typedef __attribute__((address_space(3))) void lds_void;
@@ -347,10 +231,22 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, int64_t
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)n, 0x00020000);
 }
 
+// Buffer over an array of `bytes` whose base is ALIGN-aligned, read with
+// loads of at most ALIGN bytes at multiples of their size.  The range is
+// rounded up to ALIGN: a load that holds the array's last bytes is then
+// performed whole (the hardware range check would zero the partial word),
+// and it stays inside the ALIGN-aligned block of the last byte, so it reads
+// only mapped memory; the bytes past the array are masked by the caller.
+template <int ALIGN>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_aligned(const void* base, int64_t bytes) {
+    return rsrc(base, (bytes + ALIGN - 1) / ALIGN * ALIGN);
+}
+
 // Direct-to-LDS load of BYTES (4 or 16) per active lane: lane l's bytes from
 // buffer offset `voff` land at LDS byte address `dst` + l * BYTES (`dst`
-// wave-uniform); an offset past the buffer
-// reads as zero.  Inline assembly, so the compiler does not count it: the
+// wave-uniform, passed in M0); an offset past the buffer reads as zero.
+// GFX9 needs one wait state between an SALU write of M0 and an LDS-DMA load
+// that reads it (else the load may take the previous M0), hence the s_nop.  Inline assembly, so the compiler does not count it: the
 // kernel waits for these loads itself (vmcnt), and issues them before the
 // weight loads the compiler does count, so the compiler's own waits for
 // those (loads complete in order) also cover them.
@@ -358,11 +254,11 @@ template <int BYTES>
 __device__ __forceinline__ void dma(__amdgpu_buffer_rsrc_t r, uint32_t dst, uint32_t voff) {
     const uint32_t m0 = __builtin_amdgcn_readfirstlane(dst);
     if constexpr (BYTES == 16)
-        asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(m0), "v"(voff), "s"(r)
-                     : "memory");
+        asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(m0), "v"(voff), "s"(r)
+                     : "memory", "m0");
     else
-        asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds" ::"s"(m0), "v"(voff), "s"(r)
-                     : "memory");
+        asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, 0 offen lds" ::"s"(m0), "v"(voff), "s"(r)
+                     : "memory", "m0");
 }
 
 template <int N>
@@ -469,18 +365,225 @@ __device__ __forceinline__ void stage_meta(const SpmmArgs& a, uint8_t* ldsm, int
     }
 }
 
+// ---- residual pass ---------------------------------------------------------
+//
+// Residual rows of the slab owned by this wave (rl = wave + W*j), taken
+// chunk by chunk of K (the columns whose B rows are in LDS).  Columns ascend
+// within a row, so each row keeps a cursor (first entry not yet consumed)
+// across chunks.  A pass covers 64*EPL consecutive entries of a row, EPL per
+// lane (lane l: entries ld + 64*EPL*p + EPL*l + i), read with one buffer load
+// per array: the column indices (CSR) or gap bytes (delta-coded), and the
+// values.  Offsets past an array read zero, and entries outside
+// [lo, hi) are masked when consumed, so no load sits in a branch.  NP passes
+// per row are loaded before the chunk's 2:4 work, so they land during it.
+//
+// A delta-coded residual stores each column as its gap from the previous
+// one: a lane sums its EPL gap bytes, a wave prefix sum places the lanes,
+// and the row keeps the column of the entry before the cursor.
+template <int DT, int NRW, int EPL, int NP, bool DELTA>
+struct ResPass {
+    static constexpr int PASS = 64 * EPL;                     // entries per pass
+    static constexpr int CW = DELTA ? 1 : EPL;                // index words per lane per pass
+    static constexpr int VW = (EPL * SN<DT>::ES + 3) / 4;     // value words per lane per pass
+    int32_t lo[NRW], hi[NRW], ld[NRW];                        // entries (nnz < 2^31)
+    bool open[NRW];
+    int32_t base[NRW];                                        // DELTA: column of entry lo - 1 (-1 at row start)
+    uint32_t cw[NRW][NP][CW];
+    uint32_t vw[NRW][NP][VW];
+};
+
+template <int DT, int NRW, int EPL, int NP, bool DELTA>
+__device__ __forceinline__ void residual_begin(ResPass<DT, NRW, EPL, NP, DELTA>& st, const SpmmArgs& a,
+                                               const int32_t* cursor, int64_t r0, int nrows, bool first_chunk,
+                                               int wave, int waves) {
+    // all row bounds are read before any is used (rows past the slab read
+    // its last row and are masked)
+    int32_t p0[NRW], p1[NRW];
+#pragma unroll
+    for (int j = 0; j < NRW; ++j) {
+        const int64_t m = r0 + min(wave + waves * j, nrows - 1);
+        p0[j] = a.row_ptr[m];
+        p1[j] = a.row_ptr[m + 1];
+    }
+#pragma unroll
+    for (int j = 0; j < NRW; ++j) {
+        const int rl = wave + waves * j;
+        const bool valid = rl < nrows;
+        st.hi[j] = valid ? (int32_t)min<int64_t>(p1[j], a.nnz_r) : 0;
+        st.lo[j] = valid ? (first_chunk || cursor == nullptr ? max(p0[j], 0) : cursor[rl]) : 0;
+        st.open[j] = st.lo[j] < st.hi[j];
+        if constexpr (DELTA) st.base[j] = valid && !first_chunk && cursor != nullptr ? cursor[64 + rl] : -1;
+    }
+}
+
+// Issue NP passes of every open row from its cursor (rounded down to a
+// multiple of 4 entries, so every load is aligned to its size).
+template <int DT, int NRW, int EPL, int NP, bool DELTA>
+__device__ __forceinline__ void residual_load(ResPass<DT, NRW, EPL, NP, DELTA>& st, __amdgpu_buffer_rsrc_t rc,
+                                              __amdgpu_buffer_rsrc_t rv, int lane) {
+    using R = ResPass<DT, NRW, EPL, NP, DELTA>;
+    constexpr int ES = SN<DT>::ES, IB = DELTA ? 1 : 4;        // value / index bytes per entry
+#pragma unroll
+    for (int j = 0; j < NRW; ++j) {
+        st.ld[j] = st.lo[j] & ~3;
+#pragma unroll
+        for (int p = 0; p < NP; ++p) {
+            // below 2^31 + 2^12 entries' bytes: the host keeps nnz * IB under 2^31
+            const uint32_t e0 = (uint32_t)st.ld[j] + (uint32_t)(R::PASS * p + EPL * lane);
+            const uint32_t oc = st.open[j] ? e0 * IB : kOob;
+            const uint32_t ov = st.open[j] ? e0 * ES : kOob;
+            if constexpr (DELTA) {
+                if constexpr (EPL == 4) st.cw[j][p][0] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rc, oc, 0, 0);
+                else st.cw[j][p][0] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rc, oc, 0, 0);
+            } else if constexpr (EPL == 4) {
+                const i32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rc, oc, 0, 0);
+                __builtin_memcpy(st.cw[j][p], &v, 16);
+            } else {
+                const i32x2 v = __builtin_amdgcn_raw_buffer_load_b64(rc, oc, 0, 0);
+                __builtin_memcpy(st.cw[j][p], &v, 8);
+            }
+            if constexpr (EPL * ES == 8) {
+                const i32x2 v = __builtin_amdgcn_raw_buffer_load_b64(rv, ov, 0, 0);
+                __builtin_memcpy(st.vw[j][p], &v, 8);
+            } else if constexpr (EPL * ES == 4) {
+                st.vw[j][p][0] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rv, ov, 0, 0);
+            } else {
+                st.vw[j][p][0] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rv, ov, 0, 0);
+            }
+        }
+    }
+}
+
+// Consume the loaded passes, row by row, pass by pass; the row's column sums
+// are reduced across the wave once per row and added to res[row][16].
+// Returns whether a row still has entries of this chunk past its NP passes.
+template <int DT, int NRW, int EPL, int NP, bool DELTA>
+__device__ __forceinline__ bool residual_consume(ResPass<DT, NRW, EPL, NP, DELTA>& st, const uint8_t* ldsb,
+                                                 void* res, int64_t kc0, int64_t kc1, int wave, int waves,
+                                                 int lane) {
+    using R = ResPass<DT, NRW, EPL, NP, DELTA>;
+    constexpr int ES = SN<DT>::ES;
+    using S = typename std::conditional<DT == DT_I8, int32_t, float>::type;
+    bool any = false;
+#pragma unroll
+    for (int j = 0; j < NRW; ++j) {
+        if (!st.open[j]) continue;
+        S acc[16];
+#pragma unroll
+        for (int n = 0; n < 16; ++n) acc[n] = S(0);
+#pragma unroll
+        for (int p = 0; p < NP; ++p) {
+            if (!st.open[j]) break;
+            const int64_t e0 = (int64_t)st.ld[j] + R::PASS * p + EPL * lane;
+            bool v[EPL];
+#pragma unroll
+            for (int i = 0; i < EPL; ++i) v[i] = e0 + i >= st.lo[j] && e0 + i < st.hi[j];
+            int32_t col[EPL];
+            if constexpr (DELTA) {
+                int pre[EPL], sum = 0;
+#pragma unroll
+                for (int i = 0; i < EPL; ++i) {
+                    sum += v[i] ? (int)((st.cw[j][p][0] >> (8 * i)) & 0xFFu) : 0;
+                    pre[i] = sum;
+                }
+                const int incl = wave_incl_sum(sum, lane);
+#pragma unroll
+                for (int i = 0; i < EPL; ++i) col[i] = st.base[j] + (incl - sum) + pre[i];
+            } else {
+#pragma unroll
+                for (int i = 0; i < EPL; ++i) col[i] = (int32_t)st.cw[j][p][i];
+            }
+            // B rows of the pass's entries in this chunk (row 0 for the
+            // others, whose value is zeroed), all reads before the products
+            uint4 w[EPL][2];
+            S vv[EPL];
+            int taken = 0;
+#pragma unroll
+            for (int i = 0; i < EPL; ++i) {
+                const int32_t cc = v[i] ? col[i] : (int32_t)kc1;
+                taken += __popcll(__ballot(cc < kc1));
+                const bool inch = cc >= kc0 && cc < kc1;
+                const uint8_t* brow = ldsb + (inch ? (int)(cc - kc0) : 0) * 16 * ES;
+                w[i][0] = *reinterpret_cast<const uint4*>(brow);
+                if constexpr (ES == 2) w[i][1] = *reinterpret_cast<const uint4*>(brow + 16);
+                if constexpr (DT == DT_I8) {
+                    const int32_t x = (int32_t)(int8_t)(st.vw[j][p][0] >> (8 * i));
+                    vv[i] = inch ? x : 0;
+                } else {
+                    const uint16_t x = (uint16_t)(st.vw[j][p][i >> 1] >> (16 * (i & 1)));
+                    vv[i] = inch ? elem_to_f32<DT>(x) : 0.0f;
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < EPL; ++i) {
+                if constexpr (DT == DT_I8) {
+                    int8_t bv[16];
+                    __builtin_memcpy(bv, &w[i][0], 16);
+#pragma unroll
+                    for (int n = 0; n < 16; ++n) acc[n] += vv[i] * (int32_t)bv[n];
+                } else {
+                    uint16_t bv[16];
+                    __builtin_memcpy(bv, &w[i][0], 16);
+                    __builtin_memcpy(bv + 8, &w[i][1], 16);
+#pragma unroll
+                    for (int n = 0; n < 16; ++n) acc[n] = fmaf(vv[i], elem_to_f32<DT>(bv[n]), acc[n]);
+                }
+            }
+            if constexpr (DELTA) {
+                // the column of the last entry taken is the next base
+                if (taken > 0) {
+                    const int t = st.lo[j] + taken - 1 - (st.ld[j] + R::PASS * p);
+#pragma unroll
+                    for (int i = 0; i < EPL; ++i)
+                        if (t % EPL == i) st.base[j] = __builtin_amdgcn_readlane(col[i], t / EPL);
+                }
+            }
+            st.lo[j] += taken;
+            // the pass was consumed to its end: the row goes on in the next
+            // pass; otherwise it reached a column of a later chunk or its end
+            st.open[j] = st.lo[j] < st.hi[j] && st.lo[j] == st.ld[j] + R::PASS * (p + 1);
+        }
+        const S tot = transpose_sum16<S>(acc, lane);
+        const int rl = wave + waves * j;
+        if (lane < 16) reinterpret_cast<S*>(res)[rl * 16 + transpose_col(lane)] += tot;
+        any |= st.open[j];
+    }
+    return any;
+}
+
+// Rows closed at the end of a chunk that still have entries go on in the next.
+template <int DT, int NRW, int EPL, int NP, bool DELTA>
+__device__ __forceinline__ void residual_reopen(ResPass<DT, NRW, EPL, NP, DELTA>& st) {
+#pragma unroll
+    for (int j = 0; j < NRW; ++j) st.open[j] = st.lo[j] < st.hi[j];
+}
+
+template <int DT, int NRW, int EPL, int NP, bool DELTA>
+__device__ __forceinline__ void residual_end(const ResPass<DT, NRW, EPL, NP, DELTA>& st, int32_t* cursor, int nrows,
+                                             int wave, int waves, int lane) {
+#pragma unroll
+    for (int j = 0; j < NRW; ++j) {
+        const int rl = wave + waves * j;
+        if (rl < nrows && lane == 0) {
+            cursor[rl] = st.lo[j];
+            if constexpr (DELTA) cursor[64 + rl] = st.base[j];
+        }
+    }
+}
+
 // One workgroup owns a slab of <= 16*TM rows and all of K.  Wave w takes the
 // k-steps w, w + W, w + 2W, ... (W waves), so the waves walk K together and
 // share each B chunk.  A wave keeps the sparse fragments of its next P
 // k-steps in flight in a register ring and refills a slot as soon as the
 // slot's k-step has been multiplied: the weight stream of every CU stays
 // P x TM KiB per wave deep from the first cycle to the last.
-template <int DT, int TM, int P>
+template <int DT, int TM, int P, bool DELTA>
 __global__ void __launch_bounds__(kWaves * 64) k_spmm_small_n(SpmmArgs a, int rows_per_wg, int chunk_steps,
                                                               int vec_b, int vec_m) {
     constexpr int W = kWaves;
     constexpr int kResRows = (16 * TM + W - 1) / W;   // residual rows per wave (dealt round-robin)
-    constexpr int kResE = kResRows > 4 ? 2 : 4;          // residual entries per lane per row per pass
+    constexpr int kResEPL = kResRows > 4 ? 2 : 4;        // residual entries per lane per pass
+    constexpr int kResNP = kResRows > 4 ? 1 : 2;         // residual passes per row loaded at once
     using T = SN<DT>;
     using Acc = AccT<DT>;
     using S = typename std::conditional<DT == DT_I8, int32_t, float>::type;
@@ -498,6 +601,10 @@ __global__ void __launch_bounds__(kWaves * 64) k_spmm_small_n(SpmmArgs a, int ro
     const int64_t ksteps = a.K / T::KS;
     const bool residual = a.row_ptr != nullptr;
     const int q = lane >> 4, rl = lane & 15;
+    // residual arrays as buffers (the host keeps each under 2^31 bytes and
+    // aligns it to 4 entries' bytes)
+    const __amdgpu_buffer_rsrc_t rcol = DELTA ? rsrc_aligned<4>(a.dcol, a.nnz_r) : rsrc_aligned<16>(a.col, a.nnz_r * 4);
+    const __amdgpu_buffer_rsrc_t rval = rsrc_aligned<4 * T::ES>(a.rvals, a.nnz_r * T::ES);
 
     // sparse operand of lane l for k-step g, tile t: row r0 + 16t + l%16,
     // stored values [q*VALS/4, (q+1)*VALS/4) of the k-step, q = l/16
@@ -537,11 +644,11 @@ __global__ void __launch_bounds__(kWaves * 64) k_spmm_small_n(SpmmArgs a, int ro
         // this wave's B and metadata loads have landed (with the ring's first
         // loads, which the first multiply waits for anyway)
         wait_vm<0>();
-        // the chunk's first residual pass is in flight during its 2:4 work
-        ResPass<DT, kResRows, kResE> rp;
+        // the chunk's first residual passes are in flight during its 2:4 work
+        ResPass<DT, kResRows, kResEPL, kResNP, DELTA> rp;
         if (residual) {
             residual_begin(rp, a, cursor, r0, nrows, c == 0, wave, W);
-            residual_load(rp, a, lane);
+            residual_load(rp, rcol, rval, lane);
         }
         if (!vec_b) stage_b<DT>(a, ldsb, c0 * T::KS, csteps * T::KS, false);
         if (!vec_m) stage_meta<DT>(a, ldsm, r0, nrows, c0, csteps, pitch, false);
@@ -573,7 +680,7 @@ __global__ void __launch_bounds__(kWaves * 64) k_spmm_small_n(SpmmArgs a, int ro
         }
         if (residual) {
             while (residual_consume(rp, ldsb, res, c0 * T::KS, (c0 + csteps) * T::KS, wave, W, lane))
-                residual_load(rp, a, lane);
+                residual_load(rp, rcol, rval, lane);
             residual_end(rp, cursor, nrows, wave, W, lane);
         }
     }
@@ -598,16 +705,23 @@ __global__ void __launch_bounds__(kWaves * 64) k_spmm_small_n(SpmmArgs a, int ro
     }
 }
 
-// Variant for products without a residual whose B is one contiguous K x 16
-// block.  The slab's metadata rows (all of K) are staged once, in 256-byte
-// row segments, behind the only barrier before the final reduction.  After
-// that every wave fetches what its k-steps need on its own -- the two 1 KiB
-// pieces of B rows (direct to a private LDS slot) and the sparse fragments
-// (to registers) -- as buffer loads from inline assembly.  A k-step beyond
-// K or a row beyond the slab uses an offset past its buffer, which reads
-// zero, so every wave issues the same GOPS loads per k-step and one
-// hand-counted wait per k-step is exact.
-template <int DT, int TM, int P>
+// Variant for products whose B is one contiguous K x 16 block.  The slab's
+// metadata rows (all of K) are staged once, in 256-byte row segments,
+// behind the only barrier before the final reduction.  After that every
+// wave fetches what its k-steps need on its own -- the two 1 KiB pieces of
+// B rows (direct to a private LDS slot) and the sparse fragments (to
+// registers) -- as buffer loads from inline assembly.  A k-step beyond K or
+// a row beyond the slab uses an offset past its buffer, which reads zero, so
+// every wave issues the same GOPS loads per k-step and one hand-counted wait
+// per k-step is exact.
+//
+// With a residual (RES), the 2:4 sums go to LDS instead of C and the
+// residual follows as an epilogue: the whole LDS (but the row sums) then
+// holds chunks of B in turn, and each wave's residual rows are consumed
+// chunk by chunk, their first passes loaded while the 2:4 stream drains and
+// the next chunk's while its B rows are staged.  A workgroup that finishes
+// its weight stream early runs its epilogue while others still stream.
+template <int DT, int TM, int P, bool RES, bool DELTA>
 __global__ void __launch_bounds__(kWaves * 64) k_spmm_small_n_ring(SpmmArgs a, int rows_per_wg) {
     constexpr int W = kWaves;
     using T = SN<DT>;
@@ -658,6 +772,13 @@ __global__ void __launch_bounds__(kWaves * 64) k_spmm_small_n_ring(SpmmArgs a, i
     dma_meta<DT>(a, lds_addr + (uint32_t)(W * P * BSTEP), r0, nrows, 0, (int)ksteps, pitch, wave);
 #pragma unroll
     for (int u = 0; u < P; ++u) issue(wave + (int64_t)W * u, u);
+    // residual rows of this wave: their bounds are read now, behind the
+    // first k-steps' loads
+    constexpr int kResRows = (16 * TM + W - 1) / W;
+    constexpr int kResEPL = kResRows > 4 ? 2 : 4;
+    constexpr int kResNP = kResRows > 4 ? 1 : 2;
+    ResPass<DT, kResRows, kResEPL, kResNP, DELTA> rp;
+    if constexpr (RES) residual_begin(rp, a, nullptr, r0, nrows, true, wave, W);
     wait_vm<P * GOPS>();                                // this wave's metadata segments have landed
     lds_barrier();                                      // and every other wave's
     const int nw = ksteps > wave ? (int)((ksteps - wave + W - 1) / W) : 0;
@@ -691,12 +812,25 @@ __global__ void __launch_bounds__(kWaves * 64) k_spmm_small_n_ring(SpmmArgs a, i
             }
         }
     }
-    // the loads past the wave's last k-step land before the LDS is reused
+    // residual: the first passes go out while the weight stream drains
+    const __amdgpu_buffer_rsrc_t rcol = DELTA ? rsrc_aligned<4>(a.dcol, a.nnz_r)
+                                              : rsrc_aligned<16>(a.col, a.nnz_r * 4);
+    const __amdgpu_buffer_rsrc_t rval = rsrc_aligned<4 * T::ES>(a.rvals, a.nnz_r * T::ES);
+    if constexpr (RES) residual_load(rp, rcol, rval, lane);
+    // the loads past the wave's last k-step land before the LDS is reused --
+    // and before their registers are: the compiler takes an asm load's
+    // output as written when the load is issued, so the ring stays in use
+    // until the wait (else a late load could overwrite a reassigned register)
     wait_vm<0>();
+#pragma unroll
+    for (int u = 0; u < P; ++u)
+#pragma unroll
+        for (int t = 0; t < TM; ++t) asm volatile("" ::"v"(av[u][t]));
     lds_barrier();
 
     // fixed-order reduction of the waves' partial tiles
     Acc* red = reinterpret_cast<Acc*>(lds);
+    S* res = reinterpret_cast<S*>(lds + kRingResOff);   // RES: the slab's row sums [64][16]
 #pragma unroll
     for (int t = 0; t < TM; ++t) red[(wave * kTMax + t) * 64 + lane] = acc[t];
     lds_barrier();
@@ -707,39 +841,90 @@ __global__ void __launch_bounds__(kWaves * 64) k_spmm_small_n_ring(SpmmArgs a, i
 #pragma unroll
         for (int w = 0; w < W; ++w) sum += reinterpret_cast<const S*>(red)[((w * kTMax + t) * 64 + ln) * 4 + r];
         const int row = 16 * t + 4 * (ln >> 4) + r, col = ln & 15;
-        if (row < nrows && col < a.N) reinterpret_cast<S*>(a.C)[(r0 + row) * a.ldc + col] = sum;
+        if constexpr (RES) res[row * 16 + col] = sum;
+        else if (row < nrows && col < a.N) reinterpret_cast<S*>(a.C)[(r0 + row) * a.ldc + col] = sum;
+    }
+    if constexpr (RES) {
+        // B in chunks over the LDS below the row sums
+        constexpr int64_t kChunkRows = kRingResOff / (16 * T::ES);
+        for (int64_t k0 = 0; k0 < a.K; k0 += kChunkRows) {
+            const int rows = (int)min<int64_t>(kChunkRows, a.K - k0);
+            lds_barrier();                                  // the previous chunk (or the partial tiles) consumed
+            dma_b<DT>(a, lds_addr, k0, rows, wave);
+            wait_vm<0>();                                   // this wave's B rows and residual passes
+            lds_barrier();
+            while (residual_consume(rp, lds, res, k0, k0 + rows, wave, W, lane)) residual_load(rp, rcol, rval, lane);
+            if (k0 + rows < a.K) {
+                residual_reopen(rp);
+                residual_load(rp, rcol, rval, lane);
+            }
+        }
+        lds_barrier();
+        for (int i = threadIdx.x; i < nrows * 16; i += blockDim.x) {
+            const int row = i >> 4, col = i & 15;
+            if (col < a.N) reinterpret_cast<S*>(a.C)[(r0 + row) * a.ldc + col] = res[i];
+        }
     }
 }
 
-template <int TM> constexpr int kRingP = TM == 4 ? 6 : 8;
+template <int TM> constexpr int kRingP = TM == 4 ? 6 : 8;      // deepest ring
+template <int TM> constexpr int kRingPLow = TM == 4 ? 4 : 6;   // when the deepest does not fit
 
 // LDS of the ring variant: the waves' B slots and the slab's metadata rows
 template <int DT, int TM>
-int64_t ring_lds(const SpmmArgs& a) {
+int64_t ring_lds(const SpmmArgs& a, int P) {
     using T = SN<DT>;
-    return (int64_t)kWaves * kRingP<TM> * 16 * T::ES * T::KS + 16 * TM * ((a.K / T::KS) * T::META + 4);
+    return (int64_t)kWaves * P * 16 * T::ES * T::KS + 16 * TM * ((a.K / T::KS) * T::META + 4);
+}
+
+// Ring depth for this problem: the deepest that fits (0: none).  Products
+// with a residual take the shallower ring, which leaves more registers for
+// the epilogue.
+template <int DT, int TM>
+int ring_depth(const SpmmArgs& a) {
+    constexpr int64_t kLds = 160 * 1024;
+    if (a.row_ptr == nullptr && ring_lds<DT, TM>(a, kRingP<TM>) <= kLds) return kRingP<TM>;
+    return ring_lds<DT, TM>(a, kRingPLow<TM>) <= kLds ? kRingPLow<TM> : 0;
+}
+
+template <int DT, int TM, int P>
+void launch_ring_p(const SpmmArgs& a, int64_t G, int64_t rows_per_wg, hipStream_t s) {
+    if (a.row_ptr == nullptr) {
+        const unsigned shm = (unsigned)ring_lds<DT, TM>(a, P);
+        hipLaunchKernelGGL((k_spmm_small_n_ring<DT, TM, P, false, false>), dim3((unsigned)G), dim3(64 * kWaves), shm,
+                           s, a, (int)rows_per_wg);
+    } else if constexpr (P == kRingPLow<TM>) {
+        // the residual epilogue uses the whole LDS
+        if (a.dcol != nullptr)
+            hipLaunchKernelGGL((k_spmm_small_n_ring<DT, TM, P, true, true>), dim3((unsigned)G), dim3(64 * kWaves),
+                               160 * 1024, s, a, (int)rows_per_wg);
+        else
+            hipLaunchKernelGGL((k_spmm_small_n_ring<DT, TM, P, true, false>), dim3((unsigned)G), dim3(64 * kWaves),
+                               160 * 1024, s, a, (int)rows_per_wg);
+    }
 }
 
 template <int DT, int TM>
 hipError_t launch_ring(const SpmmArgs& a, int64_t G, int64_t rows_per_wg, hipStream_t s) {
-    constexpr int P = kRingP<TM>;
-    const unsigned shm = (unsigned)ring_lds<DT, TM>(a);
-    hipLaunchKernelGGL((k_spmm_small_n_ring<DT, TM, P>), dim3((unsigned)G), dim3(64 * kWaves), shm, s, a,
-                       (int)rows_per_wg);
+    const int P = ring_depth<DT, TM>(a);
+    if (P == kRingP<TM>) launch_ring_p<DT, TM, kRingP<TM>>(a, G, rows_per_wg, s);
+    else if (P == kRingPLow<TM>) launch_ring_p<DT, TM, kRingPLow<TM>>(a, G, rows_per_wg, s);
+    else return hipErrorInvalidConfiguration;   // excluded by ring_ok
     return hipGetLastError();
 }
 
-// The barrier-free variant takes products without a residual whose B is one
-// contiguous K x 16 block and whose buffers are addressed with 31-bit offsets.
+// The barrier-free variant takes products whose B is one contiguous K x 16
+// block, whose ring fits the LDS and whose buffers are addressed with
+// 31-bit offsets (a residual has passed supported_t: aligned arrays, 31-bit
+// offsets).
 template <int DT>
 bool ring_ok(const SpmmArgs& a, int tm) {
     using T = SN<DT>;
     const uintptr_t bp = reinterpret_cast<uintptr_t>(a.B), mp = reinterpret_cast<uintptr_t>(a.meta);
-    const int64_t lds = tm == 1 ? ring_lds<DT, 1>(a) : tm == 2 ? ring_lds<DT, 2>(a) : tm == 3 ? ring_lds<DT, 3>(a)
-                                                                                            : ring_lds<DT, 4>(a);
-    return a.row_ptr == nullptr && a.N == 16 && a.ldb == 16 && bp % 16 == 0 && mp % 4 == 0 && a.ldm % 4 == 0 &&
-           lds <= 160 * 1024 && a.K * 16 * T::ES < 0x7fffffff && a.M * a.ldv * T::ES < 0x7fffffff &&
-           a.M * a.ldm < 0x7fffffff;
+    const int P = tm == 1 ? ring_depth<DT, 1>(a) : tm == 2 ? ring_depth<DT, 2>(a) : tm == 3 ? ring_depth<DT, 3>(a)
+                                                                                          : ring_depth<DT, 4>(a);
+    return P > 0 && a.N == 16 && a.ldb == 16 && bp % 16 == 0 && mp % 4 == 0 && a.ldm % 4 == 0 &&
+           a.K * 16 * T::ES < 0x7fffffff && a.M * a.ldv * T::ES < 0x7fffffff && a.M * a.ldm < 0x7fffffff;
 }
 
 template <int DT>
@@ -747,31 +932,58 @@ bool supported_t(const SpmmArgs& a) {
     using T = SN<DT>;
     const uintptr_t v = reinterpret_cast<uintptr_t>(a.vals);
     // vals rows 16-byte aligned; every index fits the kernel's 32-bit LDS math
-    return a.N >= 1 && a.N <= 16 && a.K > 0 && a.K % T::KS == 0 && v % 16 == 0 && (a.ldv * T::ES) % 16 == 0 &&
-           a.M > 0;
+    const bool dense_ok = a.N >= 1 && a.N <= 16 && a.K > 0 && a.K % T::KS == 0 && v % 16 == 0 &&
+                          (a.ldv * T::ES) % 16 == 0 && a.M > 0;
+    if (!dense_ok || a.row_ptr == nullptr) return dense_ok;
+    // residual arrays: aligned for the widest per-lane load (4 entries) and
+    // addressed with 31-bit byte offsets
+    const uintptr_t ip = a.dcol ? reinterpret_cast<uintptr_t>(a.dcol) : reinterpret_cast<uintptr_t>(a.col);
+    const uintptr_t rp = reinterpret_cast<uintptr_t>(a.rvals);
+    const int64_t ib = a.dcol ? 1 : 4;
+    return ip % (4 * ib) == 0 && rp % (4 * T::ES) == 0 && a.nnz_r * ib < 0x7fff0000 && a.nnz_r * T::ES < 0x7fff0000;
 }
 
 // Ring depth by tiles per slab: about 16 fragments (KiB) in flight per wave.
 template <int TM> constexpr int kRing = TM == 1 ? 16 : TM == 2 ? 8 : 4;
+
+// K-steps one LDS chunk holds: the chunk's B rows (16 columns) and the
+// padded metadata rows of the slab's 16*TM rows share the LDS data region.
+template <int DT, int TM>
+constexpr int64_t chunk_capacity() {
+    using T = SN<DT>;
+    return (kLdsData - 16 * TM * 4) / (16 * T::ES * T::KS + 16 * TM * T::META);
+}
+
+// Whether TM tiles can walk K: in one chunk, or in chunks that each hold a
+// multiple of W*P k-steps (so ring slot i % P follows the wave's k-steps
+// across chunks).
+template <int DT, int TM>
+bool chunks_fit(int64_t ksteps) {
+    return ksteps <= chunk_capacity<DT, TM>() || chunk_capacity<DT, TM>() >= kWaves * kRing<TM>;
+}
+
+static_assert(chunk_capacity<DT_F16, 4>() >= kWaves * kRing<4> && chunk_capacity<DT_I8, 4>() >= kWaves * kRing<4>,
+              "the widest slab must walk any K");
 
 template <int DT, int TM>
 hipError_t launch_tm(const SpmmArgs& a, int64_t G, int64_t rows_per_wg, hipStream_t s) {
     using T = SN<DT>;
     constexpr int P = kRing<TM>;
     const int64_t ksteps = a.K / T::KS;
-    // chunks of K: the chunk's B rows (16 columns) and the padded metadata
-    // rows of the slab's 16*TM rows share the LDS data region; a chunk that
-    // is not the last holds a multiple of W*P k-steps
-    const int64_t max_steps = (kLdsData - 16 * TM * 4) / (16 * T::ES * T::KS + 16 * TM * T::META);
+    const int64_t max_steps = chunk_capacity<DT, TM>();
     int64_t chunk = ksteps;
     if (chunk > max_steps) chunk = max_steps / (kWaves * P) * (kWaves * P);
-    if (chunk <= 0) return hipErrorInvalidConfiguration;   // excluded by the caller's choice of TM
+    if (chunk <= 0) return hipErrorInvalidConfiguration;   // excluded by launch_t (chunks_fit)
     const uintptr_t bp = reinterpret_cast<uintptr_t>(a.B), mp = reinterpret_cast<uintptr_t>(a.meta);
     const bool vec_b = a.N == 16 && a.ldb == 16 && bp % 16 == 0 &&
                        a.K * 16 * T::ES < 0x7fffffff;                // one contiguous block of B
     const bool vec_m = mp % 4 == 0 && a.ldm % 4 == 0 && (a.M - 1) * a.ldm + (a.K + 7) / 8 < 0x7fffffff;
-    hipLaunchKernelGGL((k_spmm_small_n<DT, TM, P>), dim3((unsigned)G), dim3(64 * kWaves), 0, s, a, (int)rows_per_wg,
-                       (int)chunk, (int)vec_b, (int)vec_m);
+    if (a.row_ptr != nullptr && a.dcol != nullptr)
+        hipLaunchKernelGGL((k_spmm_small_n<DT, TM, P, true>), dim3((unsigned)G), dim3(64 * kWaves), 0, s, a,
+                           (int)rows_per_wg, (int)chunk, (int)vec_b, (int)vec_m);
+    else
+        hipLaunchKernelGGL((k_spmm_small_n<DT, TM, P, false>), dim3((unsigned)G), dim3(64 * kWaves), 0, s, a,
+                           (int)rows_per_wg, (int)chunk, (int)vec_b, (int)vec_m);
     return hipGetLastError();
 }
 
@@ -791,7 +1003,14 @@ hipError_t launch_t(const SpmmArgs& a, hipStream_t s) {
             default: return launch_ring<DT, 4>(a, G, rows_per_wg, s);
         }
     }
-    switch ((rows_per_wg + 15) / 16) {
+    // a slab of fewer tiles than its deepest ring can chunk runs as a wider
+    // slab (its rows past rows_per_wg are masked)
+    int tm = (int)((rows_per_wg + 15) / 16);
+    const int64_t ksteps = a.K / SN<DT>::KS;
+    if (tm == 1 && !chunks_fit<DT, 1>(ksteps)) tm = 2;
+    if (tm == 2 && !chunks_fit<DT, 2>(ksteps)) tm = 3;
+    if (tm == 3 && !chunks_fit<DT, 3>(ksteps)) tm = 4;
+    switch (tm) {
         case 1: return launch_tm<DT, 1>(a, G, rows_per_wg, s);
         case 2: return launch_tm<DT, 2>(a, G, rows_per_wg, s);
         case 3: return launch_tm<DT, 3>(a, G, rows_per_wg, s);

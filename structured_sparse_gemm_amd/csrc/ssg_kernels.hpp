@@ -23,6 +23,13 @@ hipError_t launch_split_count(int dt, int64_t M, int64_t K, const void* A, int64
 hipError_t launch_split_fill(int dt, int64_t M, int64_t K, const void* A, int64_t lda, void* vals, int64_t ldv,
                              uint8_t* meta, int64_t ldm, const int32_t* row_ptr, int32_t* col, void* rvals, bool vec,
                              hipStream_t s);
+// Delta-coded residual from a CSR: pass 1 writes the scanned entry counts
+// (fillers included) into drow_ptr, pass 2 the gap bytes and values.
+hipError_t launch_delta_count(int64_t M, int64_t K, const int32_t* row_ptr, const int32_t* col, int64_t nnz,
+                              int32_t* drow_ptr, hipStream_t s);
+hipError_t launch_delta_fill(int dt, int64_t M, int64_t K, const int32_t* row_ptr, const int32_t* col,
+                             const void* rvals, int64_t nnz, const int32_t* drow_ptr, uint8_t* dcol, void* dvals,
+                             hipStream_t s);
 
 // Sparse operand of one SpMM call.
 struct SpmmArgs {
@@ -30,8 +37,9 @@ struct SpmmArgs {
     int64_t M, N, K;
     const void* vals; int64_t ldv;
     const uint8_t* meta; int64_t ldm;
-    const int32_t* row_ptr;     // residual CSR (nullptr: none)
-    const int32_t* col;
+    const int32_t* row_ptr;     // residual (nullptr: none)
+    const int32_t* col;         // CSR column indices, or nullptr when
+    const uint8_t* dcol;        // the residual is delta-coded (gap bytes)
     const void* rvals;
     int64_t nnz_r;
     const void* B; int64_t ldb;

@@ -122,7 +122,7 @@ ssg::SpmmArgs make_args(int ab, int64_t M, int64_t N, int64_t K, const void* val
     a.dt = to_dt(ab);
     a.M = M; a.N = N; a.K = K;
     a.vals = vals; a.ldv = ldv; a.meta = meta; a.ldm = ldm;
-    a.row_ptr = nullptr; a.col = nullptr; a.rvals = nullptr; a.nnz_r = 0;
+    a.row_ptr = nullptr; a.col = nullptr; a.dcol = nullptr; a.rvals = nullptr; a.nnz_r = 0;
     a.B = B; a.ldb = ldb; a.C = C; a.ldc = ldc;
     return a;
 }
@@ -249,8 +249,65 @@ int ssg_spmm_2to4_residual_ex(int algo, int ab, int c, int64_t M, int64_t N, int
     const size_t need = ssg_spmm_workspace_bytes(ab, M, N, K);
     if (ws_bytes < need || (need > 0 && !ws)) return fail(SSG_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
     ssg::SpmmArgs a = make_args(ab, M, N, K, vals, ldv, meta, ldm, B, ldb, C, ldc);
-    a.row_ptr = row_ptr; a.col = col; a.rvals = rvals; a.nnz_r = nnz_r;
+    // an empty residual adds nothing: the plain 2:4 product (the residual
+    // kernels may read entry 0 of a non-empty residual unconditionally)
+    if (nnz_r > 0) { a.row_ptr = row_ptr; a.col = col; a.rvals = rvals; a.nnz_r = nnz_r; }
     return run_spmm(algo, a, (hipStream_t)stream);
+}
+
+int ssg_residual_delta_count(int64_t M, int64_t K, const int32_t* row_ptr, const int32_t* col, int64_t nnz_r,
+                             int32_t* drow_ptr, void* stream) {
+    if (M < 0 || K < 0) return fail(SSG_ERR_SHAPE, "negative size M=%lld K=%lld", (long long)M, (long long)K);
+    if (nnz_r < 0 || nnz_r > INT32_MAX) return fail(SSG_ERR_FORMAT, "nnz_r=%lld out of range", (long long)nnz_r);
+    if (!drow_ptr) return fail(SSG_ERR_NULL, "drow_ptr is NULL");
+    if (M > 0 && !row_ptr) return fail(SSG_ERR_NULL, "row_ptr is NULL");
+    if (nnz_r > 0 && !col) return fail(SSG_ERR_NULL, "col is NULL with nnz_r > 0");
+    // every entry plus at most one filler per 255 columns of each row
+    if (M > 0 && nnz_r + M * (K / 255 + 1) > INT32_MAX)
+        return fail(SSG_ERR_SHAPE, "delta-coded residual of %lld rows x %lld columns may not fit int32 indices",
+                    (long long)M, (long long)K);
+    hipError_t e = ssg::launch_delta_count(M, K, row_ptr, col, nnz_r, drow_ptr, (hipStream_t)stream);
+    return e == hipSuccess ? SSG_OK : hip_fail(e, "delta_count launch");
+}
+
+int ssg_residual_delta_fill(int dt, int64_t M, int64_t K, const int32_t* row_ptr, const int32_t* col,
+                            const void* rvals, int64_t nnz_r, const int32_t* drow_ptr, uint8_t* dcol, void* dvals,
+                            void* stream) {
+    if (!in_dtype(dt)) return fail(SSG_ERR_DTYPE, "element type %d is not SSG_F16, SSG_BF16 or SSG_I8", dt);
+    if (M < 0 || K < 0) return fail(SSG_ERR_SHAPE, "negative size M=%lld K=%lld", (long long)M, (long long)K);
+    if (nnz_r < 0 || nnz_r > INT32_MAX) return fail(SSG_ERR_FORMAT, "nnz_r=%lld out of range", (long long)nnz_r);
+    if (M > 0 && (!row_ptr || !drow_ptr)) return fail(SSG_ERR_NULL, "row_ptr or drow_ptr is NULL");
+    if (nnz_r > 0 && (!col || !rvals || !dcol || !dvals))
+        return fail(SSG_ERR_NULL, "col, rvals, dcol or dvals is NULL with nnz_r > 0");
+    hipError_t e = ssg::launch_delta_fill(to_dt(dt), M, K, row_ptr, col, rvals, nnz_r, drow_ptr, dcol, dvals,
+                                          (hipStream_t)stream);
+    return e == hipSuccess ? SSG_OK : hip_fail(e, "delta_fill launch");
+}
+
+int ssg_spmm_2to4_residual_delta_ex(int algo, int ab, int c, int64_t M, int64_t N, int64_t K, const void* vals,
+                                    int64_t ldv, const uint8_t* meta, int64_t ldm, const int32_t* drow_ptr,
+                                    const uint8_t* dcol, const void* dvals, int64_t nnz_d, const void* B,
+                                    int64_t ldb, void* C, int64_t ldc, void* ws, size_t ws_bytes, void* stream) {
+    int rc = check_spmm(ab, c, M, N, K, vals, ldv, meta, ldm, B, ldb, C, ldc);
+    if (rc) return rc;
+    if (nnz_d < 0 || nnz_d > INT32_MAX) return fail(SSG_ERR_FORMAT, "nnz_d=%lld out of range", (long long)nnz_d);
+    if (M > 0 && !drow_ptr) return fail(SSG_ERR_NULL, "drow_ptr is NULL");
+    if (nnz_d > 0 && (!dcol || !dvals)) return fail(SSG_ERR_NULL, "dcol or dvals is NULL with nnz_d > 0");
+    const size_t need = ssg_spmm_workspace_bytes(ab, M, N, K);
+    if (ws_bytes < need || (need > 0 && !ws)) return fail(SSG_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
+    ssg::SpmmArgs a = make_args(ab, M, N, K, vals, ldv, meta, ldm, B, ldb, C, ldc);
+    // an empty residual adds nothing: the plain 2:4 product (the residual
+    // kernels may read entry 0 of a non-empty residual unconditionally)
+    if (nnz_d > 0) { a.row_ptr = drow_ptr; a.dcol = dcol; a.rvals = dvals; a.nnz_r = nnz_d; }
+    return run_spmm(algo, a, (hipStream_t)stream);
+}
+
+int ssg_spmm_2to4_residual_delta(int ab, int c, int64_t M, int64_t N, int64_t K, const void* vals, int64_t ldv,
+                                 const uint8_t* meta, int64_t ldm, const int32_t* drow_ptr, const uint8_t* dcol,
+                                 const void* dvals, int64_t nnz_d, const void* B, int64_t ldb, void* C, int64_t ldc,
+                                 void* ws, size_t ws_bytes, void* stream) {
+    return ssg_spmm_2to4_residual_delta_ex(SSG_ALGO_AUTO, ab, c, M, N, K, vals, ldv, meta, ldm, drow_ptr, dcol, dvals,
+                                           nnz_d, B, ldb, C, ldc, ws, ws_bytes, stream);
 }
 
 int ssg_spmm_2to4_residual(int ab, int c, int64_t M, int64_t N, int64_t K, const void* vals, int64_t ldv,

@@ -77,6 +77,28 @@ def test_dense_argument_errors(lib):
     assert lib.ssg_split_count(F16, 1 << 20, 1 << 14, FAKE, 1 << 14, FAKE, None) == _abi.SSG_ERR_SHAPE
 
 
+def test_delta_code_argument_errors(lib):
+    assert lib.ssg_residual_delta_count(4, 64, FAKE, FAKE, 3, None, None) == _abi.SSG_ERR_NULL
+    assert lib.ssg_residual_delta_count(4, 64, None, FAKE, 3, FAKE, None) == _abi.SSG_ERR_NULL
+    assert lib.ssg_residual_delta_count(4, 64, FAKE, None, 3, FAKE, None) == _abi.SSG_ERR_NULL
+    assert lib.ssg_residual_delta_count(-1, 64, FAKE, FAKE, 3, FAKE, None) == _abi.SSG_ERR_SHAPE
+    assert lib.ssg_residual_delta_count(4, 64, FAKE, FAKE, -1, FAKE, None) == _abi.SSG_ERR_FORMAT
+    # worst-case coded length beyond int32
+    assert lib.ssg_residual_delta_count(1 << 20, 1 << 20, FAKE, FAKE, 3, FAKE, None) == _abi.SSG_ERR_SHAPE
+    assert lib.ssg_residual_delta_fill(F32, 4, 64, FAKE, FAKE, FAKE, 3, FAKE, FAKE, FAKE, None) == _abi.SSG_ERR_DTYPE
+    assert lib.ssg_residual_delta_fill(F16, 4, 64, FAKE, FAKE, FAKE, 3, FAKE, None, FAKE, None) == _abi.SSG_ERR_NULL
+    assert lib.ssg_residual_delta_fill(F16, 4, 64, FAKE, FAKE, FAKE, 3, None, FAKE, FAKE, None) == _abi.SSG_ERR_NULL
+    # the product: the same host checks as the CSR form, plus its own pointers
+    args = (F16, F32, 16, 16, 64, FAKE, 32, FAKE, 8)
+    tail = (FAKE, 16, FAKE, 16, None, 0, None)
+    assert lib.ssg_spmm_2to4_residual_delta(*args, None, FAKE, FAKE, 5, *tail) == _abi.SSG_ERR_NULL
+    assert lib.ssg_spmm_2to4_residual_delta(*args, FAKE, None, FAKE, 5, *tail) == _abi.SSG_ERR_NULL
+    assert lib.ssg_spmm_2to4_residual_delta(*args, FAKE, FAKE, FAKE, -2, *tail) == _abi.SSG_ERR_FORMAT
+    assert lib.ssg_spmm_2to4_residual_delta(I8, F32, 16, 16, 64, FAKE, 32, FAKE, 8, FAKE, FAKE, FAKE, 5,
+                                            *tail) == _abi.SSG_ERR_DTYPE
+    assert lib.ssg_spmm_2to4_residual_delta_ex(9, *args, FAKE, FAKE, FAKE, 5, *tail) == _abi.SSG_ERR_ALGO
+
+
 def test_last_error_names_the_problem(lib):
     assert lib.ssg_compress_2to4(F16, 4, 8, FAKE, 7, FAKE, 4, FAKE, 1, None) == _abi.SSG_ERR_STRIDE
     assert "lda=7" in lib.ssg_last_error().decode()
@@ -129,6 +151,6 @@ def test_python_binding_has_no_cpu_fallback():
 def test_python_binding_names_match_the_abi():
     for name in declared_functions():
         if name in ("ssg_abi_version", "ssg_status_str", "ssg_last_error", "ssg_vals_cols", "ssg_meta_cols",
-                    "ssg_spmm_2to4_ex", "ssg_spmm_2to4_residual_ex"):
+                    "ssg_spmm_2to4_ex", "ssg_spmm_2to4_residual_ex", "ssg_spmm_2to4_residual_delta_ex"):
             continue
         assert hasattr(ssg, name), name

@@ -197,6 +197,155 @@ def test_spmm_residual_matches_oracle(algo, dt, shape):
     check_product(dt, C.cpu().numpy(), cref, sref, "residual %s %s" % (dt, shape))
 
 
+# ------------------------------------------------------------------ delta-coded residual
+
+def far_csr(M, K, seed, per_row=6):
+    """CSR rows with a few columns spread over K, so gaps above 255 (fillers)
+    are common, plus empty rows."""
+    rng = np.random.default_rng(seed)
+    cols = [np.sort(rng.choice(K, size=int(rng.integers(0, per_row + 1)), replace=False)) for _ in range(M)]
+    row_ptr = np.concatenate([[0], np.cumsum([len(c) for c in cols])]).astype(np.int32)
+    col = np.concatenate(cols).astype(np.int32)
+    return row_ptr, col
+
+
+def dev_or_empty(x: np.ndarray, dt: str = None) -> torch.Tensor:
+    if dt is None:
+        return torch.from_numpy(np.ascontiguousarray(x)).cuda()
+    if len(x) == 0:
+        return torch.empty(0, dtype=W.TORCH_DTYPE[dt], device="cuda")
+    return to_dev(x, dt)
+
+
+@pytest.mark.parametrize("dt", DTS)
+@pytest.mark.parametrize("case", ["split", "far", "empty_rows", "one_row"])
+def test_delta_encode_bitexact(dt, case):
+    if case == "split":
+        K = 1100
+        a = U.random_matrix(dt, 70, K, "sparse", seed=71)
+        _, _, row_ptr, col, rvals = oracle.split(dt, a)
+    elif case == "far":
+        K = 5000
+        row_ptr, col = far_csr(300, K, 5)
+        rvals = U.random_matrix(dt, 1, max(len(col), 1), "normal", 6)[0, :len(col)]
+    elif case == "empty_rows":
+        K = 64
+        row_ptr, col = np.zeros(9, np.int32), np.zeros(0, np.int32)
+        rvals = np.zeros(0, U.store_dtype(dt))
+    else:   # one long row: several 256-entry blocks of the encoder, gaps of 1 to 600
+        K = 200000
+        rng = np.random.default_rng(9)
+        col = np.cumsum(rng.integers(1, 601, size=700)).astype(np.int32)
+        col = col[col < K]
+        row_ptr = np.array([0, len(col)], np.int32)
+        rvals = U.random_matrix(dt, 1, len(col), "normal", 10)[0]
+    want = oracle.delta_encode(dt, row_ptr, col, rvals, K)
+    got = ssg.delta_encode(dev_or_empty(row_ptr), dev_or_empty(col), dev_or_empty(rvals, dt), K)
+    assert np.array_equal(got[0].cpu().numpy(), want[0])
+    assert np.array_equal(got[1].cpu().numpy(), want[1])
+    assert np.array_equal(to_host(got[2]) if len(want[2]) else np.zeros(0, U.store_dtype(dt)), want[2])
+
+
+DELTA_SHAPES = [(16, 64, 16), (40, 256, 16), (130, 2048, 16), (40, 8192, 16), (64, 128, 40), (200, 512, 256)]
+
+
+@pytest.mark.parametrize("algo", ALGOS, ids=ALGO_IDS)
+@pytest.mark.parametrize("dt", DTS)
+@pytest.mark.parametrize("shape", DELTA_SHAPES)
+def test_spmm_residual_delta_matches_oracle(algo, dt, shape):
+    M, K, N = shape
+    a = U.random_matrix(dt, M, K, "sparse", seed=M * K + 1)
+    b = U.random_matrix(dt, K, N, "normal", seed=N + 1)
+    vals, meta, row_ptr, col, rvals = oracle.split(dt, a)
+    drow_ptr, dcol, dvals = oracle.delta_encode(dt, row_ptr, col, rvals, K)
+    C = run_algo(algo, lambda: ssg.spmm_residual_delta(to_dev(vals, dt), dev_or_empty(meta), dev_or_empty(drow_ptr),
+                                                       dev_or_empty(dcol), dev_or_empty(dvals, dt), to_dev(b, dt),
+                                                       algo=algo))
+    cref, sref = oracle.spmm_residual_delta(dt, vals, meta, drow_ptr, dcol, dvals, b, K)
+    check_product(dt, C.cpu().numpy(), cref, sref, "residual delta %s %s" % (dt, shape))
+
+
+@pytest.mark.parametrize("algo", ALGOS, ids=ALGO_IDS)
+@pytest.mark.parametrize("dt", DTS)
+@pytest.mark.parametrize("shape", [(48, 4096, 16), (33, 16384, 16)])
+def test_spmm_residual_delta_with_fillers(algo, dt, shape):
+    # a 2:4 layer plus a residual whose entries lie far apart (many fillers),
+    # across several LDS chunks of K for the small-N kernel
+    M, K, N = shape
+    a = U.random_matrix(dt, M, K, "normal", seed=K + 5)
+    b = U.random_matrix(dt, K, N, "normal", seed=K + 6)
+    vals, meta = oracle.compress(dt, a)
+    row_ptr, col = far_csr(M, K, K, per_row=12)
+    rvals = U.random_matrix(dt, 1, max(len(col), 1), "normal", 7)[0, :len(col)]
+    drow_ptr, dcol, dvals = oracle.delta_encode(dt, row_ptr, col, rvals, K)
+    assert (dcol == 255).sum() > len(col) // 2
+    C = run_algo(algo, lambda: ssg.spmm_residual_delta(to_dev(vals, dt), dev_or_empty(meta), dev_or_empty(drow_ptr),
+                                                       dev_or_empty(dcol), dev_or_empty(dvals, dt), to_dev(b, dt),
+                                                       algo=algo))
+    cref, sref = oracle.spmm_residual(dt, vals, meta, row_ptr, col, rvals, b, K)
+    check_product(dt, C.cpu().numpy(), cref, sref, "residual delta fillers %s %s" % (dt, shape))
+
+
+@pytest.mark.parametrize("dt", DTS)
+@pytest.mark.parametrize("shape", [(40, 8192, 16), (20, 12288, 8), (100, 10240, 16)])
+def test_spmm_residual_small_n_long_k(dt, shape):
+    # narrow slabs whose K needs several LDS chunks run as wider slabs
+    M, K, N = shape
+    a = U.random_matrix(dt, M, K, "sparse", seed=K + M)
+    b = U.random_matrix(dt, K, N, "normal", seed=K + N)
+    vals, meta, row_ptr, col, rvals = oracle.split(dt, a)
+    C = ssg.spmm_residual(to_dev(vals, dt), dev_or_empty(meta), dev_or_empty(row_ptr), dev_or_empty(col),
+                          dev_or_empty(rvals, dt), to_dev(b, dt), algo=ssg.SSG_ALGO_SMALL_N)
+    cref, sref = oracle.spmm_residual(dt, vals, meta, row_ptr, col, rvals, b, K)
+    check_product(dt, C.cpu().numpy(), cref, sref, "residual long K %s %s" % (dt, shape))
+
+
+@pytest.mark.parametrize("algo", ALGOS, ids=ALGO_IDS)
+@pytest.mark.parametrize("dt", ["f16", "bf16"])
+@pytest.mark.parametrize("delta", [False, True])
+@pytest.mark.parametrize("shape", [(40, 256, 16), (33, 512, 16), (70, 1024, 8), (17, 8192, 16)])   # nnz % 4: 2, 3, 0, 3
+def test_spmm_residual_exact_small_integers(algo, dt, delta, shape):
+    # small integers: every product and partial sum is exact in fp32, so the
+    # fp16/bf16 result must equal the oracle's exactly -- a dropped or
+    # doubled residual entry cannot hide inside the rounding tolerance
+    M, K, N = shape
+    rng = np.random.default_rng(M * K + N)
+    x = rng.integers(-3, 4, size=(M, K)) * (rng.random((M, K)) < 0.5)
+    a = U.encode(dt, x)
+    b = U.encode(dt, rng.integers(-3, 4, size=(K, N)))
+    vals, meta, row_ptr, col, rvals = oracle.split(dt, a)
+    if delta:
+        row_ptr, col, rvals = oracle.delta_encode(dt, row_ptr, col, rvals, K)
+    fn = ssg.spmm_residual_delta if delta else ssg.spmm_residual
+    C = run_algo(algo, lambda: fn(to_dev(vals, dt), dev_or_empty(meta), dev_or_empty(row_ptr), dev_or_empty(col),
+                                  dev_or_empty(rvals, dt), to_dev(b, dt), algo=algo))
+    want = x.astype(np.int64) @ U.to_f64(dt, b).astype(np.int64)
+    assert np.array_equal(C.cpu().numpy().astype(np.float64), want.astype(np.float64))
+
+
+@pytest.mark.parametrize("dt", DTS)
+@pytest.mark.parametrize("delta", [False, True])
+def test_spmm_residual_unaligned_arrays(dt, delta):
+    # residual arrays at odd element offsets: the tiled kernels do not take
+    # them (SSG_ERR_ALGO when forced), AUTO runs them on the generic kernel
+    M, K, N = 48, 512, 16
+    a = U.random_matrix(dt, M, K, "sparse", seed=77)
+    b = U.random_matrix(dt, K, N, "normal", seed=78)
+    vals, meta, row_ptr, col, rvals = oracle.split(dt, a)
+    if delta:
+        row_ptr, col, rvals = oracle.delta_encode(dt, row_ptr, col, rvals, K)
+    cbuf = dev_or_empty(np.concatenate([col[:1], col]))[1:]
+    vbuf = dev_or_empty(np.concatenate([rvals[:1], rvals]), dt)[1:]
+    args = (to_dev(vals, dt), dev_or_empty(meta), dev_or_empty(row_ptr), cbuf, vbuf, to_dev(b, dt))
+    fn = ssg.spmm_residual_delta if delta else ssg.spmm_residual
+    with pytest.raises(ssg.SsgError):
+        fn(*args, algo=ssg.SSG_ALGO_SMALL_N)
+    C = fn(*args)
+    cref, sref = (oracle.spmm_residual_delta if delta else oracle.spmm_residual)(dt, vals, meta, row_ptr, col, rvals,
+                                                                                 b, K)
+    check_product(dt, C.cpu().numpy(), cref, sref, "unaligned residual %s" % dt)
+
+
 @pytest.mark.parametrize("dt", ["f16", "bf16"])
 def test_identity_B_gives_the_pruned_matrix_exactly(dt):
     K = 256
@@ -308,6 +457,13 @@ def test_full_size_workload(key):
         C = ssg.spmm(vals, meta, B)
     else:
         C = ssg.spmm_residual(vals, meta, row_ptr, col, rvals, B)
+        # the delta-coded form of the same residual, encoded on the GPU from
+        # the GPU's split: bit-exact with the oracle's code, same product
+        drow_ptr, dcol, dvals = ssg.delta_encode(row_ptr, col, rvals, w.K)
+        d = oracle.delta_encode(w.dtype, *residual, w.K)
+        assert np.array_equal(drow_ptr.cpu().numpy(), d[0]) and np.array_equal(dcol.cpu().numpy(), d[1])
+        assert np.array_equal(to_host(dvals), d[2])
+        Cd = ssg.spmm_residual_delta(vals, meta, drow_ptr, dcol, dvals, B).cpu().numpy()
     C = C.cpu().numpy()
     if w.M * w.N <= 1 << 16:
         cref, sref = (oracle.spmm(w.dtype, r[0], r[1], b, w.K) if residual is None
@@ -317,3 +473,6 @@ def test_full_size_workload(key):
         ms, ns = sample_entries(w.M, w.N, 3000, seed=w.index)
         cref, sref = oracle.spmm_entries(w.dtype, r[0], r[1], b, w.K, ms, ns, residual=residual)
         check_product(w.dtype, C[ms, ns], cref, sref, key)
+        if residual is not None:
+            dref, dsref = oracle.spmm_entries(w.dtype, r[0], r[1], b, w.K, ms, ns, residual=d, delta=True)
+            check_product(w.dtype, Cd[ms, ns], dref, dsref, key + " delta")
