@@ -251,6 +251,76 @@ def bench_workload(key: str, iters: int, read_GBps: float, delta: bool = False, 
     return r
 
 
+def crossover(iters: int) -> dict:
+    """Unstructured sparsity against dense and 2:4 at the fp16 decode shape
+    M = K = 8192, N = 16: for each density, the vendor dense GEMM on the
+    matrix with its zeros, the plain CSR and delta-coded sparse products,
+    and the exact 2:4 + residual split of the same matrix.  Operand copies
+    (>= 1 GiB) are rotated so the Infinity Cache serves no repeated reads."""
+    import numpy as np
+    import torch
+
+    import structured_sparse_gemm_amd as ssg
+    M = K = 8192
+    N = 16
+    g = torch.Generator(device="cuda")
+    g.manual_seed(5000)
+    B = torch.randn((K, N), generator=g, device="cuda").half()
+    stream = torch.cuda.current_stream()
+    out = torch.empty((M, N), dtype=torch.float32, device="cuda")
+
+    def timed(base, launch):
+        nbytes = sum(t.numel() * t.element_size() for t in base)
+        copies = max(1, int(np.ceil((1 << 30) / nbytes)))
+        sets = [base] + [tuple(t.clone() for t in base) for _ in range(copies - 1)]
+        n = max(iters, copies)
+        for i in range(n):
+            launch(sets[i % copies])
+        torch.cuda.synchronize()
+        t = time_kernel(lambda i: launch(sets[i % copies]), n, stream)
+        del sets
+        torch.cuda.empty_cache()
+        return t * 1e6, nbytes
+
+    rows = []
+    for d in (0.002, 0.005, 0.01, 0.02, 0.05, 0.1, 0.2, 0.3, 0.5):
+        A = torch.randn((M, K), generator=g, device="cuda") * 0.02
+        A = torch.where(torch.rand((M, K), generator=g, device="cuda") < d, A, torch.zeros((), device="cuda"))
+        A = A.half()
+        nz = A.nonzero()                                   # row-major order: columns ascend within a row
+        row_ptr = torch.zeros(M + 1, dtype=torch.int32, device="cuda")
+        row_ptr[1:] = torch.cumsum(torch.bincount(nz[:, 0], minlength=M), 0).int()
+        col = nz[:, 1].int().contiguous()
+        vals = A[nz[:, 0], nz[:, 1]].contiguous()
+        del nz
+        dl = ssg.delta_encode(row_ptr, col, vals, K)
+        sp = ssg.split(A)
+        ref = A.float() @ B.float()
+        r = {"density": d, "nnz": int(col.numel()), "delta_entries": int(dl[1].numel())}
+        r["dense_us"], r["dense_bytes"] = timed((A,), lambda o: torch.matmul(o[0], B))
+        r["csr_us"], r["csr_bytes"] = timed((row_ptr, col, vals), lambda o: ssg.ssg_spmm_csr(*o, B, out))
+        err_csr = float((out - ref).abs().max() / ref.abs().max())
+        r["delta_us"], r["delta_bytes"] = timed(dl, lambda o: ssg.ssg_spmm_csr_delta(*o, B, out))
+        err_delta = float((out - ref).abs().max() / ref.abs().max())
+        r["split_us"], r["split_bytes"] = timed(sp, lambda o: ssg.ssg_spmm_2to4_residual(*o, B, out))
+        err_split = float((out - ref).abs().max() / ref.abs().max())
+        r["max_rel_err_vs_fp32_dense"] = max(err_csr, err_delta, err_split)
+        rows.append(r)
+        print("crossover: density %.3f: dense %.1f us, csr %.1f us, delta %.1f us, 2:4+residual %.1f us"
+              % (d, r["dense_us"], r["csr_us"], r["delta_us"], r["split_us"]), file=sys.stderr, flush=True)
+        del A, row_ptr, col, vals, dl, sp, ref
+        torch.cuda.empty_cache()
+
+    def below(key):
+        ok = [r["density"] for r in rows if r[key] < r["dense_us"]]
+        return max(ok) if ok else None
+    return {"study": "unstructured sparsity vs dense vs 2:4 at the fp16 decode shape M=K=8192, N=16",
+            "timing": "HIP events around back-to-back launches, >= 1 GiB of operand copies rotated",
+            "rows": rows,
+            "sparse_faster_than_dense_up_to_density": {"csr": below("csr_us"), "delta": below("delta_us"),
+                                                        "split": below("split_us")}}
+
+
 def main() -> int:
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
@@ -264,6 +334,8 @@ def main() -> int:
     p.add_argument("--calib-copy", action="store_true",
                    help="first run a plain elementwise copy of 256 MiB (read 256 MiB, write 256 MiB) three times, "
                         "outside the timed region: the reference for scaling HBM byte counters")
+    p.add_argument("--crossover", action="store_true",
+                   help="instead of the benchmark, run the unstructured-sparsity crossover study and print its JSON")
     args = p.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus %d)" % args.gpus,
@@ -277,6 +349,10 @@ def main() -> int:
     if not torch.cuda.is_available():
         print("bench.py needs a ROCm device", file=sys.stderr)
         return 1
+
+    if args.crossover:
+        print(json.dumps(crossover(args.workload_iters or 100)))
+        return 0
 
     if args.calib_copy:
         src = torch.ones(64 << 20, dtype=torch.float32, device="cuda")

@@ -197,6 +197,21 @@ int ssg_spmm_2to4_residual_delta(int ab, int c, int64_t M, int64_t N, int64_t K,
                                  int64_t nnz_d, const void* B, int64_t ldb, void* C, int64_t ldc,
                                  void* ws, size_t ws_bytes, void* stream);
 
+/* Unstructured sparse x dense, the baseline the 2:4 format is weighed
+ * against ("Chapter 26 -- Sparsity: The Hardware View", sections "Why
+ * Hardware Wants Dense, Regular Data" and "The Honest Numbers on
+ * Unstructured Sparsity"): C = S x B for a sparse S [M, K] given as a CSR
+ * (row_ptr, col ascending within each row, vals) or delta-coded (as
+ * above), with no 2:4 layer.  Same (input, output) pairs and accumulation
+ * as ssg_spmm_2to4; nnz / nnz_d must equal the last row pointer (trusted).
+ * N <= 16 with B a contiguous K x 16 block runs on the small-N kernel,
+ * anything else on the generic one. */
+int ssg_spmm_csr(int ab, int c, int64_t M, int64_t N, int64_t K, const int32_t* row_ptr, const int32_t* col,
+                 const void* vals, int64_t nnz, const void* B, int64_t ldb, void* C, int64_t ldc, void* stream);
+int ssg_spmm_csr_delta(int ab, int c, int64_t M, int64_t N, int64_t K, const int32_t* drow_ptr, const uint8_t* dcol,
+                       const void* dvals, int64_t nnz_d, const void* B, int64_t ldb, void* C, int64_t ldc,
+                       void* stream);
+
 /* As the SpMM calls above with an explicit algorithm (ssg_algo). */
 int ssg_spmm_2to4_ex(int algo, int ab, int c, int64_t M, int64_t N, int64_t K,
                      const void* vals, int64_t ldv, const uint8_t* meta, int64_t ldm,

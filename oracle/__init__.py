@@ -87,6 +87,8 @@ def _load():
             lib.orc_delta_fill.argtypes = [ctypes.c_int, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp]
             lib.orc_spmm_residual_delta.argtypes = lib.orc_spmm_residual.argtypes
             lib.orc_spmm_entries_delta.argtypes = lib.orc_spmm_entries.argtypes
+            lib.orc_spmm_csr.argtypes = [ctypes.c_int, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _i64, _vp, _vp, _vp,
+                                         _i64]
             lib.orc_num_threads.restype = ctypes.c_int
             _lib = lib
     return _lib
@@ -251,6 +253,27 @@ def spmm(dt: str, vals, meta, B, K: int):
 
 def spmm_residual(dt: str, vals, meta, row_ptr, col, rvals, B, K: int):
     return _mm(dt, vals, meta, B, K, (row_ptr, col, rvals))
+
+
+def spmm_csr(dt: str, row_ptr, col, vals, B, K: int):
+    """C = S @ B for an unstructured sparse S given as CSR: (C fp64, S) or (C int64, None)."""
+    B = _mat(B, dt)
+    row_ptr = np.ascontiguousarray(row_ptr, dtype=np.int32)
+    col = np.ascontiguousarray(col, dtype=np.int32)
+    vals = np.ascontiguousarray(vals, dtype=_store_dtype(dt))
+    M, N = row_ptr.shape[0] - 1, B.shape[1]
+    if B.shape[0] != K:
+        raise OracleError("B has %d rows, K is %d" % (B.shape[0], K))
+    if dt == "i8":
+        C, S = np.zeros((M, N), dtype=np.int64), None
+        Cf, Ci = None, C
+    else:
+        C, S = np.zeros((M, N), dtype=np.float64), np.zeros((M, N), dtype=np.float64)
+        Cf, Ci = C, None
+    _check(_load().orc_spmm_csr(DTYPES[dt], M, N, K, _p(row_ptr), _p(col) if col.size else None,
+                                _p(vals) if vals.size else None, _p(B), _ld(B) if K > 0 else max(N, 1),
+                                _p(Cf), _p(Ci), _p(S), max(N, 1)), "spmm_csr")
+    return C, S
 
 
 def spmm_residual_delta(dt: str, vals, meta, drow_ptr, dcol, dvals, B, K: int):

@@ -482,6 +482,48 @@ static int entries_impl(int dt, int64_t M, int64_t N, int64_t K,
     return rc;
 }
 
+/* ---- unstructured sparse x dense product ----
+ * [P3] sections "Why Hardware Wants Dense, Regular Data" and "The Honest
+ * Numbers on Unstructured Sparsity" set the unstructured baseline the 2:4
+ * format is weighed against: a sparse matrix stored as its non-zeros with
+ * their column indices.  C[m,n] = sum over the row's entries j, in CSR
+ * order, of vals[j] * B[col[j], n] (fp64 / int64), with the bound S. */
+int orc_spmm_csr(int dt, int64_t M, int64_t N, int64_t K, const int32_t* row_ptr, const int32_t* col,
+                 const void* vals, const void* B, int64_t ldb, double* Cf, int64_t* Ci, double* S, int64_t ldc) {
+    if (!valid_dtype(dt)) return ORC_EDTYPE;
+    if (M < 0 || N < 0 || K < 0) return ORC_ESHAPE;
+    if (!row_ptr) return ORC_ENULL;
+    if (M > 0 && row_ptr[M] > 0 && (!col || !vals)) return ORC_ENULL;
+    if (K > 0 && N > 0 && !B) return ORC_ENULL;
+    if (M > 0 && N > 0 && (dt == ORC_I8 ? !Ci : !Cf)) return ORC_ENULL;
+    if (ldb < N || ldc < N) return ORC_ESTRIDE;
+    for (int64_t m = 0; m < M; ++m)
+        if (row_ptr[m + 1] < row_ptr[m]) return ORC_EFORMAT;
+    for (int64_t m = 0; m < M; ++m) {
+        for (int64_t n = 0; n < N; ++n) {
+            double acc = 0.0, s = 0.0;
+            int64_t acci = 0;
+            for (int64_t j = row_ptr[m]; j < row_ptr[m + 1]; ++j) {
+                int64_t k = col[j];
+                if (k < 0 || k >= K) return ORC_EFORMAT;
+                if (dt == ORC_I8) {
+                    acci += elem_i64(vals, j) * elem_i64(B, k * ldb + n);
+                } else {
+                    double t = elem_f64(dt, vals, j) * elem_f64(dt, B, k * ldb + n);
+                    acc += t;
+                    s += fabs(t);
+                }
+            }
+            if (dt == ORC_I8) Ci[m * ldc + n] = acci;
+            else {
+                Cf[m * ldc + n] = acc;
+                if (S) S[m * ldc + n] = s;
+            }
+        }
+    }
+    return ORC_OK;
+}
+
 int orc_spmm_entries(int dt, int64_t M, int64_t N, int64_t K,
                      const void* vals, int64_t ldv, const uint8_t* meta, int64_t ldm,
                      const int32_t* row_ptr, const int32_t* col, const void* rvals,

@@ -120,6 +120,12 @@ int orc_spmm_residual_delta(int dt, int64_t M, int64_t N, int64_t K,
                             const int32_t* drow_ptr, const uint8_t* dcol, const void* dvals,
                             const void* B, int64_t ldb, double* Cf, int64_t* Ci, double* S, int64_t ldc);
 
+/* Unstructured sparse x dense: C[m,n] = sum over row m's CSR entries j of
+ * vals[j] * B[col[j], n], in CSR order (fp64 with the bound S; int64 for
+ * int8).  Columns must lie in [0, K) (else ORC_EFORMAT). */
+int orc_spmm_csr(int dt, int64_t M, int64_t N, int64_t K, const int32_t* row_ptr, const int32_t* col,
+                 const void* vals, const void* B, int64_t ldb, double* Cf, int64_t* Ci, double* S, int64_t ldc);
+
 /* Selected outputs only: for e < n_entries, (m, n) = (ms[e], ns[e]); writes
  * Cf[e]/Ci[e] and S[e].  row_ptr may be NULL (no residual). */
 int orc_spmm_entries(int dt, int64_t M, int64_t N, int64_t K,

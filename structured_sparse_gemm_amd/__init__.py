@@ -26,7 +26,8 @@ __all__ = [
     "spmm_residual_delta", "vals_cols", "meta_cols",
     "ssg_prune_2to4", "ssg_compress_2to4", "ssg_decompress_2to4", "ssg_split_count", "ssg_split_fill",
     "ssg_residual_delta_count", "ssg_residual_delta_fill", "ssg_spmm_workspace_bytes", "ssg_spmm_2to4",
-    "ssg_spmm_2to4_residual", "ssg_spmm_2to4_residual_delta", "ssg_spmm_select_algo",
+    "ssg_spmm_2to4_residual", "ssg_spmm_2to4_residual_delta", "ssg_spmm_select_algo", "ssg_spmm_csr",
+    "ssg_spmm_csr_delta", "spmm_csr", "spmm_csr_delta",
     "SSG_ALGO_AUTO", "SSG_ALGO_GENERIC", "SSG_ALGO_SMALL_N", "SSG_ALGO_LARGE_N", "library_path",
 ]
 
@@ -191,6 +192,24 @@ def ssg_spmm_2to4_residual_delta(vals, meta, drow_ptr, dcol, dvals, B, C, ws=Non
                                                   _stream(C, stream)), "ssg_spmm_2to4_residual_delta")
 
 
+def ssg_spmm_csr(row_ptr, col, vals, B, C, stream=None) -> None:
+    ab = _dtype(vals)
+    M, N, K = row_ptr.numel() - 1, B.shape[1], B.shape[0]
+    nnz = int(col.numel()) if col is not None else 0
+    _check(_lib().ssg_spmm_csr(ab, _OUT[ab][0], M, N, K, _ptr(row_ptr, "row_ptr"), _ptr(col, "col"),
+                               _ptr(vals, "vals"), nnz, _ptr(B, "B"), _ld(B, "B"), _ptr(C, "C"), _ld(C, "C"),
+                               _stream(C, stream)), "ssg_spmm_csr")
+
+
+def ssg_spmm_csr_delta(drow_ptr, dcol, dvals, B, C, stream=None) -> None:
+    ab = _dtype(dvals)
+    M, N, K = drow_ptr.numel() - 1, B.shape[1], B.shape[0]
+    nnz = int(dcol.numel()) if dcol is not None else 0
+    _check(_lib().ssg_spmm_csr_delta(ab, _OUT[ab][0], M, N, K, _ptr(drow_ptr, "drow_ptr"), _ptr(dcol, "dcol"),
+                                     _ptr(dvals, "dvals"), nnz, _ptr(B, "B"), _ld(B, "B"), _ptr(C, "C"),
+                                     _ld(C, "C"), _stream(C, stream)), "ssg_spmm_csr_delta")
+
+
 def ssg_spmm_select_algo(vals, meta, B, C) -> int:
     return int(_lib().ssg_spmm_select_algo(_dtype(vals), vals.shape[0], B.shape[1], B.shape[0], _ptr(vals, "vals"),
                                            _ld(vals, "vals"), _ptr(meta, "meta"), _ld(meta, "meta"), _ptr(B, "B"),
@@ -274,4 +293,20 @@ def spmm_residual_delta(vals, meta, drow_ptr, dcol, dvals, B, algo: int = SSG_AL
     ab = _dtype(vals)
     C = torch.empty((vals.shape[0], B.shape[1]), dtype=_OUT[ab][1], device=vals.device) if out is None else out
     ssg_spmm_2to4_residual_delta(vals, meta, drow_ptr, dcol, dvals, B, C, algo=algo)
+    return C
+
+
+def spmm_csr(row_ptr, col, vals, B, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """C = S @ B for an unstructured sparse S given as CSR (no 2:4 layer)."""
+    ab = _dtype(vals)
+    C = torch.empty((row_ptr.numel() - 1, B.shape[1]), dtype=_OUT[ab][1], device=B.device) if out is None else out
+    ssg_spmm_csr(row_ptr, col, vals, B, C)
+    return C
+
+
+def spmm_csr_delta(drow_ptr, dcol, dvals, B, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """C = S @ B for an unstructured sparse S in the delta-coded form (no 2:4 layer)."""
+    ab = _dtype(dvals)
+    C = torch.empty((drow_ptr.numel() - 1, B.shape[1]), dtype=_OUT[ab][1], device=B.device) if out is None else out
+    ssg_spmm_csr_delta(drow_ptr, dcol, dvals, B, C)
     return C

@@ -46,6 +46,8 @@ SIGNATURES = {
                                           _vp, _i64, _vp, _i64, _vp, _sz, _vp]),
     "ssg_spmm_2to4_residual_delta_ex": (_i, [_i, _i, _i, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _vp, _vp,
                                              _i64, _vp, _i64, _vp, _i64, _vp, _sz, _vp]),
+    "ssg_spmm_csr": (_i, [_i, _i, _i64, _i64, _i64, _vp, _vp, _vp, _i64, _vp, _i64, _vp, _i64, _vp]),
+    "ssg_spmm_csr_delta": (_i, [_i, _i, _i64, _i64, _i64, _vp, _vp, _vp, _i64, _vp, _i64, _vp, _i64, _vp]),
     "ssg_spmm_select_algo": (_i, [_i, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64]),
 }
 

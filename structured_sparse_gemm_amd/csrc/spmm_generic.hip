@@ -61,7 +61,8 @@ __global__ void __launch_bounds__(256) k_spmm_generic(SpmmArgs a) {
         AT acc = AT(0);
         const uint8_t* mrow = a.meta + m * a.ldm;
         const int64_t vbase = m * a.ldv;
-        for (int64_t g = 0; g < a.K / 4; ++g) {
+        // no 2:4 layer (vals == nullptr): an unstructured sparse product
+        for (int64_t g = 0; a.vals != nullptr && g < a.K / 4; ++g) {
             const uint32_t nib = (mrow[g >> 1] >> (4 * (g & 1))) & 0xFu;
             mac<DT>(acc, a.vals, vbase + 2 * g, a.B, (4 * g + (nib & 3u)) * a.ldb + n);
             mac<DT>(acc, a.vals, vbase + 2 * g + 1, a.B, (4 * g + (nib >> 2)) * a.ldb + n);

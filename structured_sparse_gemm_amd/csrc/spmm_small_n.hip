@@ -600,6 +600,7 @@ __global__ void __launch_bounds__(kWaves * 64) k_spmm_small_n(SpmmArgs a, int ro
     const int nrows = (int)min<int64_t>(rows_per_wg, a.M - r0);
     const int64_t ksteps = a.K / T::KS;
     const bool residual = a.row_ptr != nullptr;
+    const bool l24 = a.vals != nullptr;                 // false: the residual alone (unstructured product)
     const int q = lane >> 4, rl = lane & 15;
     // residual arrays as buffers (the host keeps each under 2^31 bytes and
     // aligns it to 4 entries' bytes)
@@ -636,8 +637,8 @@ __global__ void __launch_bounds__(kWaves * 64) k_spmm_small_n(SpmmArgs a, int ro
         // metadata: waiting for the staging loads then also waits for them
         // (loads complete in order), but the weight stream is already running.
         if (vec_b) dma_b<DT>(a, lds_addr, c0 * T::KS, csteps * T::KS, wave);
-        if (vec_m) dma_meta<DT>(a, lds_addr + (uint32_t)(ldsm - lds), r0, nrows, c0, csteps, pitch, wave);
-        if (c == 0) {
+        if (vec_m && l24) dma_meta<DT>(a, lds_addr + (uint32_t)(ldsm - lds), r0, nrows, c0, csteps, pitch, wave);
+        if (c == 0 && l24) {
 #pragma unroll
             for (int u = 0; u < P; ++u) load_a(wave + (int64_t)W * u, ring[u]);
         }
@@ -651,13 +652,13 @@ __global__ void __launch_bounds__(kWaves * 64) k_spmm_small_n(SpmmArgs a, int ro
             residual_load(rp, rcol, rval, lane);
         }
         if (!vec_b) stage_b<DT>(a, ldsb, c0 * T::KS, csteps * T::KS, false);
-        if (!vec_m) stage_meta<DT>(a, ldsm, r0, nrows, c0, csteps, pitch, false);
+        if (!vec_m && l24) stage_meta<DT>(a, ldsm, r0, nrows, c0, csteps, pitch, false);
         lds_barrier();
 
         // this wave's k-steps of the chunk: local kk = wave + W*i; a full
         // chunk holds a multiple of W*P k-steps, so ring slot i % P belongs
         // to the wave's global k-step sequence across chunks
-        const int nw = csteps > wave ? (csteps - wave + W - 1) / W : 0;
+        const int nw = l24 && csteps > wave ? (csteps - wave + W - 1) / W : 0;
         for (int i0 = 0; i0 < nw; i0 += P) {
 #pragma unroll
             for (int u = 0; u < P; ++u) {
@@ -751,7 +752,7 @@ __global__ void __launch_bounds__(kWaves * 64) k_spmm_small_n_ring(SpmmArgs a, i
     for (int t = 0; t < TM; ++t)
         voff[t] = 16 * t + rl < nrows ? (uint32_t)((16 * t + rl) * a.ldv * T::ES + q * 16) : kOob;
 
-    i32x4 av[P][TM];   // native vector registers, so they can be tied to the wait below
+    i32x4 av[P][TM] = {};   // native vector registers, so they can be tied to the waits below
     // k-step g of this wave into ring slot u
     auto issue = [&](int64_t g, int u) {
         const bool in = g < ksteps;
@@ -769,9 +770,14 @@ __global__ void __launch_bounds__(kWaves * 64) k_spmm_small_n_ring(SpmmArgs a, i
     Acc acc[TM];
 #pragma unroll
     for (int t = 0; t < TM; ++t) acc[t] = Acc{0, 0, 0, 0};
-    dma_meta<DT>(a, lds_addr + (uint32_t)(W * P * BSTEP), r0, nrows, 0, (int)ksteps, pitch, wave);
+    // without a 2:4 layer (an unstructured product of the residual alone)
+    // the weight stream is empty
+    const bool l24 = a.vals != nullptr;
+    if (l24) {
+        dma_meta<DT>(a, lds_addr + (uint32_t)(W * P * BSTEP), r0, nrows, 0, (int)ksteps, pitch, wave);
 #pragma unroll
-    for (int u = 0; u < P; ++u) issue(wave + (int64_t)W * u, u);
+        for (int u = 0; u < P; ++u) issue(wave + (int64_t)W * u, u);
+    }
     // residual rows of this wave: their bounds are read now, behind the
     // first k-steps' loads
     constexpr int kResRows = (16 * TM + W - 1) / W;
@@ -781,7 +787,7 @@ __global__ void __launch_bounds__(kWaves * 64) k_spmm_small_n_ring(SpmmArgs a, i
     if constexpr (RES) residual_begin(rp, a, nullptr, r0, nrows, true, wave, W);
     wait_vm<P * GOPS>();                                // this wave's metadata segments have landed
     lds_barrier();                                      // and every other wave's
-    const int nw = ksteps > wave ? (int)((ksteps - wave + W - 1) / W) : 0;
+    const int nw = l24 && ksteps > wave ? (int)((ksteps - wave + W - 1) / W) : 0;
     for (int i0 = 0; i0 < nw; i0 += P) {
 #pragma unroll
         for (int u = 0; u < P; ++u) {

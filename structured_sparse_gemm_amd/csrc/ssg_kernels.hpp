@@ -35,8 +35,8 @@ hipError_t launch_delta_fill(int dt, int64_t M, int64_t K, const int32_t* row_pt
 struct SpmmArgs {
     int dt;                     // DT_F16 / DT_BF16 / DT_I8
     int64_t M, N, K;
-    const void* vals; int64_t ldv;
-    const uint8_t* meta; int64_t ldm;
+    const void* vals; int64_t ldv;     // 2:4 layer (vals == nullptr: none, an
+    const uint8_t* meta; int64_t ldm;  // unstructured product of the residual)
     const int32_t* row_ptr;     // residual (nullptr: none)
     const int32_t* col;         // CSR column indices, or nullptr when
     const uint8_t* dcol;        // the residual is delta-coded (gap bytes)

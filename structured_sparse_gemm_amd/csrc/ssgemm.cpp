@@ -310,6 +310,60 @@ int ssg_spmm_2to4_residual_delta(int ab, int c, int64_t M, int64_t N, int64_t K,
                                            nnz_d, B, ldb, C, ldc, ws, ws_bytes, stream);
 }
 
+namespace {
+
+// C = residual x B with no 2:4 layer: the small-N kernel (its weight stream
+// empty) where it takes the problem, else the generic one.
+int run_unstructured(int ab, int c, int64_t M, int64_t N, int64_t K, const int32_t* row_ptr, const int32_t* col,
+                     const uint8_t* dcol, const void* vals, int64_t nnz, const void* B, int64_t ldb, void* C,
+                     int64_t ldc, void* stream) {
+    const bool pair_ok = (ab == SSG_F16 && c == SSG_F32) || (ab == SSG_BF16 && c == SSG_F32) ||
+                         (ab == SSG_I8 && c == SSG_I32);
+    if (!pair_ok) return fail(SSG_ERR_DTYPE, "unsupported (input, output) types (%d, %d)", ab, c);
+    if (M < 0 || N < 0 || K < 0) return fail(SSG_ERR_SHAPE, "negative size");
+    if (N > ((int64_t)1 << 31) || M > ((int64_t)1 << 40)) return fail(SSG_ERR_SHAPE, "size too large");
+    if (nnz < 0 || nnz > INT32_MAX) return fail(SSG_ERR_FORMAT, "nnz=%lld out of range", (long long)nnz);
+    if (M > 0 && !row_ptr) return fail(SSG_ERR_NULL, "row_ptr is NULL");
+    if (nnz > 0 && ((!col && !dcol) || !vals)) return fail(SSG_ERR_NULL, "column indices or values are NULL");
+    if (K > 0 && N > 0 && !B) return fail(SSG_ERR_NULL, "B is NULL");
+    if (M > 0 && N > 0 && !C) return fail(SSG_ERR_NULL, "C is NULL");
+    if (ldb < N) return fail(SSG_ERR_STRIDE, "ldb=%lld < N=%lld", (long long)ldb, (long long)N);
+    if (ldc < N) return fail(SSG_ERR_STRIDE, "ldc=%lld < N=%lld", (long long)ldc, (long long)N);
+    if (M == 0 || N == 0) return SSG_OK;
+    ssg::SpmmArgs a{};
+    a.dt = to_dt(ab);
+    a.M = M; a.N = N; a.K = K;
+    a.vals = nullptr; a.ldv = 0; a.meta = nullptr; a.ldm = 0;
+    a.row_ptr = row_ptr; a.col = dcol ? nullptr : col; a.dcol = dcol; a.rvals = vals; a.nnz_r = nnz;
+    a.B = B; a.ldb = ldb; a.C = C; a.ldc = ldc;
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e;
+    if (nnz == 0 || K == 0) {
+        // the product is zero: the generic kernel writes it (no entries to read)
+        a.row_ptr = nullptr;
+        e = ssg::launch_spmm_generic(a, s);
+    } else if (ssg::supported_small_n(a)) {
+        e = ssg::launch_spmm_small_n(a, s);
+    } else {
+        e = ssg::launch_spmm_generic(a, s);
+    }
+    return e == hipSuccess ? SSG_OK : hip_fail(e, "unstructured spmm launch");
+}
+
+}  // namespace
+
+int ssg_spmm_csr(int ab, int c, int64_t M, int64_t N, int64_t K, const int32_t* row_ptr, const int32_t* col,
+                 const void* vals, int64_t nnz, const void* B, int64_t ldb, void* C, int64_t ldc, void* stream) {
+    return run_unstructured(ab, c, M, N, K, row_ptr, col, nullptr, vals, nnz, B, ldb, C, ldc, stream);
+}
+
+int ssg_spmm_csr_delta(int ab, int c, int64_t M, int64_t N, int64_t K, const int32_t* drow_ptr, const uint8_t* dcol,
+                       const void* dvals, int64_t nnz_d, const void* B, int64_t ldb, void* C, int64_t ldc,
+                       void* stream) {
+    if (nnz_d > 0 && !dcol) return fail(SSG_ERR_NULL, "dcol is NULL with nnz_d > 0");
+    return run_unstructured(ab, c, M, N, K, drow_ptr, nullptr, dcol, dvals, nnz_d, B, ldb, C, ldc, stream);
+}
+
 int ssg_spmm_2to4_residual(int ab, int c, int64_t M, int64_t N, int64_t K, const void* vals, int64_t ldv,
                            const uint8_t* meta, int64_t ldm, const int32_t* row_ptr, const int32_t* col,
                            const void* rvals, int64_t nnz_r, const void* B, int64_t ldb, void* C, int64_t ldc,

@@ -303,7 +303,8 @@ def test_spmm_residual_small_n_long_k(dt, shape):
 @pytest.mark.parametrize("algo", ALGOS, ids=ALGO_IDS)
 @pytest.mark.parametrize("dt", ["f16", "bf16"])
 @pytest.mark.parametrize("delta", [False, True])
-@pytest.mark.parametrize("shape", [(40, 256, 16), (33, 512, 16), (70, 1024, 8), (17, 8192, 16)])   # nnz % 4: 2, 3, 0, 3
+@pytest.mark.parametrize("shape", [(40, 256, 16), (33, 512, 16), (70, 1024, 8), (17, 8192, 16),
+                                   (8200, 512, 16), (8192, 4992 + 64, 16)])
 def test_spmm_residual_exact_small_integers(algo, dt, delta, shape):
     # small integers: every product and partial sum is exact in fp32, so the
     # fp16/bf16 result must equal the oracle's exactly -- a dropped or
@@ -321,6 +322,57 @@ def test_spmm_residual_exact_small_integers(algo, dt, delta, shape):
                                   dev_or_empty(rvals, dt), to_dev(b, dt), algo=algo))
     want = x.astype(np.int64) @ U.to_f64(dt, b).astype(np.int64)
     assert np.array_equal(C.cpu().numpy().astype(np.float64), want.astype(np.float64))
+
+
+# ------------------------------------------------------------------ unstructured products
+
+def random_csr(M, K, density, seed):
+    rng = np.random.default_rng(seed)
+    cols = [np.nonzero(rng.random(K) < density)[0] for _ in range(M)]
+    row_ptr = np.concatenate([[0], np.cumsum([len(c) for c in cols])]).astype(np.int32)
+    col = np.concatenate(cols).astype(np.int32) if row_ptr[-1] else np.zeros(0, np.int32)
+    return row_ptr, col
+
+
+CSR_SHAPES = [(40, 256, 16), (130, 2048, 16), (64, 512, 8), (33, 300, 5), (100, 1024, 40), (8192, 5056, 16)]
+
+
+@pytest.mark.parametrize("dt", DTS)
+@pytest.mark.parametrize("delta", [False, True])
+@pytest.mark.parametrize("shape", CSR_SHAPES)
+def test_spmm_csr_matches_oracle(dt, delta, shape):
+    # small integers in fp16/bf16 keep every sum exact: compared bit for bit
+    M, K, N = shape
+    row_ptr, col = random_csr(M, K, 0.1 if M < 8192 else 0.02, M + K)
+    rng = np.random.default_rng(K)
+    vals = U.encode(dt, rng.integers(1, 4, size=len(col)) * rng.choice([-1, 1], size=len(col)))
+    b = U.encode(dt, rng.integers(-3, 4, size=(K, N)))
+    cref, _ = oracle.spmm_csr(dt, row_ptr, col, vals, b, K)
+    if delta:
+        d = oracle.delta_encode(dt, row_ptr, col, vals, K)
+        C = ssg.spmm_csr_delta(dev_or_empty(d[0]), dev_or_empty(d[1]), dev_or_empty(d[2], dt), to_dev(b, dt))
+    else:
+        C = ssg.spmm_csr(dev_or_empty(row_ptr), dev_or_empty(col), dev_or_empty(vals, dt), to_dev(b, dt))
+    assert np.array_equal(C.cpu().numpy().astype(np.float64), np.asarray(cref, dtype=np.float64))
+
+
+@pytest.mark.parametrize("dt", ["f16", "bf16"])
+def test_spmm_csr_random_values_within_tolerance(dt):
+    M, K, N = 300, 4096, 16
+    row_ptr, col = random_csr(M, K, 0.05, 5)
+    vals = U.random_matrix(dt, 1, len(col), "normal", 6)[0]
+    b = U.random_matrix(dt, K, N, "normal", 7)
+    cref, sref = oracle.spmm_csr(dt, row_ptr, col, vals, b, K)
+    C = ssg.spmm_csr(dev_or_empty(row_ptr), dev_or_empty(col), dev_or_empty(vals, dt), to_dev(b, dt))
+    check_fp(C.cpu().numpy(), cref, sref, "csr %s" % dt)
+
+
+def test_spmm_csr_empty_is_zero():
+    row_ptr = np.zeros(65, np.int32)
+    b = U.encode("f16", np.ones((256, 16)))
+    C = ssg.spmm_csr(dev_or_empty(row_ptr), None, dev_or_empty(np.zeros(0, np.uint16), "f16"), to_dev(b, "f16"),
+                     out=torch.full((64, 16), 7.0, device="cuda"))
+    assert not C.cpu().numpy().any()
 
 
 @pytest.mark.parametrize("dt", DTS)

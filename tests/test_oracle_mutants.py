@@ -45,6 +45,8 @@ MUTANTS = [
     ("filler carries the entry's value", "elem_zero(dt, dvals, pos);", "elem_copy(dt, dvals, pos, rvals, j);"),
     ("delta decode starts at column 0", "int64_t k = -1;                            /* delta-coded",
      "int64_t k = 0;                            /* delta-coded"),
+    ("csr product skips the row's first entry", "for (int64_t j = row_ptr[m]; j < row_ptr[m + 1]; ++j) {\n                int64_t k = col[j];",
+     "for (int64_t j = row_ptr[m] + 1; j < row_ptr[m + 1]; ++j) {\n                int64_t k = col[j];"),
     ("bound accumulates signed terms", "s += fabs(t);\n                    }\n                    Cf[m * ldc + n] = acc;",
      "s += t;\n                    }\n                    Cf[m * ldc + n] = acc;"),
 ]

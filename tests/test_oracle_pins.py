@@ -338,6 +338,29 @@ def test_spmm_residual_delta_with_fillers_bruteforce():
     assert np.array_equal(C, want)
 
 
+@pytest.mark.parametrize("dt", DTS)
+def test_spmm_csr_equals_dense_product_of_the_scattered_matrix(dt):
+    M, K, N = 30, 200, 7
+    row_ptr, col = _random_csr(M, K, 0.15, 21)
+    vals = U.random_matrix(dt, 1, max(len(col), 1), "normal", 22)[0, :len(col)]
+    B = U.random_matrix(dt, K, N, "normal", 23)
+    C, S = oracle.spmm_csr(dt, row_ptr, col, vals, B, K)
+    D = np.zeros((M, K))
+    D[np.repeat(np.arange(M), np.diff(row_ptr)), col] = U.to_f64(dt, vals)   # independent scatter
+    if dt == "i8":
+        assert np.array_equal(C, D.astype(np.int64) @ U.to_i64(B))
+    else:
+        ref = D @ U.to_f64(dt, B)
+        assert np.allclose(C, ref, rtol=1e-12, atol=1e-12 * np.abs(ref).max())
+        assert np.allclose(S, np.abs(D) @ np.abs(U.to_f64(dt, B)), rtol=1e-12)
+    # and the same matrix as a residual on an all-zero 2:4 layer
+    if K % 4 == 0:
+        vz = np.zeros((M, K // 2), dtype=U.store_dtype(dt))
+        mz = np.full((M, (K + 7) // 8), 0x44, dtype=np.uint8)
+        C2, _ = oracle.spmm_residual(dt, vz, mz, row_ptr, col, vals, B, K)
+        assert np.array_equal(C, C2)
+
+
 def test_delta_code_rejects_bad_csr():
     K = 100
     for row_ptr, col in [([0, 2], [5, 5]), ([0, 2], [7, 3]), ([0, 1], [100]), ([0, 1], [-1]), ([0, 2, 1], [1, 2])]:
