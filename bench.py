@@ -163,10 +163,12 @@ def read_bandwidth_GBps() -> float:
     return n / s / 1e9
 
 
-def bench_workload(key: str, iters: int, read_GBps: float, delta: bool = False, dense_cmp: bool = True):
+def bench_workload(key: str, iters: int, read_GBps: float, delta: bool = False, dense_cmp: bool = True,
+                   packed: bool = False):
     """Kernel-level numbers for one workload (compression outside the timing),
     next to a dense GEMM of the same shape from the vendor library.  With
-    delta=True the residual is delta-coded (one-byte column gaps)."""
+    delta=True the residual is delta-coded (one-byte column gaps); with
+    packed=True the 2:4 operand is in the packed decode layout."""
     import numpy as np
     import torch
 
@@ -178,17 +180,21 @@ def bench_workload(key: str, iters: int, read_GBps: float, delta: bool = False, 
     ops = ssg.split(a) if w.residual else ssg.compress(a)
     if delta:
         ops = ops[:2] + ssg.delta_encode(ops[2], ops[3], ops[4], w.K)
+    if packed:
+        ops = ssg.pack_decode(ops[0], ops[1], w.K)
     wbytes = sum(t.numel() * t.element_size() for t in ops)
     copies = 1
     if w.klass == "small_n":
         copies = max(1, int(np.ceil((1 << 30) / wbytes)))
     sets = [ops] + [tuple(t.clone() for t in ops) for _ in range(copies - 1)]
     out = torch.empty((w.M, w.N), dtype=torch.int32 if w.dtype == "i8" else torch.float32, device="cuda")
-    algo = ssg.ssg_spmm_select_algo(ops[0], ops[1], b, out)
+    algo = ssg.SSG_ALGO_SMALL_N if packed else ssg.ssg_spmm_select_algo(ops[0], ops[1], b, out)
 
     def launch(i):
         o = sets[i % copies]
-        if delta:
+        if packed:
+            ssg.ssg_spmm_2to4_packed(o[0], o[1], w.M, b, out)
+        elif delta:
             ssg.ssg_spmm_2to4_residual_delta(*o, b, out)
         elif w.residual:
             ssg.ssg_spmm_2to4_residual(*o, b, out)
@@ -206,7 +212,8 @@ def bench_workload(key: str, iters: int, read_GBps: float, delta: bool = False, 
     flops = 2.0 * w.M * w.N * w.K
     bbytes = b.numel() * b.element_size()
     cbytes = out.numel() * out.element_size()
-    r = {"title": w.title + (", residual delta-coded" if delta else ""), "algo": ssg.ALGO_NAMES[algo],
+    r = {"title": w.title + (", residual delta-coded" if delta else "") + (", packed decode layout" if packed else ""),
+         "algo": ssg.ALGO_NAMES[algo] + (" (packed)" if packed else ""),
          "us_per_launch": s * 1e6,
          "timing": "HIP graph of %d launches, replayed twice; replay output matches eager: %s" % (n, graph_ok),
          "dense_equiv_TFLOPs": flops / s / 1e12, "compressed_weight_bytes": wbytes,
@@ -484,6 +491,9 @@ def main() -> int:
             if W.WORKLOADS[k].residual:
                 print("bench: workload %s, delta-coded residual ..." % k, file=sys.stderr, flush=True)
                 table[k + "_delta"] = bench_workload(k, it, rbw, delta=True, dense_cmp=False)
+            elif W.WORKLOADS[k].klass == "small_n" and W.WORKLOADS[k].N == 16:
+                print("bench: workload %s, packed decode layout ..." % k, file=sys.stderr, flush=True)
+                table[k + "_packed"] = bench_workload(k, it, rbw, dense_cmp=False, packed=True)
         out["workloads"] = table
     print(json.dumps(out))
     return 0

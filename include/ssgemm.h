@@ -212,6 +212,35 @@ int ssg_spmm_csr_delta(int ab, int c, int64_t M, int64_t N, int64_t K, const int
                        const void* dvals, int64_t nnz_d, const void* B, int64_t ldb, void* C, int64_t ldc,
                        void* stream);
 
+/* Packed decode layout: the 2:4 operand rearranged, offline like the
+ * compression, into the order the small-N kernel consumes it, for
+ * bandwidth-bound decode products ("Chapter 26 -- Sparsity: The Hardware
+ * View", section "2:4 in the Memory-Bound Regime": there the bytes streamed
+ * set the time).  For each 16-row tile and k-step (64 dense k for
+ * fp16/bf16, 128 for int8): pvals holds one 1 KiB block, lane l = 16q + r
+ * of the sparse MFMA carrying row r's 16 stored-value bytes
+ * [16q, 16q + 16) of the k-step; pmeta holds one block of 64 index words,
+ * lane l's being row r's metadata bytes [2q, 2q + 2) (fp16/bf16) or
+ * [4q, 4q + 4) (int8) of the k-step.  Tiles follow each other, a tile's
+ * blocks are consecutive in k, rows past M are zero.  The same bytes as
+ * (vals, meta), only reordered.
+ *
+ * ssg_packed_sizes: bytes of pvals and pmeta.  K must be a multiple of the
+ * k-step (SSG_ERR_SHAPE otherwise). */
+int ssg_packed_sizes(int dt, int64_t M, int64_t K, int64_t* vals_bytes, int64_t* meta_bytes);
+
+/* Pack (vals, meta) (rows 16-byte aligned) into caller-allocated pvals and
+ * pmeta of ssg_packed_sizes() bytes. */
+int ssg_pack_2to4_decode(int dt, int64_t M, int64_t K, const void* vals, int64_t ldv, const uint8_t* meta,
+                         int64_t ldm, void* pvals, void* pmeta, void* stream);
+
+/* C = expand(packed) x B for N == 16 with B one contiguous K x 16 block
+ * (ldb == 16, 16-byte aligned); pvals 16-byte aligned, pmeta aligned to
+ * its index words.  Other N give SSG_ERR_ALGO.  Accumulation as
+ * ssg_spmm_2to4. */
+int ssg_spmm_2to4_packed(int ab, int c, int64_t M, int64_t N, int64_t K, const void* pvals, const void* pmeta,
+                         const void* B, int64_t ldb, void* C, int64_t ldc, void* stream);
+
 /* As the SpMM calls above with an explicit algorithm (ssg_algo). */
 int ssg_spmm_2to4_ex(int algo, int ab, int c, int64_t M, int64_t N, int64_t K,
                      const void* vals, int64_t ldv, const uint8_t* meta, int64_t ldm,

@@ -27,7 +27,8 @@ __all__ = [
     "ssg_prune_2to4", "ssg_compress_2to4", "ssg_decompress_2to4", "ssg_split_count", "ssg_split_fill",
     "ssg_residual_delta_count", "ssg_residual_delta_fill", "ssg_spmm_workspace_bytes", "ssg_spmm_2to4",
     "ssg_spmm_2to4_residual", "ssg_spmm_2to4_residual_delta", "ssg_spmm_select_algo", "ssg_spmm_csr",
-    "ssg_spmm_csr_delta", "spmm_csr", "spmm_csr_delta",
+    "ssg_spmm_csr_delta", "spmm_csr", "spmm_csr_delta", "ssg_packed_sizes", "ssg_pack_2to4_decode",
+    "ssg_spmm_2to4_packed", "pack_decode", "spmm_packed",
     "SSG_ALGO_AUTO", "SSG_ALGO_GENERIC", "SSG_ALGO_SMALL_N", "SSG_ALGO_LARGE_N", "library_path",
 ]
 
@@ -210,6 +211,28 @@ def ssg_spmm_csr_delta(drow_ptr, dcol, dvals, B, C, stream=None) -> None:
                                      _ld(C, "C"), _stream(C, stream)), "ssg_spmm_csr_delta")
 
 
+def ssg_packed_sizes(dtype: torch.dtype, M: int, K: int) -> Tuple[int, int]:
+    import ctypes
+    vb, mb = ctypes.c_int64(0), ctypes.c_int64(0)
+    _check(_lib().ssg_packed_sizes(_DT[dtype], M, K, ctypes.byref(vb), ctypes.byref(mb)), "ssg_packed_sizes")
+    return int(vb.value), int(mb.value)
+
+
+def ssg_pack_2to4_decode(vals, meta, K: int, pvals, pmeta, stream=None) -> None:
+    M = vals.shape[0]
+    _check(_lib().ssg_pack_2to4_decode(_dtype(vals), M, K, _ptr(vals, "vals"), _ld(vals, "vals"), _ptr(meta, "meta"),
+                                       _ld(meta, "meta"), _ptr(pvals, "pvals"), _ptr(pmeta, "pmeta"),
+                                       _stream(vals, stream)), "ssg_pack_2to4_decode")
+
+
+def ssg_spmm_2to4_packed(pvals, pmeta, M: int, B, C, stream=None) -> None:
+    ab = _dtype(B)
+    N, K = B.shape[1], B.shape[0]
+    _check(_lib().ssg_spmm_2to4_packed(ab, _OUT[ab][0], M, N, K, _ptr(pvals, "pvals"), _ptr(pmeta, "pmeta"),
+                                       _ptr(B, "B"), _ld(B, "B"), _ptr(C, "C"), _ld(C, "C"), _stream(C, stream)),
+           "ssg_spmm_2to4_packed")
+
+
 def ssg_spmm_select_algo(vals, meta, B, C) -> int:
     return int(_lib().ssg_spmm_select_algo(_dtype(vals), vals.shape[0], B.shape[1], B.shape[0], _ptr(vals, "vals"),
                                            _ld(vals, "vals"), _ptr(meta, "meta"), _ld(meta, "meta"), _ptr(B, "B"),
@@ -309,4 +332,23 @@ def spmm_csr_delta(drow_ptr, dcol, dvals, B, out: Optional[torch.Tensor] = None)
     ab = _dtype(dvals)
     C = torch.empty((drow_ptr.numel() - 1, B.shape[1]), dtype=_OUT[ab][1], device=B.device) if out is None else out
     ssg_spmm_csr_delta(drow_ptr, dcol, dvals, B, C)
+    return C
+
+
+def pack_decode(vals: torch.Tensor, meta: torch.Tensor, K: Optional[int] = None):
+    """(pvals, pmeta) byte tensors of the packed decode layout of (vals, meta)."""
+    K = 2 * vals.shape[1] if K is None else K
+    vb, mb = ssg_packed_sizes(vals.dtype, vals.shape[0], K)
+    pvals = torch.empty(vb, dtype=torch.uint8, device=vals.device)
+    pmeta = torch.empty(mb, dtype=torch.uint8, device=vals.device)
+    ssg_pack_2to4_decode(vals, meta, K, pvals, pmeta)
+    return pvals, pmeta
+
+
+def spmm_packed(pvals: torch.Tensor, pmeta: torch.Tensor, M: int, B: torch.Tensor,
+                out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """C = expand(packed) @ B, B [K, 16]: fp32 for fp16/bf16, int32 for int8."""
+    ab = _dtype(B)
+    C = torch.empty((M, B.shape[1]), dtype=_OUT[ab][1], device=B.device) if out is None else out
+    ssg_spmm_2to4_packed(pvals, pmeta, M, B, C)
     return C

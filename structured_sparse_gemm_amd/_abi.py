@@ -48,6 +48,9 @@ SIGNATURES = {
                                              _i64, _vp, _i64, _vp, _i64, _vp, _sz, _vp]),
     "ssg_spmm_csr": (_i, [_i, _i, _i64, _i64, _i64, _vp, _vp, _vp, _i64, _vp, _i64, _vp, _i64, _vp]),
     "ssg_spmm_csr_delta": (_i, [_i, _i, _i64, _i64, _i64, _vp, _vp, _vp, _i64, _vp, _i64, _vp, _i64, _vp]),
+    "ssg_packed_sizes": (_i, [_i, _i64, _i64, ctypes.POINTER(_i64), ctypes.POINTER(_i64)]),
+    "ssg_pack_2to4_decode": (_i, [_i, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _vp, _vp]),
+    "ssg_spmm_2to4_packed": (_i, [_i, _i, _i64, _i64, _i64, _vp, _vp, _vp, _i64, _vp, _i64, _vp]),
     "ssg_spmm_select_algo": (_i, [_i, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64]),
 }
 

@@ -873,6 +873,179 @@ __global__ void __launch_bounds__(kWaves * 64) k_spmm_small_n_ring(SpmmArgs a, i
     }
 }
 
+// ---- packed decode layout --------------------------------------------------
+//
+// The decode kernel's sparse operand in the order it is consumed: for each
+// 16-row tile and k-step, the 64 lanes' fragments (lane l = 16q + r holds
+// row r's stored values [q*VALS/4, (q+1)*VALS/4) of the k-step, 16 bytes)
+// as one 1 KiB block, and their index words (the 2 or 4 metadata bytes the
+// sparse MFMA takes per lane) as one 128- or 256-byte block.  A tile's
+// blocks are consecutive in k.  Rows past M are zero.  The product reads
+// each block with one fully coalesced load per wave instead of 16 row
+// pieces of 64 bytes, and needs no metadata staging.
+
+template <int DT>
+__global__ void __launch_bounds__(256) k_pack(int64_t M, int64_t K, const uint8_t* vals, int64_t ldv_bytes,
+                                              const uint8_t* meta, int64_t ldm, uint8_t* pvals, uint8_t* pmeta) {
+    using T = SN<DT>;
+    constexpr int IDXB = T::META / 4;
+    const int64_t ksteps = K / T::KS, tiles = (M + 15) / 16;
+    const int64_t n = tiles * ksteps * 64;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
+        const int lane = (int)(i & 63);
+        const int64_t blk = i >> 6, tile = blk / ksteps, g = blk - tile * ksteps;
+        const int64_t row = 16 * tile + (lane & 15);
+        const int q = lane >> 4;
+        uint4 v = make_uint4(0, 0, 0, 0);
+        uint8_t mb[IDXB] = {};
+        if (row < M) {
+            v = *reinterpret_cast<const uint4*>(vals + row * ldv_bytes + g * T::VALS * T::ES + q * 16);
+#pragma unroll
+            for (int b = 0; b < IDXB; ++b) mb[b] = meta[row * ldm + g * T::META + q * IDXB + b];
+        }
+        *reinterpret_cast<uint4*>(pvals + i * 16) = v;
+#pragma unroll
+        for (int b = 0; b < IDXB; ++b) pmeta[i * IDXB + b] = mb[b];
+    }
+}
+
+// Product on the packed layout (B one contiguous K x 16 block): the ring
+// kernel's scheme with the index words loaded per k-step next to the
+// fragments, so nothing is staged before the loop.  Workgroup b takes the
+// tiles [b*T/G, (b+1)*T/G) (at most TM); tiles past its range read zero.
+template <int DT, int TM, int P>
+__global__ void __launch_bounds__(kWaves * 64) k_spmm_packed(SpmmArgs a, const uint8_t* pvals, const uint8_t* pmeta,
+                                                             int64_t tiles) {
+    constexpr int W = kWaves;
+    using T = SN<DT>;
+    using Acc = AccT<DT>;
+    using S = typename std::conditional<DT == DT_I8, int32_t, float>::type;
+    constexpr int IDXB = T::META / 4;                   // index bytes per lane per k-step
+    constexpr int BSTEP = 16 * T::ES * T::KS;           // B bytes per k-step (2 KiB)
+    constexpr int GOPS = 2 + 2 * TM;                    // loads per k-step per wave
+    static_assert(P * GOPS < 64, "vmcnt");
+    static_assert(W * kTMax * 1024 <= W * P * BSTEP, "LDS");
+    extern __shared__ __attribute__((aligned(1024))) uint8_t lds[];   // the waves' B slots
+    const uint32_t lds_addr = (uint32_t)(uintptr_t)(const lds_void*)lds;
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t t0 = (int64_t)blockIdx.x * tiles / gridDim.x, t1 = ((int64_t)blockIdx.x + 1) * tiles / gridDim.x;
+    const int nt = (int)(t1 - t0);
+    const int64_t ksteps = a.K / T::KS;
+
+    const __amdgpu_buffer_rsrc_t rv = rsrc(pvals, tiles * ksteps * 1024);
+    const __amdgpu_buffer_rsrc_t rm = rsrc(pmeta, tiles * ksteps * 64 * IDXB);
+    const __amdgpu_buffer_rsrc_t rb = rsrc(a.B, a.K * 16 * T::ES);
+    uint32_t voff[TM], moff[TM];
+#pragma unroll
+    for (int t = 0; t < TM; ++t) {
+        voff[t] = t < nt ? (uint32_t)(((t0 + t) * ksteps * 64 + lane) * 16) : kOob;
+        moff[t] = t < nt ? (uint32_t)(((t0 + t) * ksteps * 64 + lane) * IDXB) : kOob;
+    }
+
+    i32x4 av[P][TM] = {};   // native vector registers, so they can be tied to the waits below
+    int mv[P][TM] = {};
+    auto issue = [&](int64_t g, int u) {
+        const bool in = g < ksteps;
+        const uint32_t slot = lds_addr + (uint32_t)((wave * P + u) * BSTEP);
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+            dma<16>(rb, slot + j * 1024, in ? (uint32_t)(g * BSTEP + j * 1024 + lane * 16) : kOob);
+#pragma unroll
+        for (int t = 0; t < TM; ++t) {
+            const uint32_t o = in ? voff[t] + (uint32_t)(g * 1024) : kOob;
+            const uint32_t om = in ? moff[t] + (uint32_t)(g * 64 * IDXB) : kOob;
+            asm volatile("buffer_load_dwordx4 %0, %1, %2, 0 offen" : "=v"(av[u][t]) : "v"(o), "s"(rv) : "memory");
+            if constexpr (IDXB == 4)
+                asm volatile("buffer_load_dword %0, %1, %2, 0 offen" : "=v"(mv[u][t]) : "v"(om), "s"(rm) : "memory");
+            else
+                asm volatile("buffer_load_ushort %0, %1, %2, 0 offen" : "=v"(mv[u][t]) : "v"(om), "s"(rm) : "memory");
+        }
+    };
+
+    Acc acc[TM];
+#pragma unroll
+    for (int t = 0; t < TM; ++t) acc[t] = Acc{0, 0, 0, 0};
+#pragma unroll
+    for (int u = 0; u < P; ++u) issue(wave + (int64_t)W * u, u);
+    const int nw = ksteps > wave ? (int)((ksteps - wave + W - 1) / W) : 0;
+    for (int i0 = 0; i0 < nw; i0 += P) {
+#pragma unroll
+        for (int u = 0; u < P; ++u) {
+            const int i = i0 + u;
+            if (i < nw) {
+                // the oldest k-step in flight has landed once only the P-1
+                // younger ones remain; its registers are tied to the wait so
+                // no use moves above it
+                wait_vm<(P - 1) * GOPS>();
+#pragma unroll
+                for (int t = 0; t < TM; ++t) asm volatile("" : "+v"(av[u][t]), "+v"(mv[u][t]));
+                uint4 b[2];
+                load_b_operand<DT>(lds + (wave * P + u) * BSTEP, 0, lane, b);
+#pragma unroll
+                for (int t = 0; t < TM; ++t) {
+                    uint4 f;
+                    __builtin_memcpy(&f, &av[u][t], 16);
+                    acc[t] = smfmac<DT>(f, b, acc[t], (uint32_t)mv[u][t]);
+                }
+                // the slot's LDS reads are done before its next B rows land
+                __builtin_amdgcn_s_waitcnt(0xC07F);
+                issue(wave + (int64_t)W * (i + P), u);
+            }
+        }
+    }
+    // the loads past the wave's last k-step land before the LDS is reused,
+    // and before their registers are (an asm load's output counts as
+    // written when issued, so the ring stays in use until the wait)
+    wait_vm<0>();
+#pragma unroll
+    for (int u = 0; u < P; ++u)
+#pragma unroll
+        for (int t = 0; t < TM; ++t) asm volatile("" ::"v"(av[u][t]), "v"(mv[u][t]));
+    lds_barrier();
+
+    // fixed-order reduction of the waves' partial tiles
+    Acc* red = reinterpret_cast<Acc*>(lds);
+#pragma unroll
+    for (int t = 0; t < TM; ++t) red[(wave * kTMax + t) * 64 + lane] = acc[t];
+    lds_barrier();
+    for (int i = threadIdx.x; i < nt * 256; i += blockDim.x) {
+        const int t = i >> 8, ln = (i >> 2) & 63, r = i & 3;
+        S sum = S(0);
+#pragma unroll
+        for (int w = 0; w < W; ++w) sum += reinterpret_cast<const S*>(red)[((w * kTMax + t) * 64 + ln) * 4 + r];
+        const int64_t row = 16 * (t0 + t) + 4 * (ln >> 4) + r;
+        const int col = ln & 15;
+        if (row < a.M && col < a.N) reinterpret_cast<S*>(a.C)[row * a.ldc + col] = sum;
+    }
+}
+
+template <int TM> constexpr int kPackedP = TM == 1 ? 8 : TM == 2 ? 8 : TM == 3 ? 7 : 6;
+
+template <int DT, int TM>
+hipError_t launch_packed_tm(const SpmmArgs& a, const uint8_t* pv, const uint8_t* pm, int64_t tiles, int64_t G,
+                            hipStream_t s) {
+    constexpr int P = kPackedP<TM>;
+    const unsigned shm = (unsigned)(kWaves * P * 16 * SN<DT>::ES * SN<DT>::KS);
+    hipLaunchKernelGGL((k_spmm_packed<DT, TM, P>), dim3((unsigned)G), dim3(64 * kWaves), shm, s, a, pv, pm, tiles);
+    return hipGetLastError();
+}
+
+template <int DT>
+hipError_t launch_packed_t(const SpmmArgs& a, const uint8_t* pv, const uint8_t* pm, hipStream_t s) {
+    const int64_t tiles = (a.M + 15) / 16;
+    int64_t G = tiles < 256 ? tiles : 256;
+    if (G * kTMax < tiles) G = (tiles + kTMax - 1) / kTMax;
+    const int tm = (int)((tiles + G - 1) / G);
+    switch (tm) {
+        case 1: return launch_packed_tm<DT, 1>(a, pv, pm, tiles, G, s);
+        case 2: return launch_packed_tm<DT, 2>(a, pv, pm, tiles, G, s);
+        case 3: return launch_packed_tm<DT, 3>(a, pv, pm, tiles, G, s);
+        default: return launch_packed_tm<DT, 4>(a, pv, pm, tiles, G, s);
+    }
+}
+
 template <int TM> constexpr int kRingP = TM == 4 ? 6 : 8;      // deepest ring
 template <int TM> constexpr int kRingPLow = TM == 4 ? 4 : 6;   // when the deepest does not fit
 
@@ -1032,6 +1205,38 @@ bool supported_small_n(const SpmmArgs& a) {
         case DT_BF16: return supported_t<DT_BF16>(a);
         case DT_I8: return supported_t<DT_I8>(a);
         default: return false;
+    }
+}
+
+hipError_t launch_pack_decode(int dt, int64_t M, int64_t K, const void* vals, int64_t ldv, const uint8_t* meta,
+                              int64_t ldm, void* pvals, void* pmeta, hipStream_t s) {
+    const int64_t ks = dt == DT_I8 ? SN<DT_I8>::KS : SN<DT_F16>::KS;
+    const int64_t n = ((M + 15) / 16) * (K / ks) * 64;
+    if (n == 0) return hipSuccess;
+    const unsigned grid = (unsigned)((n + 255) / 256 < 65536 ? (n + 255) / 256 : 65536);
+    const int64_t es = dt == DT_I8 ? 1 : 2;
+    switch (dt) {
+        case DT_F16: case DT_BF16:
+            hipLaunchKernelGGL(k_pack<DT_F16>, dim3(grid), dim3(256), 0, s, M, K, (const uint8_t*)vals, ldv * es, meta,
+                               ldm, (uint8_t*)pvals, (uint8_t*)pmeta);
+            break;
+        case DT_I8:
+            hipLaunchKernelGGL(k_pack<DT_I8>, dim3(grid), dim3(256), 0, s, M, K, (const uint8_t*)vals, ldv * es, meta,
+                               ldm, (uint8_t*)pvals, (uint8_t*)pmeta);
+            break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_spmm_packed(const SpmmArgs& a, const void* pvals, const void* pmeta, hipStream_t s) {
+    const uint8_t* pv = (const uint8_t*)pvals;
+    const uint8_t* pm = (const uint8_t*)pmeta;
+    switch (a.dt) {
+        case DT_F16: return launch_packed_t<DT_F16>(a, pv, pm, s);
+        case DT_BF16: return launch_packed_t<DT_BF16>(a, pv, pm, s);
+        case DT_I8: return launch_packed_t<DT_I8>(a, pv, pm, s);
+        default: return hipErrorInvalidValue;
     }
 }
 

@@ -54,6 +54,12 @@ hipError_t launch_residual_add(const SpmmArgs& a, hipStream_t s);
 // (shape, alignment); the launchers assume it does.
 bool supported_small_n(const SpmmArgs& a);
 hipError_t launch_spmm_small_n(const SpmmArgs& a, hipStream_t s);
+// Packed decode layout (see spmm_small_n.hip): pack from (vals, meta), and
+// the product on it (B one contiguous K x 16 block, K a multiple of the
+// k-step; a.vals / a.meta unused).
+hipError_t launch_pack_decode(int dt, int64_t M, int64_t K, const void* vals, int64_t ldv, const uint8_t* meta,
+                              int64_t ldm, void* pvals, void* pmeta, hipStream_t s);
+hipError_t launch_spmm_packed(const SpmmArgs& a, const void* pvals, const void* pmeta, hipStream_t s);
 bool supported_large_n(const SpmmArgs& a);          // pipelined kernel or the basic one
 hipError_t launch_spmm_large_n(const SpmmArgs& a, hipStream_t s);
 bool supported_large_n_basic(const SpmmArgs& a);

@@ -364,6 +364,68 @@ int ssg_spmm_csr_delta(int ab, int c, int64_t M, int64_t N, int64_t K, const int
     return run_unstructured(ab, c, M, N, K, drow_ptr, nullptr, dcol, dvals, nnz_d, B, ldb, C, ldc, stream);
 }
 
+namespace {
+
+int64_t kstep_of(int dt) { return dt == SSG_I8 ? 128 : 64; }
+int64_t idx_bytes_of(int dt) { return dt == SSG_I8 ? 4 : 2; }
+
+// Sizes of the packed decode layout; fails on K not a multiple of the k-step
+// or a layout beyond the kernels' 31-bit offsets.
+int packed_sizes(int dt, int64_t M, int64_t K, int64_t* vb, int64_t* mb) {
+    if (!in_dtype(dt)) return fail(SSG_ERR_DTYPE, "element type %d is not SSG_F16, SSG_BF16 or SSG_I8", dt);
+    if (M < 0 || K < 0) return fail(SSG_ERR_SHAPE, "negative size M=%lld K=%lld", (long long)M, (long long)K);
+    if (K % kstep_of(dt) != 0)
+        return fail(SSG_ERR_SHAPE, "K=%lld is not a multiple of %lld", (long long)K, (long long)kstep_of(dt));
+    const int64_t blocks = ((M + 15) / 16) * (K / kstep_of(dt));
+    if (blocks > (int64_t)0x7fffffff / 1024) return fail(SSG_ERR_SHAPE, "packed layout too large");
+    *vb = blocks * 1024;
+    *mb = blocks * 64 * idx_bytes_of(dt);
+    return SSG_OK;
+}
+
+}  // namespace
+
+int ssg_packed_sizes(int dt, int64_t M, int64_t K, int64_t* vals_bytes, int64_t* meta_bytes) {
+    if (!vals_bytes || !meta_bytes) return fail(SSG_ERR_NULL, "size pointers are NULL");
+    return packed_sizes(dt, M, K, vals_bytes, meta_bytes);
+}
+
+int ssg_pack_2to4_decode(int dt, int64_t M, int64_t K, const void* vals, int64_t ldv, const uint8_t* meta,
+                         int64_t ldm, void* pvals, void* pmeta, void* stream) {
+    int64_t vb, mb;
+    int rc = packed_sizes(dt, M, K, &vb, &mb);
+    if (rc) return rc;
+    rc = check_compressed(M, K, vals, ldv, meta, ldm, true);
+    if (rc) return rc;
+    if (vb > 0 && (!pvals || !pmeta)) return fail(SSG_ERR_NULL, "pvals or pmeta is NULL");
+    if (!rows_aligned16(vals, ldv, dt)) return fail(SSG_ERR_STRIDE, "vals rows must be 16-byte aligned");
+    hipError_t e = ssg::launch_pack_decode(to_dt(dt), M, K, vals, ldv, meta, ldm, pvals, pmeta, (hipStream_t)stream);
+    return e == hipSuccess ? SSG_OK : hip_fail(e, "pack launch");
+}
+
+int ssg_spmm_2to4_packed(int ab, int c, int64_t M, int64_t N, int64_t K, const void* pvals, const void* pmeta,
+                         const void* B, int64_t ldb, void* C, int64_t ldc, void* stream) {
+    const bool pair_ok = (ab == SSG_F16 && c == SSG_F32) || (ab == SSG_BF16 && c == SSG_F32) ||
+                         (ab == SSG_I8 && c == SSG_I32);
+    if (!pair_ok) return fail(SSG_ERR_DTYPE, "unsupported (input, output) types (%d, %d)", ab, c);
+    int64_t vb, mb;
+    int rc = packed_sizes(ab, M, K, &vb, &mb);
+    if (rc) return rc;
+    if (M == 0) return SSG_OK;
+    if (N != 16 || ldb != 16)
+        return fail(SSG_ERR_ALGO, "the packed product takes N == 16 with ldb == 16 (got N=%lld, ldb=%lld)",
+                    (long long)N, (long long)ldb);
+    if (K == 0) return fail(SSG_ERR_SHAPE, "K must be positive");
+    if (!pvals || !pmeta || !B || !C) return fail(SSG_ERR_NULL, "a required pointer is NULL");
+    if (!al(pvals, 16) || !al(pmeta, (uintptr_t)idx_bytes_of(ab)) || !al(B, 16))
+        return fail(SSG_ERR_STRIDE, "pvals and B must be 16-byte aligned, pmeta aligned to its index words");
+    if (ldc < N) return fail(SSG_ERR_STRIDE, "ldc=%lld < N=%lld", (long long)ldc, (long long)N);
+    if (K * 16 * esize(ab) >= 0x7fffffff) return fail(SSG_ERR_SHAPE, "B too large for 31-bit offsets");
+    ssg::SpmmArgs a = make_args(ab, M, N, K, nullptr, 0, nullptr, 0, B, ldb, C, ldc);
+    hipError_t e = ssg::launch_spmm_packed(a, pvals, pmeta, (hipStream_t)stream);
+    return e == hipSuccess ? SSG_OK : hip_fail(e, "packed spmm launch");
+}
+
 int ssg_spmm_2to4_residual(int ab, int c, int64_t M, int64_t N, int64_t K, const void* vals, int64_t ldv,
                            const uint8_t* meta, int64_t ldm, const int32_t* row_ptr, const int32_t* col,
                            const void* rvals, int64_t nnz_r, const void* B, int64_t ldb, void* C, int64_t ldc,

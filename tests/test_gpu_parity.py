@@ -324,6 +324,77 @@ def test_spmm_residual_exact_small_integers(algo, dt, delta, shape):
     assert np.array_equal(C.cpu().numpy().astype(np.float64), want.astype(np.float64))
 
 
+# ------------------------------------------------------------------ packed decode layout
+
+def expected_packed(dt, vals_bits, meta, M, K):
+    """The packed layout written out from its definition (a reordering)."""
+    es = 1 if dt == "i8" else 2
+    ks = 128 if dt == "i8" else 64
+    ib = 4 if dt == "i8" else 2
+    vb = np.ascontiguousarray(vals_bits).view(np.uint8).reshape(M, -1)
+    tiles, nk = (M + 15) // 16, K // ks
+    pv = np.zeros((tiles, nk, 64, 16), np.uint8)
+    pm = np.zeros((tiles, nk, 64, ib), np.uint8)
+    for lane in range(64):
+        r, q = lane % 16, lane // 16
+        for t in range(tiles):
+            row = 16 * t + r
+            if row >= M:
+                continue
+            for g in range(nk):
+                pv[t, g, lane] = vb[row, g * (ks // 2) * es + 16 * q: g * (ks // 2) * es + 16 * q + 16]
+                pm[t, g, lane] = meta[row, g * (ks // 8) + ib * q: g * (ks // 8) + ib * q + ib]
+    return pv.reshape(-1), pm.reshape(-1)
+
+
+@pytest.mark.parametrize("dt", DTS)
+@pytest.mark.parametrize("shape", [(16, 128), (40, 256), (33, 512)])
+def test_pack_decode_layout(dt, shape):
+    M, K = shape
+    a = U.random_matrix(dt, M, K, "normal", seed=M + K)
+    vals, meta = oracle.compress(dt, a)
+    pv, pm = ssg.pack_decode(to_dev(vals, dt), dev_or_empty(meta), K)
+    ev, em = expected_packed(dt, vals, meta, M, K)
+    assert np.array_equal(pv.cpu().numpy(), ev) and np.array_equal(pm.cpu().numpy(), em)
+
+
+PACKED_SHAPES = [(16, 128, 16), (40, 256, 16), (130, 2048, 16), (1000, 1024, 16), (4100, 512, 16), (16400, 256, 16)]
+
+
+@pytest.mark.parametrize("dt", DTS)
+@pytest.mark.parametrize("shape", PACKED_SHAPES)
+def test_spmm_packed_matches_oracle(dt, shape):
+    M, K, N = shape
+    a = U.random_matrix(dt, M, K, "normal", seed=M + 2 * K)
+    b = U.random_matrix(dt, K, N, "normal", seed=N + 3)
+    vals, meta = oracle.compress(dt, a)
+    pv, pm = ssg.pack_decode(to_dev(vals, dt), dev_or_empty(meta), K)
+    C = ssg.spmm_packed(pv, pm, M, to_dev(b, dt))
+    cref, sref = oracle.spmm(dt, vals, meta, b, K)
+    check_product(dt, C.cpu().numpy(), cref, sref, "packed %s %s" % (dt, shape))
+
+
+def test_spmm_packed_takes_only_16_columns():
+    vals, meta = oracle.compress("f16", U.random_matrix("f16", 32, 128, "normal", 1))
+    pv, pm = ssg.pack_decode(to_dev(vals, "f16"), dev_or_empty(meta), 128)
+    with pytest.raises(ssg.SsgError) as e:
+        ssg.spmm_packed(pv, pm, 32, to_dev(U.random_matrix("f16", 128, 8, "normal", 2), "f16"))
+    assert e.value.status == 8
+
+
+def test_full_size_decode_packed():
+    w = W.WORKLOADS["c3"]
+    a_cpu, b_cpu = W.gen_a(w), W.gen_b(w)
+    a, b = W.bits(a_cpu), W.bits(b_cpu)
+    vals, meta = ssg.compress(a_cpu.cuda())
+    pv, pm = ssg.pack_decode(vals, meta, w.K)
+    C = ssg.spmm_packed(pv, pm, w.M, b_cpu.cuda()).cpu().numpy()
+    r = oracle.compress(w.dtype, a)
+    ms, ns = sample_entries(w.M, w.N, 3000, seed=w.index + 50)
+    cref, sref = oracle.spmm_entries(w.dtype, r[0], r[1], b, w.K, ms, ns)
+    check_product(w.dtype, C[ms, ns], cref, sref, "c3 packed")
+
+
 # ------------------------------------------------------------------ unstructured products
 
 def random_csr(M, K, density, seed):
