@@ -9,8 +9,8 @@ its header for the passages of the pages it follows).  This module only
 builds it with gcc, loads it with ctypes and marshals numpy arrays:
 
 * fp16 / bf16 matrices are passed as ``numpy.uint16`` arrays of raw bits;
-* int8 matrices as ``numpy.int8``;
-* dtype names are ``"f16"``, ``"bf16"`` and ``"i8"``.
+* int8 matrices as ``numpy.int8``; 8-bit floats as ``numpy.uint8`` bits;
+* dtype names are ``"f16"``, ``"bf16"``, ``"i8"``, ``"e4m3"`` and ``"e5m2"``.
 """
 from __future__ import annotations
 
@@ -29,7 +29,7 @@ _LIB = os.path.join(_HERE, "liboracle.so")
 # planted mistake) to show that the pins catch it.
 _OVERRIDE = os.environ.get("SSG_ORACLE_LIB")
 
-DTYPES = {"f16": 0, "bf16": 1, "i8": 2}
+DTYPES = {"f16": 0, "bf16": 1, "i8": 2, "e4m3": 3, "e5m2": 4}
 ERRORS = {
     -1: "null pointer", -2: "bad shape", -3: "bad stride", -4: "bad dtype",
     -5: "non-finite input", -6: "bad format", -7: "out of memory", -8: "out of range",
@@ -68,6 +68,10 @@ def _load():
             lib.orc_f16_to_f64.restype = ctypes.c_double
             lib.orc_bf16_to_f64.argtypes = [ctypes.c_uint16]
             lib.orc_bf16_to_f64.restype = ctypes.c_double
+            lib.orc_e4m3_to_f64.argtypes = [ctypes.c_uint8]
+            lib.orc_e4m3_to_f64.restype = ctypes.c_double
+            lib.orc_e5m2_to_f64.argtypes = [ctypes.c_uint8]
+            lib.orc_e5m2_to_f64.restype = ctypes.c_double
             lib.orc_select_group.argtypes = [_vp, _vp]
             lib.orc_select_group.restype = None
             lib.orc_compress.argtypes = [ctypes.c_int, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _i64]
@@ -110,7 +114,7 @@ def _p(a):
 def _store_dtype(dt: str):
     if dt not in DTYPES:
         raise OracleError("unknown dtype %r" % (dt,))
-    return np.int8 if dt == "i8" else np.uint16
+    return np.int8 if dt == "i8" else (np.uint8 if dt in ("e4m3", "e5m2") else np.uint16)
 
 
 def _mat(a, dt: str) -> np.ndarray:
@@ -138,6 +142,14 @@ def f16_to_f64(bits: int) -> float:
 
 def bf16_to_f64(bits: int) -> float:
     return _load().orc_bf16_to_f64(int(bits))
+
+
+def e4m3_to_f64(bits: int) -> float:
+    return _load().orc_e4m3_to_f64(int(bits))
+
+
+def e5m2_to_f64(bits: int) -> float:
+    return _load().orc_e5m2_to_f64(int(bits))
 
 
 def select_group(mag) -> list:

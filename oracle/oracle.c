@@ -49,11 +49,43 @@ double orc_bf16_to_f64(uint16_t bits) {
     return sign ? -v : v;
 }
 
-static int valid_dtype(int dt) { return dt == ORC_F16 || dt == ORC_BF16 || dt == ORC_I8; }
-static size_t esize(int dt) { return dt == ORC_I8 ? 1 : 2; }
+double orc_e4m3_to_f64(uint8_t bits) {
+    /* E4M3: 1 sign bit, 4 exponent bits (bias 7), 3 fraction bits; the
+     * all-ones exponent is a normal binade except S.1111.111 = NaN. */
+    int sign = bits >> 7, e = (bits >> 3) & 0xF, f = bits & 0x7;
+    double v;
+    if (e == 15 && f == 7)
+        v = NAN;
+    else if (e == 0)
+        v = ldexp((double)f, -9);                  /* subnormal: f * 2^-6 * 2^-3 */
+    else
+        v = ldexp((double)(8 + f), e - 10);        /* (1 + f/2^3) * 2^(e-7) */
+    return sign ? -v : v;
+}
+
+double orc_e5m2_to_f64(uint8_t bits) {
+    /* E5M2: 1 sign bit, 5 exponent bits (bias 15), 2 fraction bits, with
+     * infinities and NaNs in the all-ones exponent as in IEEE-754. */
+    int sign = bits >> 7, e = (bits >> 2) & 0x1F, f = bits & 0x3;
+    double v;
+    if (e == 31)
+        v = f ? NAN : INFINITY;
+    else if (e == 0)
+        v = ldexp((double)f, -16);                 /* subnormal: f * 2^-14 * 2^-2 */
+    else
+        v = ldexp((double)(4 + f), e - 17);        /* (1 + f/2^2) * 2^(e-15) */
+    return sign ? -v : v;
+}
+
+static int valid_dtype(int dt) {
+    return dt == ORC_F16 || dt == ORC_BF16 || dt == ORC_I8 || dt == ORC_E4M3 || dt == ORC_E5M2;
+}
+static size_t esize(int dt) { return dt == ORC_F16 || dt == ORC_BF16 ? 2 : 1; }
 
 static double elem_f64(int dt, const void* base, int64_t i) {
     if (dt == ORC_I8) return (double)((const int8_t*)base)[i];
+    if (dt == ORC_E4M3) return orc_e4m3_to_f64(((const uint8_t*)base)[i]);
+    if (dt == ORC_E5M2) return orc_e5m2_to_f64(((const uint8_t*)base)[i]);
     uint16_t u = ((const uint16_t*)base)[i];
     return dt == ORC_F16 ? orc_f16_to_f64(u) : orc_bf16_to_f64(u);
 }

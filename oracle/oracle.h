@@ -36,7 +36,9 @@
  *     orc_delta_count below.
  *
  * Element types: ORC_F16 (IEEE-754 binary16), ORC_BF16 (bfloat16),
- * ORC_I8 (two's-complement int8).  All matrices are row-major with an
+ * ORC_I8 (two's-complement int8), ORC_E4M3 / ORC_E5M2 (OCP 8-bit floats;
+ * [P3] section "The Combination: Sparsity + Quantization" stacks 2:4 with
+ * 8-bit formats).  All matrices are row-major with an
  * explicit leading dimension in elements.  Return value 0 = success,
  * negative = invalid argument (see ORC_E* below); nothing is ever allocated
  * on behalf of the caller except internal scratch freed before return.
@@ -49,13 +51,17 @@
 extern "C" {
 #endif
 
-enum { ORC_F16 = 0, ORC_BF16 = 1, ORC_I8 = 2 };
+enum { ORC_F16 = 0, ORC_BF16 = 1, ORC_I8 = 2, ORC_E4M3 = 3, ORC_E5M2 = 4 };
 enum { ORC_OK = 0, ORC_ENULL = -1, ORC_ESHAPE = -2, ORC_ESTRIDE = -3, ORC_EDTYPE = -4,
        ORC_ENONFINITE = -5, ORC_EFORMAT = -6, ORC_ENOMEM = -7, ORC_ERANGE = -8 };
 
 /* Exact value of a binary16 / bfloat16 bit pattern (NaN -> NaN, Inf -> Inf). */
 double orc_f16_to_f64(uint16_t bits);
 double orc_bf16_to_f64(uint16_t bits);
+/* Exact value of an 8-bit float (OCP FP8): E4M3 (bias 7, no infinities,
+ * S.1111.111 is NaN) and E5M2 (bias 15, IEEE-style infinities and NaNs). */
+double orc_e4m3_to_f64(uint8_t bits);
+double orc_e5m2_to_f64(uint8_t bits);
 
 /* Top-2 of a group of 4 magnitudes, ties to the lower position:
  * keep[p] = 1 iff fewer than two other positions q outrank p, where q outranks

@@ -8,19 +8,22 @@ import itertools
 import numpy as np
 import torch
 
-from workloads import encode, random_matrix, store_dtype  # noqa: F401  (seeded input families)
+from workloads import TORCH_DTYPE, encode, random_matrix, store_dtype  # noqa: F401  (seeded input families)
 
 PAIRS = list(itertools.combinations(range(4), 2))   # (0,1) (0,2) (0,3) (1,2) (1,3) (2,3)
 VALID_NIBBLES = {p | (q << 2) for p, q in PAIRS}     # {0x4, 0x8, 0xC, 0x9, 0xD, 0xE}
 
 
 def to_f64(dt: str, a: np.ndarray) -> np.ndarray:
-    """Values of raw storage as float64, decoded by numpy (fp16) or torch (bf16)."""
+    """Values of raw storage as float64, decoded by numpy (fp16) or torch (bf16, fp8)."""
     a = np.ascontiguousarray(a)
     if dt == "i8":
         return a.astype(np.float64)
     if dt == "f16":
         return a.view(np.float16).astype(np.float64)
+    if dt in ("e4m3", "e5m2"):
+        t = torch.from_numpy(a.view(np.uint8).copy()).view(TORCH_DTYPE[dt])
+        return t.to(torch.float64).numpy()
     return torch.from_numpy(a.view(np.int16).copy()).view(torch.bfloat16).to(torch.float64).numpy()
 
 

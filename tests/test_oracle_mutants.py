@@ -47,6 +47,8 @@ MUTANTS = [
      "int64_t k = 0;                            /* delta-coded"),
     ("csr product skips the row's first entry", "for (int64_t j = row_ptr[m]; j < row_ptr[m + 1]; ++j) {\n                int64_t k = col[j];",
      "for (int64_t j = row_ptr[m] + 1; j < row_ptr[m + 1]; ++j) {\n                int64_t k = col[j];"),
+    ("e4m3 exponent bias", "v = ldexp((double)(8 + f), e - 10);", "v = ldexp((double)(8 + f), e - 9);"),
+    ("e5m2 subnormal scale", "v = ldexp((double)f, -16);", "v = ldexp((double)f, -15);"),
     ("bound accumulates signed terms", "s += fabs(t);\n                    }\n                    Cf[m * ldc + n] = acc;",
      "s += t;\n                    }\n                    Cf[m * ldc + n] = acc;"),
 ]

@@ -12,7 +12,7 @@ import oracle
 from tests import _util as U
 
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
-DTS = ["f16", "bf16", "i8"]
+DTS = ["f16", "bf16", "i8", "e4m3", "e5m2"]
 FAMILIES = ["normal", "ties", "sparse", "extreme"]
 
 
@@ -41,6 +41,21 @@ def test_bf16_decoder_matches_torch_on_every_bit_pattern():
     nan = np.isnan(ref)
     assert np.array_equal(np.isnan(got), nan)
     assert np.array_equal(got[~nan], ref[~nan])
+
+
+@pytest.mark.parametrize("dt,fn", [("e4m3", "e4m3_to_f64"), ("e5m2", "e5m2_to_f64")])
+def test_fp8_decoders_match_torch_on_every_bit_pattern(dt, fn):
+    bits = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(bits.copy()).view(U.TORCH_DTYPE[dt]).to(torch.float64).numpy()
+    got = np.array([getattr(oracle, fn)(b) for b in bits])
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+    assert np.signbit(got[0x80]) and not np.signbit(got[0])
+    # the format's own landmarks
+    top = {"e4m3": 448.0, "e5m2": 57344.0}[dt]
+    tiny = {"e4m3": 2.0 ** -9, "e5m2": 2.0 ** -16}[dt]
+    assert np.nanmax(got[np.isfinite(got)]) == top and got[1] == tiny
 
 
 # ---------------------------------------------------------------- selection
@@ -479,6 +494,10 @@ def test_errors():
         oracle.prune("bf16", inf)
     with pytest.raises(oracle.OracleError):
         oracle.compress("f32", A)
+    for dt, bad in (("e4m3", 0x7F), ("e5m2", 0x7C), ("e5m2", 0xFE)):   # NaN, +Inf, NaN
+        a8 = np.array([[0x38, bad, 0, 0x38]], dtype=np.uint8)
+        with pytest.raises(oracle.OracleError, match="non-finite"):
+            oracle.compress(dt, a8)
 
 
 def test_empty_inputs():

@@ -11,6 +11,8 @@ Recipe, per workload:
 * floating-point values are drawn in fp32 (``randn`` times the stated sigma)
   and rounded to nearest-even into fp16 / bf16;
 * int8 values are drawn with ``randint`` over the stated closed range;
+* 8-bit float (OCP E4M3 / E5M2) values are drawn in fp32 and converted by
+  torch's round-to-nearest-even;
 * the moderately-unstructured workload keeps each A element independently
   with probability 0.5 (``rand < 0.5``); dropped elements are set to +0 with
   ``torch.where`` so a negative value never turns into -0.
@@ -27,7 +29,9 @@ from typing import Optional
 import numpy as np
 import torch
 
-TORCH_DTYPE = {"f16": torch.float16, "bf16": torch.bfloat16, "i8": torch.int8}
+TORCH_DTYPE = {"f16": torch.float16, "bf16": torch.bfloat16, "i8": torch.int8,
+               "e4m3": torch.float8_e4m3fn, "e5m2": torch.float8_e5m2}
+FP8 = ("e4m3", "e5m2")
 
 
 @dataclass(frozen=True)
@@ -103,6 +107,8 @@ def bits(t: torch.Tensor) -> np.ndarray:
         return t.view(torch.int16).numpy().view(np.uint16)
     if t.dtype == torch.int8:
         return t.numpy()
+    if t.dtype in (torch.float8_e4m3fn, torch.float8_e5m2):
+        return t.view(torch.uint8).numpy()
     raise TypeError("unsupported dtype %s" % (t.dtype,))
 
 
@@ -111,13 +117,15 @@ def from_bits(a: np.ndarray, dtype: str) -> torch.Tensor:
     a = np.ascontiguousarray(a)
     if dtype == "i8":
         return torch.from_numpy(a.astype(np.int8, copy=True))
+    if dtype in FP8:
+        return torch.from_numpy(a.astype(np.uint8, copy=True)).view(TORCH_DTYPE[dtype])
     return torch.from_numpy(a.astype(np.uint16, copy=True).view(np.int16)).view(TORCH_DTYPE[dtype])
 
 
 # ---------------------------------------------------------------- small random families for tests
 
 def store_dtype(dt: str):
-    return np.int8 if dt == "i8" else np.uint16
+    return np.int8 if dt == "i8" else (np.uint8 if dt in FP8 else np.uint16)
 
 
 def encode(dt: str, values) -> np.ndarray:
@@ -127,6 +135,10 @@ def encode(dt: str, values) -> np.ndarray:
         return v.astype(np.int8)
     if dt == "f16":
         return v.astype(np.float16).view(np.uint16)
+    if dt in FP8:
+        # fp32 first, then torch's round-to-nearest-even into the 8-bit format
+        t = torch.from_numpy(v.astype(np.float32)).to(TORCH_DTYPE[dt])
+        return t.view(torch.uint8).numpy().copy()
     t = torch.from_numpy(v.astype(np.float32)).to(torch.bfloat16)
     return t.view(torch.int16).numpy().view(np.uint16)
 
@@ -158,6 +170,10 @@ def random_matrix(dt: str, M: int, K: int, family: str, seed: int) -> np.ndarray
         v = rng.choice([-60000.0, 60000.0, 1e-7, -1e-7, 0.0, -0.0, 1.0], size=(M, K))
     if dt == "bf16" and family == "extreme":
         v = rng.choice([-3e38, 3e38, 1e-40, -1e-40, 0.0, -0.0, 1.0], size=(M, K))
+    if dt == "e4m3" and family == "extreme":
+        v = rng.choice([-448.0, 448.0, 2.0 ** -9, -2.0 ** -9, 0.0, -0.0, 1.0], size=(M, K))
+    if dt == "e5m2" and family == "extreme":
+        v = rng.choice([-57344.0, 57344.0, 2.0 ** -16, -2.0 ** -16, 0.0, -0.0, 1.0], size=(M, K))
     return encode(dt, v)
 
 
