@@ -35,6 +35,7 @@ sys.path.insert(0, ROOT)
 PEAK = {  # MI355X published peaks
     "hbm_GBps": 8000.0,
     "f16": 2516.6, "bf16": 2516.6, "i8": 5033.2,      # dense MFMA, TFLOP/s or TOPS
+    "e4m3": 5033.2, "e5m2": 5033.2,
 }
 METRIC = "2:4 SpMM dense-equiv TFLOP/s (large N) and compressed-weight HBM GB/s (small N)"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
@@ -239,6 +240,11 @@ def bench_workload(key: str, iters: int, read_GBps: float, delta: bool = False, 
     del a
     if w.dtype == "i8":
         dfn = lambda x: torch._int_mm(x, b)
+    elif w.dtype in ("e4m3", "e5m2"):
+        # the vendor fp8 GEMM through torch: unit scales, B column-major, fp32 out
+        one = torch.ones((), dtype=torch.float32, device="cuda")
+        bt = b.t().contiguous().t()
+        dfn = lambda x: torch._scaled_mm(x, bt, scale_a=one, scale_b=one, out_dtype=torch.float32)
     else:
         dfn = lambda x: torch.matmul(x, b)
     nd = max(iters, dcopies)
@@ -249,7 +255,8 @@ def bench_workload(key: str, iters: int, read_GBps: float, delta: bool = False, 
         sd = time_kernel(lambda i: dfn(dsets[i % dcopies]), nd, stream)
         r["dense_gemm_us"] = sd * 1e6
         r["dense_gemm"] = "torch %s on dense weights of the same shape (%s output), back-to-back launches" % (
-            "_int_mm" if w.dtype == "i8" else "matmul", "int32" if w.dtype == "i8" else w.dtype)
+            {"i8": "_int_mm", "e4m3": "_scaled_mm", "e5m2": "_scaled_mm"}.get(w.dtype, "matmul"),
+            {"i8": "int32", "e4m3": "fp32", "e5m2": "fp32"}.get(w.dtype, w.dtype))
         r["speedup_vs_dense"] = sd / s
     except RuntimeError as e:
         r["dense_gemm"] = "unavailable: %s" % str(e).splitlines()[0][:120]
@@ -484,7 +491,7 @@ def main() -> int:
         rbw = read_bandwidth_GBps()
         out["measured_read_GBps"] = rbw
         table = {}
-        for k in ("c1", "c3", "c4", "c5"):
+        for k in ("c1", "c3", "c4", "c5", "c3f8", "c4f8"):
             print("bench: workload %s ..." % k, file=sys.stderr, flush=True)
             it = args.workload_iters or (200 if W.WORKLOADS[k].klass != "large_n" else 20)
             table[k] = bench_workload(k, it, rbw)

@@ -30,7 +30,7 @@
  *         of the last byte is 0 (ldm >= ceil(K/8)).  Valid nibbles are
  *         0x4, 0x8, 0xC, 0x9, 0xD, 0xE.
  *   B     [K, N]  dense activation (ldb >= N)
- *   C     [M, N]  fp32 for fp16/bf16 inputs, int32 for int8 inputs (ldc >= N)
+ *   C     [M, N]  fp32 for fp16/bf16/fp8 inputs, int32 for int8 inputs (ldc >= N)
  *   residual: CSR, row_ptr int32 [M+1] (row_ptr[0] = 0), col int32 [nnz]
  *         ascending within a row, rvals [nnz] in the element type of A; or
  *         delta-coded (one-byte column gaps, described before
@@ -78,7 +78,16 @@ typedef enum {
     SSG_ERR_ALGO = 8        /* the requested algorithm cannot run this problem */
 } ssg_status;
 
-typedef enum { SSG_F16 = 0, SSG_BF16 = 1, SSG_I8 = 2, SSG_F32 = 3, SSG_I32 = 4 } ssg_dtype;
+/* Element types.  SSG_E4M3 / SSG_E5M2 are the OCP 8-bit floats (sign, 4 / 5
+ * exponent bits with bias 7 / 15, 3 / 2 fraction bits; E4M3 has no
+ * infinities and S.1111.111 is NaN), which the pages stack with 2:4
+ * ("Chapter 26 -- Sparsity: The Hardware View", section "The Combination:
+ * Sparsity + Quantization"); they take the int8 layouts (1 byte per value,
+ * 4 metadata bytes per 16 stored values of a sparse-MFMA lane) and
+ * accumulate into fp32. */
+typedef enum {
+    SSG_F16 = 0, SSG_BF16 = 1, SSG_I8 = 2, SSG_F32 = 3, SSG_I32 = 4, SSG_E4M3 = 5, SSG_E5M2 = 6
+} ssg_dtype;
 
 /* SpMM algorithms.  AUTO picks by shape; the others force one kernel family
  * (for A/B comparison and tests) and return SSG_ERR_ALGO when the problem is
@@ -135,7 +144,8 @@ int ssg_split_fill(int dt, int64_t M, int64_t K, const void* A, int64_t lda,
 size_t ssg_spmm_workspace_bytes(int ab, int64_t M, int64_t N, int64_t K);
 
 /* C = expand(vals, meta) x B.  (ab, c) must be (SSG_F16, SSG_F32),
- * (SSG_BF16, SSG_F32) or (SSG_I8, SSG_I32).  fp16/bf16 products are
+ * (SSG_BF16, SSG_F32), (SSG_E4M3, SSG_F32), (SSG_E5M2, SSG_F32) or
+ * (SSG_I8, SSG_I32).  fp16/bf16 products are
  * accumulated in fp32 in an order that is fixed for a given shape and
  * algorithm (results are reproducible run to run); int8 accumulates exactly
  * in int32 (the caller keeps |C| < 2^31).  Metadata nibbles must be valid

@@ -32,8 +32,10 @@ __all__ = [
     "SSG_ALGO_AUTO", "SSG_ALGO_GENERIC", "SSG_ALGO_SMALL_N", "SSG_ALGO_LARGE_N", "library_path",
 ]
 
-_DT = {torch.float16: SSG_F16, torch.bfloat16: SSG_BF16, torch.int8: SSG_I8}
-_OUT = {SSG_F16: (SSG_F32, torch.float32), SSG_BF16: (SSG_F32, torch.float32), SSG_I8: (SSG_I32, torch.int32)}
+_DT = {torch.float16: SSG_F16, torch.bfloat16: SSG_BF16, torch.int8: SSG_I8,
+       torch.float8_e4m3fn: _abi.SSG_E4M3, torch.float8_e5m2: _abi.SSG_E5M2}
+_OUT = {SSG_F16: (SSG_F32, torch.float32), SSG_BF16: (SSG_F32, torch.float32), SSG_I8: (SSG_I32, torch.int32),
+        _abi.SSG_E4M3: (SSG_F32, torch.float32), _abi.SSG_E5M2: (SSG_F32, torch.float32)}
 ALGO_NAMES = {SSG_ALGO_AUTO: "auto", SSG_ALGO_GENERIC: "generic", SSG_ALGO_SMALL_N: "small_n",
               SSG_ALGO_LARGE_N: "large_n"}
 

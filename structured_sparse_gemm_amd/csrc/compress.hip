@@ -31,13 +31,17 @@ constexpr int kChunkElems = 32;
 #endif
 constexpr int64_t kCompressBlocks = SSG_COMPRESS_BLOCKS;   // grid cap of the compress pass
 
-// Raw storage word of one element: uint16_t for fp16/bf16, int8_t for int8.
+// Raw storage word of one element: uint16_t for fp16/bf16, int8_t for int8,
+// uint8_t for the 8-bit floats.
 template <int DT> struct Store { using T = uint16_t; };
 template <> struct Store<DT_I8> { using T = int8_t; };
+template <> struct Store<DT_E4M3> { using T = uint8_t; };
+template <> struct Store<DT_E5M2> { using T = uint8_t; };
 
 template <int DT>
 __device__ __forceinline__ uint32_t key_of(typename Store<DT>::T x) {
     if constexpr (DT == DT_I8) return mag_key8((int32_t)x);
+    else if constexpr (dt_is_fp8(DT)) return mag_key_fp8((uint32_t)x);
     else return mag_key16((uint32_t)x);
 }
 
@@ -470,6 +474,8 @@ inline unsigned blocks_for(int64_t threads, int per_block) {
         case DT_F16: { constexpr int D = DT_F16; BODY; } break;           \
         case DT_BF16: { constexpr int D = DT_BF16; BODY; } break;         \
         case DT_I8: { constexpr int D = DT_I8; BODY; } break;             \
+        case DT_E4M3: { constexpr int D = DT_E4M3; BODY; } break;         \
+        case DT_E5M2: { constexpr int D = DT_E5M2; BODY; } break;         \
         default: return hipErrorInvalidValue;                            \
     }
 

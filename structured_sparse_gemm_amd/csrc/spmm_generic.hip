@@ -25,6 +25,8 @@ template <int DT>
 __device__ __forceinline__ void mac(typename Acc<DT>::T& acc, const void* a, int64_t ia, const void* b, int64_t ib) {
     if constexpr (DT == DT_I8) {
         acc += (int32_t)((const int8_t*)a)[ia] * (int32_t)((const int8_t*)b)[ib];
+    } else if constexpr (dt_is_fp8(DT)) {
+        acc = fmaf(elem_to_f32<DT>(((const uint8_t*)a)[ia]), elem_to_f32<DT>(((const uint8_t*)b)[ib]), acc);
     } else {
         acc = fmaf(elem_to_f32<DT>(((const uint16_t*)a)[ia]), elem_to_f32<DT>(((const uint16_t*)b)[ib]), acc);
     }
@@ -97,6 +99,12 @@ hipError_t launch_spmm_generic(const SpmmArgs& a, hipStream_t s) {
         case DT_F16: hipLaunchKernelGGL(k_spmm_generic<DT_F16>, grid_for(a, threads), dim3(threads), 0, s, a); break;
         case DT_BF16: hipLaunchKernelGGL(k_spmm_generic<DT_BF16>, grid_for(a, threads), dim3(threads), 0, s, a); break;
         case DT_I8: hipLaunchKernelGGL(k_spmm_generic<DT_I8>, grid_for(a, threads), dim3(threads), 0, s, a); break;
+        case DT_E4M3:
+            hipLaunchKernelGGL(k_spmm_generic<DT_E4M3>, grid_for(a, threads), dim3(threads), 0, s, a);
+            break;
+        case DT_E5M2:
+            hipLaunchKernelGGL(k_spmm_generic<DT_E5M2>, grid_for(a, threads), dim3(threads), 0, s, a);
+            break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
@@ -109,6 +117,12 @@ hipError_t launch_residual_add(const SpmmArgs& a, hipStream_t s) {
         case DT_F16: hipLaunchKernelGGL(k_residual_add<DT_F16>, grid_for(a, threads), dim3(threads), 0, s, a); break;
         case DT_BF16: hipLaunchKernelGGL(k_residual_add<DT_BF16>, grid_for(a, threads), dim3(threads), 0, s, a); break;
         case DT_I8: hipLaunchKernelGGL(k_residual_add<DT_I8>, grid_for(a, threads), dim3(threads), 0, s, a); break;
+        case DT_E4M3:
+            hipLaunchKernelGGL(k_residual_add<DT_E4M3>, grid_for(a, threads), dim3(threads), 0, s, a);
+            break;
+        case DT_E5M2:
+            hipLaunchKernelGGL(k_residual_add<DT_E5M2>, grid_for(a, threads), dim3(threads), 0, s, a);
+            break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

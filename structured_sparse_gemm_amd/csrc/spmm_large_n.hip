@@ -64,6 +64,8 @@ template <> struct PT<DT_I8> {
     static constexpr int EPC = 16;
     static constexpr int MB = 2;
 };
+template <> struct PT<DT_E4M3> : PT<DT_I8> {};   // 8-bit floats: the int8 shapes
+template <> struct PT<DT_E5M2> : PT<DT_I8> {};
 
 template <int DT>
 struct Lay {
@@ -92,7 +94,7 @@ struct Lay {
 __device__ __forceinline__ int swz_a(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
 
 template <int DT> __device__ __forceinline__ int swz(int r) {
-    if constexpr (DT == DT_I8) return 2 * (r & 7);
+    if constexpr (dt_bytes(DT) == 1) return 2 * (r & 7);
     else return 4 * (r & 3);
 }
 
@@ -110,6 +112,13 @@ __device__ __forceinline__ Acc16<DT> mma(uint4 a, const uint4 (&b)[2], Acc16<DT>
         __builtin_memcpy(&av, &a, 16);
         __builtin_memcpy(&bv, b, 32);
         return __builtin_amdgcn_smfmac_i32_32x32x64_i8(av, bv, c, (int)idx, 0, 0);
+    } else if constexpr (dt_is_fp8(DT)) {
+        i32x4 av;
+        i32x8 bv;
+        __builtin_memcpy(&av, &a, 16);
+        __builtin_memcpy(&bv, b, 32);
+        if constexpr (DT == DT_E4M3) return __builtin_amdgcn_smfmac_f32_32x32x64_fp8_fp8(av, bv, c, (int)idx, 0, 0);
+        else return __builtin_amdgcn_smfmac_f32_32x32x64_bf8_bf8(av, bv, c, (int)idx, 0, 0);
     } else if constexpr (DT == DT_F16) {
         f16x8 av;
         f16x16 bv;
@@ -135,7 +144,7 @@ template <int DT>
 __device__ __forceinline__ void b_frag(const uint8_t* bt, int s, int cb, int lane, uint4 (&b)[2]) {
     using L = Lay<DT>;
     const int bb = lane >> 5, h = (lane >> 4) & 1, i = lane & 15;
-    if constexpr (DT == DT_I8) {
+    if constexpr (dt_bytes(DT) == 1) {
         const int q = i >> 1, r = i & 1;
         const int c = (cb >> 4) + h;                       // 16-byte chunk of the 16 columns
         i32x2 v[4];
@@ -447,6 +456,8 @@ bool pipe_ok(const SpmmArgs& a) {
         case DT_F16: return pipe_supported<DT_F16>(a);
         case DT_BF16: return pipe_supported<DT_BF16>(a);
         case DT_I8: return pipe_supported<DT_I8>(a);
+        case DT_E4M3: return pipe_supported<DT_E4M3>(a);
+        case DT_E5M2: return pipe_supported<DT_E5M2>(a);
         default: return false;
     }
 }
@@ -461,6 +472,8 @@ hipError_t launch_spmm_large_n(const SpmmArgs& a, hipStream_t s) {
         case DT_F16: return pipe_launch<DT_F16>(a, s);
         case DT_BF16: return pipe_launch<DT_BF16>(a, s);
         case DT_I8: return pipe_launch<DT_I8>(a, s);
+        case DT_E4M3: return pipe_launch<DT_E4M3>(a, s);
+        case DT_E5M2: return pipe_launch<DT_E5M2>(a, s);
         default: return hipErrorInvalidValue;
     }
 }

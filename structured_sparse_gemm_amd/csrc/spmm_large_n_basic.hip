@@ -49,6 +49,8 @@ template <> struct LN<DT_I8> {
     static constexpr int IDXB = 4;
     static constexpr int PAD = 32;
 };
+template <> struct LN<DT_E4M3> : LN<DT_I8> {};   // 8-bit floats: the int8 shapes
+template <> struct LN<DT_E5M2> : LN<DT_I8> {};
 
 template <int DT> using Acc16 = typename std::conditional<DT == DT_I8, i32x16, f32x16>::type;
 
@@ -63,6 +65,13 @@ __device__ __forceinline__ Acc16<DT> smfmac32(uint4 a, const uint4 (&b)[2], Acc1
         __builtin_memcpy(&av, &a, 16);
         __builtin_memcpy(&bv, b, 32);
         return __builtin_amdgcn_smfmac_i32_32x32x64_i8(av, bv, c, (int)idx, 0, 0);
+    } else if constexpr (dt_is_fp8(DT)) {
+        i32x4 av;
+        i32x8 bv;
+        __builtin_memcpy(&av, &a, 16);
+        __builtin_memcpy(&bv, b, 32);
+        if constexpr (DT == DT_E4M3) return __builtin_amdgcn_smfmac_f32_32x32x64_fp8_fp8(av, bv, c, (int)idx, 0, 0);
+        else return __builtin_amdgcn_smfmac_f32_32x32x64_bf8_bf8(av, bv, c, (int)idx, 0, 0);
     } else if constexpr (DT == DT_F16) {
         f16x8 av;
         f16x16 bv;
@@ -88,7 +97,7 @@ __device__ __forceinline__ Acc16<DT> smfmac32(uint4 a, const uint4 (&b)[2], Acc1
 template <int DT, int PITCH>
 __device__ __forceinline__ void b_operand(const uint8_t* buf, int cb, int lane, uint4 (&b)[2]) {
     const int bb = lane >> 5, h = (lane >> 4) & 1, i = lane & 15;
-    if constexpr (DT == DT_I8) {
+    if constexpr (dt_bytes(DT) == 1) {
         const int q = i >> 1, r = i & 1;
         const uint8_t* p = buf + (16 * bb + q) * PITCH + cb + 16 * h + 8 * r;
         i32x2 v0 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(p));
@@ -291,6 +300,8 @@ bool supported_large_n_basic(const SpmmArgs& a) {
         case DT_F16: return supported_t<DT_F16>(a);
         case DT_BF16: return supported_t<DT_BF16>(a);
         case DT_I8: return supported_t<DT_I8>(a);
+        case DT_E4M3: return supported_t<DT_E4M3>(a);
+        case DT_E5M2: return supported_t<DT_E5M2>(a);
         default: return false;
     }
 }
@@ -300,6 +311,8 @@ hipError_t launch_spmm_large_n_basic(const SpmmArgs& a, hipStream_t s) {
         case DT_F16: return launch_t<DT_F16>(a, s);
         case DT_BF16: return launch_t<DT_BF16>(a, s);
         case DT_I8: return launch_t<DT_I8>(a, s);
+        case DT_E4M3: return launch_t<DT_E4M3>(a, s);
+        case DT_E5M2: return launch_t<DT_E5M2>(a, s);
         default: return hipErrorInvalidValue;
     }
 }

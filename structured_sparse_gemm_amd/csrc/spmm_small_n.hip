@@ -62,6 +62,8 @@ template <> struct SN<DT_I8> {
     static constexpr int ES = 1;
     static constexpr int META = 16;
 };
+template <> struct SN<DT_E4M3> : SN<DT_I8> {};   // 8-bit floats: the int8 shapes
+template <> struct SN<DT_E5M2> : SN<DT_I8> {};
 
 template <int DT> using AccT = typename std::conditional<DT == DT_I8, i32x4, f32x4>::type;
 
@@ -74,7 +76,7 @@ typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
 template <int DT>
 __device__ __forceinline__ void load_b_operand(const uint8_t* ldsb, int kstep, int lane, uint4 (&b)[2]) {
     const int bb = lane >> 4, i = lane & 15;
-    if constexpr (DT == DT_I8) {
+    if constexpr (SN<DT>::ES == 1) {
         // rows of 16 bytes; tr8: source lane 2q+r names row q, bytes [8r, 8r+8)
         const int q = i >> 1, r = i & 1;
         const uint8_t* base = ldsb + (kstep * 128 + 16 * bb + q) * 16 + 8 * r;
@@ -110,6 +112,13 @@ __device__ __forceinline__ AccT<DT> smfmac(uint4 a, const uint4 (&b)[2], AccT<DT
         __builtin_memcpy(&av, &a, 16);
         __builtin_memcpy(&bv, b, 32);
         return __builtin_amdgcn_smfmac_i32_16x16x128_i8(av, bv, c, (int)idx, 0, 0);
+    } else if constexpr (dt_is_fp8(DT)) {
+        i32x4 av;
+        i32x8 bv;
+        __builtin_memcpy(&av, &a, 16);
+        __builtin_memcpy(&bv, b, 32);
+        if constexpr (DT == DT_E4M3) return __builtin_amdgcn_smfmac_f32_16x16x128_fp8_fp8(av, bv, c, (int)idx, 0, 0);
+        else return __builtin_amdgcn_smfmac_f32_16x16x128_bf8_bf8(av, bv, c, (int)idx, 0, 0);
     } else if constexpr (DT == DT_F16) {
         f16x8 av;
         f16x16 bv;
@@ -509,6 +518,8 @@ __device__ __forceinline__ bool residual_consume(ResPass<DT, NRW, EPL, NP, DELTA
                 if constexpr (DT == DT_I8) {
                     const int32_t x = (int32_t)(int8_t)(st.vw[j][p][0] >> (8 * i));
                     vv[i] = inch ? x : 0;
+                } else if constexpr (ES == 1) {
+                    vv[i] = inch ? elem_to_f32<DT>(st.vw[j][p][0] >> (8 * i)) : 0.0f;
                 } else {
                     const uint16_t x = (uint16_t)(st.vw[j][p][i >> 1] >> (16 * (i & 1)));
                     vv[i] = inch ? elem_to_f32<DT>(x) : 0.0f;
@@ -521,6 +532,11 @@ __device__ __forceinline__ bool residual_consume(ResPass<DT, NRW, EPL, NP, DELTA
                     __builtin_memcpy(bv, &w[i][0], 16);
 #pragma unroll
                     for (int n = 0; n < 16; ++n) acc[n] += vv[i] * (int32_t)bv[n];
+                } else if constexpr (ES == 1) {
+                    uint8_t bv[16];
+                    __builtin_memcpy(bv, &w[i][0], 16);
+#pragma unroll
+                    for (int n = 0; n < 16; ++n) acc[n] = fmaf(vv[i], elem_to_f32<DT>(bv[n]), acc[n]);
                 } else {
                     uint16_t bv[16];
                     __builtin_memcpy(bv, &w[i][0], 16);
@@ -671,7 +687,7 @@ __global__ void __launch_bounds__(kWaves * 64) k_spmm_small_n(SpmmArgs a, int ro
                     for (int t = 0; t < TM; ++t) {
                         const uint8_t* mp = ldsm + (16 * t + rl) * pitch + kk * T::META + q * (T::META / 4);
                         uint32_t ix;
-                        if constexpr (DT == DT_I8) ix = *reinterpret_cast<const uint32_t*>(mp);
+                        if constexpr (SN<DT>::META == 16) ix = *reinterpret_cast<const uint32_t*>(mp);
                         else ix = *reinterpret_cast<const uint16_t*>(mp);
                         acc[t] = smfmac<DT>(ring[u][t], b, acc[t], ix);
                     }
@@ -806,7 +822,7 @@ __global__ void __launch_bounds__(kWaves * 64) k_spmm_small_n_ring(SpmmArgs a, i
                 for (int t = 0; t < TM; ++t) {
                     const uint8_t* mp = ldsm + (16 * t + rl) * pitch + g * T::META + q * (T::META / 4);
                     uint32_t ix;
-                    if constexpr (DT == DT_I8) ix = *reinterpret_cast<const uint32_t*>(mp);
+                    if constexpr (SN<DT>::META == 16) ix = *reinterpret_cast<const uint32_t*>(mp);
                     else ix = *reinterpret_cast<const uint16_t*>(mp);
                     uint4 f;
                     __builtin_memcpy(&f, &av[u][t], 16);
@@ -1204,23 +1220,25 @@ bool supported_small_n(const SpmmArgs& a) {
         case DT_F16: return supported_t<DT_F16>(a);
         case DT_BF16: return supported_t<DT_BF16>(a);
         case DT_I8: return supported_t<DT_I8>(a);
+        case DT_E4M3: return supported_t<DT_E4M3>(a);
+        case DT_E5M2: return supported_t<DT_E5M2>(a);
         default: return false;
     }
 }
 
 hipError_t launch_pack_decode(int dt, int64_t M, int64_t K, const void* vals, int64_t ldv, const uint8_t* meta,
                               int64_t ldm, void* pvals, void* pmeta, hipStream_t s) {
-    const int64_t ks = dt == DT_I8 ? SN<DT_I8>::KS : SN<DT_F16>::KS;
+    const int64_t ks = dt_bytes(dt) == 1 ? SN<DT_I8>::KS : SN<DT_F16>::KS;
     const int64_t n = ((M + 15) / 16) * (K / ks) * 64;
     if (n == 0) return hipSuccess;
     const unsigned grid = (unsigned)((n + 255) / 256 < 65536 ? (n + 255) / 256 : 65536);
-    const int64_t es = dt == DT_I8 ? 1 : 2;
+    const int64_t es = dt_bytes(dt);
     switch (dt) {
         case DT_F16: case DT_BF16:
             hipLaunchKernelGGL(k_pack<DT_F16>, dim3(grid), dim3(256), 0, s, M, K, (const uint8_t*)vals, ldv * es, meta,
                                ldm, (uint8_t*)pvals, (uint8_t*)pmeta);
             break;
-        case DT_I8:
+        case DT_I8: case DT_E4M3: case DT_E5M2:
             hipLaunchKernelGGL(k_pack<DT_I8>, dim3(grid), dim3(256), 0, s, M, K, (const uint8_t*)vals, ldv * es, meta,
                                ldm, (uint8_t*)pvals, (uint8_t*)pmeta);
             break;
@@ -1236,6 +1254,8 @@ hipError_t launch_spmm_packed(const SpmmArgs& a, const void* pvals, const void* 
         case DT_F16: return launch_packed_t<DT_F16>(a, pv, pm, s);
         case DT_BF16: return launch_packed_t<DT_BF16>(a, pv, pm, s);
         case DT_I8: return launch_packed_t<DT_I8>(a, pv, pm, s);
+        case DT_E4M3: return launch_packed_t<DT_E4M3>(a, pv, pm, s);
+        case DT_E5M2: return launch_packed_t<DT_E5M2>(a, pv, pm, s);
         default: return hipErrorInvalidValue;
     }
 }
@@ -1245,6 +1265,8 @@ hipError_t launch_spmm_small_n(const SpmmArgs& a, hipStream_t s) {
         case DT_F16: return launch_t<DT_F16>(a, s);
         case DT_BF16: return launch_t<DT_BF16>(a, s);
         case DT_I8: return launch_t<DT_I8>(a, s);
+        case DT_E4M3: return launch_t<DT_E4M3>(a, s);
+        case DT_E5M2: return launch_t<DT_E5M2>(a, s);
         default: return hipErrorInvalidValue;
     }
 }

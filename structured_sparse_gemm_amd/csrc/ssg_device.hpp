@@ -30,6 +30,8 @@ typedef int i32x2 __attribute__((ext_vector_type(2)));
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ uint32_t mag_key16(uint32_t bits) { return bits & 0x7FFFu; }
 __device__ __forceinline__ uint32_t mag_key8(int32_t v) { return (uint32_t)(v < 0 ? -v : v); }
+// 8-bit floats are sign-magnitude too: the 7 low bits order like |x|.
+__device__ __forceinline__ uint32_t mag_key_fp8(uint32_t bits) { return bits & 0x7Fu; }
 
 // The two kept positions of a group as a nibble i0 | (i1 << 2), i0 < i1.
 // Position p is kept iff fewer than two others outrank it; q outranks p when
@@ -63,10 +65,28 @@ __device__ __forceinline__ float f16_bits_to_f32(uint16_t b) {
 }
 __device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 
+// 8-bit floats, exact: E4M3 (bias 7, S.1111.111 = NaN, no infinities) and
+// E5M2 (bias 15, IEEE-style infinities and NaNs), from their bit fields.
+__device__ __forceinline__ float e4m3_bits_to_f32(uint32_t b) {
+    const uint32_t s = (b & 0x80u) << 24, e = (b >> 3) & 0xFu, m = b & 7u;
+    if (e == 0xFu && m == 7u) return __uint_as_float(s | 0x7FC00000u);
+    if (e == 0u) return __uint_as_float(s | __float_as_uint((float)m * 0.001953125f));   // m * 2^-9
+    return __uint_as_float(s | ((e + 120u) << 23) | (m << 20));
+}
+__device__ __forceinline__ float e5m2_bits_to_f32(uint32_t b) {
+    const uint32_t s = (b & 0x80u) << 24, e = (b >> 2) & 0x1Fu, m = b & 3u;
+    if (e == 0x1Fu) return __uint_as_float(s | (m ? 0x7FC00000u : 0x7F800000u));
+    if (e == 0u) return __uint_as_float(s | __float_as_uint((float)m * 1.52587890625e-05f));   // m * 2^-16
+    return __uint_as_float(s | ((e + 112u) << 23) | (m << 21));
+}
+
+// Element bits (the low 16 or 8 bits of b) to fp32 for the float types.
 template <int DT>
-__device__ __forceinline__ float elem_to_f32(uint16_t b) {
-    if constexpr (DT == DT_F16) return f16_bits_to_f32(b);
-    else return bf16_bits_to_f32(b);
+__device__ __forceinline__ float elem_to_f32(uint32_t b) {
+    if constexpr (DT == DT_F16) return f16_bits_to_f32((uint16_t)b);
+    else if constexpr (DT == DT_BF16) return bf16_bits_to_f32((uint16_t)b);
+    else if constexpr (DT == DT_E4M3) return e4m3_bits_to_f32(b & 0xFFu);
+    else return e5m2_bits_to_f32(b & 0xFFu);
 }
 
 }  // namespace ssg

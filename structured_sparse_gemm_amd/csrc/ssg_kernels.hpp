@@ -10,7 +10,12 @@
 
 namespace ssg {
 
-enum Dtype { DT_F16 = 0, DT_BF16 = 1, DT_I8 = 2 };
+// DT_E4M3 / DT_E5M2: OCP 8-bit floats (sign, 4/5 exponent bits with bias
+// 7/15, 3/2 fraction bits), products accumulated in fp32.
+enum Dtype { DT_F16 = 0, DT_BF16 = 1, DT_I8 = 2, DT_E4M3 = 3, DT_E5M2 = 4 };
+
+constexpr bool dt_is_fp8(int dt) { return dt == DT_E4M3 || dt == DT_E5M2; }
+constexpr int dt_bytes(int dt) { return dt == DT_F16 || dt == DT_BF16 ? 2 : 1; }
 
 hipError_t launch_compress(int dt, int64_t M, int64_t K, const void* A, int64_t lda, void* vals, int64_t ldv,
                            uint8_t* meta, int64_t ldm, bool vec, hipStream_t s);

@@ -31,8 +31,16 @@ int hip_fail(hipError_t e, const char* what) {
     return fail(SSG_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
-bool in_dtype(int dt) { return dt == SSG_F16 || dt == SSG_BF16 || dt == SSG_I8; }
-int64_t esize(int dt) { return dt == SSG_I8 ? 1 : 2; }
+bool in_dtype(int dt) {
+    return dt == SSG_F16 || dt == SSG_BF16 || dt == SSG_I8 || dt == SSG_E4M3 || dt == SSG_E5M2;
+}
+int64_t esize(int dt) { return dt == SSG_F16 || dt == SSG_BF16 ? 2 : 1; }
+
+// The (input, output) type pairs of the products: 16-bit and 8-bit floats
+// accumulate into fp32, int8 into int32.
+bool pair_ok(int ab, int c) {
+    return (ab == SSG_I8 && c == SSG_I32) || (ab != SSG_I8 && in_dtype(ab) && c == SSG_F32);
+}
 bool al(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
 // A row chunk of 32 elements is 16-byte aligned when the base is and the
@@ -40,7 +48,7 @@ bool al(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a
 bool rows_aligned16(const void* p, int64_t ld, int dt) { return al(p, 16) && (ld * esize(dt)) % 16 == 0; }
 
 int check_dense(int dt, int64_t M, int64_t K, const void* A, int64_t lda) {
-    if (!in_dtype(dt)) return fail(SSG_ERR_DTYPE, "element type %d is not SSG_F16, SSG_BF16 or SSG_I8", dt);
+    if (!in_dtype(dt)) return fail(SSG_ERR_DTYPE, "element type %d is not SSG_F16, SSG_BF16, SSG_I8, SSG_E4M3 or SSG_E5M2", dt);
     if (M < 0 || K < 0) return fail(SSG_ERR_SHAPE, "negative size M=%lld K=%lld", (long long)M, (long long)K);
     if (K % 4 != 0) return fail(SSG_ERR_SHAPE, "K=%lld is not a multiple of 4", (long long)K);
     // thread count of the chunked kernels must fit a 1-D grid
@@ -63,13 +71,19 @@ bool vec_compressed(int dt, const void* vals, int64_t ldv, const uint8_t* meta, 
     return rows_aligned16(vals, ldv, dt) && al(meta, 4) && ldm % 4 == 0;
 }
 
-int to_dt(int dt) { return dt == SSG_F16 ? ssg::DT_F16 : (dt == SSG_BF16 ? ssg::DT_BF16 : ssg::DT_I8); }
+int to_dt(int dt) {
+    switch (dt) {
+        case SSG_F16: return ssg::DT_F16;
+        case SSG_BF16: return ssg::DT_BF16;
+        case SSG_E4M3: return ssg::DT_E4M3;
+        case SSG_E5M2: return ssg::DT_E5M2;
+        default: return ssg::DT_I8;
+    }
+}
 
 int check_spmm(int ab, int c, int64_t M, int64_t N, int64_t K, const void* vals, int64_t ldv, const uint8_t* meta,
                int64_t ldm, const void* B, int64_t ldb, const void* C, int64_t ldc) {
-    const bool pair_ok = (ab == SSG_F16 && c == SSG_F32) || (ab == SSG_BF16 && c == SSG_F32) ||
-                         (ab == SSG_I8 && c == SSG_I32);
-    if (!pair_ok) return fail(SSG_ERR_DTYPE, "unsupported (input, output) types (%d, %d)", ab, c);
+    if (!pair_ok(ab, c)) return fail(SSG_ERR_DTYPE, "unsupported (input, output) types (%d, %d)", ab, c);
     if (M < 0 || N < 0 || K < 0) return fail(SSG_ERR_SHAPE, "negative size");
     if (K % 4 != 0) return fail(SSG_ERR_SHAPE, "K=%lld is not a multiple of 4", (long long)K);
     if (N > ((int64_t)1 << 31) || M > ((int64_t)1 << 40)) return fail(SSG_ERR_SHAPE, "size too large");
@@ -273,7 +287,7 @@ int ssg_residual_delta_count(int64_t M, int64_t K, const int32_t* row_ptr, const
 int ssg_residual_delta_fill(int dt, int64_t M, int64_t K, const int32_t* row_ptr, const int32_t* col,
                             const void* rvals, int64_t nnz_r, const int32_t* drow_ptr, uint8_t* dcol, void* dvals,
                             void* stream) {
-    if (!in_dtype(dt)) return fail(SSG_ERR_DTYPE, "element type %d is not SSG_F16, SSG_BF16 or SSG_I8", dt);
+    if (!in_dtype(dt)) return fail(SSG_ERR_DTYPE, "element type %d is not SSG_F16, SSG_BF16, SSG_I8, SSG_E4M3 or SSG_E5M2", dt);
     if (M < 0 || K < 0) return fail(SSG_ERR_SHAPE, "negative size M=%lld K=%lld", (long long)M, (long long)K);
     if (nnz_r < 0 || nnz_r > INT32_MAX) return fail(SSG_ERR_FORMAT, "nnz_r=%lld out of range", (long long)nnz_r);
     if (M > 0 && (!row_ptr || !drow_ptr)) return fail(SSG_ERR_NULL, "row_ptr or drow_ptr is NULL");
@@ -317,9 +331,7 @@ namespace {
 int run_unstructured(int ab, int c, int64_t M, int64_t N, int64_t K, const int32_t* row_ptr, const int32_t* col,
                      const uint8_t* dcol, const void* vals, int64_t nnz, const void* B, int64_t ldb, void* C,
                      int64_t ldc, void* stream) {
-    const bool pair_ok = (ab == SSG_F16 && c == SSG_F32) || (ab == SSG_BF16 && c == SSG_F32) ||
-                         (ab == SSG_I8 && c == SSG_I32);
-    if (!pair_ok) return fail(SSG_ERR_DTYPE, "unsupported (input, output) types (%d, %d)", ab, c);
+    if (!pair_ok(ab, c)) return fail(SSG_ERR_DTYPE, "unsupported (input, output) types (%d, %d)", ab, c);
     if (M < 0 || N < 0 || K < 0) return fail(SSG_ERR_SHAPE, "negative size");
     if (N > ((int64_t)1 << 31) || M > ((int64_t)1 << 40)) return fail(SSG_ERR_SHAPE, "size too large");
     if (nnz < 0 || nnz > INT32_MAX) return fail(SSG_ERR_FORMAT, "nnz=%lld out of range", (long long)nnz);
@@ -366,13 +378,13 @@ int ssg_spmm_csr_delta(int ab, int c, int64_t M, int64_t N, int64_t K, const int
 
 namespace {
 
-int64_t kstep_of(int dt) { return dt == SSG_I8 ? 128 : 64; }
-int64_t idx_bytes_of(int dt) { return dt == SSG_I8 ? 4 : 2; }
+int64_t kstep_of(int dt) { return esize(dt) == 1 ? 128 : 64; }
+int64_t idx_bytes_of(int dt) { return esize(dt) == 1 ? 4 : 2; }
 
 // Sizes of the packed decode layout; fails on K not a multiple of the k-step
 // or a layout beyond the kernels' 31-bit offsets.
 int packed_sizes(int dt, int64_t M, int64_t K, int64_t* vb, int64_t* mb) {
-    if (!in_dtype(dt)) return fail(SSG_ERR_DTYPE, "element type %d is not SSG_F16, SSG_BF16 or SSG_I8", dt);
+    if (!in_dtype(dt)) return fail(SSG_ERR_DTYPE, "element type %d is not SSG_F16, SSG_BF16, SSG_I8, SSG_E4M3 or SSG_E5M2", dt);
     if (M < 0 || K < 0) return fail(SSG_ERR_SHAPE, "negative size M=%lld K=%lld", (long long)M, (long long)K);
     if (K % kstep_of(dt) != 0)
         return fail(SSG_ERR_SHAPE, "K=%lld is not a multiple of %lld", (long long)K, (long long)kstep_of(dt));
@@ -405,9 +417,7 @@ int ssg_pack_2to4_decode(int dt, int64_t M, int64_t K, const void* vals, int64_t
 
 int ssg_spmm_2to4_packed(int ab, int c, int64_t M, int64_t N, int64_t K, const void* pvals, const void* pmeta,
                          const void* B, int64_t ldb, void* C, int64_t ldc, void* stream) {
-    const bool pair_ok = (ab == SSG_F16 && c == SSG_F32) || (ab == SSG_BF16 && c == SSG_F32) ||
-                         (ab == SSG_I8 && c == SSG_I32);
-    if (!pair_ok) return fail(SSG_ERR_DTYPE, "unsupported (input, output) types (%d, %d)", ab, c);
+    if (!pair_ok(ab, c)) return fail(SSG_ERR_DTYPE, "unsupported (input, output) types (%d, %d)", ab, c);
     int64_t vb, mb;
     int rc = packed_sizes(ab, M, K, &vb, &mb);
     if (rc) return rc;

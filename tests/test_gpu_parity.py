@@ -19,7 +19,8 @@ from tests import _util as U
 
 pytestmark = pytest.mark.gpu
 
-DTS = ["f16", "bf16", "i8"]
+DTS = ["f16", "bf16", "i8", "e4m3", "e5m2"]
+FLOATS = ["f16", "bf16", "e4m3", "e5m2"]
 FRO_TOL = 1e-3
 ELEM_TOL = 1e-2
 ALGOS = [ssg.SSG_ALGO_GENERIC, ssg.SSG_ALGO_SMALL_N, ssg.SSG_ALGO_LARGE_N]
@@ -40,7 +41,7 @@ def to_dev(a_bits: np.ndarray, dt: str) -> torch.Tensor:
 
 def to_host(t: torch.Tensor) -> np.ndarray:
     t = t.cpu()
-    if t.dtype in (torch.float16, torch.bfloat16, torch.int8):
+    if t.dtype in (torch.float16, torch.bfloat16, torch.int8, torch.float8_e4m3fn, torch.float8_e5m2):
         return W.bits(t)
     return t.numpy()
 
@@ -113,7 +114,8 @@ def test_compress_strided_and_unaligned(dt, extra, offset):
     ssg.ssg_prune_2to4(A, P)
     assert np.array_equal(to_host(P.contiguous()), oracle.prune(dt, a))
     # neighbours of the strided outputs were not touched
-    assert not vb[:, :offset].any() and not vb[:, offset + K // 2:].any()
+    bits = vb.view(torch.uint8) if vb.element_size() == 1 else vb.view(torch.int16)   # torch has no any() on fp8
+    assert not bits[:, :offset].any() and not bits[:, offset + K // 2:].any()
     assert not mb[:, :offset].any() and not mb[:, offset + (K + 7) // 8:].any()
 
 
@@ -301,7 +303,7 @@ def test_spmm_residual_small_n_long_k(dt, shape):
 
 
 @pytest.mark.parametrize("algo", ALGOS, ids=ALGO_IDS)
-@pytest.mark.parametrize("dt", ["f16", "bf16"])
+@pytest.mark.parametrize("dt", FLOATS)
 @pytest.mark.parametrize("delta", [False, True])
 @pytest.mark.parametrize("shape", [(40, 256, 16), (33, 512, 16), (70, 1024, 8), (17, 8192, 16),
                                    (8200, 512, 16), (8192, 4992 + 64, 16)])
@@ -328,9 +330,9 @@ def test_spmm_residual_exact_small_integers(algo, dt, delta, shape):
 
 def expected_packed(dt, vals_bits, meta, M, K):
     """The packed layout written out from its definition (a reordering)."""
-    es = 1 if dt == "i8" else 2
-    ks = 128 if dt == "i8" else 64
-    ib = 4 if dt == "i8" else 2
+    es = 2 if dt in ("f16", "bf16") else 1
+    ks = 64 if es == 2 else 128
+    ib = 2 if es == 2 else 4
     vb = np.ascontiguousarray(vals_bits).view(np.uint8).reshape(M, -1)
     tiles, nk = (M + 15) // 16, K // ks
     pv = np.zeros((tiles, nk, 64, 16), np.uint8)
@@ -427,7 +429,7 @@ def test_spmm_csr_matches_oracle(dt, delta, shape):
     assert np.array_equal(C.cpu().numpy().astype(np.float64), np.asarray(cref, dtype=np.float64))
 
 
-@pytest.mark.parametrize("dt", ["f16", "bf16"])
+@pytest.mark.parametrize("dt", FLOATS)
 def test_spmm_csr_random_values_within_tolerance(dt):
     M, K, N = 300, 4096, 16
     row_ptr, col = random_csr(M, K, 0.05, 5)
@@ -469,7 +471,7 @@ def test_spmm_residual_unaligned_arrays(dt, delta):
     check_product(dt, C.cpu().numpy(), cref, sref, "unaligned residual %s" % dt)
 
 
-@pytest.mark.parametrize("dt", ["f16", "bf16"])
+@pytest.mark.parametrize("dt", FLOATS)
 def test_identity_B_gives_the_pruned_matrix_exactly(dt):
     K = 256
     a = U.random_matrix(dt, 64, K, "normal", seed=9)

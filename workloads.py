@@ -38,7 +38,7 @@ FP8 = ("e4m3", "e5m2")
 class Workload:
     key: str
     title: str
-    dtype: str            # "f16" | "bf16" | "i8"
+    dtype: str            # "f16" | "bf16" | "i8" | "e4m3" | "e5m2"
     M: int
     K: int
     N: int
@@ -68,6 +68,11 @@ WORKLOADS = {
                    a_sigma=0.02, klass="large_n"),
     "c5": Workload("c5", "fp16 moderately-unstructured SpMM M=K=8192 N=16 (50% mask, 2:4 + residual)",
                    "f16", 8192, 8192, 16, 5, a_sigma=0.02, keep_prob=0.5, klass="small_n"),
+    # the decode and prefill shapes again with 8-bit float (OCP E4M3) operands
+    "c3f8": Workload("c3f8", "fp8 (E4M3) decode-shape SpMM M=11008 K=4096 N=16", "e4m3", 11008, 4096, 16, 6,
+                     a_sigma=0.02, klass="small_n"),
+    "c4f8": Workload("c4f8", "fp8 (E4M3) prefill-shape SpMM M=28672 K=8192 N=2048", "e4m3", 28672, 8192, 2048, 7,
+                     a_sigma=0.02, klass="large_n"),
 }
 
 
