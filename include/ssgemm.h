@@ -81,8 +81,8 @@ typedef enum {
 /* Element types.  SSG_E4M3 / SSG_E5M2 are the OCP 8-bit floats (sign, 4 / 5
  * exponent bits with bias 7 / 15, 3 / 2 fraction bits; E4M3 has no
  * infinities and S.1111.111 is NaN), which the pages stack with 2:4
- * ("Chapter 26 -- Sparsity: The Hardware View", section "The Combination:
- * Sparsity + Quantization"); they take the int8 layouts (1 byte per value,
+ * ("Chapter 26 -- Sparsity: The Hardware View", section "Sparsity +
+ * Quantization Combine"); they take the int8 layouts (1 byte per value,
  * 4 metadata bytes per 16 stored values of a sparse-MFMA lane) and
  * accumulate into fp32. */
 typedef enum {

@@ -37,7 +37,7 @@
  *
  * Element types: ORC_F16 (IEEE-754 binary16), ORC_BF16 (bfloat16),
  * ORC_I8 (two's-complement int8), ORC_E4M3 / ORC_E5M2 (OCP 8-bit floats;
- * [P3] section "The Combination: Sparsity + Quantization" stacks 2:4 with
+ * [P3] section "Sparsity + Quantization Combine" stacks 2:4 with
  * 8-bit formats).  All matrices are row-major with an
  * explicit leading dimension in elements.  Return value 0 = success,
  * negative = invalid argument (see ORC_E* below); nothing is ever allocated
