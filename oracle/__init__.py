@@ -91,6 +91,14 @@ def _load():
             lib.orc_delta_fill.argtypes = [ctypes.c_int, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp]
             lib.orc_spmm_residual_delta.argtypes = lib.orc_spmm_residual.argtypes
             lib.orc_spmm_entries_delta.argtypes = lib.orc_spmm_entries.argtypes
+            lib.orc_select_nm.argtypes = [ctypes.c_int, ctypes.c_int, _vp, _vp]
+            lib.orc_select_nm.restype = None
+            lib.orc_compress_nm.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, _i64, _i64, _vp, _i64, _vp,
+                                            _i64, _vp, _i64]
+            lib.orc_decompress_nm.argtypes = lib.orc_compress_nm.argtypes
+            lib.orc_decompress_nm.restype = _i64
+            lib.orc_spmm_nm.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, _i64, _i64, _i64, _vp, _i64, _vp,
+                                        _i64, _vp, _i64, _vp, _vp, _vp, _i64]
             lib.orc_spmm_csr.argtypes = [ctypes.c_int, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _i64, _vp, _vp, _vp,
                                          _i64]
             lib.orc_num_threads.restype = ctypes.c_int
@@ -319,6 +327,59 @@ def spmm_entries(dt: str, vals, meta, B, K: int, ms, ns, residual=None, delta: b
                                   max(meta.shape[1], 1), _p(rp), _p(col), _p(rv), _p(B),
                                   _ld(B) if K > 0 else max(N, 1), E, _p(ms), _p(ns), _p(Cf), _p(Ci), _p(S))
     _check(rc, "spmm_entries")
+    return C, S
+
+
+def select_nm(n: int, m: int, mag) -> list:
+    """keep flags (0/1) of the top-n rule for m magnitudes."""
+    g = np.ascontiguousarray(np.asarray(mag, dtype=np.float64).reshape(m))
+    keep = np.zeros(m, dtype=np.int32)
+    _load().orc_select_nm(n, m, _p(g), _p(keep))
+    return [int(x) for x in keep]
+
+
+def compress_nm(dt: str, n: int, m: int, A):
+    """N:M compressed form of A: (vals [M, K/m*n], mask uint8 [M, ceil(K/8)]);
+    mask bit k % 8 of byte k / 8 is set iff element k is kept."""
+    A = _mat(A, dt)
+    M, K = A.shape
+    vc = K // m * n if m > 0 else 0
+    vals = np.zeros((M, vc), dtype=A.dtype)
+    mask = np.zeros((M, meta_cols(K)), dtype=np.uint8)
+    _check(_load().orc_compress_nm(DTYPES[dt], n, m, M, K, _p(A), _ld(A), _p(vals), max(vc, 1), _p(mask),
+                                   max(meta_cols(K), 1)), "compress_nm")
+    return vals, mask
+
+
+def decompress_nm(dt: str, n: int, m: int, vals, mask, K: int):
+    """(D, number of groups whose mask does not hold exactly n bits)."""
+    vals = _mat(vals, dt)
+    mask = np.ascontiguousarray(np.asarray(mask, dtype=np.uint8))
+    M = vals.shape[0]
+    D = np.zeros((M, K), dtype=vals.dtype)
+    bad = _load().orc_decompress_nm(DTYPES[dt], n, m, M, K, _p(vals), max(vals.shape[1], 1), _p(mask),
+                                    max(mask.shape[1], 1), _p(D), max(K, 1))
+    _check(bad, "decompress_nm")
+    return D, int(bad)
+
+
+def spmm_nm(dt: str, n: int, m: int, vals, mask, B, K: int):
+    """C = decompress_nm(vals, mask) @ B: (C fp64, S) for floats, (C int64, None) for int8."""
+    vals = _mat(vals, dt)
+    B = _mat(B, dt)
+    mask = np.ascontiguousarray(np.asarray(mask, dtype=np.uint8))
+    M, N = vals.shape[0], B.shape[1]
+    if B.shape[0] != K:
+        raise OracleError("B has %d rows, K is %d" % (B.shape[0], K))
+    if dt == "i8":
+        C, S = np.zeros((M, N), dtype=np.int64), None
+        Cf, Ci = None, C
+    else:
+        C, S = np.zeros((M, N), dtype=np.float64), np.zeros((M, N), dtype=np.float64)
+        Cf, Ci = C, None
+    _check(_load().orc_spmm_nm(DTYPES[dt], n, m, M, N, K, _p(vals), max(vals.shape[1], 1), _p(mask),
+                               max(mask.shape[1], 1), _p(B), _ld(B) if K > 0 else max(N, 1), _p(Cf), _p(Ci),
+                               _p(S), max(N, 1)), "spmm_nm")
     return C, S
 
 

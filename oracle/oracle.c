@@ -574,6 +574,159 @@ int orc_spmm_entries_delta(int dt, int64_t M, int64_t N, int64_t K,
                         Cf, Ci, S);
 }
 
+/* ---- N:M generalization ----
+ * [P3] section "Block Sparsity, N:M Generalizations, and Channel Pruning"
+ * lists N:M patterns other than 2:4 (1:4, 2:8, 4:8) and gives no selection
+ * rule or storage.  Reading taken here: the 2:4 rule widened, i.e. each group
+ * of nm_m consecutive elements along K keeps its nm_n largest magnitudes
+ * (ties to the lower position); the kept values are stored in ascending
+ * position order, nm_n per group, and the kept positions as one bit per
+ * dense element (bit k % 8 of byte k / 8 of the row's mask, set iff element k
+ * is kept).  The product expands a row to dense and sums over k ascending,
+ * as for 2:4. */
+
+static int nm_ok(int nm_n, int nm_m) { return nm_m >= 2 && nm_m <= 16 && nm_n >= 1 && nm_n < nm_m; }
+
+void orc_select_nm(int nm_n, int nm_m, const double* mag, int* keep) {
+    for (int p = 0; p < nm_m; ++p) {
+        int rank = 0;
+        for (int q = 0; q < nm_m; ++q) {
+            if (q == p) continue;
+            if (mag[q] > mag[p] || (mag[q] == mag[p] && q < p)) ++rank;
+        }
+        keep[p] = rank < nm_n;
+    }
+}
+
+static int check_nm_shape(int dt, int nm_n, int nm_m, int64_t M, int64_t K) {
+    if (!valid_dtype(dt)) return ORC_EDTYPE;
+    if (!nm_ok(nm_n, nm_m) || M < 0 || K < 0 || K % nm_m != 0) return ORC_ESHAPE;
+    return ORC_OK;
+}
+
+int orc_compress_nm(int dt, int nm_n, int nm_m, int64_t M, int64_t K, const void* A, int64_t lda,
+                    void* vals, int64_t ldv, uint8_t* mask, int64_t ldmask) {
+    int rc = check_nm_shape(dt, nm_n, nm_m, M, K);
+    if (rc) return rc;
+    if (M > 0 && K > 0 && (!A || !vals || !mask)) return ORC_ENULL;
+    if (lda < K || ldv < K / nm_m * nm_n || ldmask < meta_cols(K)) return ORC_ESTRIDE;
+    for (int64_t m = 0; m < M; ++m) {
+        for (int64_t j = 0; j < meta_cols(K); ++j) mask[m * ldmask + j] = 0;
+        for (int64_t g = 0; g < K / nm_m; ++g) {
+            double mag[16];
+            int keep[16], t = 0;
+            for (int p = 0; p < nm_m; ++p) {
+                double x = elem_f64(dt, A, m * lda + g * nm_m + p);
+                if (!isfinite(x)) return ORC_ENONFINITE;
+                mag[p] = fabs(x);
+            }
+            orc_select_nm(nm_n, nm_m, mag, keep);
+            for (int p = 0; p < nm_m; ++p) {
+                if (!keep[p]) continue;
+                int64_t k = g * nm_m + p;
+                elem_copy(dt, vals, m * ldv + g * nm_n + t++, A, m * lda + k);
+                mask[m * ldmask + k / 8] |= (uint8_t)(1u << (k % 8));
+            }
+        }
+    }
+    return ORC_OK;
+}
+
+static int mask_bit(const uint8_t* mask, int64_t ldmask, int64_t m, int64_t k) {
+    return (mask[m * ldmask + k / 8] >> (k % 8)) & 1;
+}
+
+/* Dense row m of the N:M operand.  Returns 1 if every group has exactly
+ * nm_n mask bits; a group that has not is left zero. */
+static int64_t nm_row(int dt, int nm_n, int nm_m, int64_t K, const void* vals, int64_t ldv,
+                      const uint8_t* mask, int64_t ldmask, int64_t m, double* rowf, int64_t* rowi,
+                      void* D, int64_t ldd) {
+    int64_t bad = 0;
+    for (int64_t k = 0; k < K; ++k) {
+        if (rowf) { rowf[k] = 0.0; rowi[k] = 0; }
+        if (D) elem_zero(dt, D, m * ldd + k);
+    }
+    for (int64_t g = 0; g < K / nm_m; ++g) {
+        int cnt = 0;
+        for (int p = 0; p < nm_m; ++p) cnt += mask_bit(mask, ldmask, m, g * nm_m + p);
+        if (cnt != nm_n) { ++bad; continue; }
+        int t = 0;
+        for (int p = 0; p < nm_m; ++p) {
+            int64_t k = g * nm_m + p;
+            if (!mask_bit(mask, ldmask, m, k)) continue;
+            int64_t v = m * ldv + g * nm_n + t++;
+            if (rowf) {
+                rowf[k] = elem_f64(dt, vals, v);
+                if (dt == ORC_I8) rowi[k] = elem_i64(vals, v);
+            }
+            if (D) elem_copy(dt, D, m * ldd + k, vals, v);
+        }
+    }
+    return bad;
+}
+
+int64_t orc_decompress_nm(int dt, int nm_n, int nm_m, int64_t M, int64_t K, const void* vals, int64_t ldv,
+                          const uint8_t* mask, int64_t ldmask, void* D, int64_t ldd) {
+    int rc = check_nm_shape(dt, nm_n, nm_m, M, K);
+    if (rc) return rc;
+    if (M > 0 && K > 0 && (!vals || !mask || !D)) return ORC_ENULL;
+    if (ldv < K / nm_m * nm_n || ldmask < meta_cols(K) || ldd < K) return ORC_ESTRIDE;
+    int64_t bad = 0;
+    for (int64_t m = 0; m < M; ++m) bad += nm_row(dt, nm_n, nm_m, K, vals, ldv, mask, ldmask, m, NULL, NULL, D, ldd);
+    return bad;
+}
+
+int orc_spmm_nm(int dt, int nm_n, int nm_m, int64_t M, int64_t N, int64_t K, const void* vals, int64_t ldv,
+                const uint8_t* mask, int64_t ldmask, const void* B, int64_t ldb, double* Cf, int64_t* Ci, double* S,
+                int64_t ldc) {
+    int rc = check_nm_shape(dt, nm_n, nm_m, M, K);
+    if (rc) return rc;
+    if (N < 0) return ORC_ESHAPE;
+    if (M > 0 && K > 0 && (!vals || !mask)) return ORC_ENULL;
+    if (K > 0 && N > 0 && !B) return ORC_ENULL;
+    if (M > 0 && N > 0 && (dt == ORC_I8 ? !Ci : !Cf)) return ORC_ENULL;
+    if (ldv < K / nm_m * nm_n || ldmask < meta_cols(K) || ldb < N || ldc < N) return ORC_ESTRIDE;
+    if (M == 0 || N == 0) return ORC_OK;
+    int err = ORC_OK;
+#pragma omp parallel
+    {
+        double* rowf = (double*)malloc(sizeof(double) * (size_t)(K > 0 ? K : 1));
+        int64_t* rowi = (int64_t*)malloc(sizeof(int64_t) * (size_t)(K > 0 ? K : 1));
+        if (!rowf || !rowi) {
+#pragma omp critical
+            err = ORC_ENOMEM;
+        }
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t m = 0; m < M; ++m) {
+            if (!rowf || !rowi) continue;
+            if (nm_row(dt, nm_n, nm_m, K, vals, ldv, mask, ldmask, m, rowf, rowi, NULL, 0)) {
+#pragma omp critical
+                err = ORC_EFORMAT;
+                continue;
+            }
+            for (int64_t n = 0; n < N; ++n) {
+                if (dt == ORC_I8) {
+                    int64_t acc = 0;
+                    for (int64_t k = 0; k < K; ++k) acc += rowi[k] * elem_i64(B, k * ldb + n);
+                    Ci[m * ldc + n] = acc;
+                } else {
+                    double acc = 0.0, s = 0.0;
+                    for (int64_t k = 0; k < K; ++k) {
+                        double t = rowf[k] * elem_f64(dt, B, k * ldb + n);
+                        acc += t;
+                        s += fabs(t);
+                    }
+                    Cf[m * ldc + n] = acc;
+                    if (S) S[m * ldc + n] = s;
+                }
+            }
+        }
+        free(rowf);
+        free(rowi);
+    }
+    return err;
+}
+
 int orc_num_threads(void) {
 #ifdef _OPENMP
     return omp_get_max_threads();

@@ -147,6 +147,27 @@ int orc_spmm_entries_delta(int dt, int64_t M, int64_t N, int64_t K,
                            const void* B, int64_t ldb, int64_t n_entries,
                            const int64_t* ms, const int64_t* ns, double* Cf, int64_t* Ci, double* S);
 
+/* N:M generalization ([P3] section "Block Sparsity, N:M Generalizations,
+ * and Channel Pruning"; selection and storage are this library's reading).
+ * 1 <= nm_n < nm_m <= 16, K % nm_m == 0.
+ *
+ * orc_select_nm: keep[p] = 1 iff fewer than nm_n other positions q outrank
+ * p (mag[q] > mag[p], or equal and q < p).
+ * orc_compress_nm: vals[M, K/nm_m*nm_n] holds the kept values of group g at
+ * columns g*nm_n .. g*nm_n+nm_n-1 in ascending position order;
+ * mask[M, ceil(K/8)] has bit k%8 of byte k/8 set iff element k is kept.
+ * orc_decompress_nm: dense expansion; groups whose mask does not hold exactly
+ * nm_n bits are written as zeros and counted (the count is returned).
+ * orc_spmm_nm: as orc_spmm on the expansion (ORC_EFORMAT on a bad group). */
+void orc_select_nm(int nm_n, int nm_m, const double* mag, int* keep);
+int orc_compress_nm(int dt, int nm_n, int nm_m, int64_t M, int64_t K, const void* A, int64_t lda,
+                    void* vals, int64_t ldv, uint8_t* mask, int64_t ldmask);
+int64_t orc_decompress_nm(int dt, int nm_n, int nm_m, int64_t M, int64_t K, const void* vals, int64_t ldv,
+                          const uint8_t* mask, int64_t ldmask, void* D, int64_t ldd);
+int orc_spmm_nm(int dt, int nm_n, int nm_m, int64_t M, int64_t N, int64_t K, const void* vals, int64_t ldv,
+                const uint8_t* mask, int64_t ldmask, const void* B, int64_t ldb, double* Cf, int64_t* Ci, double* S,
+                int64_t ldc);
+
 /* Number of threads an OpenMP parallel region would use (1 without OpenMP). */
 int orc_num_threads(void);
 

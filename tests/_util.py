@@ -57,3 +57,36 @@ def brute_keep_mask(dt: str, A: np.ndarray) -> np.ndarray:
 
 def is_zero(dt: str, a: np.ndarray) -> np.ndarray:
     return to_f64(dt, a) == 0.0
+
+
+NM_PATTERNS = [(1, 4), (2, 4), (2, 8), (4, 8)]     # the N:M patterns the GPU library implements
+
+
+def brute_subset(mags, n: int) -> tuple:
+    """Kept positions of one group of len(mags) by enumerating every n-subset:
+    the subset whose magnitudes, sorted descending, are greatest; among
+    equals, the lexicographically smallest positions (itertools yields the
+    subsets in that order, so the first best one is kept)."""
+    best = None
+    for sub in itertools.combinations(range(len(mags)), n):
+        key = tuple(sorted((mags[p] for p in sub), reverse=True))
+        if best is None or key > best[0]:
+            best = (key, sub)
+    return best[1]
+
+
+def brute_keep_mask_nm(dt: str, A: np.ndarray, n: int, m: int) -> np.ndarray:
+    """Boolean N:M keep mask [M, K] by subset enumeration (python loops: small inputs)."""
+    mag = np.abs(to_f64(dt, A))
+    M, K = A.shape
+    keep = np.zeros((M, K), dtype=bool)
+    for r in range(M):
+        for g in range(K // m):
+            for p in brute_subset(list(mag[r, m * g:m * g + m]), n):
+                keep[r, m * g + p] = True
+    return keep
+
+
+def mask_bits(mask: np.ndarray, K: int) -> np.ndarray:
+    """Boolean [M, K] of a per-row bitmask (bit k % 8 of byte k / 8)."""
+    return np.unpackbits(np.ascontiguousarray(mask, dtype=np.uint8), axis=1, bitorder="little")[:, :K].astype(bool)

@@ -18,9 +18,12 @@ HDR = os.path.join(ROOT, "oracle", "oracle.h")
 PINS = os.path.join(ROOT, "tests", "test_oracle_pins.py")
 
 MUTANTS = [
-    ("ties to the higher position", "(mag[q] == mag[p] && q < p)", "(mag[q] == mag[p] && q > p)"),
+    ("ties to the higher position",
+     "if (mag[q] > mag[p] || (mag[q] == mag[p] && q < p)) ++rank;\n        }\n        keep[p] = rank < 2;",
+     "if (mag[q] > mag[p] || (mag[q] == mag[p] && q > p)) ++rank;\n        }\n        keep[p] = rank < 2;"),
     ("keeps the two smallest", "keep[p] = rank < 2;", "keep[p] = rank > 1;"),
-    ("signed magnitude", "mag[p] = fabs(x);", "mag[p] = x;"),
+    ("signed magnitude", 'mag[p] = fabs(x);                          /* int8: |-128| = 128 */', 'mag[p] = x;                          /* int8: |-128| = 128 */'),
+    ("N:M signed magnitude", "mag[p] = fabs(x);\n            }\n            orc_select_nm", "mag[p] = x;\n            }\n            orc_select_nm"),
     ("index fields swapped", "(uint8_t)(pos[0] | (pos[1] << 2))", "(uint8_t)(pos[1] | (pos[0] << 2))"),
     ("group nibbles swapped", "meta[m * ldm + g / 2] |= (uint8_t)(nib << (4 * (g % 2)));",
      "meta[m * ldm + g / 2] |= (uint8_t)(nib << (4 * ((g + 1) % 2)));"),
@@ -49,8 +52,21 @@ MUTANTS = [
      "for (int64_t j = row_ptr[m] + 1; j < row_ptr[m + 1]; ++j) {\n                int64_t k = col[j];"),
     ("e4m3 exponent bias", "v = ldexp((double)(8 + f), e - 10);", "v = ldexp((double)(8 + f), e - 9);"),
     ("e5m2 subnormal scale", "v = ldexp((double)f, -16);", "v = ldexp((double)f, -15);"),
-    ("bound accumulates signed terms", "s += fabs(t);\n                    }\n                    Cf[m * ldc + n] = acc;",
-     "s += t;\n                    }\n                    Cf[m * ldc + n] = acc;"),
+    ("N:M ties to the higher position",
+     "if (mag[q] > mag[p] || (mag[q] == mag[p] && q < p)) ++rank;\n        }\n        keep[p] = rank < nm_n;",
+     "if (mag[q] > mag[p] || (mag[q] == mag[p] && q > p)) ++rank;\n        }\n        keep[p] = rank < nm_n;"),
+    ("N:M keeps one more per group", "keep[p] = rank < nm_n;", "keep[p] = rank <= nm_n;"),
+    ("N:M mask bits in reversed order", "mask[m * ldmask + k / 8] |= (uint8_t)(1u << (k % 8));",
+     "mask[m * ldmask + k / 8] |= (uint8_t)(1u << (7 - k % 8));"),
+    ("N:M values of a group stored at the 2:4 stride", "elem_copy(dt, vals, m * ldv + g * nm_n + t++, A, m * lda + k);",
+     "elem_copy(dt, vals, m * ldv + g * (nm_m / 2) + t++, A, m * lda + k);"),
+    ("N:M expansion takes a group's values in reverse", "int64_t v = m * ldv + g * nm_n + t++;",
+     "int64_t v = m * ldv + g * nm_n + (nm_n - 1 - t++);"),
+    ("N:M accepts groups with fewer bits", "if (cnt != nm_n) { ++bad; continue; }", "if (cnt > nm_n) { ++bad; continue; }"),
+    ("N:M expansion drops the sign", "rowf[k] = elem_f64(dt, vals, v);", "rowf[k] = fabs(elem_f64(dt, vals, v));"),
+    ("bound accumulates signed terms",
+     "bt[n * K + k];\n                        acc += t;\n                        s += fabs(t);\n                    }\n                    Cf[m * ldc + n] = acc;",
+     "bt[n * K + k];\n                        acc += t;\n                        s += t;\n                    }\n                    Cf[m * ldc + n] = acc;"),
 ]
 
 

@@ -508,3 +508,148 @@ def test_empty_inputs():
         A = np.zeros((3, 0), dtype=U.store_dtype(dt))
         v, m = oracle.compress(dt, A)
         assert v.shape == (3, 0) and m.shape == (3, 0)
+
+
+# ---------------------------------------------------------------- N:M generalization
+
+@pytest.mark.parametrize("pat", ["1:4", "2:4", "2:8", "4:8"])
+def test_nm_hand_worked_rows(pat):
+    n, m = map(int, pat.split(":"))
+    for case in _golden("nm_select.json")["cases"]:
+        if case["dt"] == "i8":
+            row = np.array([case["row"]], dtype=np.int8)
+            want = case["expect"][pat]
+        else:
+            row = np.array([case["row_bits"]], dtype=np.uint16)
+            want = case["expect_bits"][pat]
+        vals, mask = oracle.compress_nm(case["dt"], n, m, row)
+        assert [int(v) for v in vals[0]] == want["vals"], case["why"]
+        assert [int(b) for b in mask[0]] == want["mask"], case["why"]
+
+
+@pytest.mark.parametrize("n,m", [(1, 4), (2, 4), (3, 4), (1, 8), (2, 8), (3, 8), (4, 8), (5, 8), (2, 16)])
+def test_select_nm_equals_subset_enumeration(n, m):
+    rng = np.random.default_rng(100 * n + m)
+    for trial in range(300):
+        hi = 1 + trial % 4                              # few distinct magnitudes: many ties
+        mags = [float(x) for x in rng.integers(0, hi + 1, size=m)]
+        keep = oracle.select_nm(n, m, mags)
+        sub = U.brute_subset(mags, n)
+        assert keep == [int(p in sub) for p in range(m)], mags
+
+
+@pytest.mark.parametrize("dt", DTS)
+@pytest.mark.parametrize("n,m", U.NM_PATTERNS)
+def test_compress_nm_matches_subset_enumeration(dt, n, m):
+    for seed in range(12):
+        for fam in FAMILIES:
+            A = U.random_matrix(dt, 6, 16, fam, seed)
+            keep = U.brute_keep_mask_nm(dt, A, n, m)
+            vals, mask = oracle.compress_nm(dt, n, m, A)
+            assert np.array_equal(U.mask_bits(mask, 16), keep)
+            # values: the kept elements, row by row in ascending k
+            assert np.array_equal(vals, A[keep].reshape(6, 16 * n // m))
+
+
+@pytest.mark.parametrize("dt", DTS)
+def test_nm_2_of_4_is_the_2to4_format(dt):
+    A = U.random_matrix(dt, 20, 72, "ties", 5)
+    v24, meta = oracle.compress(dt, A)
+    vnm, mask = oracle.compress_nm(dt, 2, 4, A)
+    assert np.array_equal(v24, vnm)
+    nib = np.stack([meta & 0xF, meta >> 4], axis=-1).reshape(20, -1)[:, :18]
+    pos = np.zeros((20, 72), dtype=bool)
+    for g in range(18):
+        pos[np.arange(20), 4 * g + (nib[:, g] & 3)] = True
+        pos[np.arange(20), 4 * g + (nib[:, g] >> 2)] = True
+    assert np.array_equal(U.mask_bits(mask, 72), pos)
+    B = U.random_matrix(dt, 72, 9, "normal", 6)
+    C24, S24 = oracle.spmm(dt, v24, meta, B, 72)
+    Cnm, Snm = oracle.spmm_nm(dt, 2, 4, vnm, mask, B, 72)
+    assert np.array_equal(C24, Cnm)
+    if S24 is not None:
+        assert np.array_equal(S24, Snm)
+
+
+@pytest.mark.parametrize("dt", DTS)
+@pytest.mark.parametrize("n,m", U.NM_PATTERNS)
+def test_nm_invariants_and_roundtrip(dt, n, m):
+    M, K = 12, 64
+    for fam in FAMILIES:
+        A = U.random_matrix(dt, M, K, fam, 13)
+        vals, mask = oracle.compress_nm(dt, n, m, A)
+        keep = U.mask_bits(mask, K)
+        assert vals.shape == (M, K * n // m) and mask.shape == (M, K // 8)
+        assert (keep.reshape(M, K // m, m).sum(-1) == n).all()
+        mag = np.abs(U.to_f64(dt, A)).reshape(M, K // m, m)
+        kg = keep.reshape(M, K // m, m)
+        assert (np.where(kg, mag, np.inf).min(-1) >= np.where(~kg, mag, -np.inf).max(-1)).all()
+        D, bad = oracle.decompress_nm(dt, n, m, vals, mask, K)
+        assert bad == 0
+        assert np.array_equal(D[keep], A[keep]) and (D[~keep] == 0).all()
+        v2, m2 = oracle.compress_nm(dt, n, m, D)        # re-selecting the expansion keeps the same set
+        assert np.array_equal(v2, vals) and np.array_equal(m2, mask)
+    # n:m keeps a subset of what a larger n keeps for the same m
+    if n < m // 2:
+        A = U.random_matrix(dt, M, K, "normal", 14)
+        small = U.mask_bits(oracle.compress_nm(dt, n, m, A)[1], K)
+        big = U.mask_bits(oracle.compress_nm(dt, m // 2, m, A)[1], K)
+        assert (big | ~small).all()
+
+
+@pytest.mark.parametrize("dt", DTS)
+@pytest.mark.parametrize("n,m", U.NM_PATTERNS)
+def test_spmm_nm_bruteforce_exact(dt, n, m):
+    for seed in range(8):
+        A = _exact_small(dt, (8, 16), seed)
+        B = _exact_small(dt, (16, 5), seed + 500)
+        keep = U.brute_keep_mask_nm(dt, A, n, m)
+        a = [[int(x) for x in row] for row in U.to_f64(dt, A)]
+        b = [[int(x) for x in row] for row in U.to_f64(dt, B)]
+        want = [[sum(a[r][k] * b[k][c] for k in range(16) if keep[r, k]) for c in range(5)] for r in range(8)]
+        vals, mask = oracle.compress_nm(dt, n, m, A)
+        C, S = oracle.spmm_nm(dt, n, m, vals, mask, B, 16)
+        assert np.array_equal(np.asarray(C, dtype=np.float64), np.array(want, dtype=np.float64))
+        if S is not None:
+            sw = [[sum(abs(a[r][k] * b[k][c]) for k in range(16) if keep[r, k]) for c in range(5)] for r in range(8)]
+            assert np.array_equal(S, np.array(sw, dtype=np.float64))
+
+
+@pytest.mark.parametrize("dt", DTS)
+@pytest.mark.parametrize("n,m", U.NM_PATTERNS)
+def test_spmm_nm_matches_numpy_matmul(dt, n, m):
+    M, K, N = 33, 200, 17
+    A = U.random_matrix(dt, M, K, "normal", 41)
+    B = U.random_matrix(dt, K, N, "normal", 42)
+    vals, mask = oracle.compress_nm(dt, n, m, A)
+    C, S = oracle.spmm_nm(dt, n, m, vals, mask, B, K)
+    P = np.where(U.brute_keep_mask_nm(dt, A, n, m), U.to_f64(dt, A), 0.0)
+    if dt == "i8":
+        assert np.array_equal(C, P.astype(np.int64) @ U.to_i64(B))
+    else:
+        Bf = U.to_f64(dt, B)
+        ref = P @ Bf
+        assert np.allclose(C, ref, rtol=1e-12, atol=1e-12 * np.abs(ref).max())
+        assert np.allclose(S, np.abs(P) @ np.abs(Bf), rtol=1e-12, atol=0)
+
+
+def test_nm_bad_masks_and_errors():
+    A = U.random_matrix("i8", 3, 16, "normal", 1)
+    vals, mask = oracle.compress_nm("i8", 2, 8, A)
+    bad = mask.copy()
+    bad[1, 0] |= 0xFF                                   # row 1, group 0: eight bits set
+    bad[2, 1] = 0x01                                    # row 2, group 1: one bit set
+    D, nbad = oracle.decompress_nm("i8", 2, 8, vals, bad, 16)
+    assert nbad == 2
+    assert (D[1, :8] == 0).all() and (D[2, 8:] == 0).all()
+    D0, _ = oracle.decompress_nm("i8", 2, 8, vals, mask, 16)
+    assert np.array_equal(D[0], D0[0]) and np.array_equal(D[1, 8:], D0[1, 8:])
+    B = U.random_matrix("i8", 16, 4, "normal", 2)
+    with pytest.raises(oracle.OracleError, match="bad format"):
+        oracle.spmm_nm("i8", 2, 8, vals, bad, B, 16)
+    for n, m, K in [(4, 4, 16), (0, 4, 16), (2, 8, 12), (1, 1, 16)]:
+        with pytest.raises(oracle.OracleError, match="shape"):
+            oracle.compress_nm("i8", n, m, U.random_matrix("i8", 2, K, "normal", 3))
+    nan = U.encode("f16", [1.0, float("nan"), 0.0, 2.0]).reshape(1, 4)
+    with pytest.raises(oracle.OracleError):
+        oracle.compress_nm("f16", 1, 4, nan)
