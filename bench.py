@@ -165,11 +165,12 @@ def read_bandwidth_GBps() -> float:
 
 
 def bench_workload(key: str, iters: int, read_GBps: float, delta: bool = False, dense_cmp: bool = True,
-                   packed: bool = False):
+                   packed: bool = False, nm=None):
     """Kernel-level numbers for one workload (compression outside the timing),
     next to a dense GEMM of the same shape from the vendor library.  With
     delta=True the residual is delta-coded (one-byte column gaps); with
-    packed=True the 2:4 operand is in the packed decode layout."""
+    packed=True the 2:4 operand is in the packed decode layout; with
+    nm=(n, m) the weight is in the n:m form (kept values plus keep mask)."""
     import numpy as np
     import torch
 
@@ -178,7 +179,10 @@ def bench_workload(key: str, iters: int, read_GBps: float, delta: bool = False, 
     w = W.WORKLOADS[key]
     a = W.gen_a(w).cuda()
     b = W.gen_b(w).cuda()
-    ops = ssg.split(a) if w.residual else ssg.compress(a)
+    if nm is not None:
+        ops = ssg.compress_nm(a, nm[0], nm[1])
+    else:
+        ops = ssg.split(a) if w.residual else ssg.compress(a)
     if delta:
         ops = ops[:2] + ssg.delta_encode(ops[2], ops[3], ops[4], w.K)
     if packed:
@@ -189,11 +193,13 @@ def bench_workload(key: str, iters: int, read_GBps: float, delta: bool = False, 
         copies = max(1, int(np.ceil((1 << 30) / wbytes)))
     sets = [ops] + [tuple(t.clone() for t in ops) for _ in range(copies - 1)]
     out = torch.empty((w.M, w.N), dtype=torch.int32 if w.dtype == "i8" else torch.float32, device="cuda")
-    algo = ssg.SSG_ALGO_SMALL_N if packed else ssg.ssg_spmm_select_algo(ops[0], ops[1], b, out)
+    algo = ssg.SSG_ALGO_SMALL_N if packed or nm else ssg.ssg_spmm_select_algo(ops[0], ops[1], b, out)
 
     def launch(i):
         o = sets[i % copies]
-        if packed:
+        if nm is not None:
+            ssg.ssg_spmm_nm(o[0], o[1], nm[0], nm[1], w.K, b, out)
+        elif packed:
             ssg.ssg_spmm_2to4_packed(o[0], o[1], w.M, b, out)
         elif delta:
             ssg.ssg_spmm_2to4_residual_delta(*o, b, out)
@@ -213,8 +219,9 @@ def bench_workload(key: str, iters: int, read_GBps: float, delta: bool = False, 
     flops = 2.0 * w.M * w.N * w.K
     bbytes = b.numel() * b.element_size()
     cbytes = out.numel() * out.element_size()
-    r = {"title": w.title + (", residual delta-coded" if delta else "") + (", packed decode layout" if packed else ""),
-         "algo": ssg.ALGO_NAMES[algo] + (" (packed)" if packed else ""),
+    r = {"title": w.title + (", residual delta-coded" if delta else "") + (", packed decode layout" if packed else "")
+         + (", %d:%d" % tuple(nm) if nm else ""),
+         "algo": "nm (dense MFMA on the expanded operand)" if nm else ssg.ALGO_NAMES[algo] + (" (packed)" if packed else ""),
          "us_per_launch": s * 1e6,
          "timing": "HIP graph of %d launches, replayed twice; replay output matches eager: %s" % (n, graph_ok),
          "dense_equiv_TFLOPs": flops / s / 1e12, "compressed_weight_bytes": wbytes,
@@ -348,6 +355,7 @@ def main() -> int:
     p.add_argument("--calib-copy", action="store_true",
                    help="first run a plain elementwise copy of 256 MiB (read 256 MiB, write 256 MiB) three times, "
                         "outside the timed region: the reference for scaling HBM byte counters")
+    p.add_argument("--only", default="", help="comma-separated workload keys of the table (default: all)")
     p.add_argument("--crossover", action="store_true",
                    help="instead of the benchmark, run the unstructured-sparsity crossover study and print its JSON")
     args = p.parse_args()
@@ -491,7 +499,16 @@ def main() -> int:
         rbw = read_bandwidth_GBps()
         out["measured_read_GBps"] = rbw
         table = {}
-        for k in ("c1", "c3", "c4", "c5", "c3f8", "c4f8"):
+        only = [k for k in args.only.split(",") if k]
+        for k in ("c1", "c3", "c4", "c5", "c3f8", "c4f8", "c3nm"):
+            if only and k not in only:
+                continue
+            if k == "c3nm":
+                for i, (n, m) in enumerate(((1, 4), (2, 4), (2, 8), (4, 8))):
+                    print("bench: workload %s, %d:%d ..." % (k, n, m), file=sys.stderr, flush=True)
+                    table["%s_%d:%d" % (k, n, m)] = bench_workload(k, args.workload_iters or 200, rbw,
+                                                                   dense_cmp=i == 0, nm=(n, m))
+                continue
             print("bench: workload %s ..." % k, file=sys.stderr, flush=True)
             it = args.workload_iters or (200 if W.WORKLOADS[k].klass != "large_n" else 20)
             table[k] = bench_workload(k, it, rbw)

@@ -251,6 +251,54 @@ int ssg_pack_2to4_decode(int dt, int64_t M, int64_t K, const void* vals, int64_t
 int ssg_spmm_2to4_packed(int ab, int c, int64_t M, int64_t N, int64_t K, const void* pvals, const void* pmeta,
                          const void* B, int64_t ldb, void* C, int64_t ldc, void* stream);
 
+/* N:M patterns other than 2:4 ("Chapter 26 -- Sparsity: The Hardware View",
+ * section "Block Sparsity, N:M Generalizations, and Channel Pruning", which
+ * lists 1:4, 2:8 and 4:8 and gives no selection rule or storage; what
+ * follows is this library's reading).  (nm_n, nm_m) is one of (1, 4),
+ * (2, 4), (2, 8), (4, 8) (else SSG_ERR_SHAPE); K % nm_m == 0.
+ *
+ * Selection: in each group of nm_m consecutive elements along K, position
+ * p is kept iff fewer than nm_n other positions outrank it (the 2:4 rule
+ * above with nm_n in place of two).
+ * Layout:
+ *   vals  [M, K/nm_m*nm_n] kept values, group g at columns
+ *         g*nm_n .. g*nm_n+nm_n-1 in ascending position order
+ *         (ldv >= K/nm_m*nm_n);
+ *   mask  [M, ceil(K/8)] uint8, bit k%8 of byte k/8 set iff element k is
+ *         kept; bits past K are 0 (ldmask >= ceil(K/8)).
+ * For 2:4 this holds the same values as ssg_compress_2to4 with the
+ * positions as bits instead of nibbles.
+ *
+ * ssg_nm_vals_cols: K / nm_m * nm_n. */
+int64_t ssg_nm_vals_cols(int nm_n, int nm_m, int64_t K);
+
+/* (vals, mask) = the N:M form of A (values bit-copied). */
+int ssg_compress_nm(int dt, int nm_n, int nm_m, int64_t M, int64_t K, const void* A, int64_t lda,
+                    void* vals, int64_t ldv, uint8_t* mask, int64_t ldmask, void* stream);
+
+/* D = dense expansion of (vals, mask): each group's stored values at its
+ * mask bits in ascending order, +0 elsewhere.  A group whose mask does not
+ * hold exactly nm_n bits is written as zeros and, if bad_count is not NULL,
+ * counted into the device int32 *bad_count (added atomically). */
+int ssg_decompress_nm(int dt, int nm_n, int nm_m, int64_t M, int64_t K, const void* vals, int64_t ldv,
+                      const uint8_t* mask, int64_t ldmask, void* D, int64_t ldd, int32_t* bad_count,
+                      void* stream);
+
+/* C = expand_nm(vals, mask) x B on the dense MFMA (gfx950 has no sparse form
+ * for these patterns; the stored operand is expanded in registers, so the
+ * gain is the bytes streamed, which set the time of decode shapes).  (ab, c)
+ * as ssg_spmm_2to4.  Alignment: vals 16-byte aligned and ldv * element size
+ * a multiple of 16; mask 8-byte aligned and ldmask a multiple of 8; B
+ * 16-byte aligned and ldb * element size a multiple of 16 (strides are only
+ * checked where there is more than one row), else SSG_ERR_STRIDE.  Any N
+ * (one workgroup column per 16 columns of B, at most 65535 of them).
+ * K == 0 zero-fills C.  Accumulation as ssg_spmm_2to4.  A mask group with
+ * the wrong number of bits gives unspecified values in its row's outputs,
+ * never out-of-bounds accesses. */
+int ssg_spmm_nm(int ab, int c, int nm_n, int nm_m, int64_t M, int64_t N, int64_t K, const void* vals, int64_t ldv,
+                const uint8_t* mask, int64_t ldmask, const void* B, int64_t ldb, void* C, int64_t ldc,
+                void* stream);
+
 /* As the SpMM calls above with an explicit algorithm (ssg_algo). */
 int ssg_spmm_2to4_ex(int algo, int ab, int c, int64_t M, int64_t N, int64_t K,
                      const void* vals, int64_t ldv, const uint8_t* meta, int64_t ldm,

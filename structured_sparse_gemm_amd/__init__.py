@@ -29,6 +29,7 @@ __all__ = [
     "ssg_spmm_2to4_residual", "ssg_spmm_2to4_residual_delta", "ssg_spmm_select_algo", "ssg_spmm_csr",
     "ssg_spmm_csr_delta", "spmm_csr", "spmm_csr_delta", "ssg_packed_sizes", "ssg_pack_2to4_decode",
     "ssg_spmm_2to4_packed", "pack_decode", "spmm_packed",
+    "ssg_compress_nm", "ssg_decompress_nm", "ssg_spmm_nm", "compress_nm", "decompress_nm", "spmm_nm",
     "SSG_ALGO_AUTO", "SSG_ALGO_GENERIC", "SSG_ALGO_SMALL_N", "SSG_ALGO_LARGE_N", "library_path",
 ]
 
@@ -241,6 +242,28 @@ def ssg_spmm_select_algo(vals, meta, B, C) -> int:
                                            _ld(B, "B"), _ptr(C, "C"), _ld(C, "C")))
 
 
+def ssg_compress_nm(A: torch.Tensor, n: int, m: int, vals: torch.Tensor, mask: torch.Tensor, stream=None) -> None:
+    _check(_lib().ssg_compress_nm(_dtype(A), n, m, A.shape[0], A.shape[1], _ptr(A, "A"), _ld(A, "A"),
+                                  _ptr(vals, "vals"), _ld(vals, "vals"), _ptr(mask, "mask"), _ld(mask, "mask"),
+                                  _stream(A, stream)), "ssg_compress_nm")
+
+
+def ssg_decompress_nm(vals: torch.Tensor, mask: torch.Tensor, n: int, m: int, D: torch.Tensor,
+                      bad_count: Optional[torch.Tensor] = None, stream=None) -> None:
+    _check(_lib().ssg_decompress_nm(_dtype(vals), n, m, D.shape[0], D.shape[1], _ptr(vals, "vals"),
+                                    _ld(vals, "vals"), _ptr(mask, "mask"), _ld(mask, "mask"), _ptr(D, "D"),
+                                    _ld(D, "D"), _ptr(bad_count, "bad_count"), _stream(D, stream)),
+           "ssg_decompress_nm")
+
+
+def ssg_spmm_nm(vals: torch.Tensor, mask: torch.Tensor, n: int, m: int, K: int, B: torch.Tensor, C: torch.Tensor,
+                stream=None) -> None:
+    ab = _dtype(vals)
+    _check(_lib().ssg_spmm_nm(ab, _OUT[ab][0], n, m, vals.shape[0], B.shape[1], K, _ptr(vals, "vals"),
+                              _ld(vals, "vals"), _ptr(mask, "mask"), _ld(mask, "mask"), _ptr(B, "B"), _ld(B, "B"),
+                              _ptr(C, "C"), _ld(C, "C"), _stream(C, stream)), "ssg_spmm_nm")
+
+
 # ---------------------------------------------------------------- allocating helpers
 
 def prune(A: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
@@ -334,6 +357,40 @@ def spmm_csr_delta(drow_ptr, dcol, dvals, B, out: Optional[torch.Tensor] = None)
     ab = _dtype(dvals)
     C = torch.empty((drow_ptr.numel() - 1, B.shape[1]), dtype=_OUT[ab][1], device=B.device) if out is None else out
     ssg_spmm_csr_delta(drow_ptr, dcol, dvals, B, C)
+    return C
+
+
+def _padded(rows: int, cols: int, dtype: torch.dtype, align: int, device) -> torch.Tensor:
+    """[rows, cols] view of a buffer whose rows start every `align` bytes."""
+    es = torch.empty((), dtype=dtype).element_size()
+    ld = max(1, -(-cols * es // align) * align // es)
+    return torch.empty((rows, ld), dtype=dtype, device=device)[:, :cols]
+
+
+def compress_nm(A: torch.Tensor, n: int, m: int) -> Tuple[torch.Tensor, torch.Tensor]:
+    """(vals [M, K/m*n], mask [M, ceil(K/8)] uint8) of a dense [M, K] weight under
+    the n:m rule; rows padded to 16 (vals) and 8 (mask) bytes as the product
+    wants them."""
+    M, K = A.shape
+    vals = _padded(M, K // m * n, A.dtype, 16, A.device)
+    mask = _padded(M, (K + 7) // 8, torch.uint8, 8, A.device)
+    ssg_compress_nm(A, n, m, vals, mask)
+    return vals, mask
+
+
+def decompress_nm(vals: torch.Tensor, mask: torch.Tensor, n: int, m: int, K: int, count_bad: bool = False):
+    D = torch.empty((vals.shape[0], K), dtype=vals.dtype, device=vals.device)
+    bad = torch.zeros(1, dtype=torch.int32, device=vals.device) if count_bad else None
+    ssg_decompress_nm(vals, mask, n, m, D, bad)
+    return (D, int(bad.item())) if count_bad else D
+
+
+def spmm_nm(vals: torch.Tensor, mask: torch.Tensor, n: int, m: int, B: torch.Tensor,
+            out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """C = expand_nm(vals, mask) @ B, K = B.shape[0]: fp32 for float inputs, int32 for int8."""
+    ab = _dtype(vals)
+    C = torch.empty((vals.shape[0], B.shape[1]), dtype=_OUT[ab][1], device=vals.device) if out is None else out
+    ssg_spmm_nm(vals, mask, n, m, B.shape[0], B, C)
     return C
 
 

@@ -70,4 +70,15 @@ hipError_t launch_spmm_large_n(const SpmmArgs& a, hipStream_t s);
 bool supported_large_n_basic(const SpmmArgs& a);
 hipError_t launch_spmm_large_n_basic(const SpmmArgs& a, hipStream_t s);
 
+// N:M patterns other than 2:4 (spmm_nm.hip): kept values plus a keep mask
+// (bit k%8 of byte k/8 of a row).  (n, m) in {(1,4), (2,4), (2,8), (4,8)}.
+bool nm_pattern_supported(int n, int m);
+hipError_t launch_compress_nm(int dt, int n, int m, int64_t M, int64_t K, const void* A, int64_t lda, void* vals,
+                              int64_t ldv, uint8_t* mask, int64_t ldm, bool vec, hipStream_t s);
+hipError_t launch_decompress_nm(int dt, int n, int m, int64_t M, int64_t K, const void* vals, int64_t ldv,
+                                const uint8_t* mask, int64_t ldm, void* D, int64_t ldd, int32_t* bad, hipStream_t s);
+// Product; a.vals / a.meta are the stored values and the mask, rows 16- and
+// 8-byte aligned, B rows 16-byte aligned.
+hipError_t launch_spmm_nm(int n, int m, const SpmmArgs& a, hipStream_t s);
+
 }  // namespace ssg

@@ -436,6 +436,96 @@ int ssg_spmm_2to4_packed(int ab, int c, int64_t M, int64_t N, int64_t K, const v
     return e == hipSuccess ? SSG_OK : hip_fail(e, "packed spmm launch");
 }
 
+int64_t ssg_nm_vals_cols(int nm_n, int nm_m, int64_t K) {
+    return nm_m > 0 && nm_n >= 0 ? K / nm_m * nm_n : 0;
+}
+
+}  // extern "C"
+
+namespace {
+
+int check_nm(int dt, int nm_n, int nm_m, int64_t M, int64_t K, const void* vals, int64_t ldv, const uint8_t* mask,
+             int64_t ldm) {
+    if (!in_dtype(dt)) return fail(SSG_ERR_DTYPE, "element type %d is not SSG_F16, SSG_BF16, SSG_I8, SSG_E4M3 or SSG_E5M2", dt);
+    if (!ssg::nm_pattern_supported(nm_n, nm_m))
+        return fail(SSG_ERR_SHAPE, "pattern %d:%d is not one of 1:4, 2:4, 2:8, 4:8", nm_n, nm_m);
+    if (M < 0 || K < 0) return fail(SSG_ERR_SHAPE, "negative size M=%lld K=%lld", (long long)M, (long long)K);
+    if (K % nm_m != 0) return fail(SSG_ERR_SHAPE, "K=%lld is not a multiple of %d", (long long)K, nm_m);
+    if ((M * ((K + 31) / 32)) / 256 >= (int64_t)1 << 31)
+        return fail(SSG_ERR_SHAPE, "M*K too large (%lld x %lld)", (long long)M, (long long)K);
+    if (M > 0 && K > 0 && (!vals || !mask)) return fail(SSG_ERR_NULL, "vals or mask is NULL");
+    if (ldv < K / nm_m * nm_n)
+        return fail(SSG_ERR_STRIDE, "ldv=%lld < K/%d*%d=%lld", (long long)ldv, nm_m, nm_n, (long long)(K / nm_m * nm_n));
+    if (ldm < (K + 7) / 8) return fail(SSG_ERR_STRIDE, "ldmask=%lld < ceil(K/8)=%lld", (long long)ldm, (long long)((K + 7) / 8));
+    return SSG_OK;
+}
+
+// The compress / expand kernels' 32-element chunks: A or D rows 16-byte
+// aligned, value rows 8-byte aligned, mask rows 4-byte aligned.
+bool vec_nm(int dt, const void* dense, int64_t ldd, const void* vals, int64_t ldv, const uint8_t* mask, int64_t ldm) {
+    return rows_aligned16(dense, ldd, dt) && al(vals, 8) && (ldv * esize(dt)) % 8 == 0 && al(mask, 4) && ldm % 4 == 0;
+}
+
+}  // namespace
+
+extern "C" {
+
+int ssg_compress_nm(int dt, int nm_n, int nm_m, int64_t M, int64_t K, const void* A, int64_t lda, void* vals,
+                    int64_t ldv, uint8_t* mask, int64_t ldmask, void* stream) {
+    int rc = check_nm(dt, nm_n, nm_m, M, K, vals, ldv, mask, ldmask);
+    if (rc) return rc;
+    if (M > 0 && K > 0 && !A) return fail(SSG_ERR_NULL, "A is NULL");
+    if (lda < K) return fail(SSG_ERR_STRIDE, "lda=%lld < K=%lld", (long long)lda, (long long)K);
+    hipError_t e = ssg::launch_compress_nm(to_dt(dt), nm_n, nm_m, M, K, A, lda, vals, ldv, mask, ldmask,
+                                           vec_nm(dt, A, lda, vals, ldv, mask, ldmask), (hipStream_t)stream);
+    return e == hipSuccess ? SSG_OK : hip_fail(e, "compress_nm launch");
+}
+
+int ssg_decompress_nm(int dt, int nm_n, int nm_m, int64_t M, int64_t K, const void* vals, int64_t ldv,
+                      const uint8_t* mask, int64_t ldmask, void* D, int64_t ldd, int32_t* bad_count, void* stream) {
+    int rc = check_nm(dt, nm_n, nm_m, M, K, vals, ldv, mask, ldmask);
+    if (rc) return rc;
+    if (M > 0 && K > 0 && !D) return fail(SSG_ERR_NULL, "D is NULL");
+    if (ldd < K) return fail(SSG_ERR_STRIDE, "ldd=%lld < K=%lld", (long long)ldd, (long long)K);
+    hipError_t e = ssg::launch_decompress_nm(to_dt(dt), nm_n, nm_m, M, K, vals, ldv, mask, ldmask, D, ldd, bad_count,
+                                             (hipStream_t)stream);
+    return e == hipSuccess ? SSG_OK : hip_fail(e, "decompress_nm launch");
+}
+
+int ssg_spmm_nm(int ab, int c, int nm_n, int nm_m, int64_t M, int64_t N, int64_t K, const void* vals, int64_t ldv,
+                const uint8_t* mask, int64_t ldmask, const void* B, int64_t ldb, void* C, int64_t ldc, void* stream) {
+    if (!pair_ok(ab, c)) return fail(SSG_ERR_DTYPE, "unsupported (input, output) types (%d, %d)", ab, c);
+    int rc = check_nm(ab, nm_n, nm_m, M, K, vals, ldv, mask, ldmask);
+    if (rc) return rc;
+    // one grid row per 16 columns of B
+    if (N < 0 || (N + 15) / 16 > 65535) return fail(SSG_ERR_SHAPE, "N=%lld out of range", (long long)N);
+    if (K > 0 && N > 0 && !B) return fail(SSG_ERR_NULL, "B is NULL");
+    if (M > 0 && N > 0 && !C) return fail(SSG_ERR_NULL, "C is NULL");
+    if (ldb < N) return fail(SSG_ERR_STRIDE, "ldb=%lld < N=%lld", (long long)ldb, (long long)N);
+    if (ldc < N) return fail(SSG_ERR_STRIDE, "ldc=%lld < N=%lld", (long long)ldc, (long long)N);
+    if (M == 0 || N == 0) return SSG_OK;
+    const int64_t es = esize(ab);
+    if (K == 0) {
+        // an empty sum: the generic kernel writes the zeros and reads nothing
+        hipError_t e = ssg::launch_spmm_generic(make_args(ab, M, N, 0, nullptr, 0, nullptr, 0, B, ldb, C, ldc),
+                                                (hipStream_t)stream);
+        return e == hipSuccess ? SSG_OK : hip_fail(e, "zero fill");
+    }
+    // row strides matter only where there is more than one row
+    if (!al(vals, 16) || (M > 1 && (ldv * es) % 16 != 0))
+        return fail(SSG_ERR_STRIDE, "vals rows must be 16-byte aligned (base and ldv * element size)");
+    if (!al(mask, 8) || (M > 1 && ldmask % 8 != 0))
+        return fail(SSG_ERR_STRIDE, "mask rows must be 8-byte aligned (base and ldmask)");
+    if (!al(B, 16) || (K > 1 && (ldb * es) % 16 != 0))
+        return fail(SSG_ERR_STRIDE, "B rows must be 16-byte aligned (base and ldb * element size)");
+    // 32-bit buffer offsets: a workgroup's 64 rows of vals / mask, all of B
+    if (64 * ldv * es >= 0x7fffffff || 64 * ldmask >= 0x7fffffff || K * ldb * es >= 0x7fffffff)
+        return fail(SSG_ERR_SHAPE, "operands too large for 31-bit buffer offsets");
+    ssg::SpmmArgs a = make_args(ab, M, N, K, vals, ldv, mask, ldmask, B, ldb, C, ldc);
+    hipError_t e = ssg::launch_spmm_nm(nm_n, nm_m, a, (hipStream_t)stream);
+    return e == hipSuccess ? SSG_OK : hip_fail(e, "spmm_nm launch");
+}
+
 int ssg_spmm_2to4_residual(int ab, int c, int64_t M, int64_t N, int64_t K, const void* vals, int64_t ldv,
                            const uint8_t* meta, int64_t ldm, const int32_t* row_ptr, const int32_t* col,
                            const void* rvals, int64_t nnz_r, const void* B, int64_t ldb, void* C, int64_t ldc,

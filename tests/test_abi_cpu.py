@@ -99,6 +99,37 @@ def test_delta_code_argument_errors(lib):
     assert lib.ssg_spmm_2to4_residual_delta_ex(9, *args, FAKE, FAKE, FAKE, 5, *tail) == _abi.SSG_ERR_ALGO
 
 
+def test_nm_argument_errors(lib):
+    assert [lib.ssg_nm_vals_cols(n, m, 4096) for n, m in [(1, 4), (2, 4), (2, 8), (4, 8)]] == [1024, 2048, 1024, 2048]
+    c = lib.ssg_compress_nm
+    # patterns without kernels, K not a multiple of m, strides, nulls, dtype
+    for n, m in [(3, 8), (1, 8), (4, 4), (0, 4), (2, 16)]:
+        assert c(F16, n, m, 4, 64, FAKE, 64, FAKE, 64, FAKE, 8, None) == _abi.SSG_ERR_SHAPE
+    assert c(F16, 2, 8, 4, 60, FAKE, 60, FAKE, 16, FAKE, 8, None) == _abi.SSG_ERR_SHAPE
+    assert c(F16, 2, 8, 4, 64, FAKE, 63, FAKE, 16, FAKE, 8, None) == _abi.SSG_ERR_STRIDE
+    assert c(F16, 2, 8, 4, 64, FAKE, 64, FAKE, 15, FAKE, 8, None) == _abi.SSG_ERR_STRIDE
+    assert c(F16, 2, 8, 4, 64, FAKE, 64, FAKE, 16, FAKE, 7, None) == _abi.SSG_ERR_STRIDE
+    assert c(F16, 2, 8, 4, 64, None, 64, FAKE, 16, FAKE, 8, None) == _abi.SSG_ERR_NULL
+    assert c(F16, 2, 8, 4, 64, FAKE, 64, FAKE, 16, None, 8, None) == _abi.SSG_ERR_NULL
+    assert c(F32, 2, 8, 4, 64, FAKE, 64, FAKE, 16, FAKE, 8, None) == _abi.SSG_ERR_DTYPE
+    assert c(I8, 1, 4, 0, 64, FAKE, 64, FAKE, 16, FAKE, 8, None) == 0          # nothing to do
+    assert lib.ssg_decompress_nm(F16, 2, 8, 4, 64, FAKE, 16, FAKE, 8, FAKE, 63, None, None) == _abi.SSG_ERR_STRIDE
+    p = lib.ssg_spmm_nm
+    ok = (FAKE, 16, FAKE, 8, FAKE, 16, FAKE, 16, None)
+    assert p(F16, I32, 2, 8, 8, 16, 64, *ok) == _abi.SSG_ERR_DTYPE
+    assert p(F16, F32, 3, 8, 8, 16, 64, *ok) == _abi.SSG_ERR_SHAPE
+    assert p(F16, F32, 2, 8, 8, 16, 64, FAKE, 20, FAKE, 8, FAKE, 16, FAKE, 16, None) == _abi.SSG_ERR_STRIDE  # 40-byte vals rows
+    assert p(F16, F32, 2, 8, 8, 16, 64, FAKE, 16, FAKE, 12, FAKE, 16, FAKE, 16, None) == _abi.SSG_ERR_STRIDE  # mask rows
+    assert p(F16, F32, 2, 8, 8, 12, 64, FAKE, 16, FAKE, 8, FAKE, 12, FAKE, 12, None) == _abi.SSG_ERR_STRIDE  # 24-byte B rows
+    assert p(F16, F32, 2, 8, 8, 16, 64, ctypes.c_void_p(0x1008), 16, FAKE, 8, FAKE, 16, FAKE, 16,
+             None) == _abi.SSG_ERR_STRIDE
+    assert p(F16, F32, 2, 8, 8, 16, 64, FAKE, 16, FAKE, 8, None, 16, FAKE, 16, None) == _abi.SSG_ERR_NULL
+    assert p(F16, F32, 2, 8, 8, 16, 64, FAKE, 16, FAKE, 8, FAKE, 16, None, 16, None) == _abi.SSG_ERR_NULL
+    assert p(F16, F32, 2, 8, 8, 16 * 65536, 64, FAKE, 16, FAKE, 8, FAKE, 16 * 65536, FAKE, 16 * 65536,
+             None) == _abi.SSG_ERR_SHAPE
+    assert p(F16, F32, 2, 8, 0, 16, 64, *ok) == 0                           # M == 0: nothing to do
+
+
 def test_last_error_names_the_problem(lib):
     assert lib.ssg_compress_2to4(F16, 4, 8, FAKE, 7, FAKE, 4, FAKE, 1, None) == _abi.SSG_ERR_STRIDE
     assert "lda=7" in lib.ssg_last_error().decode()
@@ -151,6 +182,7 @@ def test_python_binding_has_no_cpu_fallback():
 def test_python_binding_names_match_the_abi():
     for name in declared_functions():
         if name in ("ssg_abi_version", "ssg_status_str", "ssg_last_error", "ssg_vals_cols", "ssg_meta_cols",
+                    "ssg_nm_vals_cols",
                     "ssg_spmm_2to4_ex", "ssg_spmm_2to4_residual_ex", "ssg_spmm_2to4_residual_delta_ex"):
             continue
         assert hasattr(ssg, name), name

@@ -73,6 +73,10 @@ WORKLOADS = {
                      a_sigma=0.02, klass="small_n"),
     "c4f8": Workload("c4f8", "fp8 (E4M3) prefill-shape SpMM M=28672 K=8192 N=2048", "e4m3", 28672, 8192, 2048, 7,
                      a_sigma=0.02, klass="large_n"),
+    # the decode shape as the dense weight that N:M patterns other than 2:4
+    # (1:4, 2:8, 4:8) are selected from
+    "c3nm": Workload("c3nm", "fp16 N:M decode-shape SpMM M=11008 K=4096 N=16", "f16", 11008, 4096, 16, 8,
+                     a_sigma=0.02, klass="small_n"),
 }
 
 
