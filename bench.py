@@ -181,11 +181,13 @@ def bench_workload(key: str, iters: int, read_GBps: float, delta: bool = False, 
     b = W.gen_b(w).cuda()
     if nm is not None:
         ops = ssg.compress_nm(a, nm[0], nm[1])
+        if packed:
+            ops = ssg.pack_nm(ops[0], ops[1], nm[0], nm[1], w.K)
     else:
         ops = ssg.split(a) if w.residual else ssg.compress(a)
     if delta:
         ops = ops[:2] + ssg.delta_encode(ops[2], ops[3], ops[4], w.K)
-    if packed:
+    if packed and nm is None:
         ops = ssg.pack_decode(ops[0], ops[1], w.K)
     wbytes = sum(t.numel() * t.element_size() for t in ops)
     copies = 1
@@ -197,7 +199,9 @@ def bench_workload(key: str, iters: int, read_GBps: float, delta: bool = False, 
 
     def launch(i):
         o = sets[i % copies]
-        if nm is not None:
+        if nm is not None and packed:
+            ssg.ssg_spmm_nm_packed(o[0], o[1], nm[0], nm[1], w.M, b, out)
+        elif nm is not None:
             ssg.ssg_spmm_nm(o[0], o[1], nm[0], nm[1], w.K, b, out)
         elif packed:
             ssg.ssg_spmm_2to4_packed(o[0], o[1], w.M, b, out)
@@ -221,7 +225,7 @@ def bench_workload(key: str, iters: int, read_GBps: float, delta: bool = False, 
     cbytes = out.numel() * out.element_size()
     r = {"title": w.title + (", residual delta-coded" if delta else "") + (", packed decode layout" if packed else "")
          + (", %d:%d" % tuple(nm) if nm else ""),
-         "algo": "nm (dense MFMA on the expanded operand)" if nm else ssg.ALGO_NAMES[algo] + (" (packed)" if packed else ""),
+         "algo": ("nm (dense MFMA on the expanded operand)" if nm else ssg.ALGO_NAMES[algo]) + (" (packed)" if packed else ""),
          "us_per_launch": s * 1e6,
          "timing": "HIP graph of %d launches, replayed twice; replay output matches eager: %s" % (n, graph_ok),
          "dense_equiv_TFLOPs": flops / s / 1e12, "compressed_weight_bytes": wbytes,
@@ -508,6 +512,10 @@ def main() -> int:
                     print("bench: workload %s, %d:%d ..." % (k, n, m), file=sys.stderr, flush=True)
                     table["%s_%d:%d" % (k, n, m)] = bench_workload(k, args.workload_iters or 200, rbw,
                                                                    dense_cmp=i == 0, nm=(n, m))
+                    print("bench: workload %s, %d:%d, packed decode layout ..." % (k, n, m), file=sys.stderr,
+                          flush=True)
+                    table["%s_%d:%d_packed" % (k, n, m)] = bench_workload(k, args.workload_iters or 200, rbw,
+                                                                          dense_cmp=False, nm=(n, m), packed=True)
                 continue
             print("bench: workload %s ..." % k, file=sys.stderr, flush=True)
             it = args.workload_iters or (200 if W.WORKLOADS[k].klass != "large_n" else 20)

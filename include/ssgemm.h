@@ -299,6 +299,31 @@ int ssg_spmm_nm(int ab, int c, int nm_n, int nm_m, int64_t M, int64_t N, int64_t
                 const uint8_t* mask, int64_t ldmask, const void* B, int64_t ldb, void* C, int64_t ldc,
                 void* stream);
 
+/* Packed decode layout of the N:M operand, made offline like the
+ * compression: for each 16-row tile and super-step (4*D dense k, with
+ * D = 16 / element size * nm_m / nm_n: the k one 16-byte load of stored
+ * values covers), pvals holds one 1 KiB block in which lane l = 16q + r
+ * carries row r's stored bytes [64g + 16q, 64g + 16q + 16) of super-step g,
+ * and pmask one block of 64 * D/8 bytes, lane l's being row r's mask bytes
+ * [g*D/2 + q*D/8, +D/8).  Tiles follow each other, a tile's blocks are
+ * consecutive in g; bytes past a row's end and rows past M are zero.  The
+ * same bytes as (vals, mask), reordered, so every load of the product is
+ * one coalesced block.
+ *
+ * ssg_nm_packed_sizes: bytes of pvals and pmask. */
+int ssg_nm_packed_sizes(int dt, int nm_n, int nm_m, int64_t M, int64_t K, int64_t* vals_bytes,
+                        int64_t* mask_bytes);
+
+/* Pack (vals, mask) into caller-allocated pvals (16-byte aligned) and pmask
+ * (8-byte aligned) of ssg_nm_packed_sizes() bytes. */
+int ssg_pack_nm_decode(int dt, int nm_n, int nm_m, int64_t M, int64_t K, const void* vals, int64_t ldv,
+                       const uint8_t* mask, int64_t ldmask, void* pvals, void* pmask, void* stream);
+
+/* C = expand_nm(packed) x B, as ssg_spmm_nm (B alignment, any N, same
+ * accumulation) with K > 0. */
+int ssg_spmm_nm_packed(int ab, int c, int nm_n, int nm_m, int64_t M, int64_t N, int64_t K, const void* pvals,
+                       const void* pmask, const void* B, int64_t ldb, void* C, int64_t ldc, void* stream);
+
 /* As the SpMM calls above with an explicit algorithm (ssg_algo). */
 int ssg_spmm_2to4_ex(int algo, int ab, int c, int64_t M, int64_t N, int64_t K,
                      const void* vals, int64_t ldv, const uint8_t* meta, int64_t ldm,

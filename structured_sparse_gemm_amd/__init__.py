@@ -30,6 +30,7 @@ __all__ = [
     "ssg_spmm_csr_delta", "spmm_csr", "spmm_csr_delta", "ssg_packed_sizes", "ssg_pack_2to4_decode",
     "ssg_spmm_2to4_packed", "pack_decode", "spmm_packed",
     "ssg_compress_nm", "ssg_decompress_nm", "ssg_spmm_nm", "compress_nm", "decompress_nm", "spmm_nm",
+    "ssg_nm_packed_sizes", "ssg_pack_nm_decode", "ssg_spmm_nm_packed", "pack_nm", "spmm_nm_packed",
     "SSG_ALGO_AUTO", "SSG_ALGO_GENERIC", "SSG_ALGO_SMALL_N", "SSG_ALGO_LARGE_N", "library_path",
 ]
 
@@ -264,6 +265,29 @@ def ssg_spmm_nm(vals: torch.Tensor, mask: torch.Tensor, n: int, m: int, K: int, 
                               _ptr(C, "C"), _ld(C, "C"), _stream(C, stream)), "ssg_spmm_nm")
 
 
+def ssg_nm_packed_sizes(dtype: torch.dtype, n: int, m: int, M: int, K: int) -> Tuple[int, int]:
+    import ctypes
+    vb, mb = ctypes.c_int64(0), ctypes.c_int64(0)
+    dt = _DT.get(dtype)
+    if dt is None:
+        raise SsgError(_abi.SSG_ERR_DTYPE, "unsupported element type %s" % (dtype,))
+    _check(_lib().ssg_nm_packed_sizes(dt, n, m, M, K, ctypes.byref(vb), ctypes.byref(mb)), "ssg_nm_packed_sizes")
+    return vb.value, mb.value
+
+
+def ssg_pack_nm_decode(vals, mask, n: int, m: int, K: int, pvals, pmask, stream=None) -> None:
+    _check(_lib().ssg_pack_nm_decode(_dtype(vals), n, m, vals.shape[0], K, _ptr(vals, "vals"), _ld(vals, "vals"),
+                                     _ptr(mask, "mask"), _ld(mask, "mask"), _ptr(pvals, "pvals"),
+                                     _ptr(pmask, "pmask"), _stream(vals, stream)), "ssg_pack_nm_decode")
+
+
+def ssg_spmm_nm_packed(pvals, pmask, n: int, m: int, M: int, B, C, stream=None) -> None:
+    ab = _dtype(B)
+    _check(_lib().ssg_spmm_nm_packed(ab, _OUT[ab][0], n, m, M, B.shape[1], B.shape[0], _ptr(pvals, "pvals"),
+                                     _ptr(pmask, "pmask"), _ptr(B, "B"), _ld(B, "B"), _ptr(C, "C"), _ld(C, "C"),
+                                     _stream(C, stream)), "ssg_spmm_nm_packed")
+
+
 # ---------------------------------------------------------------- allocating helpers
 
 def prune(A: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
@@ -391,6 +415,23 @@ def spmm_nm(vals: torch.Tensor, mask: torch.Tensor, n: int, m: int, B: torch.Ten
     ab = _dtype(vals)
     C = torch.empty((vals.shape[0], B.shape[1]), dtype=_OUT[ab][1], device=vals.device) if out is None else out
     ssg_spmm_nm(vals, mask, n, m, B.shape[0], B, C)
+    return C
+
+
+def pack_nm(vals: torch.Tensor, mask: torch.Tensor, n: int, m: int, K: int):
+    """(pvals, pmask) byte tensors of the packed decode layout of an n:m operand."""
+    vb, mb = ssg_nm_packed_sizes(vals.dtype, n, m, vals.shape[0], K)
+    pvals = torch.empty(vb, dtype=torch.uint8, device=vals.device)
+    pmask = torch.empty(mb, dtype=torch.uint8, device=vals.device)
+    ssg_pack_nm_decode(vals, mask, n, m, K, pvals, pmask)
+    return pvals, pmask
+
+
+def spmm_nm_packed(pvals: torch.Tensor, pmask: torch.Tensor, n: int, m: int, M: int, B: torch.Tensor,
+                   out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    ab = _dtype(B)
+    C = torch.empty((M, B.shape[1]), dtype=_OUT[ab][1], device=B.device) if out is None else out
+    ssg_spmm_nm_packed(pvals, pmask, n, m, M, B, C)
     return C
 
 

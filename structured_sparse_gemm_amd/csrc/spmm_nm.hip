@@ -302,8 +302,9 @@ __device__ __forceinline__ uint64_t mask_bits(const typename MaskReg<MB>::T& r) 
 }
 
 // C[:, 16*blockIdx.y + (0..15)] for the workgroup's tiles.  a.vals / a.meta
-// are the stored values and the keep mask (rows 16- and 8-byte aligned).
-template <int DT, int NN, int MM, int TM>
+// are the stored values and the keep mask (rows 16- and 8-byte aligned), or
+// with PK their packed decode layout (k_pack_nm).
+template <int DT, int NN, int MM, int TM, bool PK>
 __global__ void __launch_bounds__(kNmWaves * 64) k_spmm_nm(SpmmArgs a, int64_t tiles) {
     using S = NmShape<DT, NN, MM>;
     constexpr int W = kNmWaves, P = S::P;
@@ -327,17 +328,24 @@ __global__ void __launch_bounds__(kNmWaves * 64) k_spmm_nm(SpmmArgs a, int64_t t
     const int64_t nsteps = (a.K + S::SK - 1) / S::SK;
     const int64_t ldvb = a.ldv * S::ES, ldbb = a.ldb * S::ES;
 
-    // ranges rounded up to the load sizes (bases are aligned to them), so a
-    // single row whose stride is not a multiple of them still reads whole
-    const __amdgpu_buffer_rsrc_t rv = rsrc_aligned<16>(reinterpret_cast<const uint8_t*>(a.vals) + r0 * ldvb, rows * ldvb);
-    const __amdgpu_buffer_rsrc_t rm = rsrc_aligned<8>(a.meta + r0 * a.ldm, rows * a.ldm);
+    // row-major: ranges rounded up to the load sizes (bases are aligned to
+    // them), so a single row whose stride is not a multiple of them still
+    // reads whole.  Packed: the workgroup's tiles' blocks, consecutive.
+    const uint8_t* vbase = reinterpret_cast<const uint8_t*>(a.vals);
+    const __amdgpu_buffer_rsrc_t rv =
+        PK ? rsrc(vbase + t0 * nsteps * 1024, nt * nsteps * 1024)
+           : rsrc_aligned<16>(vbase + r0 * ldvb, rows * ldvb);
+    const __amdgpu_buffer_rsrc_t rm =
+        PK ? rsrc(a.meta + t0 * nsteps * 64 * S::MB, nt * nsteps * 64 * S::MB)
+           : rsrc_aligned<8>(a.meta + r0 * a.ldm, rows * a.ldm);
     const __amdgpu_buffer_rsrc_t rb = rsrc_aligned<16>(a.B, a.K * ldbb);
     const int r = lane & 15, q = lane >> 4;
+    constexpr uint32_t VSTEP = PK ? 1024 : 64, MSTEP = PK ? 64 * S::MB : 4 * S::MB;   // bytes per super-step
     uint32_t voff[TM], moff[TM];
 #pragma unroll
     for (int t = 0; t < TM; ++t) {
-        voff[t] = (uint32_t)((16 * t + r) * ldvb + 16 * q);
-        moff[t] = (uint32_t)((16 * t + r) * a.ldm + S::MB * q);
+        voff[t] = PK ? (uint32_t)((t * nsteps * 64 + lane) * 16) : (uint32_t)((16 * t + r) * ldvb + 16 * q);
+        moff[t] = PK ? (uint32_t)((t * nsteps * 64 + lane) * S::MB) : (uint32_t)((16 * t + r) * a.ldm + S::MB * q);
     }
     // lane's B piece of one direct-to-LDS load: 16 bytes of row
     // (j*1024 + 16*lane) / (16*ES) of the super-step
@@ -359,8 +367,8 @@ __global__ void __launch_bounds__(kNmWaves * 64) k_spmm_nm(SpmmArgs a, int64_t t
 #pragma unroll
         for (int t = 0; t < TM; ++t) {
             const bool live = in && t < nt;
-            const uint32_t o = live ? voff[t] + (uint32_t)(g * 64) : kOob;
-            const uint32_t om = live ? moff[t] + (uint32_t)(g * 4 * S::MB) : kOob;
+            const uint32_t o = live ? voff[t] + (uint32_t)(g * VSTEP) : kOob;
+            const uint32_t om = live ? moff[t] + (uint32_t)(g * MSTEP) : kOob;
             asm volatile("buffer_load_dwordx4 %0, %1, %2, 0 offen" : "=v"(av[u][t]) : "v"(o), "s"(rv) : "memory");
             load_mask<S::MB>(mv[u][t], om, rm);
         }
@@ -451,25 +459,56 @@ __global__ void __launch_bounds__(kNmWaves * 64) k_spmm_nm(SpmmArgs a, int64_t t
     }
 }
 
-template <int DT, int NN, int MM, int TM>
+template <int DT, int NN, int MM, int TM, bool PK>
 hipError_t launch_nm_tm(const SpmmArgs& a, int64_t tiles, int64_t G, hipStream_t s) {
     using S = NmShape<DT, NN, MM>;
     const unsigned shm = (unsigned)(kNmWaves * S::P * S::BSTEP + S::LUT);
     const dim3 grid((unsigned)G, (unsigned)((a.N + 15) / 16));
-    hipLaunchKernelGGL((k_spmm_nm<DT, NN, MM, TM>), grid, dim3(64 * kNmWaves), shm, s, a, tiles);
+    hipLaunchKernelGGL((k_spmm_nm<DT, NN, MM, TM, PK>), grid, dim3(64 * kNmWaves), shm, s, a, tiles);
     return hipGetLastError();
 }
 
-template <int DT, int NN, int MM>
+template <int DT, int NN, int MM, bool PK>
 hipError_t launch_nm_t(const SpmmArgs& a, hipStream_t s) {
     const int64_t tiles = (a.M + 15) / 16;
     int64_t G = tiles < 256 ? tiles : 256;
     if (G * kNmTMax < tiles) G = (tiles + kNmTMax - 1) / kNmTMax;
     switch ((int)((tiles + G - 1) / G)) {
-        case 1: return launch_nm_tm<DT, NN, MM, 1>(a, tiles, G, s);
-        case 2: return launch_nm_tm<DT, NN, MM, 2>(a, tiles, G, s);
-        case 3: return launch_nm_tm<DT, NN, MM, 3>(a, tiles, G, s);
-        default: return launch_nm_tm<DT, NN, MM, 4>(a, tiles, G, s);
+        case 1: return launch_nm_tm<DT, NN, MM, 1, PK>(a, tiles, G, s);
+        case 2: return launch_nm_tm<DT, NN, MM, 2, PK>(a, tiles, G, s);
+        case 3: return launch_nm_tm<DT, NN, MM, 3, PK>(a, tiles, G, s);
+        default: return launch_nm_tm<DT, NN, MM, 4, PK>(a, tiles, G, s);
+    }
+}
+
+// ---- packed decode layout ----------------------------------------------------
+//
+// The product's operand in the order it is consumed: for each 16-row tile
+// and super-step, the 64 lanes' 16 value bytes (lane l = 16q + r: row r's
+// stored bytes [64g + 16q, 64g + 16q + 16) of super-step g) as one 1 KiB
+// block, and their MB mask bytes (row r's mask bytes [4g*MB + q*MB, +MB))
+// as one block of 64*MB bytes.  A tile's blocks follow each other in g;
+// bytes past a row's end and rows past M are zero.  Each load of the
+// product is then one fully coalesced block instead of 16 row pieces.
+__global__ void __launch_bounds__(256) k_pack_nm(int64_t M, int64_t tiles, int64_t nsteps, const uint8_t* vals,
+                                                 int64_t ldvb, int64_t vrow, const uint8_t* mask, int64_t ldm,
+                                                 int64_t mrow, int mb, uint8_t* pvals, uint8_t* pmask) {
+    const int64_t n = tiles * nsteps * 64;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
+        const int lane = (int)(i & 63);
+        const int64_t blk = i >> 6, tile = blk / nsteps, g = blk - tile * nsteps;
+        const int64_t row = 16 * tile + (lane & 15);
+        const int q = lane >> 4;
+        const int64_t v0 = g * 64 + 16 * q, m0 = g * 4 * mb + (int64_t)q * mb;
+        uint8_t v[16], m[8];
+#pragma unroll
+        for (int b = 0; b < 16; ++b) v[b] = row < M && v0 + b < vrow ? vals[row * ldvb + v0 + b] : 0;
+#pragma unroll
+        for (int b = 0; b < 8; ++b) m[b] = b < mb && row < M && m0 + b < mrow ? mask[row * ldm + m0 + b] : 0;
+        uint4 w;
+        __builtin_memcpy(&w, v, 16);
+        *reinterpret_cast<uint4*>(pvals + i * 16) = w;
+        for (int b = 0; b < mb; ++b) pmask[i * mb + b] = m[b];
     }
 }
 
@@ -531,7 +570,9 @@ struct DecompressNm {
 
 template <int D, int NN, int MM>
 struct SpmmNm {
-    static hipError_t run(const SpmmArgs* a, hipStream_t s) { return launch_nm_t<D, NN, MM>(*a, s); }
+    static hipError_t run(const SpmmArgs* a, bool packed, hipStream_t s) {
+        return packed ? launch_nm_t<D, NN, MM, true>(*a, s) : launch_nm_t<D, NN, MM, false>(*a, s);
+    }
 };
 
 hipError_t launch_compress_nm(int dt, int n, int m, int64_t M, int64_t K, const void* A, int64_t lda, void* vals,
@@ -546,8 +587,31 @@ hipError_t launch_decompress_nm(int dt, int n, int m, int64_t M, int64_t K, cons
     return nm_dispatch<DecompressNm>(dt, n, m, M, K, vals, ldv, mask, ldm, D, ldd, bad, s);
 }
 
-hipError_t launch_spmm_nm(int n, int m, const SpmmArgs& a, hipStream_t s) {
-    return nm_dispatch<SpmmNm>(a.dt, n, m, &a, s);
+hipError_t launch_spmm_nm(int n, int m, const SpmmArgs& a, bool packed, hipStream_t s) {
+    return nm_dispatch<SpmmNm>(a.dt, n, m, &a, packed, s);
+}
+
+void nm_packed_geometry(int dt, int n, int m, int64_t M, int64_t K, int64_t* tiles, int64_t* nsteps, int* mb) {
+    const int es = dt_bytes(dt);
+    const int64_t d = (16 / es) * m / n;        // dense k per lane per super-step
+    *tiles = (M + 15) / 16;
+    *nsteps = (K + 4 * d - 1) / (4 * d);
+    *mb = (int)(d / 8);
+}
+
+hipError_t launch_pack_nm(int dt, int n, int m, int64_t M, int64_t K, const void* vals, int64_t ldv,
+                          const uint8_t* mask, int64_t ldm, void* pvals, void* pmask, hipStream_t s) {
+    int64_t tiles, nsteps;
+    int mb;
+    nm_packed_geometry(dt, n, m, M, K, &tiles, &nsteps, &mb);
+    const int64_t lanes = tiles * nsteps * 64;
+    if (lanes == 0) return hipSuccess;
+    const int64_t g = (lanes + 255) / 256;
+    const int es = dt_bytes(dt);
+    hipLaunchKernelGGL(k_pack_nm, dim3((unsigned)(g < 8192 ? g : 8192)), dim3(256), 0, s, M, tiles, nsteps,
+                       (const uint8_t*)vals, ldv * es, K / m * n * es, mask, ldm, (K + 7) / 8, mb, (uint8_t*)pvals,
+                       (uint8_t*)pmask);
+    return hipGetLastError();
 }
 
 }  // namespace ssg

@@ -78,7 +78,14 @@ hipError_t launch_compress_nm(int dt, int n, int m, int64_t M, int64_t K, const 
 hipError_t launch_decompress_nm(int dt, int n, int m, int64_t M, int64_t K, const void* vals, int64_t ldv,
                                 const uint8_t* mask, int64_t ldm, void* D, int64_t ldd, int32_t* bad, hipStream_t s);
 // Product; a.vals / a.meta are the stored values and the mask, rows 16- and
-// 8-byte aligned, B rows 16-byte aligned.
-hipError_t launch_spmm_nm(int n, int m, const SpmmArgs& a, hipStream_t s);
+// 8-byte aligned, or (packed) their packed decode layout; B rows 16-byte
+// aligned.
+hipError_t launch_spmm_nm(int n, int m, const SpmmArgs& a, bool packed, hipStream_t s);
+// Packed decode layout of the N:M operand: tiles of 16 rows, super-steps of
+// 4*D dense k, mb mask bytes per lane per super-step; pvals holds
+// tiles*nsteps KiB, pmask tiles*nsteps*64*mb bytes.
+void nm_packed_geometry(int dt, int n, int m, int64_t M, int64_t K, int64_t* tiles, int64_t* nsteps, int* mb);
+hipError_t launch_pack_nm(int dt, int n, int m, int64_t M, int64_t K, const void* vals, int64_t ldv,
+                          const uint8_t* mask, int64_t ldm, void* pvals, void* pmask, hipStream_t s);
 
 }  // namespace ssg

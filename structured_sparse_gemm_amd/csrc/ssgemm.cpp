@@ -444,8 +444,7 @@ int64_t ssg_nm_vals_cols(int nm_n, int nm_m, int64_t K) {
 
 namespace {
 
-int check_nm(int dt, int nm_n, int nm_m, int64_t M, int64_t K, const void* vals, int64_t ldv, const uint8_t* mask,
-             int64_t ldm) {
+int check_nm_shape(int dt, int nm_n, int nm_m, int64_t M, int64_t K) {
     if (!in_dtype(dt)) return fail(SSG_ERR_DTYPE, "element type %d is not SSG_F16, SSG_BF16, SSG_I8, SSG_E4M3 or SSG_E5M2", dt);
     if (!ssg::nm_pattern_supported(nm_n, nm_m))
         return fail(SSG_ERR_SHAPE, "pattern %d:%d is not one of 1:4, 2:4, 2:8, 4:8", nm_n, nm_m);
@@ -453,6 +452,13 @@ int check_nm(int dt, int nm_n, int nm_m, int64_t M, int64_t K, const void* vals,
     if (K % nm_m != 0) return fail(SSG_ERR_SHAPE, "K=%lld is not a multiple of %d", (long long)K, nm_m);
     if ((M * ((K + 31) / 32)) / 256 >= (int64_t)1 << 31)
         return fail(SSG_ERR_SHAPE, "M*K too large (%lld x %lld)", (long long)M, (long long)K);
+    return SSG_OK;
+}
+
+int check_nm(int dt, int nm_n, int nm_m, int64_t M, int64_t K, const void* vals, int64_t ldv, const uint8_t* mask,
+             int64_t ldm) {
+    int rc = check_nm_shape(dt, nm_n, nm_m, M, K);
+    if (rc) return rc;
     if (M > 0 && K > 0 && (!vals || !mask)) return fail(SSG_ERR_NULL, "vals or mask is NULL");
     if (ldv < K / nm_m * nm_n)
         return fail(SSG_ERR_STRIDE, "ldv=%lld < K/%d*%d=%lld", (long long)ldv, nm_m, nm_n, (long long)(K / nm_m * nm_n));
@@ -522,8 +528,59 @@ int ssg_spmm_nm(int ab, int c, int nm_n, int nm_m, int64_t M, int64_t N, int64_t
     if (64 * ldv * es >= 0x7fffffff || 64 * ldmask >= 0x7fffffff || K * ldb * es >= 0x7fffffff)
         return fail(SSG_ERR_SHAPE, "operands too large for 31-bit buffer offsets");
     ssg::SpmmArgs a = make_args(ab, M, N, K, vals, ldv, mask, ldmask, B, ldb, C, ldc);
-    hipError_t e = ssg::launch_spmm_nm(nm_n, nm_m, a, (hipStream_t)stream);
+    hipError_t e = ssg::launch_spmm_nm(nm_n, nm_m, a, false, (hipStream_t)stream);
     return e == hipSuccess ? SSG_OK : hip_fail(e, "spmm_nm launch");
+}
+
+int ssg_nm_packed_sizes(int dt, int nm_n, int nm_m, int64_t M, int64_t K, int64_t* vals_bytes,
+                        int64_t* mask_bytes) {
+    int rc = check_nm_shape(dt, nm_n, nm_m, M, K);
+    if (rc) return rc;
+    if (!vals_bytes || !mask_bytes) return fail(SSG_ERR_NULL, "vals_bytes or mask_bytes is NULL");
+    int64_t tiles, nsteps;
+    int mb;
+    ssg::nm_packed_geometry(to_dt(dt), nm_n, nm_m, M, K, &tiles, &nsteps, &mb);
+    *vals_bytes = tiles * nsteps * 1024;
+    *mask_bytes = tiles * nsteps * 64 * mb;
+    return SSG_OK;
+}
+
+int ssg_pack_nm_decode(int dt, int nm_n, int nm_m, int64_t M, int64_t K, const void* vals, int64_t ldv,
+                       const uint8_t* mask, int64_t ldmask, void* pvals, void* pmask, void* stream) {
+    int rc = check_nm(dt, nm_n, nm_m, M, K, vals, ldv, mask, ldmask);
+    if (rc) return rc;
+    int64_t vb, mb;
+    rc = ssg_nm_packed_sizes(dt, nm_n, nm_m, M, K, &vb, &mb);
+    if (rc) return rc;
+    if (vb > 0 && (!pvals || !pmask)) return fail(SSG_ERR_NULL, "pvals or pmask is NULL");
+    if (!al(pvals, 16) || !al(pmask, 8)) return fail(SSG_ERR_STRIDE, "pvals must be 16-byte and pmask 8-byte aligned");
+    hipError_t e = ssg::launch_pack_nm(to_dt(dt), nm_n, nm_m, M, K, vals, ldv, mask, ldmask, pvals, pmask,
+                                       (hipStream_t)stream);
+    return e == hipSuccess ? SSG_OK : hip_fail(e, "pack_nm launch");
+}
+
+int ssg_spmm_nm_packed(int ab, int c, int nm_n, int nm_m, int64_t M, int64_t N, int64_t K, const void* pvals,
+                       const void* pmask, const void* B, int64_t ldb, void* C, int64_t ldc, void* stream) {
+    if (!pair_ok(ab, c)) return fail(SSG_ERR_DTYPE, "unsupported (input, output) types (%d, %d)", ab, c);
+    int64_t vb, mb;
+    int rc = ssg_nm_packed_sizes(ab, nm_n, nm_m, M, K, &vb, &mb);
+    if (rc) return rc;
+    if (N < 0 || (N + 15) / 16 > 65535) return fail(SSG_ERR_SHAPE, "N=%lld out of range", (long long)N);
+    if (M == 0 || N == 0) return SSG_OK;
+    if (K == 0) return fail(SSG_ERR_SHAPE, "K must be positive");
+    if (!pvals || !pmask || !B || !C) return fail(SSG_ERR_NULL, "a required pointer is NULL");
+    if (ldb < N) return fail(SSG_ERR_STRIDE, "ldb=%lld < N=%lld", (long long)ldb, (long long)N);
+    if (ldc < N) return fail(SSG_ERR_STRIDE, "ldc=%lld < N=%lld", (long long)ldc, (long long)N);
+    const int64_t es = esize(ab);
+    if (!al(pvals, 16) || !al(pmask, 8)) return fail(SSG_ERR_STRIDE, "pvals must be 16-byte and pmask 8-byte aligned");
+    if (!al(B, 16) || (K > 1 && (ldb * es) % 16 != 0))
+        return fail(SSG_ERR_STRIDE, "B rows must be 16-byte aligned (base and ldb * element size)");
+    // 32-bit buffer offsets: a workgroup's 4 tiles of blocks, all of B
+    if (4 * (vb / ((M + 15) / 16)) >= 0x7fffffff || K * ldb * es >= 0x7fffffff)
+        return fail(SSG_ERR_SHAPE, "operands too large for 31-bit buffer offsets");
+    ssg::SpmmArgs a = make_args(ab, M, N, K, pvals, 0, static_cast<const uint8_t*>(pmask), 0, B, ldb, C, ldc);
+    hipError_t e = ssg::launch_spmm_nm(nm_n, nm_m, a, true, (hipStream_t)stream);
+    return e == hipSuccess ? SSG_OK : hip_fail(e, "spmm_nm_packed launch");
 }
 
 int ssg_spmm_2to4_residual(int ab, int c, int64_t M, int64_t N, int64_t K, const void* vals, int64_t ldv,

@@ -128,6 +128,23 @@ def test_nm_argument_errors(lib):
     assert p(F16, F32, 2, 8, 8, 16 * 65536, 64, FAKE, 16, FAKE, 8, FAKE, 16 * 65536, FAKE, 16 * 65536,
              None) == _abi.SSG_ERR_SHAPE
     assert p(F16, F32, 2, 8, 0, 16, 64, *ok) == 0                           # M == 0: nothing to do
+    # packed layout: sizes by their closed form, argument errors
+    vb, mb = ctypes.c_int64(0), ctypes.c_int64(0)
+    for dt, n, m, M, K, want in [(F16, 1, 4, 11008, 4096, (688 * 32 * 1024, 688 * 32 * 64 * 4)),
+                                 (F16, 2, 4, 20, 100, (2 * 2 * 1024, 2 * 2 * 64 * 2)),
+                                 (I8, 2, 8, 16, 4096, (1 * 16 * 1024, 1 * 16 * 64 * 8)),
+                                 (I8, 4, 8, 17, 128, (2 * 1 * 1024, 2 * 1 * 64 * 4))]:
+        assert lib.ssg_nm_packed_sizes(dt, n, m, M, K, ctypes.byref(vb), ctypes.byref(mb)) == 0
+        assert (vb.value, mb.value) == want
+    assert lib.ssg_nm_packed_sizes(F16, 3, 8, 16, 64, ctypes.byref(vb), ctypes.byref(mb)) == _abi.SSG_ERR_SHAPE
+    assert lib.ssg_nm_packed_sizes(F16, 2, 8, 16, 64, None, ctypes.byref(mb)) == _abi.SSG_ERR_NULL
+    q = lib.ssg_spmm_nm_packed
+    assert q(F16, F32, 2, 8, 8, 16, 0, FAKE, FAKE, FAKE, 16, FAKE, 16, None) == _abi.SSG_ERR_SHAPE
+    assert q(F16, F32, 2, 8, 8, 16, 64, ctypes.c_void_p(0x1004), FAKE, FAKE, 16, FAKE, 16,
+             None) == _abi.SSG_ERR_STRIDE
+    assert q(F16, F32, 2, 8, 8, 16, 64, FAKE, FAKE, FAKE, 12, FAKE, 16, None) == _abi.SSG_ERR_STRIDE
+    assert q(F16, F32, 2, 8, 8, 16, 64, None, FAKE, FAKE, 16, FAKE, 16, None) == _abi.SSG_ERR_NULL
+    assert lib.ssg_pack_nm_decode(F16, 2, 8, 8, 64, FAKE, 16, FAKE, 8, None, FAKE, None) == _abi.SSG_ERR_NULL
 
 
 def test_last_error_names_the_problem(lib):

@@ -206,3 +206,59 @@ def test_spmm_nm_argument_errors():
         vb[:, :64] = vals
         ssg.ssg_spmm_nm(vb[:, :64], mask, 2, 8, 256, B, C)      # 130-byte rows of vals
     assert e.value.status == ssg._abi.SSG_ERR_STRIDE
+
+
+# ------------------------------------------------------------------ packed decode layout
+
+def expected_packed_nm(dt, n, m, vals, mask, M, K):
+    """The packed layout written out from its definition with numpy: per tile
+    and super-step, lane l = 16q + r carries row r's value bytes
+    [64g + 16q, +16) and mask bytes [g*D/2 + q*D/8, +D/8)."""
+    es = 2 if dt in ("f16", "bf16") else 1
+    D = (16 // es) * m // n
+    SK, MB = 4 * D, D // 8
+    nsteps, tiles = -(-K // SK), -(-M // 16)
+    vb = np.ascontiguousarray(vals).view(np.uint8).reshape(M, -1)
+    Vp = np.zeros((tiles * 16, nsteps * 64), dtype=np.uint8)
+    Vp[:M, :vb.shape[1]] = vb
+    Mp = np.zeros((tiles * 16, nsteps * 4 * MB), dtype=np.uint8)
+    Mp[:M, :mask.shape[1]] = mask
+    pv = Vp.reshape(tiles, 16, nsteps, 4, 16).transpose(0, 2, 3, 1, 4).reshape(-1)
+    pm = Mp.reshape(tiles, 16, nsteps, 4, MB).transpose(0, 2, 3, 1, 4).reshape(-1)
+    return pv, pm
+
+
+@pytest.mark.parametrize("dt", DTS)
+@pytest.mark.parametrize("pat", PATS, ids=PAT_IDS)
+@pytest.mark.parametrize("shape", [(1, 64, 16), (37, 264, 5), (300, 2048, 40), (8200, 512, 16)],
+                         ids=["1x64x16", "37x264x5", "300x2048x40", "8200x512x16"])
+def test_packed_layout_and_product(dt, pat, shape):
+    n, m = pat
+    M, K, N = shape
+    a = U.random_matrix(dt, M, K, "normal", seed=M + 2 * K + N)
+    b = U.random_matrix(dt, K, N, "normal", seed=M * 5 + N)
+    vals, mask = ssg.compress_nm(to_dev(a, dt), n, m)
+    pvals, pmask = ssg.pack_nm(vals, mask, n, m, K)
+    rv, rmask = oracle.compress_nm(dt, n, m, a)
+    ev, em = expected_packed_nm(dt, n, m, rv, rmask, M, K)
+    assert np.array_equal(pvals.cpu().numpy(), ev)
+    assert np.array_equal(pmask.cpu().numpy(), em)
+    C = ssg.spmm_nm_packed(pvals, pmask, n, m, M, b_dev(b, dt))
+    c_ref, s_ref = oracle.spmm_nm(dt, n, m, rv, rmask, b, K)
+    check_product(dt, to_host(C), c_ref, s_ref, "packed %s %d:%d %s" % (dt, n, m, shape))
+
+
+@pytest.mark.parametrize("pat", PATS, ids=PAT_IDS)
+@pytest.mark.parametrize("dt", ["f16", "i8", "e4m3"])
+def test_packed_decode_workload_full_size(dt, pat):
+    n, m = pat
+    w = W.WORKLOADS["c3nm"]
+    w = W.Workload(w.key, w.title, dt, w.M, w.K, w.N, w.index, a_sigma=w.a_sigma, klass=w.klass)
+    a_t, b_t = W.gen_a(w), W.gen_b(w)
+    a, b = W.bits(a_t), W.bits(b_t)
+    vals, mask = ssg.compress_nm(a_t.cuda(), n, m)
+    pvals, pmask = ssg.pack_nm(vals, mask, n, m, w.K)
+    C = ssg.spmm_nm_packed(pvals, pmask, n, m, w.M, b_t.cuda())
+    rv, rmask = oracle.compress_nm(dt, n, m, a)
+    c_ref, s_ref = oracle.spmm_nm(dt, n, m, rv, rmask, b, w.K)
+    check_product(dt, to_host(C), c_ref, s_ref, "c3nm packed %s %d:%d" % (dt, n, m))
