@@ -262,3 +262,23 @@ def test_packed_decode_workload_full_size(dt, pat):
     rv, rmask = oracle.compress_nm(dt, n, m, a)
     c_ref, s_ref = oracle.spmm_nm(dt, n, m, rv, rmask, b, w.K)
     check_product(dt, to_host(C), c_ref, s_ref, "c3nm packed %s %d:%d" % (dt, n, m))
+
+
+@pytest.mark.parametrize("dt", ["f16", "i8", "e4m3"])
+@pytest.mark.parametrize("pat", [(1, 4), (2, 8)], ids=["1:4", "2:8"])
+def test_patterns_within_2to4_run_on_the_sparse_mfma(dt, pat):
+    """1:4 and 2:8 never keep more than two values in an aligned group of
+    four, so the 2:4 form of their expansion is the same matrix and the
+    2:4 prefill kernel computes the same product."""
+    n, m = pat
+    M, K, N = 512, 1024, 512
+    a = U.random_matrix(dt, M, K, "normal", seed=3 + n + m)
+    b = U.random_matrix(dt, K, N, "normal", seed=4 + n + m)
+    vals, mask = ssg.compress_nm(to_dev(a, dt), n, m)
+    D = ssg.decompress_nm(vals, mask, n, m, K)
+    v24, meta = ssg.compress(D)
+    assert np.array_equal(to_host(ssg.decompress(v24, meta, K)), to_host(D))
+    C = ssg.spmm(v24, meta, to_dev(b, dt), algo=ssg.SSG_ALGO_LARGE_N)
+    rv, rmask = oracle.compress_nm(dt, n, m, a)
+    c_ref, s_ref = oracle.spmm_nm(dt, n, m, rv, rmask, b, K)
+    check_product(dt, to_host(C), c_ref, s_ref, "%d:%d via 2:4 large-N" % pat)
