@@ -44,7 +44,8 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 # source files that make up each profiled kernel (counters go stale when one changes)
 KERNEL_SOURCES = {
     "spmm_large_n": ("spmm_large_n.hip", "ssg_device.hpp", "ssg_kernels.hpp"),
-    "spmm_small_n": ("spmm_small_n.hip", "ssg_device.hpp", "ssg_kernels.hpp"),
+    "spmm_small_n": ("spmm_small_n.hip", "ssg_device.hpp", "ssg_kernels.hpp", "ssg_stream.hpp"),
+    "spmm_nm": ("spmm_nm.hip", "ssg_device.hpp", "ssg_kernels.hpp", "ssg_stream.hpp"),
     "compress": ("compress.hip", "ssg_device.hpp", "ssg_kernels.hpp"),
 }
 
