@@ -29,7 +29,7 @@ _LIB = os.path.join(_HERE, "liboracle.so")
 # planted mistake) to show that the pins catch it.
 _OVERRIDE = os.environ.get("SSG_ORACLE_LIB")
 
-DTYPES = {"f16": 0, "bf16": 1, "i8": 2, "e4m3": 3, "e5m2": 4}
+DTYPES = {"f16": 0, "bf16": 1, "i8": 2, "e4m3": 3, "e5m2": 4, "i4": 5}
 ERRORS = {
     -1: "null pointer", -2: "bad shape", -3: "bad stride", -4: "bad dtype",
     -5: "non-finite input", -6: "bad format", -7: "out of memory", -8: "out of range",
@@ -99,6 +99,10 @@ def _load():
             lib.orc_decompress_nm.restype = _i64
             lib.orc_spmm_nm.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, _i64, _i64, _i64, _vp, _i64, _vp,
                                         _i64, _vp, _i64, _vp, _vp, _vp, _i64]
+            lib.orc_spmm_nm_w4a16.argtypes = [ctypes.c_int, ctypes.c_int, _i64, _i64, _i64, _vp, _i64, _vp, _i64,
+                                              _vp, _i64, _vp, _vp, _i64]
+            lib.orc_i4_to_f64.argtypes = [ctypes.c_uint8, ctypes.c_int]
+            lib.orc_i4_to_f64.restype = ctypes.c_double
             lib.orc_spmm_csr.argtypes = [ctypes.c_int, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _i64, _vp, _vp, _vp,
                                          _i64]
             lib.orc_num_threads.restype = ctypes.c_int
@@ -122,7 +126,7 @@ def _p(a):
 def _store_dtype(dt: str):
     if dt not in DTYPES:
         raise OracleError("unknown dtype %r" % (dt,))
-    return np.int8 if dt == "i8" else (np.uint8 if dt in ("e4m3", "e5m2") else np.uint16)
+    return np.int8 if dt == "i8" else (np.uint8 if dt in ("e4m3", "e5m2", "i4") else np.uint16)
 
 
 def _mat(a, dt: str) -> np.ndarray:
@@ -338,34 +342,58 @@ def select_nm(n: int, m: int, mag) -> list:
     return [int(x) for x in keep]
 
 
+def i4_to_f64(byte: int, high: bool) -> float:
+    return _load().orc_i4_to_f64(int(byte), int(bool(high)))
+
+
+def _per(dt: str) -> int:
+    """Elements per storage unit: 2 for 4-bit integers (two per byte), else 1."""
+    return 2 if dt == "i4" else 1
+
+
 def compress_nm(dt: str, n: int, m: int, A):
     """N:M compressed form of A: (vals [M, K/m*n], mask uint8 [M, ceil(K/8)]);
-    mask bit k % 8 of byte k / 8 is set iff element k is kept."""
+    mask bit k % 8 of byte k / 8 is set iff element k is kept.  For "i4" the
+    arrays hold two elements per byte (A [M, K/2], vals [M, K/m*n/2])."""
     A = _mat(A, dt)
-    M, K = A.shape
+    e = _per(dt)
+    M, K = A.shape[0], A.shape[1] * e
     vc = K // m * n if m > 0 else 0
-    vals = np.zeros((M, vc), dtype=A.dtype)
+    vals = np.zeros((M, -(-vc // e)), dtype=A.dtype)
     mask = np.zeros((M, meta_cols(K)), dtype=np.uint8)
-    _check(_load().orc_compress_nm(DTYPES[dt], n, m, M, K, _p(A), _ld(A), _p(vals), max(vc, 1), _p(mask),
-                                   max(meta_cols(K), 1)), "compress_nm")
+    _check(_load().orc_compress_nm(DTYPES[dt], n, m, M, K, _p(A), _ld(A) * e, _p(vals), max(vals.shape[1] * e, e),
+                                   _p(mask), max(meta_cols(K), 1)), "compress_nm")
     return vals, mask
 
 
 def decompress_nm(dt: str, n: int, m: int, vals, mask, K: int):
     """(D, number of groups whose mask does not hold exactly n bits)."""
     vals = _mat(vals, dt)
+    e = _per(dt)
     mask = np.ascontiguousarray(np.asarray(mask, dtype=np.uint8))
     M = vals.shape[0]
-    D = np.zeros((M, K), dtype=vals.dtype)
-    bad = _load().orc_decompress_nm(DTYPES[dt], n, m, M, K, _p(vals), max(vals.shape[1], 1), _p(mask),
-                                    max(mask.shape[1], 1), _p(D), max(K, 1))
+    D = np.zeros((M, -(-K // e)), dtype=vals.dtype)
+    bad = _load().orc_decompress_nm(DTYPES[dt], n, m, M, K, _p(vals), max(vals.shape[1] * e, e), _p(mask),
+                                    max(mask.shape[1], 1), _p(D), max(D.shape[1] * e, e))
     _check(bad, "decompress_nm")
     return D, int(bad)
 
 
 def spmm_nm(dt: str, n: int, m: int, vals, mask, B, K: int):
-    """C = decompress_nm(vals, mask) @ B: (C fp64, S) for floats, (C int64, None) for int8."""
+    """C = decompress_nm(vals, mask) @ B: (C fp64, S) for floats, (C int64, None) for int8.
+    For "i4" weights B is fp16 (raw uint16 bits)."""
     vals = _mat(vals, dt)
+    if dt == "i4":
+        B = _mat(B, "f16")
+        mask = np.ascontiguousarray(np.asarray(mask, dtype=np.uint8))
+        M, N = vals.shape[0], B.shape[1]
+        if B.shape[0] != K:
+            raise OracleError("B has %d rows, K is %d" % (B.shape[0], K))
+        C, S = np.zeros((M, N), dtype=np.float64), np.zeros((M, N), dtype=np.float64)
+        _check(_load().orc_spmm_nm_w4a16(n, m, M, N, K, _p(vals), max(vals.shape[1] * 2, 2), _p(mask),
+                                         max(mask.shape[1], 1), _p(B), _ld(B) if K > 0 else max(N, 1), _p(C), _p(S),
+                                         max(N, 1)), "spmm_nm_w4a16")
+        return C, S
     B = _mat(B, dt)
     mask = np.ascontiguousarray(np.asarray(mask, dtype=np.uint8))
     M, N = vals.shape[0], B.shape[1]

@@ -82,7 +82,22 @@ static int valid_dtype(int dt) {
 }
 static size_t esize(int dt) { return dt == ORC_F16 || dt == ORC_BF16 ? 2 : 1; }
 
+/* 4-bit two's-complement integers, two per byte: element i is the low
+ * nibble of byte i/2 for even i, the high nibble for odd i. */
+static int i4_get(const void* base, int64_t i) {
+    int nib = (((const uint8_t*)base)[i / 2] >> (4 * (i % 2))) & 0xF;
+    return nib >= 8 ? nib - 16 : nib;
+}
+static void i4_set(void* base, int64_t i, int v) {
+    uint8_t* b = (uint8_t*)base + i / 2;
+    int sh = 4 * (int)(i % 2);
+    *b = (uint8_t)((*b & ~(0xF << sh)) | ((v & 0xF) << sh));
+}
+
+double orc_i4_to_f64(uint8_t byte, int high) { return (double)i4_get(&byte, high ? 1 : 0); }
+
 static double elem_f64(int dt, const void* base, int64_t i) {
+    if (dt == ORC_I4) return (double)i4_get(base, i);
     if (dt == ORC_I8) return (double)((const int8_t*)base)[i];
     if (dt == ORC_E4M3) return orc_e4m3_to_f64(((const uint8_t*)base)[i]);
     if (dt == ORC_E5M2) return orc_e5m2_to_f64(((const uint8_t*)base)[i]);
@@ -93,11 +108,13 @@ static double elem_f64(int dt, const void* base, int64_t i) {
 static int64_t elem_i64(const void* base, int64_t i) { return (int64_t)((const int8_t*)base)[i]; }
 
 static void elem_copy(int dt, void* dst, int64_t di, const void* src, int64_t si) {
+    if (dt == ORC_I4) { i4_set(dst, di, i4_get(src, si)); return; }
     size_t s = esize(dt);
     memcpy((char*)dst + (size_t)di * s, (const char*)src + (size_t)si * s, s);
 }
 
 static void elem_zero(int dt, void* dst, int64_t di) {
+    if (dt == ORC_I4) { i4_set(dst, di, 0); return; }
     memset((char*)dst + (size_t)di * esize(dt), 0, esize(dt));
 }
 
@@ -599,7 +616,8 @@ void orc_select_nm(int nm_n, int nm_m, const double* mag, int* keep) {
 }
 
 static int check_nm_shape(int dt, int nm_n, int nm_m, int64_t M, int64_t K) {
-    if (!valid_dtype(dt)) return ORC_EDTYPE;
+    if (!valid_dtype(dt) && dt != ORC_I4) return ORC_EDTYPE;
+    if (dt == ORC_I4 && K % 2 != 0) return ORC_ESHAPE;
     if (!nm_ok(nm_n, nm_m) || M < 0 || K < 0 || K % nm_m != 0) return ORC_ESHAPE;
     return ORC_OK;
 }
@@ -610,6 +628,7 @@ int orc_compress_nm(int dt, int nm_n, int nm_m, int64_t M, int64_t K, const void
     if (rc) return rc;
     if (M > 0 && K > 0 && (!A || !vals || !mask)) return ORC_ENULL;
     if (lda < K || ldv < K / nm_m * nm_n || ldmask < meta_cols(K)) return ORC_ESTRIDE;
+    if (dt == ORC_I4 && (lda % 2 || ldv % 2)) return ORC_ESTRIDE;   /* rows start on whole bytes */
     for (int64_t m = 0; m < M; ++m) {
         for (int64_t j = 0; j < meta_cols(K); ++j) mask[m * ldmask + j] = 0;
         for (int64_t g = 0; g < K / nm_m; ++g) {
@@ -671,16 +690,20 @@ int64_t orc_decompress_nm(int dt, int nm_n, int nm_m, int64_t M, int64_t K, cons
     if (rc) return rc;
     if (M > 0 && K > 0 && (!vals || !mask || !D)) return ORC_ENULL;
     if (ldv < K / nm_m * nm_n || ldmask < meta_cols(K) || ldd < K) return ORC_ESTRIDE;
+    if (dt == ORC_I4 && (ldv % 2 || ldd % 2)) return ORC_ESTRIDE;
     int64_t bad = 0;
     for (int64_t m = 0; m < M; ++m) bad += nm_row(dt, nm_n, nm_m, K, vals, ldv, mask, ldmask, m, NULL, NULL, D, ldd);
     return bad;
 }
 
-int orc_spmm_nm(int dt, int nm_n, int nm_m, int64_t M, int64_t N, int64_t K, const void* vals, int64_t ldv,
-                const uint8_t* mask, int64_t ldmask, const void* B, int64_t ldb, double* Cf, int64_t* Ci, double* S,
-                int64_t ldc) {
+/* adt: element type of the N:M operand; bdt: that of B (the same, or fp16
+ * for 4-bit weights).  int8 x int8 sums in int64, everything else in fp64. */
+static int spmm_nm_impl(int dt, int bdt, int nm_n, int nm_m, int64_t M, int64_t N, int64_t K, const void* vals,
+                        int64_t ldv, const uint8_t* mask, int64_t ldmask, const void* B, int64_t ldb, double* Cf,
+                        int64_t* Ci, double* S, int64_t ldc) {
     int rc = check_nm_shape(dt, nm_n, nm_m, M, K);
     if (rc) return rc;
+    if (dt == ORC_I4 && ldv % 2) return ORC_ESTRIDE;
     if (N < 0) return ORC_ESHAPE;
     if (M > 0 && K > 0 && (!vals || !mask)) return ORC_ENULL;
     if (K > 0 && N > 0 && !B) return ORC_ENULL;
@@ -712,7 +735,7 @@ int orc_spmm_nm(int dt, int nm_n, int nm_m, int64_t M, int64_t N, int64_t K, con
                 } else {
                     double acc = 0.0, s = 0.0;
                     for (int64_t k = 0; k < K; ++k) {
-                        double t = rowf[k] * elem_f64(dt, B, k * ldb + n);
+                        double t = rowf[k] * elem_f64(bdt, B, k * ldb + n);
                         acc += t;
                         s += fabs(t);
                     }
@@ -725,6 +748,19 @@ int orc_spmm_nm(int dt, int nm_n, int nm_m, int64_t M, int64_t N, int64_t K, con
         free(rowi);
     }
     return err;
+}
+
+int orc_spmm_nm(int dt, int nm_n, int nm_m, int64_t M, int64_t N, int64_t K, const void* vals, int64_t ldv,
+                const uint8_t* mask, int64_t ldmask, const void* B, int64_t ldb, double* Cf, int64_t* Ci, double* S,
+                int64_t ldc) {
+    if (dt == ORC_I4) return ORC_EDTYPE;                  /* 4-bit weights take fp16 B: orc_spmm_nm_w4a16 */
+    return spmm_nm_impl(dt, dt, nm_n, nm_m, M, N, K, vals, ldv, mask, ldmask, B, ldb, Cf, Ci, S, ldc);
+}
+
+int orc_spmm_nm_w4a16(int nm_n, int nm_m, int64_t M, int64_t N, int64_t K, const void* vals, int64_t ldv,
+                      const uint8_t* mask, int64_t ldmask, const void* B, int64_t ldb, double* Cf, double* S,
+                      int64_t ldc) {
+    return spmm_nm_impl(ORC_I4, ORC_F16, nm_n, nm_m, M, N, K, vals, ldv, mask, ldmask, B, ldb, Cf, NULL, S, ldc);
 }
 
 int orc_num_threads(void) {

@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-enum { ORC_F16 = 0, ORC_BF16 = 1, ORC_I8 = 2, ORC_E4M3 = 3, ORC_E5M2 = 4 };
+enum { ORC_F16 = 0, ORC_BF16 = 1, ORC_I8 = 2, ORC_E4M3 = 3, ORC_E5M2 = 4, ORC_I4 = 5 };
 enum { ORC_OK = 0, ORC_ENULL = -1, ORC_ESHAPE = -2, ORC_ESTRIDE = -3, ORC_EDTYPE = -4,
        ORC_ENONFINITE = -5, ORC_EFORMAT = -6, ORC_ENOMEM = -7, ORC_ERANGE = -8 };
 
@@ -62,6 +62,13 @@ double orc_bf16_to_f64(uint16_t bits);
  * S.1111.111 is NaN) and E5M2 (bias 15, IEEE-style infinities and NaNs). */
 double orc_e4m3_to_f64(uint8_t bits);
 double orc_e5m2_to_f64(uint8_t bits);
+/* ORC_I4: 4-bit two's-complement integers (-8..7), two per byte, element i
+ * in the low nibble of byte i/2 for even i and the high nibble for odd i
+ * ([P3] "Sparsity + Quantization Combine" stacks 2:4 with 4-bit weights).
+ * Only the N:M functions below take it, as the weight; leading dimensions
+ * stay counted in elements and must be even.  orc_i4_to_f64: the value of
+ * the low (high = 0) or high nibble of a byte. */
+double orc_i4_to_f64(uint8_t byte, int high);
 
 /* Top-2 of a group of 4 magnitudes, ties to the lower position:
  * keep[p] = 1 iff fewer than two other positions q outrank p, where q outranks
@@ -167,6 +174,11 @@ int64_t orc_decompress_nm(int dt, int nm_n, int nm_m, int64_t M, int64_t K, cons
 int orc_spmm_nm(int dt, int nm_n, int nm_m, int64_t M, int64_t N, int64_t K, const void* vals, int64_t ldv,
                 const uint8_t* mask, int64_t ldmask, const void* B, int64_t ldb, double* Cf, int64_t* Ci, double* S,
                 int64_t ldc);
+/* Weight-only 4-bit: the N:M operand holds ORC_I4 values, B is fp16; the
+ * product is summed in fp64 with the bound S, as orc_spmm_nm for floats. */
+int orc_spmm_nm_w4a16(int nm_n, int nm_m, int64_t M, int64_t N, int64_t K, const void* vals, int64_t ldv,
+                      const uint8_t* mask, int64_t ldmask, const void* B, int64_t ldb, double* Cf, double* S,
+                      int64_t ldc);
 
 /* Number of threads an OpenMP parallel region would use (1 without OpenMP). */
 int orc_num_threads(void);

@@ -17,6 +17,11 @@ VALID_NIBBLES = {p | (q << 2) for p, q in PAIRS}     # {0x4, 0x8, 0xC, 0x9, 0xD,
 def to_f64(dt: str, a: np.ndarray) -> np.ndarray:
     """Values of raw storage as float64, decoded by numpy (fp16) or torch (bf16, fp8)."""
     a = np.ascontiguousarray(a)
+    if dt == "i4":                                   # two 4-bit integers per byte, low nibble first
+        lo = (a & 0xF).astype(np.int64)
+        hi = (a >> 4).astype(np.int64)
+        v = np.stack([lo, hi], axis=-1).reshape(a.shape[0], -1)
+        return np.where(v >= 8, v - 16, v).astype(np.float64)
     if dt == "i8":
         return a.astype(np.float64)
     if dt == "f16":
@@ -78,7 +83,7 @@ def brute_subset(mags, n: int) -> tuple:
 def brute_keep_mask_nm(dt: str, A: np.ndarray, n: int, m: int) -> np.ndarray:
     """Boolean N:M keep mask [M, K] by subset enumeration (python loops: small inputs)."""
     mag = np.abs(to_f64(dt, A))
-    M, K = A.shape
+    M, K = mag.shape
     keep = np.zeros((M, K), dtype=bool)
     for r in range(M):
         for g in range(K // m):

@@ -64,6 +64,11 @@ MUTANTS = [
      "int64_t v = m * ldv + g * nm_n + (nm_n - 1 - t++);"),
     ("N:M accepts groups with fewer bits", "if (cnt != nm_n) { ++bad; continue; }", "if (cnt > nm_n) { ++bad; continue; }"),
     ("N:M expansion drops the sign", "rowf[k] = elem_f64(dt, vals, v);", "rowf[k] = fabs(elem_f64(dt, vals, v));"),
+    ("i4 nibbles in the other order", "int nib = (((const uint8_t*)base)[i / 2] >> (4 * (i % 2))) & 0xF;",
+     "int nib = (((const uint8_t*)base)[i / 2] >> (4 * (1 - i % 2))) & 0xF;"),
+    ("i4 sign extended from the wrong bit", "return nib >= 8 ? nib - 16 : nib;", "return nib >= 8 ? nib - 8 : nib;"),
+    ("i4 store keeps the old nibble", "*b = (uint8_t)((*b & ~(0xF << sh)) | ((v & 0xF) << sh));",
+     "*b = (uint8_t)(*b | ((v & 0xF) << sh));"),
     ("bound accumulates signed terms",
      "bt[n * K + k];\n                        acc += t;\n                        s += fabs(t);\n                    }\n                    Cf[m * ldc + n] = acc;",
      "bt[n * K + k];\n                        acc += t;\n                        s += t;\n                    }\n                    Cf[m * ldc + n] = acc;"),

@@ -9,6 +9,7 @@ import pytest
 import torch
 
 import oracle
+import workloads as W
 from tests import _util as U
 
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
@@ -516,7 +517,12 @@ def test_empty_inputs():
 def test_nm_hand_worked_rows(pat):
     n, m = map(int, pat.split(":"))
     for case in _golden("nm_select.json")["cases"]:
-        if case["dt"] == "i8":
+        if case["dt"] == "i4":
+            row = np.array([case["row_bytes"]], dtype=np.uint8)
+            assert np.array_equal(W.pack_i4(np.array([case["row"]])), row)      # the packing itself
+            assert list(U.to_f64("i4", row)[0]) == case["row"]
+            want = case["expect_bytes"][pat]
+        elif case["dt"] == "i8":
             row = np.array([case["row"]], dtype=np.int8)
             want = case["expect"][pat]
         else:
@@ -653,3 +659,96 @@ def test_nm_bad_masks_and_errors():
     nan = U.encode("f16", [1.0, float("nan"), 0.0, 2.0]).reshape(1, 4)
     with pytest.raises(oracle.OracleError):
         oracle.compress_nm("f16", 1, 4, nan)
+
+
+# ---------------------------------------------------------------- 4-bit weights (N:M family)
+
+def test_i4_decoder_on_every_byte():
+    for b in range(256):
+        lo, hi = b & 0xF, b >> 4
+        assert oracle.i4_to_f64(b, False) == (lo - 16 if lo >= 8 else lo)
+        assert oracle.i4_to_f64(b, True) == (hi - 16 if hi >= 8 else hi)
+        assert list(U.to_f64("i4", np.array([[b]], dtype=np.uint8))[0]) == [oracle.i4_to_f64(b, False),
+                                                                         oracle.i4_to_f64(b, True)]
+
+
+@pytest.mark.parametrize("n,m", [(1, 4), (2, 4), (2, 8), (4, 8), (3, 8)])
+def test_i4_compress_matches_subset_enumeration(n, m):
+    for seed in range(10):
+        for fam in FAMILIES:
+            A = U.random_matrix("i4", 6, 32, fam, seed)
+            keep = U.brute_keep_mask_nm("i4", A, n, m)
+            vals, mask = oracle.compress_nm("i4", n, m, A)
+            assert np.array_equal(U.mask_bits(mask, 32), keep)
+            assert np.array_equal(U.to_f64("i4", vals), U.to_f64("i4", A)[keep].reshape(6, 32 * n // m))
+            D, bad = oracle.decompress_nm("i4", n, m, vals, mask, 32)
+            assert bad == 0
+            assert np.array_equal(U.to_f64("i4", D), np.where(keep, U.to_f64("i4", A), 0.0))
+
+
+def test_i4_2_of_4_selects_as_int8_does():
+    """The same integers stored as int8 go through the independent 2:4
+    compressor: the kept values and positions agree."""
+    rng = np.random.default_rng(9)
+    v = rng.choice([-8, -7, -2, -1, 0, 1, 2, 7], size=(16, 64))
+    v24, meta = oracle.compress("i8", v.astype(np.int8))
+    vi4, mask = oracle.compress_nm("i4", 2, 4, W.pack_i4(v))
+    assert np.array_equal(U.to_f64("i4", vi4), v24.astype(np.float64))
+    nib = np.stack([meta & 0xF, meta >> 4], axis=-1).reshape(16, -1)
+    pos = np.zeros((16, 64), dtype=bool)
+    for g in range(16):
+        pos[np.arange(16), 4 * g + (nib[:, g] & 3)] = True
+        pos[np.arange(16), 4 * g + (nib[:, g] >> 2)] = True
+    assert np.array_equal(U.mask_bits(mask, 64), pos)
+
+
+@pytest.mark.parametrize("n,m", [(2, 4), (2, 8), (4, 8)])
+def test_i4_w4a16_product_exact(n, m):
+    for seed in range(6):
+        A = U.random_matrix("i4", 8, 32, "normal", seed)
+        b = np.random.default_rng(seed + 50).integers(-3, 4, size=(32, 5))
+        B = U.encode("f16", b)
+        keep = U.brute_keep_mask_nm("i4", A, n, m)
+        a = U.to_f64("i4", A).astype(np.int64)
+        want = np.array([[sum(int(a[r, k]) * int(b[k, c]) for k in range(32) if keep[r, k]) for c in range(5)]
+                         for r in range(8)], dtype=np.float64)
+        vals, mask = oracle.compress_nm("i4", n, m, A)
+        C, S = oracle.spmm_nm("i4", n, m, vals, mask, B, 32)
+        assert np.array_equal(C, want)
+        sw = np.array([[sum(abs(int(a[r, k]) * int(b[k, c])) for k in range(32) if keep[r, k]) for c in range(5)]
+                       for r in range(8)], dtype=np.float64)
+        assert np.array_equal(S, sw)
+
+
+def test_i4_w4a16_product_matches_numpy():
+    A = U.random_matrix("i4", 33, 256, "normal", 3)
+    B = U.random_matrix("f16", 256, 17, "normal", 4)
+    vals, mask = oracle.compress_nm("i4", 2, 4, A)
+    C, S = oracle.spmm_nm("i4", 2, 4, vals, mask, B, 256)
+    P = np.where(U.brute_keep_mask_nm("i4", A, 2, 4), U.to_f64("i4", A), 0.0)
+    Bf = U.to_f64("f16", B)
+    assert np.allclose(C, P @ Bf, rtol=1e-12, atol=1e-12 * np.abs(P @ Bf).max())
+    assert np.allclose(S, np.abs(P) @ np.abs(Bf), rtol=1e-12, atol=0)
+
+
+@pytest.mark.parametrize("dt", ["i4", "i8", "f16"])
+def test_nm_outputs_overwrite_whatever_the_buffers_held(dt):
+    """Compression and expansion write every byte of their outputs: buffers
+    filled with 0xFF beforehand end up as they do when they start zeroed."""
+    import ctypes
+    A = U.random_matrix(dt, 5, 32, "sparse", 21)
+    e = 2 if dt == "i4" else 1
+    vals, mask = oracle.compress_nm(dt, 2, 8, A)
+    D0, _ = oracle.decompress_nm(dt, 2, 8, vals, mask, 32)
+    lib = oracle._load()
+    dirty_v = np.full_like(vals, 0xFF if vals.dtype != np.int8 else -1)
+    dirty_m = np.full_like(mask, 0xFF)
+    rc = lib.orc_compress_nm(oracle.DTYPES[dt], 2, 8, 5, 32, A.ctypes.data_as(ctypes.c_void_p), 32,
+                             dirty_v.ctypes.data_as(ctypes.c_void_p), vals.shape[1] * e,
+                             dirty_m.ctypes.data_as(ctypes.c_void_p), mask.shape[1])
+    assert rc == 0 and np.array_equal(dirty_v, vals) and np.array_equal(dirty_m, mask)
+    dirty_d = np.full_like(D0, 0xFF if D0.dtype != np.int8 else -1)
+    bad = lib.orc_decompress_nm(oracle.DTYPES[dt], 2, 8, 5, 32, vals.ctypes.data_as(ctypes.c_void_p),
+                                vals.shape[1] * e, mask.ctypes.data_as(ctypes.c_void_p), mask.shape[1],
+                                dirty_d.ctypes.data_as(ctypes.c_void_p), D0.shape[1] * e)
+    assert bad == 0 and np.array_equal(dirty_d, D0)

@@ -30,7 +30,8 @@ import numpy as np
 import torch
 
 TORCH_DTYPE = {"f16": torch.float16, "bf16": torch.bfloat16, "i8": torch.int8,
-               "e4m3": torch.float8_e4m3fn, "e5m2": torch.float8_e5m2}
+               "e4m3": torch.float8_e4m3fn, "e5m2": torch.float8_e5m2,
+               "i4": torch.uint8}   # 4-bit integers, two per byte (storage only)
 FP8 = ("e4m3", "e5m2")
 
 
@@ -38,7 +39,7 @@ FP8 = ("e4m3", "e5m2")
 class Workload:
     key: str
     title: str
-    dtype: str            # "f16" | "bf16" | "i8" | "e4m3" | "e5m2"
+    dtype: str            # "f16" | "bf16" | "i8" | "e4m3" | "e5m2" | "i4" (weights only)
     M: int
     K: int
     N: int
@@ -48,6 +49,7 @@ class Workload:
     b_range: tuple = (-128, 127)   # int8: B uniform over this closed range
     keep_prob: Optional[float] = None   # moderately-unstructured mask
     klass: str = "latency"              # "latency" | "large_n" | "small_n"
+    b_dtype: Optional[str] = None       # B's element type when it differs from A's (4-bit weights: fp16)
 
     def with_shape(self, M=None, K=None, N=None) -> "Workload":
         """Same distribution and seeds at another shape (for reduced-size tests)."""
@@ -86,9 +88,23 @@ def _gen(seed: int) -> torch.Generator:
     return g
 
 
+def pack_i4(v) -> np.ndarray:
+    """4-bit two's-complement storage of integers in [-8, 7]: element k of a
+    row in the low nibble of byte k/2 for even k, the high nibble for odd k."""
+    v = np.asarray(v, dtype=np.int64)
+    if v.shape[-1] % 2 or (v < -8).any() or (v > 7).any():
+        raise ValueError("pack_i4 takes an even number of columns of values in [-8, 7]")
+    u = (v & 0xF).astype(np.uint8)
+    return (u[..., 0::2] | (u[..., 1::2] << 4)).astype(np.uint8)
+
+
 def gen_a(w: Workload) -> torch.Tensor:
-    """Dense A [M, K] on the CPU (before any pruning)."""
+    """Dense A [M, K] on the CPU (before any pruning); 4-bit weights as
+    [M, K/2] bytes."""
     g = _gen(1000 + w.index)
+    if w.dtype == "i4":
+        a = torch.randint(-8, 8, (w.M, w.K), generator=g, dtype=torch.int8)
+        return torch.from_numpy(pack_i4(a.numpy()))
     if w.dtype == "i8":
         lo, hi = w.a_range
         a = torch.randint(lo, hi + 1, (w.M, w.K), generator=g, dtype=torch.int8)
@@ -103,10 +119,11 @@ def gen_a(w: Workload) -> torch.Tensor:
 def gen_b(w: Workload) -> torch.Tensor:
     """Dense B [K, N] on the CPU."""
     g = _gen(2000 + w.index)
-    if w.dtype == "i8":
+    bt = w.b_dtype or w.dtype
+    if bt == "i8":
         lo, hi = w.b_range
         return torch.randint(lo, hi + 1, (w.K, w.N), generator=g, dtype=torch.int8)
-    return torch.randn((w.K, w.N), generator=g, dtype=torch.float32).to(TORCH_DTYPE[w.dtype])
+    return torch.randn((w.K, w.N), generator=g, dtype=torch.float32).to(TORCH_DTYPE[bt])
 
 
 def bits(t: torch.Tensor) -> np.ndarray:
@@ -114,7 +131,7 @@ def bits(t: torch.Tensor) -> np.ndarray:
     t = t.contiguous()
     if t.dtype in (torch.float16, torch.bfloat16):
         return t.view(torch.int16).numpy().view(np.uint16)
-    if t.dtype == torch.int8:
+    if t.dtype in (torch.int8, torch.uint8):
         return t.numpy()
     if t.dtype in (torch.float8_e4m3fn, torch.float8_e5m2):
         return t.view(torch.uint8).numpy()
@@ -126,6 +143,8 @@ def from_bits(a: np.ndarray, dtype: str) -> torch.Tensor:
     a = np.ascontiguousarray(a)
     if dtype == "i8":
         return torch.from_numpy(a.astype(np.int8, copy=True))
+    if dtype == "i4":
+        return torch.from_numpy(a.astype(np.uint8, copy=True))
     if dtype in FP8:
         return torch.from_numpy(a.astype(np.uint8, copy=True)).view(TORCH_DTYPE[dtype])
     return torch.from_numpy(a.astype(np.uint16, copy=True).view(np.int16)).view(TORCH_DTYPE[dtype])
@@ -134,7 +153,7 @@ def from_bits(a: np.ndarray, dtype: str) -> torch.Tensor:
 # ---------------------------------------------------------------- small random families for tests
 
 def store_dtype(dt: str):
-    return np.int8 if dt == "i8" else (np.uint8 if dt in FP8 else np.uint16)
+    return np.int8 if dt == "i8" else (np.uint8 if dt in FP8 or dt == "i4" else np.uint16)
 
 
 def encode(dt: str, values) -> np.ndarray:
@@ -142,6 +161,8 @@ def encode(dt: str, values) -> np.ndarray:
     v = np.asarray(values, dtype=np.float64)
     if dt == "i8":
         return v.astype(np.int8)
+    if dt == "i4":
+        return pack_i4(v.astype(np.int64))
     if dt == "f16":
         return v.astype(np.float16).view(np.uint16)
     if dt in FP8:
@@ -159,6 +180,16 @@ def random_matrix(dt: str, M: int, K: int, family: str, seed: int) -> np.ndarray
     -0), "sparse" (about half the entries +0), "extreme" (int8 -128/127 or
     large/small fp magnitudes)."""
     rng = np.random.default_rng(seed)
+    if dt == "i4":                                   # [M, K/2] bytes
+        if family == "normal":
+            a = rng.integers(-8, 8, size=(M, K))
+        elif family == "ties":
+            a = rng.choice([-2, -1, 0, 1, 2], size=(M, K))
+        elif family == "sparse":
+            a = rng.integers(-8, 8, size=(M, K)) * (rng.random((M, K)) < 0.5)
+        else:
+            a = rng.choice([-8, -7, 7, 0, 1, -1], size=(M, K))
+        return pack_i4(a)
     if dt == "i8":
         if family == "normal":
             a = rng.integers(-127, 128, size=(M, K))
