@@ -86,7 +86,7 @@ typedef enum {
  * 4 metadata bytes per 16 stored values of a sparse-MFMA lane) and
  * accumulate into fp32. */
 typedef enum {
-    SSG_F16 = 0, SSG_BF16 = 1, SSG_I8 = 2, SSG_F32 = 3, SSG_I32 = 4, SSG_E4M3 = 5, SSG_E5M2 = 6
+    SSG_F16 = 0, SSG_BF16 = 1, SSG_I8 = 2, SSG_F32 = 3, SSG_I32 = 4, SSG_E4M3 = 5, SSG_E5M2 = 6, SSG_I4 = 7
 } ssg_dtype;
 
 /* SpMM algorithms.  AUTO picks by shape; the others force one kernel family
@@ -268,6 +268,15 @@ int ssg_spmm_2to4_packed(int ab, int c, int64_t M, int64_t N, int64_t K, const v
  *         kept; bits past K are 0 (ldmask >= ceil(K/8)).
  * For 2:4 this holds the same values as ssg_compress_2to4 with the
  * positions as bits instead of nibbles.
+ *
+ * 4-bit weights (SSG_I4; "Chapter 26", section "Sparsity + Quantization
+ * Combine", stacks 2:4 with 4-bit values): two's-complement integers in
+ * [-8, 7], two per byte, element k of a row in the low nibble of byte k/2
+ * for even k and the high nibble for odd k; A, vals and D are byte arrays
+ * whose leading dimensions stay counted in elements and must be even.
+ * Patterns 2:4, 2:8, 4:8 (whole bytes per group).  The products take them
+ * as weight-only quantized weights: B is fp16, C fp32 ((ab, c) =
+ * (SSG_I4, SSG_F32)); the values enter the fp16 MFMA exactly.
  *
  * ssg_nm_vals_cols: K / nm_m * nm_n. */
 int64_t ssg_nm_vals_cols(int nm_n, int nm_m, int64_t K);

@@ -34,10 +34,18 @@ __all__ = [
     "SSG_ALGO_AUTO", "SSG_ALGO_GENERIC", "SSG_ALGO_SMALL_N", "SSG_ALGO_LARGE_N", "library_path",
 ]
 
+# torch.uint8 element tensors are 4-bit weights, two per byte (the N:M calls
+# only; their element counts are twice the byte counts)
 _DT = {torch.float16: SSG_F16, torch.bfloat16: SSG_BF16, torch.int8: SSG_I8,
-       torch.float8_e4m3fn: _abi.SSG_E4M3, torch.float8_e5m2: _abi.SSG_E5M2}
+       torch.float8_e4m3fn: _abi.SSG_E4M3, torch.float8_e5m2: _abi.SSG_E5M2, torch.uint8: _abi.SSG_I4}
 _OUT = {SSG_F16: (SSG_F32, torch.float32), SSG_BF16: (SSG_F32, torch.float32), SSG_I8: (SSG_I32, torch.int32),
-        _abi.SSG_E4M3: (SSG_F32, torch.float32), _abi.SSG_E5M2: (SSG_F32, torch.float32)}
+        _abi.SSG_E4M3: (SSG_F32, torch.float32), _abi.SSG_E5M2: (SSG_F32, torch.float32),
+        _abi.SSG_I4: (SSG_F32, torch.float32)}
+
+
+def _per(t: torch.Tensor) -> int:
+    """Elements per storage unit of an element tensor: 2 for 4-bit weights."""
+    return 2 if t.dtype == torch.uint8 else 1
 ALGO_NAMES = {SSG_ALGO_AUTO: "auto", SSG_ALGO_GENERIC: "generic", SSG_ALGO_SMALL_N: "small_n",
               SSG_ALGO_LARGE_N: "large_n"}
 
@@ -244,16 +252,18 @@ def ssg_spmm_select_algo(vals, meta, B, C) -> int:
 
 
 def ssg_compress_nm(A: torch.Tensor, n: int, m: int, vals: torch.Tensor, mask: torch.Tensor, stream=None) -> None:
-    _check(_lib().ssg_compress_nm(_dtype(A), n, m, A.shape[0], A.shape[1], _ptr(A, "A"), _ld(A, "A"),
-                                  _ptr(vals, "vals"), _ld(vals, "vals"), _ptr(mask, "mask"), _ld(mask, "mask"),
+    e = _per(A)
+    _check(_lib().ssg_compress_nm(_dtype(A), n, m, A.shape[0], A.shape[1] * e, _ptr(A, "A"), _ld(A, "A") * e,
+                                  _ptr(vals, "vals"), _ld(vals, "vals") * e, _ptr(mask, "mask"), _ld(mask, "mask"),
                                   _stream(A, stream)), "ssg_compress_nm")
 
 
 def ssg_decompress_nm(vals: torch.Tensor, mask: torch.Tensor, n: int, m: int, D: torch.Tensor,
                       bad_count: Optional[torch.Tensor] = None, stream=None) -> None:
-    _check(_lib().ssg_decompress_nm(_dtype(vals), n, m, D.shape[0], D.shape[1], _ptr(vals, "vals"),
-                                    _ld(vals, "vals"), _ptr(mask, "mask"), _ld(mask, "mask"), _ptr(D, "D"),
-                                    _ld(D, "D"), _ptr(bad_count, "bad_count"), _stream(D, stream)),
+    e = _per(vals)
+    _check(_lib().ssg_decompress_nm(_dtype(vals), n, m, D.shape[0], D.shape[1] * e, _ptr(vals, "vals"),
+                                    _ld(vals, "vals") * e, _ptr(mask, "mask"), _ld(mask, "mask"), _ptr(D, "D"),
+                                    _ld(D, "D") * e, _ptr(bad_count, "bad_count"), _stream(D, stream)),
            "ssg_decompress_nm")
 
 
@@ -261,7 +271,8 @@ def ssg_spmm_nm(vals: torch.Tensor, mask: torch.Tensor, n: int, m: int, K: int, 
                 stream=None) -> None:
     ab = _dtype(vals)
     _check(_lib().ssg_spmm_nm(ab, _OUT[ab][0], n, m, vals.shape[0], B.shape[1], K, _ptr(vals, "vals"),
-                              _ld(vals, "vals"), _ptr(mask, "mask"), _ld(mask, "mask"), _ptr(B, "B"), _ld(B, "B"),
+                              _ld(vals, "vals") * _per(vals), _ptr(mask, "mask"), _ld(mask, "mask"), _ptr(B, "B"),
+                              _ld(B, "B"),
                               _ptr(C, "C"), _ld(C, "C"), _stream(C, stream)), "ssg_spmm_nm")
 
 
@@ -276,13 +287,15 @@ def ssg_nm_packed_sizes(dtype: torch.dtype, n: int, m: int, M: int, K: int) -> T
 
 
 def ssg_pack_nm_decode(vals, mask, n: int, m: int, K: int, pvals, pmask, stream=None) -> None:
-    _check(_lib().ssg_pack_nm_decode(_dtype(vals), n, m, vals.shape[0], K, _ptr(vals, "vals"), _ld(vals, "vals"),
+    _check(_lib().ssg_pack_nm_decode(_dtype(vals), n, m, vals.shape[0], K, _ptr(vals, "vals"),
+                                     _ld(vals, "vals") * _per(vals),
                                      _ptr(mask, "mask"), _ld(mask, "mask"), _ptr(pvals, "pvals"),
                                      _ptr(pmask, "pmask"), _stream(vals, stream)), "ssg_pack_nm_decode")
 
 
-def ssg_spmm_nm_packed(pvals, pmask, n: int, m: int, M: int, B, C, stream=None) -> None:
-    ab = _dtype(B)
+def ssg_spmm_nm_packed(pvals, pmask, n: int, m: int, M: int, B, C, stream=None, i4: bool = False) -> None:
+    """i4: the packed weights are 4-bit (B is then fp16)."""
+    ab = _abi.SSG_I4 if i4 else _dtype(B)
     _check(_lib().ssg_spmm_nm_packed(ab, _OUT[ab][0], n, m, M, B.shape[1], B.shape[0], _ptr(pvals, "pvals"),
                                      _ptr(pmask, "pmask"), _ptr(B, "B"), _ld(B, "B"), _ptr(C, "C"), _ld(C, "C"),
                                      _stream(C, stream)), "ssg_spmm_nm_packed")
@@ -395,15 +408,16 @@ def compress_nm(A: torch.Tensor, n: int, m: int) -> Tuple[torch.Tensor, torch.Te
     """(vals [M, K/m*n], mask [M, ceil(K/8)] uint8) of a dense [M, K] weight under
     the n:m rule; rows padded to 16 (vals) and 8 (mask) bytes as the product
     wants them."""
-    M, K = A.shape
-    vals = _padded(M, K // m * n, A.dtype, 16, A.device)
+    e = _per(A)
+    M, K = A.shape[0], A.shape[1] * e
+    vals = _padded(M, K // m * n // e, A.dtype, 16, A.device)
     mask = _padded(M, (K + 7) // 8, torch.uint8, 8, A.device)
     ssg_compress_nm(A, n, m, vals, mask)
     return vals, mask
 
 
 def decompress_nm(vals: torch.Tensor, mask: torch.Tensor, n: int, m: int, K: int, count_bad: bool = False):
-    D = torch.empty((vals.shape[0], K), dtype=vals.dtype, device=vals.device)
+    D = torch.empty((vals.shape[0], K // _per(vals)), dtype=vals.dtype, device=vals.device)
     bad = torch.zeros(1, dtype=torch.int32, device=vals.device) if count_bad else None
     ssg_decompress_nm(vals, mask, n, m, D, bad)
     return (D, int(bad.item())) if count_bad else D
@@ -428,10 +442,10 @@ def pack_nm(vals: torch.Tensor, mask: torch.Tensor, n: int, m: int, K: int):
 
 
 def spmm_nm_packed(pvals: torch.Tensor, pmask: torch.Tensor, n: int, m: int, M: int, B: torch.Tensor,
-                   out: Optional[torch.Tensor] = None) -> torch.Tensor:
-    ab = _dtype(B)
+                   out: Optional[torch.Tensor] = None, i4: bool = False) -> torch.Tensor:
+    ab = _abi.SSG_I4 if i4 else _dtype(B)
     C = torch.empty((M, B.shape[1]), dtype=_OUT[ab][1], device=B.device) if out is None else out
-    ssg_spmm_nm_packed(pvals, pmask, n, m, M, B, C)
+    ssg_spmm_nm_packed(pvals, pmask, n, m, M, B, C, i4=i4)
     return C
 
 

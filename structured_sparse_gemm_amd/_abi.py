@@ -12,7 +12,7 @@ LIB_PATH = os.path.join(PKG, "libssgemm.so")
 
 SSG_OK, SSG_ERR_NULL, SSG_ERR_SHAPE, SSG_ERR_STRIDE, SSG_ERR_DTYPE = 0, 1, 2, 3, 4
 SSG_ERR_FORMAT, SSG_ERR_WORKSPACE, SSG_ERR_HIP, SSG_ERR_ALGO = 5, 6, 7, 8
-SSG_F16, SSG_BF16, SSG_I8, SSG_F32, SSG_I32, SSG_E4M3, SSG_E5M2 = 0, 1, 2, 3, 4, 5, 6
+SSG_F16, SSG_BF16, SSG_I8, SSG_F32, SSG_I32, SSG_E4M3, SSG_E5M2, SSG_I4 = 0, 1, 2, 3, 4, 5, 6, 7
 SSG_ALGO_AUTO, SSG_ALGO_GENERIC, SSG_ALGO_SMALL_N, SSG_ALGO_LARGE_N = 0, 1, 2, 3
 
 _i = ctypes.c_int

@@ -42,14 +42,17 @@ namespace {
 constexpr int kNmWaves = 8;
 constexpr int kNmTMax = 4;
 
+// Working element of the compress / expand kernels: the storage word, or
+// for 4-bit weights the value widened to int8 (stored two per byte).
 template <int DT> struct NmStore { using T = uint16_t; };
 template <> struct NmStore<DT_I8> { using T = int8_t; };
 template <> struct NmStore<DT_E4M3> { using T = uint8_t; };
 template <> struct NmStore<DT_E5M2> { using T = uint8_t; };
+template <> struct NmStore<DT_I4> { using T = int8_t; };
 
 template <int DT>
 __device__ __forceinline__ uint32_t nm_key(typename NmStore<DT>::T x) {
-    if constexpr (DT == DT_I8) return mag_key8((int32_t)x);
+    if constexpr (DT == DT_I8 || DT == DT_I4) return mag_key8((int32_t)x);
     else if constexpr (dt_is_fp8(DT)) return mag_key_fp8((uint32_t)x);
     else return mag_key16((uint32_t)x);
 }
@@ -57,15 +60,97 @@ __device__ __forceinline__ uint32_t nm_key(typename NmStore<DT>::T x) {
 // ---- compress / expand ------------------------------------------------------
 //
 // One thread per chunk of 32 dense elements of a row (32 / MM whole groups):
-// it writes 4 whole mask bytes and 32*NN/MM values, so no byte is shared.
-// The ragged last chunk of a row (K % 32) takes element-wise accesses.
+// it writes 4 whole mask bytes and 32*NN/MM values, so no byte is shared
+// (4-bit weights: NN is even, so a chunk's values fill whole bytes).  The
+// ragged last chunk of a row (K % 32) takes element-wise accesses.
 
 constexpr int kNmChunk = 32;
 
+// n elements of a row from `row` (element index i0 on) into x; 4-bit
+// weights are sign-extended from their nibbles.  `vec`: 16-byte loads.
+template <int DT>
+__device__ __forceinline__ void nm_load(const void* row, int64_t i0, int n, bool vec,
+                                        typename NmStore<DT>::T (&x)[kNmChunk]) {
+    using T = typename NmStore<DT>::T;
+    if constexpr (DT == DT_I4) {
+        const uint8_t* b = reinterpret_cast<const uint8_t*>(row) + i0 / 2;
+        uint8_t by[kNmChunk / 2];
+        if (vec && n == kNmChunk) {
+            const uint4 w = *reinterpret_cast<const uint4*>(b);
+            __builtin_memcpy(by, &w, 16);
+        } else {
+#pragma unroll
+            for (int i = 0; i < kNmChunk / 2; ++i) by[i] = 2 * i < n ? b[i] : 0;
+        }
+#pragma unroll
+        for (int i = 0; i < kNmChunk; ++i) {
+            const int nib = (by[i / 2] >> (4 * (i % 2))) & 0xF;
+            x[i] = (T)(nib >= 8 ? nib - 16 : nib);
+        }
+    } else {
+        const T* a = reinterpret_cast<const T*>(row) + i0;
+        if (vec && n == kNmChunk) {
+            uint4 w[kNmChunk * sizeof(T) / 16];
+#pragma unroll
+            for (int i = 0; i < (int)(kNmChunk * sizeof(T) / 16); ++i) w[i] = reinterpret_cast<const uint4*>(a)[i];
+            __builtin_memcpy(x, w, sizeof(x));
+        } else {
+#pragma unroll
+            for (int i = 0; i < kNmChunk; ++i) x[i] = i < n ? a[i] : T(0);
+        }
+    }
+}
+
+// The first n of v (NV entries) to `row` from element i0 on; 4-bit values
+// are packed two per byte (n and i0 even).  `vec`: NV entries as 8-byte stores.
+template <int DT, int NV>
+__device__ __forceinline__ void nm_store(void* row, int64_t i0, int n, bool vec, const typename NmStore<DT>::T (&v)[NV]) {
+    using T = typename NmStore<DT>::T;
+    if constexpr (DT == DT_I4) {
+        uint8_t* b = reinterpret_cast<uint8_t*>(row) + i0 / 2;
+        uint8_t by[NV / 2];
+#pragma unroll
+        for (int i = 0; i < NV / 2; ++i) by[i] = (uint8_t)((v[2 * i] & 0xF) | ((v[2 * i + 1] & 0xF) << 4));
+        if (vec && n == NV) {
+            if constexpr (NV / 2 >= 8) {
+                uint2 w[NV / 16];
+                __builtin_memcpy(w, by, NV / 2);
+#pragma unroll
+                for (int i = 0; i < NV / 16; ++i) reinterpret_cast<uint2*>(b)[i] = w[i];
+            } else {
+                uint32_t w;
+                __builtin_memcpy(&w, by, 4);
+                *reinterpret_cast<uint32_t*>(b) = w;
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < NV / 2; ++i)
+                if (2 * i < n) b[i] = by[i];
+        }
+    } else {
+        T* a = reinterpret_cast<T*>(row) + i0;
+        if (vec && n == NV) {
+            constexpr int VB = NV * (int)sizeof(T);           // 8, 16 or 32 bytes
+            uint2 w[VB / 8];
+            __builtin_memcpy(w, v, VB);
+#pragma unroll
+            for (int i = 0; i < VB / 8; ++i) reinterpret_cast<uint2*>(a)[i] = w[i];
+        } else {
+#pragma unroll
+            for (int i = 0; i < NV; ++i)
+                if (i < n) a[i] = v[i];
+        }
+    }
+}
+
+// Bytes of a row of ld elements.
+template <int DT> __device__ __forceinline__ int64_t nm_row_bytes(int64_t ld) {
+    return DT == DT_I4 ? ld / 2 : ld * (int64_t)sizeof(typename NmStore<DT>::T);
+}
+
 template <int DT, int NN, int MM>
-__global__ void __launch_bounds__(256) k_compress_nm(int64_t M, int64_t K, const typename NmStore<DT>::T* A,
-                                                     int64_t lda, typename NmStore<DT>::T* vals, int64_t ldv,
-                                                     uint8_t* mask, int64_t ldm, int vec) {
+__global__ void __launch_bounds__(256) k_compress_nm(int64_t M, int64_t K, const void* A, int64_t lda, void* vals,
+                                                     int64_t ldv, uint8_t* mask, int64_t ldm, int vec) {
     using T = typename NmStore<DT>::T;
     constexpr int G = kNmChunk / MM, NV = kNmChunk / MM * NN;
     const int64_t chunks = (K + kNmChunk - 1) / kNmChunk;
@@ -73,18 +158,8 @@ __global__ void __launch_bounds__(256) k_compress_nm(int64_t M, int64_t K, const
          t += (int64_t)gridDim.x * blockDim.x) {
         const int64_t m = t / chunks, c = t - m * chunks;
         const int ne = (int)min<int64_t>(kNmChunk, K - c * kNmChunk);   // a multiple of MM
-        const bool full = vec && ne == kNmChunk;
-        const T* arow = A + m * lda + c * kNmChunk;
         T x[kNmChunk];
-        if (full) {
-            uint4 w[kNmChunk * sizeof(T) / 16];
-#pragma unroll
-            for (int i = 0; i < (int)(kNmChunk * sizeof(T) / 16); ++i) w[i] = reinterpret_cast<const uint4*>(arow)[i];
-            __builtin_memcpy(x, w, sizeof(x));
-        } else {
-#pragma unroll
-            for (int i = 0; i < kNmChunk; ++i) x[i] = i < ne ? arow[i] : T(0);
-        }
+        nm_load<DT>(reinterpret_cast<const uint8_t*>(A) + m * nm_row_bytes<DT>(lda), c * kNmChunk, ne, vec != 0, x);
         uint32_t bits = 0;
         T v[NV];
 #pragma unroll
@@ -109,20 +184,12 @@ __global__ void __launch_bounds__(256) k_compress_nm(int64_t M, int64_t K, const
                 if (keep && g * MM < ne) bits |= 1u << (g * MM + p);
             }
         }
-        T* vrow = vals + m * ldv + c * NV;
+        nm_store<DT, NV>(reinterpret_cast<uint8_t*>(vals) + m * nm_row_bytes<DT>(ldv), c * NV, ne / MM * NN,
+                         vec != 0, v);
         uint8_t* mrow = mask + m * ldm + c * (kNmChunk / 8);
-        if (full) {
-            constexpr int VB = NV * (int)sizeof(T);           // 8, 16 or 32 bytes
-            uint2 w[VB / 8];
-            __builtin_memcpy(w, v, VB);
-#pragma unroll
-            for (int i = 0; i < VB / 8; ++i) reinterpret_cast<uint2*>(vrow)[i] = w[i];
+        if (vec && ne == kNmChunk) {
             *reinterpret_cast<uint32_t*>(mrow) = bits;
         } else {
-            const int nv = ne / MM * NN;
-#pragma unroll
-            for (int i = 0; i < NV; ++i)
-                if (i < nv) vrow[i] = v[i];
 #pragma unroll
             for (int b = 0; b < kNmChunk / 8; ++b)
                 if (8 * b < ne) mrow[b] = (uint8_t)(bits >> (8 * b));
@@ -133,9 +200,9 @@ __global__ void __launch_bounds__(256) k_compress_nm(int64_t M, int64_t K, const
 // Dense expansion; a group whose mask does not hold exactly NN bits is
 // written as zeros and counted into *bad (if not null).
 template <int DT, int NN, int MM>
-__global__ void __launch_bounds__(256) k_decompress_nm(int64_t M, int64_t K, const typename NmStore<DT>::T* vals,
-                                                       int64_t ldv, const uint8_t* mask, int64_t ldm,
-                                                       typename NmStore<DT>::T* D, int64_t ldd, int32_t* bad) {
+__global__ void __launch_bounds__(256) k_decompress_nm(int64_t M, int64_t K, const void* vals, int64_t ldv,
+                                                       const uint8_t* mask, int64_t ldm, void* D, int64_t ldd,
+                                                       int32_t* bad) {
     using T = typename NmStore<DT>::T;
     constexpr int G = kNmChunk / MM, NV = kNmChunk / MM * NN;
     const int64_t chunks = (K + kNmChunk - 1) / kNmChunk;
@@ -143,7 +210,9 @@ __global__ void __launch_bounds__(256) k_decompress_nm(int64_t M, int64_t K, con
          t += (int64_t)gridDim.x * blockDim.x) {
         const int64_t m = t / chunks, c = t - m * chunks;
         const int ne = (int)min<int64_t>(kNmChunk, K - c * kNmChunk);
-        const T* vrow = vals + m * ldv + c * NV;
+        T vin[kNmChunk];                                   // the chunk's stored values (NV of them)
+        nm_load<DT>(reinterpret_cast<const uint8_t*>(vals) + m * nm_row_bytes<DT>(ldv), c * NV, ne / MM * NN, false,
+                    vin);
         const uint8_t* mrow = mask + m * ldm + c * (kNmChunk / 8);
         uint32_t bits = 0;
 #pragma unroll
@@ -163,44 +232,91 @@ __global__ void __launch_bounds__(256) k_decompress_nm(int64_t M, int64_t K, con
                 T val = T(0);
 #pragma unroll
                 for (int j = 0; j < NN; ++j)
-                    if (on && cnt == j && g * MM < ne) val = vrow[g * NN + j];
+                    if (on && cnt == j && g * MM < ne) val = vin[g * NN + j];
                 out[g * MM + p] = val;
                 cnt += on ? 1 : 0;
             }
         }
-        T* drow = D + m * ldd + c * kNmChunk;
-#pragma unroll
-        for (int i = 0; i < kNmChunk; ++i)
-            if (i < ne) drow[i] = out[i];
+        nm_store<DT, kNmChunk>(reinterpret_cast<uint8_t*>(D) + m * nm_row_bytes<DT>(ldd), c * kNmChunk, ne, false,
+                               out);
         if (bad && nbad) atomicAdd(bad, nbad);
     }
 }
 
 // ---- product ----------------------------------------------------------------
 
+// 4-bit weights (W4) run as fp16: their values are widened to fp16 in
+// registers before the expansion, and B is fp16.
 template <int DT, int NN, int MM>
 struct NmShape {
-    static constexpr int ES = dt_bytes(DT);
+    static constexpr bool W4 = DT == DT_I4;
+    static constexpr int ES = W4 ? 2 : dt_bytes(DT);    // element bytes of the MFMA operands (and B)
     static constexpr int FB = dt_is_fp8(DT) ? 8 : 16;   // A (and B) bytes per lane per MFMA
     static constexpr int E = FB / ES;                    // dense k per lane per MFMA
-    static constexpr int V = 16 / ES;                    // stored values per lane per super-step
-    static constexpr int D = V * MM / NN;                // dense k per lane per super-step
+    static constexpr int D = W4 ? 32 : 16 / ES * MM / NN;   // dense k per lane per super-step
+    static constexpr int V = D * NN / MM;                // stored values per lane per super-step
+    static constexpr int VB = W4 ? V / 2 : 16;           // their bytes: one 16-, 8- or 4-byte load
+    static constexpr int VW = V * ES / 4;                // dwords of them (widened for W4)
     static constexpr int F = D / E;                      // MFMAs per tile per super-step
     static constexpr int SK = 4 * D;                     // dense k per super-step
     static constexpr int GL = D / MM;                    // groups per lane per super-step
-    static constexpr int GB = NN * ES;                   // stored bytes per group
+    static constexpr int GB = NN * ES;                   // stored (widened) bytes per group
     static constexpr int OW = MM * ES / 4;               // dense dwords per group
     static constexpr int MB = D / 8;                     // mask bytes per lane per super-step
     static constexpr int BSTEP = SK * 16 * ES;           // B bytes per super-step (16 columns)
     static constexpr int NB = BSTEP / 1024;              // direct-to-LDS loads of B per super-step
     static constexpr int P = NB >= 4 ? 4 : 6;            // super-steps in flight per wave
     static constexpr int LUT = (1 << MM) * OW * 4;       // selector table bytes
-    static_assert(D % MM == 0 && D % E == 0 && D % 8 == 0, "shape");
+    static_assert(D % MM == 0 && D % E == 0 && D % 8 == 0 && V % 8 == 0, "shape");
+    static_assert(!W4 || NN % 2 == 0, "4-bit weights: whole bytes per group");
     static_assert((GB <= 4 && 4 % GB == 0) || GB == 8, "a group's stored bytes lie in one or two whole dwords");
     static_assert(BSTEP % 1024 == 0, "B rows per super-step");
 };
 
 template <int DT> using NmAcc = typename std::conditional<DT == DT_I8, i32x4, f32x4>::type;
+
+// Registers of one lane's stored values per super-step, loaded as one
+// buffer load of VB bytes.
+template <int VB> struct ValReg { using T = i32x4; };
+template <> struct ValReg<8> { using T = i32x2; };
+template <> struct ValReg<4> { using T = int; };
+
+template <int VB>
+__device__ __forceinline__ void load_vals(typename ValReg<VB>::T& r, uint32_t off, __amdgpu_buffer_rsrc_t rs) {
+    if constexpr (VB == 16)
+        asm volatile("buffer_load_dwordx4 %0, %1, %2, 0 offen" : "=v"(r) : "v"(off), "s"(rs) : "memory");
+    else if constexpr (VB == 8)
+        asm volatile("buffer_load_dwordx2 %0, %1, %2, 0 offen" : "=v"(r) : "v"(off), "s"(rs) : "memory");
+    else
+        asm volatile("buffer_load_dword %0, %1, %2, 0 offen" : "=v"(r) : "v"(off), "s"(rs) : "memory");
+}
+
+typedef _Float16 nm_h2 __attribute__((ext_vector_type(2)));
+
+// The lane's stored values as VW dwords of MFMA elements: a copy, or for
+// 4-bit weights each byte's two nibbles widened to a pair of fp16.  A
+// nibble u (two's complement) becomes fp16 1024 + (u ^ 8) by placing u ^ 8
+// in the low mantissa bits of 0x6400, and 1024 + 8 is then subtracted:
+// exact, since every value involved is an integer below 2048.
+template <int DT, int NN, int MM>
+__device__ __forceinline__ void widen_vals(const typename ValReg<NmShape<DT, NN, MM>::VB>::T& r, uint32_t (&vw)[NmShape<DT, NN, MM>::VW]) {
+    using S = NmShape<DT, NN, MM>;
+    if constexpr (S::W4) {
+        uint32_t raw[S::VB / 4];
+        __builtin_memcpy(raw, &r, S::VB);
+#pragma unroll
+        for (int i = 0; i < S::VW; ++i) {
+            const uint32_t b = (raw[i / 4] >> (8 * (i % 4))) & 0xFFu;
+            const uint32_t w = ((b & 0xFu) | ((b & 0xF0u) << 12)) ^ 0x64086408u;
+            nm_h2 h;
+            __builtin_memcpy(&h, &w, 4);
+            h = h - nm_h2{(_Float16)1032.0f, (_Float16)1032.0f};
+            __builtin_memcpy(&vw[i], &h, 4);
+        }
+    } else {
+        __builtin_memcpy(vw, &r, 16);
+    }
+}
 
 template <int DT>
 __device__ __forceinline__ NmAcc<DT> nm_mfma(const uint32_t* a, const uint32_t* b, NmAcc<DT> c) {
@@ -326,25 +442,25 @@ __global__ void __launch_bounds__(kNmWaves * 64) k_spmm_nm(SpmmArgs a, int64_t t
     const int64_t rows = min<int64_t>(16 * nt, a.M - r0);
     const int64_t ct = blockIdx.y;
     const int64_t nsteps = (a.K + S::SK - 1) / S::SK;
-    const int64_t ldvb = a.ldv * S::ES, ldbb = a.ldb * S::ES;
+    const int64_t ldvb = S::W4 ? a.ldv / 2 : a.ldv * S::ES, ldbb = a.ldb * S::ES;
 
     // row-major: ranges rounded up to the load sizes (bases are aligned to
     // them), so a single row whose stride is not a multiple of them still
     // reads whole.  Packed: the workgroup's tiles' blocks, consecutive.
     const uint8_t* vbase = reinterpret_cast<const uint8_t*>(a.vals);
     const __amdgpu_buffer_rsrc_t rv =
-        PK ? rsrc(vbase + t0 * nsteps * 1024, nt * nsteps * 1024)
+        PK ? rsrc(vbase + t0 * nsteps * 64 * S::VB, nt * nsteps * 64 * S::VB)
            : rsrc_aligned<16>(vbase + r0 * ldvb, rows * ldvb);
     const __amdgpu_buffer_rsrc_t rm =
         PK ? rsrc(a.meta + t0 * nsteps * 64 * S::MB, nt * nsteps * 64 * S::MB)
            : rsrc_aligned<8>(a.meta + r0 * a.ldm, rows * a.ldm);
     const __amdgpu_buffer_rsrc_t rb = rsrc_aligned<16>(a.B, a.K * ldbb);
     const int r = lane & 15, q = lane >> 4;
-    constexpr uint32_t VSTEP = PK ? 1024 : 64, MSTEP = PK ? 64 * S::MB : 4 * S::MB;   // bytes per super-step
+    constexpr uint32_t VSTEP = PK ? 64 * S::VB : 4 * S::VB, MSTEP = PK ? 64 * S::MB : 4 * S::MB;   // bytes per super-step
     uint32_t voff[TM], moff[TM];
 #pragma unroll
     for (int t = 0; t < TM; ++t) {
-        voff[t] = PK ? (uint32_t)((t * nsteps * 64 + lane) * 16) : (uint32_t)((16 * t + r) * ldvb + 16 * q);
+        voff[t] = PK ? (uint32_t)((t * nsteps * 64 + lane) * S::VB) : (uint32_t)((16 * t + r) * ldvb + S::VB * q);
         moff[t] = PK ? (uint32_t)((t * nsteps * 64 + lane) * S::MB) : (uint32_t)((16 * t + r) * a.ldm + S::MB * q);
     }
     // lane's B piece of one direct-to-LDS load: 16 bytes of row
@@ -353,7 +469,7 @@ __global__ void __launch_bounds__(kNmWaves * 64) k_spmm_nm(SpmmArgs a, int64_t t
 
     build_lut<DT, NN, MM>(lut);
 
-    i32x4 av[P][TM] = {};
+    typename ValReg<S::VB>::T av[P][TM] = {};
     MR mv[P][TM] = {};
     auto issue = [&](int64_t g, int u) {
         const bool in = g < nsteps;
@@ -369,7 +485,7 @@ __global__ void __launch_bounds__(kNmWaves * 64) k_spmm_nm(SpmmArgs a, int64_t t
             const bool live = in && t < nt;
             const uint32_t o = live ? voff[t] + (uint32_t)(g * VSTEP) : kOob;
             const uint32_t om = live ? moff[t] + (uint32_t)(g * MSTEP) : kOob;
-            asm volatile("buffer_load_dwordx4 %0, %1, %2, 0 offen" : "=v"(av[u][t]) : "v"(o), "s"(rv) : "memory");
+            load_vals<S::VB>(av[u][t], o, rv);
             load_mask<S::MB>(mv[u][t], om, rm);
         }
     };
@@ -401,8 +517,8 @@ __global__ void __launch_bounds__(kNmWaves * 64) k_spmm_nm(SpmmArgs a, int64_t t
                 const uint64_t keepm = nv >= S::D ? ~0ull : (nv <= 0 ? 0ull : ((1ull << nv) - 1ull));
 #pragma unroll
                 for (int t = 0; t < TM; ++t) {
-                    uint32_t vw[4];
-                    __builtin_memcpy(vw, &av[u][t], 16);
+                    uint32_t vw[S::VW];
+                    widen_vals<DT, NN, MM>(av[u][t], vw);
                     const uint64_t mk = mask_bits<S::MB>(mv[u][t]) & keepm;
                     uint32_t dense[S::GL * S::OW];
 #pragma unroll
@@ -425,7 +541,8 @@ __global__ void __launch_bounds__(kNmWaves * 64) k_spmm_nm(SpmmArgs a, int64_t t
                         for (int s = 0; s < S::OW; ++s) dense[gg * S::OW + s] = __builtin_amdgcn_perm(s0, s1, sv[s]);
                     }
 #pragma unroll
-                    for (int f = 0; f < S::F; ++f) acc[t] = nm_mfma<DT>(dense + f * (S::FB / 4), bf[f], acc[t]);
+                    for (int f = 0; f < S::F; ++f)
+                        acc[t] = nm_mfma<S::W4 ? DT_F16 : DT>(dense + f * (S::FB / 4), bf[f], acc[t]);
                 }
                 // the slot's LDS reads are done before its next B rows land
                 __builtin_amdgcn_s_waitcnt(0xC07F);
@@ -484,14 +601,15 @@ hipError_t launch_nm_t(const SpmmArgs& a, hipStream_t s) {
 // ---- packed decode layout ----------------------------------------------------
 //
 // The product's operand in the order it is consumed: for each 16-row tile
-// and super-step, the 64 lanes' 16 value bytes (lane l = 16q + r: row r's
-// stored bytes [64g + 16q, 64g + 16q + 16) of super-step g) as one 1 KiB
-// block, and their MB mask bytes (row r's mask bytes [4g*MB + q*MB, +MB))
-// as one block of 64*MB bytes.  A tile's blocks follow each other in g;
-// bytes past a row's end and rows past M are zero.  Each load of the
-// product is then one fully coalesced block instead of 16 row pieces.
+// and super-step, the 64 lanes' VB value bytes (lane l = 16q + r: row r's
+// stored bytes [4g*VB + q*VB, +VB) of super-step g; VB = 16, or 8 / 4 for
+// 4-bit weights) as one block of 64*VB bytes, and their MB mask bytes (row
+// r's mask bytes [4g*MB + q*MB, +MB)) as one block of 64*MB bytes.  A
+// tile's blocks follow each other in g; bytes past a row's end and rows
+// past M are zero.  Each load of the product is then one fully coalesced
+// block instead of 16 row pieces.
 __global__ void __launch_bounds__(256) k_pack_nm(int64_t M, int64_t tiles, int64_t nsteps, const uint8_t* vals,
-                                                 int64_t ldvb, int64_t vrow, const uint8_t* mask, int64_t ldm,
+                                                 int64_t ldvb, int64_t vrow, int vb, const uint8_t* mask, int64_t ldm,
                                                  int64_t mrow, int mb, uint8_t* pvals, uint8_t* pmask) {
     const int64_t n = tiles * nsteps * 64;
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
@@ -499,23 +617,19 @@ __global__ void __launch_bounds__(256) k_pack_nm(int64_t M, int64_t tiles, int64
         const int64_t blk = i >> 6, tile = blk / nsteps, g = blk - tile * nsteps;
         const int64_t row = 16 * tile + (lane & 15);
         const int q = lane >> 4;
-        const int64_t v0 = g * 64 + 16 * q, m0 = g * 4 * mb + (int64_t)q * mb;
-        uint8_t v[16], m[8];
-#pragma unroll
-        for (int b = 0; b < 16; ++b) v[b] = row < M && v0 + b < vrow ? vals[row * ldvb + v0 + b] : 0;
-#pragma unroll
-        for (int b = 0; b < 8; ++b) m[b] = b < mb && row < M && m0 + b < mrow ? mask[row * ldm + m0 + b] : 0;
-        uint4 w;
-        __builtin_memcpy(&w, v, 16);
-        *reinterpret_cast<uint4*>(pvals + i * 16) = w;
-        for (int b = 0; b < mb; ++b) pmask[i * mb + b] = m[b];
+        const int64_t v0 = g * 4 * vb + (int64_t)q * vb, m0 = g * 4 * mb + (int64_t)q * mb;
+        for (int b = 0; b < vb; ++b) pvals[i * vb + b] = row < M && v0 + b < vrow ? vals[row * ldvb + v0 + b] : 0;
+        for (int b = 0; b < mb; ++b) pmask[i * mb + b] = row < M && m0 + b < mrow ? mask[row * ldm + m0 + b] : 0;
     }
 }
 
 // Op<DT, NN, MM>::run(args...) for the runtime (dt, n, m).
 template <template <int, int, int> class Op, int D, typename... Args>
 hipError_t nm_pat(int n, int m, Args... args) {
-    if (n == 1 && m == 4) return Op<D, 1, 4>::run(args...);
+    if (n == 1 && m == 4) {
+        if constexpr (D == DT_I4) return hipErrorInvalidValue;   // 4-bit weights: whole bytes per group
+        else return Op<D, 1, 4>::run(args...);
+    }
     if (n == 2 && m == 4) return Op<D, 2, 4>::run(args...);
     if (n == 2 && m == 8) return Op<D, 2, 8>::run(args...);
     if (n == 4 && m == 8) return Op<D, 4, 8>::run(args...);
@@ -530,6 +644,7 @@ hipError_t nm_dispatch(int dt, int n, int m, Args... args) {
         case DT_I8: return nm_pat<Op, DT_I8>(n, m, args...);
         case DT_E4M3: return nm_pat<Op, DT_E4M3>(n, m, args...);
         case DT_E5M2: return nm_pat<Op, DT_E5M2>(n, m, args...);
+        case DT_I4: return nm_pat<Op, DT_I4>(n, m, args...);
         default: return hipErrorInvalidValue;
     }
 }
@@ -550,9 +665,8 @@ template <int D, int NN, int MM>
 struct CompressNm {
     static hipError_t run(int64_t M, int64_t K, const void* A, int64_t lda, void* vals, int64_t ldv, uint8_t* mask,
                           int64_t ldm, bool vec, hipStream_t s) {
-        using T = typename NmStore<D>::T;
-        hipLaunchKernelGGL((k_compress_nm<D, NN, MM>), dim3(nm_grid(M, K)), dim3(256), 0, s, M, K, (const T*)A, lda,
-                           (T*)vals, ldv, mask, ldm, (int)vec);
+        hipLaunchKernelGGL((k_compress_nm<D, NN, MM>), dim3(nm_grid(M, K)), dim3(256), 0, s, M, K, A, lda, vals, ldv,
+                           mask, ldm, (int)vec);
         return hipGetLastError();
     }
 };
@@ -561,9 +675,8 @@ template <int D, int NN, int MM>
 struct DecompressNm {
     static hipError_t run(int64_t M, int64_t K, const void* vals, int64_t ldv, const uint8_t* mask, int64_t ldm,
                           void* Dm, int64_t ldd, int32_t* bad, hipStream_t s) {
-        using T = typename NmStore<D>::T;
-        hipLaunchKernelGGL((k_decompress_nm<D, NN, MM>), dim3(nm_grid(M, K)), dim3(256), 0, s, M, K, (const T*)vals,
-                           ldv, mask, ldm, (T*)Dm, ldd, bad);
+        hipLaunchKernelGGL((k_decompress_nm<D, NN, MM>), dim3(nm_grid(M, K)), dim3(256), 0, s, M, K, vals, ldv, mask,
+                           ldm, Dm, ldd, bad);
         return hipGetLastError();
     }
 };
@@ -591,25 +704,29 @@ hipError_t launch_spmm_nm(int n, int m, const SpmmArgs& a, bool packed, hipStrea
     return nm_dispatch<SpmmNm>(a.dt, n, m, &a, packed, s);
 }
 
-void nm_packed_geometry(int dt, int n, int m, int64_t M, int64_t K, int64_t* tiles, int64_t* nsteps, int* mb) {
-    const int es = dt_bytes(dt);
-    const int64_t d = (16 / es) * m / n;        // dense k per lane per super-step
+void nm_packed_geometry(int dt, int n, int m, int64_t M, int64_t K, int64_t* tiles, int64_t* nsteps, int* vb,
+                        int* mb) {
+    // dense k per lane per super-step, as NmShape
+    const int64_t d = dt == DT_I4 ? 32 : (16 / dt_bytes(dt)) * m / n;
     *tiles = (M + 15) / 16;
     *nsteps = (K + 4 * d - 1) / (4 * d);
+    *vb = dt == DT_I4 ? (int)(d * n / m / 2) : 16;
     *mb = (int)(d / 8);
 }
 
 hipError_t launch_pack_nm(int dt, int n, int m, int64_t M, int64_t K, const void* vals, int64_t ldv,
                           const uint8_t* mask, int64_t ldm, void* pvals, void* pmask, hipStream_t s) {
     int64_t tiles, nsteps;
-    int mb;
-    nm_packed_geometry(dt, n, m, M, K, &tiles, &nsteps, &mb);
+    int vb, mb;
+    nm_packed_geometry(dt, n, m, M, K, &tiles, &nsteps, &vb, &mb);
     const int64_t lanes = tiles * nsteps * 64;
     if (lanes == 0) return hipSuccess;
     const int64_t g = (lanes + 255) / 256;
-    const int es = dt_bytes(dt);
+    // row bytes of the stored values: 4-bit weights are two per byte
+    const int64_t ldvb = dt == DT_I4 ? ldv / 2 : ldv * dt_bytes(dt);
+    const int64_t vrow = dt == DT_I4 ? K / m * n / 2 : K / m * n * dt_bytes(dt);
     hipLaunchKernelGGL(k_pack_nm, dim3((unsigned)(g < 8192 ? g : 8192)), dim3(256), 0, s, M, tiles, nsteps,
-                       (const uint8_t*)vals, ldv * es, K / m * n * es, mask, ldm, (K + 7) / 8, mb, (uint8_t*)pvals,
+                       (const uint8_t*)vals, ldvb, vrow, vb, mask, ldm, (K + 7) / 8, mb, (uint8_t*)pvals,
                        (uint8_t*)pmask);
     return hipGetLastError();
 }

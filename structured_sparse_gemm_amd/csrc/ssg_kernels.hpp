@@ -12,7 +12,9 @@ namespace ssg {
 
 // DT_E4M3 / DT_E5M2: OCP 8-bit floats (sign, 4/5 exponent bits with bias
 // 7/15, 3/2 fraction bits), products accumulated in fp32.
-enum Dtype { DT_F16 = 0, DT_BF16 = 1, DT_I8 = 2, DT_E4M3 = 3, DT_E5M2 = 4 };
+// DT_I4: 4-bit two's-complement weights, two per byte (low nibble first),
+// taken by the N:M kernels only, against fp16 activations.
+enum Dtype { DT_F16 = 0, DT_BF16 = 1, DT_I8 = 2, DT_E4M3 = 3, DT_E5M2 = 4, DT_I4 = 5 };
 
 constexpr bool dt_is_fp8(int dt) { return dt == DT_E4M3 || dt == DT_E5M2; }
 constexpr int dt_bytes(int dt) { return dt == DT_F16 || dt == DT_BF16 ? 2 : 1; }
@@ -82,9 +84,10 @@ hipError_t launch_decompress_nm(int dt, int n, int m, int64_t M, int64_t K, cons
 // aligned.
 hipError_t launch_spmm_nm(int n, int m, const SpmmArgs& a, bool packed, hipStream_t s);
 // Packed decode layout of the N:M operand: tiles of 16 rows, super-steps of
-// 4*D dense k, mb mask bytes per lane per super-step; pvals holds
-// tiles*nsteps KiB, pmask tiles*nsteps*64*mb bytes.
-void nm_packed_geometry(int dt, int n, int m, int64_t M, int64_t K, int64_t* tiles, int64_t* nsteps, int* mb);
+// 4*D dense k, vb value bytes and mb mask bytes per lane per super-step;
+// pvals holds tiles*nsteps*64*vb bytes, pmask tiles*nsteps*64*mb.
+void nm_packed_geometry(int dt, int n, int m, int64_t M, int64_t K, int64_t* tiles, int64_t* nsteps, int* vb,
+                        int* mb);
 hipError_t launch_pack_nm(int dt, int n, int m, int64_t M, int64_t K, const void* vals, int64_t ldv,
                           const uint8_t* mask, int64_t ldm, void* pvals, void* pmask, hipStream_t s);
 

@@ -77,6 +77,7 @@ int to_dt(int dt) {
         case SSG_BF16: return ssg::DT_BF16;
         case SSG_E4M3: return ssg::DT_E4M3;
         case SSG_E5M2: return ssg::DT_E5M2;
+        case SSG_I4: return ssg::DT_I4;
         default: return ssg::DT_I8;
     }
 }
@@ -444,10 +445,19 @@ int64_t ssg_nm_vals_cols(int nm_n, int nm_m, int64_t K) {
 
 namespace {
 
+// Bytes of a row of ld elements (4-bit weights: two per byte).
+int64_t row_bytes(int dt, int64_t ld) { return dt == SSG_I4 ? ld / 2 : ld * esize(dt); }
+
+// N:M products: the 2:4 pairs, and 4-bit weights with fp16 B into fp32.
+bool nm_pair_ok(int ab, int c) { return pair_ok(ab, c) || (ab == SSG_I4 && c == SSG_F32); }
+
 int check_nm_shape(int dt, int nm_n, int nm_m, int64_t M, int64_t K) {
-    if (!in_dtype(dt)) return fail(SSG_ERR_DTYPE, "element type %d is not SSG_F16, SSG_BF16, SSG_I8, SSG_E4M3 or SSG_E5M2", dt);
+    if (!in_dtype(dt) && dt != SSG_I4)
+        return fail(SSG_ERR_DTYPE, "element type %d is not SSG_F16, SSG_BF16, SSG_I8, SSG_E4M3, SSG_E5M2 or SSG_I4", dt);
     if (!ssg::nm_pattern_supported(nm_n, nm_m))
         return fail(SSG_ERR_SHAPE, "pattern %d:%d is not one of 1:4, 2:4, 2:8, 4:8", nm_n, nm_m);
+    if (dt == SSG_I4 && nm_n % 2)
+        return fail(SSG_ERR_SHAPE, "4-bit weights take 2:4, 2:8 or 4:8 (whole bytes per group), not %d:%d", nm_n, nm_m);
     if (M < 0 || K < 0) return fail(SSG_ERR_SHAPE, "negative size M=%lld K=%lld", (long long)M, (long long)K);
     if (K % nm_m != 0) return fail(SSG_ERR_SHAPE, "K=%lld is not a multiple of %d", (long long)K, nm_m);
     if ((M * ((K + 31) / 32)) / 256 >= (int64_t)1 << 31)
@@ -463,13 +473,15 @@ int check_nm(int dt, int nm_n, int nm_m, int64_t M, int64_t K, const void* vals,
     if (ldv < K / nm_m * nm_n)
         return fail(SSG_ERR_STRIDE, "ldv=%lld < K/%d*%d=%lld", (long long)ldv, nm_m, nm_n, (long long)(K / nm_m * nm_n));
     if (ldm < (K + 7) / 8) return fail(SSG_ERR_STRIDE, "ldmask=%lld < ceil(K/8)=%lld", (long long)ldm, (long long)((K + 7) / 8));
+    if (dt == SSG_I4 && ldv % 2) return fail(SSG_ERR_STRIDE, "4-bit rows start on whole bytes: ldv=%lld is odd", (long long)ldv);
     return SSG_OK;
 }
 
 // The compress / expand kernels' 32-element chunks: A or D rows 16-byte
 // aligned, value rows 8-byte aligned, mask rows 4-byte aligned.
 bool vec_nm(int dt, const void* dense, int64_t ldd, const void* vals, int64_t ldv, const uint8_t* mask, int64_t ldm) {
-    return rows_aligned16(dense, ldd, dt) && al(vals, 8) && (ldv * esize(dt)) % 8 == 0 && al(mask, 4) && ldm % 4 == 0;
+    return al(dense, 16) && row_bytes(dt, ldd) % 16 == 0 && al(vals, 8) && row_bytes(dt, ldv) % 8 == 0 &&
+           al(mask, 4) && ldm % 4 == 0;
 }
 
 }  // namespace
@@ -482,6 +494,7 @@ int ssg_compress_nm(int dt, int nm_n, int nm_m, int64_t M, int64_t K, const void
     if (rc) return rc;
     if (M > 0 && K > 0 && !A) return fail(SSG_ERR_NULL, "A is NULL");
     if (lda < K) return fail(SSG_ERR_STRIDE, "lda=%lld < K=%lld", (long long)lda, (long long)K);
+    if (dt == SSG_I4 && lda % 2) return fail(SSG_ERR_STRIDE, "4-bit rows start on whole bytes: lda=%lld is odd", (long long)lda);
     hipError_t e = ssg::launch_compress_nm(to_dt(dt), nm_n, nm_m, M, K, A, lda, vals, ldv, mask, ldmask,
                                            vec_nm(dt, A, lda, vals, ldv, mask, ldmask), (hipStream_t)stream);
     return e == hipSuccess ? SSG_OK : hip_fail(e, "compress_nm launch");
@@ -493,6 +506,7 @@ int ssg_decompress_nm(int dt, int nm_n, int nm_m, int64_t M, int64_t K, const vo
     if (rc) return rc;
     if (M > 0 && K > 0 && !D) return fail(SSG_ERR_NULL, "D is NULL");
     if (ldd < K) return fail(SSG_ERR_STRIDE, "ldd=%lld < K=%lld", (long long)ldd, (long long)K);
+    if (dt == SSG_I4 && ldd % 2) return fail(SSG_ERR_STRIDE, "4-bit rows start on whole bytes: ldd=%lld is odd", (long long)ldd);
     hipError_t e = ssg::launch_decompress_nm(to_dt(dt), nm_n, nm_m, M, K, vals, ldv, mask, ldmask, D, ldd, bad_count,
                                              (hipStream_t)stream);
     return e == hipSuccess ? SSG_OK : hip_fail(e, "decompress_nm launch");
@@ -500,7 +514,7 @@ int ssg_decompress_nm(int dt, int nm_n, int nm_m, int64_t M, int64_t K, const vo
 
 int ssg_spmm_nm(int ab, int c, int nm_n, int nm_m, int64_t M, int64_t N, int64_t K, const void* vals, int64_t ldv,
                 const uint8_t* mask, int64_t ldmask, const void* B, int64_t ldb, void* C, int64_t ldc, void* stream) {
-    if (!pair_ok(ab, c)) return fail(SSG_ERR_DTYPE, "unsupported (input, output) types (%d, %d)", ab, c);
+    if (!nm_pair_ok(ab, c)) return fail(SSG_ERR_DTYPE, "unsupported (input, output) types (%d, %d)", ab, c);
     int rc = check_nm(ab, nm_n, nm_m, M, K, vals, ldv, mask, ldmask);
     if (rc) return rc;
     // one grid row per 16 columns of B
@@ -510,22 +524,23 @@ int ssg_spmm_nm(int ab, int c, int nm_n, int nm_m, int64_t M, int64_t N, int64_t
     if (ldb < N) return fail(SSG_ERR_STRIDE, "ldb=%lld < N=%lld", (long long)ldb, (long long)N);
     if (ldc < N) return fail(SSG_ERR_STRIDE, "ldc=%lld < N=%lld", (long long)ldc, (long long)N);
     if (M == 0 || N == 0) return SSG_OK;
-    const int64_t es = esize(ab);
+    const int bt = ab == SSG_I4 ? SSG_F16 : ab;          // B's element type
+    const int64_t es = esize(bt);
     if (K == 0) {
         // an empty sum: the generic kernel writes the zeros and reads nothing
-        hipError_t e = ssg::launch_spmm_generic(make_args(ab, M, N, 0, nullptr, 0, nullptr, 0, B, ldb, C, ldc),
+        hipError_t e = ssg::launch_spmm_generic(make_args(bt, M, N, 0, nullptr, 0, nullptr, 0, B, ldb, C, ldc),
                                                 (hipStream_t)stream);
         return e == hipSuccess ? SSG_OK : hip_fail(e, "zero fill");
     }
     // row strides matter only where there is more than one row
-    if (!al(vals, 16) || (M > 1 && (ldv * es) % 16 != 0))
-        return fail(SSG_ERR_STRIDE, "vals rows must be 16-byte aligned (base and ldv * element size)");
+    if (!al(vals, 16) || (M > 1 && row_bytes(ab, ldv) % 16 != 0))
+        return fail(SSG_ERR_STRIDE, "vals rows must be 16-byte aligned (base and row bytes)");
     if (!al(mask, 8) || (M > 1 && ldmask % 8 != 0))
         return fail(SSG_ERR_STRIDE, "mask rows must be 8-byte aligned (base and ldmask)");
     if (!al(B, 16) || (K > 1 && (ldb * es) % 16 != 0))
         return fail(SSG_ERR_STRIDE, "B rows must be 16-byte aligned (base and ldb * element size)");
     // 32-bit buffer offsets: a workgroup's 64 rows of vals / mask, all of B
-    if (64 * ldv * es >= 0x7fffffff || 64 * ldmask >= 0x7fffffff || K * ldb * es >= 0x7fffffff)
+    if (64 * row_bytes(ab, ldv) >= 0x7fffffff || 64 * ldmask >= 0x7fffffff || K * ldb * es >= 0x7fffffff)
         return fail(SSG_ERR_SHAPE, "operands too large for 31-bit buffer offsets");
     ssg::SpmmArgs a = make_args(ab, M, N, K, vals, ldv, mask, ldmask, B, ldb, C, ldc);
     hipError_t e = ssg::launch_spmm_nm(nm_n, nm_m, a, false, (hipStream_t)stream);
@@ -538,9 +553,9 @@ int ssg_nm_packed_sizes(int dt, int nm_n, int nm_m, int64_t M, int64_t K, int64_
     if (rc) return rc;
     if (!vals_bytes || !mask_bytes) return fail(SSG_ERR_NULL, "vals_bytes or mask_bytes is NULL");
     int64_t tiles, nsteps;
-    int mb;
-    ssg::nm_packed_geometry(to_dt(dt), nm_n, nm_m, M, K, &tiles, &nsteps, &mb);
-    *vals_bytes = tiles * nsteps * 1024;
+    int vb, mb;
+    ssg::nm_packed_geometry(to_dt(dt), nm_n, nm_m, M, K, &tiles, &nsteps, &vb, &mb);
+    *vals_bytes = tiles * nsteps * 64 * vb;
     *mask_bytes = tiles * nsteps * 64 * mb;
     return SSG_OK;
 }
@@ -561,7 +576,7 @@ int ssg_pack_nm_decode(int dt, int nm_n, int nm_m, int64_t M, int64_t K, const v
 
 int ssg_spmm_nm_packed(int ab, int c, int nm_n, int nm_m, int64_t M, int64_t N, int64_t K, const void* pvals,
                        const void* pmask, const void* B, int64_t ldb, void* C, int64_t ldc, void* stream) {
-    if (!pair_ok(ab, c)) return fail(SSG_ERR_DTYPE, "unsupported (input, output) types (%d, %d)", ab, c);
+    if (!nm_pair_ok(ab, c)) return fail(SSG_ERR_DTYPE, "unsupported (input, output) types (%d, %d)", ab, c);
     int64_t vb, mb;
     int rc = ssg_nm_packed_sizes(ab, nm_n, nm_m, M, K, &vb, &mb);
     if (rc) return rc;
@@ -571,7 +586,7 @@ int ssg_spmm_nm_packed(int ab, int c, int nm_n, int nm_m, int64_t M, int64_t N, 
     if (!pvals || !pmask || !B || !C) return fail(SSG_ERR_NULL, "a required pointer is NULL");
     if (ldb < N) return fail(SSG_ERR_STRIDE, "ldb=%lld < N=%lld", (long long)ldb, (long long)N);
     if (ldc < N) return fail(SSG_ERR_STRIDE, "ldc=%lld < N=%lld", (long long)ldc, (long long)N);
-    const int64_t es = esize(ab);
+    const int64_t es = esize(ab == SSG_I4 ? SSG_F16 : ab);   // B's element size
     if (!al(pvals, 16) || !al(pmask, 8)) return fail(SSG_ERR_STRIDE, "pvals must be 16-byte and pmask 8-byte aligned");
     if (!al(B, 16) || (K > 1 && (ldb * es) % 16 != 0))
         return fail(SSG_ERR_STRIDE, "B rows must be 16-byte aligned (base and ldb * element size)");

@@ -215,15 +215,16 @@ def expected_packed_nm(dt, n, m, vals, mask, M, K):
     and super-step, lane l = 16q + r carries row r's value bytes
     [64g + 16q, +16) and mask bytes [g*D/2 + q*D/8, +D/8)."""
     es = 2 if dt in ("f16", "bf16") else 1
-    D = (16 // es) * m // n
+    D = 32 if dt == "i4" else (16 // es) * m // n
+    VB = D * n // m // 2 if dt == "i4" else 16        # value bytes per lane per super-step
     SK, MB = 4 * D, D // 8
     nsteps, tiles = -(-K // SK), -(-M // 16)
     vb = np.ascontiguousarray(vals).view(np.uint8).reshape(M, -1)
-    Vp = np.zeros((tiles * 16, nsteps * 64), dtype=np.uint8)
+    Vp = np.zeros((tiles * 16, nsteps * 4 * VB), dtype=np.uint8)
     Vp[:M, :vb.shape[1]] = vb
     Mp = np.zeros((tiles * 16, nsteps * 4 * MB), dtype=np.uint8)
     Mp[:M, :mask.shape[1]] = mask
-    pv = Vp.reshape(tiles, 16, nsteps, 4, 16).transpose(0, 2, 3, 1, 4).reshape(-1)
+    pv = Vp.reshape(tiles, 16, nsteps, 4, VB).transpose(0, 2, 3, 1, 4).reshape(-1)
     pm = Mp.reshape(tiles, 16, nsteps, 4, MB).transpose(0, 2, 3, 1, 4).reshape(-1)
     return pv, pm
 
@@ -282,3 +283,103 @@ def test_patterns_within_2to4_run_on_the_sparse_mfma(dt, pat):
     rv, rmask = oracle.compress_nm(dt, n, m, a)
     c_ref, s_ref = oracle.spmm_nm(dt, n, m, rv, rmask, b, K)
     check_product(dt, to_host(C), c_ref, s_ref, "%d:%d via 2:4 large-N" % pat)
+
+
+# ------------------------------------------------------------------ 4-bit weights, fp16 activations
+
+I4_PATS = [(2, 4), (2, 8), (4, 8)]
+I4_IDS = ["%d:%d" % p for p in I4_PATS]
+
+
+@pytest.mark.parametrize("pat", I4_PATS, ids=I4_IDS)
+@pytest.mark.parametrize("fam", ["normal", "ties", "sparse", "extreme"])
+@pytest.mark.parametrize("shape", [(1, 8), (3, 40), (37, 200), (128, 4096), (33, 8200)])
+def test_i4_compress_and_expand_bitexact(pat, fam, shape):
+    n, m = pat
+    M, K = shape
+    if K % m:
+        K += m - K % m
+    a = U.random_matrix("i4", M, K, fam, seed=M + K + n + 7 * m)
+    vals, mask = ssg.compress_nm(to_dev(a, "i4"), n, m)
+    rv, rmask = oracle.compress_nm("i4", n, m, a)
+    assert np.array_equal(to_host(vals.contiguous()), rv)
+    assert np.array_equal(to_host(mask.contiguous()), rmask)
+    D, bad = ssg.decompress_nm(vals, mask, n, m, K, count_bad=True)
+    rd, rbad = oracle.decompress_nm("i4", n, m, rv, rmask, K)
+    assert bad == rbad == 0
+    assert np.array_equal(to_host(D), rd)
+
+
+@pytest.mark.parametrize("pat", I4_PATS, ids=I4_IDS)
+@pytest.mark.parametrize("shape", PRODUCT_SHAPES, ids=["x".join(map(str, s)) for s in PRODUCT_SHAPES])
+def test_i4_w4a16_product_matches_oracle(pat, shape):
+    n, m = pat
+    M, K, N = shape
+    if K % m:
+        K += m - K % m
+    a = U.random_matrix("i4", M, K, "normal", seed=M + K + N + 1)
+    b = U.random_matrix("f16", K, N, "normal", seed=M * 3 + N + 1)
+    vals, mask = ssg.compress_nm(to_dev(a, "i4"), n, m)
+    B = b_dev(b, "f16")
+    C = ssg.spmm_nm(vals, mask, n, m, B)
+    rv, rmask = oracle.compress_nm("i4", n, m, a)
+    c_ref, s_ref = oracle.spmm_nm("i4", n, m, rv, rmask, b, K)
+    check_product("f16", to_host(C), c_ref, s_ref, "i4 %d:%d %s" % (n, m, shape))
+    pvals, pmask = ssg.pack_nm(vals, mask, n, m, K)
+    ev, em = expected_packed_nm("i4", n, m, rv, rmask, M, K)
+    assert np.array_equal(pvals.cpu().numpy(), ev)
+    assert np.array_equal(pmask.cpu().numpy(), em)
+    Cp = ssg.spmm_nm_packed(pvals, pmask, n, m, M, B, i4=True)
+    check_product("f16", to_host(Cp), c_ref, s_ref, "i4 packed %d:%d %s" % (n, m, shape))
+
+
+@pytest.mark.parametrize("pat", I4_PATS, ids=I4_IDS)
+def test_i4_w4a16_exact_small_integers(pat):
+    """Every 4-bit value times a small integer, and every partial sum, is exact
+    in fp32: a misplaced element, a wrong nibble or a sign error shows as a
+    hard mismatch."""
+    n, m = pat
+    M, K, N = 160, 2304, 16
+    a = U.random_matrix("i4", M, K, "normal", seed=5 * n + m)
+    b = U.encode("f16", np.random.default_rng(2 * n + m).integers(-3, 4, size=(K, N)))
+    vals, mask = ssg.compress_nm(to_dev(a, "i4"), n, m)
+    B = to_dev(b, "f16")
+    rv, rmask = oracle.compress_nm("i4", n, m, a)
+    c_ref, _ = oracle.spmm_nm("i4", n, m, rv, rmask, b, K)
+    assert np.array_equal(to_host(ssg.spmm_nm(vals, mask, n, m, B)).astype(np.float64), c_ref)
+    pv, pm = ssg.pack_nm(vals, mask, n, m, K)
+    assert np.array_equal(to_host(ssg.spmm_nm_packed(pv, pm, n, m, M, B, i4=True)).astype(np.float64), c_ref)
+
+
+@pytest.mark.parametrize("pat", I4_PATS, ids=I4_IDS)
+def test_i4_decode_workload_full_size(pat):
+    """The fp16 decode shape 11008 x 4096 x 16 with 4-bit weights, in full."""
+    n, m = pat
+    w = W.Workload("c3w4", "4-bit weights", "i4", 11008, 4096, 16, 9, klass="small_n", b_dtype="f16")
+    a_t, b_t = W.gen_a(w), W.gen_b(w)
+    a, b = W.bits(a_t), W.bits(b_t)
+    vals, mask = ssg.compress_nm(a_t.cuda(), n, m)
+    rv, rmask = oracle.compress_nm("i4", n, m, a)
+    assert np.array_equal(to_host(vals.contiguous()), rv)
+    assert np.array_equal(to_host(mask.contiguous()), rmask)
+    c_ref, s_ref = oracle.spmm_nm("i4", n, m, rv, rmask, b, w.K)
+    C = ssg.spmm_nm(vals, mask, n, m, b_t.cuda())
+    check_product("f16", to_host(C), c_ref, s_ref, "c3w4 %d:%d" % pat)
+    pv, pm = ssg.pack_nm(vals, mask, n, m, w.K)
+    Cp = ssg.spmm_nm_packed(pv, pm, n, m, w.M, b_t.cuda(), i4=True)
+    check_product("f16", to_host(Cp), c_ref, s_ref, "c3w4 packed %d:%d" % pat)
+
+
+def test_i4_argument_errors():
+    a = U.random_matrix("i4", 16, 256, "normal", seed=1)
+    A = to_dev(a, "i4")
+    with pytest.raises(ssg.SsgError) as e:
+        ssg.compress_nm(A, 1, 4)                                    # half a byte per group
+    assert e.value.status == ssg._abi.SSG_ERR_SHAPE
+    vals, mask = ssg.compress_nm(A, 2, 4)
+    B = torch.zeros((256, 16), dtype=torch.float16, device="cuda")
+    C = torch.empty((16, 16), dtype=torch.int32, device="cuda")
+    with pytest.raises(ssg.SsgError) as e:
+        ssg._check(ssg._lib().ssg_spmm_nm(ssg._abi.SSG_I4, ssg.SSG_I32, 2, 4, 16, 16, 256, vals.data_ptr(), 256,
+                                          mask.data_ptr(), 32, B.data_ptr(), 16, C.data_ptr(), 16, None), "w4")
+    assert e.value.status == ssg._abi.SSG_ERR_DTYPE
