@@ -201,7 +201,7 @@ def bench_workload(key: str, iters: int, read_GBps: float, delta: bool = False, 
     def launch(i):
         o = sets[i % copies]
         if nm is not None and packed:
-            ssg.ssg_spmm_nm_packed(o[0], o[1], nm[0], nm[1], w.M, b, out)
+            ssg.ssg_spmm_nm_packed(o[0], o[1], nm[0], nm[1], w.M, b, out, i4=w.dtype == "i4")
         elif nm is not None:
             ssg.ssg_spmm_nm(o[0], o[1], nm[0], nm[1], w.K, b, out)
         elif packed:
@@ -244,8 +244,9 @@ def bench_workload(key: str, iters: int, read_GBps: float, delta: bool = False, 
         return r
 
     # dense comparator: the same product as a dense GEMM (vendor library via
-    # torch), weights as a dense matrix, copies rotated like the sparse ones
-    dense = a
+    # torch), weights as a dense matrix, copies rotated like the sparse ones;
+    # for 4-bit weights, dense fp16 weights of the same shape
+    dense = a if w.dtype != "i4" else (torch.randn((w.M, w.K), device="cuda") * 0.02).half()
     dbytes = dense.numel() * dense.element_size()
     dcopies = max(1, int(np.ceil((1 << 30) / dbytes))) if w.klass == "small_n" else 1
     dsets = [dense] + [dense.clone() for _ in range(dcopies - 1)]
@@ -505,11 +506,12 @@ def main() -> int:
         out["measured_read_GBps"] = rbw
         table = {}
         only = [k for k in args.only.split(",") if k]
-        for k in ("c1", "c3", "c4", "c5", "c3f8", "c4f8", "c3nm"):
+        for k in ("c1", "c3", "c4", "c5", "c3f8", "c4f8", "c3nm", "c3w4"):
             if only and k not in only:
                 continue
-            if k == "c3nm":
-                for i, (n, m) in enumerate(((1, 4), (2, 4), (2, 8), (4, 8))):
+            if k in ("c3nm", "c3w4"):
+                pats = ((1, 4), (2, 4), (2, 8), (4, 8)) if k == "c3nm" else ((2, 4), (2, 8), (4, 8))
+                for i, (n, m) in enumerate(pats):
                     print("bench: workload %s, %d:%d ..." % (k, n, m), file=sys.stderr, flush=True)
                     table["%s_%d:%d" % (k, n, m)] = bench_workload(k, args.workload_iters or 200, rbw,
                                                                    dense_cmp=i == 0, nm=(n, m))

@@ -79,6 +79,9 @@ WORKLOADS = {
     # (1:4, 2:8, 4:8) are selected from
     "c3nm": Workload("c3nm", "fp16 N:M decode-shape SpMM M=11008 K=4096 N=16", "f16", 11008, 4096, 16, 8,
                      a_sigma=0.02, klass="small_n"),
+    # the decode shape with 4-bit weights (uniform over [-8, 7]) and fp16 activations
+    "c3w4": Workload("c3w4", "4-bit-weight N:M decode-shape SpMM M=11008 K=4096 N=16 (fp16 activations)", "i4",
+                     11008, 4096, 16, 9, klass="small_n", b_dtype="f16"),
 }
 
 
