@@ -4,9 +4,12 @@
 
 Headline workload: int8 2:4 SpMM with M = K = N = 4096 (A uniform in
 [-127, 127] pruned 2:4 by magnitude, B uniform int8, int32 accumulate).  One
-step is the whole hot path over one batch: prune + compress A on the GPU,
-then C = expand(vals, meta) x B.  `value` is dense-equivalent throughput
-2*M*N*K / step time, inputs resident in HBM before the timed region.
+step is the whole hot path over one batch: prune + compress A on the GPU
+straight into the packed prefill layout (the large-N kernel's LDS image of
+each 256-row tile), then C = expand(packed) x B on the large-N kernel.
+`value` is dense-equivalent throughput 2*M*N*K / step time, inputs resident
+in HBM before the timed region.  The row-major product of the same operand
+is timed beside it.
 
 Also printed, in the same JSON line:
 * roofline: the SpMM kernel's own launch duration from HIP events recorded on
@@ -166,12 +169,13 @@ def read_bandwidth_GBps() -> float:
 
 
 def bench_workload(key: str, iters: int, read_GBps: float, delta: bool = False, dense_cmp: bool = True,
-                   packed: bool = False, nm=None):
+                   packed: bool = False, nm=None, prefill: bool = False):
     """Kernel-level numbers for one workload (compression outside the timing),
     next to a dense GEMM of the same shape from the vendor library.  With
     delta=True the residual is delta-coded (one-byte column gaps); with
     packed=True the 2:4 operand is in the packed decode layout; with
-    nm=(n, m) the weight is in the n:m form (kept values plus keep mask)."""
+    prefill=True in the packed prefill layout; with nm=(n, m) the weight is
+    in the n:m form (kept values plus keep mask)."""
     import numpy as np
     import torch
 
@@ -184,6 +188,8 @@ def bench_workload(key: str, iters: int, read_GBps: float, delta: bool = False, 
         ops = ssg.compress_nm(a, nm[0], nm[1])
         if packed:
             ops = ssg.pack_nm(ops[0], ops[1], nm[0], nm[1], w.K)
+    elif prefill:
+        ops = ssg.compress_prefill(a)
     else:
         ops = ssg.split(a) if w.residual else ssg.compress(a)
     if delta:
@@ -196,7 +202,8 @@ def bench_workload(key: str, iters: int, read_GBps: float, delta: bool = False, 
         copies = max(1, int(np.ceil((1 << 30) / wbytes)))
     sets = [ops] + [tuple(t.clone() for t in ops) for _ in range(copies - 1)]
     out = torch.empty((w.M, w.N), dtype=torch.int32 if w.dtype == "i8" else torch.float32, device="cuda")
-    algo = ssg.SSG_ALGO_SMALL_N if packed or nm else ssg.ssg_spmm_select_algo(ops[0], ops[1], b, out)
+    algo = (ssg.SSG_ALGO_SMALL_N if packed or nm else ssg.SSG_ALGO_LARGE_N if prefill
+            else ssg.ssg_spmm_select_algo(ops[0], ops[1], b, out))
 
     def launch(i):
         o = sets[i % copies]
@@ -206,6 +213,8 @@ def bench_workload(key: str, iters: int, read_GBps: float, delta: bool = False, 
             ssg.ssg_spmm_nm(o[0], o[1], nm[0], nm[1], w.K, b, out)
         elif packed:
             ssg.ssg_spmm_2to4_packed(o[0], o[1], w.M, b, out)
+        elif prefill:
+            ssg.ssg_spmm_2to4_prefill(o[0], o[1], w.M, b, out)
         elif delta:
             ssg.ssg_spmm_2to4_residual_delta(*o, b, out)
         elif w.residual:
@@ -225,8 +234,9 @@ def bench_workload(key: str, iters: int, read_GBps: float, delta: bool = False, 
     bbytes = b.numel() * b.element_size()
     cbytes = out.numel() * out.element_size()
     r = {"title": w.title + (", residual delta-coded" if delta else "") + (", packed decode layout" if packed else "")
-         + (", %d:%d" % tuple(nm) if nm else ""),
-         "algo": ("nm (dense MFMA on the expanded operand)" if nm else ssg.ALGO_NAMES[algo]) + (" (packed)" if packed else ""),
+         + (", packed prefill layout" if prefill else "") + (", %d:%d" % tuple(nm) if nm else ""),
+         "algo": ("nm (dense MFMA on the expanded operand)" if nm else ssg.ALGO_NAMES[algo])
+         + (" (packed)" if packed else "") + (" (packed prefill)" if prefill else ""),
          "us_per_launch": s * 1e6,
          "timing": "HIP graph of %d launches, replayed twice; replay output matches eager: %s" % (n, graph_ok),
          "dense_equiv_TFLOPs": flops / s / 1e12, "compressed_weight_bytes": wbytes,
@@ -395,14 +405,15 @@ def main() -> int:
     print("bench: %s" % w.title, file=sys.stderr, flush=True)
     a_cpu, b_cpu = W.gen_a(w), W.gen_b(w)
     A, B = a_cpu.cuda(), b_cpu.cuda()
-    vals = torch.empty((w.M, w.K // 2), dtype=A.dtype, device="cuda")
-    meta = torch.empty((w.M, (w.K + 7) // 8), dtype=torch.uint8, device="cuda")
+    vb, mb = ssg.ssg_prefill_packed_sizes(A.dtype, w.M, w.K)
+    vals = torch.empty(vb, dtype=torch.uint8, device="cuda")       # packed prefill layout
+    meta = torch.empty(mb, dtype=torch.uint8, device="cuda")
     C = torch.empty((w.M, w.N), dtype=torch.int32, device="cuda")
     stream = torch.cuda.current_stream()
 
     def step():
-        ssg.ssg_compress_2to4(A, vals, meta)
-        ssg.ssg_spmm_2to4(vals, meta, B, C)
+        ssg.ssg_compress_2to4_prefill(A, vals, meta)
+        ssg.ssg_spmm_2to4_prefill(vals, meta, w.M, B, C)
 
     for _ in range(args.warmup):
         step()
@@ -442,8 +453,15 @@ def main() -> int:
     # kernel durations: back-to-back launches between two HIP events on the
     # stream the kernels run on
     reps = max(args.steps, 20)
-    spmm_s = time_kernel(lambda i: ssg.ssg_spmm_2to4(vals, meta, B, C), reps, stream)
-    comp_s = time_kernel(lambda i: ssg.ssg_compress_2to4(A, vals, meta), reps, stream)
+    spmm_s = time_kernel(lambda i: ssg.ssg_spmm_2to4_prefill(vals, meta, w.M, B, C), reps, stream)
+    comp_s = time_kernel(lambda i: ssg.ssg_compress_2to4_prefill(A, vals, meta), reps, stream)
+    # the same product from the row-major (interchange) operand
+    rvals, rmeta = ssg.compress(A)
+    C_rm = ssg.spmm(rvals, rmeta, B, algo=ssg.SSG_ALGO_LARGE_N)
+    torch.cuda.synchronize()
+    rowmajor = {"spmm_us": time_kernel(lambda i: ssg.ssg_spmm_2to4(rvals, rmeta, B, C_rm), reps, stream) * 1e6,
+                "same_result_bits": bool(torch.equal(C_rm, C))}
+    del rvals, rmeta, C_rm
     flops = 2.0 * w.M * w.N * w.K
     algo_ops = float(w.M) * w.N * w.K          # two ops per stored product, half the positions stored
     print("bench: step %.3f ms (graph replay; compress %.1f us, spmm %.1f us)" % (ms, comp_s * 1e6, spmm_s * 1e6),
@@ -460,7 +478,7 @@ def main() -> int:
         dense_note = {"dense_gemm": "unavailable: %s" % str(e).splitlines()[0][:120]}
 
     roofline = {
-        "kernel": "spmm_large_n (int8 sparse MFMA 32x32x64)",
+        "kernel": "spmm_large_n on the packed prefill layout (int8 sparse MFMA 32x32x64)",
         "bound": "mfma",
         "achieved": algo_ops / spmm_s / 1e12,
         "peak": PEAK["i8"],
@@ -484,10 +502,12 @@ def main() -> int:
         "vs_baseline": None,
         "dtype": "i8",
         "data": "synthetic",
-        "config": {"workload": "int8 2:4 SpMM M=K=N=4096; step = prune+compress A, then SpMM (int32 out)",
+        "config": {"workload": "int8 2:4 SpMM M=K=N=4096; step = prune+compress A (packed prefill layout), "
+                               "then SpMM (int32 out)",
                    "M": w.M, "K": w.K, "N": w.N, "seeds": [1000 + w.index, 2000 + w.index]},
         "spmm_only_dense_equiv_TFLOPs": flops / spmm_s / 1e12,
         "compress_us": comp_s * 1e6,
+        "rowmajor_operand": rowmajor,
         "launch": "HIP graph of the step (compress + SpMM), replayed; replays match eager outputs: %s" % graph_ok,
         "device": "%s, HIP %s" % (torch.cuda.get_device_name(0), torch.version.hip),
         "roofline": roofline,
@@ -523,6 +543,9 @@ def main() -> int:
             print("bench: workload %s ..." % k, file=sys.stderr, flush=True)
             it = args.workload_iters or (200 if W.WORKLOADS[k].klass != "large_n" else 20)
             table[k] = bench_workload(k, it, rbw)
+            if W.WORKLOADS[k].klass == "large_n" and k != "c1":
+                print("bench: workload %s, packed prefill layout ..." % k, file=sys.stderr, flush=True)
+                table[k + "_prefill"] = bench_workload(k, it, rbw, dense_cmp=False, prefill=True)
             if W.WORKLOADS[k].residual:
                 print("bench: workload %s, delta-coded residual ..." % k, file=sys.stderr, flush=True)
                 table[k + "_delta"] = bench_workload(k, it, rbw, delta=True, dense_cmp=False)

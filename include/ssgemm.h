@@ -251,6 +251,46 @@ int ssg_pack_2to4_decode(int dt, int64_t M, int64_t K, const void* vals, int64_t
 int ssg_spmm_2to4_packed(int ab, int c, int64_t M, int64_t N, int64_t K, const void* pvals, const void* pmeta,
                          const void* B, int64_t ldb, void* C, int64_t ldc, void* stream);
 
+/* Packed prefill layout: the 2:4 operand rearranged, offline like the
+ * compression, into the order the large-N (compute-bound) kernel stages it
+ * in LDS, so that every load of stored values or metadata is one contiguous
+ * piece ("Chapter 26 -- Sparsity: The Hardware View", section "2:4: ~2x on
+ * the Matmul, Less End-to-End": in the compute-bound regime the doubled
+ * sparse matrix rate pays only if the operands keep up).  In bytes it is the
+ * same for every element type.  Rows are grouped in tiles of 256; a stage is
+ * 64 stored-value bytes of a row (64 dense k for fp16/bf16, 128 for the
+ * 8-bit types); a metadata block is 32 metadata bytes of a row (256 dense k).
+ *   pvals: tile t, stage s -> 16 KiB block (t * stages + s); row r of the tile
+ *          at byte r * 64 of it, its 16-byte chunk c (stored-value bytes
+ *          [64 s + 16 c, +16) of the row) at chunk position
+ *          c ^ (((r >> 1) ^ (r >> 3)) & 3).
+ *   pmeta: tile t, block g -> 8 KiB block (t * mblocks + g); row r's metadata
+ *          bytes [32 g, 32 g + 32) at byte r * 32 of it.
+ * stages = K / 64 (fp16/bf16) or K / 128 (8-bit); mblocks = ceil(K / 256).
+ * Rows past M and metadata bytes past K / 8 hold zeros.  The same bytes as
+ * (vals, meta), only reordered.
+ *
+ * ssg_prefill_packed_sizes: bytes of pvals and pmeta.  K must be a multiple
+ * of the stage (SSG_ERR_SHAPE otherwise). */
+int ssg_prefill_packed_sizes(int dt, int64_t M, int64_t K, int64_t* vals_bytes, int64_t* meta_bytes);
+
+/* Prune and compress A (as ssg_compress_2to4) straight into the packed
+ * prefill layout: caller-allocated pvals (16-byte aligned) and pmeta (4-byte
+ * aligned) of ssg_prefill_packed_sizes() bytes, every byte written. */
+int ssg_compress_2to4_prefill(int dt, int64_t M, int64_t K, const void* A, int64_t lda, void* pvals, void* pmeta,
+                              void* stream);
+
+/* Pack (vals, meta) (vals rows 16-byte aligned) into the packed prefill
+ * layout; the result equals ssg_compress_2to4_prefill of the dense matrix. */
+int ssg_pack_2to4_prefill(int dt, int64_t M, int64_t K, const void* vals, int64_t ldv, const uint8_t* meta,
+                          int64_t ldm, void* pvals, void* pmeta, void* stream);
+
+/* C = expand(packed prefill) x B on the large-N kernel, with the pairs and
+ * accumulation of ssg_spmm_2to4.  Needs N a multiple of 8 (16-bit) or 16
+ * (8-bit), B rows 16-byte aligned (SSG_ERR_ALGO otherwise), K > 0. */
+int ssg_spmm_2to4_prefill(int ab, int c, int64_t M, int64_t N, int64_t K, const void* pvals, const void* pmeta,
+                          const void* B, int64_t ldb, void* C, int64_t ldc, void* stream);
+
 /* N:M patterns other than 2:4 ("Chapter 26 -- Sparsity: The Hardware View",
  * section "Block Sparsity, N:M Generalizations, and Channel Pruning", which
  * lists 1:4, 2:8 and 4:8 and gives no selection rule or storage; what

@@ -29,6 +29,8 @@ __all__ = [
     "ssg_spmm_2to4_residual", "ssg_spmm_2to4_residual_delta", "ssg_spmm_select_algo", "ssg_spmm_csr",
     "ssg_spmm_csr_delta", "spmm_csr", "spmm_csr_delta", "ssg_packed_sizes", "ssg_pack_2to4_decode",
     "ssg_spmm_2to4_packed", "pack_decode", "spmm_packed",
+    "ssg_prefill_packed_sizes", "ssg_compress_2to4_prefill", "ssg_pack_2to4_prefill", "ssg_spmm_2to4_prefill",
+    "compress_prefill", "pack_prefill", "spmm_prefill",
     "ssg_compress_nm", "ssg_decompress_nm", "ssg_spmm_nm", "compress_nm", "decompress_nm", "spmm_nm",
     "ssg_nm_packed_sizes", "ssg_pack_nm_decode", "ssg_spmm_nm_packed", "pack_nm", "spmm_nm_packed",
     "SSG_ALGO_AUTO", "SSG_ALGO_GENERIC", "SSG_ALGO_SMALL_N", "SSG_ALGO_LARGE_N", "library_path",
@@ -245,6 +247,35 @@ def ssg_spmm_2to4_packed(pvals, pmeta, M: int, B, C, stream=None) -> None:
            "ssg_spmm_2to4_packed")
 
 
+def ssg_prefill_packed_sizes(dtype: torch.dtype, M: int, K: int) -> Tuple[int, int]:
+    import ctypes
+    vb, mb = ctypes.c_int64(0), ctypes.c_int64(0)
+    _check(_lib().ssg_prefill_packed_sizes(_DT[dtype], M, K, ctypes.byref(vb), ctypes.byref(mb)),
+           "ssg_prefill_packed_sizes")
+    return int(vb.value), int(mb.value)
+
+
+def ssg_compress_2to4_prefill(A: torch.Tensor, pvals, pmeta, stream=None) -> None:
+    M, K = A.shape
+    _check(_lib().ssg_compress_2to4_prefill(_dtype(A), M, K, _ptr(A, "A"), _ld(A, "A"), _ptr(pvals, "pvals"),
+                                            _ptr(pmeta, "pmeta"), _stream(A, stream)), "ssg_compress_2to4_prefill")
+
+
+def ssg_pack_2to4_prefill(vals, meta, K: int, pvals, pmeta, stream=None) -> None:
+    M = vals.shape[0]
+    _check(_lib().ssg_pack_2to4_prefill(_dtype(vals), M, K, _ptr(vals, "vals"), _ld(vals, "vals"),
+                                        _ptr(meta, "meta"), _ld(meta, "meta"), _ptr(pvals, "pvals"),
+                                        _ptr(pmeta, "pmeta"), _stream(vals, stream)), "ssg_pack_2to4_prefill")
+
+
+def ssg_spmm_2to4_prefill(pvals, pmeta, M: int, B, C, stream=None) -> None:
+    ab = _dtype(B)
+    N, K = B.shape[1], B.shape[0]
+    _check(_lib().ssg_spmm_2to4_prefill(ab, _OUT[ab][0], M, N, K, _ptr(pvals, "pvals"), _ptr(pmeta, "pmeta"),
+                                        _ptr(B, "B"), _ld(B, "B"), _ptr(C, "C"), _ld(C, "C"), _stream(C, stream)),
+           "ssg_spmm_2to4_prefill")
+
+
 def ssg_spmm_select_algo(vals, meta, B, C) -> int:
     return int(_lib().ssg_spmm_select_algo(_dtype(vals), vals.shape[0], B.shape[1], B.shape[0], _ptr(vals, "vals"),
                                            _ld(vals, "vals"), _ptr(meta, "meta"), _ld(meta, "meta"), _ptr(B, "B"),
@@ -457,6 +488,38 @@ def pack_decode(vals: torch.Tensor, meta: torch.Tensor, K: Optional[int] = None)
     pmeta = torch.empty(mb, dtype=torch.uint8, device=vals.device)
     ssg_pack_2to4_decode(vals, meta, K, pvals, pmeta)
     return pvals, pmeta
+
+
+def _prefill_buffers(dtype: torch.dtype, M: int, K: int, device):
+    vb, mb = ssg_prefill_packed_sizes(dtype, M, K)
+    return (torch.empty(vb, dtype=torch.uint8, device=device), torch.empty(mb, dtype=torch.uint8, device=device))
+
+
+def compress_prefill(A: torch.Tensor):
+    """(pvals, pmeta) byte tensors of the packed prefill layout of a dense [M, K]
+    weight, compressed straight into it."""
+    M, K = A.shape
+    pvals, pmeta = _prefill_buffers(A.dtype, M, K, A.device)
+    ssg_compress_2to4_prefill(A, pvals, pmeta)
+    return pvals, pmeta
+
+
+def pack_prefill(vals: torch.Tensor, meta: torch.Tensor, K: Optional[int] = None):
+    """(pvals, pmeta) byte tensors of the packed prefill layout of (vals, meta)."""
+    K = 2 * vals.shape[1] if K is None else K
+    pvals, pmeta = _prefill_buffers(vals.dtype, vals.shape[0], K, vals.device)
+    ssg_pack_2to4_prefill(vals, meta, K, pvals, pmeta)
+    return pvals, pmeta
+
+
+def spmm_prefill(pvals: torch.Tensor, pmeta: torch.Tensor, M: int, B: torch.Tensor,
+                 out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """C = expand(packed prefill) @ B on the large-N kernel: fp32 for float
+    inputs, int32 for int8."""
+    ab = _dtype(B)
+    C = torch.empty((M, B.shape[1]), dtype=_OUT[ab][1], device=B.device) if out is None else out
+    ssg_spmm_2to4_prefill(pvals, pmeta, M, B, C)
+    return C
 
 
 def spmm_packed(pvals: torch.Tensor, pmeta: torch.Tensor, M: int, B: torch.Tensor,

@@ -107,20 +107,45 @@ __device__ __forceinline__ void store_compressed(typename Store<DT>::T* vrow, ui
 // Grid-stride loop over chunks with the next chunk's loads in flight while
 // the current one is selected and stored, so reads and writes of the pass
 // overlap instead of running as one load phase followed by one store phase.
+// Packed prefill output: the chunk's stored values (whole 16-byte chunks of
+// the layout) and its metadata word at their places in (pvals, pmeta); the
+// last chunk of a row also zeroes the row's metadata bytes past K / 8 in its
+// last block.  K is a multiple of 64, so every chunk is full.
 template <int DT>
+__device__ __forceinline__ void store_prefill(uint8_t* pv, uint8_t* pm, int64_t m, int64_t c, int64_t K,
+                                              int64_t stages, int64_t mblocks,
+                                              const typename Store<DT>::T (&v)[2 * kChunkGroups], uint32_t word) {
+    using T = typename Store<DT>::T;
+    constexpr int kVecs = 2 * kChunkGroups * sizeof(T) / 16;
+    uint4 w[kVecs];
+    __builtin_memcpy(w, v, sizeof(w));
+#pragma unroll
+    for (int i = 0; i < kVecs; ++i)
+        *reinterpret_cast<uint4*>(pv + prefill_vals_offset(m, (c * kVecs + i) * 16, stages)) = w[i];
+    *reinterpret_cast<uint32_t*>(pm + prefill_meta_offset(m, c * 4, mblocks)) = word;
+    if ((c + 1) * kChunkElems == K)
+        for (int64_t j = K / 8; j < mblocks * 32; j += 4)
+            *reinterpret_cast<uint32_t*>(pm + prefill_meta_offset(m, j, mblocks)) = 0u;
+}
+
+// PF: write the packed prefill layout (vals / meta are pvals / pmeta, rows
+// run to the 256-row tile boundary past M with zeros) instead of row-major.
+template <int DT, bool PF>
 __global__ void __launch_bounds__(256) k_compress(int64_t M, int64_t K, const typename Store<DT>::T* __restrict__ A,
                                                   int64_t lda, typename Store<DT>::T* __restrict__ vals, int64_t ldv,
                                                   uint8_t* __restrict__ meta, int64_t ldm, int vec) {
     using T = typename Store<DT>::T;
     const int64_t chunks = (K + kChunkElems - 1) / kChunkElems;
-    const int64_t total = M * chunks;
+    const int64_t rows = PF ? (M + 255) / 256 * 256 : M;
+    const int64_t total = rows * chunks;
+    const int64_t stages = K / 2 * (int64_t)sizeof(T) / 64, mblocks = (K + 255) / 256;
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
     int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (t >= total) return;
     int64_t m = t / chunks, c = t - m * chunks;
     int ng = (int)min<int64_t>(kChunkGroups, (K - c * kChunkElems) / 4);
     T x[kChunkElems];
-    load_chunk<DT>(A + m * lda + c * kChunkElems, ng, vec != 0, x);
+    load_chunk<DT>(A + min(m, M - 1) * lda + c * kChunkElems, ng, vec != 0, x);
     for (;;) {
         const int64_t tn = t + stride;
         const bool more = tn < total;
@@ -131,12 +156,21 @@ __global__ void __launch_bounds__(256) k_compress(int64_t M, int64_t K, const ty
             mn = tn / chunks;
             cn = tn - mn * chunks;
             ngn = (int)min<int64_t>(kChunkGroups, (K - cn * kChunkElems) / 4);
-            load_chunk<DT>(A + mn * lda + cn * kChunkElems, ngn, vec != 0, xn);
+            load_chunk<DT>(A + min(mn, M - 1) * lda + cn * kChunkElems, ngn, vec != 0, xn);
         }
         T v[2 * kChunkGroups];
-        const uint32_t word = select_chunk<DT>(x, ng, v);
-        store_compressed<DT>(vals + m * ldv + c * 2 * kChunkGroups, meta + m * ldm + c * (kChunkGroups / 2), ng,
-                             vec != 0, v, word);
+        uint32_t word = select_chunk<DT>(x, ng, v);
+        if constexpr (PF) {
+            if (m >= M) {   // padding row of the last tile
+                word = 0;
+#pragma unroll
+                for (int i = 0; i < 2 * kChunkGroups; ++i) v[i] = T(0);
+            }
+            store_prefill<DT>(reinterpret_cast<uint8_t*>(vals), meta, m, c, K, stages, mblocks, v, word);
+        } else {
+            store_compressed<DT>(vals + m * ldv + c * 2 * kChunkGroups, meta + m * ldm + c * (kChunkGroups / 2), ng,
+                                 vec != 0, v, word);
+        }
         if (!more) break;
 #pragma unroll
         for (int i = 0; i < kChunkElems; ++i) x[i] = xn[i];
@@ -489,8 +523,22 @@ hipError_t launch_compress(int dt, int64_t M, int64_t K, const void* A, int64_t 
     if (blocks > kCompressBlocks) blocks = kCompressBlocks;
     SSG_DISPATCH_DT(dt, {
         using T = typename Store<D>::T;
-        hipLaunchKernelGGL(k_compress<D>, dim3((unsigned)blocks), dim3(256), 0, s, M, K, (const T*)A, lda,
+        hipLaunchKernelGGL((k_compress<D, false>), dim3((unsigned)blocks), dim3(256), 0, s, M, K, (const T*)A, lda,
                            (T*)vals, ldv, meta, ldm, (int)vec);
+    });
+    return hipGetLastError();
+}
+
+hipError_t launch_compress_prefill(int dt, int64_t M, int64_t K, const void* A, int64_t lda, void* pvals,
+                                   void* pmeta, bool vec, hipStream_t s) {
+    const int64_t threads = (M + 255) / 256 * 256 * (K / kChunkElems);
+    if (threads == 0) return hipSuccess;
+    int64_t blocks = blocks_for(threads, 256);
+    if (blocks > kCompressBlocks) blocks = kCompressBlocks;
+    SSG_DISPATCH_DT(dt, {
+        using T = typename Store<D>::T;
+        hipLaunchKernelGGL((k_compress<D, true>), dim3((unsigned)blocks), dim3(256), 0, s, M, K, (const T*)A, lda,
+                           (T*)pvals, 0, (uint8_t*)pmeta, 0, (int)vec);
     });
     return hipGetLastError();
 }

@@ -33,6 +33,17 @@
 // * Tiles are ordered so each XCD (workgroups are dealt round-robin to the 8
 //   XCDs) gets a contiguous range of tiles, walked 4 row tiles at a time, so
 //   the 32 tiles in flight on an XCD share their A and B panels in its L2.
+// * Packed prefill operand (PK): the sparse values and metadata arrive
+//   already in this kernel's LDS image, one contiguous 16 KiB block of values
+//   per 256-row tile and stage (rows 64 bytes apart, chunks swizzled as
+//   above) and one 8 KiB block of metadata per tile and metadata block.  Each
+//   of their loads is then a contiguous 1 KiB / 256 B piece instead of 16 rows
+//   x 64 bytes / 8 rows x 32 bytes, which halves the cache lines the load
+//   path must track for the values and quarters them for the metadata.  The
+//   loads of a stage are also spread over the reads and MFMAs of the next
+//   k-step instead of being issued in one burst after the barrier.
+#include <algorithm>
+
 #include "ssg_device.hpp"
 #include "ssg_kernels.hpp"
 
@@ -91,7 +102,8 @@ struct Lay {
 // c ^ swz_a(r) of the row's 64 bytes: the 8 or 16 lanes that a
 // ds_read_b128 serves together (consecutive rows, one chunk) then land on
 // distinct 16-byte bank groups.
-__device__ __forceinline__ int swz_a(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
+// (the packed prefill layout stores its blocks in this same order)
+__device__ __forceinline__ int swz_a(int r) { return prefill_swz(r); }
 
 template <int DT> __device__ __forceinline__ int swz(int r) {
     if constexpr (dt_bytes(DT) == 1) return 2 * (r & 7);
@@ -178,6 +190,7 @@ struct Ctx {
     const uint8_t* bbase;   // B column n0
     int64_t vbytes, mbytes, bbytes;   // bytes from each base to the end of its buffer
     int64_t vstage, bstage;           // bytes per stage along K
+    int64_t mstep;                    // bytes per metadata block along K
     uint32_t boff[8], aoff[4], moff[8];
 };
 
@@ -257,12 +270,12 @@ __device__ __forceinline__ void issue(const Ctx& x, uint8_t* st, int64_t it, int
 template <int DT>
 __device__ __forceinline__ void issue_meta(const Ctx& x, uint8_t* mt, int64_t g, int wave) {
     using L = Lay<DT>;
-    const __amdgpu_buffer_rsrc_t rm = rsrc(x.mbase + g * L::MBLK_ROWB, x.mbytes - g * L::MBLK_ROWB);
+    const __amdgpu_buffer_rsrc_t rm = rsrc(x.mbase + g * x.mstep, x.mbytes - g * x.mstep);
 #pragma unroll
     for (int j = 0; j < L::M_LOADS; ++j) dma<4>(rm, mt + (wave * L::M_LOADS + j) * 256, x.moff[j]);
 }
 
-template <int DT>
+template <int DT, bool PK>
 __global__ void __launch_bounds__(kThreads) k_spmm_pipe(SpmmArgs a, int tiles_m, int tiles_n) {
     using T = PT<DT>;
     using L = Lay<DT>;
@@ -288,14 +301,28 @@ __global__ void __launch_bounds__(kThreads) k_spmm_pipe(SpmmArgs a, int tiles_m,
     const int64_t m0 = (int64_t)tm * kBM, n0 = (int64_t)tn * kBN;
 
     // per-lane load offsets (constant across stages)
+    const int64_t nit = a.K / T::BK;
+    const int64_t nmb = (nit + T::MB - 1) / T::MB;       // metadata blocks along K
     Ctx x;
-    x.vbase = reinterpret_cast<const uint8_t*>(a.vals) + m0 * a.ldv * T::ES;
-    x.mbase = a.meta + m0 * a.ldm;
+    if constexpr (PK) {
+        // this tile's stage blocks of values and metadata blocks; a stage or
+        // block past K is an empty range and reads zero
+        x.vbase = reinterpret_cast<const uint8_t*>(a.vals) + tm * nit * L::A_BYTES;
+        x.mbase = a.meta + tm * nmb * L::MBLK;
+        x.vbytes = nit * L::A_BYTES;
+        x.mbytes = nmb * L::MBLK;
+        x.vstage = L::A_BYTES;
+        x.mstep = L::MBLK;
+    } else {
+        x.vbase = reinterpret_cast<const uint8_t*>(a.vals) + m0 * a.ldv * T::ES;
+        x.mbase = a.meta + m0 * a.ldm;
+        x.vbytes = ((a.M - 1) * a.ldv + a.K / 2 - m0 * a.ldv) * T::ES;
+        x.mbytes = (a.M - 1) * a.ldm + (a.K + 7) / 8 - m0 * a.ldm;
+        x.vstage = L::A_ROWB;
+        x.mstep = L::MBLK_ROWB;
+    }
     x.bbase = reinterpret_cast<const uint8_t*>(a.B) + n0 * T::ES;
-    x.vbytes = ((a.M - 1) * a.ldv + a.K / 2 - m0 * a.ldv) * T::ES;
-    x.mbytes = (a.M - 1) * a.ldm + (a.K + 7) / 8 - m0 * a.ldm;
     x.bbytes = ((a.K - 1) * a.ldb + a.N - n0) * T::ES;
-    x.vstage = L::A_ROWB;
     x.bstage = (int64_t)T::BK * a.ldb * T::ES;
 #pragma unroll
     for (int j = 0; j < L::B_LOADS; ++j) {
@@ -309,12 +336,14 @@ __global__ void __launch_bounds__(kThreads) k_spmm_pipe(SpmmArgs a, int tiles_m,
         const int row = 16 * (wave * L::A_LOADS + j) + (lane >> 2);
         const int c = (lane & 3) ^ swz_a(row);
         x.aoff[j] = (m0 + row < a.M) ? (uint32_t)(row * a.ldv * T::ES + 16 * c) : kOob;
+        if constexpr (PK) x.aoff[j] = (uint32_t)((wave * L::A_LOADS + j) * 1024 + lane * 16);
     }
 #pragma unroll
     for (int j = 0; j < L::M_LOADS; ++j) {
         // 8 rows x 32 bytes per load: lane -> row 8*ins + lane/8, dword lane%8
         const int row = 8 * (wave * L::M_LOADS + j) + (lane >> 3);
         x.moff[j] = (m0 + row < a.M) ? (uint32_t)(row * a.ldm + 4 * (lane & 7)) : kOob;
+        if constexpr (PK) x.moff[j] = (uint32_t)((wave * L::M_LOADS + j) * 256 + lane * 4);
     }
 
     Acc acc[4][4];
@@ -325,7 +354,6 @@ __global__ void __launch_bounds__(kThreads) k_spmm_pipe(SpmmArgs a, int tiles_m,
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[i][j][e] = S(0);
 
-    const int64_t nit = a.K / T::BK;
     const int q = lane >> 5, rl = lane & 31;
 
     // Operands of one MFMA k-step (sub-step) from an LDS stage: 4 sparse
@@ -403,11 +431,32 @@ __global__ void __launch_bounds__(kThreads) k_spmm_pipe(SpmmArgs a, int tiles_m,
         else wait_vm<L::VM_PER_STAGE>();
         __builtin_amdgcn_s_waitcnt(0xC07F);
         barrier();
-        issue<DT>(x, lds + slot * L::STAGE, it + 3, wave);
+        uint8_t* const dst = lds + slot * L::STAGE;
+        if constexpr (!PK) issue<DT>(x, dst, it + 3, wave);
         if ((it + 1) % T::MB == 0) issue_meta<DT>(x, mlds + (((it + 1) / T::MB + 1) & 1) * L::MBLK, (it + 1) / T::MB + 1, wave);
         slot = slot == kStages - 1 ? 0 : slot + 1;
         const uint8_t* nx = lds + slot * L::STAGE;
-        read_ops(nx, 0, o0);
+        if constexpr (PK) {
+            // the same loads as issue(), each placed after one of the reads
+            // of the next k-step so they leave the wave between its MFMAs
+            const __amdgpu_buffer_rsrc_t rb = rsrc(x.bbase + (it + 3) * x.bstage, x.bbytes - (it + 3) * x.bstage);
+            const __amdgpu_buffer_rsrc_t ra = rsrc(x.vbase + (it + 3) * x.vstage, x.vbytes - (it + 3) * x.vstage);
+            static_assert(L::A_LOADS == 4 && L::B_LOADS == 8, "spread issue assumes 4 + 8 loads per stage");
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int row = 32 * (wm * 4 + i) + rl;
+                o0.av[i] = *reinterpret_cast<const uint4*>(nx + L::B_BYTES + row * L::A_ROWB + ((q ^ swz_a(row)) << 4));
+                dma<16>(ra, dst + L::B_BYTES + (wave * L::A_LOADS + i) * 1024, x.aoff[i]);
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                b_frag<DT>(nx, 0, wn * 128 + 32 * j, lane, o0.b[j]);
+                dma<16>(rb, dst + (wave * L::B_LOADS + 2 * j) * 1024, x.boff[2 * j]);
+                dma<16>(rb, dst + (wave * L::B_LOADS + 2 * j + 1) * 1024, x.boff[2 * j + 1]);
+            }
+        } else {
+            read_ops(nx, 0, o0);
+        }
         read_idx(it + 1, 0, ix0);
         mmas(o1, ix1);
         interleave<16, kOpsReads>();
@@ -444,11 +493,45 @@ bool pipe_supported(const SpmmArgs& a) {
            ((a.K - 1) * a.ldb + a.N) * T::ES < 0x7fffffff && tiles < 0x7fffffff;
 }
 
-template <int DT>
+template <int DT, bool PK = false>
 hipError_t pipe_launch(const SpmmArgs& a, hipStream_t s) {
     const int tm = (int)((a.M + kBM - 1) / kBM), tn = (int)((a.N + kBN - 1) / kBN);
-    hipLaunchKernelGGL(k_spmm_pipe<DT>, dim3((unsigned)(tm * tn)), dim3(kThreads), 0, s, a, tm, tn);
+    hipLaunchKernelGGL((k_spmm_pipe<DT, PK>), dim3((unsigned)(tm * tn)), dim3(kThreads), 0, s, a, tm, tn);
     return hipGetLastError();
+}
+
+// Row-major (vals, meta) -> packed prefill layout.  One thread per 16-byte
+// chunk of pvals (a copy of one 16-byte chunk of a vals row, or zeros past
+// M) and per 4 bytes of pmeta (copied bytewise: meta rows need no
+// alignment; zeros past M and past K / 8).
+__global__ void __launch_bounds__(256) k_pack_prefill(int64_t M, int64_t K, const uint8_t* vals, int64_t ldv_bytes,
+                                                      const uint8_t* meta, int64_t ldm, int64_t stages, int64_t mblocks,
+                                                      int64_t vchunks, int64_t mwords, uint8_t* pvals,
+                                                      uint8_t* pmeta) {
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < vchunks + mwords; i += stride) {
+        if (i < vchunks) {
+            // chunk position p of row r in block (t, s)
+            const int64_t blk = i >> 10, t = blk / stages, st = blk - t * stages;
+            const int r = (int)((i >> 2) & 255), p = (int)(i & 3);
+            const int64_t m = t * 256 + r;
+            uint4 w = make_uint4(0, 0, 0, 0);
+            if (m < M) w = *reinterpret_cast<const uint4*>(vals + m * ldv_bytes + st * 64 + ((p ^ prefill_swz(r)) << 4));
+            *reinterpret_cast<uint4*>(pvals + (i << 4)) = w;
+        } else {
+            const int64_t k = i - vchunks;     // 4-byte word k of pmeta
+            const int64_t blk = k >> 11, t = blk / mblocks, g = blk - t * mblocks;
+            const int r = (int)((k >> 3) & 255), d = (int)(k & 7);
+            const int64_t m = t * 256 + r;
+            uint32_t w = 0;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int64_t j = g * 32 + d * 4 + e;
+                if (m < M && j < K / 8) w |= (uint32_t)meta[m * ldm + j] << (8 * e);
+            }
+            *reinterpret_cast<uint32_t*>(pmeta + (k << 2)) = w;
+        }
+    }
 }
 
 bool pipe_ok(const SpmmArgs& a) {
@@ -463,6 +546,47 @@ bool pipe_ok(const SpmmArgs& a) {
 }
 
 }  // namespace
+
+void prefill_geometry(int dt, int64_t M, int64_t K, int64_t* tiles, int64_t* stages, int64_t* mblocks) {
+    *tiles = (M + kBM - 1) / kBM;
+    *stages = K / 2 * dt_bytes(dt) / 64;
+    *mblocks = (K + 255) / 256;
+}
+
+hipError_t launch_pack_prefill(int dt, int64_t M, int64_t K, const void* vals, int64_t ldv, const uint8_t* meta,
+                               int64_t ldm, void* pvals, void* pmeta, hipStream_t s) {
+    int64_t tiles, stages, mblocks;
+    prefill_geometry(dt, M, K, &tiles, &stages, &mblocks);
+    const int64_t vchunks = tiles * stages * 1024, mwords = tiles * mblocks * 2048;
+    if (vchunks + mwords == 0) return hipSuccess;
+    const int64_t grid = std::min<int64_t>((vchunks + mwords + 255) / 256, 8192);
+    hipLaunchKernelGGL(k_pack_prefill, dim3((unsigned)grid), dim3(256), 0, s, M, K, (const uint8_t*)vals,
+                       ldv * dt_bytes(dt), meta, ldm, stages, mblocks, vchunks, mwords, (uint8_t*)pvals,
+                       (uint8_t*)pmeta);
+    return hipGetLastError();
+}
+
+bool supported_prefill_packed(const SpmmArgs& a) {
+    const int es = dt_bytes(a.dt), bk = es == 1 ? 128 : 64, epc = 16 / es;
+    const uintptr_t v = reinterpret_cast<uintptr_t>(a.vals), m = reinterpret_cast<uintptr_t>(a.meta),
+                    b = reinterpret_cast<uintptr_t>(a.B);
+    const int64_t tiles = ((a.M + kBM - 1) / kBM) * ((a.N + kBN - 1) / kBN);
+    return a.M > 0 && a.N > 0 && a.K > 0 && a.K % bk == 0 && a.N % epc == 0 && v % 16 == 0 && m % 4 == 0 &&
+           b % 16 == 0 && (a.ldb * es) % 16 == 0 &&
+           // one tile's blocks and all of B addressed with 31-bit offsets
+           a.K / 2 * es * 256 < 0x7fffffff && ((a.K - 1) * a.ldb + a.N) * es < 0x7fffffff && tiles < 0x7fffffff;
+}
+
+hipError_t launch_spmm_prefill_packed(const SpmmArgs& a, hipStream_t s) {
+    switch (a.dt) {
+        case DT_F16: return pipe_launch<DT_F16, true>(a, s);
+        case DT_BF16: return pipe_launch<DT_BF16, true>(a, s);
+        case DT_I8: return pipe_launch<DT_I8, true>(a, s);
+        case DT_E4M3: return pipe_launch<DT_E4M3, true>(a, s);
+        case DT_E5M2: return pipe_launch<DT_E5M2, true>(a, s);
+        default: return hipErrorInvalidValue;
+    }
+}
 
 bool supported_large_n(const SpmmArgs& a) { return pipe_ok(a) || supported_large_n_basic(a); }
 

@@ -57,6 +57,31 @@ __device__ __forceinline__ uint32_t select_nibble(uint32_t k0, uint32_t k1, uint
 
 __device__ __forceinline__ bool nibble_valid(uint32_t nib) { return (nib & 3u) < (nib >> 2); }
 
+// ---------------------------------------------------------------------------
+// Packed prefill layout of a 2:4 operand: the large-N kernel's LDS image of
+// each 256-row tile, so that kernel loads it in contiguous pieces.  In bytes
+// it is the same for every element type: a stage is 64 stored-value bytes of
+// every row (64 dense k for fp16/bf16, 128 for 8-bit types) and a metadata
+// block 32 metadata bytes of every row (256 dense k).
+// * pvals: tile t, stage s -> 16 KiB block (t * stages + s); row r of the tile
+//   at r * 64 in it, its 16-byte chunk c at chunk position c ^ prefill_swz(r).
+// * pmeta: tile t, block g -> 8 KiB block (t * mblocks + g); row r's metadata
+//   bytes [32 g, 32 g + 32) at r * 32 in it.
+// Rows past M and metadata bytes past K / 8 hold zeros.
+// ---------------------------------------------------------------------------
+__host__ __device__ __forceinline__ int prefill_swz(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
+
+// Offset in pvals of stored-value byte b of row m.
+__host__ __device__ __forceinline__ int64_t prefill_vals_offset(int64_t m, int64_t b, int64_t stages) {
+    const int r = (int)(m & 255);
+    return (((m >> 8) * stages + (b >> 6)) << 14) + r * 64 + ((((int)(b >> 4) & 3) ^ prefill_swz(r)) << 4) + (b & 15);
+}
+
+// Offset in pmeta of metadata byte j of row m.
+__host__ __device__ __forceinline__ int64_t prefill_meta_offset(int64_t m, int64_t j, int64_t mblocks) {
+    return (((m >> 8) * mblocks + (j >> 5)) << 13) + (m & 255) * 32 + (j & 31);
+}
+
 // Element conversion to fp32 (bit-exact widening).
 __device__ __forceinline__ float f16_bits_to_f32(uint16_t b) {
     _Float16 h;

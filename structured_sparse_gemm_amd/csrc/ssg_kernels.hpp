@@ -71,6 +71,16 @@ bool supported_large_n(const SpmmArgs& a);          // pipelined kernel or the b
 hipError_t launch_spmm_large_n(const SpmmArgs& a, hipStream_t s);
 bool supported_large_n_basic(const SpmmArgs& a);
 hipError_t launch_spmm_large_n_basic(const SpmmArgs& a, hipStream_t s);
+// Packed prefill layout (see ssg_device.hpp): geometry, the compress pass
+// that writes it directly, the pack from (vals, meta), and the large-N
+// product on it (a.vals / a.meta are pvals / pmeta).
+void prefill_geometry(int dt, int64_t M, int64_t K, int64_t* tiles, int64_t* stages, int64_t* mblocks);
+hipError_t launch_compress_prefill(int dt, int64_t M, int64_t K, const void* A, int64_t lda, void* pvals,
+                                   void* pmeta, bool vec, hipStream_t s);
+hipError_t launch_pack_prefill(int dt, int64_t M, int64_t K, const void* vals, int64_t ldv, const uint8_t* meta,
+                               int64_t ldm, void* pvals, void* pmeta, hipStream_t s);
+bool supported_prefill_packed(const SpmmArgs& a);
+hipError_t launch_spmm_prefill_packed(const SpmmArgs& a, hipStream_t s);
 
 // N:M patterns other than 2:4 (spmm_nm.hip): kept values plus a keep mask
 // (bit k%8 of byte k/8 of a row).  (n, m) in {(1,4), (2,4), (2,8), (4,8)}.

@@ -437,6 +437,90 @@ int ssg_spmm_2to4_packed(int ab, int c, int64_t M, int64_t N, int64_t K, const v
     return e == hipSuccess ? SSG_OK : hip_fail(e, "packed spmm launch");
 }
 
+namespace {
+
+// Sizes of the packed prefill layout; fails on K not a multiple of the stage
+// (64 dense k for 16-bit types, 128 for 8-bit) or a tile's blocks beyond the
+// kernel's 31-bit offsets.
+int prefill_sizes(int dt, int64_t M, int64_t K, int64_t* vb, int64_t* mb) {
+    if (!in_dtype(dt)) return fail(SSG_ERR_DTYPE, "element type %d is not SSG_F16, SSG_BF16, SSG_I8, SSG_E4M3 or SSG_E5M2", dt);
+    if (M < 0 || K < 0) return fail(SSG_ERR_SHAPE, "negative size M=%lld K=%lld", (long long)M, (long long)K);
+    const int64_t bk = esize(dt) == 1 ? 128 : 64;
+    if (K % bk != 0) return fail(SSG_ERR_SHAPE, "K=%lld is not a multiple of %lld", (long long)K, (long long)bk);
+    if (K / 2 * esize(dt) * 256 >= 0x7fffffff || M > ((int64_t)1 << 40))
+        return fail(SSG_ERR_SHAPE, "packed prefill layout too large (M=%lld, K=%lld)", (long long)M, (long long)K);
+    int64_t tiles, stages, mblocks;
+    ssg::prefill_geometry(to_dt(dt), M, K, &tiles, &stages, &mblocks);
+    *vb = tiles * stages * 16384;
+    *mb = tiles * mblocks * 8192;
+    return SSG_OK;
+}
+
+int check_prefill_out(int64_t vb, const void* pvals, const void* pmeta) {
+    if (vb > 0 && (!pvals || !pmeta)) return fail(SSG_ERR_NULL, "pvals or pmeta is NULL");
+    if (!al(pvals, 16) || !al(pmeta, 4)) return fail(SSG_ERR_STRIDE, "pvals must be 16-byte and pmeta 4-byte aligned");
+    return SSG_OK;
+}
+
+}  // namespace
+
+int ssg_prefill_packed_sizes(int dt, int64_t M, int64_t K, int64_t* vals_bytes, int64_t* meta_bytes) {
+    if (!vals_bytes || !meta_bytes) return fail(SSG_ERR_NULL, "size pointers are NULL");
+    return prefill_sizes(dt, M, K, vals_bytes, meta_bytes);
+}
+
+int ssg_compress_2to4_prefill(int dt, int64_t M, int64_t K, const void* A, int64_t lda, void* pvals, void* pmeta,
+                              void* stream) {
+    int64_t vb, mb;
+    int rc = prefill_sizes(dt, M, K, &vb, &mb);
+    if (rc) return rc;
+    rc = check_dense(dt, M, K, A, lda);
+    if (rc) return rc;
+    rc = check_prefill_out(vb, pvals, pmeta);
+    if (rc) return rc;
+    if (vb == 0) return SSG_OK;
+    hipError_t e = ssg::launch_compress_prefill(to_dt(dt), M, K, A, lda, pvals, pmeta, rows_aligned16(A, lda, dt),
+                                                (hipStream_t)stream);
+    return e == hipSuccess ? SSG_OK : hip_fail(e, "compress (packed prefill) launch");
+}
+
+int ssg_pack_2to4_prefill(int dt, int64_t M, int64_t K, const void* vals, int64_t ldv, const uint8_t* meta,
+                          int64_t ldm, void* pvals, void* pmeta, void* stream) {
+    int64_t vb, mb;
+    int rc = prefill_sizes(dt, M, K, &vb, &mb);
+    if (rc) return rc;
+    rc = check_compressed(M, K, vals, ldv, meta, ldm, true);
+    if (rc) return rc;
+    rc = check_prefill_out(vb, pvals, pmeta);
+    if (rc) return rc;
+    if (vb == 0) return SSG_OK;
+    if (!rows_aligned16(vals, ldv, dt)) return fail(SSG_ERR_STRIDE, "vals rows must be 16-byte aligned");
+    hipError_t e = ssg::launch_pack_prefill(to_dt(dt), M, K, vals, ldv, meta, ldm, pvals, pmeta, (hipStream_t)stream);
+    return e == hipSuccess ? SSG_OK : hip_fail(e, "pack (prefill) launch");
+}
+
+int ssg_spmm_2to4_prefill(int ab, int c, int64_t M, int64_t N, int64_t K, const void* pvals, const void* pmeta,
+                          const void* B, int64_t ldb, void* C, int64_t ldc, void* stream) {
+    if (!pair_ok(ab, c)) return fail(SSG_ERR_DTYPE, "unsupported (input, output) types (%d, %d)", ab, c);
+    if (N < 0 || N > ((int64_t)1 << 31)) return fail(SSG_ERR_SHAPE, "N=%lld out of range", (long long)N);
+    int64_t vb, mb;
+    int rc = prefill_sizes(ab, M, K, &vb, &mb);
+    if (rc) return rc;
+    if (ldb < N) return fail(SSG_ERR_STRIDE, "ldb=%lld < N=%lld", (long long)ldb, (long long)N);
+    if (ldc < N) return fail(SSG_ERR_STRIDE, "ldc=%lld < N=%lld", (long long)ldc, (long long)N);
+    if (M == 0 || N == 0) return SSG_OK;
+    if (K == 0) return fail(SSG_ERR_SHAPE, "K must be positive");
+    if (!pvals || !pmeta || !B || !C) return fail(SSG_ERR_NULL, "a required pointer is NULL");
+    ssg::SpmmArgs a = make_args(ab, M, N, K, pvals, 0, static_cast<const uint8_t*>(pmeta), 0, B, ldb, C, ldc);
+    if (!ssg::supported_prefill_packed(a))
+        return fail(SSG_ERR_ALGO,
+                    "the packed prefill product needs N a multiple of %d, pvals and B rows 16-byte aligned, pmeta "
+                    "4-byte aligned and B within 31-bit offsets",
+                    (int)(16 / esize(ab)));
+    hipError_t e = ssg::launch_spmm_prefill_packed(a, (hipStream_t)stream);
+    return e == hipSuccess ? SSG_OK : hip_fail(e, "packed prefill spmm launch");
+}
+
 int64_t ssg_nm_vals_cols(int nm_n, int nm_m, int64_t K) {
     return nm_m > 0 && nm_n >= 0 ? K / nm_m * nm_n : 0;
 }

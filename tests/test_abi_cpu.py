@@ -203,3 +203,37 @@ def test_python_binding_names_match_the_abi():
                     "ssg_spmm_2to4_ex", "ssg_spmm_2to4_residual_ex", "ssg_spmm_2to4_residual_delta_ex"):
             continue
         assert hasattr(ssg, name), name
+
+
+def test_prefill_argument_errors(lib):
+    E4M3 = _abi.SSG_E4M3
+    vb, mb = ctypes.c_int64(-1), ctypes.c_int64(-1)
+    # sizes: 256-row tiles x K/2*s bytes of values; 8 KiB per tile and 256 dense k of metadata
+    for dt, M, K, v, m in [(F16, 300, 192, 2 * 256 * 192, 2 * 8192), (I8, 256, 4096, 256 * 2048, 16 * 8192),
+                           (E4M3, 1, 384, 256 * 192, 2 * 8192), (BF16, 0, 64, 0, 0)]:
+        assert lib.ssg_prefill_packed_sizes(dt, M, K, ctypes.byref(vb), ctypes.byref(mb)) == 0
+        assert (vb.value, mb.value) == (v, m)
+    # K not a multiple of the stage (64 dense k for 16-bit, 128 for 8-bit)
+    assert lib.ssg_prefill_packed_sizes(F16, 8, 96, ctypes.byref(vb), ctypes.byref(mb)) == _abi.SSG_ERR_SHAPE
+    assert lib.ssg_prefill_packed_sizes(I8, 8, 64, ctypes.byref(vb), ctypes.byref(mb)) == _abi.SSG_ERR_SHAPE
+    assert lib.ssg_prefill_packed_sizes(F32, 8, 64, ctypes.byref(vb), ctypes.byref(mb)) == _abi.SSG_ERR_DTYPE
+    assert lib.ssg_prefill_packed_sizes(F16, 8, 64, None, None) == _abi.SSG_ERR_NULL
+    c = lib.ssg_compress_2to4_prefill
+    assert c(F16, 8, 96, FAKE, 96, FAKE, FAKE, None) == _abi.SSG_ERR_SHAPE
+    assert c(F16, 8, 64, FAKE, 63, FAKE, FAKE, None) == _abi.SSG_ERR_STRIDE
+    assert c(F16, 8, 64, FAKE, 64, None, FAKE, None) == _abi.SSG_ERR_NULL
+    assert c(F16, 8, 64, FAKE, 64, ctypes.c_void_p(0x1008), FAKE, None) == _abi.SSG_ERR_STRIDE
+    assert c(F16, 0, 64, FAKE, 64, None, None, None) == 0          # nothing to write
+    p = lib.ssg_pack_2to4_prefill
+    assert p(I8, 8, 128, FAKE, 63, FAKE, 16, FAKE, FAKE, None) == _abi.SSG_ERR_STRIDE
+    assert p(I8, 8, 128, FAKE, 64, FAKE, 15, FAKE, FAKE, None) == _abi.SSG_ERR_STRIDE
+    assert p(I8, 8, 128, ctypes.c_void_p(0x1004), 64, FAKE, 16, FAKE, FAKE, None) == _abi.SSG_ERR_STRIDE
+    s = lib.ssg_spmm_2to4_prefill
+    assert s(F16, I32, 8, 16, 64, FAKE, FAKE, FAKE, 16, FAKE, 16, None) == _abi.SSG_ERR_DTYPE
+    assert s(F16, F32, 8, 16, 96, FAKE, FAKE, FAKE, 16, FAKE, 16, None) == _abi.SSG_ERR_SHAPE
+    assert s(F16, F32, 8, 16, 64, FAKE, FAKE, FAKE, 15, FAKE, 16, None) == _abi.SSG_ERR_STRIDE
+    assert s(F16, F32, 8, 16, 64, FAKE, FAKE, FAKE, 16, FAKE, 15, None) == _abi.SSG_ERR_STRIDE
+    assert s(F16, F32, 8, 16, 64, None, FAKE, FAKE, 16, FAKE, 16, None) == _abi.SSG_ERR_NULL
+    assert s(I8, I32, 8, 8, 128, FAKE, FAKE, FAKE, 8, FAKE, 8, None) == _abi.SSG_ERR_ALGO   # N % 16
+    assert s(F16, F32, 8, 12, 64, FAKE, FAKE, FAKE, 12, FAKE, 12, None) == _abi.SSG_ERR_ALGO   # N % 8
+    assert s(F16, F32, 0, 16, 64, None, None, None, 16, None, 16, None) == 0

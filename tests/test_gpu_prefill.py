@@ -1,0 +1,149 @@
+"""The packed prefill layout (the large-N kernel's LDS image of each 256-row
+tile) and the product on it, through the C ABI.
+
+* layout: bit-exact with the layout written out below from its definition
+  in include/ssgemm.h, both from the pack of (vals, meta) and from the
+  compressor that writes it directly;
+* product: against the oracle (int8 exact, floats within the stated
+  tolerance), and bit for bit equal to the large-N kernel on the row-major
+  operand, which stages the same LDS bytes and runs the same MFMA sequence.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import structured_sparse_gemm_amd as ssg
+import workloads as W
+from tests import _util as U
+from tests.test_gpu_parity import check_product, dev_or_empty, sample_entries, to_dev
+
+pytestmark = pytest.mark.gpu
+
+DTS = ["f16", "bf16", "i8", "e4m3", "e5m2"]
+
+
+@pytest.fixture(scope="module", autouse=True)
+def device():
+    if not torch.cuda.is_available():
+        pytest.skip("no ROCm device")
+    torch.cuda.init()
+    return torch.device("cuda:0")
+
+
+def swz(r):
+    return ((r >> 1) ^ (r >> 3)) & 3
+
+
+def expected_prefill(dt, vals_bits, meta, M, K):
+    """The packed prefill layout written out from its definition."""
+    es = 2 if dt in ("f16", "bf16") else 1
+    stages, mblocks, tiles = K * es // 128, (K + 255) // 256, (M + 255) // 256
+    vb = np.zeros((tiles * 256, K // 2 * es), np.uint8)
+    vb[:M] = np.ascontiguousarray(vals_bits).view(np.uint8).reshape(M, -1)
+    mb = np.zeros((tiles * 256, mblocks * 32), np.uint8)
+    mb[:M, :K // 8] = meta[:, :K // 8]
+    src = vb.reshape(tiles, 256, stages, 4, 16)
+    pv = np.zeros((tiles, stages, 256, 4, 16), np.uint8)
+    for r in range(256):
+        for c in range(4):
+            pv[:, :, r, c ^ swz(r)] = src[:, r, :, c]
+    pm = mb.reshape(tiles, 256, mblocks, 32).transpose(0, 2, 1, 3)
+    return pv.reshape(-1), np.ascontiguousarray(pm).reshape(-1)
+
+
+def shapes_for(dt):
+    # (M, K): one row; ragged tiles; K whose last metadata block is partial
+    if dt in ("f16", "bf16"):
+        return [(1, 64), (300, 192), (256, 512), (513, 1024)]
+    return [(1, 128), (300, 384), (256, 512), (513, 1152)]
+
+
+@pytest.mark.parametrize("dt", DTS)
+@pytest.mark.parametrize("which", [0, 1, 2, 3])
+def test_prefill_layout(dt, which):
+    M, K = shapes_for(dt)[which]
+    a = U.random_matrix(dt, M, K, "normal", seed=M + 5 * K)
+    vals, meta = oracle.compress(dt, a)
+    ev, em = expected_prefill(dt, vals, meta, M, K)
+    vb, mb = ssg.ssg_prefill_packed_sizes(W.TORCH_DTYPE[dt], M, K)
+    assert (vb, mb) == (ev.size, em.size)
+    pv, pm = ssg.pack_prefill(to_dev(vals, dt), dev_or_empty(meta), K)
+    assert np.array_equal(pv.cpu().numpy(), ev), "pack: values"
+    assert np.array_equal(pm.cpu().numpy(), em), "pack: metadata"
+    # the compressor writing the layout directly; the buffers start as 0xA5
+    # so that a byte it fails to write shows
+    pv2 = torch.full((vb,), 0xA5, dtype=torch.uint8, device="cuda")
+    pm2 = torch.full((mb,), 0xA5, dtype=torch.uint8, device="cuda")
+    ssg.ssg_compress_2to4_prefill(to_dev(a, dt), pv2, pm2)
+    assert np.array_equal(pv2.cpu().numpy(), ev), "compress: values"
+    assert np.array_equal(pm2.cpu().numpy(), em), "compress: metadata"
+
+
+PRODUCT_SHAPES = [(64, 128, 16), (300, 384, 272), (256, 512, 256), (520, 1152, 528)]
+
+
+@pytest.mark.parametrize("dt", DTS)
+@pytest.mark.parametrize("shape", PRODUCT_SHAPES)
+def test_spmm_prefill_matches_oracle(dt, shape):
+    M, K, N = shape
+    a = U.random_matrix(dt, M, K, "normal", seed=M + 7 * K)
+    b = U.random_matrix(dt, K, N, "normal", seed=N + 11)
+    vals, meta = oracle.compress(dt, a)
+    pv, pm = ssg.compress_prefill(to_dev(a, dt))
+    B = to_dev(b, dt)
+    C = ssg.spmm_prefill(pv, pm, M, B)
+    cref, sref = oracle.spmm(dt, vals, meta, b, K)
+    check_product(dt, C.cpu().numpy(), cref, sref, "prefill %s %s" % (dt, shape))
+    # same LDS bytes, same MFMA order as the row-major large-N kernel
+    C_rm = ssg.spmm(to_dev(vals, dt), dev_or_empty(meta), B, algo=ssg.SSG_ALGO_LARGE_N)
+    assert torch.equal(C.view(torch.int32), C_rm.view(torch.int32))
+
+
+def test_spmm_prefill_exact_small_integers():
+    # fp16 values that are small integers: every product and partial sum is
+    # exact in fp32, so the product must equal the oracle's exactly
+    M, K, N = 300, 640, 264
+    rng = np.random.default_rng(3)
+    a = rng.integers(-3, 4, size=(M, K)).astype(np.float16).view(np.uint16)
+    b = rng.integers(-3, 4, size=(K, N)).astype(np.float16).view(np.uint16)
+    vals, meta = oracle.compress("f16", a)
+    pv, pm = ssg.compress_prefill(to_dev(a, "f16"))
+    C = ssg.spmm_prefill(pv, pm, M, to_dev(b, "f16")).cpu().numpy().astype(np.float64)
+    cref, _ = oracle.spmm("f16", vals, meta, b, K)
+    assert np.array_equal(C, cref)
+
+
+def test_spmm_prefill_argument_errors():
+    a = U.random_matrix("i8", 64, 128, "normal", 1)
+    pv, pm = ssg.compress_prefill(to_dev(a, "i8"))
+    b = to_dev(U.random_matrix("i8", 128, 8, "normal", 2), "i8")
+    with pytest.raises(ssg.SsgError) as e:      # N not a multiple of 16 for 8-bit inputs
+        ssg.spmm_prefill(pv, pm, 64, b)
+    assert e.value.status == 8
+    with pytest.raises(ssg.SsgError) as e:      # K not a multiple of the stage
+        ssg.compress_prefill(to_dev(U.random_matrix("i8", 64, 64, "normal", 3), "i8"))
+    assert e.value.status == 2
+
+
+@pytest.mark.parametrize("key", ["c2", "c4"])
+def test_full_size_prefill(key):
+    w = W.WORKLOADS[key]
+    print("full-size packed prefill %s: %s" % (key, w.title), flush=True)
+    a_cpu, b_cpu = W.gen_a(w), W.gen_b(w)
+    a, b = W.bits(a_cpu), W.bits(b_cpu)
+    A, B = a_cpu.cuda(), b_cpu.cuda()
+    pv, pm = ssg.compress_prefill(A)
+    vals, meta = ssg.compress(A)
+    del A
+    pv2, pm2 = ssg.pack_prefill(vals, meta, w.K)
+    assert torch.equal(pv, pv2) and torch.equal(pm, pm2)
+    del pv2, pm2
+    C = ssg.spmm_prefill(pv, pm, w.M, B)
+    C_rm = ssg.spmm(vals, meta, B, algo=ssg.SSG_ALGO_LARGE_N)
+    assert torch.equal(C.view(torch.int32), C_rm.view(torch.int32))
+    del C_rm
+    r = oracle.compress(w.dtype, a)
+    ms, ns = sample_entries(w.M, w.N, 3000, seed=w.index + 70)
+    cref, sref = oracle.spmm_entries(w.dtype, r[0], r[1], b, w.K, ms, ns)
+    check_product(w.dtype, C.cpu().numpy()[ms, ns], cref, sref, key + " packed prefill")
