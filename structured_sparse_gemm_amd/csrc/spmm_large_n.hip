@@ -464,7 +464,9 @@ __global__ void __launch_bounds__(kThreads) k_spmm_pipe(SpmmArgs a, int tiles_m,
     // the zero-filling loads of the stages past K land before the LDS is released
     wait_vm<0>();
 
-    // epilogue: D element e of lane l is row 8*(e/4) + 4*(l/32) + e%4, column l%32
+    // epilogue: D element e of lane l is row 8*(e/4) + 4*(l/32) + e%4, column l%32.
+    // C is written once and not read back here: non-temporal stores keep it
+    // from displacing the operand panels the other tiles still stream.
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
 #pragma unroll
@@ -473,7 +475,8 @@ __global__ void __launch_bounds__(kThreads) k_spmm_pipe(SpmmArgs a, int tiles_m,
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
                 const int64_t row = m0 + wm * 128 + 32 * i + 8 * (e >> 2) + 4 * q + (e & 3);
-                if (row < a.M && col < a.N) reinterpret_cast<S*>(a.C)[row * a.ldc + col] = acc[i][j][e];
+                if (row < a.M && col < a.N)
+                    __builtin_nontemporal_store((S)acc[i][j][e], reinterpret_cast<S*>(a.C) + row * a.ldc + col);
             }
         }
     }
