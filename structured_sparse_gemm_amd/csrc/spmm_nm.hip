@@ -281,14 +281,19 @@ template <int VB> struct ValReg { using T = i32x4; };
 template <> struct ValReg<8> { using T = i32x2; };
 template <> struct ValReg<4> { using T = int; };
 
-template <int VB>
+// NT: a non-temporal load, for the packed layout, whose lines are each read
+// once and whole (in the row-major layout a line's halves are read in
+// different super-steps, and the second half wants the line still in L2).
+#define SSG_NM_LOAD(OP, POL) asm volatile("buffer_load_" OP " %0, %1, %2, 0 offen" POL : "=v"(r) : "v"(off), "s"(rs) : "memory")
+template <int VB, bool NT>
 __device__ __forceinline__ void load_vals(typename ValReg<VB>::T& r, uint32_t off, __amdgpu_buffer_rsrc_t rs) {
-    if constexpr (VB == 16)
-        asm volatile("buffer_load_dwordx4 %0, %1, %2, 0 offen" : "=v"(r) : "v"(off), "s"(rs) : "memory");
-    else if constexpr (VB == 8)
-        asm volatile("buffer_load_dwordx2 %0, %1, %2, 0 offen" : "=v"(r) : "v"(off), "s"(rs) : "memory");
-    else
-        asm volatile("buffer_load_dword %0, %1, %2, 0 offen" : "=v"(r) : "v"(off), "s"(rs) : "memory");
+    if constexpr (VB == 16) {
+        if constexpr (NT) SSG_NM_LOAD("dwordx4", " nt"); else SSG_NM_LOAD("dwordx4", "");
+    } else if constexpr (VB == 8) {
+        if constexpr (NT) SSG_NM_LOAD("dwordx2", " nt"); else SSG_NM_LOAD("dwordx2", "");
+    } else {
+        if constexpr (NT) SSG_NM_LOAD("dword", " nt"); else SSG_NM_LOAD("dword", "");
+    }
 }
 
 typedef _Float16 nm_h2 __attribute__((ext_vector_type(2)));
@@ -401,15 +406,17 @@ __device__ __forceinline__ void nm_load_b(const uint8_t* slot, int lane, int f, 
 template <int MB> struct MaskReg { using T = int; };
 template <> struct MaskReg<8> { using T = i32x2; };
 
-template <int MB>
+template <int MB, bool NT>
 __device__ __forceinline__ void load_mask(typename MaskReg<MB>::T& r, uint32_t off, __amdgpu_buffer_rsrc_t rs) {
-    if constexpr (MB == 8)
-        asm volatile("buffer_load_dwordx2 %0, %1, %2, 0 offen" : "=v"(r) : "v"(off), "s"(rs) : "memory");
-    else if constexpr (MB == 4)
-        asm volatile("buffer_load_dword %0, %1, %2, 0 offen" : "=v"(r) : "v"(off), "s"(rs) : "memory");
-    else
-        asm volatile("buffer_load_ushort %0, %1, %2, 0 offen" : "=v"(r) : "v"(off), "s"(rs) : "memory");
+    if constexpr (MB == 8) {
+        if constexpr (NT) SSG_NM_LOAD("dwordx2", " nt"); else SSG_NM_LOAD("dwordx2", "");
+    } else if constexpr (MB == 4) {
+        if constexpr (NT) SSG_NM_LOAD("dword", " nt"); else SSG_NM_LOAD("dword", "");
+    } else {
+        if constexpr (NT) SSG_NM_LOAD("ushort", " nt"); else SSG_NM_LOAD("ushort", "");
+    }
 }
+#undef SSG_NM_LOAD
 
 template <int MB>
 __device__ __forceinline__ uint64_t mask_bits(const typename MaskReg<MB>::T& r) {
@@ -485,8 +492,8 @@ __global__ void __launch_bounds__(kNmWaves * 64) k_spmm_nm(SpmmArgs a, int64_t t
             const bool live = in && t < nt;
             const uint32_t o = live ? voff[t] + (uint32_t)(g * VSTEP) : kOob;
             const uint32_t om = live ? moff[t] + (uint32_t)(g * MSTEP) : kOob;
-            load_vals<S::VB>(av[u][t], o, rv);
-            load_mask<S::MB>(mv[u][t], om, rm);
+            load_vals<S::VB, PK>(av[u][t], o, rv);
+            load_mask<S::MB, PK>(mv[u][t], om, rm);
         }
     };
 

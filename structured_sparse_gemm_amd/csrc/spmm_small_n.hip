@@ -920,11 +920,13 @@ __global__ void __launch_bounds__(kWaves * 64) k_spmm_packed(SpmmArgs a, const u
         for (int t = 0; t < TM; ++t) {
             const uint32_t o = in ? voff[t] + (uint32_t)(g * 1024) : kOob;
             const uint32_t om = in ? moff[t] + (uint32_t)(g * 64 * IDXB) : kOob;
-            asm volatile("buffer_load_dwordx4 %0, %1, %2, 0 offen" : "=v"(av[u][t]) : "v"(o), "s"(rv) : "memory");
+            // non-temporal: every line of the packed blocks is read once, whole,
+            // so nothing is lost by not keeping it, and B stays in L2
+            asm volatile("buffer_load_dwordx4 %0, %1, %2, 0 offen nt" : "=v"(av[u][t]) : "v"(o), "s"(rv) : "memory");
             if constexpr (IDXB == 4)
-                asm volatile("buffer_load_dword %0, %1, %2, 0 offen" : "=v"(mv[u][t]) : "v"(om), "s"(rm) : "memory");
+                asm volatile("buffer_load_dword %0, %1, %2, 0 offen nt" : "=v"(mv[u][t]) : "v"(om), "s"(rm) : "memory");
             else
-                asm volatile("buffer_load_ushort %0, %1, %2, 0 offen" : "=v"(mv[u][t]) : "v"(om), "s"(rm) : "memory");
+                asm volatile("buffer_load_ushort %0, %1, %2, 0 offen nt" : "=v"(mv[u][t]) : "v"(om), "s"(rm) : "memory");
         }
     };
 
