@@ -195,7 +195,7 @@ def bench_workload(key: str, iters: int, read_GBps: float, delta: bool = False, 
     if delta:
         ops = ops[:2] + ssg.delta_encode(ops[2], ops[3], ops[4], w.K)
     if packed and nm is None:
-        ops = ssg.pack_decode(ops[0], ops[1], w.K)
+        ops = ssg.pack_decode(ops[0], ops[1], w.K) + tuple(ops[2:])
     wbytes = sum(t.numel() * t.element_size() for t in ops)
     copies = 1
     if w.klass == "small_n":
@@ -211,6 +211,10 @@ def bench_workload(key: str, iters: int, read_GBps: float, delta: bool = False, 
             ssg.ssg_spmm_nm_packed(o[0], o[1], nm[0], nm[1], w.M, b, out, i4=w.dtype == "i4")
         elif nm is not None:
             ssg.ssg_spmm_nm(o[0], o[1], nm[0], nm[1], w.K, b, out)
+        elif packed and delta:
+            ssg.ssg_spmm_2to4_packed_residual_delta(o[0], o[1], w.M, o[2], o[3], o[4], b, out)
+        elif packed and w.residual:
+            ssg.ssg_spmm_2to4_packed_residual(o[0], o[1], w.M, o[2], o[3], o[4], b, out)
         elif packed:
             ssg.ssg_spmm_2to4_packed(o[0], o[1], w.M, b, out)
         elif prefill:
@@ -552,6 +556,11 @@ def main() -> int:
             if W.WORKLOADS[k].residual:
                 print("bench: workload %s, delta-coded residual ..." % k, file=sys.stderr, flush=True)
                 table[k + "_delta"] = bench_workload(k, it, rbw, delta=True, dense_cmp=False)
+                print("bench: workload %s, packed decode layout ..." % k, file=sys.stderr, flush=True)
+                table[k + "_packed"] = bench_workload(k, it, rbw, dense_cmp=False, packed=True)
+                print("bench: workload %s, packed decode layout, delta-coded residual ..." % k, file=sys.stderr,
+                      flush=True)
+                table[k + "_delta_packed"] = bench_workload(k, it, rbw, delta=True, dense_cmp=False, packed=True)
             elif W.WORKLOADS[k].klass == "small_n" and W.WORKLOADS[k].N == 16:
                 print("bench: workload %s, packed decode layout ..." % k, file=sys.stderr, flush=True)
                 table[k + "_packed"] = bench_workload(k, it, rbw, dense_cmp=False, packed=True)

@@ -251,6 +251,21 @@ int ssg_pack_2to4_decode(int dt, int64_t M, int64_t K, const void* vals, int64_t
 int ssg_spmm_2to4_packed(int ab, int c, int64_t M, int64_t N, int64_t K, const void* pvals, const void* pmeta,
                          const void* B, int64_t ldb, void* C, int64_t ldc, void* stream);
 
+/* The same product plus a residual layer ("How sparse LLM weights cut GPU
+ * inference cost without quantization", section "How the three-layer
+ * format makes moderate sparsity fast"): C = expand(packed) x B + R x B,
+ * with R as in ssg_spmm_2to4_residual (CSR, int32 columns) or
+ * ssg_spmm_2to4_residual_delta (one-byte gaps).  The residual arrays
+ * (col or dcol, and the values) must be aligned to 4 entries and under 2^31
+ * bytes (SSG_ERR_ALGO otherwise); row pointers are trusted as there. */
+int ssg_spmm_2to4_packed_residual(int ab, int c, int64_t M, int64_t N, int64_t K, const void* pvals,
+                                  const void* pmeta, const int32_t* row_ptr, const int32_t* col, const void* rvals,
+                                  int64_t nnz_r, const void* B, int64_t ldb, void* C, int64_t ldc, void* stream);
+int ssg_spmm_2to4_packed_residual_delta(int ab, int c, int64_t M, int64_t N, int64_t K, const void* pvals,
+                                        const void* pmeta, const int32_t* drow_ptr, const uint8_t* dcol,
+                                        const void* dvals, int64_t nnz_d, const void* B, int64_t ldb, void* C,
+                                        int64_t ldc, void* stream);
+
 /* Packed prefill layout: the 2:4 operand rearranged, offline like the
  * compression, into the order the large-N (compute-bound) kernel stages it
  * in LDS, so that every load of stored values or metadata is one contiguous

@@ -29,6 +29,8 @@ __all__ = [
     "ssg_spmm_2to4_residual", "ssg_spmm_2to4_residual_delta", "ssg_spmm_select_algo", "ssg_spmm_csr",
     "ssg_spmm_csr_delta", "spmm_csr", "spmm_csr_delta", "ssg_packed_sizes", "ssg_pack_2to4_decode",
     "ssg_spmm_2to4_packed", "pack_decode", "spmm_packed",
+    "ssg_spmm_2to4_packed_residual", "ssg_spmm_2to4_packed_residual_delta", "spmm_packed_residual",
+    "spmm_packed_residual_delta",
     "ssg_prefill_packed_sizes", "ssg_compress_2to4_prefill", "ssg_pack_2to4_prefill", "ssg_spmm_2to4_prefill",
     "compress_prefill", "pack_prefill", "spmm_prefill",
     "ssg_compress_nm", "ssg_decompress_nm", "ssg_spmm_nm", "compress_nm", "decompress_nm", "spmm_nm",
@@ -276,6 +278,27 @@ def ssg_spmm_2to4_prefill(pvals, pmeta, M: int, B, C, stream=None) -> None:
            "ssg_spmm_2to4_prefill")
 
 
+def ssg_spmm_2to4_packed_residual(pvals, pmeta, M: int, row_ptr, col, rvals, B, C, stream=None) -> None:
+    ab = _dtype(B)
+    N, K = B.shape[1], B.shape[0]
+    nnz = int(col.numel()) if col is not None else 0
+    _check(_lib().ssg_spmm_2to4_packed_residual(ab, _OUT[ab][0], M, N, K, _ptr(pvals, "pvals"), _ptr(pmeta, "pmeta"),
+                                                _ptr(row_ptr, "row_ptr"), _ptr(col, "col"), _ptr(rvals, "rvals"), nnz,
+                                                _ptr(B, "B"), _ld(B, "B"), _ptr(C, "C"), _ld(C, "C"),
+                                                _stream(C, stream)), "ssg_spmm_2to4_packed_residual")
+
+
+def ssg_spmm_2to4_packed_residual_delta(pvals, pmeta, M: int, drow_ptr, dcol, dvals, B, C, stream=None) -> None:
+    ab = _dtype(B)
+    N, K = B.shape[1], B.shape[0]
+    nnz = int(dcol.numel()) if dcol is not None else 0
+    _check(_lib().ssg_spmm_2to4_packed_residual_delta(ab, _OUT[ab][0], M, N, K, _ptr(pvals, "pvals"),
+                                                      _ptr(pmeta, "pmeta"), _ptr(drow_ptr, "drow_ptr"),
+                                                      _ptr(dcol, "dcol"), _ptr(dvals, "dvals"), nnz, _ptr(B, "B"),
+                                                      _ld(B, "B"), _ptr(C, "C"), _ld(C, "C"), _stream(C, stream)),
+           "ssg_spmm_2to4_packed_residual_delta")
+
+
 def ssg_spmm_select_algo(vals, meta, B, C) -> int:
     return int(_lib().ssg_spmm_select_algo(_dtype(vals), vals.shape[0], B.shape[1], B.shape[0], _ptr(vals, "vals"),
                                            _ld(vals, "vals"), _ptr(meta, "meta"), _ld(meta, "meta"), _ptr(B, "B"),
@@ -519,6 +542,24 @@ def spmm_prefill(pvals: torch.Tensor, pmeta: torch.Tensor, M: int, B: torch.Tens
     ab = _dtype(B)
     C = torch.empty((M, B.shape[1]), dtype=_OUT[ab][1], device=B.device) if out is None else out
     ssg_spmm_2to4_prefill(pvals, pmeta, M, B, C)
+    return C
+
+
+def spmm_packed_residual(pvals, pmeta, M: int, row_ptr, col, rvals, B: torch.Tensor,
+                         out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """C = expand(packed) @ B + residual(CSR) @ B, B [K, 16]."""
+    ab = _dtype(B)
+    C = torch.empty((M, B.shape[1]), dtype=_OUT[ab][1], device=B.device) if out is None else out
+    ssg_spmm_2to4_packed_residual(pvals, pmeta, M, row_ptr, col, rvals, B, C)
+    return C
+
+
+def spmm_packed_residual_delta(pvals, pmeta, M: int, drow_ptr, dcol, dvals, B: torch.Tensor,
+                               out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """C = expand(packed) @ B + residual(delta-coded) @ B, B [K, 16]."""
+    ab = _dtype(B)
+    C = torch.empty((M, B.shape[1]), dtype=_OUT[ab][1], device=B.device) if out is None else out
+    ssg_spmm_2to4_packed_residual_delta(pvals, pmeta, M, drow_ptr, dcol, dvals, B, C)
     return C
 
 

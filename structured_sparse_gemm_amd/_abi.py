@@ -51,6 +51,10 @@ SIGNATURES = {
     "ssg_packed_sizes": (_i, [_i, _i64, _i64, ctypes.POINTER(_i64), ctypes.POINTER(_i64)]),
     "ssg_pack_2to4_decode": (_i, [_i, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _vp, _vp]),
     "ssg_spmm_2to4_packed": (_i, [_i, _i, _i64, _i64, _i64, _vp, _vp, _vp, _i64, _vp, _i64, _vp]),
+    "ssg_spmm_2to4_packed_residual": (_i, [_i, _i, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _i64, _vp, _i64, _vp,
+                                           _i64, _vp]),
+    "ssg_spmm_2to4_packed_residual_delta": (_i, [_i, _i, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _i64, _vp, _i64,
+                                                 _vp, _i64, _vp]),
     "ssg_prefill_packed_sizes": (_i, [_i, _i64, _i64, ctypes.POINTER(_i64), ctypes.POINTER(_i64)]),
     "ssg_compress_2to4_prefill": (_i, [_i, _i64, _i64, _vp, _i64, _vp, _vp, _vp]),
     "ssg_pack_2to4_prefill": (_i, [_i, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _vp, _vp]),

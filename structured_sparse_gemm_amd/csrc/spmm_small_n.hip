@@ -877,7 +877,11 @@ __global__ void __launch_bounds__(256) k_pack(int64_t M, int64_t K, const uint8_
 // kernel's scheme with the index words loaded per k-step next to the
 // fragments, so nothing is staged before the loop.  Workgroup b takes the
 // tiles [b*T/G, (b+1)*T/G) (at most TM); tiles past its range read zero.
-template <int DT, int TM, int P>
+// With a residual (RES) the workgroup's rows get the ring kernel's residual
+// epilogue: the 2:4 sums go to LDS, the first residual passes are loaded
+// while the weight stream drains, then B is staged in chunks over the LDS
+// below the row sums and the residual rows are consumed chunk by chunk.
+template <int DT, int TM, int P, bool RES, bool DELTA>
 __global__ void __launch_bounds__(kWaves * 64) k_spmm_packed(SpmmArgs a, const uint8_t* pvals, const uint8_t* pmeta,
                                                              int64_t tiles) {
     constexpr int W = kWaves;
@@ -935,6 +939,15 @@ __global__ void __launch_bounds__(kWaves * 64) k_spmm_packed(SpmmArgs a, const u
     for (int t = 0; t < TM; ++t) acc[t] = Acc{0, 0, 0, 0};
 #pragma unroll
     for (int u = 0; u < P; ++u) issue(wave + (int64_t)W * u, u);
+    // residual rows of the workgroup (rows [r0, r0 + nrows)): their bounds
+    // are read now, behind the first k-steps' loads
+    const int64_t r0 = 16 * t0;
+    const int nrows = (int)min<int64_t>(16 * nt, a.M - r0);
+    constexpr int kResRows = (16 * TM + W - 1) / W;
+    constexpr int kResEPL = kResRows > 4 ? 2 : 4;
+    constexpr int kResNP = kResRows > 4 ? 1 : 2;
+    ResPass<DT, kResRows, kResEPL, kResNP, DELTA> rp;
+    if constexpr (RES) residual_begin(rp, a, nullptr, r0, nrows, true, wave, W);
     const int nw = ksteps > wave ? (int)((ksteps - wave + W - 1) / W) : 0;
     for (int i0 = 0; i0 < nw; i0 += P) {
 #pragma unroll
@@ -961,6 +974,11 @@ __global__ void __launch_bounds__(kWaves * 64) k_spmm_packed(SpmmArgs a, const u
             }
         }
     }
+    // residual: the first passes go out while the weight stream drains
+    const __amdgpu_buffer_rsrc_t rcol = DELTA ? rsrc_aligned<4>(a.dcol, a.nnz_r)
+                                              : rsrc_aligned<16>(a.col, a.nnz_r * 4);
+    const __amdgpu_buffer_rsrc_t rval = rsrc_aligned<4 * T::ES>(a.rvals, a.nnz_r * T::ES);
+    if constexpr (RES) residual_load(rp, rcol, rval, lane);
     // the loads past the wave's last k-step land before the LDS is reused,
     // and before their registers are (an asm load's output counts as
     // written when issued, so the ring stays in use until the wait)
@@ -973,6 +991,7 @@ __global__ void __launch_bounds__(kWaves * 64) k_spmm_packed(SpmmArgs a, const u
 
     // fixed-order reduction of the waves' partial tiles
     Acc* red = reinterpret_cast<Acc*>(lds);
+    S* res = reinterpret_cast<S*>(lds + kRingResOff);   // RES: the rows' sums [64][16]
 #pragma unroll
     for (int t = 0; t < TM; ++t) red[(wave * kTMax + t) * 64 + lane] = acc[t];
     lds_barrier();
@@ -981,20 +1000,59 @@ __global__ void __launch_bounds__(kWaves * 64) k_spmm_packed(SpmmArgs a, const u
         S sum = S(0);
 #pragma unroll
         for (int w = 0; w < W; ++w) sum += reinterpret_cast<const S*>(red)[((w * kTMax + t) * 64 + ln) * 4 + r];
-        const int64_t row = 16 * (t0 + t) + 4 * (ln >> 4) + r;
+        const int lrow = 16 * t + 4 * (ln >> 4) + r;
+        const int64_t row = r0 + lrow;
         const int col = ln & 15;
-        if (row < a.M && col < a.N) reinterpret_cast<S*>(a.C)[row * a.ldc + col] = sum;
+        if constexpr (RES) res[lrow * 16 + col] = sum;
+        else if (row < a.M && col < a.N) reinterpret_cast<S*>(a.C)[row * a.ldc + col] = sum;
+    }
+    if constexpr (RES) {
+        // B in chunks over the LDS below the row sums
+        constexpr int64_t kChunkRows = kRingResOff / (16 * T::ES);
+        for (int64_t k0 = 0; k0 < a.K; k0 += kChunkRows) {
+            const int rows = (int)min<int64_t>(kChunkRows, a.K - k0);
+            lds_barrier();                                  // the previous chunk (or the partial tiles) consumed
+            dma_b<DT>(a, lds_addr, k0, rows, wave);
+            wait_vm<0>();                                   // this wave's B rows and residual passes
+            lds_barrier();
+            while (residual_consume(rp, lds, res, k0, k0 + rows, wave, W, lane)) residual_load(rp, rcol, rval, lane);
+            if (k0 + rows < a.K) {
+                residual_reopen(rp);
+                residual_load(rp, rcol, rval, lane);
+            }
+        }
+        lds_barrier();
+        for (int i = threadIdx.x; i < nrows * 16; i += blockDim.x) {
+            const int row = i >> 4, col = i & 15;
+            if (col < a.N) reinterpret_cast<S*>(a.C)[(r0 + row) * a.ldc + col] = res[i];
+        }
     }
 }
 
 template <int TM> constexpr int kPackedP = TM == 1 ? 8 : TM == 2 ? 8 : TM == 3 ? 7 : 6;
 
+// with a residual: the shallower ring (registers for the epilogue) and the
+// whole LDS (B chunks below the row sums)
+template <int TM> constexpr int kPackedResP = TM == 4 ? 4 : 6;
+
 template <int DT, int TM>
 hipError_t launch_packed_tm(const SpmmArgs& a, const uint8_t* pv, const uint8_t* pm, int64_t tiles, int64_t G,
                             hipStream_t s) {
-    constexpr int P = kPackedP<TM>;
-    const unsigned shm = (unsigned)(kWaves * P * 16 * SN<DT>::ES * SN<DT>::KS);
-    hipLaunchKernelGGL((k_spmm_packed<DT, TM, P>), dim3((unsigned)G), dim3(64 * kWaves), shm, s, a, pv, pm, tiles);
+    if (a.row_ptr == nullptr) {
+        constexpr int P = kPackedP<TM>;
+        const unsigned shm = (unsigned)(kWaves * P * 16 * SN<DT>::ES * SN<DT>::KS);
+        hipLaunchKernelGGL((k_spmm_packed<DT, TM, P, false, false>), dim3((unsigned)G), dim3(64 * kWaves), shm, s, a,
+                           pv, pm, tiles);
+    } else {
+        constexpr int P = kPackedResP<TM>;
+        static_assert(kWaves * P * 16 * 2 * 64 <= kRingResOff, "ring slots below the row sums");
+        if (a.dcol != nullptr)
+            hipLaunchKernelGGL((k_spmm_packed<DT, TM, P, true, true>), dim3((unsigned)G), dim3(64 * kWaves),
+                               160 * 1024, s, a, pv, pm, tiles);
+        else
+            hipLaunchKernelGGL((k_spmm_packed<DT, TM, P, true, false>), dim3((unsigned)G), dim3(64 * kWaves),
+                               160 * 1024, s, a, pv, pm, tiles);
+    }
     return hipGetLastError();
 }
 

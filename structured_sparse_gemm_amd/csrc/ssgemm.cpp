@@ -416,8 +416,13 @@ int ssg_pack_2to4_decode(int dt, int64_t M, int64_t K, const void* vals, int64_t
     return e == hipSuccess ? SSG_OK : hip_fail(e, "pack launch");
 }
 
-int ssg_spmm_2to4_packed(int ab, int c, int64_t M, int64_t N, int64_t K, const void* pvals, const void* pmeta,
-                         const void* B, int64_t ldb, void* C, int64_t ldc, void* stream) {
+namespace {
+
+// The packed decode product, with an optional residual (CSR: col != NULL,
+// delta-coded: dcol != NULL; nnz == 0: none).
+int run_packed(int ab, int c, int64_t M, int64_t N, int64_t K, const void* pvals, const void* pmeta,
+               const int32_t* row_ptr, const int32_t* col, const uint8_t* dcol, const void* rvals, int64_t nnz,
+               const void* B, int64_t ldb, void* C, int64_t ldc, void* stream) {
     if (!pair_ok(ab, c)) return fail(SSG_ERR_DTYPE, "unsupported (input, output) types (%d, %d)", ab, c);
     int64_t vb, mb;
     int rc = packed_sizes(ab, M, K, &vb, &mb);
@@ -433,8 +438,44 @@ int ssg_spmm_2to4_packed(int ab, int c, int64_t M, int64_t N, int64_t K, const v
     if (ldc < N) return fail(SSG_ERR_STRIDE, "ldc=%lld < N=%lld", (long long)ldc, (long long)N);
     if (K * 16 * esize(ab) >= 0x7fffffff) return fail(SSG_ERR_SHAPE, "B too large for 31-bit offsets");
     ssg::SpmmArgs a = make_args(ab, M, N, K, nullptr, 0, nullptr, 0, B, ldb, C, ldc);
+    if (nnz > 0) {
+        // the residual epilogue reads up to 4 entries per lane with one load
+        // per array, at 31-bit byte offsets
+        const int64_t ib = dcol ? 1 : 4;
+        const void* idx = dcol ? static_cast<const void*>(dcol) : static_cast<const void*>(col);
+        if (!al(idx, (uintptr_t)(4 * ib)) || !al(rvals, (uintptr_t)(4 * esize(ab))) || nnz * ib >= 0x7fff0000 ||
+            nnz * esize(ab) >= 0x7fff0000)
+            return fail(SSG_ERR_ALGO, "residual arrays must be aligned to 4 entries and under 2^31 bytes");
+        a.row_ptr = row_ptr; a.col = col; a.dcol = dcol; a.rvals = rvals; a.nnz_r = nnz;
+    }
     hipError_t e = ssg::launch_spmm_packed(a, pvals, pmeta, (hipStream_t)stream);
     return e == hipSuccess ? SSG_OK : hip_fail(e, "packed spmm launch");
+}
+
+}  // namespace
+
+int ssg_spmm_2to4_packed(int ab, int c, int64_t M, int64_t N, int64_t K, const void* pvals, const void* pmeta,
+                         const void* B, int64_t ldb, void* C, int64_t ldc, void* stream) {
+    return run_packed(ab, c, M, N, K, pvals, pmeta, nullptr, nullptr, nullptr, nullptr, 0, B, ldb, C, ldc, stream);
+}
+
+int ssg_spmm_2to4_packed_residual(int ab, int c, int64_t M, int64_t N, int64_t K, const void* pvals,
+                                  const void* pmeta, const int32_t* row_ptr, const int32_t* col, const void* rvals,
+                                  int64_t nnz_r, const void* B, int64_t ldb, void* C, int64_t ldc, void* stream) {
+    if (nnz_r < 0 || nnz_r > INT32_MAX) return fail(SSG_ERR_FORMAT, "nnz_r=%lld out of range", (long long)nnz_r);
+    if (M > 0 && !row_ptr) return fail(SSG_ERR_NULL, "row_ptr is NULL");
+    if (nnz_r > 0 && (!col || !rvals)) return fail(SSG_ERR_NULL, "col or rvals is NULL with nnz_r > 0");
+    return run_packed(ab, c, M, N, K, pvals, pmeta, row_ptr, col, nullptr, rvals, nnz_r, B, ldb, C, ldc, stream);
+}
+
+int ssg_spmm_2to4_packed_residual_delta(int ab, int c, int64_t M, int64_t N, int64_t K, const void* pvals,
+                                        const void* pmeta, const int32_t* drow_ptr, const uint8_t* dcol,
+                                        const void* dvals, int64_t nnz_d, const void* B, int64_t ldb, void* C,
+                                        int64_t ldc, void* stream) {
+    if (nnz_d < 0 || nnz_d > INT32_MAX) return fail(SSG_ERR_FORMAT, "nnz_d=%lld out of range", (long long)nnz_d);
+    if (M > 0 && !drow_ptr) return fail(SSG_ERR_NULL, "drow_ptr is NULL");
+    if (nnz_d > 0 && (!dcol || !dvals)) return fail(SSG_ERR_NULL, "dcol or dvals is NULL with nnz_d > 0");
+    return run_packed(ab, c, M, N, K, pvals, pmeta, drow_ptr, nullptr, dcol, dvals, nnz_d, B, ldb, C, ldc, stream);
 }
 
 namespace {

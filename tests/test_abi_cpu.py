@@ -237,3 +237,21 @@ def test_prefill_argument_errors(lib):
     assert s(I8, I32, 8, 8, 128, FAKE, FAKE, FAKE, 8, FAKE, 8, None) == _abi.SSG_ERR_ALGO   # N % 16
     assert s(F16, F32, 8, 12, 64, FAKE, FAKE, FAKE, 12, FAKE, 12, None) == _abi.SSG_ERR_ALGO   # N % 8
     assert s(F16, F32, 0, 16, 64, None, None, None, 16, None, 16, None) == 0
+
+
+def test_packed_residual_argument_errors(lib):
+    r = lib.ssg_spmm_2to4_packed_residual
+    d = lib.ssg_spmm_2to4_packed_residual_delta
+    assert r(F16, F32, 32, 16, 128, FAKE, FAKE, FAKE, FAKE, FAKE, -1, FAKE, 16, FAKE, 16, None) == _abi.SSG_ERR_FORMAT
+    assert r(F16, F32, 32, 16, 128, FAKE, FAKE, None, FAKE, FAKE, 4, FAKE, 16, FAKE, 16, None) == _abi.SSG_ERR_NULL
+    assert r(F16, F32, 32, 16, 128, FAKE, FAKE, FAKE, None, FAKE, 4, FAKE, 16, FAKE, 16, None) == _abi.SSG_ERR_NULL
+    assert r(F16, I32, 32, 16, 128, FAKE, FAKE, FAKE, FAKE, FAKE, 4, FAKE, 16, FAKE, 16, None) == _abi.SSG_ERR_DTYPE
+    assert r(F16, F32, 32, 16, 96, FAKE, FAKE, FAKE, FAKE, FAKE, 4, FAKE, 16, FAKE, 16, None) == _abi.SSG_ERR_SHAPE
+    assert r(F16, F32, 32, 8, 128, FAKE, FAKE, FAKE, FAKE, FAKE, 4, FAKE, 8, FAKE, 8, None) == _abi.SSG_ERR_ALGO
+    # column indices not aligned to 4 entries (16 bytes)
+    assert r(F16, F32, 32, 16, 128, FAKE, FAKE, FAKE, ctypes.c_void_p(0x1004), FAKE, 4, FAKE, 16, FAKE, 16,
+             None) == _abi.SSG_ERR_ALGO
+    assert d(F16, F32, 32, 16, 128, FAKE, FAKE, FAKE, FAKE, None, 4, FAKE, 16, FAKE, 16, None) == _abi.SSG_ERR_NULL
+    assert d(F16, F32, 32, 16, 128, FAKE, FAKE, FAKE, ctypes.c_void_p(0x1002), FAKE, 4, FAKE, 16, FAKE, 16,
+             None) == _abi.SSG_ERR_ALGO
+    assert r(F16, F32, 0, 16, 128, None, None, None, None, None, 0, FAKE, 16, None, 16, None) == 0

@@ -384,6 +384,69 @@ def test_spmm_packed_takes_only_16_columns():
     assert e.value.status == 8
 
 
+PACKED_RES_SHAPES = [(16, 128), (40, 256), (300, 1024), (1000, 2048), (4100, 512)]
+
+
+@pytest.mark.parametrize("dt", DTS)
+@pytest.mark.parametrize("code", ["csr", "delta"])
+@pytest.mark.parametrize("shape", PACKED_RES_SHAPES)
+def test_spmm_packed_residual_matches_oracle(dt, code, shape):
+    M, K = shape
+    a = U.random_matrix(dt, M, K, "sparse", seed=M + 5 * K)
+    b = U.random_matrix(dt, K, 16, "normal", seed=K + 9)
+    vals, meta, row_ptr, col, rvals = oracle.split(dt, a)
+    pv, pm = ssg.pack_decode(to_dev(vals, dt), dev_or_empty(meta), K)
+    B = to_dev(b, dt)
+    V, Mt = to_dev(vals, dt), dev_or_empty(meta)
+    if code == "csr":
+        rp, cl, rv = dev_or_empty(row_ptr), dev_or_empty(col), dev_or_empty(rvals, dt)
+        C = ssg.spmm_packed_residual(pv, pm, M, rp, cl, rv, B)
+        C_ring = ssg.spmm_residual(V, Mt, rp, cl, rv, B)
+    else:
+        d = oracle.delta_encode(dt, row_ptr, col, rvals, K)
+        dr, dc, dv = dev_or_empty(d[0]), dev_or_empty(d[1]), dev_or_empty(d[2], dt)
+        C = ssg.spmm_packed_residual_delta(pv, pm, M, dr, dc, dv, B)
+        C_ring = ssg.spmm_residual_delta(V, Mt, dr, dc, dv, B)
+    cref, sref = oracle.spmm_residual(dt, vals, meta, row_ptr, col, rvals, b, K)
+    check_product(dt, C.cpu().numpy(), cref, sref, "packed residual %s %s %s" % (dt, code, shape))
+    if dt == "i8":      # integer sums: the same bits as the row-major kernel
+        assert torch.equal(C, C_ring)
+
+
+def test_spmm_packed_residual_exact_small_integers():
+    # fp16 small integers: every partial sum exact in fp32, so the product
+    # equals the oracle's exactly, residual included
+    M, K = 300, 1024
+    rng = np.random.default_rng(11)
+    dense = rng.integers(-3, 4, size=(M, K)) * (rng.random((M, K)) < 0.5)
+    a = dense.astype(np.float16).view(np.uint16)
+    b = rng.integers(-3, 4, size=(K, 16)).astype(np.float16).view(np.uint16)
+    vals, meta, row_ptr, col, rvals = oracle.split("f16", a)
+    pv, pm = ssg.pack_decode(to_dev(vals, "f16"), dev_or_empty(meta), K)
+    C = ssg.spmm_packed_residual(pv, pm, M, dev_or_empty(row_ptr), dev_or_empty(col), dev_or_empty(rvals, "f16"),
+                                 to_dev(b, "f16")).cpu().numpy().astype(np.float64)
+    cref, _ = oracle.spmm_residual("f16", vals, meta, row_ptr, col, rvals, b, K)
+    assert np.array_equal(C, cref)
+
+
+def test_full_size_residual_packed():
+    w = W.WORKLOADS["c5"]
+    print("full-size packed residual: %s" % w.title, flush=True)
+    a_cpu, b_cpu = W.gen_a(w), W.gen_b(w)
+    a, b = W.bits(a_cpu), W.bits(b_cpu)
+    vals, meta, row_ptr, col, rvals = ssg.split(a_cpu.cuda())
+    pv, pm = ssg.pack_decode(vals, meta, w.K)
+    B = b_cpu.cuda()
+    C = ssg.spmm_packed_residual(pv, pm, w.M, row_ptr, col, rvals, B).cpu().numpy()
+    drow_ptr, dcol, dvals = ssg.delta_encode(row_ptr, col, rvals, w.K)
+    Cd = ssg.spmm_packed_residual_delta(pv, pm, w.M, drow_ptr, dcol, dvals, B).cpu().numpy()
+    r = oracle.split(w.dtype, a)
+    ms, ns = sample_entries(w.M, w.N, 3000, seed=w.index + 80)
+    cref, sref = oracle.spmm_entries(w.dtype, r[0], r[1], b, w.K, ms, ns, residual=(r[2], r[3], r[4]))
+    check_product(w.dtype, C[ms, ns], cref, sref, "c5 packed residual")
+    check_product(w.dtype, Cd[ms, ns], cref, sref, "c5 packed residual, delta-coded")
+
+
 def test_full_size_decode_packed():
     w = W.WORKLOADS["c3"]
     a_cpu, b_cpu = W.gen_a(w), W.gen_b(w)
