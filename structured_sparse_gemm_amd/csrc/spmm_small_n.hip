@@ -1029,11 +1029,15 @@ __global__ void __launch_bounds__(kWaves * 64) k_spmm_packed(SpmmArgs a, const u
     }
 }
 
-template <int TM> constexpr int kPackedP = TM == 1 ? 8 : TM == 2 ? 8 : TM == 3 ? 7 : 6;
+// Ring depth of the packed product by tiles per workgroup: about 4 to 8
+// fragments (KiB) in flight per wave.  Deeper rings put most of a decode-size
+// operand in flight at once and measured slower (fp16 11008 x 4096: 12.5 us
+// at 7 k-steps deep, 11.1 us at 2).
+template <int TM> constexpr int kPackedP = TM == 1 ? 4 : TM == 2 ? 3 : 2;
 
 // with a residual: the shallower ring (registers for the epilogue) and the
 // whole LDS (B chunks below the row sums)
-template <int TM> constexpr int kPackedResP = TM == 4 ? 4 : 6;
+template <int TM> constexpr int kPackedResP = TM == 4 ? 2 : 3;
 
 template <int DT, int TM>
 hipError_t launch_packed_tm(const SpmmArgs& a, const uint8_t* pv, const uint8_t* pm, int64_t tiles, int64_t G,
