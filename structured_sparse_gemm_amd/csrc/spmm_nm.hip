@@ -265,7 +265,10 @@ struct NmShape {
     static constexpr int MB = D / 8;                     // mask bytes per lane per super-step
     static constexpr int BSTEP = SK * 16 * ES;           // B bytes per super-step (16 columns)
     static constexpr int NB = BSTEP / 1024;              // direct-to-LDS loads of B per super-step
-    static constexpr int P = NB >= 4 ? 4 : 6;            // super-steps in flight per wave
+    // super-steps in flight per wave: shallow rings measured faster than
+    // deep ones (fp16 11008 x 4096 x 16, packed: 1:4 11.5 us at 4, 9.3 us at
+    // 2; 2:4 13.5 us at 6, 11.6 us at 2)
+    static constexpr int P = 2;
     static constexpr int LUT = (1 << MM) * OW * 4;       // selector table bytes
     static_assert(D % MM == 0 && D % E == 0 && D % 8 == 0 && V % 8 == 0, "shape");
     static_assert(!W4 || NN % 2 == 0, "4-bit weights: whole bytes per group");

@@ -1029,11 +1029,11 @@ __global__ void __launch_bounds__(kWaves * 64) k_spmm_packed(SpmmArgs a, const u
     }
 }
 
-// Ring depth of the packed product by tiles per workgroup: about 4 to 8
+// Ring depth of the packed product by tiles per workgroup: about 3 to 8
 // fragments (KiB) in flight per wave.  Deeper rings put most of a decode-size
 // operand in flight at once and measured slower (fp16 11008 x 4096: 12.5 us
-// at 7 k-steps deep, 11.1 us at 2).
-template <int TM> constexpr int kPackedP = TM == 1 ? 4 : TM == 2 ? 3 : 2;
+// at 7 k-steps deep, 11.0 us at 2; 8192 x 8192: 17.7 us at 8, 15.0 us at 2).
+template <int TM> constexpr int kPackedP = TM == 1 ? 3 : 2;
 
 // with a residual: the shallower ring (registers for the epilogue) and the
 // whole LDS (B chunks below the row sums)
@@ -1074,8 +1074,11 @@ hipError_t launch_packed_t(const SpmmArgs& a, const uint8_t* pv, const uint8_t* 
     }
 }
 
-template <int TM> constexpr int kRingP = TM == 4 ? 6 : 8;      // deepest ring
-template <int TM> constexpr int kRingPLow = TM == 4 ? 4 : 6;   // when the deepest does not fit
+// Ring depths (k-steps in flight per wave).  As for the packed product,
+// shallow rings measured faster than deep ones (fp16 11008 x 4096 x 16:
+// 16.2 us at 8 k-steps, 14.9 us at 4, 14.3 us at 3).
+template <int TM> constexpr int kRingP = TM == 4 ? 2 : 3;      // deepest ring
+template <int TM> constexpr int kRingPLow = 2;                 // when the deepest does not fit
 
 // LDS of the ring variant: the waves' B slots and the slab's metadata rows
 template <int DT, int TM>
