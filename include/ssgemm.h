@@ -140,7 +140,10 @@ int ssg_split_fill(int dt, int64_t M, int64_t K, const void* A, int64_t lda,
                    void* vals, int64_t ldv, uint8_t* meta, int64_t ldm,
                    const int32_t* row_ptr, int32_t* col, void* rvals, void* stream);
 
-/* Workspace the SpMM calls need for this problem (bytes; may be 0). */
+/* Workspace the SpMM calls need for this problem (bytes; may be 0).  It is
+ * 0 except for 0 < N < 16, where it holds B padded to 16 zero-extended
+ * columns (K * 16 elements, rounded up to 256 bytes; 16-byte aligned): the
+ * decode kernels then take B as one contiguous K x 16 block. */
 size_t ssg_spmm_workspace_bytes(int ab, int64_t M, int64_t N, int64_t K);
 
 /* C = expand(vals, meta) x B.  (ab, c) must be (SSG_F16, SSG_F32),

@@ -33,6 +33,8 @@
 //   wave reduction per row.
 // * Partial tiles of the waves are summed through LDS in wave order, so the
 //   fp32 result is the same on every run.
+#include <algorithm>
+
 #include "ssg_device.hpp"
 #include "ssg_kernels.hpp"
 #include "ssg_stream.hpp"
@@ -1133,7 +1135,9 @@ bool ring_ok(const SpmmArgs& a, int tm) {
     const uintptr_t bp = reinterpret_cast<uintptr_t>(a.B), mp = reinterpret_cast<uintptr_t>(a.meta);
     const int P = tm == 1 ? ring_depth<DT, 1>(a) : tm == 2 ? ring_depth<DT, 2>(a) : tm == 3 ? ring_depth<DT, 3>(a)
                                                                                           : ring_depth<DT, 4>(a);
-    return P > 0 && a.N == 16 && a.ldb == 16 && bp % 16 == 0 && mp % 4 == 0 && a.ldm % 4 == 0 &&
+    // B rows of 16 elements (N < 16: columns past N are computed and never
+    // stored; the host pads a narrower B into the workspace)
+    return P > 0 && a.N <= 16 && a.ldb == 16 && bp % 16 == 0 && mp % 4 == 0 && a.ldm % 4 == 0 &&
            a.K * 16 * T::ES < 0x7fffffff && a.M * a.ldv * T::ES < 0x7fffffff && a.M * a.ldm < 0x7fffffff;
 }
 
@@ -1259,6 +1263,27 @@ hipError_t launch_pack_decode(int dt, int64_t M, int64_t K, const void* vals, in
             break;
         default: return hipErrorInvalidValue;
     }
+    return hipGetLastError();
+}
+
+// B [K, N] (N < 16, row stride ldb) copied to K x 16 with zero columns past N,
+// so the decode kernels that take B as one contiguous K x 16 block apply.
+template <typename E>
+__global__ void __launch_bounds__(256) k_pad_b(int64_t K, int64_t N, const E* B, int64_t ldb, E* out) {
+    const int64_t n = K * 16;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t k = i >> 4, c = i & 15;
+        out[i] = c < N ? B[k * ldb + c] : E(0);
+    }
+}
+
+hipError_t launch_pad_b(int dt, int64_t K, int64_t N, const void* B, int64_t ldb, void* out, hipStream_t s) {
+    const int64_t n = K * 16;
+    const unsigned grid = (unsigned)std::min<int64_t>((n + 255) / 256, 2048);
+    if (dt_bytes(dt) == 2)
+        hipLaunchKernelGGL(k_pad_b<uint16_t>, dim3(grid), dim3(256), 0, s, K, N, (const uint16_t*)B, ldb, (uint16_t*)out);
+    else
+        hipLaunchKernelGGL(k_pad_b<uint8_t>, dim3(grid), dim3(256), 0, s, K, N, (const uint8_t*)B, ldb, (uint8_t*)out);
     return hipGetLastError();
 }
 

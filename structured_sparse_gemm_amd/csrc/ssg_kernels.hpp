@@ -61,6 +61,8 @@ hipError_t launch_residual_add(const SpmmArgs& a, hipStream_t s);
 // (shape, alignment); the launchers assume it does.
 bool supported_small_n(const SpmmArgs& a);
 hipError_t launch_spmm_small_n(const SpmmArgs& a, hipStream_t s);
+// B [K, N] with N < 16 copied to out [K, 16] (zero columns past N).
+hipError_t launch_pad_b(int dt, int64_t K, int64_t N, const void* B, int64_t ldb, void* out, hipStream_t s);
 // Packed decode layout (see spmm_small_n.hip): pack from (vals, meta), and
 // the product on it (B one contiguous K x 16 block, K a multiple of the
 // k-step; a.vals / a.meta unused).

@@ -103,8 +103,28 @@ int pick_algo(const ssg::SpmmArgs& a) {
     return SSG_ALGO_GENERIC;
 }
 
-int run_spmm(int algo, const ssg::SpmmArgs& a, hipStream_t s) {
+// Workspace of a product with 0 < N < 16: B padded to 16 columns, which lets
+// the decode kernels that take B as one contiguous K x 16 block run.
+int64_t padded_b_bytes(int ab, int64_t N, int64_t K) {
+    return N > 0 && N < 16 && K > 0 ? (K * 16 * esize(ab) + 255) / 256 * 256 : 0;
+}
+
+int run_spmm(int algo, ssg::SpmmArgs a, hipStream_t s, void* ws, size_t ws_bytes) {
     if (a.M == 0 || a.N == 0) return SSG_OK;
+    // B narrower than 16 columns: padded into the workspace for the decode kernels
+    const int64_t es = (a.dt == ssg::DT_F16 || a.dt == ssg::DT_BF16) ? 2 : 1;
+    const int64_t pad = a.N < 16 && a.K > 0 ? (a.K * 16 * es + 255) / 256 * 256 : 0;
+    if ((algo == SSG_ALGO_AUTO || algo == SSG_ALGO_SMALL_N) && pad > 0 && a.ldb != 16 && ws != nullptr &&
+        (int64_t)ws_bytes >= pad && al(ws, 16) && a.K * 16 * es < 0x7fffffff) {
+        ssg::SpmmArgs p = a;
+        p.B = ws;
+        p.ldb = 16;
+        if (ssg::supported_small_n(p)) {
+            hipError_t e = ssg::launch_pad_b(a.dt, a.K, a.N, a.B, a.ldb, ws, s);
+            if (e != hipSuccess) return hip_fail(e, "B padding launch");
+            a = p;
+        }
+    }
     if (algo == SSG_ALGO_AUTO) algo = pick_algo(a);
     hipError_t e = hipSuccess;
     switch (algo) {
@@ -231,8 +251,9 @@ int ssg_split_fill(int dt, int64_t M, int64_t K, const void* A, int64_t lda, voi
 }
 
 size_t ssg_spmm_workspace_bytes(int ab, int64_t M, int64_t N, int64_t K) {
-    (void)ab; (void)M; (void)N; (void)K;
-    return 0;
+    (void)M;
+    if (!in_dtype(ab) || N < 0 || K < 0) return 0;
+    return (size_t)padded_b_bytes(ab, N, K);
 }
 
 int ssg_spmm_2to4_ex(int algo, int ab, int c, int64_t M, int64_t N, int64_t K, const void* vals, int64_t ldv,
@@ -242,7 +263,8 @@ int ssg_spmm_2to4_ex(int algo, int ab, int c, int64_t M, int64_t N, int64_t K, c
     if (rc) return rc;
     const size_t need = ssg_spmm_workspace_bytes(ab, M, N, K);
     if (ws_bytes < need || (need > 0 && !ws)) return fail(SSG_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
-    return run_spmm(algo, make_args(ab, M, N, K, vals, ldv, meta, ldm, B, ldb, C, ldc), (hipStream_t)stream);
+    return run_spmm(algo, make_args(ab, M, N, K, vals, ldv, meta, ldm, B, ldb, C, ldc), (hipStream_t)stream, ws,
+                    ws_bytes);
 }
 
 int ssg_spmm_2to4(int ab, int c, int64_t M, int64_t N, int64_t K, const void* vals, int64_t ldv, const uint8_t* meta,
@@ -267,7 +289,7 @@ int ssg_spmm_2to4_residual_ex(int algo, int ab, int c, int64_t M, int64_t N, int
     // an empty residual adds nothing: the plain 2:4 product (the residual
     // kernels may read entry 0 of a non-empty residual unconditionally)
     if (nnz_r > 0) { a.row_ptr = row_ptr; a.col = col; a.rvals = rvals; a.nnz_r = nnz_r; }
-    return run_spmm(algo, a, (hipStream_t)stream);
+    return run_spmm(algo, a, (hipStream_t)stream, ws, ws_bytes);
 }
 
 int ssg_residual_delta_count(int64_t M, int64_t K, const int32_t* row_ptr, const int32_t* col, int64_t nnz_r,
@@ -314,7 +336,7 @@ int ssg_spmm_2to4_residual_delta_ex(int algo, int ab, int c, int64_t M, int64_t 
     // an empty residual adds nothing: the plain 2:4 product (the residual
     // kernels may read entry 0 of a non-empty residual unconditionally)
     if (nnz_d > 0) { a.row_ptr = drow_ptr; a.dcol = dcol; a.rvals = dvals; a.nnz_r = nnz_d; }
-    return run_spmm(algo, a, (hipStream_t)stream);
+    return run_spmm(algo, a, (hipStream_t)stream, ws, ws_bytes);
 }
 
 int ssg_spmm_2to4_residual_delta(int ab, int c, int64_t M, int64_t N, int64_t K, const void* vals, int64_t ldv,

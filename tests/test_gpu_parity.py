@@ -384,6 +384,38 @@ def test_spmm_packed_takes_only_16_columns():
     assert e.value.status == 8
 
 
+NARROW_SHAPES = [(11008, 4096, 1), (1000, 2048, 5), (300, 1024, 8), (4100, 512, 15)]
+
+
+@pytest.mark.parametrize("dt", DTS)
+@pytest.mark.parametrize("shape", NARROW_SHAPES)
+def test_spmm_narrow_b(dt, shape):
+    # N < 16 with a strided B: the product pads B to 16 columns in its
+    # workspace and runs the decode kernel that takes a contiguous K x 16 B
+    M, K, N = shape
+    a = U.random_matrix(dt, M, K, "normal", seed=M + 3 * K)
+    b = U.random_matrix(dt, K, N, "normal", seed=N + 29)
+    vals, meta = oracle.compress(dt, a)
+    assert ssg.ssg_spmm_workspace_bytes(W.TORCH_DTYPE[dt], M, N, K) >= K * 16 * (2 if dt in ("f16", "bf16") else 1)
+    B = strided(to_dev(b, dt), 3)
+    C = ssg.spmm(to_dev(vals, dt), dev_or_empty(meta), B)
+    cref, sref = oracle.spmm(dt, vals, meta, b, K)
+    check_product(dt, C.cpu().numpy(), cref, sref, "narrow %s %s" % (dt, shape))
+
+
+@pytest.mark.parametrize("dt", DTS)
+def test_spmm_residual_narrow_b(dt):
+    M, K, N = 300, 1024, 8
+    a = U.random_matrix(dt, M, K, "sparse", seed=41)
+    b = U.random_matrix(dt, K, N, "normal", seed=43)
+    vals, meta, row_ptr, col, rvals = oracle.split(dt, a)
+    B = strided(to_dev(b, dt), 5)
+    C = ssg.spmm_residual(to_dev(vals, dt), dev_or_empty(meta), dev_or_empty(row_ptr), dev_or_empty(col),
+                          dev_or_empty(rvals, dt), B)
+    cref, sref = oracle.spmm_residual(dt, vals, meta, row_ptr, col, rvals, b, K)
+    check_product(dt, C.cpu().numpy(), cref, sref, "narrow residual %s" % dt)
+
+
 PACKED_RES_SHAPES = [(16, 128), (40, 256), (300, 1024), (1000, 2048), (4100, 512)]
 
 
