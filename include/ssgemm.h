@@ -274,16 +274,17 @@ int ssg_spmm_2to4_packed_residual_delta(int ab, int c, int64_t M, int64_t N, int
  * in LDS, so that every load of stored values or metadata is one contiguous
  * piece ("Chapter 26 -- Sparsity: The Hardware View", section "2:4: ~2x on
  * the Matmul, Less End-to-End": in the compute-bound regime the doubled
- * sparse matrix rate pays only if the operands keep up).  In bytes it is the
- * same for every element type.  Rows are grouped in tiles of 256; a stage is
+ * sparse matrix rate pays only if the operands keep up).  Rows are grouped in tiles of 256; a stage is
  * 64 stored-value bytes of a row (64 dense k for fp16/bf16, 128 for the
  * 8-bit types); a metadata block is 32 metadata bytes of a row (256 dense k).
  *   pvals: tile t, stage s -> 16 KiB block (t * stages + s); row r of the tile
  *          at byte r * 64 of it, its 16-byte chunk c (stored-value bytes
  *          [64 s + 16 c, +16) of the row) at chunk position
  *          c ^ (((r >> 1) ^ (r >> 3)) & 3).
- *   pmeta: tile t, block g -> 8 KiB block (t * mblocks + g); row r's metadata
- *          bytes [32 g, 32 g + 32) at byte r * 32 of it.
+ *   pmeta: tile t, block g -> 8 KiB block (t * mblocks + g), index-word
+ *          major: index word w of row r (its metadata bytes
+ *          [32 g + w IW, 32 g + w IW + IW), IW = 4 for the 8-bit types and 2
+ *          for fp16/bf16) at byte w * 256 * IW + r * IW of it.
  * stages = K / 64 (fp16/bf16) or K / 128 (8-bit); mblocks = ceil(K / 256).
  * Rows past M and metadata bytes past K / 8 hold zeros.  The same bytes as
  * (vals, meta), only reordered.

@@ -122,10 +122,20 @@ __device__ __forceinline__ void store_prefill(uint8_t* pv, uint8_t* pm, int64_t 
 #pragma unroll
     for (int i = 0; i < kVecs; ++i)
         *reinterpret_cast<uint4*>(pv + prefill_vals_offset(m, (c * kVecs + i) * 16, stages)) = w[i];
-    *reinterpret_cast<uint32_t*>(pm + prefill_meta_offset(m, c * 4, mblocks)) = word;
-    if ((c + 1) * kChunkElems == K)
-        for (int64_t j = K / 8; j < mblocks * 32; j += 4)
-            *reinterpret_cast<uint32_t*>(pm + prefill_meta_offset(m, j, mblocks)) = 0u;
+    // the chunk's 4 metadata bytes are one index word (8-bit) or two (16-bit)
+    constexpr int IW = sizeof(T) == 1 ? 4 : 2;
+    if constexpr (IW == 4) {
+        *reinterpret_cast<uint32_t*>(pm + prefill_meta_offset(m, c * 4, mblocks, IW)) = word;
+        if ((c + 1) * kChunkElems == K)
+            for (int64_t j = K / 8; j < mblocks * 32; j += 4)
+                *reinterpret_cast<uint32_t*>(pm + prefill_meta_offset(m, j, mblocks, IW)) = 0u;
+    } else {
+        *reinterpret_cast<uint16_t*>(pm + prefill_meta_offset(m, c * 4, mblocks, IW)) = (uint16_t)word;
+        *reinterpret_cast<uint16_t*>(pm + prefill_meta_offset(m, c * 4 + 2, mblocks, IW)) = (uint16_t)(word >> 16);
+        if ((c + 1) * kChunkElems == K)
+            for (int64_t j = K / 8; j < mblocks * 32; j += 2)
+                *reinterpret_cast<uint16_t*>(pm + prefill_meta_offset(m, j, mblocks, IW)) = 0;
+    }
 }
 
 // PF: write the packed prefill layout (vals / meta are pvals / pmeta, rows

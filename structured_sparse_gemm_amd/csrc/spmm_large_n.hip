@@ -378,6 +378,19 @@ __global__ void __launch_bounds__(kThreads) k_spmm_pipe(SpmmArgs a, int tiles_m,
     // 2s + q of the row's 16.  Stage t's bytes are at (t % MB) * MSTAGE of
     // each row of metadata block t / MB.
     auto read_idx = [&](int64_t t, int s, uint32_t (&ix)[4]) {
+        if constexpr (PK) {
+            // packed: the block is index-word major ([word][256 rows]), so the
+            // 32 rows of one word that a read serves are contiguous
+            const uint8_t* mb = mlds + ((t / T::MB) & 1) * L::MBLK;
+            const int w = ((int)(t % T::MB) * T::MSTAGE + s * (T::MSTAGE / 2) + q * T::IDXB) / T::IDXB;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int row = 32 * (wm * 4 + i) + rl;
+                if constexpr (T::IDXB == 4) ix[i] = *reinterpret_cast<const uint32_t*>(mb + w * 1024 + row * 4);
+                else ix[i] = *reinterpret_cast<const uint16_t*>(mb + w * 512 + row * 2);
+            }
+            return;
+        }
         const uint8_t* mt = mlds + ((t / T::MB) & 1) * L::MBLK + (t % T::MB) * T::MSTAGE + s * (T::MSTAGE / 2);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -505,11 +518,11 @@ hipError_t pipe_launch(const SpmmArgs& a, hipStream_t s) {
 
 // Row-major (vals, meta) -> packed prefill layout.  One thread per 16-byte
 // chunk of pvals (a copy of one 16-byte chunk of a vals row, or zeros past
-// M) and per 4 bytes of pmeta (copied bytewise: meta rows need no
-// alignment; zeros past M and past K / 8).
+// M) and per 4 bytes of pmeta (gathered bytewise from the index-word-major
+// positions: meta rows need no alignment; zeros past M and past K / 8).
 __global__ void __launch_bounds__(256) k_pack_prefill(int64_t M, int64_t K, const uint8_t* vals, int64_t ldv_bytes,
                                                       const uint8_t* meta, int64_t ldm, int64_t stages, int64_t mblocks,
-                                                      int64_t vchunks, int64_t mwords, uint8_t* pvals,
+                                                      int64_t vchunks, int64_t mwords, int iw, uint8_t* pvals,
                                                       uint8_t* pmeta) {
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < vchunks + mwords; i += stride) {
@@ -524,13 +537,14 @@ __global__ void __launch_bounds__(256) k_pack_prefill(int64_t M, int64_t K, cons
         } else {
             const int64_t k = i - vchunks;     // 4-byte word k of pmeta
             const int64_t blk = k >> 11, t = blk / mblocks, g = blk - t * mblocks;
-            const int r = (int)((k >> 3) & 255), d = (int)(k & 7);
-            const int64_t m = t * 256 + r;
             uint32_t w = 0;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const int64_t j = g * 32 + d * 4 + e;
-                if (m < M && j < K / 8) w |= (uint32_t)meta[m * ldm + j] << (8 * e);
+                // byte o of the block: index word o / (256 iw) of row (o / iw) % 256
+                const int o = (int)((k & 2047) * 4 + e);
+                const int r = (o / iw) & 255, j = (o / (256 * iw)) * iw + o % iw;
+                const int64_t m = t * 256 + r;
+                if (m < M && g * 32 + j < K / 8) w |= (uint32_t)meta[m * ldm + g * 32 + j] << (8 * e);
             }
             *reinterpret_cast<uint32_t*>(pmeta + (k << 2)) = w;
         }
@@ -564,8 +578,8 @@ hipError_t launch_pack_prefill(int dt, int64_t M, int64_t K, const void* vals, i
     if (vchunks + mwords == 0) return hipSuccess;
     const int64_t grid = std::min<int64_t>((vchunks + mwords + 255) / 256, 8192);
     hipLaunchKernelGGL(k_pack_prefill, dim3((unsigned)grid), dim3(256), 0, s, M, K, (const uint8_t*)vals,
-                       ldv * dt_bytes(dt), meta, ldm, stages, mblocks, vchunks, mwords, (uint8_t*)pvals,
-                       (uint8_t*)pmeta);
+                       ldv * dt_bytes(dt), meta, ldm, stages, mblocks, vchunks, mwords, dt_bytes(dt) == 1 ? 4 : 2,
+                       (uint8_t*)pvals, (uint8_t*)pmeta);
     return hipGetLastError();
 }
 

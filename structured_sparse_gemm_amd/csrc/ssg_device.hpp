@@ -65,8 +65,10 @@ __device__ __forceinline__ bool nibble_valid(uint32_t nib) { return (nib & 3u) <
 // block 32 metadata bytes of every row (256 dense k).
 // * pvals: tile t, stage s -> 16 KiB block (t * stages + s); row r of the tile
 //   at r * 64 in it, its 16-byte chunk c at chunk position c ^ prefill_swz(r).
-// * pmeta: tile t, block g -> 8 KiB block (t * mblocks + g); row r's metadata
-//   bytes [32 g, 32 g + 32) at r * 32 in it.
+// * pmeta: tile t, block g -> 8 KiB block (t * mblocks + g), index-word
+//   major: index word w of row r (its metadata bytes [32 g + w IW, + IW),
+//   IW = 4 for 8-bit types, 2 for 16-bit ones) at w * 256 IW + r IW, so the
+//   32 rows whose words one MFMA reads are contiguous in LDS.
 // Rows past M and metadata bytes past K / 8 hold zeros.
 // ---------------------------------------------------------------------------
 __host__ __device__ __forceinline__ int prefill_swz(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
@@ -77,9 +79,9 @@ __host__ __device__ __forceinline__ int64_t prefill_vals_offset(int64_t m, int64
     return (((m >> 8) * stages + (b >> 6)) << 14) + r * 64 + ((((int)(b >> 4) & 3) ^ prefill_swz(r)) << 4) + (b & 15);
 }
 
-// Offset in pmeta of metadata byte j of row m.
-__host__ __device__ __forceinline__ int64_t prefill_meta_offset(int64_t m, int64_t j, int64_t mblocks) {
-    return (((m >> 8) * mblocks + (j >> 5)) << 13) + (m & 255) * 32 + (j & 31);
+// Offset in pmeta of metadata byte j of row m (iw: index-word bytes).
+__host__ __device__ __forceinline__ int64_t prefill_meta_offset(int64_t m, int64_t j, int64_t mblocks, int iw) {
+    return (((m >> 8) * mblocks + (j >> 5)) << 13) + ((j & 31) / iw) * 256 * iw + (m & 255) * iw + (j & 31) % iw;
 }
 
 // Element conversion to fp32 (bit-exact widening).

@@ -6,7 +6,7 @@ tile) and the product on it, through the C ABI.
   compressor that writes it directly;
 * product: against the oracle (int8 exact, floats within the stated
   tolerance), and bit for bit equal to the large-N kernel on the row-major
-  operand, which stages the same LDS bytes and runs the same MFMA sequence.
+  operand, which feeds the same operands to the same MFMA sequence.
 """
 import numpy as np
 import pytest
@@ -48,7 +48,9 @@ def expected_prefill(dt, vals_bits, meta, M, K):
     for r in range(256):
         for c in range(4):
             pv[:, :, r, c ^ swz(r)] = src[:, r, :, c]
-    pm = mb.reshape(tiles, 256, mblocks, 32).transpose(0, 2, 1, 3)
+    # metadata blocks index-word major: [tile][block][word][row][iw bytes]
+    iw = 4 if es == 1 else 2
+    pm = mb.reshape(tiles, 256, mblocks, 32 // iw, iw).transpose(0, 2, 3, 1, 4)
     return pv.reshape(-1), np.ascontiguousarray(pm).reshape(-1)
 
 
