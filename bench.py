@@ -2,26 +2,30 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]
 
-Headline workload: int8 2:4 SpMM with M = K = N = 4096 (A uniform in
-[-127, 127] pruned 2:4 by magnitude, B uniform int8, int32 accumulate).  One
-step is the whole hot path over one batch: prune + compress A on the GPU
-straight into the packed prefill layout (the large-N kernel's LDS image of
-each 256-row tile), then C = expand(packed) x B on the large-N kernel.
-`value` is dense-equivalent throughput 2*M*N*K / step time, inputs resident
-in HBM before the timed region.  The row-major product of the same operand
-is timed beside it.
+Headline workload: the largest configuration, the bf16 prefill-shape 2:4
+SpMM M=28672 K=8192 N=2048 (A ~ N(0, 0.02^2) magnitude-pruned 2:4 along K,
+B ~ N(0, 1), fp32 accumulate).  One step is the whole hot path over one
+batch: prune + compress A on the GPU straight into the packed prefill layout
+(the large-N kernel's LDS image of each tile), then C = expand(packed) x B on
+the large-N kernel.  `value` is dense-equivalent throughput 2*M*N*K / step
+time, inputs resident in HBM before the timed region.  The row-major product
+of the same operand is timed beside it.
 
 Also printed, in the same JSON line:
 * roofline: the SpMM kernel's own launch duration from HIP events recorded on
-  the stream it runs on; achieved = algorithmic ops (M*N*K: two ops per
-  stored non-zero product) / duration, against the dense int8 MFMA peak;
-  traffic from the committed rocprofv3 counter summary if it was taken on the
-  current kernel source, else null;
-* cpu_baseline: the CPU oracle (plain C, fp64/int64) timed on this host on a
-  bounded sample of rows of the same workload;
-* workloads: kernel time and roofline fraction of the other four shapes
-  (small-N ones rotate >= 1 GiB of operand copies so the 256 MB Infinity Cache
-  cannot serve repeated reads).
+  the stream it runs on; achieved = algorithmic flops (M*N*K: two per stored
+  non-zero product) / duration, against the dense bf16 MFMA peak; traffic
+  from the committed rocprofv3 counter summary if it was taken on the current
+  kernel source, else null;
+* cpu_baseline: the CPU oracle (plain C, fp64) timed on this host on a
+  bounded sample of rows of the same workload, checked against the GPU rows;
+* oracle_baselines: the oracle on every configuration (single thread for the
+  three small ones, all threads for the two large ones on row samples), with
+  its compression / split timed apart from its product;
+* workloads: kernel time and roofline fraction of the other shapes (small-N
+  ones rotate >= 1 GiB of operand copies so the 256 MB Infinity Cache cannot
+  serve repeated reads), each small-N line also against the measured
+  streaming-read rate of the same number of bytes.
 """
 from __future__ import annotations
 
@@ -76,41 +80,64 @@ def traffic_for(workload: str, kernel: str):
     return e.get("bytes_per_launch")
 
 
-def cpu_baseline(w, a_cpu, b_cpu, target_s: float):
-    """The oracle on the first R rows of the workload, R sized to about target_s."""
-    import numpy as np
+_ORACLE_DEFAULT_THREADS = {}
 
+
+def cpu_baseline(w, a_cpu, b_cpu, target_s: float, threads: int = 0):
+    """The oracle on the first R rows of the workload, R sized to about
+    target_s of its product (all rows if they take less).  Compression (or the
+    residual split) and the product are timed apart.  threads = 0: all host
+    threads.  Returns the record and (rows, C, S) of the sample."""
     import oracle
     import workloads as W
     a, b = W.bits(a_cpu), W.bits(b_cpu)
+    # all threads = the OpenMP default (OMP_NUM_THREADS where it is set)
+    default = _ORACLE_DEFAULT_THREADS.setdefault("n", oracle.num_threads())
+    oracle.set_num_threads(threads if threads > 0 else default)
 
     def run(rows):
         t0 = time.perf_counter()
         if w.residual:
             v, m, rp, col, rv = oracle.split(w.dtype, a[:rows])
-            c, _ = oracle.spmm_residual(w.dtype, v, m, rp, col, rv, b, w.K)
+            t1 = time.perf_counter()
+            c, sb = oracle.spmm_residual(w.dtype, v, m, rp, col, rv, b, w.K)
         else:
             v, m = oracle.compress(w.dtype, a[:rows])
-            c, _ = oracle.spmm(w.dtype, v, m, b, w.K)
-        return time.perf_counter() - t0, c
+            t1 = time.perf_counter()
+            c, sb = oracle.spmm(w.dtype, v, m, b, w.K)
+        return t1 - t0, time.perf_counter() - t1, c, sb
 
-    rows = 8
-    t, c = run(rows)
-    # grow the sample until it takes about target_s (the first calls are
-    # dominated by fixed costs such as converting B, so scale in steps)
-    while t < 0.5 * target_s and rows < w.M:
-        rows = int(max(rows + 1, min(w.M, rows * min(8.0, 0.9 * target_s / max(t, 1e-6)))))
-        t, c = run(rows)
+    rows = min(w.M, 8)
+    tc, tp, c, sb = run(rows)
+    # grow the sample until its product takes about target_s (the first calls
+    # are dominated by fixed costs such as converting B, so scale in steps)
+    while tp < 0.5 * target_s and rows < w.M:
+        rows = int(max(rows + 1, min(w.M, rows * min(8.0, 0.9 * target_s / max(tp, 1e-6)))))
+        tc, tp, c, sb = run(rows)
+    cores = oracle.num_threads()
+    oracle.set_num_threads(default)
     return {
-        "value": 2.0 * rows * w.N * w.K / t / 1e12,
+        "value": 2.0 * rows * w.N * w.K / tp / 1e12,
         "unit": "TFLOP/s",
-        "cores": oracle.num_threads(),
+        "cores": cores,
         "kind": "oracle",
-        "sample": "first %d of %d rows of A with all of B (%s + product), %.1f s" % (
-            rows, w.M, "split" if w.residual else "prune/compress", t),
-        "seconds": t,
+        "sample": "first %d of %d rows of A with all of B: product %.2f s (dense-equivalent rate), "
+                  "%s %.2f s" % (rows, w.M, tp, "split" if w.residual else "prune/compress", tc),
+        "product_seconds": tp,
+        ("split_seconds" if w.residual else "compress_seconds"): tc,
         "rows": rows,
-    }, (rows, c)
+    }, (rows, c, sb)
+
+
+def sample_matches(dtype: str, c_gpu, c_ref, s_ref) -> bool:
+    """The GPU rows against the oracle's at the parity bar: int8 exact;
+    floats relative Frobenius error <= 1e-3 and |err| <= 1e-2 * sum|a b|."""
+    import numpy as np
+    if dtype == "i8":
+        return bool(np.array_equal(np.asarray(c_gpu).astype(np.int64), c_ref))
+    c = np.asarray(c_gpu, dtype=np.float64)
+    fro = np.linalg.norm(c - c_ref) / max(np.linalg.norm(c_ref), 1e-300)
+    return bool(fro <= 1e-3 and (np.abs(c - c_ref) <= 1e-2 * s_ref).all())
 
 
 def time_kernel(fn, iters: int, stream) -> float:
@@ -147,28 +174,34 @@ def graph_time(launches, reps: int, stream) -> float:
     return e0.elapsed_time(e1) * 1e-3 / (reps * len(launches))
 
 
-def read_bandwidth_GBps() -> float:
-    """Achievable HBM read rate on this device: a 2 GiB read-only reduction."""
+_READ_BW = {}
+
+
+def read_bandwidth_GBps(nbytes: int, reps: int = 2) -> float:
+    """Achievable read rate (GB/s) for a stream of nbytes: the library's
+    streaming-read probe over copies of that size rotated through >= 1 GiB
+    (so the Infinity Cache serves no repeated read), launched like the
+    workloads (one HIP graph of back-to-back launches)."""
+    import numpy as np
     import torch
-    x = torch.ones(512 << 20, dtype=torch.float32, device="cuda")
-    for _ in range(2):
-        x.sum()
-    torch.cuda.synchronize()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(5):
-        x.sum()
-    e1.record()
-    e1.synchronize()
-    s = e0.elapsed_time(e1) * 1e-3 / 5
-    n = x.numel() * 4
-    del x
+
+    import structured_sparse_gemm_amd as ssg
+    nbytes = max(16, (int(nbytes) + 15) // 16 * 16)
+    if nbytes in _READ_BW:
+        return _READ_BW[nbytes]
+    copies = max(2, int(np.ceil((1 << 30) / nbytes)))
+    bufs = [torch.zeros(nbytes // 4, dtype=torch.int32, device="cuda") for _ in range(copies)]
+    sink = torch.zeros(max(1, ssg.ssg_stream_read_sink_words(nbytes)), dtype=torch.int32, device="cuda")
+    n = max(copies, 50)
+    s = graph_time([lambda i=i: ssg.ssg_stream_read(bufs[i % copies], sink) for i in range(n)], reps,
+                   torch.cuda.current_stream())
+    del bufs, sink
     torch.cuda.empty_cache()
-    return n / s / 1e9
+    _READ_BW[nbytes] = nbytes / s / 1e9
+    return _READ_BW[nbytes]
 
 
-def bench_workload(key: str, iters: int, read_GBps: float, delta: bool = False, dense_cmp: bool = True,
+def bench_workload(key: str, iters: int, delta: bool = False, dense_cmp: bool = True,
                    packed: bool = False, nm=None, prefill: bool = False):
     """Kernel-level numbers for one workload (compression outside the timing),
     next to a dense GEMM of the same shape from the vendor library.  With
@@ -248,10 +281,17 @@ def bench_workload(key: str, iters: int, read_GBps: float, delta: bool = False, 
     if w.klass == "large_n":
         r["frac_dense_peak"] = flops / s / 1e12 / PEAK[w.dtype]
         r["frac_sparse_peak"] = r["frac_dense_peak"] / 2
+        # roofline of the kernel: algorithmic ops (two per stored product) over
+        # the launch duration, against the dense MFMA peak of the dtype
+        r["roofline"] = {"bound": "mfma", "achieved": flops / 2 / s / 1e12, "peak": PEAK[w.dtype],
+                         "unit": "TFLOP/s", "frac": flops / 2 / s / 1e12 / PEAK[w.dtype],
+                         "traffic": traffic_for(key, "spmm_large_n") if prefill else None}
     else:
         r["frac_hbm_weights"] = wbytes / s / 1e9 / PEAK["hbm_GBps"]
         r["frac_hbm_all_bytes"] = (wbytes + bbytes + cbytes) / s / 1e9 / PEAK["hbm_GBps"]
-        r["frac_measured_read_bw_weights"] = wbytes / s / 1e9 / read_GBps
+        rbw = read_bandwidth_GBps(wbytes)
+        r["measured_read_GBps_same_bytes"] = rbw
+        r["frac_measured_read_bw_weights"] = wbytes / s / 1e9 / rbw
     del sets, ops, out
     torch.cuda.empty_cache()
     if not dense_cmp:
@@ -365,10 +405,11 @@ def crossover(iters: int) -> dict:
 def main() -> int:
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="oracle sample size, in seconds of CPU work")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-oracle-table", action="store_true", help="skip the oracle timings of the other configs")
     p.add_argument("--no-workloads", action="store_true", help="skip the per-workload table")
     p.add_argument("--workload-iters", type=int, default=0,
                    help="launches per workload in the table (default 200 for small N, 20 for large N)")
@@ -404,7 +445,7 @@ def main() -> int:
         torch.cuda.synchronize()
         del src, dst
 
-    key = "c2"
+    key = "c4"
     w = W.WORKLOADS[key]
     print("bench: %s" % w.title, file=sys.stderr, flush=True)
     a_cpu, b_cpu = W.gen_a(w), W.gen_b(w)
@@ -412,7 +453,8 @@ def main() -> int:
     vb, mb = ssg.ssg_prefill_packed_sizes(A.dtype, w.M, w.K)
     vals = torch.empty(vb, dtype=torch.uint8, device="cuda")       # packed prefill layout
     meta = torch.empty(mb, dtype=torch.uint8, device="cuda")
-    C = torch.empty((w.M, w.N), dtype=torch.int32, device="cuda")
+    out_dt = torch.int32 if w.dtype == "i8" else torch.float32
+    C = torch.empty((w.M, w.N), dtype=out_dt, device="cuda")
     stream = torch.cuda.current_stream()
 
     def step():
@@ -445,9 +487,11 @@ def main() -> int:
         torch.cuda.synchronize()
         graph.replay()
         torch.cuda.synchronize()
-        graph_ok &= bool(torch.equal(vals, ref_vals) and torch.equal(meta, ref_meta) and torch.equal(C, ref_C))
+        graph_ok &= bool(torch.equal(vals, ref_vals) and torch.equal(meta, ref_meta) and
+                         torch.equal(C.view(torch.int32), ref_C.view(torch.int32)))
         step()
         torch.cuda.synchronize()
+    del ref_vals, ref_meta
 
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -455,6 +499,7 @@ def main() -> int:
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms = (t1 - t0) * 1e3 / args.steps
+    del graph
 
     # kernel durations: back-to-back launches between two HIP events on the
     # stream the kernels run on
@@ -466,34 +511,37 @@ def main() -> int:
     C_rm = ssg.spmm(rvals, rmeta, B, algo=ssg.SSG_ALGO_LARGE_N)
     torch.cuda.synchronize()
     rowmajor = {"spmm_us": time_kernel(lambda i: ssg.ssg_spmm_2to4(rvals, rmeta, B, C_rm), reps, stream) * 1e6,
-                "same_result_bits": bool(torch.equal(C_rm, C))}
+                "same_result_bits": bool(torch.equal(C_rm.view(torch.int32), C.view(torch.int32)))}
     del rvals, rmeta, C_rm
+    torch.cuda.empty_cache()
     flops = 2.0 * w.M * w.N * w.K
-    algo_ops = float(w.M) * w.N * w.K          # two ops per stored product, half the positions stored
+    algo_ops = float(w.M) * w.N * w.K          # two per stored product, half the positions stored
     print("bench: step %.3f ms (graph replay; compress %.1f us, spmm %.1f us)" % (ms, comp_s * 1e6, spmm_s * 1e6),
           file=sys.stderr, flush=True)
 
     dense_note = None
     try:
-        torch._int_mm(A, B)
+        torch.matmul(A, B)
         torch.cuda.synchronize()
-        dense_s = time_kernel(lambda i: torch._int_mm(A, B), reps, stream)
+        dense_s = time_kernel(lambda i: torch.matmul(A, B), reps, stream)
         dense_note = {"dense_gemm_us": dense_s * 1e6, "speedup_spmm_vs_dense": dense_s / spmm_s,
-                      "dense_gemm": "torch _int_mm (int8 x int8 -> int32) on the dense weights, back-to-back launches"}
+                      "dense_gemm": "torch matmul (bf16 x bf16 -> bf16, vendor library) on the dense weights, "
+                                    "back-to-back launches"}
     except RuntimeError as e:
         dense_note = {"dense_gemm": "unavailable: %s" % str(e).splitlines()[0][:120]}
+    torch.cuda.empty_cache()
 
     roofline = {
-        "kernel": "spmm_large_n on the packed prefill layout (int8 sparse MFMA 32x32x64)",
+        "kernel": "spmm_large_n on the packed prefill layout (bf16 sparse MFMA 32x32x32)",
         "bound": "mfma",
         "achieved": algo_ops / spmm_s / 1e12,
-        "peak": PEAK["i8"],
+        "peak": PEAK[w.dtype],
         "unit": "TFLOP/s",
-        "frac": algo_ops / spmm_s / 1e12 / PEAK["i8"],
+        "frac": algo_ops / spmm_s / 1e12 / PEAK[w.dtype],
         "traffic": traffic_for(key, "spmm_large_n"),
         "launch_us": spmm_s * 1e6,
-        "dense_equiv_frac_of_dense_peak": flops / spmm_s / 1e12 / PEAK["i8"],
-        "algorithmic_ops_per_launch": algo_ops,
+        "dense_equiv_frac_of_dense_peak": flops / spmm_s / 1e12 / PEAK[w.dtype],
+        "algorithmic_flops_per_launch": algo_ops,
     }
     out = {
         "metric": METRIC,
@@ -506,12 +554,13 @@ def main() -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "i8",
+        "dtype": w.dtype,
         "data": "synthetic",
-        "config": {"workload": "int8 2:4 SpMM M=K=N=4096; step = prune+compress A (packed prefill layout), "
-                               "then SpMM (int32 out)",
+        "config": {"workload": "bf16 2:4 SpMM M=28672 K=8192 N=2048 (prefill shape); step = prune+compress A "
+                               "(packed prefill layout), then SpMM (fp32 out)",
                    "M": w.M, "K": w.K, "N": w.N, "seeds": [1000 + w.index, 2000 + w.index]},
         "spmm_only_dense_equiv_TFLOPs": flops / spmm_s / 1e12,
+        "spmm_us": spmm_s * 1e6,
         "compress_us": comp_s * 1e6,
         "rowmajor_operand": rowmajor,
         "launch": "one HIP graph of the %d timed steps (each: compress + SpMM), replayed once; check replays "
@@ -522,48 +571,58 @@ def main() -> int:
     }
     if not args.no_cpu_baseline:
         print("bench: cpu baseline (oracle) ...", file=sys.stderr, flush=True)
-        cb, (rows, cref) = cpu_baseline(w, a_cpu, b_cpu, args.cpu_seconds)
-        import numpy as np
-        cb["sample_matches_gpu"] = bool(np.array_equal(C[:rows].cpu().numpy().astype(np.int64), cref))
+        cb, (rows, cref, sref) = cpu_baseline(w, a_cpu, b_cpu, args.cpu_seconds)
+        cb["sample_matches_gpu"] = sample_matches(w.dtype, C[:rows].cpu().numpy(), cref, sref)
         out["cpu_baseline"] = cb
-    del A, B, vals, meta, C
+    del A, B, vals, meta, C, a_cpu, b_cpu
     torch.cuda.empty_cache()
+    if not args.no_cpu_baseline and not args.no_oracle_table:
+        # the oracle on every configuration: one thread for the three small
+        # ones (whole), all threads on row samples of the two large ones
+        table = {}
+        for k, threads, secs in (("c1", 1, 1.0), ("c3", 1, 3.0), ("c5", 1, 3.0), ("c2", 0, 3.0)):
+            wk = W.WORKLOADS[k]
+            print("bench: oracle on %s ..." % k, file=sys.stderr, flush=True)
+            rec, _ = cpu_baseline(wk, W.gen_a(wk), W.gen_b(wk), secs, threads=threads)
+            table[k] = rec
+        table["c4"] = {kk: vv for kk, vv in out.get("cpu_baseline", {}).items()}
+        out["oracle_baselines"] = table
     if not args.no_workloads:
-        rbw = read_bandwidth_GBps()
-        out["measured_read_GBps"] = rbw
+        out["measured_read_GBps_1GiB"] = read_bandwidth_GBps(1 << 30)
         table = {}
         only = [k for k in args.only.split(",") if k]
-        for k in ("c1", "c3", "c4", "c5", "c3f8", "c4f8", "c3nm", "c3w4"):
+        for k in ("c1", "c2", "c3", "c4", "c5", "c3f8", "c4f8", "c3nm", "c3w4"):
             if only and k not in only:
                 continue
             if k in ("c3nm", "c3w4"):
                 pats = ((1, 4), (2, 4), (2, 8), (4, 8)) if k == "c3nm" else ((2, 4), (2, 8), (4, 8))
                 for i, (n, m) in enumerate(pats):
                     print("bench: workload %s, %d:%d ..." % (k, n, m), file=sys.stderr, flush=True)
-                    table["%s_%d:%d" % (k, n, m)] = bench_workload(k, args.workload_iters or 200, rbw,
+                    table["%s_%d:%d" % (k, n, m)] = bench_workload(k, args.workload_iters or 200,
                                                                    dense_cmp=i == 0, nm=(n, m))
                     print("bench: workload %s, %d:%d, packed decode layout ..." % (k, n, m), file=sys.stderr,
                           flush=True)
-                    table["%s_%d:%d_packed" % (k, n, m)] = bench_workload(k, args.workload_iters or 200, rbw,
+                    table["%s_%d:%d_packed" % (k, n, m)] = bench_workload(k, args.workload_iters or 200,
                                                                           dense_cmp=False, nm=(n, m), packed=True)
                 continue
             print("bench: workload %s ..." % k, file=sys.stderr, flush=True)
             it = args.workload_iters or (200 if W.WORKLOADS[k].klass != "large_n" else 20)
-            table[k] = bench_workload(k, it, rbw)
-            if W.WORKLOADS[k].klass == "large_n" and k != "c1":
+            if k != key:                                 # the headline's row-major product is timed above
+                table[k] = bench_workload(k, it)
+            if W.WORKLOADS[k].klass == "large_n" and k not in ("c1", key):
                 print("bench: workload %s, packed prefill layout ..." % k, file=sys.stderr, flush=True)
-                table[k + "_prefill"] = bench_workload(k, it, rbw, dense_cmp=False, prefill=True)
+                table[k + "_prefill"] = bench_workload(k, it, dense_cmp=False, prefill=True)
             if W.WORKLOADS[k].residual:
                 print("bench: workload %s, delta-coded residual ..." % k, file=sys.stderr, flush=True)
-                table[k + "_delta"] = bench_workload(k, it, rbw, delta=True, dense_cmp=False)
+                table[k + "_delta"] = bench_workload(k, it, delta=True, dense_cmp=False)
                 print("bench: workload %s, packed decode layout ..." % k, file=sys.stderr, flush=True)
-                table[k + "_packed"] = bench_workload(k, it, rbw, dense_cmp=False, packed=True)
+                table[k + "_packed"] = bench_workload(k, it, dense_cmp=False, packed=True)
                 print("bench: workload %s, packed decode layout, delta-coded residual ..." % k, file=sys.stderr,
                       flush=True)
-                table[k + "_delta_packed"] = bench_workload(k, it, rbw, delta=True, dense_cmp=False, packed=True)
+                table[k + "_delta_packed"] = bench_workload(k, it, delta=True, dense_cmp=False, packed=True)
             elif W.WORKLOADS[k].klass == "small_n" and W.WORKLOADS[k].N == 16:
                 print("bench: workload %s, packed decode layout ..." % k, file=sys.stderr, flush=True)
-                table[k + "_packed"] = bench_workload(k, it, rbw, dense_cmp=False, packed=True)
+                table[k + "_packed"] = bench_workload(k, it, dense_cmp=False, packed=True)
         out["workloads"] = table
     print(json.dumps(out))
     return 0

@@ -73,7 +73,7 @@ typedef enum {
     SSG_ERR_STRIDE = 3,     /* a leading dimension smaller than its row */
     SSG_ERR_DTYPE = 4,      /* unsupported element type or (input, output) pair */
     SSG_ERR_FORMAT = 5,     /* inconsistent sparse operand arguments (nnz_r < 0 or above 2^31 - 1) */
-    SSG_ERR_WORKSPACE = 6,  /* workspace smaller than ssg_spmm_workspace_bytes() */
+    SSG_ERR_WORKSPACE = 6,  /* a needed workspace is missing, too small or misaligned */
     SSG_ERR_HIP = 7,        /* a HIP runtime call failed; see ssg_last_error() */
     SSG_ERR_ALGO = 8        /* the requested algorithm cannot run this problem */
 } ssg_status;
@@ -140,10 +140,16 @@ int ssg_split_fill(int dt, int64_t M, int64_t K, const void* A, int64_t lda,
                    void* vals, int64_t ldv, uint8_t* meta, int64_t ldm,
                    const int32_t* row_ptr, int32_t* col, void* rvals, void* stream);
 
-/* Workspace the SpMM calls need for this problem (bytes; may be 0).  It is
- * 0 except for 0 < N < 16, where it holds B padded to 16 zero-extended
- * columns (K * 16 elements, rounded up to 256 bytes; 16-byte aligned): the
- * decode kernels then take B as one contiguous K x 16 block. */
+/* Workspace the SpMM calls may need for this problem (bytes; may be 0).  It
+ * is 0 except for 0 < N < 16 (and M > 0, K % 4 == 0, K * 16 elements under
+ * 2^31 bytes), where it holds B padded to 16 zero-extended columns (K * 16
+ * elements, rounded up to 256 bytes): the decode kernels then take B as one
+ * contiguous K x 16 block.  A product requires it (16-byte aligned, at least
+ * this size; else SSG_ERR_WORKSPACE) only when it takes that padded path:
+ * algorithm AUTO or SMALL_N, and an operand the small-N kernel accepts
+ * (vals rows 16-byte aligned, K a multiple of its k-step, residual arrays
+ * aligned).  Forced GENERIC or LARGE_N calls never touch it and may pass
+ * ws = NULL.  The workspace is used on `stream` only. */
 size_t ssg_spmm_workspace_bytes(int ab, int64_t M, int64_t N, int64_t K);
 
 /* C = expand(vals, meta) x B.  (ab, c) must be (SSG_F16, SSG_F32),
@@ -413,6 +419,18 @@ int ssg_spmm_2to4_residual_delta_ex(int algo, int ab, int c, int64_t M, int64_t 
 int ssg_spmm_select_algo(int ab, int64_t M, int64_t N, int64_t K,
                          const void* vals, int64_t ldv, const uint8_t* meta, int64_t ldm,
                          const void* B, int64_t ldb, const void* C, int64_t ldc);
+
+/* Measurement helper (not part of the product): one streaming read of
+ * `bytes` bytes of device memory at src (16-byte aligned, bytes a multiple
+ * of 16), 16 bytes per lane per load, non-temporal, every byte once.  Its
+ * rate is the achievable read bandwidth the bandwidth-bound products ("2:4 in
+ * the Memory-Bound Regime" of "Chapter 26 -- Sparsity: The Hardware View":
+ * the bytes streamed set the time) are compared against.  sink is device
+ * memory of ssg_stream_read_sink_words(bytes) uint32 words; it is written
+ * only when a workgroup's fold of the data hits one fixed value, which keeps
+ * the loads from being optimised away. */
+int64_t ssg_stream_read_sink_words(int64_t bytes);
+int ssg_stream_read(const void* src, int64_t bytes, uint32_t* sink, void* stream);
 
 #ifdef __cplusplus
 }

@@ -106,6 +106,8 @@ def _load():
             lib.orc_spmm_csr.argtypes = [ctypes.c_int, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _i64, _vp, _vp, _vp,
                                          _i64]
             lib.orc_num_threads.restype = ctypes.c_int
+            lib.orc_set_num_threads.argtypes = [ctypes.c_int]
+            lib.orc_set_num_threads.restype = None
             _lib = lib
     return _lib
 
@@ -413,3 +415,8 @@ def spmm_nm(dt: str, n: int, m: int, vals, mask, B, K: int):
 
 def num_threads() -> int:
     return int(_load().orc_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    """Threads of the oracle's parallel loops from now on (timing only)."""
+    _load().orc_set_num_threads(int(n))

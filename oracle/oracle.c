@@ -770,3 +770,13 @@ int orc_num_threads(void) {
     return 1;
 #endif
 }
+
+/* Threads the parallel loops use from now on (n >= 1); for timing the
+ * oracle on one core as well as on all of them. */
+void orc_set_num_threads(int n) {
+#ifdef _OPENMP
+    if (n >= 1) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}

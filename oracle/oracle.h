@@ -182,6 +182,7 @@ int orc_spmm_nm_w4a16(int nm_n, int nm_m, int64_t M, int64_t N, int64_t K, const
 
 /* Number of threads an OpenMP parallel region would use (1 without OpenMP). */
 int orc_num_threads(void);
+void orc_set_num_threads(int n);
 
 #ifdef __cplusplus
 }

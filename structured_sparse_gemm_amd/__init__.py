@@ -35,6 +35,7 @@ __all__ = [
     "compress_prefill", "pack_prefill", "spmm_prefill",
     "ssg_compress_nm", "ssg_decompress_nm", "ssg_spmm_nm", "compress_nm", "decompress_nm", "spmm_nm",
     "ssg_nm_packed_sizes", "ssg_pack_nm_decode", "ssg_spmm_nm_packed", "pack_nm", "spmm_nm_packed",
+    "ssg_stream_read_sink_words", "ssg_stream_read",
     "SSG_ALGO_AUTO", "SSG_ALGO_GENERIC", "SSG_ALGO_SMALL_N", "SSG_ALGO_LARGE_N", "library_path",
 ]
 
@@ -166,17 +167,32 @@ def ssg_spmm_workspace_bytes(dtype: torch.dtype, M: int, N: int, K: int) -> int:
     return int(_lib().ssg_spmm_workspace_bytes(_DT[dtype], M, N, K))
 
 
-def _workspace(dt_t: torch.dtype, M, N, K, device, ws):
+def _torch_stream(t: torch.Tensor, stream):
+    """The torch stream object of a `stream` argument (None: the current stream;
+    a raw hipStream_t handle is wrapped)."""
+    if stream is None:
+        return torch.cuda.current_stream(t.device)
+    if isinstance(stream, torch.cuda.Stream):
+        return stream
+    return torch.cuda.ExternalStream(int(stream), device=t.device)
+
+
+def _workspace(dt_t: torch.dtype, M, N, K, device, ws, stream=None):
+    """The caller's workspace, or a new one allocated on the stream the
+    kernels run on, so the caching allocator does not hand its memory to
+    another stream while they may still use it."""
     need = ssg_spmm_workspace_bytes(dt_t, M, N, K)
-    if ws is None and need > 0:
-        ws = torch.empty(need, dtype=torch.uint8, device=device)
+    if ws is None and need > 0 and torch.device(device).type == "cuda":   # host tensors fail in _ptr
+        probe = torch.empty(0, device=device)
+        with torch.cuda.stream(_torch_stream(probe, stream)):
+            ws = torch.empty(need, dtype=torch.uint8, device=device)
     return ws, (ws.numel() * ws.element_size() if ws is not None else 0)
 
 
 def ssg_spmm_2to4(vals, meta, B, C, ws=None, algo: int = SSG_ALGO_AUTO, stream=None) -> None:
     ab = _dtype(vals)
     M, N, K = vals.shape[0], B.shape[1], B.shape[0]
-    ws, wsb = _workspace(vals.dtype, M, N, K, vals.device, ws)
+    ws, wsb = _workspace(vals.dtype, M, N, K, vals.device, ws, stream)
     _check(_lib().ssg_spmm_2to4_ex(algo, ab, _OUT[ab][0], M, N, K, _ptr(vals, "vals"), _ld(vals, "vals"),
                                    _ptr(meta, "meta"), _ld(meta, "meta"), _ptr(B, "B"), _ld(B, "B"), _ptr(C, "C"),
                                    _ld(C, "C"), _ptr(ws, "ws"), wsb, _stream(C, stream)), "ssg_spmm_2to4")
@@ -187,7 +203,7 @@ def ssg_spmm_2to4_residual(vals, meta, row_ptr, col, rvals, B, C, ws=None, algo:
     ab = _dtype(vals)
     M, N, K = vals.shape[0], B.shape[1], B.shape[0]
     nnz = int(col.numel()) if col is not None else 0
-    ws, wsb = _workspace(vals.dtype, M, N, K, vals.device, ws)
+    ws, wsb = _workspace(vals.dtype, M, N, K, vals.device, ws, stream)
     _check(_lib().ssg_spmm_2to4_residual_ex(algo, ab, _OUT[ab][0], M, N, K, _ptr(vals, "vals"), _ld(vals, "vals"),
                                             _ptr(meta, "meta"), _ld(meta, "meta"), _ptr(row_ptr, "row_ptr"),
                                             _ptr(col, "col"), _ptr(rvals, "rvals"), nnz, _ptr(B, "B"), _ld(B, "B"),
@@ -200,7 +216,7 @@ def ssg_spmm_2to4_residual_delta(vals, meta, drow_ptr, dcol, dvals, B, C, ws=Non
     ab = _dtype(vals)
     M, N, K = vals.shape[0], B.shape[1], B.shape[0]
     nnz = int(dcol.numel()) if dcol is not None else 0
-    ws, wsb = _workspace(vals.dtype, M, N, K, vals.device, ws)
+    ws, wsb = _workspace(vals.dtype, M, N, K, vals.device, ws, stream)
     _check(_lib().ssg_spmm_2to4_residual_delta_ex(algo, ab, _OUT[ab][0], M, N, K, _ptr(vals, "vals"),
                                                   _ld(vals, "vals"), _ptr(meta, "meta"), _ld(meta, "meta"),
                                                   _ptr(drow_ptr, "drow_ptr"), _ptr(dcol, "dcol"),
@@ -303,6 +319,17 @@ def ssg_spmm_select_algo(vals, meta, B, C) -> int:
     return int(_lib().ssg_spmm_select_algo(_dtype(vals), vals.shape[0], B.shape[1], B.shape[0], _ptr(vals, "vals"),
                                            _ld(vals, "vals"), _ptr(meta, "meta"), _ld(meta, "meta"), _ptr(B, "B"),
                                            _ld(B, "B"), _ptr(C, "C"), _ld(C, "C")))
+
+
+def ssg_stream_read_sink_words(nbytes: int) -> int:
+    return int(_lib().ssg_stream_read_sink_words(nbytes))
+
+
+def ssg_stream_read(src: torch.Tensor, sink: torch.Tensor, stream=None) -> None:
+    """Measurement helper: one streaming read of every byte of src."""
+    nbytes = src.numel() * src.element_size()
+    _check(_lib().ssg_stream_read(_ptr(src, "src"), nbytes, _ptr(sink, "sink"), _stream(src, stream)),
+           "ssg_stream_read")
 
 
 def ssg_compress_nm(A: torch.Tensor, n: int, m: int, vals: torch.Tensor, mask: torch.Tensor, stream=None) -> None:

@@ -1135,9 +1135,10 @@ bool ring_ok(const SpmmArgs& a, int tm) {
     const uintptr_t bp = reinterpret_cast<uintptr_t>(a.B), mp = reinterpret_cast<uintptr_t>(a.meta);
     const int P = tm == 1 ? ring_depth<DT, 1>(a) : tm == 2 ? ring_depth<DT, 2>(a) : tm == 3 ? ring_depth<DT, 3>(a)
                                                                                           : ring_depth<DT, 4>(a);
-    // B rows of 16 elements (N < 16: columns past N are computed and never
-    // stored; the host pads a narrower B into the workspace)
-    return P > 0 && a.N <= 16 && a.ldb == 16 && bp % 16 == 0 && mp % 4 == 0 && a.ldm % 4 == 0 &&
+    // B rows of 16 readable elements: N == 16, or a narrower B that the host
+    // padded into the workspace (columns past N are computed and never stored)
+    return P > 0 && (a.N == 16 || (a.N < 16 && a.b_pad16)) && a.ldb == 16 && bp % 16 == 0 && mp % 4 == 0 &&
+           a.ldm % 4 == 0 &&
            a.K * 16 * T::ES < 0x7fffffff && a.M * a.ldv * T::ES < 0x7fffffff && a.M * a.ldm < 0x7fffffff;
 }
 

@@ -51,6 +51,8 @@ struct SpmmArgs {
     int64_t nnz_r;
     const void* B; int64_t ldb;
     void* C; int64_t ldc;       // fp32 or int32
+    int b_pad16;                // B is the library's copy padded to 16 columns
+                                // (readable past column N up to 16)
 };
 
 hipError_t launch_spmm_generic(const SpmmArgs& a, hipStream_t s);
@@ -102,5 +104,10 @@ void nm_packed_geometry(int dt, int n, int m, int64_t M, int64_t K, int64_t* til
                         int* mb);
 hipError_t launch_pack_nm(int dt, int n, int m, int64_t M, int64_t K, const void* vals, int64_t ldv,
                           const uint8_t* mask, int64_t ldm, void* pvals, void* pmask, hipStream_t s);
+
+// Measurement: a streaming read of `bytes` (a multiple of 16) from src; the
+// sink holds stream_read_grid(bytes) words and is written only by chance.
+int64_t stream_read_grid(int64_t bytes);
+hipError_t launch_stream_read(const void* src, int64_t bytes, uint32_t* sink, hipStream_t s);
 
 }  // namespace ssg

@@ -104,26 +104,46 @@ int pick_algo(const ssg::SpmmArgs& a) {
 }
 
 // Workspace of a product with 0 < N < 16: B padded to 16 columns, which lets
-// the decode kernels that take B as one contiguous K x 16 block run.
+// the decode kernels that take B as one contiguous K x 16 block run.  Zero
+// where that copy could not be addressed with 31-bit offsets.
 int64_t padded_b_bytes(int ab, int64_t N, int64_t K) {
-    return N > 0 && N < 16 && K > 0 ? (K * 16 * esize(ab) + 255) / 256 * 256 : 0;
+    if (!(N > 0 && N < 16 && K > 0) || K * 16 * esize(ab) >= 0x7fffffff) return 0;
+    return (K * 16 * esize(ab) + 255) / 256 * 256;
 }
 
-int run_spmm(int algo, ssg::SpmmArgs a, hipStream_t s, void* ws, size_t ws_bytes) {
+// Workspace bytes this call will use: the padded copy of B, when algorithm
+// `algo` takes the padded decode path for this problem (AUTO or SMALL_N, and
+// the small-N kernel accepts the problem with a padded B); else 0.
+int64_t pad_need(int algo, const ssg::SpmmArgs& a) {
+    if (algo != SSG_ALGO_AUTO && algo != SSG_ALGO_SMALL_N) return 0;
+    const int64_t bytes = padded_b_bytes(a.dt == ssg::DT_F16 || a.dt == ssg::DT_BF16 ? SSG_F16 : SSG_I8, a.N, a.K);
+    if (bytes == 0 || a.M <= 0) return 0;
+    ssg::SpmmArgs p = a;
+    p.B = reinterpret_cast<const void*>(uintptr_t(256));   // stands for any 16-byte aligned workspace (not read)
+    p.ldb = 16;
+    p.b_pad16 = 1;
+    return ssg::supported_small_n(p) ? bytes : 0;
+}
+
+int check_workspace(int64_t need, const void* ws, size_t ws_bytes) {
+    if (need == 0) return SSG_OK;
+    if (!ws || (int64_t)ws_bytes < need)
+        return fail(SSG_ERR_WORKSPACE, "workspace %zu < %lld bytes", ws ? ws_bytes : (size_t)0, (long long)need);
+    if (!al(ws, 16)) return fail(SSG_ERR_WORKSPACE, "workspace must be 16-byte aligned");
+    return SSG_OK;
+}
+
+// Runs the product; the caller has validated the arguments and the workspace
+// against pad_need(algo, a).
+int run_spmm(int algo, ssg::SpmmArgs a, hipStream_t s, void* ws) {
     if (a.M == 0 || a.N == 0) return SSG_OK;
     // B narrower than 16 columns: padded into the workspace for the decode kernels
-    const int64_t es = (a.dt == ssg::DT_F16 || a.dt == ssg::DT_BF16) ? 2 : 1;
-    const int64_t pad = a.N < 16 && a.K > 0 ? (a.K * 16 * es + 255) / 256 * 256 : 0;
-    if ((algo == SSG_ALGO_AUTO || algo == SSG_ALGO_SMALL_N) && pad > 0 && a.ldb != 16 && ws != nullptr &&
-        (int64_t)ws_bytes >= pad && al(ws, 16) && a.K * 16 * es < 0x7fffffff) {
-        ssg::SpmmArgs p = a;
-        p.B = ws;
-        p.ldb = 16;
-        if (ssg::supported_small_n(p)) {
-            hipError_t e = ssg::launch_pad_b(a.dt, a.K, a.N, a.B, a.ldb, ws, s);
-            if (e != hipSuccess) return hip_fail(e, "B padding launch");
-            a = p;
-        }
+    if (pad_need(algo, a) > 0) {
+        hipError_t e = ssg::launch_pad_b(a.dt, a.K, a.N, a.B, a.ldb, ws, s);
+        if (e != hipSuccess) return hip_fail(e, "B padding launch");
+        a.B = ws;
+        a.ldb = 16;
+        a.b_pad16 = 1;
     }
     if (algo == SSG_ALGO_AUTO) algo = pick_algo(a);
     hipError_t e = hipSuccess;
@@ -251,8 +271,7 @@ int ssg_split_fill(int dt, int64_t M, int64_t K, const void* A, int64_t lda, voi
 }
 
 size_t ssg_spmm_workspace_bytes(int ab, int64_t M, int64_t N, int64_t K) {
-    (void)M;
-    if (!in_dtype(ab) || N < 0 || K < 0) return 0;
+    if (!in_dtype(ab) || M <= 0 || N < 0 || K < 0 || K % 4) return 0;
     return (size_t)padded_b_bytes(ab, N, K);
 }
 
@@ -261,10 +280,10 @@ int ssg_spmm_2to4_ex(int algo, int ab, int c, int64_t M, int64_t N, int64_t K, c
                      size_t ws_bytes, void* stream) {
     int rc = check_spmm(ab, c, M, N, K, vals, ldv, meta, ldm, B, ldb, C, ldc);
     if (rc) return rc;
-    const size_t need = ssg_spmm_workspace_bytes(ab, M, N, K);
-    if (ws_bytes < need || (need > 0 && !ws)) return fail(SSG_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
-    return run_spmm(algo, make_args(ab, M, N, K, vals, ldv, meta, ldm, B, ldb, C, ldc), (hipStream_t)stream, ws,
-                    ws_bytes);
+    const ssg::SpmmArgs a = make_args(ab, M, N, K, vals, ldv, meta, ldm, B, ldb, C, ldc);
+    rc = check_workspace(pad_need(algo, a), ws, ws_bytes);
+    if (rc) return rc;
+    return run_spmm(algo, a, (hipStream_t)stream, ws);
 }
 
 int ssg_spmm_2to4(int ab, int c, int64_t M, int64_t N, int64_t K, const void* vals, int64_t ldv, const uint8_t* meta,
@@ -283,13 +302,13 @@ int ssg_spmm_2to4_residual_ex(int algo, int ab, int c, int64_t M, int64_t N, int
     if (nnz_r < 0 || nnz_r > INT32_MAX) return fail(SSG_ERR_FORMAT, "nnz_r=%lld out of range", (long long)nnz_r);
     if (M > 0 && !row_ptr) return fail(SSG_ERR_NULL, "row_ptr is NULL");
     if (nnz_r > 0 && (!col || !rvals)) return fail(SSG_ERR_NULL, "col or rvals is NULL with nnz_r > 0");
-    const size_t need = ssg_spmm_workspace_bytes(ab, M, N, K);
-    if (ws_bytes < need || (need > 0 && !ws)) return fail(SSG_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
     ssg::SpmmArgs a = make_args(ab, M, N, K, vals, ldv, meta, ldm, B, ldb, C, ldc);
     // an empty residual adds nothing: the plain 2:4 product (the residual
     // kernels may read entry 0 of a non-empty residual unconditionally)
     if (nnz_r > 0) { a.row_ptr = row_ptr; a.col = col; a.rvals = rvals; a.nnz_r = nnz_r; }
-    return run_spmm(algo, a, (hipStream_t)stream, ws, ws_bytes);
+    rc = check_workspace(pad_need(algo, a), ws, ws_bytes);
+    if (rc) return rc;
+    return run_spmm(algo, a, (hipStream_t)stream, ws);
 }
 
 int ssg_residual_delta_count(int64_t M, int64_t K, const int32_t* row_ptr, const int32_t* col, int64_t nnz_r,
@@ -330,13 +349,13 @@ int ssg_spmm_2to4_residual_delta_ex(int algo, int ab, int c, int64_t M, int64_t 
     if (nnz_d < 0 || nnz_d > INT32_MAX) return fail(SSG_ERR_FORMAT, "nnz_d=%lld out of range", (long long)nnz_d);
     if (M > 0 && !drow_ptr) return fail(SSG_ERR_NULL, "drow_ptr is NULL");
     if (nnz_d > 0 && (!dcol || !dvals)) return fail(SSG_ERR_NULL, "dcol or dvals is NULL with nnz_d > 0");
-    const size_t need = ssg_spmm_workspace_bytes(ab, M, N, K);
-    if (ws_bytes < need || (need > 0 && !ws)) return fail(SSG_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
     ssg::SpmmArgs a = make_args(ab, M, N, K, vals, ldv, meta, ldm, B, ldb, C, ldc);
     // an empty residual adds nothing: the plain 2:4 product (the residual
     // kernels may read entry 0 of a non-empty residual unconditionally)
     if (nnz_d > 0) { a.row_ptr = drow_ptr; a.dcol = dcol; a.rvals = dvals; a.nnz_r = nnz_d; }
-    return run_spmm(algo, a, (hipStream_t)stream, ws, ws_bytes);
+    rc = check_workspace(pad_need(algo, a), ws, ws_bytes);
+    if (rc) return rc;
+    return run_spmm(algo, a, (hipStream_t)stream, ws);
 }
 
 int ssg_spmm_2to4_residual_delta(int ab, int c, int64_t M, int64_t N, int64_t K, const void* vals, int64_t ldv,
@@ -584,6 +603,18 @@ int ssg_spmm_2to4_prefill(int ab, int c, int64_t M, int64_t N, int64_t K, const 
     return e == hipSuccess ? SSG_OK : hip_fail(e, "packed prefill spmm launch");
 }
 
+int64_t ssg_stream_read_sink_words(int64_t bytes) { return bytes > 0 ? ssg::stream_read_grid(bytes) : 0; }
+
+int ssg_stream_read(const void* src, int64_t bytes, uint32_t* sink, void* stream) {
+    if (bytes < 0 || bytes % 16) return fail(SSG_ERR_SHAPE, "bytes=%lld is not a non-negative multiple of 16",
+                                             (long long)bytes);
+    if (bytes == 0) return SSG_OK;
+    if (!src || !sink) return fail(SSG_ERR_NULL, "src or sink is NULL");
+    if (!al(src, 16)) return fail(SSG_ERR_STRIDE, "src must be 16-byte aligned");
+    hipError_t e = ssg::launch_stream_read(src, bytes, sink, (hipStream_t)stream);
+    return e == hipSuccess ? SSG_OK : hip_fail(e, "stream read launch");
+}
+
 int64_t ssg_nm_vals_cols(int nm_n, int nm_m, int64_t K) {
     return nm_m > 0 && nm_n >= 0 ? K / nm_m * nm_n : 0;
 }
@@ -760,3 +791,4 @@ int ssg_spmm_select_algo(int ab, int64_t M, int64_t N, int64_t K, const void* va
 }
 
 }  // extern "C"
+

@@ -403,6 +403,53 @@ def test_spmm_narrow_b(dt, shape):
     check_product(dt, C.cpu().numpy(), cref, sref, "narrow %s %s" % (dt, shape))
 
 
+@pytest.mark.parametrize("dt", ["f16", "i8"])
+def test_spmm_narrow_b_with_row_stride_16(dt):
+    # N < 16 inside rows of 16 elements: the product still pads B (it reads
+    # nothing past the last row's N-th element) and the result is exact/within tolerance
+    M, K, N = 300, 1024, 5
+    a = U.random_matrix(dt, M, K, "normal", seed=71)
+    b = U.random_matrix(dt, K, N, "normal", seed=73)
+    vals, meta = oracle.compress(dt, a)
+    B = strided(to_dev(b, dt), 16 - N)
+    assert B.stride(0) == 16
+    C = ssg.spmm(to_dev(vals, dt), dev_or_empty(meta), B)
+    cref, sref = oracle.spmm(dt, vals, meta, b, K)
+    check_product(dt, C.cpu().numpy(), cref, sref, "narrow B, ldb 16, %s" % dt)
+
+
+def test_spmm_narrow_b_on_a_side_stream():
+    # the workspace is allocated on the stream the kernels run on
+    M, K, N = 1000, 2048, 3
+    a = U.random_matrix("f16", M, K, "normal", seed=75)
+    b = U.random_matrix("f16", K, N, "normal", seed=77)
+    vals, meta = oracle.compress("f16", a)
+    V, Mt, B = to_dev(vals, "f16"), dev_or_empty(meta), to_dev(b, "f16")
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    C = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    with torch.cuda.stream(side):
+        C.record_stream(side)
+    ssg.ssg_spmm_2to4(V, Mt, B, C, stream=side)
+    side.synchronize()
+    cref, sref = oracle.spmm("f16", vals, meta, b, K)
+    check_product("f16", C.cpu().numpy(), cref, sref, "narrow B on a side stream")
+
+
+def test_forced_kernels_need_no_workspace():
+    # only the padded decode path uses the workspace: forced generic and
+    # large-N products of a narrow B run without one
+    M, K, N = 64, 256, 5
+    a = U.random_matrix("i8", M, K, "normal", seed=79)
+    b = U.random_matrix("i8", K, N, "normal", seed=81)
+    vals, meta = oracle.compress("i8", a)
+    cref, _ = oracle.spmm("i8", vals, meta, b, K)
+    for algo in (ssg.SSG_ALGO_GENERIC,):
+        C = torch.empty((M, N), dtype=torch.int32, device="cuda")
+        ssg.ssg_spmm_2to4(to_dev(vals, "i8"), dev_or_empty(meta), to_dev(b, "i8"), C, ws=None, algo=algo)
+        assert np.array_equal(C.cpu().numpy().astype(np.int64), cref)
+
+
 @pytest.mark.parametrize("dt", DTS)
 def test_spmm_residual_narrow_b(dt):
     M, K, N = 300, 1024, 8
