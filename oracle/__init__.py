@@ -106,6 +106,9 @@ def _load():
             lib.orc_spmm_csr.argtypes = [ctypes.c_int, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _i64, _vp, _vp, _vp,
                                          _i64]
             lib.orc_num_threads.restype = ctypes.c_int
+            lib.orc_cbm_sizes.argtypes = [ctypes.c_int, _i64, _i64, _vp, _vp]
+            lib.orc_cbm_encode.argtypes = [ctypes.c_int, _i64, _i64, _vp, _i64, _vp, _vp, _vp, _vp, _vp, _vp]
+            lib.orc_cbm_decode.argtypes = [ctypes.c_int, _i64, _i64, _vp, _i64, _vp, _vp, _vp, _vp, _vp, _vp]
             lib.orc_set_num_threads.argtypes = [ctypes.c_int]
             lib.orc_set_num_threads.restype = None
             _lib = lib
@@ -305,6 +308,47 @@ def spmm_csr(dt: str, row_ptr, col, vals, B, K: int):
 def spmm_residual_delta(dt: str, vals, meta, drow_ptr, dcol, dvals, B, K: int):
     """As spmm_residual with a delta-coded residual (see delta_encode)."""
     return _mm(dt, vals, meta, B, K, (drow_ptr, dcol, dvals), delta=True)
+
+
+def cbm_sizes(dt: str, M: int, K: int):
+    """(mask bytes, blocks) of the complement-bitmap residual layout; roff has blocks + 1 entries."""
+    mb, nb = ctypes.c_int64(0), ctypes.c_int64(0)
+    _check(_load().orc_cbm_sizes(DTYPES[dt], M, K, ctypes.byref(mb), ctypes.byref(nb)), "cbm_sizes")
+    return int(mb.value), int(nb.value)
+
+
+def cbm_encode(dt: str, meta, row_ptr, col, rvals, M: int, K: int):
+    """(rmask uint8, roff int32, cvals) of a CSR residual whose entries sit at
+    the complement positions of the 2:4 layer (meta) -- see orc_cbm_encode."""
+    mb, nb = cbm_sizes(dt, M, K)
+    meta = np.ascontiguousarray(np.asarray(meta, dtype=np.uint8))
+    row_ptr = np.ascontiguousarray(row_ptr, dtype=np.int32)
+    col = np.ascontiguousarray(col, dtype=np.int32)
+    rvals = np.ascontiguousarray(rvals, dtype=_store_dtype(dt))
+    nnz = int(row_ptr[M]) if M > 0 else 0
+    rmask = np.zeros(max(mb, 1), dtype=np.uint8)
+    roff = np.zeros(nb + 1, dtype=np.int32)
+    cvals = np.zeros(max(nnz, 1), dtype=_store_dtype(dt))
+    _check(_load().orc_cbm_encode(DTYPES[dt], M, K, _p(meta) if meta.size else None, max(meta.shape[-1], 1),
+                                  _p(row_ptr), _p(col) if col.size else None, _p(rvals) if rvals.size else None,
+                                  _p(rmask), _p(roff), _p(cvals)), "cbm_encode")
+    return rmask[:mb], roff, cvals[:nnz]
+
+
+def cbm_decode(dt: str, meta, rmask, roff, cvals, M: int, K: int):
+    """The CSR (row_ptr, col, rvals) of a complement-bitmap residual."""
+    meta = np.ascontiguousarray(np.asarray(meta, dtype=np.uint8))
+    rmask = np.ascontiguousarray(rmask, dtype=np.uint8)
+    roff = np.ascontiguousarray(roff, dtype=np.int32)
+    cvals = np.ascontiguousarray(cvals, dtype=_store_dtype(dt))
+    nnz = int(roff[-1])
+    row_ptr = np.zeros(M + 1, dtype=np.int32)
+    col = np.zeros(max(nnz, 1), dtype=np.int32)
+    rv = np.zeros(max(nnz, 1), dtype=_store_dtype(dt))
+    _check(_load().orc_cbm_decode(DTYPES[dt], M, K, _p(meta) if meta.size else None, max(meta.shape[-1], 1),
+                                  _p(rmask) if rmask.size else None, _p(roff), _p(cvals) if cvals.size else None,
+                                  _p(row_ptr), _p(col), _p(rv)), "cbm_decode")
+    return row_ptr, col[:nnz], rv[:nnz]
 
 
 def spmm_entries(dt: str, vals, meta, B, K: int, ms, ns, residual=None, delta: bool = False):

@@ -370,6 +370,179 @@ int orc_delta_fill(int dt, int64_t M, int64_t K, const int32_t* row_ptr, const i
     return ORC_OK;
 }
 
+/* ---- complement-bitmap residual, in the decode product's block order ----
+ * [P4] section "How the three-layer format makes moderate sparsity fast"
+ * keeps what the 2:4 layer drops in a residual layer, decoded in parallel on
+ * chip, and gives no layout.  This layout is the library's own.  It rests
+ * on one fact of the split: in a group where the 2:4 layer kept positions
+ * i0 < i1, a residual entry can only sit at one of the other two positions,
+ * c0 < c1 (the group's complement positions).  So one bit per complement
+ * position says whether the residual holds a value there.
+ *
+ * Geometry: a k-step is KS dense columns (64 for 16-bit element types, 128
+ * for 8-bit ones); tile t is rows [16t, 16t + 16); block b = t * S + g for
+ * tile t and k-step g (T = ceil(M/16) tiles, S = K / KS k-steps).  Lane
+ * l = 16q + r of block (t, g) is row 16t + r and dense columns
+ * [g*KS + q*EB, g*KS + (q+1)*EB), EB = KS / 4: GL = EB / 4 groups (4 or 8).
+ *   rmask: per block, 64 lanes x MB bytes (MB = GL / 4: 1 or 2), lane-major;
+ *          a lane's MB bytes are one little-endian word whose bit 2*gi + j
+ *          is set iff the residual has an entry at complement position c_j
+ *          of the lane's group gi (groups in ascending column order).
+ *          Rows past M have no bits.
+ *   roff:  int32 [T*S + 1]; roff[b] = entries in blocks before b, roff[T*S]
+ *          = all entries (an exclusive scan of the blocks' counts).
+ *   cvals: the entries' values, bit-copied, in block order, then lane order,
+ *          then bit order within the lane word.
+ * The bytes: GL/4 mask bytes per 64 lanes of a block plus 4 per block plus
+ * one value per entry, against the CSR's 4 + s per entry. */
+
+static int cbm_geom(int dt, int64_t M, int64_t K, int64_t* T, int64_t* S, int* GL) {
+    const int64_t KS = esize(dt) == 2 ? 64 : 128;
+    if (M < 0 || K < 0 || K % KS != 0) return ORC_ESHAPE;
+    *T = (M + 15) / 16;
+    *S = K / KS;
+    *GL = (int)(KS / 4 / 4);
+    return ORC_OK;
+}
+
+int orc_cbm_sizes(int dt, int64_t M, int64_t K, int64_t* mask_bytes, int64_t* blocks) {
+    if (!valid_dtype(dt) || dt == ORC_I4) return ORC_EDTYPE;
+    if (!mask_bytes || !blocks) return ORC_ENULL;
+    int64_t T, S;
+    int GL;
+    int rc = cbm_geom(dt, M, K, &T, &S, &GL);
+    if (rc) return rc;
+    *blocks = T * S;
+    *mask_bytes = T * S * 64 * (GL / 4);
+    return ORC_OK;
+}
+
+/* The complement positions c0 < c1 of a group whose kept pair is (i0, i1). */
+static void complement_pair(int i0, int i1, int* c0, int* c1) {
+    int n = 0, c[2] = {0, 0};
+    for (int p = 0; p < 4; ++p)
+        if (p != i0 && p != i1) c[n++] = p;
+    *c0 = c[0];
+    *c1 = c[1];
+}
+
+int orc_cbm_encode(int dt, int64_t M, int64_t K, const uint8_t* meta, int64_t ldm, const int32_t* row_ptr,
+                   const int32_t* col, const void* rvals, uint8_t* rmask, int32_t* roff, void* cvals) {
+    if (!valid_dtype(dt) || dt == ORC_I4) return ORC_EDTYPE;
+    int64_t T, S;
+    int GL;
+    int rc = cbm_geom(dt, M, K, &T, &S, &GL);
+    if (rc) return rc;
+    rc = check_csr(M, K, row_ptr, col);
+    if (rc) return rc;
+    if (!roff || (T * S > 0 && !rmask)) return ORC_ENULL;
+    if (M > 0 && K > 0 && (!meta || ldm < meta_cols(K))) return ORC_ENULL;
+    const int64_t nnz = M > 0 ? row_ptr[M] : 0;
+    if (nnz > 0 && (!rvals || !cvals)) return ORC_ENULL;
+    const int MB = GL / 4, EB = 4 * GL;
+    /* entry index of each column of the tile's 16 rows (-1: none) */
+    int64_t* at = (int64_t*)malloc(sizeof(int64_t) * 16 * (size_t)(K > 0 ? K : 1));
+    if (!at) return ORC_ENOMEM;
+    int64_t out = 0;
+    for (int64_t t = 0; t < T; ++t) {
+        for (int64_t i = 0; i < 16 * K; ++i) at[i] = -1;
+        for (int r = 0; r < 16 && 16 * t + r < M; ++r)
+            for (int64_t j = row_ptr[16 * t + r]; j < row_ptr[16 * t + r + 1]; ++j) at[r * K + col[j]] = j;
+        for (int64_t g = 0; g < S; ++g) {
+            const int64_t b = t * S + g;
+            roff[b] = (int32_t)out;
+            for (int l = 0; l < 64; ++l) {
+                const int q = l / 16, r = l % 16;   /* lane l = 16q + r */
+                const int64_t m = 16 * t + r, kb = g * 4 * EB + (int64_t)q * EB;
+                uint32_t word = 0;
+                if (m < M) {
+                    for (int gi = 0; gi < GL; ++gi) {
+                        int i0, i1, c[2];
+                        if (!decode_nibble(meta, ldm, m, kb / 4 + gi, &i0, &i1)) { free(at); return ORC_EFORMAT; }
+                        complement_pair(i0, i1, &c[0], &c[1]);
+                        for (int j = 0; j < 2; ++j) {
+                            const int64_t e = at[r * K + kb + 4 * gi + c[j]];
+                            if (e < 0) continue;
+                            word |= 1u << (2 * gi + j);
+                            elem_copy(dt, cvals, out, rvals, e);
+                            ++out;
+                        }
+                    }
+                }
+                for (int y = 0; y < MB; ++y) rmask[(b * 64 + l) * MB + y] = (uint8_t)(word >> (8 * y));
+            }
+        }
+    }
+    free(at);
+    /* every entry must sit at a complement position (the split's residual does) */
+    if (out != nnz) return ORC_EFORMAT;
+    roff[T * S] = (int32_t)out;
+    return ORC_OK;
+}
+
+int orc_cbm_decode(int dt, int64_t M, int64_t K, const uint8_t* meta, int64_t ldm, const uint8_t* rmask,
+                   const int32_t* roff, const void* cvals, int32_t* row_ptr, int32_t* col, void* rvals) {
+    if (!valid_dtype(dt) || dt == ORC_I4) return ORC_EDTYPE;
+    int64_t T, S;
+    int GL;
+    int rc = cbm_geom(dt, M, K, &T, &S, &GL);
+    if (rc) return rc;
+    if (!roff || !row_ptr || (T * S > 0 && !rmask)) return ORC_ENULL;
+    if (M > 0 && K > 0 && (!meta || ldm < meta_cols(K))) return ORC_ENULL;
+    const int MB = GL / 4, EB = 4 * GL;
+    /* pass 1: entries per row, and the block offsets checked against the bits */
+    for (int64_t m = 0; m <= M; ++m) row_ptr[m] = 0;
+    if (roff[0] != 0) return ORC_EFORMAT;
+    for (int64_t b = 0; b < T * S; ++b) {
+        int64_t n = 0;
+        for (int l = 0; l < 64; ++l) {
+            uint32_t word = 0;
+            for (int y = 0; y < MB; ++y) word |= (uint32_t)rmask[(b * 64 + l) * MB + y] << (8 * y);
+            const int64_t m = 16 * (b / S) + l % 16;
+            for (int bit = 0; bit < 2 * GL; ++bit)
+                if (word >> bit & 1u) {
+                    if (m >= M) return ORC_EFORMAT;
+                    ++row_ptr[m + 1];
+                    ++n;
+                }
+        }
+        if ((int64_t)roff[b + 1] - roff[b] != n) return ORC_EFORMAT;
+    }
+    for (int64_t m = 0; m < M; ++m) row_ptr[m + 1] += row_ptr[m];
+    const int64_t nnz = M > 0 ? row_ptr[M] : 0;
+    if (nnz > 0 && (!col || !rvals || !cvals)) return ORC_ENULL;
+    /* pass 2: for a fixed row the block, lane and bit order visits columns in
+     * ascending order, so each row is filled front to back */
+    int64_t* cur = (int64_t*)malloc(sizeof(int64_t) * (size_t)(M > 0 ? M : 1));
+    if (!cur) return ORC_ENOMEM;
+    for (int64_t m = 0; m < M; ++m) cur[m] = row_ptr[m];
+    int64_t in = 0;
+    for (int64_t b = 0; b < T * S; ++b) {
+        const int64_t t = b / S, g = b % S;
+        for (int l = 0; l < 64; ++l) {
+            const int q = l / 16, r = l % 16;
+            const int64_t m = 16 * t + r, kb = g * 4 * EB + (int64_t)q * EB;
+            uint32_t word = 0;
+            for (int y = 0; y < MB; ++y) word |= (uint32_t)rmask[(b * 64 + l) * MB + y] << (8 * y);
+            if (!word) continue;
+            for (int gi = 0; gi < GL; ++gi) {
+                int i0, i1, c[2];
+                if (!decode_nibble(meta, ldm, m, kb / 4 + gi, &i0, &i1)) { free(cur); return ORC_EFORMAT; }
+                complement_pair(i0, i1, &c[0], &c[1]);
+                for (int j = 0; j < 2; ++j)
+                    if (word >> (2 * gi + j) & 1u) {
+                        col[cur[m]] = (int32_t)(kb + 4 * gi + c[j]);
+                        elem_copy(dt, rvals, cur[m], cvals, in);
+                        ++cur[m];
+                        ++in;
+                    }
+            }
+        }
+    }
+    free(cur);
+    return ORC_OK;
+}
+
 /* ---- sparse x dense product ---- */
 
 static int check_mm(int dt, int64_t M, int64_t N, int64_t K, const void* vals, int64_t ldv,

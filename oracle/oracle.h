@@ -181,6 +181,17 @@ int orc_spmm_nm_w4a16(int nm_n, int nm_m, int64_t M, int64_t N, int64_t K, const
                       int64_t ldc);
 
 /* Number of threads an OpenMP parallel region would use (1 without OpenMP). */
+/* Complement-bitmap residual in the decode product's block order (layout
+ * at orc_cbm_encode in oracle.c): sizes (mask bytes and blocks; roff holds
+ * blocks + 1 entries), the encoding of a CSR residual whose entries sit at
+ * the complement positions of the 2:4 layer's groups (any other entry:
+ * ORC_EFORMAT), and the decoding back to CSR (columns ascending). */
+int orc_cbm_sizes(int dt, int64_t M, int64_t K, int64_t* mask_bytes, int64_t* blocks);
+int orc_cbm_encode(int dt, int64_t M, int64_t K, const uint8_t* meta, int64_t ldm, const int32_t* row_ptr,
+                   const int32_t* col, const void* rvals, uint8_t* rmask, int32_t* roff, void* cvals);
+int orc_cbm_decode(int dt, int64_t M, int64_t K, const uint8_t* meta, int64_t ldm, const uint8_t* rmask,
+                   const int32_t* roff, const void* cvals, int32_t* row_ptr, int32_t* col, void* rvals);
+
 int orc_num_threads(void);
 void orc_set_num_threads(int n);
 

@@ -69,6 +69,12 @@ MUTANTS = [
     ("i4 sign extended from the wrong bit", "return nib >= 8 ? nib - 16 : nib;", "return nib >= 8 ? nib - 8 : nib;"),
     ("i4 store keeps the old nibble", "*b = (uint8_t)((*b & ~(0xF << sh)) | ((v & 0xF) << sh));",
      "*b = (uint8_t)(*b | ((v & 0xF) << sh));"),
+    ("complement-bitmap lanes in row-major order", "const int q = l / 16, r = l % 16;   /* lane l = 16q + r */",
+     "const int q = l % 4, r = l / 4;   /* lane l = 16q + r */"),
+    ("complement-bitmap slots swapped", "word |= 1u << (2 * gi + j);", "word |= 1u << (2 * gi + 1 - j);"),
+    ("complement taken from one kept position only", "if (p != i0 && p != i1) c[n++] = p;",
+     "if (p != i0 && n < 2) c[n++] = p;"),
+    ("complement-bitmap total one short", "roff[T * S] = (int32_t)out;", "roff[T * S] = (int32_t)out - 1;"),
     ("bound accumulates signed terms",
      "bt[n * K + k];\n                        acc += t;\n                        s += fabs(t);\n                    }\n                    Cf[m * ldc + n] = acc;",
      "bt[n * K + k];\n                        acc += t;\n                        s += t;\n                    }\n                    Cf[m * ldc + n] = acc;"),

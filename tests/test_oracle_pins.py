@@ -752,3 +752,107 @@ def test_nm_outputs_overwrite_whatever_the_buffers_held(dt):
                                 vals.shape[1] * e, mask.ctypes.data_as(ctypes.c_void_p), mask.shape[1],
                                 dirty_d.ctypes.data_as(ctypes.c_void_p), D0.shape[1] * e)
     assert bad == 0 and np.array_equal(dirty_d, D0)
+
+
+# ---------------------------------------------------------------- complement-bitmap residual
+
+def _cbm_golden_matrix(dt, K):
+    g = _golden("cbm_example.json")
+    dense = np.zeros((g["M"], K))
+    for e in g["dense_nonzeros"]:
+        dense[e["row"], e["k"]] = e["v"]
+    return g, U.encode(dt, dense)
+
+
+@pytest.mark.parametrize("dt", DTS)
+def test_cbm_hand_worked_example(dt):
+    key = "16-bit" if dt in ("f16", "bf16") else "8-bit"
+    g = _golden("cbm_example.json")
+    lay = g["layouts"][key]
+    _, A = _cbm_golden_matrix(dt, lay["K"])
+    M, K = g["M"], lay["K"]
+    vals, meta, row_ptr, col, rvals = oracle.split(dt, A)
+    # the split's residual is the hand-worked CSR
+    assert list(row_ptr) == g["csr"]["row_ptr"] and list(col) == g["csr"]["col"]
+    assert np.array_equal(U.to_f64(dt, rvals), np.array(g["csr"]["val"], dtype=np.float64))
+    rmask, roff, cvals = oracle.cbm_encode(dt, meta, row_ptr, col, rvals, M, K)
+    assert oracle.cbm_sizes(dt, M, K) == (lay["mask_bytes"], lay["blocks"])
+    want = np.zeros(lay["mask_bytes"], dtype=np.uint8)
+    for i, v in lay["rmask_nonzero"].items():
+        want[int(i)] = v
+    assert np.array_equal(rmask, want)
+    assert list(roff) == lay["roff"]
+    assert np.array_equal(U.to_f64(dt, cvals), np.array(lay["cvals"], dtype=np.float64))
+
+
+def _cbm_shapes(dt):
+    ks = 64 if dt in ("f16", "bf16") else 128
+    return [(1, ks), (16, 2 * ks), (40, 4 * ks), (33, ks), (0, ks), (17, 0)]
+
+
+@pytest.mark.parametrize("dt", DTS)
+@pytest.mark.parametrize("fam", FAMILIES)
+def test_cbm_round_trip_and_invariants(dt, fam):
+    ks = 64 if dt in ("f16", "bf16") else 128
+    for M, K in _cbm_shapes(dt):
+        A = U.random_matrix(dt, M, K, fam, seed=M * 7 + K) if M * K else np.zeros((M, K), U.store_dtype(dt))
+        vals, meta, row_ptr, col, rvals = oracle.split(dt, A)
+        rmask, roff, cvals = oracle.cbm_encode(dt, meta, row_ptr, col, rvals, M, K)
+        nnz = int(row_ptr[-1]) if M else 0
+        # closed-form sizes: ceil(M/16) * K/KS blocks of 64 lanes x (1 or 2) mask bytes
+        blocks = (M + 15) // 16 * (K // ks)
+        assert rmask.size == blocks * 64 * (1 if ks == 64 else 2) and roff.size == blocks + 1
+        # one mask bit per residual entry; offsets an exclusive scan of the blocks' bits
+        per_block = np.unpackbits(rmask).reshape(blocks, -1).sum(1) if blocks else np.zeros(0, np.int64)
+        assert int(per_block.sum()) == nnz == int(roff[-1]) == cvals.size
+        assert list(roff) == list(np.concatenate([[0], np.cumsum(per_block)]).astype(int))
+        # decoding gives the split's CSR back, and with the 2:4 layer reproduces A's values
+        rp2, col2, rv2 = oracle.cbm_decode(dt, meta, rmask, roff, cvals, M, K)
+        assert np.array_equal(rp2, row_ptr) and np.array_equal(col2, col)
+        assert np.array_equal(np.asarray(rv2).view(np.uint8), np.asarray(rvals).view(np.uint8))
+        if M * K:
+            D, _ = oracle.decompress(dt, vals, meta, K)
+            Dv = U.to_f64(dt, D)
+            Dv[np.repeat(np.arange(M), np.diff(rp2)), col2] += U.to_f64(dt, rv2)
+            assert np.array_equal(Dv, U.to_f64(dt, A))
+
+
+def test_cbm_bits_only_at_complement_positions():
+    # brute force over every lane: a set bit names a non-kept position whose
+    # dense value is non-zero, and every such position has its bit
+    dt, M, K = "f16", 33, 128
+    A = U.random_matrix(dt, M, K, "sparse", seed=5)
+    vals, meta, row_ptr, col, rvals = oracle.split(dt, A)
+    rmask, roff, cvals = oracle.cbm_encode(dt, meta, row_ptr, col, rvals, M, K)
+    keep = U.brute_keep_mask(dt, A)
+    nz = ~U.is_zero(dt, A)
+    S = K // 64
+    for b in range(rmask.size // 64):
+        t, g = divmod(b, S)
+        for lane in range(64):
+            q, r = divmod(lane, 16)
+            m = 16 * t + r
+            word = int(rmask[b * 64 + lane])
+            for gi in range(4):
+                k0 = g * 64 + q * 16 + 4 * gi
+                comp = [p for p in range(4) if m < M and not keep[m, k0 + p]] if m < M else [0, 1]
+                for j in range(2):
+                    bit = word >> (2 * gi + j) & 1
+                    expect = m < M and bool(nz[m, k0 + comp[j]])
+                    assert bit == expect, (b, lane, gi, j)
+
+
+def test_cbm_rejects_an_entry_at_a_kept_position():
+    dt, M, K = "f16", 2, 64
+    A = np.zeros((M, K))
+    A[0, :4] = [1, 2, 3, 4]                       # keeps positions 2 and 3
+    vals, meta, row_ptr, col, rvals = oracle.split(dt, U.encode(dt, A))
+    assert row_ptr[-1] == 2                        # the dropped 1 and 2 at columns 0 and 1
+    one = U.encode(dt, [1.0])
+    for kept in (2, 3):
+        with pytest.raises(oracle.OracleError):
+            oracle.cbm_encode(dt, meta, np.array([0, 1, 1], np.int32), np.array([kept], np.int32), one, M, K)
+    # a complement position is accepted
+    rmask, roff, cvals = oracle.cbm_encode(dt, meta, np.array([0, 1, 1], np.int32), np.array([1], np.int32), one,
+                                           M, K)
+    assert rmask[0] == 2 and list(roff) == [0, 1]
