@@ -202,13 +202,15 @@ def read_bandwidth_GBps(nbytes: int, reps: int = 2) -> float:
 
 
 def bench_workload(key: str, iters: int, delta: bool = False, dense_cmp: bool = True,
-                   packed: bool = False, nm=None, prefill: bool = False):
+                   packed: bool = False, nm=None, prefill: bool = False, cbm: bool = False):
     """Kernel-level numbers for one workload (compression outside the timing),
     next to a dense GEMM of the same shape from the vendor library.  With
     delta=True the residual is delta-coded (one-byte column gaps); with
     packed=True the 2:4 operand is in the packed decode layout; with
     prefill=True in the packed prefill layout; with nm=(n, m) the weight is
-    in the n:m form (kept values plus keep mask)."""
+    in the n:m form (kept values plus keep mask); with cbm=True (and packed)
+    the residual is in the complement-bitmap layout, fused into the packed
+    product's k-steps."""
     import numpy as np
     import torch
 
@@ -229,6 +231,11 @@ def bench_workload(key: str, iters: int, delta: bool = False, dense_cmp: bool = 
         ops = ops[:2] + ssg.delta_encode(ops[2], ops[3], ops[4], w.K)
     if packed and nm is None:
         ops = ssg.pack_decode(ops[0], ops[1], w.K) + tuple(ops[2:])
+    if cbm:
+        vals0, meta0, rp0, col0, rv0 = ssg.split(a)
+        pv0, pm0 = ssg.pack_decode(vals0, meta0, w.K)
+        ops = (pv0, pm0) + ssg.pack_residual_cbm(meta0, rp0, col0, rv0, w.K)
+        del vals0, meta0, rp0, col0, rv0
     wbytes = sum(t.numel() * t.element_size() for t in ops)
     copies = 1
     if w.klass == "small_n":
@@ -240,7 +247,9 @@ def bench_workload(key: str, iters: int, delta: bool = False, dense_cmp: bool = 
 
     def launch(i):
         o = sets[i % copies]
-        if nm is not None and packed:
+        if cbm:
+            ssg.ssg_spmm_2to4_packed_residual_cbm(o[0], o[1], w.M, o[2], o[3], o[4], b, out)
+        elif nm is not None and packed:
             ssg.ssg_spmm_nm_packed(o[0], o[1], nm[0], nm[1], w.M, b, out, i4=w.dtype == "i4")
         elif nm is not None:
             ssg.ssg_spmm_nm(o[0], o[1], nm[0], nm[1], w.K, b, out)
@@ -271,6 +280,7 @@ def bench_workload(key: str, iters: int, delta: bool = False, dense_cmp: bool = 
     bbytes = b.numel() * b.element_size()
     cbytes = out.numel() * out.element_size()
     r = {"title": w.title + (", residual delta-coded" if delta else "") + (", packed decode layout" if packed else "")
+         + (", complement-bitmap residual fused" if cbm else "")
          + (", packed prefill layout" if prefill else "") + (", %d:%d" % tuple(nm) if nm else ""),
          "algo": ("nm (dense MFMA on the expanded operand)" if nm else ssg.ALGO_NAMES[algo])
          + (" (packed)" if packed else "") + (" (packed prefill)" if prefill else ""),
@@ -620,6 +630,9 @@ def main() -> int:
                 print("bench: workload %s, packed decode layout, delta-coded residual ..." % k, file=sys.stderr,
                       flush=True)
                 table[k + "_delta_packed"] = bench_workload(k, it, delta=True, dense_cmp=False, packed=True)
+                print("bench: workload %s, packed decode layout, complement-bitmap residual ..." % k,
+                      file=sys.stderr, flush=True)
+                table[k + "_cbm_packed"] = bench_workload(k, it, dense_cmp=False, packed=True, cbm=True)
             elif W.WORKLOADS[k].klass == "small_n" and W.WORKLOADS[k].N == 16:
                 print("bench: workload %s, packed decode layout ..." % k, file=sys.stderr, flush=True)
                 table[k + "_packed"] = bench_workload(k, it, dense_cmp=False, packed=True)

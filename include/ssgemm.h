@@ -420,6 +420,60 @@ int ssg_spmm_select_algo(int ab, int64_t M, int64_t N, int64_t K,
                          const void* vals, int64_t ldv, const uint8_t* meta, int64_t ldm,
                          const void* B, int64_t ldb, const void* C, int64_t ldc);
 
+/* Complement-bitmap residual: the residual layer in the packed decode
+ * product's block order, fused into its k-steps.  "How sparse LLM weights cut
+ * GPU inference cost without quantization", section "How the three-layer
+ * format makes moderate sparsity fast", keeps what the 2:4 layer drops in a
+ * residual layer decoded on chip in the same pipeline, and gives no layout;
+ * this one is the library's own.  It rests on one fact of the split: in a
+ * group where the 2:4 layer kept positions i0 < i1, a residual entry can
+ * only sit at one of the two other positions c0 < c1 (the complement
+ * positions).  With the packed decode geometry (16-row tiles, k-steps of KS
+ * = 64 dense columns for 16-bit types and 128 for 8-bit ones; block
+ * b = t * (K / KS) + g; lane l = 16q + r of block (t, g) = row 16t + r and
+ * dense columns [g*KS + q*KS/4, g*KS + (q+1)*KS/4), i.e. KS/16 groups):
+ *   rmask  per block, 64 lanes x MB bytes (MB = 1 for 16-bit types, 2 for
+ *          8-bit), lane-major; a lane's MB bytes are one little-endian word
+ *          whose bit 2*gi + j is set iff the residual holds a value at
+ *          complement position c_j of the lane's group gi (groups in
+ *          ascending column order); rows past M have no bits;
+ *   roff   int32 [blocks + 1]: roff[b] = values in the blocks before b,
+ *          roff[blocks] = all of them;
+ *   cvals  the values, bit-copied, in block, then lane, then bit order.
+ * Bytes: MB*64 + 4 per block plus s per entry, against 4 + s per entry for
+ * the CSR.  For a lane the residual is itself a 2:4 operand (its values at
+ * the complement positions, zeros elsewhere) whose index word is the
+ * complement of the 2:4 layer's, so the product adds one sparse MFMA per
+ * tile and k-step on the same B operand.
+ *
+ * Sizes: mask bytes and blocks (roff holds blocks + 1 entries).  K must be a
+ * multiple of KS. */
+int ssg_cbm_sizes(int dt, int64_t M, int64_t K, int64_t* mask_bytes, int64_t* blocks);
+
+/* Encoding from the CSR residual of ssg_split_fill (columns strictly
+ * ascending within [0, K) in every row) and the row-major metadata of the
+ * same 2:4 layer.  cvals holds nnz_r values (16-byte aligned for the
+ * product).  An entry at a kept position of its group, in a group with an
+ * invalid nibble, or repeating a column is left out and, if bad_count is
+ * not NULL, counted into the device int32 *bad_count (added atomically; the
+ * caller zeroes it); roff[blocks] then falls short of nnz_r.  Other
+ * violations of the CSR contract give an unspecified code but no
+ * out-of-bounds access. */
+int ssg_pack_residual_cbm(int dt, int64_t M, int64_t K, const uint8_t* meta, int64_t ldm,
+                          const int32_t* row_ptr, const int32_t* col, const void* rvals, int64_t nnz_r,
+                          uint8_t* rmask, int32_t* roff, void* cvals, int32_t* bad_count, void* stream);
+
+/* C = (expand(packed decode layout) + residual) x B, the residual in the
+ * complement-bitmap layout above, fused into every k-step.  Shapes, types
+ * and the packed operand as for ssg_spmm_2to4_packed (N == 16, ldb == 16).
+ * nvals is the number of values cvals holds (at least roff[blocks]; it bounds
+ * the loads).  Alignment: pvals, B and cvals 16 bytes; pmeta and rmask to
+ * their words; roff 4 bytes. */
+int ssg_spmm_2to4_packed_residual_cbm(int ab, int c, int64_t M, int64_t N, int64_t K,
+                                      const void* pvals, const void* pmeta, const uint8_t* rmask,
+                                      const int32_t* roff, const void* cvals, int64_t nvals,
+                                      const void* B, int64_t ldb, void* C, int64_t ldc, void* stream);
+
 /* Measurement helper (not part of the product): one streaming read of
  * `bytes` bytes of device memory at src (16-byte aligned, bytes a multiple
  * of 16), 16 bytes per lane per load, non-temporal, every byte once.  Its

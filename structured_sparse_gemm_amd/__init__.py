@@ -35,6 +35,8 @@ __all__ = [
     "compress_prefill", "pack_prefill", "spmm_prefill",
     "ssg_compress_nm", "ssg_decompress_nm", "ssg_spmm_nm", "compress_nm", "decompress_nm", "spmm_nm",
     "ssg_nm_packed_sizes", "ssg_pack_nm_decode", "ssg_spmm_nm_packed", "pack_nm", "spmm_nm_packed",
+    "ssg_cbm_sizes", "ssg_pack_residual_cbm", "ssg_spmm_2to4_packed_residual_cbm", "pack_residual_cbm",
+    "spmm_packed_residual_cbm",
     "ssg_stream_read_sink_words", "ssg_stream_read",
     "SSG_ALGO_AUTO", "SSG_ALGO_GENERIC", "SSG_ALGO_SMALL_N", "SSG_ALGO_LARGE_N", "library_path",
 ]
@@ -321,6 +323,35 @@ def ssg_spmm_select_algo(vals, meta, B, C) -> int:
                                            _ld(B, "B"), _ptr(C, "C"), _ld(C, "C")))
 
 
+def ssg_cbm_sizes(dtype: torch.dtype, M: int, K: int) -> Tuple[int, int]:
+    """(mask bytes, blocks) of the complement-bitmap residual; roff has blocks + 1 entries."""
+    import ctypes
+    mb, nb = ctypes.c_int64(0), ctypes.c_int64(0)
+    _check(_lib().ssg_cbm_sizes(_DT[dtype], M, K, ctypes.byref(mb), ctypes.byref(nb)), "ssg_cbm_sizes")
+    return int(mb.value), int(nb.value)
+
+
+def ssg_pack_residual_cbm(meta, row_ptr, col, rvals, K: int, rmask, roff, cvals, bad_count=None,
+                          stream=None) -> None:
+    M = row_ptr.numel() - 1
+    nnz = int(col.numel()) if col is not None else 0
+    _check(_lib().ssg_pack_residual_cbm(_dtype(rvals), M, K, _ptr(meta, "meta"), _ld(meta, "meta"),
+                                        _ptr(row_ptr, "row_ptr"), _ptr(col, "col"), _ptr(rvals, "rvals"), nnz,
+                                        _ptr(rmask, "rmask"), _ptr(roff, "roff"), _ptr(cvals, "cvals"),
+                                        _ptr(bad_count, "bad_count"), _stream(row_ptr, stream)),
+           "ssg_pack_residual_cbm")
+
+
+def ssg_spmm_2to4_packed_residual_cbm(pvals, pmeta, M: int, rmask, roff, cvals, B, C, stream=None) -> None:
+    ab = _dtype(B)
+    N, K = B.shape[1], B.shape[0]
+    _check(_lib().ssg_spmm_2to4_packed_residual_cbm(ab, _OUT[ab][0], M, N, K, _ptr(pvals, "pvals"),
+                                                    _ptr(pmeta, "pmeta"), _ptr(rmask, "rmask"), _ptr(roff, "roff"),
+                                                    _ptr(cvals, "cvals"), int(cvals.numel()), _ptr(B, "B"),
+                                                    _ld(B, "B"), _ptr(C, "C"), _ld(C, "C"), _stream(C, stream)),
+           "ssg_spmm_2to4_packed_residual_cbm")
+
+
 def ssg_stream_read_sink_words(nbytes: int) -> int:
     return int(_lib().ssg_stream_read_sink_words(nbytes))
 
@@ -587,6 +618,30 @@ def spmm_packed_residual_delta(pvals, pmeta, M: int, drow_ptr, dcol, dvals, B: t
     ab = _dtype(B)
     C = torch.empty((M, B.shape[1]), dtype=_OUT[ab][1], device=B.device) if out is None else out
     ssg_spmm_2to4_packed_residual_delta(pvals, pmeta, M, drow_ptr, dcol, dvals, B, C)
+    return C
+
+
+def pack_residual_cbm(meta: torch.Tensor, row_ptr: torch.Tensor, col: torch.Tensor, rvals: torch.Tensor, K: int):
+    """(rmask, roff, cvals) of the complement-bitmap layout of a CSR residual
+    (from split) against its 2:4 layer's metadata; cvals is 16-byte aligned."""
+    M = row_ptr.numel() - 1
+    mb, nb = ssg_cbm_sizes(rvals.dtype, M, K)
+    dev = row_ptr.device
+    rmask = torch.empty(mb, dtype=torch.uint8, device=dev)
+    roff = torch.empty(nb + 1, dtype=torch.int32, device=dev)
+    nnz = int(col.numel())
+    es = rvals.element_size()
+    cvals = torch.empty(-(-max(nnz, 1) * es // 16) * 16 // es, dtype=rvals.dtype, device=dev)[:nnz]
+    ssg_pack_residual_cbm(meta, row_ptr, col, rvals, K, rmask, roff, cvals)
+    return rmask, roff, cvals
+
+
+def spmm_packed_residual_cbm(pvals, pmeta, M: int, rmask, roff, cvals, B: torch.Tensor,
+                             out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """C = expand(packed) @ B + residual(complement bitmap) @ B, B [K, 16]."""
+    ab = _dtype(B)
+    C = torch.empty((M, B.shape[1]), dtype=_OUT[ab][1], device=B.device) if out is None else out
+    ssg_spmm_2to4_packed_residual_cbm(pvals, pmeta, M, rmask, roff, cvals, B, C)
     return C
 
 

@@ -107,55 +107,20 @@ __device__ __forceinline__ void store_compressed(typename Store<DT>::T* vrow, ui
 // Grid-stride loop over chunks with the next chunk's loads in flight while
 // the current one is selected and stored, so reads and writes of the pass
 // overlap instead of running as one load phase followed by one store phase.
-// Packed prefill output: the chunk's stored values (whole 16-byte chunks of
-// the layout) and its metadata word at their places in (pvals, pmeta); the
-// last chunk of a row also zeroes the row's metadata bytes past K / 8 in its
-// last block.  K is a multiple of 64, so every chunk is full.
 template <int DT>
-__device__ __forceinline__ void store_prefill(uint8_t* pv, uint8_t* pm, int64_t m, int64_t c, int64_t K,
-                                              int64_t stages, int64_t mblocks,
-                                              const typename Store<DT>::T (&v)[2 * kChunkGroups], uint32_t word) {
-    using T = typename Store<DT>::T;
-    constexpr int kVecs = 2 * kChunkGroups * sizeof(T) / 16;
-    uint4 w[kVecs];
-    __builtin_memcpy(w, v, sizeof(w));
-#pragma unroll
-    for (int i = 0; i < kVecs; ++i)
-        *reinterpret_cast<uint4*>(pv + prefill_vals_offset(m, (c * kVecs + i) * 16, stages)) = w[i];
-    // the chunk's 4 metadata bytes are one index word (8-bit) or two (16-bit)
-    constexpr int IW = sizeof(T) == 1 ? 4 : 2;
-    if constexpr (IW == 4) {
-        *reinterpret_cast<uint32_t*>(pm + prefill_meta_offset(m, c * 4, mblocks, IW)) = word;
-        if ((c + 1) * kChunkElems == K)
-            for (int64_t j = K / 8; j < mblocks * 32; j += 4)
-                *reinterpret_cast<uint32_t*>(pm + prefill_meta_offset(m, j, mblocks, IW)) = 0u;
-    } else {
-        *reinterpret_cast<uint16_t*>(pm + prefill_meta_offset(m, c * 4, mblocks, IW)) = (uint16_t)word;
-        *reinterpret_cast<uint16_t*>(pm + prefill_meta_offset(m, c * 4 + 2, mblocks, IW)) = (uint16_t)(word >> 16);
-        if ((c + 1) * kChunkElems == K)
-            for (int64_t j = K / 8; j < mblocks * 32; j += 2)
-                *reinterpret_cast<uint16_t*>(pm + prefill_meta_offset(m, j, mblocks, IW)) = 0;
-    }
-}
-
-// PF: write the packed prefill layout (vals / meta are pvals / pmeta, rows
-// run to the 256-row tile boundary past M with zeros) instead of row-major.
-template <int DT, bool PF>
 __global__ void __launch_bounds__(256) k_compress(int64_t M, int64_t K, const typename Store<DT>::T* __restrict__ A,
                                                   int64_t lda, typename Store<DT>::T* __restrict__ vals, int64_t ldv,
                                                   uint8_t* __restrict__ meta, int64_t ldm, int vec) {
     using T = typename Store<DT>::T;
     const int64_t chunks = (K + kChunkElems - 1) / kChunkElems;
-    const int64_t rows = PF ? (M + 255) / 256 * 256 : M;
-    const int64_t total = rows * chunks;
-    const int64_t stages = K / 2 * (int64_t)sizeof(T) / 64, mblocks = (K + 255) / 256;
+    const int64_t total = M * chunks;
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
     int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (t >= total) return;
     int64_t m = t / chunks, c = t - m * chunks;
     int ng = (int)min<int64_t>(kChunkGroups, (K - c * kChunkElems) / 4);
     T x[kChunkElems];
-    load_chunk<DT>(A + min(m, M - 1) * lda + c * kChunkElems, ng, vec != 0, x);
+    load_chunk<DT>(A + m * lda + c * kChunkElems, ng, vec != 0, x);
     for (;;) {
         const int64_t tn = t + stride;
         const bool more = tn < total;
@@ -166,21 +131,12 @@ __global__ void __launch_bounds__(256) k_compress(int64_t M, int64_t K, const ty
             mn = tn / chunks;
             cn = tn - mn * chunks;
             ngn = (int)min<int64_t>(kChunkGroups, (K - cn * kChunkElems) / 4);
-            load_chunk<DT>(A + min(mn, M - 1) * lda + cn * kChunkElems, ngn, vec != 0, xn);
+            load_chunk<DT>(A + mn * lda + cn * kChunkElems, ngn, vec != 0, xn);
         }
         T v[2 * kChunkGroups];
         uint32_t word = select_chunk<DT>(x, ng, v);
-        if constexpr (PF) {
-            if (m >= M) {   // padding row of the last tile
-                word = 0;
-#pragma unroll
-                for (int i = 0; i < 2 * kChunkGroups; ++i) v[i] = T(0);
-            }
-            store_prefill<DT>(reinterpret_cast<uint8_t*>(vals), meta, m, c, K, stages, mblocks, v, word);
-        } else {
-            store_compressed<DT>(vals + m * ldv + c * 2 * kChunkGroups, meta + m * ldm + c * (kChunkGroups / 2), ng,
-                                 vec != 0, v, word);
-        }
+        store_compressed<DT>(vals + m * ldv + c * 2 * kChunkGroups, meta + m * ldm + c * (kChunkGroups / 2), ng,
+                             vec != 0, v, word);
         if (!more) break;
 #pragma unroll
         for (int i = 0; i < kChunkElems; ++i) x[i] = xn[i];
@@ -189,6 +145,97 @@ __global__ void __launch_bounds__(256) k_compress(int64_t M, int64_t K, const ty
         c = cn;
         ng = ngn;
     }
+}
+
+// Packed prefill output, one workgroup per (256-row tile, metadata block):
+// the block's stored values (4 stages of 64 stored bytes per row for 16-bit
+// types, 2 for 8-bit ones) and its metadata block are assembled in LDS at
+// their positions in the layout and then written out as the two contiguous
+// runs they are in HBM (16, 32 or 64 KiB of values, 8 KiB of metadata), so
+// every store is a whole 16-byte piece and every line is written whole.
+// Thread t of 512 takes chunk c = t % 8 (32 dense k) of rows t / 8 + 64 i,
+// all 4 chunk loads in flight before the first selection; two workgroups fit
+// a CU, so one streams while the other selects and stores.  Rows past M and
+// chunks past K are zeros.
+constexpr int kPrefillThreads = 512;
+
+template <int DT>
+__global__ void __launch_bounds__(kPrefillThreads) k_compress_prefill(int64_t M, int64_t K, const typename Store<DT>::T* A,
+                                                          int64_t lda, uint8_t* __restrict__ pvals,
+                                                          uint8_t* __restrict__ pmeta, int vec, int64_t stages,
+                                                          int64_t mblocks) {
+    using T = typename Store<DT>::T;
+    constexpr int ES = (int)sizeof(T);
+    constexpr int SPB = 2 * ES;                  // stages per metadata block (256 dense k)
+    constexpr int CPS = 4 / ES;                  // 32-element chunks per stage
+    constexpr int IW = ES == 1 ? 4 : 2;          // index-word bytes
+    constexpr int kRows = 256 / (kPrefillThreads / 8);   // rows per thread
+    __shared__ __attribute__((aligned(16))) uint8_t lds[SPB * 16384 + 8192];
+    uint8_t* const lmeta = lds + SPB * 16384;
+    const int64_t tile = blockIdx.x / mblocks, g = blockIdx.x - tile * mblocks;
+    const int nst = (int)min<int64_t>(SPB, stages - g * SPB);   // stages of this block inside K
+    const int c = threadIdx.x & 7, r0 = threadIdx.x >> 3;
+    const bool in_k = c < nst * CPS;
+    const int64_t k0 = g * 256 + (int64_t)c * kChunkElems;
+
+    // raw 16-byte pieces of the chunks (kept packed until each is selected)
+    constexpr int kVecs = kChunkElems * ES / 16;
+    const bool fast = vec != 0;
+    uint4 raw[kRows][kVecs];
+#pragma unroll
+    for (int i = 0; i < kRows; ++i) {
+        const int64_t m = tile * 256 + r0 + (kPrefillThreads / 8) * i;
+        const bool ld = in_k && m < M;
+#pragma unroll
+        for (int j = 0; j < kVecs; ++j) raw[i][j] = make_uint4(0, 0, 0, 0);
+        if (ld && fast) {
+#pragma unroll
+            for (int j = 0; j < kVecs; ++j) raw[i][j] = reinterpret_cast<const uint4*>(A + m * lda + k0)[j];
+        } else if (ld) {
+            T x[kChunkElems];
+            load_chunk<DT>(A + m * lda + k0, kChunkGroups, false, x);
+            __builtin_memcpy(raw[i], x, sizeof(x));
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < kRows; ++i) {
+        const int r = r0 + (kPrefillThreads / 8) * i;
+        const bool live = in_k && tile * 256 + r < M;
+        T x[kChunkElems];
+        __builtin_memcpy(x, raw[i], sizeof(x));
+        T v[2 * kChunkGroups];
+        uint32_t word = select_chunk<DT>(x, kChunkGroups, v);
+        if (!live) {
+            word = 0;
+#pragma unroll
+            for (int e = 0; e < 2 * kChunkGroups; ++e) v[e] = T(0);
+        }
+        // the chunk's stored values: bytes [16 c ES, 16 c ES + 16 ES) of the
+        // row's stored bytes in this block, i.e. ES 16-byte pieces of stage
+        // c / CPS (pieces past the block's last stage are never written out)
+        uint4 w[ES];
+        __builtin_memcpy(w, v, sizeof(w));
+        const int st = c / CPS;
+#pragma unroll
+        for (int j = 0; j < ES; ++j) {
+            const int piece = (c % CPS) * ES + j;
+            *reinterpret_cast<uint4*>(lds + st * 16384 + r * 64 + ((piece ^ prefill_swz(r)) << 4)) = w[j];
+        }
+        // its 4 metadata bytes: index words (4 c) / IW .. of the row
+#pragma unroll
+        for (int j = 0; j < 4 / IW; ++j) {
+            const int wi = (4 * c) / IW + j;
+            if constexpr (IW == 4) *reinterpret_cast<uint32_t*>(lmeta + wi * 256 * IW + r * IW) = word;
+            else *reinterpret_cast<uint16_t*>(lmeta + wi * 256 * IW + r * IW) = (uint16_t)(word >> (16 * j));
+        }
+    }
+    __syncthreads();
+    uint8_t* const vdst = pvals + ((tile * stages + g * SPB) << 14);
+    for (int o = threadIdx.x * 16; o < nst * 16384; o += kPrefillThreads * 16)
+        *reinterpret_cast<uint4*>(vdst + o) = *reinterpret_cast<const uint4*>(lds + o);
+    uint8_t* const mdst = pmeta + ((tile * mblocks + g) << 13);
+    for (int o = threadIdx.x * 16; o < 8192; o += kPrefillThreads * 16)
+        *reinterpret_cast<uint4*>(mdst + o) = *reinterpret_cast<const uint4*>(lmeta + o);
 }
 
 template <int DT>
@@ -533,7 +580,7 @@ hipError_t launch_compress(int dt, int64_t M, int64_t K, const void* A, int64_t 
     if (blocks > kCompressBlocks) blocks = kCompressBlocks;
     SSG_DISPATCH_DT(dt, {
         using T = typename Store<D>::T;
-        hipLaunchKernelGGL((k_compress<D, false>), dim3((unsigned)blocks), dim3(256), 0, s, M, K, (const T*)A, lda,
+        hipLaunchKernelGGL((k_compress<D>), dim3((unsigned)blocks), dim3(256), 0, s, M, K, (const T*)A, lda,
                            (T*)vals, ldv, meta, ldm, (int)vec);
     });
     return hipGetLastError();
@@ -541,14 +588,14 @@ hipError_t launch_compress(int dt, int64_t M, int64_t K, const void* A, int64_t 
 
 hipError_t launch_compress_prefill(int dt, int64_t M, int64_t K, const void* A, int64_t lda, void* pvals,
                                    void* pmeta, bool vec, hipStream_t s) {
-    const int64_t threads = (M + 255) / 256 * 256 * (K / kChunkElems);
-    if (threads == 0) return hipSuccess;
-    int64_t blocks = blocks_for(threads, 256);
-    if (blocks > kCompressBlocks) blocks = kCompressBlocks;
+    int64_t tiles, stages, mblocks;
+    prefill_geometry(dt, M, K, &tiles, &stages, &mblocks);
+    const int64_t blocks = tiles * mblocks;
+    if (blocks == 0) return hipSuccess;
     SSG_DISPATCH_DT(dt, {
         using T = typename Store<D>::T;
-        hipLaunchKernelGGL((k_compress<D, true>), dim3((unsigned)blocks), dim3(256), 0, s, M, K, (const T*)A, lda,
-                           (T*)pvals, 0, (uint8_t*)pmeta, 0, (int)vec);
+        hipLaunchKernelGGL(k_compress_prefill<D>, dim3((unsigned)blocks), dim3(kPrefillThreads), 0, s, M, K, (const T*)A, lda,
+                           (uint8_t*)pvals, (uint8_t*)pmeta, (int)vec, stages, mblocks);
     });
     return hipGetLastError();
 }
@@ -615,6 +662,11 @@ hipError_t launch_delta_count(int64_t M, int64_t K, const int32_t* row_ptr, cons
                            drow_ptr);
     }
     hipLaunchKernelGGL(k_scan_rows, dim3(1), dim3(1024), 0, s, M, drow_ptr);
+    return hipGetLastError();
+}
+
+hipError_t launch_scan_counts(int64_t n, int32_t* a, hipStream_t s) {
+    hipLaunchKernelGGL(k_scan_rows, dim3(1), dim3(1024), 0, s, n, a);
     return hipGetLastError();
 }
 

@@ -1031,6 +1031,279 @@ __global__ void __launch_bounds__(kWaves * 64) k_spmm_packed(SpmmArgs a, const u
     }
 }
 
+// ---- complement-bitmap residual, fused into the packed decode product -------
+//
+// A residual entry of a group can only sit at one of the two positions the
+// 2:4 layer did not keep.  Stored per packed block (16 rows x one k-step) as
+// a 2-bit-per-group mask word per lane over those positions, a block offset
+// and the values in lane order, the residual's share of a lane's operand is
+// itself a 2:4 operand: the values at the complement positions (zeros where
+// the mask bit is clear) with the index word whose nibbles are the
+// complements of the 2:4 layer's.  It rides the same B operand and the same
+// sparse MFMA in every k-step, so the residual bytes stream with the 2:4
+// layer's instead of after them ("How sparse LLM weights cut GPU inference
+// cost without quantization", section "How the three-layer format makes
+// moderate sparsity fast": the layers are decoded on chip in one pipeline).
+
+// Complement of every nibble of an index word: kept pair {i0, i1} -> the
+// other two positions, ascending.  For the six valid nibbles this is
+// n ^ 0xA for the pairs (0, 1) and (2, 3) -- the nibbles with bit 3 clear or
+// bits 2 and 1 both set -- and n ^ 0x5 for the other four.
+__device__ __forceinline__ uint32_t complement_index(uint32_t n) {
+    const uint32_t pair01_23 = ((~n >> 3) | ((n >> 2) & (n >> 1))) & 0x11111111u;
+    return n ^ 0x55555555u ^ ((pair01_23 << 4) - pair01_23);
+}
+
+template <int DT> struct Cbm {
+    static constexpr int IDXB = SN<DT>::META / 4;          // index bytes per lane per k-step (2 / 4)
+    static constexpr int MB = IDXB / 2;                    // mask bytes per lane (1 / 2)
+    static constexpr int SLOTS = 8 * MB;                   // complement slots per lane (8 / 16)
+    static constexpr int BSTEP = 16 * SN<DT>::ES * SN<DT>::KS;
+    static constexpr int LX = 4;                           // k-steps of fragments, masks, offsets and B in flight
+    static constexpr int LY = 2;                           // k-steps of residual value windows in flight
+    static constexpr int YWIN = 2048;                      // a block's values: at most 1 KiB plus alignment
+    template <int TM> static constexpr int wave_lds() { return LX * BSTEP + LY * TM * YWIN + 16; }
+};
+
+// Residual operand of a lane from its block's value window in LDS: slot s
+// (group s / 2, complement position s % 2) holds the value of rank
+// popcount(mask below s) among the lane's values if mask bit s is set, else
+// zero (read from a zeroed pad, so no slot takes a branch).
+template <int DT>
+__device__ __forceinline__ uint4 cbm_operand(const uint8_t* win, uint32_t zoff, uint32_t e0, uint32_t mask) {
+    constexpr int ES = SN<DT>::ES;
+    uint32_t w[4];
+    if constexpr (ES == 2) {
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+            uint32_t h[2];
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const int sl = 2 * d + j;
+                const uint32_t rank = __popc(mask & ((1u << sl) - 1u));
+                const uint32_t off = (mask >> sl & 1u) ? 2u * (e0 + rank) : zoff;
+                h[j] = *reinterpret_cast<const uint16_t*>(win + off);
+            }
+            w[d] = h[0] | (h[1] << 16);
+        }
+    } else {
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+            uint32_t x = 0;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int sl = 4 * d + j;
+                const uint32_t rank = __popc(mask & ((1u << sl) - 1u));
+                const uint32_t off = (mask >> sl & 1u) ? e0 + rank : zoff;
+                x |= (uint32_t)win[off] << (8 * j);
+            }
+            w[d] = x;
+        }
+    }
+    return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+// Packed decode product with a complement-bitmap residual (B one contiguous
+// K x 16 block).  Per wave and k-step g: the 2:4 fragments, index words,
+// mask words and block offsets of its tiles plus its two 1 KiB pieces of B
+// rows (group X(g), LX k-steps ahead), and the value windows of its tiles'
+// blocks (group Y(g), two direct-to-LDS loads of 1 KiB per tile, LY k-steps
+// ahead; their addresses need the block offsets, so a Y group is issued
+// once its X group has landed).  Iteration i waits until only the previous
+// iteration's two groups are outstanding, multiplies k-step g_i, then issues
+// Y(g_{i+LY}) and X(g_{i+LX}).  Every wave issues the same loads per
+// iteration (a k-step past K, a tile past the range or a window chunk past
+// a block's values reads zero from an out-of-range offset), so the waits
+// are exact counts.  Partial tiles are summed in wave order as in the
+// plain packed product.
+template <int DT, int TM>
+__global__ void __launch_bounds__(kWaves * 64) k_spmm_packed_cbm(SpmmArgs a, const uint8_t* pvals, const uint8_t* pmeta,
+                                                                 const uint8_t* rmask, const int32_t* roff,
+                                                                 const uint8_t* cvals, int64_t nvals, int64_t tiles) {
+    constexpr int W = kWaves;
+    using T = SN<DT>;
+    using C = Cbm<DT>;
+    using Acc = AccT<DT>;
+    using S = typename std::conditional<DT == DT_I8, int32_t, float>::type;
+    constexpr int LX = C::LX, LY = C::LY, IDXB = C::IDXB, MB = C::MB;
+    constexpr int GX = 2 + 4 * TM;                      // loads of an X group per wave
+    constexpr int GY = 2 * TM;                          // loads of a Y group per wave
+    constexpr int WL = C::template wave_lds<TM>();
+    static_assert(LX % LY == 0 && GX + GY < 64, "ring");
+    static_assert(W * WL <= 160 * 1024 && W * kTMax * 1024 <= W * WL, "LDS");
+    extern __shared__ __attribute__((aligned(1024))) uint8_t lds[];
+    const uint32_t lds_addr = (uint32_t)(uintptr_t)(const lds_void*)lds;
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t t0 = (int64_t)blockIdx.x * TM;
+    const int nt = (int)min<int64_t>(TM, tiles - t0);
+    const int64_t ksteps = a.K / T::KS;
+    const uint32_t wbase = (uint32_t)(wave * WL);                 // this wave's LDS region
+    const uint32_t ybase = wbase + LX * C::BSTEP;                 // its value windows
+    const uint32_t zpad = ybase + LY * TM * C::YWIN;              // 16 zero bytes
+    if (lane == 0) *reinterpret_cast<uint4*>(lds + zpad) = make_uint4(0, 0, 0, 0);
+
+    const __amdgpu_buffer_rsrc_t rv = rsrc(pvals, tiles * ksteps * 1024);
+    const __amdgpu_buffer_rsrc_t rm = rsrc(pmeta, tiles * ksteps * 64 * IDXB);
+    const __amdgpu_buffer_rsrc_t rb = rsrc(a.B, a.K * 16 * T::ES);
+    const __amdgpu_buffer_rsrc_t rk = rsrc(rmask, tiles * ksteps * 64 * MB);
+    const __amdgpu_buffer_rsrc_t ro = rsrc(reinterpret_cast<const uint8_t*>(roff), (tiles * ksteps + 1) * 4);
+    // values: the host aligns cvals to 16 bytes, so the 16-byte block that
+    // holds the last value is mapped; bytes past the array are never used
+    const __amdgpu_buffer_rsrc_t rc = rsrc(cvals, (nvals * T::ES + 15) / 16 * 16);
+    uint32_t voff[TM], moff[TM], koff[TM], boff[TM];
+#pragma unroll
+    for (int t = 0; t < TM; ++t) {
+        const int64_t blk0 = (t0 + t) * ksteps;           // block of the tile's k-step 0
+        voff[t] = t < nt ? (uint32_t)((blk0 * 64 + lane) * 16) : kOob;
+        moff[t] = t < nt ? (uint32_t)((blk0 * 64 + lane) * IDXB) : kOob;
+        koff[t] = t < nt ? (uint32_t)((blk0 * 64 + lane) * MB) : kOob;
+        boff[t] = t < nt ? (uint32_t)(blk0 * 4) : kOob;
+    }
+
+    i32x4 av[LX][TM] = {};   // native vector registers, so they can be tied to the waits below
+    int mv[LX][TM] = {};
+    int kv[LX][TM] = {};
+    i32x2 ov[LX][TM] = {};
+    auto issue_x = [&](int64_t g, int u) {
+        const bool in = g < ksteps;
+        const uint32_t slot = lds_addr + wbase + (uint32_t)(u * C::BSTEP);
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+            dma<16>(rb, slot + j * 1024, in ? (uint32_t)(g * C::BSTEP + j * 1024 + lane * 16) : kOob);
+#pragma unroll
+        for (int t = 0; t < TM; ++t) {
+            const uint32_t o = in ? voff[t] + (uint32_t)(g * 1024) : kOob;
+            const uint32_t om = in ? moff[t] + (uint32_t)(g * 64 * IDXB) : kOob;
+            const uint32_t ok = in ? koff[t] + (uint32_t)(g * 64 * MB) : kOob;
+            const uint32_t oo = in ? boff[t] + (uint32_t)(g * 4) : kOob;
+            asm volatile("buffer_load_dwordx4 %0, %1, %2, 0 offen nt" : "=v"(av[u][t]) : "v"(o), "s"(rv) : "memory");
+            if constexpr (IDXB == 4)
+                asm volatile("buffer_load_dword %0, %1, %2, 0 offen nt" : "=v"(mv[u][t]) : "v"(om), "s"(rm) : "memory");
+            else
+                asm volatile("buffer_load_ushort %0, %1, %2, 0 offen nt" : "=v"(mv[u][t]) : "v"(om), "s"(rm) : "memory");
+            if constexpr (MB == 2)
+                asm volatile("buffer_load_ushort %0, %1, %2, 0 offen nt" : "=v"(kv[u][t]) : "v"(ok), "s"(rk) : "memory");
+            else
+                asm volatile("buffer_load_ubyte %0, %1, %2, 0 offen nt" : "=v"(kv[u][t]) : "v"(ok), "s"(rk) : "memory");
+            asm volatile("buffer_load_dwordx2 %0, %1, %2, 0 offen" : "=v"(ov[u][t]) : "v"(oo), "s"(ro) : "memory");
+        }
+    };
+    // the value windows of k-step g's blocks (X slot u landed) into Y slot y
+    auto issue_y = [&](int u, int y) {
+#pragma unroll
+        for (int t = 0; t < TM; ++t) {
+            const uint32_t start = ((uint32_t)ov[u][t][0] * T::ES) & ~15u, end = (uint32_t)ov[u][t][1] * T::ES;
+            const uint32_t win = lds_addr + ybase + (uint32_t)((y * TM + t) * C::YWIN);
+#pragma unroll
+            for (int d = 0; d < 2; ++d) {
+                const uint32_t o = start + (uint32_t)(d * 1024 + lane * 16);
+                dma<16>(rc, win + d * 1024, o < end ? o : kOob);
+            }
+        }
+    };
+
+    Acc acc[TM];
+#pragma unroll
+    for (int t = 0; t < TM; ++t) acc[t] = Acc{0, 0, 0, 0};
+    // prologue: X(g0), X(g1), Y(g0), X(g2), Y(g1), X(g3) -- the state an
+    // iteration expects: its own X and Y landed once only the previous
+    // iteration's Y and X groups remain outstanding
+    issue_x(wave, 0);
+    issue_x(wave + (int64_t)W, 1);
+    wait_vm<GX>();
+#pragma unroll
+    for (int t = 0; t < TM; ++t) asm volatile("" : "+v"(ov[0][t]));
+    issue_y(0, 0);
+    issue_x(wave + (int64_t)2 * W, 2);
+    wait_vm<GY + GX>();
+#pragma unroll
+    for (int t = 0; t < TM; ++t) asm volatile("" : "+v"(ov[1][t]));
+    issue_y(1, 1);
+    issue_x(wave + (int64_t)3 * W, 3);
+
+    const int nw = ksteps > wave ? (int)((ksteps - wave + W - 1) / W) : 0;
+    for (int i0 = 0; i0 < nw; i0 += LX) {
+#pragma unroll
+        for (int u = 0; u < LX; ++u) {
+            const int i = i0 + u;
+            if (i < nw) {
+                const int y = u % LY, u2 = (u + LY) % LX;
+                wait_vm<GY + GX>();
+#pragma unroll
+                for (int t = 0; t < TM; ++t)
+                    asm volatile("" : "+v"(av[u][t]), "+v"(mv[u][t]), "+v"(kv[u][t]), "+v"(ov[u][t]), "+v"(ov[u2][t]));
+                uint4 b[2];
+                load_b_operand<DT>(lds + wbase + u * C::BSTEP, 0, lane, b);
+#pragma unroll
+                for (int t = 0; t < TM; ++t) {
+                    uint4 f;
+                    __builtin_memcpy(&f, &av[u][t], 16);
+                    acc[t] = smfmac<DT>(f, b, acc[t], (uint32_t)mv[u][t]);
+                }
+#pragma unroll
+                for (int t = 0; t < TM; ++t) {
+                    const uint32_t mask = (uint32_t)kv[u][t];
+                    if (__builtin_amdgcn_ballot_w64(mask != 0u) != 0) {      // wave-uniform
+                        const int pc = __popc(mask);
+                        const uint32_t before = (uint32_t)(wave_incl_sum(pc, lane) - pc);
+                        const uint32_t ro0 = (uint32_t)ov[u][t][0];
+                        const uint32_t e0 = ((ro0 * T::ES) & 15u) / T::ES + before;
+                        const uint8_t* win = lds + ybase + (y * TM + t) * C::YWIN;
+                        const uint4 f = cbm_operand<DT>(win, zpad - (ybase + (uint32_t)((y * TM + t) * C::YWIN)), e0,
+                                                        mask);
+                        acc[t] = smfmac<DT>(f, b, acc[t], complement_index((uint32_t)mv[u][t]));
+                    }
+                }
+                // the slots' LDS reads are done before their next loads land
+                __builtin_amdgcn_s_waitcnt(0xC07F);
+                issue_y(u2, y);
+                issue_x(wave + (int64_t)W * (i + LX), u);
+            }
+        }
+    }
+    // the loads past the wave's last k-step land before the LDS is reused,
+    // and before their registers are (an asm load's output counts as
+    // written when issued, so the ring stays in use until the wait)
+    wait_vm<0>();
+#pragma unroll
+    for (int u = 0; u < LX; ++u)
+#pragma unroll
+        for (int t = 0; t < TM; ++t) asm volatile("" ::"v"(av[u][t]), "v"(mv[u][t]), "v"(kv[u][t]), "v"(ov[u][t]));
+    lds_barrier();
+
+    // fixed-order reduction of the waves' partial tiles
+    Acc* red = reinterpret_cast<Acc*>(lds);
+#pragma unroll
+    for (int t = 0; t < TM; ++t) red[(wave * kTMax + t) * 64 + lane] = acc[t];
+    lds_barrier();
+    const int64_t r0 = 16 * t0;
+    for (int i = threadIdx.x; i < nt * 256; i += blockDim.x) {
+        const int t = i >> 8, ln = (i >> 2) & 63, r = i & 3;
+        S sum = S(0);
+#pragma unroll
+        for (int w = 0; w < W; ++w) sum += reinterpret_cast<const S*>(red)[((w * kTMax + t) * 64 + ln) * 4 + r];
+        const int64_t row = r0 + 16 * t + 4 * (ln >> 4) + r;
+        const int col = ln & 15;
+        if (row < a.M && col < a.N) reinterpret_cast<S*>(a.C)[row * a.ldc + col] = sum;
+    }
+}
+
+template <int DT>
+hipError_t launch_packed_cbm_t(const SpmmArgs& a, const uint8_t* pv, const uint8_t* pm, const uint8_t* rmask,
+                               const int32_t* roff, const uint8_t* cvals, int64_t nvals, hipStream_t s) {
+    const int64_t tiles = (a.M + 15) / 16;
+    if (tiles <= 256) {
+        hipLaunchKernelGGL((k_spmm_packed_cbm<DT, 1>), dim3((unsigned)tiles), dim3(64 * kWaves),
+                           kWaves * Cbm<DT>::template wave_lds<1>(), s, a, pv, pm, rmask, roff, cvals, nvals, tiles);
+    } else {
+        hipLaunchKernelGGL((k_spmm_packed_cbm<DT, 2>), dim3((unsigned)((tiles + 1) / 2)), dim3(64 * kWaves),
+                           kWaves * Cbm<DT>::template wave_lds<2>(), s, a, pv, pm, rmask, roff, cvals, nvals, tiles);
+    }
+    return hipGetLastError();
+}
+
 // Ring depth of the packed product by tiles per workgroup: about 3 to 8
 // fragments (KiB) in flight per wave.  Deeper rings put most of a decode-size
 // operand in flight at once and measured slower (fp16 11008 x 4096: 12.5 us
@@ -1297,6 +1570,22 @@ hipError_t launch_spmm_packed(const SpmmArgs& a, const void* pvals, const void* 
         case DT_I8: return launch_packed_t<DT_I8>(a, pv, pm, s);
         case DT_E4M3: return launch_packed_t<DT_E4M3>(a, pv, pm, s);
         case DT_E5M2: return launch_packed_t<DT_E5M2>(a, pv, pm, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_spmm_packed_cbm(const SpmmArgs& a, const void* pvals, const void* pmeta, const void* rmask,
+                                  const int32_t* roff, const void* cvals, int64_t nvals, hipStream_t s) {
+    const uint8_t* pv = (const uint8_t*)pvals;
+    const uint8_t* pm = (const uint8_t*)pmeta;
+    const uint8_t* rk = (const uint8_t*)rmask;
+    const uint8_t* cv = (const uint8_t*)cvals;
+    switch (a.dt) {
+        case DT_F16: return launch_packed_cbm_t<DT_F16>(a, pv, pm, rk, roff, cv, nvals, s);
+        case DT_BF16: return launch_packed_cbm_t<DT_BF16>(a, pv, pm, rk, roff, cv, nvals, s);
+        case DT_I8: return launch_packed_cbm_t<DT_I8>(a, pv, pm, rk, roff, cv, nvals, s);
+        case DT_E4M3: return launch_packed_cbm_t<DT_E4M3>(a, pv, pm, rk, roff, cv, nvals, s);
+        case DT_E5M2: return launch_packed_cbm_t<DT_E5M2>(a, pv, pm, rk, roff, cv, nvals, s);
         default: return hipErrorInvalidValue;
     }
 }

@@ -71,6 +71,18 @@ hipError_t launch_pad_b(int dt, int64_t K, int64_t N, const void* B, int64_t ldb
 hipError_t launch_pack_decode(int dt, int64_t M, int64_t K, const void* vals, int64_t ldv, const uint8_t* meta,
                               int64_t ldm, void* pvals, void* pmeta, hipStream_t s);
 hipError_t launch_spmm_packed(const SpmmArgs& a, const void* pvals, const void* pmeta, hipStream_t s);
+// Complement-bitmap residual (residual_cbm.hip): blocks and mask bytes of
+// the layout, its encoder from a CSR residual and the 2:4 layer's row-major
+// metadata, and the packed decode product with it fused into every k-step
+// (B one contiguous K x 16 block; nvals = roff[blocks] values in cvals).
+void cbm_geometry(int dt, int64_t M, int64_t K, int64_t* blocks, int64_t* mask_bytes);
+hipError_t launch_pack_cbm(int dt, int64_t M, int64_t K, const uint8_t* meta, int64_t ldm, const int32_t* row_ptr,
+                           const int32_t* col, const void* rvals, int64_t nnz, void* rmask, int32_t* roff,
+                           void* cvals, int32_t* bad, hipStream_t s);
+hipError_t launch_spmm_packed_cbm(const SpmmArgs& a, const void* pvals, const void* pmeta, const void* rmask,
+                                  const int32_t* roff, const void* cvals, int64_t nvals, hipStream_t s);
+// Inclusive scan of a[1..n] in place, a[0] = 0 (one workgroup).
+hipError_t launch_scan_counts(int64_t n, int32_t* a, hipStream_t s);
 bool supported_large_n(const SpmmArgs& a);          // pipelined kernel or the basic one
 hipError_t launch_spmm_large_n(const SpmmArgs& a, hipStream_t s);
 bool supported_large_n_basic(const SpmmArgs& a);

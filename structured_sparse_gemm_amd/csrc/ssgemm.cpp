@@ -521,6 +521,74 @@ int ssg_spmm_2to4_packed_residual_delta(int ab, int c, int64_t M, int64_t N, int
 
 namespace {
 
+// Geometry of the complement-bitmap residual: K a multiple of the k-step,
+// every buffer within 31-bit offsets.
+int cbm_sizes(int dt, int64_t M, int64_t K, int64_t* mask_bytes, int64_t* blocks) {
+    if (!in_dtype(dt)) return fail(SSG_ERR_DTYPE, "element type %d is not SSG_F16, SSG_BF16, SSG_I8, SSG_E4M3 or SSG_E5M2", dt);
+    if (M < 0 || K < 0) return fail(SSG_ERR_SHAPE, "negative size M=%lld K=%lld", (long long)M, (long long)K);
+    if (K % kstep_of(dt) != 0)
+        return fail(SSG_ERR_SHAPE, "K=%lld is not a multiple of %lld", (long long)K, (long long)kstep_of(dt));
+    ssg::cbm_geometry(to_dt(dt), M, K, blocks, mask_bytes);
+    if (*mask_bytes >= 0x7fffffff || (*blocks + 1) * 4 >= 0x7fffffff)
+        return fail(SSG_ERR_SHAPE, "complement-bitmap residual too large (M=%lld, K=%lld)", (long long)M, (long long)K);
+    return SSG_OK;
+}
+
+}  // namespace
+
+int ssg_cbm_sizes(int dt, int64_t M, int64_t K, int64_t* mask_bytes, int64_t* blocks) {
+    if (!mask_bytes || !blocks) return fail(SSG_ERR_NULL, "size pointers are NULL");
+    return cbm_sizes(dt, M, K, mask_bytes, blocks);
+}
+
+int ssg_pack_residual_cbm(int dt, int64_t M, int64_t K, const uint8_t* meta, int64_t ldm, const int32_t* row_ptr,
+                          const int32_t* col, const void* rvals, int64_t nnz_r, uint8_t* rmask, int32_t* roff,
+                          void* cvals, int32_t* bad_count, void* stream) {
+    int64_t mbytes, blocks;
+    int rc = cbm_sizes(dt, M, K, &mbytes, &blocks);
+    if (rc) return rc;
+    if (nnz_r < 0 || nnz_r > INT32_MAX || nnz_r * esize(dt) >= 0x7fff0000)
+        return fail(SSG_ERR_FORMAT, "nnz_r=%lld out of range", (long long)nnz_r);
+    if (M > 0 && K > 0 && !meta) return fail(SSG_ERR_NULL, "meta is NULL");
+    if (ldm < (K + 7) / 8) return fail(SSG_ERR_STRIDE, "ldm=%lld < ceil(K/8)=%lld", (long long)ldm, (long long)((K + 7) / 8));
+    if (M > 0 && !row_ptr) return fail(SSG_ERR_NULL, "row_ptr is NULL");
+    if (nnz_r > 0 && (!col || !rvals || !cvals)) return fail(SSG_ERR_NULL, "col, rvals or cvals is NULL with nnz_r > 0");
+    if (!roff || (blocks > 0 && !rmask)) return fail(SSG_ERR_NULL, "rmask or roff is NULL");
+    hipError_t e = ssg::launch_pack_cbm(to_dt(dt), M, K, meta, ldm, row_ptr, col, rvals, nnz_r, rmask, roff, cvals,
+                                        bad_count, (hipStream_t)stream);
+    return e == hipSuccess ? SSG_OK : hip_fail(e, "complement-bitmap pack launch");
+}
+
+int ssg_spmm_2to4_packed_residual_cbm(int ab, int c, int64_t M, int64_t N, int64_t K, const void* pvals,
+                                      const void* pmeta, const uint8_t* rmask, const int32_t* roff, const void* cvals,
+                                      int64_t nvals, const void* B, int64_t ldb, void* C, int64_t ldc, void* stream) {
+    if (!pair_ok(ab, c)) return fail(SSG_ERR_DTYPE, "unsupported (input, output) types (%d, %d)", ab, c);
+    int64_t vb, mb, mbytes, blocks;
+    int rc = packed_sizes(ab, M, K, &vb, &mb);
+    if (rc) return rc;
+    rc = cbm_sizes(ab, M, K, &mbytes, &blocks);
+    if (rc) return rc;
+    if (M == 0) return SSG_OK;
+    if (N != 16 || ldb != 16)
+        return fail(SSG_ERR_ALGO, "the packed product takes N == 16 with ldb == 16 (got N=%lld, ldb=%lld)",
+                    (long long)N, (long long)ldb);
+    if (K == 0) return fail(SSG_ERR_SHAPE, "K must be positive");
+    if (!pvals || !pmeta || !B || !C || !rmask || !roff) return fail(SSG_ERR_NULL, "a required pointer is NULL");
+    if (nvals < 0 || nvals * esize(ab) >= 0x7fff0000) return fail(SSG_ERR_FORMAT, "nvals=%lld out of range", (long long)nvals);
+    if (nvals > 0 && !cvals) return fail(SSG_ERR_NULL, "cvals is NULL with nvals > 0");
+    if (!al(pvals, 16) || !al(pmeta, (uintptr_t)idx_bytes_of(ab)) || !al(B, 16) || !al(rmask, (uintptr_t)(esize(ab) == 1 ? 2 : 1)) ||
+        !al(roff, 4) || !al(cvals, 16))
+        return fail(SSG_ERR_STRIDE, "pvals, B and cvals must be 16-byte aligned, pmeta and rmask aligned to their words, "
+                                    "roff to 4 bytes");
+    if (ldc < N) return fail(SSG_ERR_STRIDE, "ldc=%lld < N=%lld", (long long)ldc, (long long)N);
+    if (K * 16 * esize(ab) >= 0x7fffffff) return fail(SSG_ERR_SHAPE, "B too large for 31-bit offsets");
+    ssg::SpmmArgs a = make_args(ab, M, N, K, nullptr, 0, nullptr, 0, B, ldb, C, ldc);
+    hipError_t e = ssg::launch_spmm_packed_cbm(a, pvals, pmeta, rmask, roff, cvals, nvals, (hipStream_t)stream);
+    return e == hipSuccess ? SSG_OK : hip_fail(e, "packed spmm (complement-bitmap residual) launch");
+}
+
+namespace {
+
 // Sizes of the packed prefill layout; fails on K not a multiple of the stage
 // (64 dense k for 16-bit types, 128 for 8-bit) or a tile's blocks beyond the
 // kernel's 31-bit offsets.
