@@ -420,6 +420,26 @@ int ssg_spmm_select_algo(int ab, int64_t M, int64_t N, int64_t K,
                          const void* vals, int64_t ldv, const uint8_t* meta, int64_t ldm,
                          const void* B, int64_t ldb, const void* C, int64_t ldc);
 
+/* For callers that cannot allocate device memory (code under HIP stream
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * product as ssg_spmm_2to4 with algorithm AUTO, without a workspace
+ * argument.  The one buffer the product may need -- B padded to 16 columns
+ * when 0 < N < 16 -- comes from a file-scope device array of the library of
+ * ssg_noalloc_scratch_bytes() = 2 MiB (K * 16 elements: K <= 65536 for
+ * 16-bit types, 131072 for 8-bit ones); a larger padded B fails with
+ * SSG_ERR_WORKSPACE and nothing is enqueued.  The call allocates nothing
+ * (no hipMalloc, hipFree or allocating library routine).  Each device the
+ * library runs on holds its own copy of the array until the process ends;
+ * its address on a device is looked up on the first call there, with that
+ * device current (the stream must belong to the current device).  Every
+ * call on a device shares that device's array and overwrites what the
+ * previous call left in it, so calls that may overlap on one device (on
+ * different streams, or from different host threads) race. */
+int64_t ssg_noalloc_scratch_bytes(void);
+int ssg_spmm_2to4_noalloc(int ab, int c, int64_t M, int64_t N, int64_t K,
+                          const void* vals, int64_t ldv, const uint8_t* meta, int64_t ldm,
+                          const void* B, int64_t ldb, void* C, int64_t ldc, void* stream);
+
 /* Complement-bitmap residual: the residual layer in the packed decode
  * product's block order, fused into its k-steps.  "How sparse LLM weights cut
  * GPU inference cost without quantization", section "How the three-layer

@@ -35,6 +35,7 @@ __all__ = [
     "compress_prefill", "pack_prefill", "spmm_prefill",
     "ssg_compress_nm", "ssg_decompress_nm", "ssg_spmm_nm", "compress_nm", "decompress_nm", "spmm_nm",
     "ssg_nm_packed_sizes", "ssg_pack_nm_decode", "ssg_spmm_nm_packed", "pack_nm", "spmm_nm_packed",
+    "ssg_noalloc_scratch_bytes", "ssg_spmm_2to4_noalloc",
     "ssg_cbm_sizes", "ssg_pack_residual_cbm", "ssg_spmm_2to4_packed_residual_cbm", "pack_residual_cbm",
     "spmm_packed_residual_cbm",
     "ssg_stream_read_sink_words", "ssg_stream_read",
@@ -321,6 +322,20 @@ def ssg_spmm_select_algo(vals, meta, B, C) -> int:
     return int(_lib().ssg_spmm_select_algo(_dtype(vals), vals.shape[0], B.shape[1], B.shape[0], _ptr(vals, "vals"),
                                            _ld(vals, "vals"), _ptr(meta, "meta"), _ld(meta, "meta"), _ptr(B, "B"),
                                            _ld(B, "B"), _ptr(C, "C"), _ld(C, "C")))
+
+
+def ssg_noalloc_scratch_bytes() -> int:
+    return int(_lib().ssg_noalloc_scratch_bytes())
+
+
+def ssg_spmm_2to4_noalloc(vals, meta, B, C, stream=None) -> None:
+    """ssg_spmm_2to4 without a workspace: nothing is allocated (the library's
+    own scratch array holds a padded narrow B)."""
+    ab = _dtype(vals)
+    M, N, K = vals.shape[0], B.shape[1], B.shape[0]
+    _check(_lib().ssg_spmm_2to4_noalloc(ab, _OUT[ab][0], M, N, K, _ptr(vals, "vals"), _ld(vals, "vals"),
+                                        _ptr(meta, "meta"), _ld(meta, "meta"), _ptr(B, "B"), _ld(B, "B"),
+                                        _ptr(C, "C"), _ld(C, "C"), _stream(C, stream)), "ssg_spmm_2to4_noalloc")
 
 
 def ssg_cbm_sizes(dtype: torch.dtype, M: int, K: int) -> Tuple[int, int]:

@@ -66,6 +66,8 @@ SIGNATURES = {
     "ssg_nm_packed_sizes": (_i, [_i, _i, _i, _i64, _i64, ctypes.POINTER(_i64), ctypes.POINTER(_i64)]),
     "ssg_pack_nm_decode": (_i, [_i, _i, _i, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _vp, _vp]),
     "ssg_spmm_nm_packed": (_i, [_i, _i, _i, _i, _i64, _i64, _i64, _vp, _vp, _vp, _i64, _vp, _i64, _vp]),
+    "ssg_noalloc_scratch_bytes": (_i64, []),
+    "ssg_spmm_2to4_noalloc": (_i, [_i, _i, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp]),
     "ssg_cbm_sizes": (_i, [_i, _i64, _i64, ctypes.POINTER(_i64), ctypes.POINTER(_i64)]),
     "ssg_pack_residual_cbm": (_i, [_i, _i64, _i64, _vp, _i64, _vp, _vp, _vp, _i64, _vp, _vp, _vp, _vp, _vp]),
     "ssg_spmm_2to4_packed_residual_cbm": (_i, [_i, _i, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _i64, _vp, _i64, _vp,

@@ -1,7 +1,8 @@
 // ssgemm.cpp -- the C ABI of libssgemm (include/ssgemm.h): host-side
 // argument validation, alignment checks and kernel dispatch.  Nothing here
-// allocates device memory or keeps mutable global state; the only
-// per-thread state is the text of the last error.
+// allocates device memory.  The mutable state is the per-thread text of the
+// last error and, for the entry point that allocates nothing, the device
+// address of its file-scope scratch array on each device it has run on.
 #include "ssgemm.h"
 
 #include <hip/hip_runtime.h>
@@ -9,6 +10,7 @@
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
+#include <mutex>
 #include <string>
 
 #include "ssg_kernels.hpp"
@@ -860,3 +862,69 @@ int ssg_spmm_select_algo(int ab, int64_t M, int64_t N, int64_t K, const void* va
 
 }  // extern "C"
 
+// ---- the product that allocates nothing --------------------------------------
+//
+// For callers that cannot allocate (code under stream capture, tight serving
+// loops): ssg_spmm_2to4_noalloc takes its padded copy of a narrow B from a
+// file-scope device array instead of a caller workspace.  Each device holds
+// its own copy of the array until the process ends; its address on a device
+// is looked up once, with that device current, and kept.  In host code the
+// array's name is not a device address: only the looked-up pointer is ever
+// passed to a kernel.
+
+namespace {
+
+constexpr int64_t kScratchBytes = (int64_t)2 << 20;   // B padded to K x 16: K <= 65536 (16-bit), 131072 (8-bit)
+constexpr int kScratchDevices = 64;
+
+__device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kScratchDevices] = {};
+
+// Device address of `scratch` on the current device (looked up on the first
+// call there).
+int scratch_for_current_device(void** out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if (dev < 0 || dev >= kScratchDevices)
+        return fail(SSG_ERR_HIP, "device %d is beyond the %d devices the scratch table holds", dev, kScratchDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return SSG_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int64_t ssg_noalloc_scratch_bytes(void) { return kScratchBytes; }
+
+int ssg_spmm_2to4_noalloc(int ab, int c, int64_t M, int64_t N, int64_t K, const void* vals, int64_t ldv,
+                          const uint8_t* meta, int64_t ldm, const void* B, int64_t ldb, void* C, int64_t ldc,
+                          void* stream) {
+    int rc = check_spmm(ab, c, M, N, K, vals, ldv, meta, ldm, B, ldb, C, ldc);
+    if (rc) return rc;
+    const ssg::SpmmArgs a = make_args(ab, M, N, K, vals, ldv, meta, ldm, B, ldb, C, ldc);
+    const int64_t need = pad_need(SSG_ALGO_AUTO, a);
+    if (need > kScratchBytes)
+        return fail(SSG_ERR_WORKSPACE,
+                    "the padded B (K=%lld x 16 columns, %lld bytes) exceeds the %lld-byte scratch of the no-alloc "
+                    "product; call ssg_spmm_2to4 with a workspace",
+                    (long long)K, (long long)need, (long long)kScratchBytes);
+    void* ws = nullptr;
+    if (need > 0) {
+        rc = scratch_for_current_device(&ws);
+        if (rc) return rc;
+    }
+    return run_spmm(SSG_ALGO_AUTO, a, (hipStream_t)stream, ws);
+}
+
+}  // extern "C"

@@ -53,6 +53,19 @@ def test_version_and_sizes(lib):
     assert lib.ssg_spmm_workspace_bytes(F16, 11008, 16, 4096) == 0
 
 
+def test_noalloc_rejects_a_padded_b_beyond_its_scratch(lib):
+    # checked on the host before anything is enqueued
+    cap = lib.ssg_noalloc_scratch_bytes()
+    assert cap == 2 << 20
+    K = cap // 32 + 64
+    assert lib.ssg_spmm_2to4_noalloc(F16, F32, 8, 5, K, FAKE, K // 2, FAKE, K // 8, FAKE, 5, FAKE, 5,
+                                     None) == _abi.SSG_ERR_WORKSPACE
+    assert "scratch" in lib.ssg_last_error().decode()
+    assert lib.ssg_spmm_2to4_noalloc(F16, I32, 8, 5, 64, FAKE, 32, FAKE, 8, FAKE, 5, FAKE, 5,
+                                     None) == _abi.SSG_ERR_DTYPE
+    assert lib.ssg_spmm_2to4_noalloc(F16, F32, 0, 5, 64, FAKE, 32, FAKE, 8, FAKE, 5, FAKE, 5, None) == 0
+
+
 def test_workspace_size_and_requirement(lib):
     ws = lib.ssg_spmm_workspace_bytes
     # B padded to K x 16 elements, rounded up to 256 bytes, for 0 < N < 16 only
