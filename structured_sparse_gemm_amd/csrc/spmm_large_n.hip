@@ -78,10 +78,11 @@ template <> struct PT<DT_I8> {
 template <> struct PT<DT_E4M3> : PT<DT_I8> {};   // 8-bit floats: the int8 shapes
 template <> struct PT<DT_E5M2> : PT<DT_I8> {};
 
-template <int DT>
+template <int DT, int BN = kBN>
 struct Lay {
     using T = PT<DT>;
-    static constexpr int ROWB = kBN * T::ES;               // B tile row bytes
+    static constexpr int NJ = BN / 64;                     // 32-column MFMA tiles per wave
+    static constexpr int ROWB = BN * T::ES;                // B tile row bytes
     static constexpr int CPR = ROWB / 16;                  // 16-byte chunks per row
     static constexpr int B_BYTES = T::BK * ROWB;           // 32 KiB
     static constexpr int A_ROWB = T::BK / 2 * T::ES;      // stored bytes per row per stage (64)
@@ -96,6 +97,7 @@ struct Lay {
     static constexpr int VM_PER_STAGE = B_LOADS + A_LOADS;
     static_assert(A_ROWB == 64 && MBLK_ROWB == 32, "layout");
     static_assert(LDS <= 160 * 1024, "LDS");
+    static_assert(B_LOADS % NJ == 0 && B_LOADS >= 1, "B loads per wave per stage");
 };
 
 // 16-byte chunk c of row r of the sparse-value tile sits at chunk
@@ -105,8 +107,10 @@ struct Lay {
 // (the packed prefill layout stores its blocks in this same order)
 __device__ __forceinline__ int swz_a(int r) { return prefill_swz(r); }
 
-template <int DT> __device__ __forceinline__ int swz(int r) {
-    if constexpr (dt_bytes(DT) == 1) return 2 * (r & 7);
+template <int DT, int BN = kBN> __device__ __forceinline__ int swz(int r) {
+    // a permutation of the row's 16-byte chunks (8-bit rows of 128 columns
+    // have 8 of them)
+    if constexpr (dt_bytes(DT) == 1) return BN == 256 ? 2 * (r & 7) : 2 * (r & 3);
     else return 4 * (r & 3);
 }
 
@@ -152,9 +156,9 @@ __device__ __forceinline__ Acc16<DT> mma(uint4 a, const uint4 (&b)[2], Acc16<DT>
 // k-step, H = 8 (16-bit) / 16 (int8).  Transposing reads act on 16-lane
 // groups: source lane 4q+r (tr16) / 2q+r (tr8) names a row and 4 / 8
 // consecutive columns; output lane i gets column i of 4 / 8 consecutive rows.
-template <int DT>
+template <int DT, int BN>
 __device__ __forceinline__ void b_frag(const uint8_t* bt, int s, int cb, int lane, uint4 (&b)[2]) {
-    using L = Lay<DT>;
+    using L = Lay<DT, BN>;
     const int bb = lane >> 5, h = (lane >> 4) & 1, i = lane & 15;
     if constexpr (dt_bytes(DT) == 1) {
         const int q = i >> 1, r = i & 1;
@@ -164,7 +168,7 @@ __device__ __forceinline__ void b_frag(const uint8_t* bt, int s, int cb, int lan
         for (int p = 0; p < 4; ++p) {
             const int row = s * 64 + (p >> 1) * 32 + 16 * bb + (p & 1) * 8 + q;
             v[p] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-                (lds_i32x2*)(bt + row * L::ROWB + ((c ^ swz<DT>(row)) << 4) + 8 * r));
+                (lds_i32x2*)(bt + row * L::ROWB + ((c ^ swz<DT, BN>(row)) << 4) + 8 * r));
         }
         b[0] = make_uint4(v[0][0], v[0][1], v[1][0], v[1][1]);
         b[1] = make_uint4(v[2][0], v[2][1], v[3][0], v[3][1]);
@@ -176,7 +180,7 @@ __device__ __forceinline__ void b_frag(const uint8_t* bt, int s, int cb, int lan
         for (int p = 0; p < 4; ++p) {
             const int row = s * 32 + (p >> 1) * 16 + 8 * bb + (p & 1) * 4 + q;
             i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (lds_i16x4*)(bt + row * L::ROWB + ((c ^ swz<DT>(row)) << 4) + 8 * (r & 1)));
+                (lds_i16x4*)(bt + row * L::ROWB + ((c ^ swz<DT, BN>(row)) << 4) + 8 * (r & 1)));
             __builtin_memcpy(&w[p], &v, 8);
         }
         b[0] = make_uint4(w[0].x, w[0].y, w[1].x, w[1].y);
@@ -248,14 +252,13 @@ __device__ __forceinline__ void interleave() {
     }
 }
 
-// LDS reads of one k-step's operands: 4 sparse fragments, 4 x 4 transposing
+// LDS reads of one k-step's operands: 4 sparse fragments, NJ x 4 transposing
 // reads of B and 4 index words
-constexpr int kOpsReads = 4 + 16 + 4;
 
 // Issue the direct-to-LDS loads of stage `it` into `st` (this wave's share).
-template <int DT>
+template <int DT, int BN>
 __device__ __forceinline__ void issue(const Ctx& x, uint8_t* st, int64_t it, int wave) {
-    using L = Lay<DT>;
+    using L = Lay<DT, BN>;
     using T = PT<DT>;
     const __amdgpu_buffer_rsrc_t rb = rsrc(x.bbase + it * x.bstage, x.bbytes - it * x.bstage);
     const __amdgpu_buffer_rsrc_t ra = rsrc(x.vbase + it * x.vstage, x.vbytes - it * x.vstage);
@@ -267,38 +270,29 @@ __device__ __forceinline__ void issue(const Ctx& x, uint8_t* st, int64_t it, int
 
 // Issue the direct-to-LDS loads of metadata block `g` (the 32 bytes of each
 // of the tile's rows that cover stages [g * MB, (g + 1) * MB)) into `mt`.
-template <int DT>
+template <int DT, int BN>
 __device__ __forceinline__ void issue_meta(const Ctx& x, uint8_t* mt, int64_t g, int wave) {
-    using L = Lay<DT>;
+    using L = Lay<DT, BN>;
     const __amdgpu_buffer_rsrc_t rm = rsrc(x.mbase + g * x.mstep, x.mbytes - g * x.mstep);
 #pragma unroll
     for (int j = 0; j < L::M_LOADS; ++j) dma<4>(rm, mt + (wave * L::M_LOADS + j) * 256, x.moff[j]);
 }
 
-template <int DT, bool PK>
-__global__ void __launch_bounds__(kThreads) k_spmm_pipe(SpmmArgs a, int tiles_m, int tiles_n) {
+// Tile (tm, tn) of width BN (256, or 128 for the half-width tiles that fill
+// the last wave of a launch): rows [256 tm, +256), columns [BN tn, +BN).
+template <int DT, bool PK, int BN>
+__device__ __forceinline__ void spmm_tile(const SpmmArgs& a, int tm, int tn, uint8_t* lds) {
     using T = PT<DT>;
-    using L = Lay<DT>;
+    using L = Lay<DT, BN>;
     using Acc = Acc16<DT>;
     using S = typename std::conditional<DT == DT_I8, int32_t, float>::type;
-    __shared__ __attribute__((aligned(1024))) uint8_t lds[L::LDS];
+    constexpr int NJ = L::NJ;
     uint8_t* const mlds = lds + kStages * L::STAGE;   // two metadata blocks
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wm = wave >> 1, wn = wave & 1;
-
-    // XCD-aware tile order
-    const int tiles = tiles_m * tiles_n;
-    int bid = blockIdx.x;
-    const int per_xcd = tiles / 8;
-    if (bid < per_xcd * 8) bid = (bid & 7) * per_xcd + (bid >> 3);
-    const int group = bid / (kGroupM * tiles_n);
-    const int first_m = group * kGroupM;
-    const int gm = min(kGroupM, tiles_m - first_m);
-    const int in_group = bid - group * kGroupM * tiles_n;
-    const int tm = first_m + in_group % gm, tn = in_group / gm;
-    const int64_t m0 = (int64_t)tm * kBM, n0 = (int64_t)tn * kBN;
+    const int64_t m0 = (int64_t)tm * kBM, n0 = (int64_t)tn * BN;
 
     // per-lane load offsets (constant across stages)
     const int64_t nit = a.K / T::BK;
@@ -327,7 +321,7 @@ __global__ void __launch_bounds__(kThreads) k_spmm_pipe(SpmmArgs a, int tiles_m,
 #pragma unroll
     for (int j = 0; j < L::B_LOADS; ++j) {
         const int slot = (wave * L::B_LOADS + j) * 64 + lane;
-        const int r = slot / L::CPR, c = (slot % L::CPR) ^ swz<DT>(r);
+        const int r = slot / L::CPR, c = (slot % L::CPR) ^ swz<DT, BN>(r);
         x.boff[j] = (n0 + (int64_t)c * T::EPC < a.N) ? (uint32_t)((r * a.ldb + c * T::EPC) * T::ES) : kOob;
     }
 #pragma unroll
@@ -346,11 +340,11 @@ __global__ void __launch_bounds__(kThreads) k_spmm_pipe(SpmmArgs a, int tiles_m,
         if constexpr (PK) x.moff[j] = (uint32_t)((wave * L::M_LOADS + j) * 256 + lane * 4);
     }
 
-    Acc acc[4][4];
+    Acc acc[4][NJ];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < NJ; ++j)
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[i][j][e] = S(0);
 
@@ -360,7 +354,7 @@ __global__ void __launch_bounds__(kThreads) k_spmm_pipe(SpmmArgs a, int tiles_m,
     // fragments of this wave's row tiles and 4 B fragments of its columns.
     struct Ops {
         uint4 av[4];
-        uint4 b[4][2];
+        uint4 b[NJ][2];
     };
     auto read_ops = [&](const uint8_t* st, int s, Ops& o) {
 #pragma unroll
@@ -370,7 +364,7 @@ __global__ void __launch_bounds__(kThreads) k_spmm_pipe(SpmmArgs a, int tiles_m,
                                                       (((2 * s + q) ^ swz_a(row)) << 4));
         }
 #pragma unroll
-        for (int j = 0; j < 4; ++j) b_frag<DT>(st, s, wn * 128 + 32 * j, lane, o.b[j]);
+        for (int j = 0; j < NJ; ++j) b_frag<DT, BN>(st, s, wn * (BN / 2) + 32 * j, lane, o.b[j]);
     };
     // Index word of sub-step s of stage t for this lane, read so that no
     // per-lane selection follows the read: 16-bit -- the 16 bits at byte
@@ -401,7 +395,7 @@ __global__ void __launch_bounds__(kThreads) k_spmm_pipe(SpmmArgs a, int tiles_m,
     };
     auto mmas = [&](const Ops& o, const uint32_t (&ix)[4]) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < NJ; ++j)
 #pragma unroll
             for (int i = 0; i < 4; ++i) acc[i][j] = mma<DT>(o.av[i], o.b[j], acc[i][j], ix[i]);
     };
@@ -417,13 +411,13 @@ __global__ void __launch_bounds__(kThreads) k_spmm_pipe(SpmmArgs a, int tiles_m,
     // after every wave's last read of block g - 2, whose buffer it takes) and
     // is first read MB - 1 iterations later.  The wait of an iteration that
     // follows such an issue leaves the block's loads outstanding too.
-    issue_meta<DT>(x, mlds, 0, wave);
-    issue<DT>(x, lds, 0, wave);
-    issue<DT>(x, lds + L::STAGE, 1, wave);
+    issue_meta<DT, BN>(x, mlds, 0, wave);
+    issue<DT, BN>(x, lds, 0, wave);
+    issue<DT, BN>(x, lds + L::STAGE, 1, wave);
     wait_vm<L::VM_PER_STAGE>();
     barrier();
-    issue<DT>(x, lds + 2 * L::STAGE, 2, wave);
-    issue_meta<DT>(x, mlds + L::MBLK, 1, wave);
+    issue<DT, BN>(x, lds + 2 * L::STAGE, 2, wave);
+    issue_meta<DT, BN>(x, mlds + L::MBLK, 1, wave);
 
     Ops o0, o1;
     uint32_t ix0[4], ix1[4];
@@ -435,7 +429,7 @@ __global__ void __launch_bounds__(kThreads) k_spmm_pipe(SpmmArgs a, int tiles_m,
         read_ops(st, 1, o1);
         read_idx(it, 1, ix1);
         mmas(o0, ix0);
-        interleave<16, kOpsReads>();
+        interleave<4 * NJ, 4 + 4 * NJ + 4>();
         // stage it+1 has landed once only stage it+2's loads remain; this
         // wave's reads of stage it are done (s_waitcnt lgkmcnt(0), through the
         // builtin so the compiler knows they have landed) before the barrier
@@ -445,8 +439,9 @@ __global__ void __launch_bounds__(kThreads) k_spmm_pipe(SpmmArgs a, int tiles_m,
         __builtin_amdgcn_s_waitcnt(0xC07F);
         barrier();
         uint8_t* const dst = lds + slot * L::STAGE;
-        if constexpr (!PK) issue<DT>(x, dst, it + 3, wave);
-        if ((it + 1) % T::MB == 0) issue_meta<DT>(x, mlds + (((it + 1) / T::MB + 1) & 1) * L::MBLK, (it + 1) / T::MB + 1, wave);
+        if constexpr (!PK) issue<DT, BN>(x, dst, it + 3, wave);
+        if ((it + 1) % T::MB == 0)
+            issue_meta<DT, BN>(x, mlds + (((it + 1) / T::MB + 1) & 1) * L::MBLK, (it + 1) / T::MB + 1, wave);
         slot = slot == kStages - 1 ? 0 : slot + 1;
         const uint8_t* nx = lds + slot * L::STAGE;
         if constexpr (PK) {
@@ -454,7 +449,8 @@ __global__ void __launch_bounds__(kThreads) k_spmm_pipe(SpmmArgs a, int tiles_m,
             // of the next k-step so they leave the wave between its MFMAs
             const __amdgpu_buffer_rsrc_t rb = rsrc(x.bbase + (it + 3) * x.bstage, x.bbytes - (it + 3) * x.bstage);
             const __amdgpu_buffer_rsrc_t ra = rsrc(x.vbase + (it + 3) * x.vstage, x.vbytes - (it + 3) * x.vstage);
-            static_assert(L::A_LOADS == 4 && L::B_LOADS == 8, "spread issue assumes 4 + 8 loads per stage");
+            static_assert(L::A_LOADS == 4, "spread issue assumes 4 loads of values per stage");
+            constexpr int BPJ = L::B_LOADS / NJ;        // B loads placed after each column tile's reads
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int row = 32 * (wm * 4 + i) + rl;
@@ -462,17 +458,18 @@ __global__ void __launch_bounds__(kThreads) k_spmm_pipe(SpmmArgs a, int tiles_m,
                 dma<16>(ra, dst + L::B_BYTES + (wave * L::A_LOADS + i) * 1024, x.aoff[i]);
             }
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                b_frag<DT>(nx, 0, wn * 128 + 32 * j, lane, o0.b[j]);
-                dma<16>(rb, dst + (wave * L::B_LOADS + 2 * j) * 1024, x.boff[2 * j]);
-                dma<16>(rb, dst + (wave * L::B_LOADS + 2 * j + 1) * 1024, x.boff[2 * j + 1]);
+            for (int j = 0; j < NJ; ++j) {
+                b_frag<DT, BN>(nx, 0, wn * (BN / 2) + 32 * j, lane, o0.b[j]);
+#pragma unroll
+                for (int u = 0; u < BPJ; ++u)
+                    dma<16>(rb, dst + (wave * L::B_LOADS + BPJ * j + u) * 1024, x.boff[BPJ * j + u]);
             }
         } else {
             read_ops(nx, 0, o0);
         }
         read_idx(it + 1, 0, ix0);
         mmas(o1, ix1);
-        interleave<16, kOpsReads>();
+        interleave<4 * NJ, 4 + 4 * NJ + 4>();
     }
     // the zero-filling loads of the stages past K land before the LDS is released
     wait_vm<0>();
@@ -483,8 +480,8 @@ __global__ void __launch_bounds__(kThreads) k_spmm_pipe(SpmmArgs a, int tiles_m,
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int64_t col = n0 + wn * 128 + 32 * j + rl;
+        for (int j = 0; j < NJ; ++j) {
+            const int64_t col = n0 + wn * (BN / 2) + 32 * j + rl;
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
                 const int64_t row = m0 + wm * 128 + 32 * i + 8 * (e >> 2) + 4 * q + (e & 3);
@@ -492,6 +489,42 @@ __global__ void __launch_bounds__(kThreads) k_spmm_pipe(SpmmArgs a, int tiles_m,
                     __builtin_nontemporal_store((S)acc[i][j][e], reinterpret_cast<S*>(a.C) + row * a.ldc + col);
             }
         }
+    }
+}
+
+// One launch: tiles of full width for row tiles [0, full_rows), and two
+// half-width tiles per tile for row tiles [full_rows, tiles_m), dispatched
+// after the full ones.  When the tiles of a launch leave the last wave of
+// workgroups at most half full, its tiles are cut in half so that the last
+// wave is full of half-length work instead of half empty.  An output's k
+// order is the same in both widths, so the result is the same bits.  Within
+// each part the order is XCD-aware: workgroups are dealt round-robin to the
+// 8 XCDs, and each XCD gets a contiguous range of tiles, walked kGroupM row
+// tiles at a time, so the tiles in flight on an XCD share their A and B
+// panels in its L2.
+__device__ __forceinline__ void xcd_order(int bid, int tiles_m, int tiles_n, int* tm, int* tn) {
+    const int tiles = tiles_m * tiles_n;
+    const int per_xcd = tiles / 8;
+    if (bid < per_xcd * 8) bid = (bid & 7) * per_xcd + (bid >> 3);
+    const int group = bid / (kGroupM * tiles_n);
+    const int first_m = group * kGroupM;
+    const int gm = min(kGroupM, tiles_m - first_m);
+    const int in_group = bid - group * kGroupM * tiles_n;
+    *tm = first_m + in_group % gm;
+    *tn = in_group / gm;
+}
+
+template <int DT, bool PK>
+__global__ void __launch_bounds__(kThreads) k_spmm_pipe(SpmmArgs a, int tiles_m, int tiles_n, int full_rows) {
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[Lay<DT>::LDS];
+    const int nfull = full_rows * tiles_n;
+    int tm, tn;
+    if ((int)blockIdx.x < nfull) {
+        xcd_order(blockIdx.x, full_rows, tiles_n, &tm, &tn);
+        spmm_tile<DT, PK, kBN>(a, tm, tn, lds);
+    } else {
+        xcd_order(blockIdx.x - nfull, tiles_m - full_rows, 2 * tiles_n, &tm, &tn);
+        spmm_tile<DT, PK, kBN / 2>(a, full_rows + tm, tn, lds);
     }
 }
 
@@ -509,10 +542,25 @@ bool pipe_supported(const SpmmArgs& a) {
            ((a.K - 1) * a.ldb + a.N) * T::ES < 0x7fffffff && tiles < 0x7fffffff;
 }
 
+// Row tiles that run at full width: all of them, unless the launch's last
+// wave of workgroups (256 CUs) would be at most half full -- then enough of
+// the last row tiles run as half-width tiles to fill it with half-length
+// work (the converted tiles number between the remainder and 256 minus it,
+// so the launch needs no more waves than before).
+int full_row_tiles(int tiles_m, int tiles_n) {
+    constexpr int kCUs = 256;
+    const int tiles = tiles_m * tiles_n, rem = tiles % kCUs;
+    if (rem == 0) return tiles_m;
+    const int half_rows = (rem + tiles_n - 1) / tiles_n, conv = half_rows * tiles_n;
+    return conv <= kCUs - rem ? tiles_m - half_rows : tiles_m;
+}
+
 template <int DT, bool PK = false>
 hipError_t pipe_launch(const SpmmArgs& a, hipStream_t s) {
     const int tm = (int)((a.M + kBM - 1) / kBM), tn = (int)((a.N + kBN - 1) / kBN);
-    hipLaunchKernelGGL((k_spmm_pipe<DT, PK>), dim3((unsigned)(tm * tn)), dim3(kThreads), 0, s, a, tm, tn);
+    const int full = full_row_tiles(tm, tn);
+    const unsigned grid = (unsigned)(full * tn + 2 * (tm - full) * tn);
+    hipLaunchKernelGGL((k_spmm_pipe<DT, PK>), dim3(grid), dim3(kThreads), 0, s, a, tm, tn, full);
     return hipGetLastError();
 }
 

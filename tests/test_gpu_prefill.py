@@ -128,6 +128,26 @@ def test_spmm_prefill_argument_errors():
     assert e.value.status == 2
 
 
+@pytest.mark.parametrize("dt", ["bf16", "i8"])
+def test_spmm_prefill_mixed_widths(dt):
+    # 20 x 13 = 260 tiles: the last wave of 256 CUs would hold 4 tiles, so
+    # the last row of 13 tiles runs as 26 half-width tiles in the same
+    # launch; every output against the oracle, and the same bits as the
+    # row-major operand (which takes the same split)
+    K = 128 if dt == "bf16" else 256
+    M, N = 256 * 20 - 37, 256 * 13 - 48
+    a = U.random_matrix(dt, M, K, "normal", seed=31)
+    b = U.random_matrix(dt, K, N, "normal", seed=37)
+    vals, meta = oracle.compress(dt, a)
+    pv, pm = ssg.compress_prefill(to_dev(a, dt))
+    B = to_dev(b, dt)
+    C = ssg.spmm_prefill(pv, pm, M, B)
+    cref, sref = oracle.spmm(dt, vals, meta, b, K)
+    check_product(dt, C.cpu().numpy(), cref, sref, "prefill mixed widths %s" % dt)
+    C_rm = ssg.spmm(to_dev(vals, dt), dev_or_empty(meta), B, algo=ssg.SSG_ALGO_LARGE_N)
+    assert torch.equal(C.view(torch.int32), C_rm.view(torch.int32))
+
+
 @pytest.mark.parametrize("key", ["c2", "c4"])
 def test_full_size_prefill(key):
     w = W.WORKLOADS[key]
@@ -146,6 +166,18 @@ def test_full_size_prefill(key):
     assert torch.equal(C.view(torch.int32), C_rm.view(torch.int32))
     del C_rm
     r = oracle.compress(w.dtype, a)
-    ms, ns = sample_entries(w.M, w.N, 3000, seed=w.index + 70)
-    cref, sref = oracle.spmm_entries(w.dtype, r[0], r[1], b, w.K, ms, ns)
-    check_product(w.dtype, C.cpu().numpy()[ms, ns], cref, sref, key + " packed prefill")
+    Ch = C.cpu().numpy()
+    if key == "c2":
+        # int8 4096^3: every output (the oracle's int64 sums, exact)
+        cref, _ = oracle.spmm(w.dtype, r[0], r[1], b, w.K)
+        assert np.array_equal(Ch.astype(np.int64), cref), "c2 packed prefill (all outputs)"
+    else:
+        # bf16 28672 x 8192 x 2048: whole rows spanning every row-tile
+        # position and all eight column tiles (both the full-width tiles and
+        # the half-width ones of the last rows), plus a random sample
+        rows = np.unique(np.concatenate([np.arange(0, w.M, 997), [255, 256, 24575, 24576, w.M - 1]]))
+        cref, sref = oracle.spmm(w.dtype, r[0][rows], r[1][rows], b, w.K)
+        check_product(w.dtype, Ch[rows], cref, sref, key + " packed prefill (whole rows)")
+        ms, ns = sample_entries(w.M, w.N, 3000, seed=w.index + 70)
+        cref, sref = oracle.spmm_entries(w.dtype, r[0], r[1], b, w.K, ms, ns)
+        check_product(w.dtype, Ch[ms, ns], cref, sref, key + " packed prefill")
