@@ -52,7 +52,7 @@ namespace ssg {
 namespace {
 
 constexpr int kBM = 256, kBN = 256, kStages = 3, kThreads = 256;
-constexpr int kGroupM = 4;             // row tiles walked together per XCD
+constexpr int kGroupM = 8;             // row tiles walked together per XCD
 constexpr uint32_t kOob = 0x80000000u; // buffer offset that reads as zero
 
 template <int DT> struct PT;

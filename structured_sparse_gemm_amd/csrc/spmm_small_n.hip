@@ -1116,11 +1116,10 @@ __device__ __forceinline__ uint4 cbm_operand(const uint8_t* win, uint32_t zoff, 
 // a block's values reads zero from an out-of-range offset), so the waits
 // are exact counts.  Partial tiles are summed in wave order as in the
 // plain packed product.
-template <int DT, int TM>
-__global__ void __launch_bounds__(kWaves * 64) k_spmm_packed_cbm(SpmmArgs a, const uint8_t* pvals, const uint8_t* pmeta,
-                                                                 const uint8_t* rmask, const int32_t* roff,
-                                                                 const uint8_t* cvals, int64_t nvals, int64_t tiles) {
-    constexpr int W = kWaves;
+template <int DT, int TM, int W>
+__global__ void __launch_bounds__(W * 64) k_spmm_packed_cbm(SpmmArgs a, const uint8_t* pvals, const uint8_t* pmeta,
+                                                            const uint8_t* rmask, const int32_t* roff,
+                                                            const uint8_t* cvals, int64_t nvals, int64_t tiles) {
     using T = SN<DT>;
     using C = Cbm<DT>;
     using Acc = AccT<DT>;
@@ -1290,17 +1289,19 @@ __global__ void __launch_bounds__(kWaves * 64) k_spmm_packed_cbm(SpmmArgs a, con
     }
 }
 
+template <int DT, int TM, int W>
+void launch_packed_cbm_w(const SpmmArgs& a, const uint8_t* pv, const uint8_t* pm, const uint8_t* rmask,
+                         const int32_t* roff, const uint8_t* cvals, int64_t nvals, int64_t tiles, hipStream_t s) {
+    hipLaunchKernelGGL((k_spmm_packed_cbm<DT, TM, W>), dim3((unsigned)((tiles + TM - 1) / TM)), dim3(64 * W),
+                       W * Cbm<DT>::template wave_lds<TM>(), s, a, pv, pm, rmask, roff, cvals, nvals, tiles);
+}
+
 template <int DT>
 hipError_t launch_packed_cbm_t(const SpmmArgs& a, const uint8_t* pv, const uint8_t* pm, const uint8_t* rmask,
                                const int32_t* roff, const uint8_t* cvals, int64_t nvals, hipStream_t s) {
     const int64_t tiles = (a.M + 15) / 16;
-    if (tiles <= 256) {
-        hipLaunchKernelGGL((k_spmm_packed_cbm<DT, 1>), dim3((unsigned)tiles), dim3(64 * kWaves),
-                           kWaves * Cbm<DT>::template wave_lds<1>(), s, a, pv, pm, rmask, roff, cvals, nvals, tiles);
-    } else {
-        hipLaunchKernelGGL((k_spmm_packed_cbm<DT, 2>), dim3((unsigned)((tiles + 1) / 2)), dim3(64 * kWaves),
-                           kWaves * Cbm<DT>::template wave_lds<2>(), s, a, pv, pm, rmask, roff, cvals, nvals, tiles);
-    }
+    if (tiles <= 256) launch_packed_cbm_w<DT, 1, kWaves>(a, pv, pm, rmask, roff, cvals, nvals, tiles, s);
+    else launch_packed_cbm_w<DT, 2, kWaves>(a, pv, pm, rmask, roff, cvals, nvals, tiles, s);
     return hipGetLastError();
 }
 
