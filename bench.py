@@ -1,6 +1,7 @@
 """Benchmark of the 2:4 SpMM hot path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]
+    python bench.py --mfma-rates      # sparse vs dense matrix-core issue rates
 
 Headline workload: the largest configuration, the bf16 prefill-shape 2:4
 SpMM M=28672 K=8192 N=2048 (A ~ N(0, 0.02^2) magnitude-pruned 2:4 along K,
@@ -16,7 +17,9 @@ Also printed, in the same JSON line:
   the stream it runs on; achieved = algorithmic flops (M*N*K: two per stored
   non-zero product) / duration, against the dense bf16 MFMA peak; traffic
   from the committed rocprofv3 counter summary if it was taken on the current
-  kernel source, else null;
+  kernel source, else null; measured_instr_ceiling: the issue rate of the
+  kernel's sparse MFMA form (and of the dense form a decode-to-dense kernel
+  would issue) from the library's instruction probe;
 * cpu_baseline: the CPU oracle (plain C, fp64) timed on this host on a
   bounded sample of rows of the same workload, checked against the GPU rows;
 * oracle_baselines: the oracle on every configuration (single thread for the
@@ -201,6 +204,36 @@ def read_bandwidth_GBps(nbytes: int, reps: int = 2) -> float:
     return _READ_BW[nbytes]
 
 
+_MFMA = {}
+
+
+def mfma_rate(form: int, per_cu: int = 1, iters: int = 2000, reps: int = 3) -> float:
+    """Dense-equivalent rate (TFLOP/s or TOPS) of one matrix-core instruction
+    form: the library's issue-rate probe on per_cu workgroups of four waves
+    per CU (one wave per SIMD for per_cu = 1), best of `reps` launches timed
+    with HIP events on the current stream."""
+    import torch
+
+    import structured_sparse_gemm_amd as ssg
+    if (form, per_cu, iters) in _MFMA:
+        return _MFMA[(form, per_cu, iters)]
+    wg = per_cu * torch.cuda.get_device_properties(0).multi_processor_count
+    sink = torch.zeros(wg, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+    ssg.ssg_mfma_probe(form, wg, 10, sink)                   # warm-up
+    best = min(time_kernel(lambda i: ssg.ssg_mfma_probe(form, wg, iters, sink), 1, stream) for _ in range(reps))
+    _MFMA[(form, per_cu, iters)] = ssg.ssg_mfma_probe_ops(form, wg, iters) / best / 1e12
+    return _MFMA[(form, per_cu, iters)]
+
+
+def mfma_rates() -> dict:
+    """Every form of the probe at one and two workgroups per CU."""
+    import structured_sparse_gemm_amd as ssg
+    return {ssg.ssg_mfma_probe_name(f): {"dense_equiv_rate_1_wave_per_simd": mfma_rate(f, 1),
+                                         "dense_equiv_rate_2_waves_per_simd": mfma_rate(f, 2)}
+            for f in range(ssg.ssg_mfma_probe_forms())}
+
+
 def bench_workload(key: str, iters: int, delta: bool = False, dense_cmp: bool = True,
                    packed: bool = False, nm=None, prefill: bool = False, cbm: bool = False):
     """Kernel-level numbers for one workload (compression outside the timing),
@@ -279,6 +312,9 @@ def bench_workload(key: str, iters: int, delta: bool = False, dense_cmp: bool = 
     flops = 2.0 * w.M * w.N * w.K
     bbytes = b.numel() * b.element_size()
     cbytes = out.numel() * out.element_size()
+    tkey = key + ("_%d:%d" % tuple(nm) if nm else "") + ("_delta" if delta else "") + ("_cbm" if cbm else "") \
+        + ("_packed" if packed else "") + ("_prefill" if prefill else "")
+    family = "spmm_nm" if nm else "spmm_large_n" if w.klass == "large_n" else "spmm_small_n"
     r = {"title": w.title + (", residual delta-coded" if delta else "") + (", packed decode layout" if packed else "")
          + (", complement-bitmap residual fused" if cbm else "")
          + (", packed prefill layout" if prefill else "") + (", %d:%d" % tuple(nm) if nm else ""),
@@ -287,6 +323,7 @@ def bench_workload(key: str, iters: int, delta: bool = False, dense_cmp: bool = 
          "us_per_launch": s * 1e6,
          "timing": "HIP graph of %d launches, replayed twice; replay output matches eager: %s" % (n, graph_ok),
          "dense_equiv_TFLOPs": flops / s / 1e12, "compressed_weight_bytes": wbytes,
+         "algorithmic_bytes_per_launch": wbytes + bbytes + cbytes,
          "compressed_weight_GBps": wbytes / s / 1e9, "operand_copies_rotated": copies}
     if w.klass == "large_n":
         r["frac_dense_peak"] = flops / s / 1e12 / PEAK[w.dtype]
@@ -295,10 +332,15 @@ def bench_workload(key: str, iters: int, delta: bool = False, dense_cmp: bool = 
         # the launch duration, against the dense MFMA peak of the dtype
         r["roofline"] = {"bound": "mfma", "achieved": flops / 2 / s / 1e12, "peak": PEAK[w.dtype],
                          "unit": "TFLOP/s", "frac": flops / 2 / s / 1e12 / PEAK[w.dtype],
-                         "traffic": traffic_for(key, "spmm_large_n") if prefill else None}
+                         "traffic": traffic_for(tkey, family)}
     else:
         r["frac_hbm_weights"] = wbytes / s / 1e9 / PEAK["hbm_GBps"]
         r["frac_hbm_all_bytes"] = (wbytes + bbytes + cbytes) / s / 1e9 / PEAK["hbm_GBps"]
+        # roofline of the kernel: the bytes it must move (compressed weights,
+        # B, C) over the launch duration, against the HBM peak
+        r["roofline"] = {"bound": "hbm", "achieved": (wbytes + bbytes + cbytes) / s / 1e9, "peak": PEAK["hbm_GBps"],
+                         "unit": "GB/s", "frac": (wbytes + bbytes + cbytes) / s / 1e9 / PEAK["hbm_GBps"],
+                         "traffic": traffic_for(tkey, family)}
         rbw = read_bandwidth_GBps(wbytes)
         r["measured_read_GBps_same_bytes"] = rbw
         r["frac_measured_read_bw_weights"] = wbytes / s / 1e9 / rbw
@@ -427,6 +469,9 @@ def main() -> int:
                    help="first run a plain elementwise copy of 256 MiB (read 256 MiB, write 256 MiB) three times, "
                         "outside the timed region: the reference for scaling HBM byte counters")
     p.add_argument("--only", default="", help="comma-separated workload keys of the table (default: all)")
+    p.add_argument("--mfma-rates", action="store_true",
+                   help="instead of the benchmark, print the issue rates of the sparse and dense matrix-core "
+                        "instruction forms (the library's probe) as JSON")
     p.add_argument("--crossover", action="store_true",
                    help="instead of the benchmark, run the unstructured-sparsity crossover study and print its JSON")
     args = p.parse_args()
@@ -445,6 +490,11 @@ def main() -> int:
 
     if args.crossover:
         print(json.dumps(crossover(args.workload_iters or 100)))
+        return 0
+
+    if args.mfma_rates:
+        print(json.dumps({"unit": "dense-equivalent TFLOP/s (TOPS for int8)", "forms": mfma_rates(),
+                          "device": torch.cuda.get_device_name(0)}))
         return 0
 
     if args.calib_copy:
@@ -552,7 +602,18 @@ def main() -> int:
         "launch_us": spmm_s * 1e6,
         "dense_equiv_frac_of_dense_peak": flops / spmm_s / 1e12 / PEAK[w.dtype],
         "algorithmic_flops_per_launch": algo_ops,
+        # unique bytes the product must move: the packed operand, B, C
+        "algorithmic_bytes_per_launch": vb + mb + B.numel() * B.element_size() + C.numel() * C.element_size(),
+        "compress_algorithmic_bytes_per_launch": A.numel() * A.element_size() + vb + mb,
+        "compress_traffic": traffic_for(key, "compress"),
     }
+    # the measured issue rate of the kernel's instruction (and of the dense
+    # form a decode-to-dense kernel would issue instead), one wave per SIMD
+    sp, de = mfma_rate(0), mfma_rate(1)
+    roofline["measured_instr_ceiling"] = {
+        "instr": ssg.ssg_mfma_probe_name(0), "algorithmic_TFLOPs": sp / 2, "dense_equiv_TFLOPs": sp,
+        "frac": algo_ops / spmm_s / 1e12 / (sp / 2),
+        "dense_instr": ssg.ssg_mfma_probe_name(1), "dense_instr_TFLOPs": de}
     out = {
         "metric": METRIC,
         "value": flops / (ms * 1e-3) / 1e12,

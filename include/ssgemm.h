@@ -506,6 +506,29 @@ int ssg_spmm_2to4_packed_residual_cbm(int ab, int c, int64_t M, int64_t N, int64
 int64_t ssg_stream_read_sink_words(int64_t bytes);
 int ssg_stream_read(const void* src, int64_t bytes, uint32_t* sink, void* stream);
 
+/* Measurement helper (not part of the product): the issue rate of one
+ * matrix-core instruction form, the ceiling of the compute-bound products
+ * and the measure for the choice between the sparse MFMA and a decode of
+ * the compressed operand to dense followed by the dense MFMA ("Chapter 26
+ * -- Sparsity: The Hardware View", section "2:4: ~2x on the Matmul, Less
+ * End-to-End": the sparse unit doubles the math rate of the matmul).
+ * Forms 0 .. ssg_mfma_probe_forms()-1, named by ssg_mfma_probe_name (NULL
+ * outside that range): sparse and dense bf16 at 32x32 and 16x16, the same
+ * for int8, then sparse and dense fp8 (E4M3) at 32x32.  One launch is
+ * `workgroups` workgroups of four 64-lane waves; every wave runs `iters`
+ * rounds of independent accumulators through the one instruction, with
+ * operands from a hash of its lane.  ssg_mfma_probe_ops gives the launch's
+ * dense-equivalent operation count (2 * rows * columns * dense k per
+ * instruction; 0 for an invalid form or a non-positive count), so that
+ * count over the launch's time is the rate.  sink is device memory of
+ * `workgroups` uint32 words, written only when a workgroup's fold of its
+ * accumulators hits one fixed value.  Errors: SSG_ERR_ALGO for an invalid
+ * form, SSG_ERR_SHAPE for non-positive counts, SSG_ERR_NULL for no sink. */
+int ssg_mfma_probe_forms(void);
+const char* ssg_mfma_probe_name(int form);
+int64_t ssg_mfma_probe_ops(int form, int64_t workgroups, int64_t iters);
+int ssg_mfma_probe(int form, int64_t workgroups, int64_t iters, uint32_t* sink, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -378,6 +378,28 @@ def ssg_stream_read(src: torch.Tensor, sink: torch.Tensor, stream=None) -> None:
            "ssg_stream_read")
 
 
+def ssg_mfma_probe_forms() -> int:
+    return int(_lib().ssg_mfma_probe_forms())
+
+
+def ssg_mfma_probe_name(form: int) -> Optional[str]:
+    name = _lib().ssg_mfma_probe_name(form)
+    return name.decode() if name is not None else None
+
+
+def ssg_mfma_probe_ops(form: int, workgroups: int, iters: int) -> int:
+    return int(_lib().ssg_mfma_probe_ops(form, workgroups, iters))
+
+
+def ssg_mfma_probe(form: int, workgroups: int, iters: int, sink: torch.Tensor, stream=None) -> None:
+    """Measurement helper: one launch of the issue-rate probe of a matrix-core
+    instruction form (sink: at least `workgroups` int32 words on the device)."""
+    if sink.numel() * sink.element_size() < 4 * workgroups:
+        raise ValueError("sink holds fewer than %d words" % workgroups)
+    _check(_lib().ssg_mfma_probe(form, workgroups, iters, _ptr(sink, "sink"), _stream(sink, stream)),
+           "ssg_mfma_probe")
+
+
 def ssg_compress_nm(A: torch.Tensor, n: int, m: int, vals: torch.Tensor, mask: torch.Tensor, stream=None) -> None:
     e = _per(A)
     _check(_lib().ssg_compress_nm(_dtype(A), n, m, A.shape[0], A.shape[1] * e, _ptr(A, "A"), _ld(A, "A") * e,

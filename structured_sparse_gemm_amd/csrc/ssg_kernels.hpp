@@ -122,4 +122,13 @@ hipError_t launch_pack_nm(int dt, int n, int m, int64_t M, int64_t K, const void
 int64_t stream_read_grid(int64_t bytes);
 hipError_t launch_stream_read(const void* src, int64_t bytes, uint32_t* sink, hipStream_t s);
 
+// Issue-rate probe of one matrix-core instruction form (0 .. forms-1):
+// workgroups of four waves, each wave `iters` rounds of its independent
+// accumulators; ops = dense-equivalent operations of one launch; sink holds
+// `workgroups` words and is written only by chance.
+int mfma_probe_forms();
+const char* mfma_probe_name(int form);
+int64_t mfma_probe_ops(int form, int64_t workgroups, int64_t iters);
+hipError_t launch_mfma_probe(int form, int64_t workgroups, int64_t iters, uint32_t* sink, hipStream_t s);
+
 }  // namespace ssg

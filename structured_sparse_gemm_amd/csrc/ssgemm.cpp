@@ -685,6 +685,25 @@ int ssg_stream_read(const void* src, int64_t bytes, uint32_t* sink, void* stream
     return e == hipSuccess ? SSG_OK : hip_fail(e, "stream read launch");
 }
 
+int ssg_mfma_probe_forms(void) { return ssg::mfma_probe_forms(); }
+
+const char* ssg_mfma_probe_name(int form) { return ssg::mfma_probe_name(form); }
+
+int64_t ssg_mfma_probe_ops(int form, int64_t workgroups, int64_t iters) {
+    return ssg::mfma_probe_ops(form, workgroups, iters);
+}
+
+int ssg_mfma_probe(int form, int64_t workgroups, int64_t iters, uint32_t* sink, void* stream) {
+    if (!ssg::mfma_probe_name(form))
+        return fail(SSG_ERR_ALGO, "form %d is not in [0, %d)", form, ssg::mfma_probe_forms());
+    if (workgroups <= 0 || workgroups > 0x7fffffff || iters <= 0)
+        return fail(SSG_ERR_SHAPE, "workgroups=%lld and iters=%lld must be positive (workgroups below 2^31)",
+                    (long long)workgroups, (long long)iters);
+    if (!sink) return fail(SSG_ERR_NULL, "sink is NULL");
+    hipError_t e = ssg::launch_mfma_probe(form, workgroups, iters, sink, (hipStream_t)stream);
+    return e == hipSuccess ? SSG_OK : hip_fail(e, "matrix-instruction probe launch");
+}
+
 int64_t ssg_nm_vals_cols(int nm_n, int nm_m, int64_t K) {
     return nm_m > 0 && nm_n >= 0 ? K / nm_m * nm_n : 0;
 }

@@ -295,3 +295,28 @@ def test_packed_residual_argument_errors(lib):
     assert d(F16, F32, 32, 16, 128, FAKE, FAKE, FAKE, ctypes.c_void_p(0x1002), FAKE, 4, FAKE, 16, FAKE, 16,
              None) == _abi.SSG_ERR_ALGO
     assert r(F16, F32, 0, 16, 128, None, None, None, None, None, 0, FAKE, 16, None, 16, None) == 0
+
+
+def test_mfma_probe_description_and_argument_errors(lib):
+    # ten forms: sparse / dense pairs; the dense-equivalent operation count of
+    # a launch is 2 * rows * columns * dense k per instruction, times the
+    # accumulators per round (8 at 32x32, 16 at 16x16), rounds, waves
+    forms = lib.ssg_mfma_probe_forms()
+    assert forms == 10
+    names = [lib.ssg_mfma_probe_name(f).decode() for f in range(forms)]
+    assert names[0] == "v_smfmac_f32_32x32x32_bf16" and names[1] == "v_mfma_f32_32x32x16_bf16"
+    assert all(n.startswith("v_smfmac_") for n in names[0::2]) and all(n.startswith("v_mfma_") for n in names[1::2])
+    assert lib.ssg_mfma_probe_name(-1) is None and lib.ssg_mfma_probe_name(forms) is None
+    assert lib.ssg_mfma_probe_ops(0, 256, 2000) == 2 * 32 * 32 * 32 * 8 * 2000 * 256 * 4
+    assert lib.ssg_mfma_probe_ops(1, 256, 2000) == 2 * 32 * 32 * 16 * 8 * 2000 * 256 * 4
+    assert lib.ssg_mfma_probe_ops(6, 3, 5) == 2 * 16 * 16 * 128 * 16 * 5 * 3 * 4
+    # a sparse form covers twice the dense k of its dense partner (fp8: the
+    # dense 32x32x64 form covers the same k)
+    for f in (0, 2, 4, 6):
+        assert lib.ssg_mfma_probe_ops(f, 1, 1) == 2 * lib.ssg_mfma_probe_ops(f + 1, 1, 1)
+    assert lib.ssg_mfma_probe_ops(8, 1, 1) == lib.ssg_mfma_probe_ops(9, 1, 1)
+    assert lib.ssg_mfma_probe_ops(forms, 1, 1) == 0 and lib.ssg_mfma_probe_ops(0, 0, 1) == 0
+    assert lib.ssg_mfma_probe(forms, 1, 1, FAKE, None) == _abi.SSG_ERR_ALGO
+    assert lib.ssg_mfma_probe(0, 0, 1, FAKE, None) == _abi.SSG_ERR_SHAPE
+    assert lib.ssg_mfma_probe(0, 1, 0, FAKE, None) == _abi.SSG_ERR_SHAPE
+    assert lib.ssg_mfma_probe(0, 1, 1, None, None) == _abi.SSG_ERR_NULL
