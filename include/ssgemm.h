@@ -287,10 +287,13 @@ int ssg_spmm_2to4_packed_residual_delta(int ab, int c, int64_t M, int64_t N, int
  *          at byte r * 64 of it, its 16-byte chunk c (stored-value bytes
  *          [64 s + 16 c, +16) of the row) at chunk position
  *          c ^ (((r >> 1) ^ (r >> 3)) & 3).
- *   pmeta: tile t, block g -> 8 KiB block (t * mblocks + g), index-word
- *          major: index word w of row r (its metadata bytes
- *          [32 g + w IW, 32 g + w IW + IW), IW = 4 for the 8-bit types and 2
- *          for fp16/bf16) at byte w * 256 * IW + r * IW of it.
+ *   pmeta: tile t, block g -> 8 KiB block (t * mblocks + g) of 512
+ *          16-byte lane chunks.  With IW = 2 (fp16/bf16) or 4 (8-bit types)
+ *          and KPC = 4 / IW, metadata byte 32 g + j of row r of the tile
+ *          (j < 32: k-step h = j / (2 IW), half q = (j / IW) % 2, byte
+ *          e = j % IW of its index word; r = 128 wm + 32 i + rl with
+ *          i < 4, rl < 32) sits in chunk ((h / KPC) * 2 + wm) * 64 + 32 q + rl
+ *          at byte ((h % KPC) * 4 + i) * IW + e.
  * stages = K / 64 (fp16/bf16) or K / 128 (8-bit); mblocks = ceil(K / 256).
  * Rows past M and metadata bytes past K / 8 hold zeros.  The same bytes as
  * (vals, meta), only reordered.

@@ -221,12 +221,14 @@ __global__ void __launch_bounds__(kPrefillThreads) k_compress_prefill(int64_t M,
             const int piece = (c % CPS) * ES + j;
             *reinterpret_cast<uint4*>(lds + st * 16384 + r * 64 + ((piece ^ prefill_swz(r)) << 4)) = w[j];
         }
-        // its 4 metadata bytes: index words (4 c) / IW .. of the row
+        // its 4 metadata bytes (block bytes [4 c, 4 c + 4) of the row): one
+        // index word for 8-bit types, two for 16-bit ones, each whole at its
+        // position in the block
 #pragma unroll
         for (int j = 0; j < 4 / IW; ++j) {
-            const int wi = (4 * c) / IW + j;
-            if constexpr (IW == 4) *reinterpret_cast<uint32_t*>(lmeta + wi * 256 * IW + r * IW) = word;
-            else *reinterpret_cast<uint16_t*>(lmeta + wi * 256 * IW + r * IW) = (uint16_t)(word >> (16 * j));
+            const int pos = prefill_meta_pos(r, 4 * c + IW * j, IW);
+            if constexpr (IW == 4) *reinterpret_cast<uint32_t*>(lmeta + pos) = word;
+            else *reinterpret_cast<uint16_t*>(lmeta + pos) = (uint16_t)(word >> (16 * j));
         }
     }
     __syncthreads();

@@ -31,7 +31,7 @@
 //   transposing reads (ds_read_b64_tr_b16 / _b8) that build the B operand
 //   then hit 16 distinct 16-byte bank groups per 256 bytes.
 // * Tiles are ordered so each XCD (workgroups are dealt round-robin to the 8
-//   XCDs) gets a contiguous range of tiles, walked 4 row tiles at a time, so
+//   XCDs) gets a contiguous range of tiles, walked 8 row tiles at a time, so
 //   the 32 tiles in flight on an XCD share their A and B panels in its L2.
 // * Packed prefill operand (PK): the sparse values and metadata arrive
 //   already in this kernel's LDS image, one contiguous 16 KiB block of values
@@ -40,8 +40,14 @@
 //   of their loads is then a contiguous 1 KiB / 256 B piece instead of 16 rows
 //   x 64 bytes / 8 rows x 32 bytes, which halves the cache lines the load
 //   path must track for the values and quarters them for the metadata.  The
-//   loads of a stage are also spread over the reads and MFMAs of the next
-//   k-step instead of being issued in one burst after the barrier.
+//   metadata block is ordered in 16-byte lane chunks, so one LDS read gives
+//   a lane the index words of its 4 row tiles for a whole stage (16-bit
+//   types, two words per index register, picked by the MFMA's index-set
+//   select) or a k-step (8-bit types), instead of one read per row tile and
+//   k-step: the LDS issues reads at a fixed rate per instruction, and these
+//   small reads cost as much of it as the operand reads.  The loads of a
+//   stage are also spread over the reads and MFMAs of the next k-step
+//   instead of being issued in one burst after the barrier.
 #include <algorithm>
 
 #include "ssg_device.hpp"
@@ -120,8 +126,12 @@ typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
 
 template <int DT> using Acc16 = typename std::conditional<DT == DT_I8, i32x16, f32x16>::type;
 
-template <int DT>
+// One sparse MFMA.  16-bit types take 16 index bits per lane: ABID selects
+// the half of idx that holds them (the instruction's index-set select), so
+// two MFMAs can share one register of two packed index words.
+template <int DT, int ABID = 0>
 __device__ __forceinline__ Acc16<DT> mma(uint4 a, const uint4 (&b)[2], Acc16<DT> c, uint32_t idx) {
+    static_assert(ABID == 0 || dt_bytes(DT) == 2, "8-bit types use the whole index register");
     if constexpr (DT == DT_I8) {
         i32x4 av;
         i32x8 bv;
@@ -140,13 +150,13 @@ __device__ __forceinline__ Acc16<DT> mma(uint4 a, const uint4 (&b)[2], Acc16<DT>
         f16x16 bv;
         __builtin_memcpy(&av, &a, 16);
         __builtin_memcpy(&bv, b, 32);
-        return __builtin_amdgcn_smfmac_f32_32x32x32_f16(av, bv, c, (int)idx, 0, 0);
+        return __builtin_amdgcn_smfmac_f32_32x32x32_f16(av, bv, c, (int)idx, 0, ABID);
     } else {
         bf16x8 av;
         bf16x16 bv;
         __builtin_memcpy(&av, &a, 16);
         __builtin_memcpy(&bv, b, 32);
-        return __builtin_amdgcn_smfmac_f32_32x32x32_bf16(av, bv, c, (int)idx, 0, 0);
+        return __builtin_amdgcn_smfmac_f32_32x32x32_bf16(av, bv, c, (int)idx, 0, ABID);
     }
 }
 
@@ -366,25 +376,15 @@ __device__ __forceinline__ void spmm_tile(const SpmmArgs& a, int tm, int tn, uin
 #pragma unroll
         for (int j = 0; j < NJ; ++j) b_frag<DT, BN>(st, s, wn * (BN / 2) + 32 * j, lane, o.b[j]);
     };
-    // Index word of sub-step s of stage t for this lane, read so that no
-    // per-lane selection follows the read: 16-bit -- the 16 bits at byte
-    // 4s + 2q of the row's 8 (a zero-extending u16 read); int8 -- dword
-    // 2s + q of the row's 16.  Stage t's bytes are at (t % MB) * MSTAGE of
-    // each row of metadata block t / MB.
+    // Index words of sub-step s of stage t for this lane, read so that no
+    // per-lane selection follows the read.  Row-major metadata: 16-bit -- the
+    // 16 bits at byte 4s + 2q of the row's 8 (a zero-extending u16 read);
+    // int8 -- dword 2s + q of the row's 16; stage t's bytes are at
+    // (t % MB) * MSTAGE of each row of metadata block t / MB.  Packed: the
+    // lane's 16-byte chunk of the block holds the words of its 4 row tiles
+    // for KPC k-steps (both of a stage for 16-bit types, whose MFMAs then
+    // take them two per register, one for 8-bit ones).
     auto read_idx = [&](int64_t t, int s, uint32_t (&ix)[4]) {
-        if constexpr (PK) {
-            // packed: the block is index-word major ([word][256 rows]), so the
-            // 32 rows of one word that a read serves are contiguous
-            const uint8_t* mb = mlds + ((t / T::MB) & 1) * L::MBLK;
-            const int w = ((int)(t % T::MB) * T::MSTAGE + s * (T::MSTAGE / 2) + q * T::IDXB) / T::IDXB;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int row = 32 * (wm * 4 + i) + rl;
-                if constexpr (T::IDXB == 4) ix[i] = *reinterpret_cast<const uint32_t*>(mb + w * 1024 + row * 4);
-                else ix[i] = *reinterpret_cast<const uint16_t*>(mb + w * 512 + row * 2);
-            }
-            return;
-        }
         const uint8_t* mt = mlds + ((t / T::MB) & 1) * L::MBLK + (t % T::MB) * T::MSTAGE + s * (T::MSTAGE / 2);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -393,11 +393,22 @@ __device__ __forceinline__ void spmm_tile(const SpmmArgs& a, int tm, int tn, uin
             else ix[i] = *reinterpret_cast<const uint16_t*>(mp);
         }
     };
-    auto mmas = [&](const Ops& o, const uint32_t (&ix)[4]) {
+    constexpr int KPC = 4 / T::IDXB;                    // k-steps per packed index chunk
+    auto read_idx_pk = [&](int64_t t, int s) -> uint4 {
+        const uint8_t* mb = mlds + ((t / T::MB) & 1) * L::MBLK;
+        const int h = (int)(t % T::MB) * 2 + s;          // k-step of the block
+        return *reinterpret_cast<const uint4*>(mb + (((h / KPC) * 2 + wm) * 64 + lane) * 16);
+    };
+    // ix[i]: the index register of row tile i; with HALVES (16-bit types,
+    // packed) row tile i's word is half i % 2 of it
+    auto mmas = [&](const Ops& o, const uint32_t (&ix)[4], auto halves) {
 #pragma unroll
         for (int j = 0; j < NJ; ++j)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) acc[i][j] = mma<DT>(o.av[i], o.b[j], acc[i][j], ix[i]);
+            for (int i = 0; i < 4; i += 2) {
+                acc[i][j] = mma<DT>(o.av[i], o.b[j], acc[i][j], ix[i]);
+                acc[i + 1][j] = mma<DT, decltype(halves)::value ? 1 : 0>(o.av[i + 1], o.b[j], acc[i + 1][j], ix[i + 1]);
+            }
     };
 
     // Pipeline: DMA stages run two ahead of the stage being multiplied; the
@@ -419,17 +430,38 @@ __device__ __forceinline__ void spmm_tile(const SpmmArgs& a, int tm, int tn, uin
     issue<DT, BN>(x, lds + 2 * L::STAGE, 2, wave);
     issue_meta<DT, BN>(x, mlds + L::MBLK, 1, wave);
 
+    // Index words: packed 16-bit -- one chunk per stage (dn: both k-steps'
+    // words, two per register); packed 8-bit -- one chunk per k-step;
+    // row-major -- one read per row tile and k-step.
+    constexpr bool PK16 = PK && T::IDXB == 2;
+    constexpr int NIX0 = PK16 ? 0 : PK ? 1 : 4, NIX1 = PK ? 1 : 4;   // index reads per half-iteration
+    using Halves = std::integral_constant<bool, PK16>;
+    auto load_ix = [&](int64_t t, int s, uint32_t (&ix)[4]) {
+        if constexpr (PK) {
+            const uint4 d = read_idx_pk(t, s);
+            ix[0] = d.x; ix[1] = d.y; ix[2] = d.z; ix[3] = d.w;
+        } else {
+            read_idx(t, s, ix);
+        }
+    };
     Ops o0, o1;
     uint32_t ix0[4], ix1[4];
-    read_idx(0, 0, ix0);
+    uint4 dn = make_uint4(0, 0, 0, 0);
+    if constexpr (PK16) dn = read_idx_pk(0, 0);
+    else load_ix(0, 0, ix0);
     read_ops(lds, 0, o0);
     int slot = 0;
     for (int64_t it = 0; it < nit; ++it) {
         const uint8_t* st = lds + slot * L::STAGE;
         read_ops(st, 1, o1);
-        read_idx(it, 1, ix1);
-        mmas(o0, ix0);
-        interleave<4 * NJ, 4 + 4 * NJ + 4>();
+        if constexpr (PK16) {
+            ix0[0] = dn.x; ix0[1] = dn.x; ix0[2] = dn.y; ix0[3] = dn.y;
+            ix1[0] = dn.z; ix1[1] = dn.z; ix1[2] = dn.w; ix1[3] = dn.w;
+        } else {
+            load_ix(it, 1, ix1);
+        }
+        mmas(o0, ix0, Halves{});
+        interleave<4 * NJ, 4 + 4 * NJ + NIX0>();
         // stage it+1 has landed once only stage it+2's loads remain; this
         // wave's reads of stage it are done (s_waitcnt lgkmcnt(0), through the
         // builtin so the compiler knows they have landed) before the barrier
@@ -467,9 +499,10 @@ __device__ __forceinline__ void spmm_tile(const SpmmArgs& a, int tm, int tn, uin
         } else {
             read_ops(nx, 0, o0);
         }
-        read_idx(it + 1, 0, ix0);
-        mmas(o1, ix1);
-        interleave<4 * NJ, 4 + 4 * NJ + 4>();
+        if constexpr (PK16) dn = read_idx_pk(it + 1, 0);
+        else load_ix(it + 1, 0, ix0);
+        mmas(o1, ix1, Halves{});
+        interleave<4 * NJ, 4 + 4 * NJ + NIX1>();
     }
     // the zero-filling loads of the stages past K land before the LDS is released
     wait_vm<0>();
@@ -566,7 +599,7 @@ hipError_t pipe_launch(const SpmmArgs& a, hipStream_t s) {
 
 // Row-major (vals, meta) -> packed prefill layout.  One thread per 16-byte
 // chunk of pvals (a copy of one 16-byte chunk of a vals row, or zeros past
-// M) and per 4 bytes of pmeta (gathered bytewise from the index-word-major
+// M) and per 4 bytes of pmeta (gathered bytewise from the lane-chunk
 // positions: meta rows need no alignment; zeros past M and past K / 8).
 __global__ void __launch_bounds__(256) k_pack_prefill(int64_t M, int64_t K, const uint8_t* vals, int64_t ldv_bytes,
                                                       const uint8_t* meta, int64_t ldm, int64_t stages, int64_t mblocks,
@@ -588,9 +621,9 @@ __global__ void __launch_bounds__(256) k_pack_prefill(int64_t M, int64_t K, cons
             uint32_t w = 0;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                // byte o of the block: index word o / (256 iw) of row (o / iw) % 256
-                const int o = (int)((k & 2047) * 4 + e);
-                const int r = (o / iw) & 255, j = (o / (256 * iw)) * iw + o % iw;
+                // byte o of the block: metadata byte j of row r of the block
+                int r, j;
+                prefill_meta_inv((int)((k & 2047) * 4 + e), iw, &r, &j);
                 const int64_t m = t * 256 + r;
                 if (m < M && g * 32 + j < K / 8) w |= (uint32_t)meta[m * ldm + g * 32 + j] << (8 * e);
             }

@@ -65,10 +65,16 @@ __device__ __forceinline__ bool nibble_valid(uint32_t nib) { return (nib & 3u) <
 // block 32 metadata bytes of every row (256 dense k).
 // * pvals: tile t, stage s -> 16 KiB block (t * stages + s); row r of the tile
 //   at r * 64 in it, its 16-byte chunk c at chunk position c ^ prefill_swz(r).
-// * pmeta: tile t, block g -> 8 KiB block (t * mblocks + g), index-word
-//   major: index word w of row r (its metadata bytes [32 g + w IW, + IW),
-//   IW = 4 for 8-bit types, 2 for 16-bit ones) at w * 256 IW + r IW, so the
-//   32 rows whose words one MFMA reads are contiguous in LDS.
+// * pmeta: tile t, block g -> 8 KiB block (t * mblocks + g) of 16-byte lane
+//   chunks, one per (MFMA k-step group, 128-row half, lane) of the kernel:
+//   chunk u = (hq * 2 + wm) * 64 + 32 q + rl holds the index words of rows
+//   128 wm + 32 i + rl (i = 0..3) for lane half q of k-steps hq * KPC + hs
+//   (hs < KPC), word (hs, i) at bytes ((hs * 4 + i) * IW, + IW).  IW = index-
+//   word bytes (2 for 16-bit types, 4 for 8-bit), KPC = 4 / IW k-steps per
+//   chunk; k-step h of the block is metadata bytes [2 IW h, 2 IW (h + 1)) of
+//   each row, lane half q its bytes [2 IW h + q IW, + IW).  One 16-byte LDS
+//   read then gives a lane every index word of its 4 row tiles for KPC
+//   k-steps.
 // Rows past M and metadata bytes past K / 8 hold zeros.
 // ---------------------------------------------------------------------------
 __host__ __device__ __forceinline__ int prefill_swz(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
@@ -79,9 +85,19 @@ __host__ __device__ __forceinline__ int64_t prefill_vals_offset(int64_t m, int64
     return (((m >> 8) * stages + (b >> 6)) << 14) + r * 64 + ((((int)(b >> 4) & 3) ^ prefill_swz(r)) << 4) + (b & 15);
 }
 
-// Offset in pmeta of metadata byte j of row m (iw: index-word bytes).
-__host__ __device__ __forceinline__ int64_t prefill_meta_offset(int64_t m, int64_t j, int64_t mblocks, int iw) {
-    return (((m >> 8) * mblocks + (j >> 5)) << 13) + ((j & 31) / iw) * 256 * iw + (m & 255) * iw + (j & 31) % iw;
+// Position in its 8 KiB metadata block of byte j (0..31) of row r (0..255)
+// of the block, and the inverse.
+__host__ __device__ __forceinline__ int prefill_meta_pos(int r, int j, int iw) {
+    const int kpc = 4 / iw, h = j / (2 * iw), q = (j / iw) & 1, e = j % iw;
+    const int wm = r >> 7, i = (r >> 5) & 3, rl = r & 31;
+    return (((h / kpc) * 2 + wm) * 64 + 32 * q + rl) * 16 + ((h % kpc) * 4 + i) * iw + e;
+}
+__host__ __device__ __forceinline__ void prefill_meta_inv(int o, int iw, int* r, int* j) {
+    const int kpc = 4 / iw, u = o >> 4, b = o & 15;
+    const int wm = (u >> 6) & 1, hq = u >> 7, q = (u >> 5) & 1, rl = u & 31;
+    const int wi = b / iw, hs = wi >> 2, i = wi & 3, e = b % iw;
+    *r = 128 * wm + 32 * i + rl;
+    *j = (hq * kpc + hs) * 2 * iw + q * iw + e;
 }
 
 // Element conversion to fp32 (bit-exact widening).

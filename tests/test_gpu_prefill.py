@@ -48,9 +48,12 @@ def expected_prefill(dt, vals_bits, meta, M, K):
     for r in range(256):
         for c in range(4):
             pv[:, :, r, c ^ swz(r)] = src[:, r, :, c]
-    # metadata blocks index-word major: [tile][block][word][row][iw bytes]
+    # metadata blocks in 16-byte lane chunks: row r = 128 wm + 32 i + rl, block
+    # byte j = ((hq * kpc + hs) * 2 + q) * iw + e (k-step h = hq * kpc + hs,
+    # lane half q, index-word byte e); order [tile][block][hq][wm][q][rl][hs][i][e]
     iw = 4 if es == 1 else 2
-    pm = mb.reshape(tiles, 256, mblocks, 32 // iw, iw).transpose(0, 2, 3, 1, 4)
+    kpc = 4 // iw
+    pm = mb.reshape(tiles, 2, 4, 32, mblocks, 4, kpc, 2, iw).transpose(0, 4, 5, 1, 7, 3, 6, 2, 8)
     return pv.reshape(-1), np.ascontiguousarray(pm).reshape(-1)
 
 
