@@ -8,9 +8,11 @@ SpMM M=28672 K=8192 N=2048 (A ~ N(0, 0.02^2) magnitude-pruned 2:4 along K,
 B ~ N(0, 1), fp32 accumulate).  One step is the whole hot path over one
 batch: prune + compress A on the GPU straight into the packed prefill layout
 (the large-N kernel's LDS image of each tile), then C = expand(packed) x B on
-the large-N kernel.  `value` is dense-equivalent throughput 2*M*N*K / step
-time, inputs resident in HBM before the timed region.  The row-major product
-of the same operand is timed beside it.
+the large-N kernel, with the activations B handed over token-major (Bt =
+B^T [N, K] row-major, as a linear layer's inputs arrive).  `value` is
+dense-equivalent throughput 2*M*N*K / step time, inputs resident in HBM
+before the timed region.  The same product with B [K, N] row-major, and with
+the row-major (interchange) operand, are timed beside it.
 
 Also printed, in the same JSON line:
 * roofline: the SpMM kernel's own launch duration from HIP events recorded on
@@ -235,12 +237,13 @@ def mfma_rates() -> dict:
 
 
 def bench_workload(key: str, iters: int, delta: bool = False, dense_cmp: bool = True,
-                   packed: bool = False, nm=None, prefill: bool = False, cbm: bool = False):
+                   packed: bool = False, nm=None, prefill: bool = False, cbm: bool = False, bt: bool = False):
     """Kernel-level numbers for one workload (compression outside the timing),
     next to a dense GEMM of the same shape from the vendor library.  With
     delta=True the residual is delta-coded (one-byte column gaps); with
     packed=True the 2:4 operand is in the packed decode layout; with
-    prefill=True in the packed prefill layout; with nm=(n, m) the weight is
+    prefill=True in the packed prefill layout (bt=True: B handed over
+    activation-major, as Bt [N, K] row-major); with nm=(n, m) the weight is
     in the n:m form (kept values plus keep mask); with cbm=True (and packed)
     the residual is in the complement-bitmap layout, fused into the packed
     product's k-steps."""
@@ -252,6 +255,7 @@ def bench_workload(key: str, iters: int, delta: bool = False, dense_cmp: bool = 
     w = W.WORKLOADS[key]
     a = W.gen_a(w).cuda()
     b = W.gen_b(w).cuda()
+    b_t = b.t().contiguous() if bt else None
     if nm is not None:
         ops = ssg.compress_nm(a, nm[0], nm[1])
         if packed:
@@ -292,6 +296,8 @@ def bench_workload(key: str, iters: int, delta: bool = False, dense_cmp: bool = 
             ssg.ssg_spmm_2to4_packed_residual(o[0], o[1], w.M, o[2], o[3], o[4], b, out)
         elif packed:
             ssg.ssg_spmm_2to4_packed(o[0], o[1], w.M, b, out)
+        elif prefill and bt:
+            ssg.ssg_spmm_2to4_prefill_bt(o[0], o[1], w.M, b_t, out)
         elif prefill:
             ssg.ssg_spmm_2to4_prefill(o[0], o[1], w.M, b, out)
         elif delta:
@@ -313,11 +319,12 @@ def bench_workload(key: str, iters: int, delta: bool = False, dense_cmp: bool = 
     bbytes = b.numel() * b.element_size()
     cbytes = out.numel() * out.element_size()
     tkey = key + ("_%d:%d" % tuple(nm) if nm else "") + ("_delta" if delta else "") + ("_cbm" if cbm else "") \
-        + ("_packed" if packed else "") + ("_prefill" if prefill else "")
+        + ("_packed" if packed else "") + ("_prefill" if prefill else "") + ("_bt" if bt else "")
     family = "spmm_nm" if nm else "spmm_large_n" if w.klass == "large_n" else "spmm_small_n"
     r = {"title": w.title + (", residual delta-coded" if delta else "") + (", packed decode layout" if packed else "")
          + (", complement-bitmap residual fused" if cbm else "")
-         + (", packed prefill layout" if prefill else "") + (", %d:%d" % tuple(nm) if nm else ""),
+         + (", packed prefill layout" if prefill else "") + (", B activation-major (Bt [N, K])" if bt else "")
+         + (", %d:%d" % tuple(nm) if nm else ""),
          "algo": ("nm (dense MFMA on the expanded operand)" if nm else ssg.ALGO_NAMES[algo])
          + (" (packed)" if packed else "") + (" (packed prefill)" if prefill else ""),
          "us_per_launch": s * 1e6,
@@ -517,9 +524,13 @@ def main() -> int:
     C = torch.empty((w.M, w.N), dtype=out_dt, device="cuda")
     stream = torch.cuda.current_stream()
 
+    # the activations handed over token-major, Bt = B^T [N, K] row-major, as
+    # a linear layer's inputs arrive (prepared before the timed region)
+    Bt = B.t().contiguous()
+
     def step():
         ssg.ssg_compress_2to4_prefill(A, vals, meta)
-        ssg.ssg_spmm_2to4_prefill(vals, meta, w.M, B, C)
+        ssg.ssg_spmm_2to4_prefill_bt(vals, meta, w.M, Bt, C)
 
     for _ in range(args.warmup):
         step()
@@ -564,8 +575,16 @@ def main() -> int:
     # kernel durations: back-to-back launches between two HIP events on the
     # stream the kernels run on
     reps = max(args.steps, 20)
-    spmm_s = time_kernel(lambda i: ssg.ssg_spmm_2to4_prefill(vals, meta, w.M, B, C), reps, stream)
+    spmm_s = time_kernel(lambda i: ssg.ssg_spmm_2to4_prefill_bt(vals, meta, w.M, Bt, C), reps, stream)
     comp_s = time_kernel(lambda i: ssg.ssg_compress_2to4_prefill(A, vals, meta), reps, stream)
+    # the same product with B [K, N] row-major
+    C_kn = torch.empty_like(C)
+    ssg.ssg_spmm_2to4_prefill(vals, meta, w.M, B, C_kn)
+    torch.cuda.synchronize()
+    b_rowmajor = {"spmm_us": time_kernel(lambda i: ssg.ssg_spmm_2to4_prefill(vals, meta, w.M, B, C_kn), reps,
+                                         stream) * 1e6,
+                  "same_result_bits": bool(torch.equal(C_kn.view(torch.int32), C.view(torch.int32)))}
+    del C_kn
     # the same product from the row-major (interchange) operand
     rvals, rmeta = ssg.compress(A)
     C_rm = ssg.spmm(rvals, rmeta, B, algo=ssg.SSG_ALGO_LARGE_N)
@@ -592,7 +611,7 @@ def main() -> int:
     torch.cuda.empty_cache()
 
     roofline = {
-        "kernel": "spmm_large_n on the packed prefill layout (bf16 sparse MFMA 32x32x32)",
+        "kernel": "spmm_large_n on the packed prefill layout, B activation-major (bf16 sparse MFMA 32x32x32)",
         "bound": "mfma",
         "achieved": algo_ops / spmm_s / 1e12,
         "peak": PEAK[w.dtype],
@@ -628,11 +647,13 @@ def main() -> int:
         "dtype": w.dtype,
         "data": "synthetic",
         "config": {"workload": "bf16 2:4 SpMM M=28672 K=8192 N=2048 (prefill shape); step = prune+compress A "
-                               "(packed prefill layout), then SpMM (fp32 out)",
+                               "(packed prefill layout), then SpMM with the activations B handed over "
+                               "token-major (Bt [N, K] row-major), fp32 out",
                    "M": w.M, "K": w.K, "N": w.N, "seeds": [1000 + w.index, 2000 + w.index]},
         "spmm_only_dense_equiv_TFLOPs": flops / spmm_s / 1e12,
         "spmm_us": spmm_s * 1e6,
         "compress_us": comp_s * 1e6,
+        "b_kn_rowmajor": b_rowmajor,
         "rowmajor_operand": rowmajor,
         "launch": "one HIP graph of the %d timed steps (each: compress + SpMM), replayed once; check replays "
                   "match eager outputs: %s" % (args.steps, graph_ok),
@@ -683,6 +704,9 @@ def main() -> int:
             if W.WORKLOADS[k].klass == "large_n" and k not in ("c1", key):
                 print("bench: workload %s, packed prefill layout ..." % k, file=sys.stderr, flush=True)
                 table[k + "_prefill"] = bench_workload(k, it, dense_cmp=False, prefill=True)
+                print("bench: workload %s, packed prefill layout, activation-major B ..." % k, file=sys.stderr,
+                      flush=True)
+                table[k + "_prefill_bt"] = bench_workload(k, it, dense_cmp=False, prefill=True, bt=True)
             if W.WORKLOADS[k].residual:
                 print("bench: workload %s, delta-coded residual ..." % k, file=sys.stderr, flush=True)
                 table[k + "_delta"] = bench_workload(k, it, delta=True, dense_cmp=False)

@@ -52,13 +52,17 @@ COMMANDS = {
 # The workload line names the bench entry whose algorithmic bytes apply; the
 # family names the sources whose hash marks the counters stale.
 PROFILED = [
-    ("k_spmm_pipe<1, true>", "c4", "spmm_large_n",
-     "bf16 28672x8192x2048 SpMM, packed prefill layout (the headline step's product)"),
+    ("k_spmm_pipe<1, true, true>", "c4", "spmm_large_n",
+     "bf16 28672x8192x2048 SpMM, packed prefill layout, B activation-major (the headline step's product)"),
     ("k_compress_prefill<1>", "c4", "compress",
      "bf16 28672x8192x2048 prune + compress into the packed prefill layout (the headline step's compress)"),
-    ("k_spmm_pipe<1, false>", "c4_rowmajor", "spmm_large_n", "bf16 28672x8192x2048 SpMM, row-major operand"),
-    ("k_spmm_pipe<2, true>", "c2_prefill", "spmm_large_n", "int8 4096^3 SpMM, packed prefill layout"),
-    ("k_spmm_pipe<2, false>", "c2", "spmm_large_n", "int8 4096^3 SpMM, row-major operand"),
+    ("k_spmm_pipe<1, true, false>", "c4_bkn", "spmm_large_n",
+     "bf16 28672x8192x2048 SpMM, packed prefill layout, B [K, N] row-major"),
+    ("k_spmm_pipe<1, false, false>", "c4_rowmajor", "spmm_large_n", "bf16 28672x8192x2048 SpMM, row-major operand"),
+    ("k_spmm_pipe<2, true, true>", "c2_prefill_bt", "spmm_large_n",
+     "int8 4096^3 SpMM, packed prefill layout, B activation-major"),
+    ("k_spmm_pipe<2, true, false>", "c2_prefill", "spmm_large_n", "int8 4096^3 SpMM, packed prefill layout"),
+    ("k_spmm_pipe<2, false, false>", "c2", "spmm_large_n", "int8 4096^3 SpMM, row-major operand"),
     (re.compile(r"k_spmm_small_n_ring<0, \d+, \d+, false, false>"), "c3", "spmm_small_n",
      "fp16 11008x4096x16 SpMM, row-major operand"),
     (re.compile(r"k_spmm_packed<0, \d+, \d+, false, false>"), "c3_packed", "spmm_small_n",
@@ -145,7 +149,7 @@ def bench_line(d: str) -> dict:
 
 
 def algorithmic_bytes(b: dict, line: str, family: str) -> int:
-    if line in ("c4", "c4_rowmajor"):
+    if line in ("c4", "c4_bkn", "c4_rowmajor"):
         key = "compress_algorithmic_bytes_per_launch" if family == "compress" else "algorithmic_bytes_per_launch"
         return int(b["roofline"][key])
     return int(b["workloads"][line]["algorithmic_bytes_per_launch"])

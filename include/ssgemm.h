@@ -319,6 +319,18 @@ int ssg_pack_2to4_prefill(int dt, int64_t M, int64_t K, const void* vals, int64_
 int ssg_spmm_2to4_prefill(int ab, int c, int64_t M, int64_t N, int64_t K, const void* pvals, const void* pmeta,
                           const void* B, int64_t ldb, void* C, int64_t ldc, void* stream);
 
+/* The same product with B given as its transpose: Bt [N, K] row-major
+ * (row stride ldbt >= K elements), the token-major layout in which a
+ * linear layer's activations arrive (C = W X^T for activations X = Bt).
+ * Each column of B is then a contiguous row, which the large-N kernel reads
+ * in 16-byte pieces (half the LDS reads per B operand of the row-major
+ * form); the result has the same bits as ssg_spmm_2to4_prefill with
+ * B = Bt^T.  Needs Bt 16-byte aligned with rows a multiple of 16 bytes, and
+ * 256 * ldbt elements within 31-bit byte offsets (SSG_ERR_ALGO otherwise);
+ * any N >= 0. */
+int ssg_spmm_2to4_prefill_bt(int ab, int c, int64_t M, int64_t N, int64_t K, const void* pvals, const void* pmeta,
+                             const void* Bt, int64_t ldbt, void* C, int64_t ldc, void* stream);
+
 /* N:M patterns other than 2:4 ("Chapter 26 -- Sparsity: The Hardware View",
  * section "Block Sparsity, N:M Generalizations, and Channel Pruning", which
  * lists 1:4, 2:8 and 4:8 and gives no selection rule or storage; what

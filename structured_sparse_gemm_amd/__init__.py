@@ -297,6 +297,14 @@ def ssg_spmm_2to4_prefill(pvals, pmeta, M: int, B, C, stream=None) -> None:
            "ssg_spmm_2to4_prefill")
 
 
+def ssg_spmm_2to4_prefill_bt(pvals, pmeta, M: int, Bt, C, stream=None) -> None:
+    ab = _dtype(Bt)
+    N, K = Bt.shape[0], Bt.shape[1]
+    _check(_lib().ssg_spmm_2to4_prefill_bt(ab, _OUT[ab][0], M, N, K, _ptr(pvals, "pvals"), _ptr(pmeta, "pmeta"),
+                                           _ptr(Bt, "Bt"), _ld(Bt, "Bt"), _ptr(C, "C"), _ld(C, "C"),
+                                           _stream(C, stream)), "ssg_spmm_2to4_prefill_bt")
+
+
 def ssg_spmm_2to4_packed_residual(pvals, pmeta, M: int, row_ptr, col, rvals, B, C, stream=None) -> None:
     ab = _dtype(B)
     N, K = B.shape[1], B.shape[0]
@@ -637,6 +645,17 @@ def spmm_prefill(pvals: torch.Tensor, pmeta: torch.Tensor, M: int, B: torch.Tens
     ab = _dtype(B)
     C = torch.empty((M, B.shape[1]), dtype=_OUT[ab][1], device=B.device) if out is None else out
     ssg_spmm_2to4_prefill(pvals, pmeta, M, B, C)
+    return C
+
+
+def spmm_prefill_bt(pvals: torch.Tensor, pmeta: torch.Tensor, M: int, Bt: torch.Tensor,
+                    out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """C = expand(packed prefill) @ Bt.T on the large-N kernel, Bt [N, K]
+    row-major (token-major activations): fp32 for float inputs, int32 for
+    int8."""
+    ab = _dtype(Bt)
+    C = torch.empty((M, Bt.shape[0]), dtype=_OUT[ab][1], device=Bt.device) if out is None else out
+    ssg_spmm_2to4_prefill_bt(pvals, pmeta, M, Bt, C)
     return C
 
 

@@ -59,6 +59,7 @@ SIGNATURES = {
     "ssg_compress_2to4_prefill": (_i, [_i, _i64, _i64, _vp, _i64, _vp, _vp, _vp]),
     "ssg_pack_2to4_prefill": (_i, [_i, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _vp, _vp]),
     "ssg_spmm_2to4_prefill": (_i, [_i, _i, _i64, _i64, _i64, _vp, _vp, _vp, _i64, _vp, _i64, _vp]),
+    "ssg_spmm_2to4_prefill_bt": (_i, [_i, _i, _i64, _i64, _i64, _vp, _vp, _vp, _i64, _vp, _i64, _vp]),
     "ssg_nm_vals_cols": (_i64, [_i, _i, _i64]),
     "ssg_compress_nm": (_i, [_i, _i, _i, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp]),
     "ssg_decompress_nm": (_i, [_i, _i, _i, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _vp]),

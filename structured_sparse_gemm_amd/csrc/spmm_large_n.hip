@@ -198,6 +198,25 @@ __device__ __forceinline__ void b_frag(const uint8_t* bt, int s, int cb, int lan
     }
 }
 
+// Activation-major B (BT): the B operand given as its transpose Bt [N, K]
+// row-major (one row of K per output column, as token-major activations
+// arrive).  Its LDS tile holds BN rows of the stage's BK * ES = 128 bytes,
+// the 8 16-byte chunks of row n XOR-swizzled by (n / 2) % 8, so the 16
+// consecutive rows that a 16-byte read serves together hit 16 distinct
+// 16-byte bank windows.  Lane l's B fragment (column cb + l%32, block
+// bb = l/32) is then two plain 16-byte reads: chunks 4s + bb and 4s + 2 + bb
+// of its row hold exactly its elements e < H and e >= H (dense k
+// (e / H) * (KSUB / 2) + H * bb + e % H of k-step s, as in b_frag).
+__device__ __forceinline__ int swz_bt(int n) { return (n >> 1) & 7; }
+
+template <int DT>
+__device__ __forceinline__ void b_frag_bt(const uint8_t* bt, int s, int cb, int lane, uint4 (&b)[2]) {
+    const int bb = lane >> 5, n = cb + (lane & 31);
+    const uint8_t* row = bt + n * 128;
+    b[0] = *reinterpret_cast<const uint4*>(row + (((4 * s + bb) ^ swz_bt(n)) << 4));
+    b[1] = *reinterpret_cast<const uint4*>(row + (((4 * s + 2 + bb) ^ swz_bt(n)) << 4));
+}
+
 struct Ctx {
     const uint8_t* vbase;   // vals row m0
     const uint8_t* mbase;   // meta row m0
@@ -290,7 +309,7 @@ __device__ __forceinline__ void issue_meta(const Ctx& x, uint8_t* mt, int64_t g,
 
 // Tile (tm, tn) of width BN (256, or 128 for the half-width tiles that fill
 // the last wave of a launch): rows [256 tm, +256), columns [BN tn, +BN).
-template <int DT, bool PK, int BN>
+template <int DT, bool PK, int BN, bool BT>
 __device__ __forceinline__ void spmm_tile(const SpmmArgs& a, int tm, int tn, uint8_t* lds) {
     using T = PT<DT>;
     using L = Lay<DT, BN>;
@@ -325,14 +344,29 @@ __device__ __forceinline__ void spmm_tile(const SpmmArgs& a, int tm, int tn, uin
         x.vstage = L::A_ROWB;
         x.mstep = L::MBLK_ROWB;
     }
-    x.bbase = reinterpret_cast<const uint8_t*>(a.B) + n0 * T::ES;
-    x.bbytes = ((a.K - 1) * a.ldb + a.N - n0) * T::ES;
-    x.bstage = (int64_t)T::BK * a.ldb * T::ES;
+    if constexpr (BT) {
+        // rows n0.. of Bt, advancing BK elements along them per stage; a
+        // stage past K reads the next row's elements (or zeros past the
+        // buffer) into a slot that is never multiplied
+        x.bbase = reinterpret_cast<const uint8_t*>(a.B) + n0 * a.ldb * T::ES;
+        x.bbytes = ((a.N - 1 - n0) * a.ldb + a.K) * T::ES;
+        x.bstage = (int64_t)T::BK * T::ES;
+    } else {
+        x.bbase = reinterpret_cast<const uint8_t*>(a.B) + n0 * T::ES;
+        x.bbytes = ((a.K - 1) * a.ldb + a.N - n0) * T::ES;
+        x.bstage = (int64_t)T::BK * a.ldb * T::ES;
+    }
 #pragma unroll
     for (int j = 0; j < L::B_LOADS; ++j) {
         const int slot = (wave * L::B_LOADS + j) * 64 + lane;
-        const int r = slot / L::CPR, c = (slot % L::CPR) ^ swz<DT, BN>(r);
-        x.boff[j] = (n0 + (int64_t)c * T::EPC < a.N) ? (uint32_t)((r * a.ldb + c * T::EPC) * T::ES) : kOob;
+        if constexpr (BT) {
+            // 8 rows x 128 bytes per load: lane -> row slot / 8, LDS chunk slot % 8
+            const int r = slot >> 3, c = (slot & 7) ^ swz_bt(r);
+            x.boff[j] = (n0 + r < a.N) ? (uint32_t)(r * a.ldb * T::ES + 16 * c) : kOob;
+        } else {
+            const int r = slot / L::CPR, c = (slot % L::CPR) ^ swz<DT, BN>(r);
+            x.boff[j] = (n0 + (int64_t)c * T::EPC < a.N) ? (uint32_t)((r * a.ldb + c * T::EPC) * T::ES) : kOob;
+        }
     }
 #pragma unroll
     for (int j = 0; j < L::A_LOADS; ++j) {
@@ -374,7 +408,10 @@ __device__ __forceinline__ void spmm_tile(const SpmmArgs& a, int tm, int tn, uin
                                                       (((2 * s + q) ^ swz_a(row)) << 4));
         }
 #pragma unroll
-        for (int j = 0; j < NJ; ++j) b_frag<DT, BN>(st, s, wn * (BN / 2) + 32 * j, lane, o.b[j]);
+        for (int j = 0; j < NJ; ++j) {
+            if constexpr (BT) b_frag_bt<DT>(st, s, wn * (BN / 2) + 32 * j, lane, o.b[j]);
+            else b_frag<DT, BN>(st, s, wn * (BN / 2) + 32 * j, lane, o.b[j]);
+        }
     };
     // Index words of sub-step s of stage t for this lane, read so that no
     // per-lane selection follows the read.  Row-major metadata: 16-bit -- the
@@ -435,6 +472,7 @@ __device__ __forceinline__ void spmm_tile(const SpmmArgs& a, int tm, int tn, uin
     // row-major -- one read per row tile and k-step.
     constexpr bool PK16 = PK && T::IDXB == 2;
     constexpr int NIX0 = PK16 ? 0 : PK ? 1 : 4, NIX1 = PK ? 1 : 4;   // index reads per half-iteration
+    constexpr int NB = BT ? 2 : 4;                                     // B reads per fragment
     using Halves = std::integral_constant<bool, PK16>;
     auto load_ix = [&](int64_t t, int s, uint32_t (&ix)[4]) {
         if constexpr (PK) {
@@ -461,7 +499,7 @@ __device__ __forceinline__ void spmm_tile(const SpmmArgs& a, int tm, int tn, uin
             load_ix(it, 1, ix1);
         }
         mmas(o0, ix0, Halves{});
-        interleave<4 * NJ, 4 + 4 * NJ + NIX0>();
+        interleave<4 * NJ, 4 + NB * NJ + NIX0>();
         // stage it+1 has landed once only stage it+2's loads remain; this
         // wave's reads of stage it are done (s_waitcnt lgkmcnt(0), through the
         // builtin so the compiler knows they have landed) before the barrier
@@ -491,7 +529,8 @@ __device__ __forceinline__ void spmm_tile(const SpmmArgs& a, int tm, int tn, uin
             }
 #pragma unroll
             for (int j = 0; j < NJ; ++j) {
-                b_frag<DT, BN>(nx, 0, wn * (BN / 2) + 32 * j, lane, o0.b[j]);
+                if constexpr (BT) b_frag_bt<DT>(nx, 0, wn * (BN / 2) + 32 * j, lane, o0.b[j]);
+                else b_frag<DT, BN>(nx, 0, wn * (BN / 2) + 32 * j, lane, o0.b[j]);
 #pragma unroll
                 for (int u = 0; u < BPJ; ++u)
                     dma<16>(rb, dst + (wave * L::B_LOADS + BPJ * j + u) * 1024, x.boff[BPJ * j + u]);
@@ -502,7 +541,7 @@ __device__ __forceinline__ void spmm_tile(const SpmmArgs& a, int tm, int tn, uin
         if constexpr (PK16) dn = read_idx_pk(it + 1, 0);
         else load_ix(it + 1, 0, ix0);
         mmas(o1, ix1, Halves{});
-        interleave<4 * NJ, 4 + 4 * NJ + NIX1>();
+        interleave<4 * NJ, 4 + NB * NJ + NIX1>();
     }
     // the zero-filling loads of the stages past K land before the LDS is released
     wait_vm<0>();
@@ -547,17 +586,17 @@ __device__ __forceinline__ void xcd_order(int bid, int tiles_m, int tiles_n, int
     *tn = in_group / gm;
 }
 
-template <int DT, bool PK>
+template <int DT, bool PK, bool BT = false>
 __global__ void __launch_bounds__(kThreads) k_spmm_pipe(SpmmArgs a, int tiles_m, int tiles_n, int full_rows) {
     __shared__ __attribute__((aligned(1024))) uint8_t lds[Lay<DT>::LDS];
     const int nfull = full_rows * tiles_n;
     int tm, tn;
     if ((int)blockIdx.x < nfull) {
         xcd_order(blockIdx.x, full_rows, tiles_n, &tm, &tn);
-        spmm_tile<DT, PK, kBN>(a, tm, tn, lds);
+        spmm_tile<DT, PK, kBN, BT>(a, tm, tn, lds);
     } else {
         xcd_order(blockIdx.x - nfull, tiles_m - full_rows, 2 * tiles_n, &tm, &tn);
-        spmm_tile<DT, PK, kBN / 2>(a, full_rows + tm, tn, lds);
+        spmm_tile<DT, PK, kBN / 2, BT>(a, full_rows + tm, tn, lds);
     }
 }
 
@@ -588,12 +627,12 @@ int full_row_tiles(int tiles_m, int tiles_n) {
     return conv <= kCUs - rem ? tiles_m - half_rows : tiles_m;
 }
 
-template <int DT, bool PK = false>
+template <int DT, bool PK = false, bool BT = false>
 hipError_t pipe_launch(const SpmmArgs& a, hipStream_t s) {
     const int tm = (int)((a.M + kBM - 1) / kBM), tn = (int)((a.N + kBN - 1) / kBN);
     const int full = full_row_tiles(tm, tn);
     const unsigned grid = (unsigned)(full * tn + 2 * (tm - full) * tn);
-    hipLaunchKernelGGL((k_spmm_pipe<DT, PK>), dim3(grid), dim3(kThreads), 0, s, a, tm, tn, full);
+    hipLaunchKernelGGL((k_spmm_pipe<DT, PK, BT>), dim3(grid), dim3(kThreads), 0, s, a, tm, tn, full);
     return hipGetLastError();
 }
 
@@ -682,6 +721,29 @@ hipError_t launch_spmm_prefill_packed(const SpmmArgs& a, hipStream_t s) {
         case DT_I8: return pipe_launch<DT_I8, true>(a, s);
         case DT_E4M3: return pipe_launch<DT_E4M3, true>(a, s);
         case DT_E5M2: return pipe_launch<DT_E5M2, true>(a, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+// Activation-major B: a.B is Bt [N, K] row-major with row stride a.ldb.
+bool supported_prefill_packed_bt(const SpmmArgs& a) {
+    const int es = dt_bytes(a.dt), bk = es == 1 ? 128 : 64;
+    const uintptr_t v = reinterpret_cast<uintptr_t>(a.vals), m = reinterpret_cast<uintptr_t>(a.meta),
+                    b = reinterpret_cast<uintptr_t>(a.B);
+    const int64_t tiles = ((a.M + kBM - 1) / kBM) * ((a.N + kBN - 1) / kBN);
+    return a.M > 0 && a.N > 0 && a.K > 0 && a.K % bk == 0 && a.ldb >= a.K && v % 16 == 0 && m % 4 == 0 &&
+           b % 16 == 0 && (a.ldb * es) % 16 == 0 &&
+           // one tile's blocks, and a tile's 256 rows of Bt, addressed with 31-bit offsets
+           a.K / 2 * es * 256 < 0x7fffffff && 256 * a.ldb * es < 0x7fffffff && tiles < 0x7fffffff;
+}
+
+hipError_t launch_spmm_prefill_packed_bt(const SpmmArgs& a, hipStream_t s) {
+    switch (a.dt) {
+        case DT_F16: return pipe_launch<DT_F16, true, true>(a, s);
+        case DT_BF16: return pipe_launch<DT_BF16, true, true>(a, s);
+        case DT_I8: return pipe_launch<DT_I8, true, true>(a, s);
+        case DT_E4M3: return pipe_launch<DT_E4M3, true, true>(a, s);
+        case DT_E5M2: return pipe_launch<DT_E5M2, true, true>(a, s);
         default: return hipErrorInvalidValue;
     }
 }

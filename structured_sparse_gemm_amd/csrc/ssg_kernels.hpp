@@ -97,6 +97,9 @@ hipError_t launch_pack_prefill(int dt, int64_t M, int64_t K, const void* vals, i
                                int64_t ldm, void* pvals, void* pmeta, hipStream_t s);
 bool supported_prefill_packed(const SpmmArgs& a);
 hipError_t launch_spmm_prefill_packed(const SpmmArgs& a, hipStream_t s);
+// The same product with B given as Bt [N, K] row-major (a.B, a.ldb).
+bool supported_prefill_packed_bt(const SpmmArgs& a);
+hipError_t launch_spmm_prefill_packed_bt(const SpmmArgs& a, hipStream_t s);
 
 // N:M patterns other than 2:4 (spmm_nm.hip): kept values plus a keep mask
 // (bit k%8 of byte k/8 of a row).  (n, m) in {(1,4), (2,4), (2,8), (4,8)}.

@@ -673,6 +673,27 @@ int ssg_spmm_2to4_prefill(int ab, int c, int64_t M, int64_t N, int64_t K, const 
     return e == hipSuccess ? SSG_OK : hip_fail(e, "packed prefill spmm launch");
 }
 
+int ssg_spmm_2to4_prefill_bt(int ab, int c, int64_t M, int64_t N, int64_t K, const void* pvals, const void* pmeta,
+                             const void* Bt, int64_t ldbt, void* C, int64_t ldc, void* stream) {
+    if (!pair_ok(ab, c)) return fail(SSG_ERR_DTYPE, "unsupported (input, output) types (%d, %d)", ab, c);
+    if (N < 0 || N > ((int64_t)1 << 31)) return fail(SSG_ERR_SHAPE, "N=%lld out of range", (long long)N);
+    int64_t vb, mb;
+    int rc = prefill_sizes(ab, M, K, &vb, &mb);
+    if (rc) return rc;
+    if (ldbt < K) return fail(SSG_ERR_STRIDE, "ldbt=%lld < K=%lld", (long long)ldbt, (long long)K);
+    if (ldc < N) return fail(SSG_ERR_STRIDE, "ldc=%lld < N=%lld", (long long)ldc, (long long)N);
+    if (M == 0 || N == 0) return SSG_OK;
+    if (K == 0) return fail(SSG_ERR_SHAPE, "K must be positive");
+    if (!pvals || !pmeta || !Bt || !C) return fail(SSG_ERR_NULL, "a required pointer is NULL");
+    ssg::SpmmArgs a = make_args(ab, M, N, K, pvals, 0, static_cast<const uint8_t*>(pmeta), 0, Bt, ldbt, C, ldc);
+    if (!ssg::supported_prefill_packed_bt(a))
+        return fail(SSG_ERR_ALGO,
+                    "the packed prefill product with Bt needs pvals and Bt rows 16-byte aligned, pmeta 4-byte "
+                    "aligned and 256 rows of Bt within 31-bit offsets");
+    hipError_t e = ssg::launch_spmm_prefill_packed_bt(a, (hipStream_t)stream);
+    return e == hipSuccess ? SSG_OK : hip_fail(e, "packed prefill spmm (Bt) launch");
+}
+
 int64_t ssg_stream_read_sink_words(int64_t bytes) { return bytes > 0 ? ssg::stream_read_grid(bytes) : 0; }
 
 int ssg_stream_read(const void* src, int64_t bytes, uint32_t* sink, void* stream) {

@@ -320,3 +320,16 @@ def test_mfma_probe_description_and_argument_errors(lib):
     assert lib.ssg_mfma_probe(0, 0, 1, FAKE, None) == _abi.SSG_ERR_SHAPE
     assert lib.ssg_mfma_probe(0, 1, 0, FAKE, None) == _abi.SSG_ERR_SHAPE
     assert lib.ssg_mfma_probe(0, 1, 1, None, None) == _abi.SSG_ERR_NULL
+
+
+def test_prefill_bt_argument_errors(lib):
+    f = lib.ssg_spmm_2to4_prefill_bt
+    assert f(BF16, F32, 64, 16, 128, FAKE, FAKE, FAKE, 100, FAKE, 16, None) == _abi.SSG_ERR_STRIDE   # ldbt < K
+    assert f(BF16, F32, 64, 16, 128, FAKE, FAKE, FAKE, 128, FAKE, 8, None) == _abi.SSG_ERR_STRIDE    # ldc < N
+    assert f(BF16, F32, 64, 16, 96, FAKE, FAKE, FAKE, 128, FAKE, 16, None) == _abi.SSG_ERR_SHAPE     # K % 64
+    assert f(BF16, I32, 64, 16, 128, FAKE, FAKE, FAKE, 128, FAKE, 16, None) == _abi.SSG_ERR_DTYPE
+    assert f(BF16, F32, 64, 16, 128, FAKE, FAKE, None, 128, FAKE, 16, None) == _abi.SSG_ERR_NULL
+    # rows of Bt 8 bytes apart from a multiple of 16; Bt misaligned
+    assert f(BF16, F32, 64, 16, 128, FAKE, FAKE, FAKE, 132, FAKE, 16, None) == _abi.SSG_ERR_ALGO
+    assert f(BF16, F32, 64, 16, 128, FAKE, FAKE, ctypes.c_void_p(0x1008), 128, FAKE, 16, None) == _abi.SSG_ERR_ALGO
+    assert f(BF16, F32, 64, 0, 128, None, None, None, 128, None, 0, None) == 0                       # N = 0

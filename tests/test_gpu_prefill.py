@@ -184,3 +184,94 @@ def test_full_size_prefill(key):
         ms, ns = sample_entries(w.M, w.N, 3000, seed=w.index + 70)
         cref, sref = oracle.spmm_entries(w.dtype, r[0], r[1], b, w.K, ms, ns)
         check_product(w.dtype, Ch[ms, ns], cref, sref, key + " packed prefill")
+
+
+# ---- activation-major B (Bt [N, K] row-major) ------------------------------
+
+BT_SHAPES = [(64, 128, 16), (300, 384, 272), (256, 512, 256), (520, 1152, 528), (77, 256, 5), (600, 384, 1)]
+
+
+@pytest.mark.parametrize("dt", DTS)
+@pytest.mark.parametrize("shape", BT_SHAPES)
+def test_spmm_prefill_bt_matches_oracle(dt, shape):
+    # any N (ragged column tiles, fewer columns than one 16-byte chunk of a
+    # B row); against the oracle of C = A B with B = Bt^T, and the same bits
+    # as the row-major operand where that one takes the shape
+    M, K, N = shape
+    a = U.random_matrix(dt, M, K, "normal", seed=M + 13 * K)
+    bt = U.random_matrix(dt, N, K, "normal", seed=N + 17)
+    b = np.ascontiguousarray(np.asarray(bt).T)
+    vals, meta = oracle.compress(dt, a)
+    pv, pm = ssg.compress_prefill(to_dev(a, dt))
+    C = ssg.spmm_prefill_bt(pv, pm, M, to_dev(bt, dt))
+    cref, sref = oracle.spmm(dt, vals, meta, b, K)
+    check_product(dt, C.cpu().numpy(), cref, sref, "prefill Bt %s %s" % (dt, shape))
+    if N % (16 // np.dtype(U.store_dtype(dt)).itemsize) == 0:
+        C_rm = ssg.spmm_prefill(pv, pm, M, to_dev(b, dt))
+        assert torch.equal(C.view(torch.int32), C_rm.view(torch.int32))
+
+
+@pytest.mark.parametrize("dt", ["bf16", "i8"])
+def test_spmm_prefill_bt_strided_and_mixed_widths(dt):
+    # Bt rows longer than K (a column slice of a wider activation matrix)
+    # and 260 tiles, so the last row tiles run as half-width tiles
+    K = 128 if dt == "bf16" else 256
+    M, N = 256 * 20 - 37, 256 * 13 - 48
+    a = U.random_matrix(dt, M, K, "normal", seed=41)
+    wide = U.random_matrix(dt, N, K + 64, "normal", seed=43)
+    bt = np.asarray(wide)[:, 32:32 + K]
+    vals, meta = oracle.compress(dt, a)
+    pv, pm = ssg.compress_prefill(to_dev(a, dt))
+    Bw = to_dev(wide, dt)
+    C = ssg.spmm_prefill_bt(pv, pm, M, Bw[:, 32:32 + K])
+    b = np.ascontiguousarray(bt.T)
+    cref, sref = oracle.spmm(dt, vals, meta, b, K)
+    check_product(dt, C.cpu().numpy(), cref, sref, "prefill Bt strided %s" % dt)
+    C_rm = ssg.spmm_prefill(pv, pm, M, to_dev(b, dt))
+    assert torch.equal(C.view(torch.int32), C_rm.view(torch.int32))
+
+
+def test_spmm_prefill_bt_exact_small_integers():
+    M, K, N = 300, 640, 264
+    rng = np.random.default_rng(5)
+    a = rng.integers(-3, 4, size=(M, K)).astype(np.float16).view(np.uint16)
+    bt = rng.integers(-3, 4, size=(N, K)).astype(np.float16).view(np.uint16)
+    vals, meta = oracle.compress("f16", a)
+    pv, pm = ssg.compress_prefill(to_dev(a, "f16"))
+    C = ssg.spmm_prefill_bt(pv, pm, M, to_dev(bt, "f16")).cpu().numpy().astype(np.float64)
+    cref, _ = oracle.spmm("f16", vals, meta, np.ascontiguousarray(bt.T), K)
+    assert np.array_equal(C, cref)
+
+
+def test_spmm_prefill_bt_argument_errors():
+    a = U.random_matrix("bf16", 64, 128, "normal", 1)
+    pv, pm = ssg.compress_prefill(to_dev(a, "bf16"))
+    wide = to_dev(U.random_matrix("bf16", 16, 136, "normal", 2), "bf16")
+    with pytest.raises(ssg.SsgError) as e:      # rows of Bt not a multiple of 16 bytes apart
+        ssg.spmm_prefill_bt(pv, pm, 64, torch.empty((16, 132), dtype=torch.bfloat16, device="cuda")[:, :128])
+    assert e.value.status == 8
+    with pytest.raises(ssg.SsgError) as e:      # Bt not 16-byte aligned
+        ssg.spmm_prefill_bt(pv, pm, 64, wide[:, 4:132])
+    assert e.value.status == 8
+
+
+def test_full_size_prefill_bt():
+    # the headline shape with token-major activations: the same bits as the
+    # row-major B product, whose full-size parity is checked above, and
+    # whole rows against the oracle
+    w = W.WORKLOADS["c4"]
+    print("full-size packed prefill, Bt: %s" % w.title, flush=True)
+    a_cpu, b_cpu = W.gen_a(w), W.gen_b(w)
+    A, B = a_cpu.cuda(), b_cpu.cuda()
+    pv, pm = ssg.compress_prefill(A)
+    vals, meta = ssg.compress(A)
+    del A
+    Bt = B.t().contiguous()
+    C = ssg.spmm_prefill_bt(pv, pm, w.M, Bt)
+    C_rm = ssg.spmm_prefill(pv, pm, w.M, B)
+    assert torch.equal(C.view(torch.int32), C_rm.view(torch.int32))
+    del C_rm, Bt
+    rows = np.array([0, 255, 256, 13001, 24575, 24576, w.M - 1])
+    r = oracle.compress(w.dtype, W.bits(a_cpu))
+    cref, sref = oracle.spmm(w.dtype, r[0][rows], r[1][rows], W.bits(b_cpu), w.K)
+    check_product(w.dtype, C.cpu().numpy()[rows], cref, sref, "c4 packed prefill, Bt (whole rows)")
