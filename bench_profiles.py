@@ -47,6 +47,9 @@ COMMANDS = {
     "rates": "mkdir -p $R/gpurun_out && timeout -k 10 120 python3 $R/bench.py --mfma-rates > $R/gpurun_out/mfma_rates.json",
 }
 
+HEADLINE = "k_spmm_pipe<1, true, true>"     # the headline step's product
+TIMED = 20                                   # launches bench.py times back to back (--steps 20)
+
 # Kernels the counter passes attribute to a workload line of bench.py:
 # (kernel name as shortened below, workload line, kernel family, what).
 # The workload line names the bench entry whose algorithmic bytes apply; the
@@ -128,6 +131,19 @@ def trace(d: str) -> None:
     for k, (calls, tot, mn, mx) in sorted(agg.items(), key=lambda kv: -kv[1][1]):
         out.append("| %s | %d | %.2f | %.2f | %.2f | %.2f |\n" % (k, calls, tot / calls / 1e3, mn / 1e3, mx / 1e3,
                                                                   tot / 1e6))
+    # the headline product's last TIMED dispatches are the back-to-back
+    # launches bench.py times with HIP events for roofline.launch_us
+    tp = os.path.join(d, "run_kernel_trace.csv")
+    if os.path.exists(tp):
+        durs = [int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in csv.DictReader(open(tp))
+                if short(r["Kernel_Name"]) == HEADLINE]
+        last = durs[-TIMED:]
+        if last:
+            out.append("\nThe headline product %s: %d dispatches in the run; its last %d, the back-to-back launches "
+                       "bench.py times with HIP events for `roofline.launch_us`, average %.2f us (min %.2f, max %.2f). "
+                       "The other dispatches run inside the steps (after a compress) and in the graph check replays."
+                       "\n" % (HEADLINE, len(durs), len(last), sum(last) / len(last) / 1e3, min(last) / 1e3,
+                                max(last) / 1e3))
     with open(os.path.join(PROFILES, "bench_kernel_trace.md"), "w") as f:
         f.write("".join(out))
 
