@@ -395,7 +395,9 @@ def crossover(iters: int) -> dict:
     """Unstructured sparsity against dense and 2:4 at the fp16 decode shape
     M = K = 8192, N = 16: for each density, the vendor dense GEMM on the
     matrix with its zeros, the plain CSR and delta-coded sparse products,
-    and the exact 2:4 + residual split of the same matrix.  Operand copies
+    and the exact 2:4 + residual split of the same matrix (CSR residual
+    epilogue, and the complement-bitmap residual fused into the packed
+    product).  Operand copies
     (>= 1 GiB) are rotated so the Infinity Cache serves no repeated reads."""
     import numpy as np
     import torch
@@ -444,11 +446,18 @@ def crossover(iters: int) -> dict:
         err_delta = float((out - ref).abs().max() / ref.abs().max())
         r["split_us"], r["split_bytes"] = timed(sp, lambda o: ssg.ssg_spmm_2to4_residual(*o, B, out))
         err_split = float((out - ref).abs().max() / ref.abs().max())
-        r["max_rel_err_vs_fp32_dense"] = max(err_csr, err_delta, err_split)
+        # the same split with the residual as a complement bitmap, fused into
+        # the packed decode product's k-steps
+        cb = ssg.pack_decode(sp[0], sp[1], K) + ssg.pack_residual_cbm(sp[1], sp[2], sp[3], sp[4], K)
+        r["split_cbm_us"], r["split_cbm_bytes"] = timed(
+            cb, lambda o: ssg.ssg_spmm_2to4_packed_residual_cbm(o[0], o[1], M, o[2], o[3], o[4], B, out))
+        err_cbm = float((out - ref).abs().max() / ref.abs().max())
+        r["max_rel_err_vs_fp32_dense"] = max(err_csr, err_delta, err_split, err_cbm)
         rows.append(r)
-        print("crossover: density %.3f: dense %.1f us, csr %.1f us, delta %.1f us, 2:4+residual %.1f us"
-              % (d, r["dense_us"], r["csr_us"], r["delta_us"], r["split_us"]), file=sys.stderr, flush=True)
-        del A, row_ptr, col, vals, dl, sp, ref
+        print("crossover: density %.3f: dense %.1f us, csr %.1f us, delta %.1f us, 2:4+residual %.1f us, "
+              "2:4+bitmap fused %.1f us" % (d, r["dense_us"], r["csr_us"], r["delta_us"], r["split_us"],
+                                            r["split_cbm_us"]), file=sys.stderr, flush=True)
+        del A, row_ptr, col, vals, dl, sp, cb, ref
         torch.cuda.empty_cache()
 
     def below(key):
@@ -458,7 +467,8 @@ def crossover(iters: int) -> dict:
             "timing": "HIP events around back-to-back launches, >= 1 GiB of operand copies rotated",
             "rows": rows,
             "sparse_faster_than_dense_up_to_density": {"csr": below("csr_us"), "delta": below("delta_us"),
-                                                        "split": below("split_us")}}
+                                                        "split": below("split_us"),
+                                                        "split_cbm": below("split_cbm_us")}}
 
 
 def main() -> int:

@@ -4,6 +4,7 @@
     python bench_profiles.py traffic FETCH_DIR WRITE_DIR
     python bench_profiles.py sq      DIR             # DIR/run_counter_collection.csv
     python bench_profiles.py rates   FILE            # the JSON of bench.py --mfma-rates
+    python bench_profiles.py crossover FILE          # the JSON of bench.py --crossover
 
 `trace` turns the --kernel-trace --stats summary of a bench run into
 profiles/bench_kernel_trace.md.  `traffic` takes the two counter passes
@@ -13,7 +14,9 @@ for the plain 256 MiB copy that `bench.py --calib-copy` runs first, and
 writes profiles/traffic.json (read by bench.py for `roofline.traffic`) and
 profiles/hbm_counters.md.  `sq` writes the LDS and matrix-core counter table
 profiles/lds_mfma_counters.md.  `rates` writes the sparse vs dense
-matrix-core issue rates to profiles/mfma_rates_sparse_vs_dense.md.  Each summary names the command that made it;
+matrix-core issue rates to profiles/mfma_rates_sparse_vs_dense.md, and
+`crossover` the density study to profiles/crossover_fp16_8192x8192x16.md.
+Each summary names the command that made it;
 COMMANDS below are those commands, run from the repository root of a GPU
 machine with R set to that root.
 """
@@ -45,6 +48,7 @@ COMMANDS = {
           "-f csv -d $R/gpurun_out/pmc_sq -o run -- python3 $R/bench.py --steps 3 --warmup 1 --no-cpu-baseline "
           "--only c2,c3,c5 --workload-iters 10",
     "rates": "mkdir -p $R/gpurun_out && timeout -k 10 120 python3 $R/bench.py --mfma-rates > $R/gpurun_out/mfma_rates.json",
+    "crossover": "mkdir -p $R/gpurun_out && timeout -k 10 600 python3 $R/bench.py --crossover > $R/gpurun_out/crossover.json",
 }
 
 HEADLINE = "k_spmm_pipe<1, true, true>"     # the headline step's product
@@ -267,6 +271,32 @@ def rates(path: str) -> None:
         f.write("".join(out))
 
 
+def crossover(path: str) -> None:
+    with open(path) as f:
+        d = json.loads(f.read())
+    out = [header("Unstructured sparsity vs dense vs 2:4 + residual: fp16 decode shape M=K=8192, N=16",
+                  [COMMANDS["crossover"]]),
+           "A is `randn * 0.02` kept with probability `density` (torch CUDA generator seeded 5000), rounded to "
+           "fp16; B is `randn` [8192, 16] fp16.  Times are HIP events around back-to-back launches with >= 1 GiB of "
+           "operand copies rotated.  dense = the vendor fp16 GEMM (torch.matmul) on A with its zeros; csr / delta = "
+           "`ssg_spmm_csr` / `ssg_spmm_csr_delta` (no 2:4 layer); 2:4+CSR = `ssg_spmm_2to4_residual` on the exact "
+           "split of A (residual epilogue); 2:4+bitmap = `ssg_spmm_2to4_packed_residual_cbm` on the same split, "
+           "packed decode layout with the complement-bitmap residual fused into its k-steps.  Operand bytes are "
+           "the sparse format's.\n\n",
+           "| density | nnz | dense us | csr us | delta us | 2:4+CSR us | 2:4+bitmap us | csr MB | delta MB | "
+           "2:4+CSR MB | 2:4+bitmap MB | max rel err vs fp32 |\n|" + "---|" * 12 + "\n"]
+    for r in d["rows"]:
+        out.append("| %.3f | %d | %.1f | %.1f | %.1f | %.1f | %.1f | %.1f | %.1f | %.1f | %.1f | %.1e |\n" % (
+            r["density"], r["nnz"], r["dense_us"], r["csr_us"], r["delta_us"], r["split_us"], r["split_cbm_us"],
+            r["csr_bytes"] / 1e6, r["delta_bytes"] / 1e6, r["split_bytes"] / 1e6, r["split_cbm_bytes"] / 1e6,
+            r["max_rel_err_vs_fp32_dense"]))
+    b = d["sparse_faster_than_dense_up_to_density"]
+    out.append("\nSparse faster than dense up to density (of the densities measured): csr %s, delta %s, 2:4+CSR %s, "
+               "2:4+bitmap %s.\n" % (b["csr"], b["delta"], b["split"], b["split_cbm"]))
+    with open(os.path.join(PROFILES, "crossover_fp16_8192x8192x16.md"), "w") as f:
+        f.write("".join(out))
+
+
 def main(argv) -> int:
     if len(argv) >= 2 and argv[0] == "trace":
         trace(argv[1])
@@ -276,6 +306,8 @@ def main(argv) -> int:
         sq(argv[1])
     elif len(argv) >= 2 and argv[0] == "rates":
         rates(argv[1])
+    elif len(argv) >= 2 and argv[0] == "crossover":
+        crossover(argv[1])
     else:
         print(__doc__, file=sys.stderr)
         return 2
