@@ -1107,15 +1107,17 @@ __device__ __forceinline__ uint4 cbm_operand(const uint8_t* win, uint32_t zoff, 
 // K x 16 block).  Per wave and k-step g: the 2:4 fragments, index words,
 // mask words and block offsets of its tiles plus its two 1 KiB pieces of B
 // rows (group X(g), LX k-steps ahead), and the value windows of its tiles'
-// blocks (group Y(g), two direct-to-LDS loads of 1 KiB per tile, LY k-steps
-// ahead; their addresses need the block offsets, so a Y group is issued
-// once its X group has landed).  Iteration i waits until only the previous
-// iteration's two groups are outstanding, multiplies k-step g_i, then issues
-// Y(g_{i+LY}) and X(g_{i+LX}).  Every wave issues the same loads per
-// iteration (a k-step past K, a tile past the range or a window chunk past
-// a block's values reads zero from an out-of-range offset), so the waits
-// are exact counts.  Partial tiles are summed in wave order as in the
-// plain packed product.
+// blocks (group Y(g), LY k-steps ahead: one direct-to-LDS load of 1 KiB per
+// tile, two for the rare block whose values span more than that from the
+// 16-byte piece holding its first; their addresses need the block offsets,
+// so a Y group is issued once its X group has landed).  Iteration i waits
+// until only the previous iteration's two groups are outstanding,
+// multiplies k-step g_i, then issues Y(g_{i+LY}) and X(g_{i+LX}).  Every
+// wave issues at least the loads the waits count (a k-step past K, a tile
+// past the range or a window piece past a block's values reads zero from an
+// out-of-range offset), so each wait is exact or, after a second window
+// load, stricter.  Partial tiles are summed in wave order as in the plain
+// packed product.
 template <int DT, int TM, int W>
 __global__ void __launch_bounds__(W * 64) k_spmm_packed_cbm(SpmmArgs a, const uint8_t* pvals, const uint8_t* pmeta,
                                                             const uint8_t* rmask, const int32_t* roff,
@@ -1126,7 +1128,12 @@ __global__ void __launch_bounds__(W * 64) k_spmm_packed_cbm(SpmmArgs a, const ui
     using S = typename std::conditional<DT == DT_I8, int32_t, float>::type;
     constexpr int LX = C::LX, LY = C::LY, IDXB = C::IDXB, MB = C::MB;
     constexpr int GX = 2 + 4 * TM;                      // loads of an X group per wave
-    constexpr int GY = 2 * TM;                          // loads of a Y group per wave
+    // loads of a Y group per wave: one per tile, plus one for a tile whose
+    // window (its block's values, from the 16-byte piece that holds the
+    // first) spans more than 1 KiB.  The waits count one per tile: an extra
+    // load makes a wait stricter (loads complete in issue order), never
+    // looser.
+    constexpr int GY = TM;
     constexpr int WL = C::template wave_lds<TM>();
     static_assert(LX % LY == 0 && GX + GY < 64, "ring");
     static_assert(W * WL <= 160 * 1024 && W * kTMax * 1024 <= W * WL, "LDS");
@@ -1195,11 +1202,9 @@ __global__ void __launch_bounds__(W * 64) k_spmm_packed_cbm(SpmmArgs a, const ui
         for (int t = 0; t < TM; ++t) {
             const uint32_t start = ((uint32_t)ov[u][t][0] * T::ES) & ~15u, end = (uint32_t)ov[u][t][1] * T::ES;
             const uint32_t win = lds_addr + ybase + (uint32_t)((y * TM + t) * C::YWIN);
-#pragma unroll
-            for (int d = 0; d < 2; ++d) {
-                const uint32_t o = start + (uint32_t)(d * 1024 + lane * 16);
-                dma<16>(rc, win + d * 1024, o < end ? o : kOob);
-            }
+            const uint32_t o = start + (uint32_t)(lane * 16);
+            dma<16>(rc, win, o < end ? o : kOob);
+            if (end > start + 1024u) dma<16>(rc, win + 1024, o + 1024u < end ? o + 1024u : kOob);   // wave-uniform
         }
     };
 
