@@ -1104,20 +1104,20 @@ __device__ __forceinline__ uint4 cbm_operand(const uint8_t* win, uint32_t zoff, 
 }
 
 // Packed decode product with a complement-bitmap residual (B one contiguous
-// K x 16 block).  Per wave and k-step g: the 2:4 fragments, index words,
-// mask words and block offsets of its tiles plus its two 1 KiB pieces of B
-// rows (group X(g), LX k-steps ahead), and the value windows of its tiles'
-// blocks (group Y(g), LY k-steps ahead: one direct-to-LDS load of 1 KiB per
-// tile, two for the rare block whose values span more than that from the
-// 16-byte piece holding its first; their addresses need the block offsets,
-// so a Y group is issued once its X group has landed).  Iteration i waits
-// until only the previous iteration's two groups are outstanding,
-// multiplies k-step g_i, then issues Y(g_{i+LY}) and X(g_{i+LX}).  Every
-// wave issues at least the loads the waits count (a k-step past K, a tile
-// past the range or a window piece past a block's values reads zero from an
-// out-of-range offset), so each wait is exact or, after a second window
-// load, stricter.  Partial tiles are summed in wave order as in the plain
-// packed product.
+// K x 16 block).  Per wave and k-step g: the 2:4 fragments, index words and
+// mask words of its tiles plus its two 1 KiB pieces of B rows (group X(g),
+// LX k-steps ahead, with the tiles' block offsets by scalar loads), and the
+// value windows of its tiles' blocks (group Y(g), LY k-steps ahead: one
+// direct-to-LDS load of 1 KiB per tile, two for the rare block whose values
+// span more than that from the 16-byte piece holding its first; their
+// addresses need the block offsets, so a Y group is issued once its X group
+// has landed).  Iteration i waits until only the previous iteration's two
+// groups are outstanding, multiplies k-step g_i, then issues Y(g_{i+LY})
+// and X(g_{i+LX}).  Every wave issues at least the vector loads the waits
+// count (a k-step past K, a tile past the range or a window piece past a
+// block's values reads zero from an out-of-range offset), so each wait is
+// exact or, after a second window load, stricter.  Partial tiles are summed
+// in wave order as in the plain packed product.
 template <int DT, int TM, int W>
 __global__ void __launch_bounds__(W * 64) k_spmm_packed_cbm(SpmmArgs a, const uint8_t* pvals, const uint8_t* pmeta,
                                                             const uint8_t* rmask, const int32_t* roff,
@@ -1127,7 +1127,7 @@ __global__ void __launch_bounds__(W * 64) k_spmm_packed_cbm(SpmmArgs a, const ui
     using Acc = AccT<DT>;
     using S = typename std::conditional<DT == DT_I8, int32_t, float>::type;
     constexpr int LX = C::LX, LY = C::LY, IDXB = C::IDXB, MB = C::MB;
-    constexpr int GX = 2 + 4 * TM;                      // loads of an X group per wave
+    constexpr int GX = 2 + 3 * TM;                      // vector loads of an X group per wave
     // loads of a Y group per wave: one per tile, plus one for a tile whose
     // window (its block's values, from the 16-byte piece that holds the
     // first) spans more than 1 KiB.  The waits count one per tile: an extra
@@ -1154,24 +1154,31 @@ __global__ void __launch_bounds__(W * 64) k_spmm_packed_cbm(SpmmArgs a, const ui
     const __amdgpu_buffer_rsrc_t rm = rsrc(pmeta, tiles * ksteps * 64 * IDXB);
     const __amdgpu_buffer_rsrc_t rb = rsrc(a.B, a.K * 16 * T::ES);
     const __amdgpu_buffer_rsrc_t rk = rsrc(rmask, tiles * ksteps * 64 * MB);
-    const __amdgpu_buffer_rsrc_t ro = rsrc(reinterpret_cast<const uint8_t*>(roff), (tiles * ksteps + 1) * 4);
     // values: the host aligns cvals to 16 bytes, so the 16-byte block that
     // holds the last value is mapped; bytes past the array are never used
     const __amdgpu_buffer_rsrc_t rc = rsrc(cvals, (nvals * T::ES + 15) / 16 * 16);
-    uint32_t voff[TM], moff[TM], koff[TM], boff[TM];
+    uint32_t voff[TM], moff[TM], koff[TM];
+    int64_t bidx[TM];
 #pragma unroll
     for (int t = 0; t < TM; ++t) {
         const int64_t blk0 = (t0 + t) * ksteps;           // block of the tile's k-step 0
         voff[t] = t < nt ? (uint32_t)((blk0 * 64 + lane) * 16) : kOob;
         moff[t] = t < nt ? (uint32_t)((blk0 * 64 + lane) * IDXB) : kOob;
         koff[t] = t < nt ? (uint32_t)((blk0 * 64 + lane) * MB) : kOob;
-        boff[t] = t < nt ? (uint32_t)(blk0 * 4) : kOob;
+        bidx[t] = t < nt ? blk0 : -1;
     }
 
     i32x4 av[LX][TM] = {};   // native vector registers, so they can be tied to the waits below
     int mv[LX][TM] = {};
     int kv[LX][TM] = {};
-    i32x2 ov[LX][TM] = {};
+    // block offsets (roff[b], roff[b + 1]) of a group's tiles: wave-uniform,
+    // so scalar loads (through the constant address space), which the
+    // compiler waits for itself; past K or past the tiles they read as an
+    // empty range
+    int2 ov[LX][TM] = {};
+    bool lv[LX][TM] = {};
+    const __attribute__((address_space(4))) int32_t* roff_c =
+        (const __attribute__((address_space(4))) int32_t*)(uintptr_t)roff;
     auto issue_x = [&](int64_t g, int u) {
         const bool in = g < ksteps;
         const uint32_t slot = lds_addr + wbase + (uint32_t)(u * C::BSTEP);
@@ -1183,7 +1190,6 @@ __global__ void __launch_bounds__(W * 64) k_spmm_packed_cbm(SpmmArgs a, const ui
             const uint32_t o = in ? voff[t] + (uint32_t)(g * 1024) : kOob;
             const uint32_t om = in ? moff[t] + (uint32_t)(g * 64 * IDXB) : kOob;
             const uint32_t ok = in ? koff[t] + (uint32_t)(g * 64 * MB) : kOob;
-            const uint32_t oo = in ? boff[t] + (uint32_t)(g * 4) : kOob;
             asm volatile("buffer_load_dwordx4 %0, %1, %2, 0 offen nt" : "=v"(av[u][t]) : "v"(o), "s"(rv) : "memory");
             if constexpr (IDXB == 4)
                 asm volatile("buffer_load_dword %0, %1, %2, 0 offen nt" : "=v"(mv[u][t]) : "v"(om), "s"(rm) : "memory");
@@ -1193,14 +1199,19 @@ __global__ void __launch_bounds__(W * 64) k_spmm_packed_cbm(SpmmArgs a, const ui
                 asm volatile("buffer_load_ushort %0, %1, %2, 0 offen nt" : "=v"(kv[u][t]) : "v"(ok), "s"(rk) : "memory");
             else
                 asm volatile("buffer_load_ubyte %0, %1, %2, 0 offen nt" : "=v"(kv[u][t]) : "v"(ok), "s"(rk) : "memory");
-            asm volatile("buffer_load_dwordx2 %0, %1, %2, 0 offen" : "=v"(ov[u][t]) : "v"(oo), "s"(ro) : "memory");
+            // the range is emptied where it is used, not here, so the
+            // compiler's wait for the scalar load sits at the use
+            lv[u][t] = in && bidx[t] >= 0;
+            const int64_t b = lv[u][t] ? bidx[t] + g : 0;
+            ov[u][t] = make_int2(roff_c[b], roff_c[b + 1]);
         }
     };
     // the value windows of k-step g's blocks (X slot u landed) into Y slot y
     auto issue_y = [&](int u, int y) {
 #pragma unroll
         for (int t = 0; t < TM; ++t) {
-            const uint32_t start = ((uint32_t)ov[u][t][0] * T::ES) & ~15u, end = (uint32_t)ov[u][t][1] * T::ES;
+            const uint32_t start = lv[u][t] ? ((uint32_t)ov[u][t].x * T::ES) & ~15u : 0u;
+            const uint32_t end = lv[u][t] ? (uint32_t)ov[u][t].y * T::ES : 0u;
             const uint32_t win = lds_addr + ybase + (uint32_t)((y * TM + t) * C::YWIN);
             const uint32_t o = start + (uint32_t)(lane * 16);
             dma<16>(rc, win, o < end ? o : kOob);
@@ -1217,13 +1228,9 @@ __global__ void __launch_bounds__(W * 64) k_spmm_packed_cbm(SpmmArgs a, const ui
     issue_x(wave, 0);
     issue_x(wave + (int64_t)W, 1);
     wait_vm<GX>();
-#pragma unroll
-    for (int t = 0; t < TM; ++t) asm volatile("" : "+v"(ov[0][t]));
     issue_y(0, 0);
     issue_x(wave + (int64_t)2 * W, 2);
     wait_vm<GY + GX>();
-#pragma unroll
-    for (int t = 0; t < TM; ++t) asm volatile("" : "+v"(ov[1][t]));
     issue_y(1, 1);
     issue_x(wave + (int64_t)3 * W, 3);
 
@@ -1237,7 +1244,7 @@ __global__ void __launch_bounds__(W * 64) k_spmm_packed_cbm(SpmmArgs a, const ui
                 wait_vm<GY + GX>();
 #pragma unroll
                 for (int t = 0; t < TM; ++t)
-                    asm volatile("" : "+v"(av[u][t]), "+v"(mv[u][t]), "+v"(kv[u][t]), "+v"(ov[u][t]), "+v"(ov[u2][t]));
+                    asm volatile("" : "+v"(av[u][t]), "+v"(mv[u][t]), "+v"(kv[u][t]));
                 uint4 b[2];
                 load_b_operand<DT>(lds + wbase + u * C::BSTEP, 0, lane, b);
 #pragma unroll
@@ -1252,7 +1259,7 @@ __global__ void __launch_bounds__(W * 64) k_spmm_packed_cbm(SpmmArgs a, const ui
                     if (__builtin_amdgcn_ballot_w64(mask != 0u) != 0) {      // wave-uniform
                         const int pc = __popc(mask);
                         const uint32_t before = (uint32_t)(wave_incl_sum(pc, lane) - pc);
-                        const uint32_t ro0 = (uint32_t)ov[u][t][0];
+                        const uint32_t ro0 = (uint32_t)ov[u][t].x;
                         const uint32_t e0 = ((ro0 * T::ES) & 15u) / T::ES + before;
                         const uint8_t* win = lds + ybase + (y * TM + t) * C::YWIN;
                         const uint4 f = cbm_operand<DT>(win, zpad - (ybase + (uint32_t)((y * TM + t) * C::YWIN)), e0,
@@ -1274,7 +1281,7 @@ __global__ void __launch_bounds__(W * 64) k_spmm_packed_cbm(SpmmArgs a, const ui
 #pragma unroll
     for (int u = 0; u < LX; ++u)
 #pragma unroll
-        for (int t = 0; t < TM; ++t) asm volatile("" ::"v"(av[u][t]), "v"(mv[u][t]), "v"(kv[u][t]), "v"(ov[u][t]));
+        for (int t = 0; t < TM; ++t) asm volatile("" ::"v"(av[u][t]), "v"(mv[u][t]), "v"(kv[u][t]));
     lds_barrier();
 
     // fixed-order reduction of the waves' partial tiles
