@@ -242,8 +242,9 @@ def bench_workload(key: str, iters: int, delta: bool = False, dense_cmp: bool = 
     next to a dense GEMM of the same shape from the vendor library.  With
     delta=True the residual is delta-coded (one-byte column gaps); with
     packed=True the 2:4 operand is in the packed decode layout; with
-    prefill=True in the packed prefill layout (bt=True: B handed over
-    activation-major, as Bt [N, K] row-major); with nm=(n, m) the weight is
+    prefill=True in the packed prefill layout (bt=True, with prefill or
+    packed: B handed over activation-major, as Bt [N, K] row-major); with
+    nm=(n, m) the weight is
     in the n:m form (kept values plus keep mask); with cbm=True (and packed)
     the residual is in the complement-bitmap layout, fused into the packed
     product's k-steps."""
@@ -284,7 +285,9 @@ def bench_workload(key: str, iters: int, delta: bool = False, dense_cmp: bool = 
 
     def launch(i):
         o = sets[i % copies]
-        if cbm:
+        if cbm and bt:
+            ssg.ssg_spmm_2to4_packed_residual_cbm_bt(o[0], o[1], w.M, o[2], o[3], o[4], b_t, out)
+        elif cbm:
             ssg.ssg_spmm_2to4_packed_residual_cbm(o[0], o[1], w.M, o[2], o[3], o[4], b, out)
         elif nm is not None and packed:
             ssg.ssg_spmm_nm_packed(o[0], o[1], nm[0], nm[1], w.M, b, out, i4=w.dtype == "i4")
@@ -294,6 +297,8 @@ def bench_workload(key: str, iters: int, delta: bool = False, dense_cmp: bool = 
             ssg.ssg_spmm_2to4_packed_residual_delta(o[0], o[1], w.M, o[2], o[3], o[4], b, out)
         elif packed and w.residual:
             ssg.ssg_spmm_2to4_packed_residual(o[0], o[1], w.M, o[2], o[3], o[4], b, out)
+        elif packed and bt:
+            ssg.ssg_spmm_2to4_packed_bt(o[0], o[1], w.M, b_t, out)
         elif packed:
             ssg.ssg_spmm_2to4_packed(o[0], o[1], w.M, b, out)
         elif prefill and bt:
@@ -728,9 +733,15 @@ def main() -> int:
                 print("bench: workload %s, packed decode layout, complement-bitmap residual ..." % k,
                       file=sys.stderr, flush=True)
                 table[k + "_cbm_packed"] = bench_workload(k, it, dense_cmp=False, packed=True, cbm=True)
+                print("bench: workload %s, packed decode layout, complement-bitmap residual, activation-major B ..."
+                      % k, file=sys.stderr, flush=True)
+                table[k + "_cbm_packed_bt"] = bench_workload(k, it, dense_cmp=False, packed=True, cbm=True, bt=True)
             elif W.WORKLOADS[k].klass == "small_n" and W.WORKLOADS[k].N == 16:
                 print("bench: workload %s, packed decode layout ..." % k, file=sys.stderr, flush=True)
                 table[k + "_packed"] = bench_workload(k, it, dense_cmp=False, packed=True)
+                print("bench: workload %s, packed decode layout, activation-major B ..." % k, file=sys.stderr,
+                      flush=True)
+                table[k + "_packed_bt"] = bench_workload(k, it, dense_cmp=False, packed=True, bt=True)
         out["workloads"] = table
     print(json.dumps(out))
     return 0

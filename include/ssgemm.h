@@ -260,6 +260,19 @@ int ssg_pack_2to4_decode(int dt, int64_t M, int64_t K, const void* vals, int64_t
 int ssg_spmm_2to4_packed(int ab, int c, int64_t M, int64_t N, int64_t K, const void* pvals, const void* pmeta,
                          const void* B, int64_t ldb, void* C, int64_t ldc, void* stream);
 
+/* The same product with B given as its transpose: Bt [N, K] row-major (row
+ * stride ldbt >= K elements), the token-major layout in which a decode
+ * step's activations arrive, for any 1 <= N <= 16 (no padding).  Each lane
+ * of the kernel loads its B operand straight into registers as two 16-byte
+ * pieces of one row of Bt, instead of staging B through LDS.  The result has
+ * the same bits as ssg_spmm_2to4_packed on B = Bt^T (N == 16).  Needs Bt
+ * 16-byte aligned, rows a multiple of 16 bytes apart (SSG_ERR_STRIDE
+ * otherwise) and 16 * ldbt elements within 31-bit byte offsets
+ * (SSG_ERR_SHAPE); N outside [1, 16] gives SSG_ERR_ALGO, N == 0 is a
+ * no-op. */
+int ssg_spmm_2to4_packed_bt(int ab, int c, int64_t M, int64_t N, int64_t K, const void* pvals, const void* pmeta,
+                            const void* Bt, int64_t ldbt, void* C, int64_t ldc, void* stream);
+
 /* The same product plus a residual layer ("How sparse LLM weights cut GPU
  * inference cost without quantization", section "How the three-layer
  * format makes moderate sparsity fast"): C = expand(packed) x B + R x B,
@@ -508,6 +521,13 @@ int ssg_spmm_2to4_packed_residual_cbm(int ab, int c, int64_t M, int64_t N, int64
                                       const void* pvals, const void* pmeta, const uint8_t* rmask,
                                       const int32_t* roff, const void* cvals, int64_t nvals,
                                       const void* B, int64_t ldb, void* C, int64_t ldc, void* stream);
+
+/* The same with B given as Bt [N, K] row-major, 1 <= N <= 16, under the
+ * conditions of ssg_spmm_2to4_packed_bt. */
+int ssg_spmm_2to4_packed_residual_cbm_bt(int ab, int c, int64_t M, int64_t N, int64_t K, const void* pvals,
+                                         const void* pmeta, const uint8_t* rmask, const int32_t* roff,
+                                         const void* cvals, int64_t nvals, const void* Bt, int64_t ldbt, void* C,
+                                         int64_t ldc, void* stream);
 
 /* Measurement helper (not part of the product): one streaming read of
  * `bytes` bytes of device memory at src (16-byte aligned, bytes a multiple

@@ -268,6 +268,14 @@ def ssg_spmm_2to4_packed(pvals, pmeta, M: int, B, C, stream=None) -> None:
            "ssg_spmm_2to4_packed")
 
 
+def ssg_spmm_2to4_packed_bt(pvals, pmeta, M: int, Bt, C, stream=None) -> None:
+    ab = _dtype(Bt)
+    N, K = Bt.shape[0], Bt.shape[1]
+    _check(_lib().ssg_spmm_2to4_packed_bt(ab, _OUT[ab][0], M, N, K, _ptr(pvals, "pvals"), _ptr(pmeta, "pmeta"),
+                                          _ptr(Bt, "Bt"), _ld(Bt, "Bt"), _ptr(C, "C"), _ld(C, "C"),
+                                          _stream(C, stream)), "ssg_spmm_2to4_packed_bt")
+
+
 def ssg_prefill_packed_sizes(dtype: torch.dtype, M: int, K: int) -> Tuple[int, int]:
     import ctypes
     vb, mb = ctypes.c_int64(0), ctypes.c_int64(0)
@@ -373,6 +381,16 @@ def ssg_spmm_2to4_packed_residual_cbm(pvals, pmeta, M: int, rmask, roff, cvals, 
                                                     _ptr(cvals, "cvals"), int(cvals.numel()), _ptr(B, "B"),
                                                     _ld(B, "B"), _ptr(C, "C"), _ld(C, "C"), _stream(C, stream)),
            "ssg_spmm_2to4_packed_residual_cbm")
+
+
+def ssg_spmm_2to4_packed_residual_cbm_bt(pvals, pmeta, M: int, rmask, roff, cvals, Bt, C, stream=None) -> None:
+    ab = _dtype(Bt)
+    N, K = Bt.shape[0], Bt.shape[1]
+    _check(_lib().ssg_spmm_2to4_packed_residual_cbm_bt(ab, _OUT[ab][0], M, N, K, _ptr(pvals, "pvals"),
+                                                       _ptr(pmeta, "pmeta"), _ptr(rmask, "rmask"), _ptr(roff, "roff"),
+                                                       _ptr(cvals, "cvals"), int(cvals.numel()), _ptr(Bt, "Bt"),
+                                                       _ld(Bt, "Bt"), _ptr(C, "C"), _ld(C, "C"), _stream(C, stream)),
+           "ssg_spmm_2to4_packed_residual_cbm_bt")
 
 
 def ssg_stream_read_sink_words(nbytes: int) -> int:
@@ -698,6 +716,25 @@ def spmm_packed_residual_cbm(pvals, pmeta, M: int, rmask, roff, cvals, B: torch.
     ab = _dtype(B)
     C = torch.empty((M, B.shape[1]), dtype=_OUT[ab][1], device=B.device) if out is None else out
     ssg_spmm_2to4_packed_residual_cbm(pvals, pmeta, M, rmask, roff, cvals, B, C)
+    return C
+
+
+def spmm_packed_residual_cbm_bt(pvals, pmeta, M: int, rmask, roff, cvals, Bt: torch.Tensor,
+                                out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """As spmm_packed_residual_cbm with B given as Bt [N, K] row-major, N <= 16."""
+    ab = _dtype(Bt)
+    C = torch.empty((M, Bt.shape[0]), dtype=_OUT[ab][1], device=Bt.device) if out is None else out
+    ssg_spmm_2to4_packed_residual_cbm_bt(pvals, pmeta, M, rmask, roff, cvals, Bt, C)
+    return C
+
+
+def spmm_packed_bt(pvals: torch.Tensor, pmeta: torch.Tensor, M: int, Bt: torch.Tensor,
+                   out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """C = expand(packed) @ Bt.T, Bt [N, K] row-major with N <= 16
+    (token-major activations of a decode step)."""
+    ab = _dtype(Bt)
+    C = torch.empty((M, Bt.shape[0]), dtype=_OUT[ab][1], device=Bt.device) if out is None else out
+    ssg_spmm_2to4_packed_bt(pvals, pmeta, M, Bt, C)
     return C
 
 

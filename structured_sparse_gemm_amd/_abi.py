@@ -51,6 +51,7 @@ SIGNATURES = {
     "ssg_packed_sizes": (_i, [_i, _i64, _i64, ctypes.POINTER(_i64), ctypes.POINTER(_i64)]),
     "ssg_pack_2to4_decode": (_i, [_i, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _vp, _vp]),
     "ssg_spmm_2to4_packed": (_i, [_i, _i, _i64, _i64, _i64, _vp, _vp, _vp, _i64, _vp, _i64, _vp]),
+    "ssg_spmm_2to4_packed_bt": (_i, [_i, _i, _i64, _i64, _i64, _vp, _vp, _vp, _i64, _vp, _i64, _vp]),
     "ssg_spmm_2to4_packed_residual": (_i, [_i, _i, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _i64, _vp, _i64, _vp,
                                            _i64, _vp]),
     "ssg_spmm_2to4_packed_residual_delta": (_i, [_i, _i, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _i64, _vp, _i64,
@@ -73,6 +74,8 @@ SIGNATURES = {
     "ssg_pack_residual_cbm": (_i, [_i, _i64, _i64, _vp, _i64, _vp, _vp, _vp, _i64, _vp, _vp, _vp, _vp, _vp]),
     "ssg_spmm_2to4_packed_residual_cbm": (_i, [_i, _i, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _i64, _vp, _i64, _vp,
                                                _i64, _vp]),
+    "ssg_spmm_2to4_packed_residual_cbm_bt": (_i, [_i, _i, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _i64, _vp, _i64,
+                                                  _vp, _i64, _vp]),
     "ssg_stream_read_sink_words": (_i64, [_i64]),
     "ssg_stream_read": (_i, [_vp, _i64, _vp, _vp]),
     "ssg_mfma_probe_forms": (_i, []),

@@ -883,7 +883,14 @@ __global__ void __launch_bounds__(256) k_pack(int64_t M, int64_t K, const uint8_
 // epilogue: the 2:4 sums go to LDS, the first residual passes are loaded
 // while the weight stream drains, then B is staged in chunks over the LDS
 // below the row sums and the residual rows are consumed chunk by chunk.
-template <int DT, int TM, int P, bool RES, bool DELTA>
+// With activation-major B (BT: a.B is Bt [N, K] row-major, N <= 16, row
+// stride a.ldb) each lane loads its own B operand of a k-step straight into
+// registers: column n = l % 16, block bb = l / 16 holds dense k (e / H) *
+// (KS / 2) + H * bb + e % H, which is two 16-byte pieces of row n of Bt, at k
+// offsets H * bb and KS / 2 + H * bb (H = KS / 8 elements).  A load then
+// reads 64 contiguous bytes of each of 16 rows, nothing passes through LDS
+// and no transposing read is needed; rows past N read zero.
+template <int DT, int TM, int P, bool RES, bool DELTA, bool BT = false>
 __global__ void __launch_bounds__(kWaves * 64) k_spmm_packed(SpmmArgs a, const uint8_t* pvals, const uint8_t* pmeta,
                                                              int64_t tiles) {
     constexpr int W = kWaves;
@@ -906,22 +913,34 @@ __global__ void __launch_bounds__(kWaves * 64) k_spmm_packed(SpmmArgs a, const u
 
     const __amdgpu_buffer_rsrc_t rv = rsrc(pvals, tiles * ksteps * 1024);
     const __amdgpu_buffer_rsrc_t rm = rsrc(pmeta, tiles * ksteps * 64 * IDXB);
-    const __amdgpu_buffer_rsrc_t rb = rsrc(a.B, a.K * 16 * T::ES);
+    const __amdgpu_buffer_rsrc_t rb = BT ? rsrc(a.B, ((a.N - 1) * a.ldb + a.K) * T::ES) : rsrc(a.B, a.K * 16 * T::ES);
     uint32_t voff[TM], moff[TM];
 #pragma unroll
     for (int t = 0; t < TM; ++t) {
         voff[t] = t < nt ? (uint32_t)(((t0 + t) * ksteps * 64 + lane) * 16) : kOob;
         moff[t] = t < nt ? (uint32_t)(((t0 + t) * ksteps * 64 + lane) * IDXB) : kOob;
     }
+    // BT: this lane's piece of row lane % 16 of Bt at k-step 0 (a row past N
+    // is an offset past the buffer)
+    const uint32_t bt_off = (lane & 15) < a.N
+                                ? (uint32_t)(((lane & 15) * a.ldb + (lane >> 4) * (T::KS / 8)) * T::ES)
+                                : kOob;
 
     i32x4 av[P][TM] = {};   // native vector registers, so they can be tied to the waits below
     int mv[P][TM] = {};
+    i32x4 bv[P][2] = {};    // BT: the wave's B operand of each k-step in flight
     auto issue = [&](int64_t g, int u) {
         const bool in = g < ksteps;
         const uint32_t slot = lds_addr + (uint32_t)((wave * P + u) * BSTEP);
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
-            dma<16>(rb, slot + j * 1024, in ? (uint32_t)(g * BSTEP + j * 1024 + lane * 16) : kOob);
+        for (int j = 0; j < 2; ++j) {
+            if constexpr (BT) {
+                const uint32_t ob = in && bt_off != kOob ? bt_off + (uint32_t)((g * T::KS + j * (T::KS / 2)) * T::ES) : kOob;
+                asm volatile("buffer_load_dwordx4 %0, %1, %2, 0 offen" : "=v"(bv[u][j]) : "v"(ob), "s"(rb) : "memory");
+            } else {
+                dma<16>(rb, slot + j * 1024, in ? (uint32_t)(g * BSTEP + j * 1024 + lane * 16) : kOob);
+            }
+        }
 #pragma unroll
         for (int t = 0; t < TM; ++t) {
             const uint32_t o = in ? voff[t] + (uint32_t)(g * 1024) : kOob;
@@ -963,7 +982,14 @@ __global__ void __launch_bounds__(kWaves * 64) k_spmm_packed(SpmmArgs a, const u
 #pragma unroll
                 for (int t = 0; t < TM; ++t) asm volatile("" : "+v"(av[u][t]), "+v"(mv[u][t]));
                 uint4 b[2];
-                load_b_operand<DT>(lds + (wave * P + u) * BSTEP, 0, lane, b);
+                if constexpr (BT) {
+                    asm volatile("" : "+v"(bv[u][0]));
+                    asm volatile("" : "+v"(bv[u][1]));
+                    __builtin_memcpy(&b[0], &bv[u][0], 16);
+                    __builtin_memcpy(&b[1], &bv[u][1], 16);
+                } else {
+                    load_b_operand<DT>(lds + (wave * P + u) * BSTEP, 0, lane, b);
+                }
 #pragma unroll
                 for (int t = 0; t < TM; ++t) {
                     uint4 f;
@@ -986,9 +1012,11 @@ __global__ void __launch_bounds__(kWaves * 64) k_spmm_packed(SpmmArgs a, const u
     // written when issued, so the ring stays in use until the wait)
     wait_vm<0>();
 #pragma unroll
-    for (int u = 0; u < P; ++u)
+    for (int u = 0; u < P; ++u) {
 #pragma unroll
         for (int t = 0; t < TM; ++t) asm volatile("" ::"v"(av[u][t]), "v"(mv[u][t]));
+        if constexpr (BT) asm volatile("" ::"v"(bv[u][0]), "v"(bv[u][1]));
+    }
     lds_barrier();
 
     // fixed-order reduction of the waves' partial tiles
@@ -1117,8 +1145,10 @@ __device__ __forceinline__ uint4 cbm_operand(const uint8_t* win, uint32_t zoff, 
 // count (a k-step past K, a tile past the range or a window piece past a
 // block's values reads zero from an out-of-range offset), so each wait is
 // exact or, after a second window load, stricter.  Partial tiles are summed
-// in wave order as in the plain packed product.
-template <int DT, int TM, int W>
+// in wave order as in the plain packed product.  With activation-major B
+// (BT) the two B pieces of an X group are the lane's own B operand, loaded
+// straight into registers as in the plain packed product.
+template <int DT, int TM, int W, bool BT = false>
 __global__ void __launch_bounds__(W * 64) k_spmm_packed_cbm(SpmmArgs a, const uint8_t* pvals, const uint8_t* pmeta,
                                                             const uint8_t* rmask, const int32_t* roff,
                                                             const uint8_t* cvals, int64_t nvals, int64_t tiles) {
@@ -1152,8 +1182,11 @@ __global__ void __launch_bounds__(W * 64) k_spmm_packed_cbm(SpmmArgs a, const ui
 
     const __amdgpu_buffer_rsrc_t rv = rsrc(pvals, tiles * ksteps * 1024);
     const __amdgpu_buffer_rsrc_t rm = rsrc(pmeta, tiles * ksteps * 64 * IDXB);
-    const __amdgpu_buffer_rsrc_t rb = rsrc(a.B, a.K * 16 * T::ES);
+    const __amdgpu_buffer_rsrc_t rb = BT ? rsrc(a.B, ((a.N - 1) * a.ldb + a.K) * T::ES) : rsrc(a.B, a.K * 16 * T::ES);
     const __amdgpu_buffer_rsrc_t rk = rsrc(rmask, tiles * ksteps * 64 * MB);
+    const uint32_t bt_off = (lane & 15) < a.N
+                                ? (uint32_t)(((lane & 15) * a.ldb + (lane >> 4) * (T::KS / 8)) * T::ES)
+                                : kOob;
     // values: the host aligns cvals to 16 bytes, so the 16-byte block that
     // holds the last value is mapped; bytes past the array are never used
     const __amdgpu_buffer_rsrc_t rc = rsrc(cvals, (nvals * T::ES + 15) / 16 * 16);
@@ -1171,6 +1204,7 @@ __global__ void __launch_bounds__(W * 64) k_spmm_packed_cbm(SpmmArgs a, const ui
     i32x4 av[LX][TM] = {};   // native vector registers, so they can be tied to the waits below
     int mv[LX][TM] = {};
     int kv[LX][TM] = {};
+    i32x4 bv[LX][2] = {};    // BT: the wave's B operand of each k-step in flight
     // block offsets (roff[b], roff[b + 1]) of a group's tiles: wave-uniform,
     // so scalar loads (through the constant address space), which the
     // compiler waits for itself; past K or past the tiles they read as an
@@ -1183,8 +1217,14 @@ __global__ void __launch_bounds__(W * 64) k_spmm_packed_cbm(SpmmArgs a, const ui
         const bool in = g < ksteps;
         const uint32_t slot = lds_addr + wbase + (uint32_t)(u * C::BSTEP);
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
-            dma<16>(rb, slot + j * 1024, in ? (uint32_t)(g * C::BSTEP + j * 1024 + lane * 16) : kOob);
+        for (int j = 0; j < 2; ++j) {
+            if constexpr (BT) {
+                const uint32_t ob = in && bt_off != kOob ? bt_off + (uint32_t)((g * T::KS + j * (T::KS / 2)) * T::ES) : kOob;
+                asm volatile("buffer_load_dwordx4 %0, %1, %2, 0 offen" : "=v"(bv[u][j]) : "v"(ob), "s"(rb) : "memory");
+            } else {
+                dma<16>(rb, slot + j * 1024, in ? (uint32_t)(g * C::BSTEP + j * 1024 + lane * 16) : kOob);
+            }
+        }
 #pragma unroll
         for (int t = 0; t < TM; ++t) {
             const uint32_t o = in ? voff[t] + (uint32_t)(g * 1024) : kOob;
@@ -1246,7 +1286,14 @@ __global__ void __launch_bounds__(W * 64) k_spmm_packed_cbm(SpmmArgs a, const ui
                 for (int t = 0; t < TM; ++t)
                     asm volatile("" : "+v"(av[u][t]), "+v"(mv[u][t]), "+v"(kv[u][t]));
                 uint4 b[2];
-                load_b_operand<DT>(lds + wbase + u * C::BSTEP, 0, lane, b);
+                if constexpr (BT) {
+                    asm volatile("" : "+v"(bv[u][0]));
+                    asm volatile("" : "+v"(bv[u][1]));
+                    __builtin_memcpy(&b[0], &bv[u][0], 16);
+                    __builtin_memcpy(&b[1], &bv[u][1], 16);
+                } else {
+                    load_b_operand<DT>(lds + wbase + u * C::BSTEP, 0, lane, b);
+                }
 #pragma unroll
                 for (int t = 0; t < TM; ++t) {
                     uint4 f;
@@ -1279,9 +1326,11 @@ __global__ void __launch_bounds__(W * 64) k_spmm_packed_cbm(SpmmArgs a, const ui
     // written when issued, so the ring stays in use until the wait)
     wait_vm<0>();
 #pragma unroll
-    for (int u = 0; u < LX; ++u)
+    for (int u = 0; u < LX; ++u) {
 #pragma unroll
         for (int t = 0; t < TM; ++t) asm volatile("" ::"v"(av[u][t]), "v"(mv[u][t]), "v"(kv[u][t]));
+        if constexpr (BT) asm volatile("" ::"v"(bv[u][0]), "v"(bv[u][1]));
+    }
     lds_barrier();
 
     // fixed-order reduction of the waves' partial tiles
@@ -1301,19 +1350,19 @@ __global__ void __launch_bounds__(W * 64) k_spmm_packed_cbm(SpmmArgs a, const ui
     }
 }
 
-template <int DT, int TM, int W>
+template <int DT, int TM, int W, bool BT>
 void launch_packed_cbm_w(const SpmmArgs& a, const uint8_t* pv, const uint8_t* pm, const uint8_t* rmask,
                          const int32_t* roff, const uint8_t* cvals, int64_t nvals, int64_t tiles, hipStream_t s) {
-    hipLaunchKernelGGL((k_spmm_packed_cbm<DT, TM, W>), dim3((unsigned)((tiles + TM - 1) / TM)), dim3(64 * W),
+    hipLaunchKernelGGL((k_spmm_packed_cbm<DT, TM, W, BT>), dim3((unsigned)((tiles + TM - 1) / TM)), dim3(64 * W),
                        W * Cbm<DT>::template wave_lds<TM>(), s, a, pv, pm, rmask, roff, cvals, nvals, tiles);
 }
 
-template <int DT>
+template <int DT, bool BT = false>
 hipError_t launch_packed_cbm_t(const SpmmArgs& a, const uint8_t* pv, const uint8_t* pm, const uint8_t* rmask,
                                const int32_t* roff, const uint8_t* cvals, int64_t nvals, hipStream_t s) {
     const int64_t tiles = (a.M + 15) / 16;
-    if (tiles <= 256) launch_packed_cbm_w<DT, 1, kWaves>(a, pv, pm, rmask, roff, cvals, nvals, tiles, s);
-    else launch_packed_cbm_w<DT, 2, kWaves>(a, pv, pm, rmask, roff, cvals, nvals, tiles, s);
+    if (tiles <= 256) launch_packed_cbm_w<DT, 1, kWaves, BT>(a, pv, pm, rmask, roff, cvals, nvals, tiles, s);
+    else launch_packed_cbm_w<DT, 2, kWaves, BT>(a, pv, pm, rmask, roff, cvals, nvals, tiles, s);
     return hipGetLastError();
 }
 
@@ -1327,14 +1376,14 @@ template <int TM> constexpr int kPackedP = TM == 1 ? 3 : 2;
 // whole LDS (B chunks below the row sums)
 template <int TM> constexpr int kPackedResP = TM == 4 ? 2 : 3;
 
-template <int DT, int TM>
+template <int DT, int TM, bool BT = false>
 hipError_t launch_packed_tm(const SpmmArgs& a, const uint8_t* pv, const uint8_t* pm, int64_t tiles, int64_t G,
                             hipStream_t s) {
-    if (a.row_ptr == nullptr) {
+    if (BT || a.row_ptr == nullptr) {
         constexpr int P = kPackedP<TM>;
         const unsigned shm = (unsigned)(kWaves * P * 16 * SN<DT>::ES * SN<DT>::KS);
-        hipLaunchKernelGGL((k_spmm_packed<DT, TM, P, false, false>), dim3((unsigned)G), dim3(64 * kWaves), shm, s, a,
-                           pv, pm, tiles);
+        hipLaunchKernelGGL((k_spmm_packed<DT, TM, P, false, false, BT>), dim3((unsigned)G), dim3(64 * kWaves), shm, s,
+                           a, pv, pm, tiles);
     } else {
         constexpr int P = kPackedResP<TM>;
         static_assert(kWaves * P * 16 * 2 * 64 <= kRingResOff, "ring slots below the row sums");
@@ -1348,17 +1397,17 @@ hipError_t launch_packed_tm(const SpmmArgs& a, const uint8_t* pv, const uint8_t*
     return hipGetLastError();
 }
 
-template <int DT>
+template <int DT, bool BT = false>
 hipError_t launch_packed_t(const SpmmArgs& a, const uint8_t* pv, const uint8_t* pm, hipStream_t s) {
     const int64_t tiles = (a.M + 15) / 16;
     int64_t G = tiles < 256 ? tiles : 256;
     if (G * kTMax < tiles) G = (tiles + kTMax - 1) / kTMax;
     const int tm = (int)((tiles + G - 1) / G);
     switch (tm) {
-        case 1: return launch_packed_tm<DT, 1>(a, pv, pm, tiles, G, s);
-        case 2: return launch_packed_tm<DT, 2>(a, pv, pm, tiles, G, s);
-        case 3: return launch_packed_tm<DT, 3>(a, pv, pm, tiles, G, s);
-        default: return launch_packed_tm<DT, 4>(a, pv, pm, tiles, G, s);
+        case 1: return launch_packed_tm<DT, 1, BT>(a, pv, pm, tiles, G, s);
+        case 2: return launch_packed_tm<DT, 2, BT>(a, pv, pm, tiles, G, s);
+        case 3: return launch_packed_tm<DT, 3, BT>(a, pv, pm, tiles, G, s);
+        default: return launch_packed_tm<DT, 4, BT>(a, pv, pm, tiles, G, s);
     }
 }
 
@@ -1587,6 +1636,19 @@ hipError_t launch_spmm_packed(const SpmmArgs& a, const void* pvals, const void* 
     }
 }
 
+hipError_t launch_spmm_packed_bt(const SpmmArgs& a, const void* pvals, const void* pmeta, hipStream_t s) {
+    const uint8_t* pv = (const uint8_t*)pvals;
+    const uint8_t* pm = (const uint8_t*)pmeta;
+    switch (a.dt) {
+        case DT_F16: return launch_packed_t<DT_F16, true>(a, pv, pm, s);
+        case DT_BF16: return launch_packed_t<DT_BF16, true>(a, pv, pm, s);
+        case DT_I8: return launch_packed_t<DT_I8, true>(a, pv, pm, s);
+        case DT_E4M3: return launch_packed_t<DT_E4M3, true>(a, pv, pm, s);
+        case DT_E5M2: return launch_packed_t<DT_E5M2, true>(a, pv, pm, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
 hipError_t launch_spmm_packed_cbm(const SpmmArgs& a, const void* pvals, const void* pmeta, const void* rmask,
                                   const int32_t* roff, const void* cvals, int64_t nvals, hipStream_t s) {
     const uint8_t* pv = (const uint8_t*)pvals;
@@ -1599,6 +1661,22 @@ hipError_t launch_spmm_packed_cbm(const SpmmArgs& a, const void* pvals, const vo
         case DT_I8: return launch_packed_cbm_t<DT_I8>(a, pv, pm, rk, roff, cv, nvals, s);
         case DT_E4M3: return launch_packed_cbm_t<DT_E4M3>(a, pv, pm, rk, roff, cv, nvals, s);
         case DT_E5M2: return launch_packed_cbm_t<DT_E5M2>(a, pv, pm, rk, roff, cv, nvals, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_spmm_packed_cbm_bt(const SpmmArgs& a, const void* pvals, const void* pmeta, const void* rmask,
+                                  const int32_t* roff, const void* cvals, int64_t nvals, hipStream_t s) {
+    const uint8_t* pv = (const uint8_t*)pvals;
+    const uint8_t* pm = (const uint8_t*)pmeta;
+    const uint8_t* rk = (const uint8_t*)rmask;
+    const uint8_t* cv = (const uint8_t*)cvals;
+    switch (a.dt) {
+        case DT_F16: return launch_packed_cbm_t<DT_F16, true>(a, pv, pm, rk, roff, cv, nvals, s);
+        case DT_BF16: return launch_packed_cbm_t<DT_BF16, true>(a, pv, pm, rk, roff, cv, nvals, s);
+        case DT_I8: return launch_packed_cbm_t<DT_I8, true>(a, pv, pm, rk, roff, cv, nvals, s);
+        case DT_E4M3: return launch_packed_cbm_t<DT_E4M3, true>(a, pv, pm, rk, roff, cv, nvals, s);
+        case DT_E5M2: return launch_packed_cbm_t<DT_E5M2, true>(a, pv, pm, rk, roff, cv, nvals, s);
         default: return hipErrorInvalidValue;
     }
 }

@@ -71,6 +71,9 @@ hipError_t launch_pad_b(int dt, int64_t K, int64_t N, const void* B, int64_t ldb
 hipError_t launch_pack_decode(int dt, int64_t M, int64_t K, const void* vals, int64_t ldv, const uint8_t* meta,
                               int64_t ldm, void* pvals, void* pmeta, hipStream_t s);
 hipError_t launch_spmm_packed(const SpmmArgs& a, const void* pvals, const void* pmeta, hipStream_t s);
+// The same product with B given as Bt [N, K] row-major (a.B, a.ldb), N <= 16:
+// each lane loads its B operand straight into registers.
+hipError_t launch_spmm_packed_bt(const SpmmArgs& a, const void* pvals, const void* pmeta, hipStream_t s);
 // Complement-bitmap residual (residual_cbm.hip): blocks and mask bytes of
 // the layout, its encoder from a CSR residual and the 2:4 layer's row-major
 // metadata, and the packed decode product with it fused into every k-step
@@ -80,6 +83,9 @@ hipError_t launch_pack_cbm(int dt, int64_t M, int64_t K, const uint8_t* meta, in
                            const int32_t* col, const void* rvals, int64_t nnz, void* rmask, int32_t* roff,
                            void* cvals, int32_t* bad, hipStream_t s);
 hipError_t launch_spmm_packed_cbm(const SpmmArgs& a, const void* pvals, const void* pmeta, const void* rmask,
+                                  const int32_t* roff, const void* cvals, int64_t nvals, hipStream_t s);
+// The same with B given as Bt [N, K] row-major (a.B, a.ldb), N <= 16.
+hipError_t launch_spmm_packed_cbm_bt(const SpmmArgs& a, const void* pvals, const void* pmeta, const void* rmask,
                                   const int32_t* roff, const void* cvals, int64_t nvals, hipStream_t s);
 // Inclusive scan of a[1..n] in place, a[0] = 0 (one workgroup).
 hipError_t launch_scan_counts(int64_t n, int32_t* a, hipStream_t s);

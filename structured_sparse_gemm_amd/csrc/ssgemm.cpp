@@ -502,6 +502,42 @@ int ssg_spmm_2to4_packed(int ab, int c, int64_t M, int64_t N, int64_t K, const v
     return run_packed(ab, c, M, N, K, pvals, pmeta, nullptr, nullptr, nullptr, nullptr, 0, B, ldb, C, ldc, stream);
 }
 
+namespace {
+
+// Validation shared by the activation-major decode products: Bt [N, K]
+// row-major, 1 <= N <= 16, rows 16-byte multiples apart, 16-byte aligned,
+// 16 rows within 31-bit offsets.
+int check_bt_decode(int ab, int64_t N, int64_t K, const void* Bt, int64_t ldbt, int64_t ldc) {
+    if (N < 1 || N > 16) return fail(SSG_ERR_ALGO, "the activation-major decode product takes 1 <= N <= 16 (got %lld)",
+                                     (long long)N);
+    if (ldbt < K) return fail(SSG_ERR_STRIDE, "ldbt=%lld < K=%lld", (long long)ldbt, (long long)K);
+    if (ldc < N) return fail(SSG_ERR_STRIDE, "ldc=%lld < N=%lld", (long long)ldc, (long long)N);
+    if (!al(Bt, 16) || (ldbt * esize(ab)) % 16 != 0)
+        return fail(SSG_ERR_STRIDE, "Bt must be 16-byte aligned with rows a multiple of 16 bytes apart");
+    if (16 * ldbt * esize(ab) >= 0x7fffffff) return fail(SSG_ERR_SHAPE, "Bt rows too long for 31-bit offsets");
+    return SSG_OK;
+}
+
+}  // namespace
+
+int ssg_spmm_2to4_packed_bt(int ab, int c, int64_t M, int64_t N, int64_t K, const void* pvals, const void* pmeta,
+                            const void* Bt, int64_t ldbt, void* C, int64_t ldc, void* stream) {
+    if (!pair_ok(ab, c)) return fail(SSG_ERR_DTYPE, "unsupported (input, output) types (%d, %d)", ab, c);
+    int64_t vb, mb;
+    int rc = packed_sizes(ab, M, K, &vb, &mb);
+    if (rc) return rc;
+    if (M == 0 || N == 0) return SSG_OK;
+    if (K == 0) return fail(SSG_ERR_SHAPE, "K must be positive");
+    rc = check_bt_decode(ab, N, K, Bt, ldbt, ldc);
+    if (rc) return rc;
+    if (!pvals || !pmeta || !Bt || !C) return fail(SSG_ERR_NULL, "a required pointer is NULL");
+    if (!al(pvals, 16) || !al(pmeta, (uintptr_t)idx_bytes_of(ab)))
+        return fail(SSG_ERR_STRIDE, "pvals must be 16-byte aligned, pmeta aligned to its index words");
+    ssg::SpmmArgs a = make_args(ab, M, N, K, nullptr, 0, nullptr, 0, Bt, ldbt, C, ldc);
+    hipError_t e = ssg::launch_spmm_packed_bt(a, pvals, pmeta, (hipStream_t)stream);
+    return e == hipSuccess ? SSG_OK : hip_fail(e, "packed spmm (Bt) launch");
+}
+
 int ssg_spmm_2to4_packed_residual(int ab, int c, int64_t M, int64_t N, int64_t K, const void* pvals,
                                   const void* pmeta, const int32_t* row_ptr, const int32_t* col, const void* rvals,
                                   int64_t nnz_r, const void* B, int64_t ldb, void* C, int64_t ldc, void* stream) {
@@ -561,19 +597,26 @@ int ssg_pack_residual_cbm(int dt, int64_t M, int64_t K, const uint8_t* meta, int
     return e == hipSuccess ? SSG_OK : hip_fail(e, "complement-bitmap pack launch");
 }
 
-int ssg_spmm_2to4_packed_residual_cbm(int ab, int c, int64_t M, int64_t N, int64_t K, const void* pvals,
-                                      const void* pmeta, const uint8_t* rmask, const int32_t* roff, const void* cvals,
-                                      int64_t nvals, const void* B, int64_t ldb, void* C, int64_t ldc, void* stream) {
+namespace {
+
+int run_packed_cbm(bool bt, int ab, int c, int64_t M, int64_t N, int64_t K, const void* pvals, const void* pmeta,
+                   const uint8_t* rmask, const int32_t* roff, const void* cvals, int64_t nvals, const void* B,
+                   int64_t ldb, void* C, int64_t ldc, void* stream) {
     if (!pair_ok(ab, c)) return fail(SSG_ERR_DTYPE, "unsupported (input, output) types (%d, %d)", ab, c);
     int64_t vb, mb, mbytes, blocks;
     int rc = packed_sizes(ab, M, K, &vb, &mb);
     if (rc) return rc;
     rc = cbm_sizes(ab, M, K, &mbytes, &blocks);
     if (rc) return rc;
-    if (M == 0) return SSG_OK;
-    if (N != 16 || ldb != 16)
+    if (M == 0 || (bt && N == 0)) return SSG_OK;
+    if (bt) {
+        if (K == 0) return fail(SSG_ERR_SHAPE, "K must be positive");
+        rc = check_bt_decode(ab, N, K, B, ldb, ldc);
+        if (rc) return rc;
+    } else if (N != 16 || ldb != 16) {
         return fail(SSG_ERR_ALGO, "the packed product takes N == 16 with ldb == 16 (got N=%lld, ldb=%lld)",
                     (long long)N, (long long)ldb);
+    }
     if (K == 0) return fail(SSG_ERR_SHAPE, "K must be positive");
     if (!pvals || !pmeta || !B || !C || !rmask || !roff) return fail(SSG_ERR_NULL, "a required pointer is NULL");
     if (nvals < 0 || nvals * esize(ab) >= 0x7fff0000) return fail(SSG_ERR_FORMAT, "nvals=%lld out of range", (long long)nvals);
@@ -585,8 +628,24 @@ int ssg_spmm_2to4_packed_residual_cbm(int ab, int c, int64_t M, int64_t N, int64
     if (ldc < N) return fail(SSG_ERR_STRIDE, "ldc=%lld < N=%lld", (long long)ldc, (long long)N);
     if (K * 16 * esize(ab) >= 0x7fffffff) return fail(SSG_ERR_SHAPE, "B too large for 31-bit offsets");
     ssg::SpmmArgs a = make_args(ab, M, N, K, nullptr, 0, nullptr, 0, B, ldb, C, ldc);
-    hipError_t e = ssg::launch_spmm_packed_cbm(a, pvals, pmeta, rmask, roff, cvals, nvals, (hipStream_t)stream);
+    hipError_t e = bt ? ssg::launch_spmm_packed_cbm_bt(a, pvals, pmeta, rmask, roff, cvals, nvals, (hipStream_t)stream)
+                      : ssg::launch_spmm_packed_cbm(a, pvals, pmeta, rmask, roff, cvals, nvals, (hipStream_t)stream);
     return e == hipSuccess ? SSG_OK : hip_fail(e, "packed spmm (complement-bitmap residual) launch");
+}
+
+}  // namespace
+
+int ssg_spmm_2to4_packed_residual_cbm(int ab, int c, int64_t M, int64_t N, int64_t K, const void* pvals,
+                                      const void* pmeta, const uint8_t* rmask, const int32_t* roff, const void* cvals,
+                                      int64_t nvals, const void* B, int64_t ldb, void* C, int64_t ldc, void* stream) {
+    return run_packed_cbm(false, ab, c, M, N, K, pvals, pmeta, rmask, roff, cvals, nvals, B, ldb, C, ldc, stream);
+}
+
+int ssg_spmm_2to4_packed_residual_cbm_bt(int ab, int c, int64_t M, int64_t N, int64_t K, const void* pvals,
+                                         const void* pmeta, const uint8_t* rmask, const int32_t* roff,
+                                         const void* cvals, int64_t nvals, const void* Bt, int64_t ldbt, void* C,
+                                         int64_t ldc, void* stream) {
+    return run_packed_cbm(true, ab, c, M, N, K, pvals, pmeta, rmask, roff, cvals, nvals, Bt, ldbt, C, ldc, stream);
 }
 
 namespace {

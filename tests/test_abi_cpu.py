@@ -333,3 +333,18 @@ def test_prefill_bt_argument_errors(lib):
     assert f(BF16, F32, 64, 16, 128, FAKE, FAKE, FAKE, 132, FAKE, 16, None) == _abi.SSG_ERR_ALGO
     assert f(BF16, F32, 64, 16, 128, FAKE, FAKE, ctypes.c_void_p(0x1008), 128, FAKE, 16, None) == _abi.SSG_ERR_ALGO
     assert f(BF16, F32, 64, 0, 128, None, None, None, 128, None, 0, None) == 0                       # N = 0
+
+
+def test_decode_bt_argument_errors(lib):
+    f = lib.ssg_spmm_2to4_packed_bt
+    g = lib.ssg_spmm_2to4_packed_residual_cbm_bt
+    assert f(F16, F32, 32, 17, 128, FAKE, FAKE, FAKE, 128, FAKE, 17, None) == _abi.SSG_ERR_ALGO     # N > 16
+    assert f(F16, F32, 32, 8, 128, FAKE, FAKE, FAKE, 100, FAKE, 8, None) == _abi.SSG_ERR_STRIDE     # ldbt < K
+    assert f(F16, F32, 32, 8, 128, FAKE, FAKE, FAKE, 132, FAKE, 8, None) == _abi.SSG_ERR_STRIDE     # rows 264 B apart
+    assert f(F16, F32, 32, 8, 128, FAKE, FAKE, ctypes.c_void_p(0x1008), 128, FAKE, 8, None) == _abi.SSG_ERR_STRIDE
+    assert f(F16, F32, 32, 8, 96, FAKE, FAKE, FAKE, 128, FAKE, 8, None) == _abi.SSG_ERR_SHAPE       # K % 64
+    assert f(F16, F32, 32, 8, 128, FAKE, FAKE, None, 128, FAKE, 8, None) == _abi.SSG_ERR_NULL
+    assert f(F16, F32, 32, 0, 128, None, None, None, 128, None, 0, None) == 0                       # N = 0
+    assert g(F16, F32, 32, 17, 128, FAKE, FAKE, FAKE, FAKE, FAKE, 4, FAKE, 128, FAKE, 17, None) == _abi.SSG_ERR_ALGO
+    assert g(F16, F32, 32, 8, 128, FAKE, FAKE, FAKE, FAKE, FAKE, 4, FAKE, 100, FAKE, 8, None) == _abi.SSG_ERR_STRIDE
+    assert g(F16, F32, 32, 8, 128, FAKE, FAKE, None, FAKE, FAKE, 4, FAKE, 128, FAKE, 8, None) == _abi.SSG_ERR_NULL
