@@ -72,18 +72,22 @@ PROFILED = [
     ("k_spmm_pipe<2, false, false>", "c2", "spmm_large_n", "int8 4096^3 SpMM, row-major operand"),
     (re.compile(r"k_spmm_small_n_ring<0, \d+, \d+, false, false>"), "c3", "spmm_small_n",
      "fp16 11008x4096x16 SpMM, row-major operand"),
-    (re.compile(r"k_spmm_packed<0, \d+, \d+, false, false>"), "c3_packed", "spmm_small_n",
+    (re.compile(r"k_spmm_packed<0, \d+, \d+, false, false, false>"), "c3_packed", "spmm_small_n",
      "fp16 11008x4096x16 SpMM, packed decode layout"),
+    (re.compile(r"k_spmm_packed<0, \d+, \d+, false, false, true>"), "c3_packed_bt", "spmm_small_n",
+     "fp16 11008x4096x16 SpMM, packed decode layout, B activation-major"),
     (re.compile(r"k_spmm_small_n_ring<0, \d+, \d+, true, false>"), "c5", "spmm_small_n",
      "fp16 8192x8192x16 2:4 + CSR residual, row-major operand"),
     (re.compile(r"k_spmm_small_n_ring<0, \d+, \d+, true, true>"), "c5_delta", "spmm_small_n",
      "fp16 8192x8192x16 2:4 + delta-coded residual, row-major operand"),
-    (re.compile(r"k_spmm_packed<0, \d+, \d+, true, false>"), "c5_packed", "spmm_small_n",
+    (re.compile(r"k_spmm_packed<0, \d+, \d+, true, false, false>"), "c5_packed", "spmm_small_n",
      "fp16 8192x8192x16 2:4 + CSR residual, packed decode layout"),
-    (re.compile(r"k_spmm_packed<0, \d+, \d+, true, true>"), "c5_delta_packed", "spmm_small_n",
+    (re.compile(r"k_spmm_packed<0, \d+, \d+, true, true, false>"), "c5_delta_packed", "spmm_small_n",
      "fp16 8192x8192x16 2:4 + delta-coded residual, packed decode layout"),
-    (re.compile(r"k_spmm_packed_cbm<0, \d+, \d+>"), "c5_cbm_packed", "spmm_small_n",
+    (re.compile(r"k_spmm_packed_cbm<0, \d+, \d+, false>"), "c5_cbm_packed", "spmm_small_n",
      "fp16 8192x8192x16 2:4 + complement-bitmap residual fused, packed decode layout"),
+    (re.compile(r"k_spmm_packed_cbm<0, \d+, \d+, true>"), "c5_cbm_packed_bt", "spmm_small_n",
+     "fp16 8192x8192x16 2:4 + complement-bitmap residual fused, packed decode layout, B activation-major"),
 ]
 
 
