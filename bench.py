@@ -2,6 +2,7 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]
     python bench.py --mfma-rates      # sparse vs dense matrix-core issue rates
+    python bench.py --lds-patterns    # LDS read rates of per-lane address patterns
 
 Headline workload: the largest configuration, the bf16 prefill-shape 2:4
 SpMM M=28672 K=8192 N=2048 (A ~ N(0, 0.02^2) magnitude-pruned 2:4 along K,
@@ -234,6 +235,60 @@ def mfma_rates() -> dict:
     return {ssg.ssg_mfma_probe_name(f): {"dense_equiv_rate_1_wave_per_simd": mfma_rate(f, 1),
                                          "dense_equiv_rate_2_waves_per_simd": mfma_rate(f, 2)}
             for f in range(ssg.ssg_mfma_probe_forms())}
+
+
+def lds_patterns() -> list:
+    """Per-lane address patterns of one 16-byte LDS read (64 byte offsets,
+    one per lane): the contiguous read, pairs of lanes k apart on one bank
+    at different addresses, and the reads of the large-N kernel's LDS images
+    (two row images of the sparse values, the lane-ordered one the packed
+    prefill layout gives, and the activation-major B tile with and without
+    its swizzle)."""
+    def swz_rows(r):
+        return ((r >> 1) ^ (r >> 3)) & 3
+
+    pats = [("contiguous (lane l at 16 l)", [16 * l for l in range(64)])]
+    for k in (1, 2, 4, 8, 16, 32):
+        pats.append(("lanes l and l+%d on one bank, 1 KiB apart" % k,
+                     [16 * (l - k) + 1024 if l & k else 16 * l for l in range(64)]))
+    pats.append(("sparse values, rows of 64 B, chunks swizzled by ((r/2)^(r/8))%4",
+                 [(l & 31) * 64 + (((l >> 5) ^ swz_rows(l & 31)) << 4) for l in range(64)]))
+    pats.append(("the same, lanes 0-15 only (the rest contiguous, 8 KiB on)",
+                 [(l & 31) * 64 + (((l >> 5) ^ swz_rows(l & 31)) << 4) if l < 16 else 8192 + 16 * l
+                  for l in range(64)]))
+    pats.append(("sparse values, rows of 64 B, unswizzled", [(l & 31) * 64 + ((l >> 5) << 4) for l in range(64)]))
+    pats.append(("sparse values, packed prefill layout (lane order)", [16 * l for l in range(64)]))
+    pats.append(("activation-major B, rows of 128 B, chunks swizzled by (n/2)%8",
+                 [(l & 31) * 128 + (((l >> 5) ^ ((l & 31) >> 1 & 7)) << 4) for l in range(64)]))
+    pats.append(("activation-major B, rows of 128 B, unswizzled", [(l & 31) * 128 + ((l >> 5) << 4) for l in range(64)]))
+    pats.append(("the 16 lanes of each group on one bank, 256 B apart", [256 * (l & 15) for l in range(64)]))
+    return pats
+
+
+def lds_read_rates(iters: int = 2000, reps: int = 3) -> list:
+    """ns per 16-byte read instruction per CU for each pattern of
+    lds_patterns(), at one and two workgroups of four waves per CU, best of
+    `reps` launches timed with HIP events on the current stream."""
+    import torch
+
+    import structured_sparse_gemm_amd as ssg
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    stream = torch.cuda.current_stream()
+    sink = torch.zeros(2 * cus, dtype=torch.int32, device="cuda")
+    pats = lds_patterns()
+    for _ in range(3):                                           # clocks up before the first timing
+        ssg.ssg_lds_read_probe(pats[0][1], 2 * cus, iters, sink)
+    out = []
+    for name, offs in pats:
+        row = {"pattern": name}
+        for per_cu in (1, 2):
+            wg = per_cu * cus
+            ssg.ssg_lds_read_probe(offs, wg, 10, sink)             # warm-up
+            best = min(time_kernel(lambda i: ssg.ssg_lds_read_probe(offs, wg, iters, sink), 1, stream)
+                       for _ in range(reps))
+            row["ns_per_read_per_cu_%d_waves" % (4 * per_cu)] = best * 1e9 / (per_cu * 4 * 8 * iters)
+        out.append(row)
+    return out
 
 
 def bench_workload(key: str, iters: int, delta: bool = False, dense_cmp: bool = True,
@@ -491,6 +546,8 @@ def main() -> int:
                    help="first run a plain elementwise copy of 256 MiB (read 256 MiB, write 256 MiB) three times, "
                         "outside the timed region: the reference for scaling HBM byte counters")
     p.add_argument("--only", default="", help="comma-separated workload keys of the table (default: all)")
+    p.add_argument("--lds-patterns", action="store_true",
+                   help="print the LDS read rate of each per-lane address pattern and exit")
     p.add_argument("--mfma-rates", action="store_true",
                    help="instead of the benchmark, print the issue rates of the sparse and dense matrix-core "
                         "instruction forms (the library's probe) as JSON")
@@ -516,6 +573,11 @@ def main() -> int:
 
     if args.mfma_rates:
         print(json.dumps({"unit": "dense-equivalent TFLOP/s (TOPS for int8)", "forms": mfma_rates(),
+                          "device": torch.cuda.get_device_name(0)}))
+        return 0
+
+    if args.lds_patterns:
+        print(json.dumps({"unit": "ns per 16-byte read instruction per CU", "patterns": lds_read_rates(),
                           "device": torch.cuda.get_device_name(0)}))
         return 0
 

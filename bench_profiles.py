@@ -5,6 +5,7 @@
     python bench_profiles.py sq      DIR             # DIR/run_counter_collection.csv
     python bench_profiles.py rates   FILE            # the JSON of bench.py --mfma-rates
     python bench_profiles.py crossover FILE          # the JSON of bench.py --crossover
+    python bench_profiles.py lds     FILE            # the JSON of bench.py --lds-patterns
 
 `trace` turns the --kernel-trace --stats summary of a bench run into
 profiles/bench_kernel_trace.md.  `traffic` takes the two counter passes
@@ -15,7 +16,9 @@ writes profiles/traffic.json (read by bench.py for `roofline.traffic`) and
 profiles/hbm_counters.md.  `sq` writes the LDS and matrix-core counter table
 profiles/lds_mfma_counters.md.  `rates` writes the sparse vs dense
 matrix-core issue rates to profiles/mfma_rates_sparse_vs_dense.md, and
-`crossover` the density study to profiles/crossover_fp16_8192x8192x16.md.
+`crossover` the density study to profiles/crossover_fp16_8192x8192x16.md,
+and `lds` the LDS read rates of per-lane address patterns to
+profiles/lds_read_patterns.md.
 Each summary names the command that made it;
 COMMANDS below are those commands, run from the repository root of a GPU
 machine with R set to that root.
@@ -49,6 +52,7 @@ COMMANDS = {
           "--only c2,c3,c5 --workload-iters 10",
     "rates": "mkdir -p $R/gpurun_out && timeout -k 10 120 python3 $R/bench.py --mfma-rates > $R/gpurun_out/mfma_rates.json",
     "crossover": "mkdir -p $R/gpurun_out && timeout -k 10 600 python3 $R/bench.py --crossover > $R/gpurun_out/crossover.json",
+    "lds": "mkdir -p $R/gpurun_out && timeout -k 10 120 python3 $R/bench.py --lds-patterns > $R/gpurun_out/lds_patterns.json",
 }
 
 HEADLINE = "k_spmm_pipe<1, true, true>"     # the headline step's product
@@ -301,6 +305,21 @@ def crossover(path: str) -> None:
         f.write("".join(out))
 
 
+def lds(path: str) -> None:
+    with open(path) as f:
+        d = json.loads(f.read())
+    out = [header("LDS read rates of per-lane address patterns (the library's probe)", [COMMANDS["lds"]]),
+           "One 16-byte read (ds_read_b128) per lane at the pattern's offset, eight reads 4 KiB apart in flight "
+           "per wave, every value consumed; ns per read instruction per CU, best of three launches, at one and two "
+           "workgroups of four waves per CU.  A read of 64 lanes moves 1 KiB.  Device: %s.\n\n" % d.get("device", "?"),
+           "| pattern | 4 waves per CU | 8 waves per CU |\n|---|---|---|\n"]
+    for r in d["patterns"]:
+        out.append("| %s | %.2f | %.2f |\n" % (r["pattern"], r["ns_per_read_per_cu_4_waves"],
+                                              r["ns_per_read_per_cu_8_waves"]))
+    with open(os.path.join(PROFILES, "lds_read_patterns.md"), "w") as f:
+        f.write("".join(out))
+
+
 def main(argv) -> int:
     if len(argv) >= 2 and argv[0] == "trace":
         trace(argv[1])
@@ -312,6 +331,8 @@ def main(argv) -> int:
         rates(argv[1])
     elif len(argv) >= 2 and argv[0] == "crossover":
         crossover(argv[1])
+    elif len(argv) >= 2 and argv[0] == "lds":
+        lds(argv[1])
     else:
         print(__doc__, file=sys.stderr)
         return 2

@@ -296,10 +296,11 @@ int ssg_spmm_2to4_packed_residual_delta(int ab, int c, int64_t M, int64_t N, int
  * sparse matrix rate pays only if the operands keep up).  Rows are grouped in tiles of 256; a stage is
  * 64 stored-value bytes of a row (64 dense k for fp16/bf16, 128 for the
  * 8-bit types); a metadata block is 32 metadata bytes of a row (256 dense k).
- *   pvals: tile t, stage s -> 16 KiB block (t * stages + s); row r of the tile
- *          at byte r * 64 of it, its 16-byte chunk c (stored-value bytes
- *          [64 s + 16 c, +16) of the row) at chunk position
- *          c ^ (((r >> 1) ^ (r >> 3)) & 3).
+ *   pvals: tile t, stage s -> 16 KiB block (t * stages + s) of 1024
+ *          16-byte lane chunks.  The 16-byte chunk c < 4 of row
+ *          r = 32 rt + rl of the tile (stored-value bytes [64 s + 16 c, +16)
+ *          of the row; rt < 8, rl < 32) sits at chunk
+ *          (2 rt + c / 2) * 64 + 32 (c % 2) + rl.
  *   pmeta: tile t, block g -> 8 KiB block (t * mblocks + g) of 512
  *          16-byte lane chunks.  With IW = 2 (fp16/bf16) or 4 (8-bit types)
  *          and KPC = 4 / IW, metadata byte 32 g + j of row r of the tile
@@ -563,6 +564,21 @@ int ssg_mfma_probe_forms(void);
 const char* ssg_mfma_probe_name(int form);
 int64_t ssg_mfma_probe_ops(int form, int64_t workgroups, int64_t iters);
 int ssg_mfma_probe(int form, int64_t workgroups, int64_t iters, uint32_t* sink, void* stream);
+
+/* Measurement helper (not part of the product): the rate of 16-byte LDS
+ * reads (ds_read_b128) for one pattern of per-lane addresses, the measure
+ * behind the LDS images of the large-N kernel, whose operand reads must
+ * keep up with the sparse matrix unit ("Chapter 26 -- Sparsity: The
+ * Hardware View", section "2:4: ~2x on the Matmul, Less End-to-End").
+ * offsets: host array of 64 byte offsets, each a multiple of 16 and at most
+ * 65536 - 7 * 4096 - 16 = 36848.  One launch is `workgroups` workgroups of
+ * four 64-lane waves, each with 64 KiB of LDS; lane l of every wave reads
+ * the 16 bytes at offsets[l] + 4096 j for j < 8, `iters` times (8 * iters
+ * reads per wave).  sink is device memory of `workgroups` uint32 words,
+ * written only when a workgroup's fold of the data hits one fixed value.
+ * Errors: SSG_ERR_NULL for no offsets or sink, SSG_ERR_SHAPE for
+ * non-positive counts or an offset that is misaligned or too large. */
+int ssg_lds_read_probe(const uint32_t* offsets, int64_t workgroups, int64_t iters, uint32_t* sink, void* stream);
 
 #ifdef __cplusplus
 }

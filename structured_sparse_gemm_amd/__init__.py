@@ -13,6 +13,7 @@ allocate their outputs.
 """
 from __future__ import annotations
 
+import ctypes
 from typing import Optional, Tuple
 
 import torch
@@ -38,7 +39,10 @@ __all__ = [
     "ssg_noalloc_scratch_bytes", "ssg_spmm_2to4_noalloc",
     "ssg_cbm_sizes", "ssg_pack_residual_cbm", "ssg_spmm_2to4_packed_residual_cbm", "pack_residual_cbm",
     "spmm_packed_residual_cbm",
+    "ssg_spmm_2to4_prefill_bt", "spmm_prefill_bt", "ssg_spmm_2to4_packed_bt", "spmm_packed_bt",
+    "ssg_spmm_2to4_packed_residual_cbm_bt", "spmm_packed_residual_cbm_bt",
     "ssg_stream_read_sink_words", "ssg_stream_read",
+    "ssg_mfma_probe_forms", "ssg_mfma_probe_name", "ssg_mfma_probe_ops", "ssg_mfma_probe", "ssg_lds_read_probe",
     "SSG_ALGO_AUTO", "SSG_ALGO_GENERIC", "SSG_ALGO_SMALL_N", "SSG_ALGO_LARGE_N", "library_path",
 ]
 
@@ -424,6 +428,19 @@ def ssg_mfma_probe(form: int, workgroups: int, iters: int, sink: torch.Tensor, s
         raise ValueError("sink holds fewer than %d words" % workgroups)
     _check(_lib().ssg_mfma_probe(form, workgroups, iters, _ptr(sink, "sink"), _stream(sink, stream)),
            "ssg_mfma_probe")
+
+
+def ssg_lds_read_probe(offsets, workgroups: int, iters: int, sink: torch.Tensor, stream=None) -> None:
+    """Measurement helper: one launch of the LDS read probe (offsets: 64 byte
+    offsets, one per lane; sink: at least `workgroups` int32 words on the
+    device)."""
+    offs = (ctypes.c_uint32 * 64)(*[int(o) for o in offsets]) if len(offsets) == 64 else None
+    if offs is None:
+        raise ValueError("offsets must hold 64 entries, one per lane")
+    if sink.numel() * sink.element_size() < 4 * workgroups:
+        raise ValueError("sink holds fewer than %d words" % workgroups)
+    _check(_lib().ssg_lds_read_probe(ctypes.cast(offs, ctypes.c_void_p), workgroups, iters, _ptr(sink, "sink"),
+                                     _stream(sink, stream)), "ssg_lds_read_probe")
 
 
 def ssg_compress_nm(A: torch.Tensor, n: int, m: int, vals: torch.Tensor, mask: torch.Tensor, stream=None) -> None:

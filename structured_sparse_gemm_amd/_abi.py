@@ -82,6 +82,7 @@ SIGNATURES = {
     "ssg_mfma_probe_name": (ctypes.c_char_p, [_i]),
     "ssg_mfma_probe_ops": (_i64, [_i, _i64, _i64]),
     "ssg_mfma_probe": (_i, [_i, _i64, _i64, _vp, _vp]),
+    "ssg_lds_read_probe": (_i, [_vp, _i64, _i64, _vp, _vp]),
     "ssg_spmm_select_algo": (_i, [_i, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64]),
 }
 

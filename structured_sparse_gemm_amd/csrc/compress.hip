@@ -219,7 +219,7 @@ __global__ void __launch_bounds__(kPrefillThreads) k_compress_prefill(int64_t M,
 #pragma unroll
         for (int j = 0; j < ES; ++j) {
             const int piece = (c % CPS) * ES + j;
-            *reinterpret_cast<uint4*>(lds + st * 16384 + r * 64 + ((piece ^ prefill_swz(r)) << 4)) = w[j];
+            *reinterpret_cast<uint4*>(lds + st * 16384 + (prefill_vals_unit(r, piece) << 4)) = w[j];
         }
         // its 4 metadata bytes (block bytes [4 c, 4 c + 4) of the row): one
         // index word for 8-bit types, two for 16-bit ones, each whole at its

@@ -17,6 +17,11 @@
 // [2^-63, 2), int8 bytes uniform, fp8 bytes uniform over the finite
 // E4M3 values of magnitude at most 240, valid 2:4 index nibbles), so
 // the instruction stream is nothing but that form.
+//
+// The rate of 16-byte LDS reads (ds_read_b128) for one pattern of per-lane
+// addresses, the measure behind the LDS images of the large-N kernel.
+// Every wave repeats eight reads of its lanes' addresses, 4 KiB apart, and
+// folds the data into a word as the other probes do.
 #include <algorithm>
 
 #include "ssg_device.hpp"
@@ -224,6 +229,45 @@ const char* mfma_probe_name(int form) { return form >= 0 && form < kNumForms ? k
 int64_t mfma_probe_ops(int form, int64_t workgroups, int64_t iters) {
     if (form < 0 || form >= kNumForms || workgroups <= 0 || iters <= 0) return 0;
     return kForms[form].ops * kForms[form].nacc * iters * workgroups * (kMfmaThreads / 64);
+}
+
+constexpr int kLdsProbeThreads = 256;
+typedef __attribute__((address_space(3))) const void lds_cvoid;
+
+__global__ void __launch_bounds__(kLdsProbeThreads) k_lds_read(LdsPattern pat, int64_t iters, uint32_t* sink) {
+    __shared__ __attribute__((aligned(1024))) i32x4 buf[4096];     // 64 KiB
+    for (int i = threadIdx.x; i < 4096; i += kLdsProbeThreads) buf[i] = i32x4{i, 3 * i, i ^ 0x55, i + 7};
+    __syncthreads();
+    const int lane = threadIdx.x & 63;
+    const uint32_t addr = (uint32_t)(uintptr_t)(lds_cvoid*)buf + pat.off[lane];
+    i32x4 x = {0, 0, 0, 0};
+    for (int64_t it = 0; it < iters; ++it) {
+        // eight reads in flight, then one wait, in one statement: no output
+        // register is reused while its read is outstanding
+        i32x4 r0, r1, r2, r3, r4, r5, r6, r7;
+        asm volatile(
+            "ds_read_b128 %0, %8 offset:0\n\t"
+            "ds_read_b128 %1, %8 offset:4096\n\t"
+            "ds_read_b128 %2, %8 offset:8192\n\t"
+            "ds_read_b128 %3, %8 offset:12288\n\t"
+            "ds_read_b128 %4, %8 offset:16384\n\t"
+            "ds_read_b128 %5, %8 offset:20480\n\t"
+            "ds_read_b128 %6, %8 offset:24576\n\t"
+            "ds_read_b128 %7, %8 offset:28672\n\t"
+            "s_waitcnt lgkmcnt(0)"
+            : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3), "=&v"(r4), "=&v"(r5), "=&v"(r6), "=&v"(r7)
+            : "v"(addr)
+            : "memory");
+        x ^= r0 ^ r1 ^ r2 ^ r3 ^ r4 ^ r5 ^ r6 ^ r7;
+    }
+    const uint32_t f = (uint32_t)(x.x ^ x.y ^ x.z ^ x.w);
+    if (f == 0x9E3779B9u) sink[blockIdx.x] = f;
+}
+
+hipError_t launch_lds_read_probe(const LdsPattern& pat, int64_t workgroups, int64_t iters, uint32_t* sink,
+                                 hipStream_t s) {
+    hipLaunchKernelGGL(k_lds_read, dim3((unsigned)workgroups), dim3(kLdsProbeThreads), 0, s, pat, iters, sink);
+    return hipGetLastError();
 }
 
 hipError_t launch_mfma_probe(int form, int64_t workgroups, int64_t iters, uint32_t* sink, hipStream_t s) {

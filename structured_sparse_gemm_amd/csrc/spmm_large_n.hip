@@ -106,12 +106,12 @@ struct Lay {
     static_assert(B_LOADS % NJ == 0 && B_LOADS >= 1, "B loads per wave per stage");
 };
 
-// 16-byte chunk c of row r of the sparse-value tile sits at chunk
-// c ^ swz_a(r) of the row's 64 bytes: the 8 or 16 lanes that a
-// ds_read_b128 serves together (consecutive rows, one chunk) then land on
-// distinct 16-byte bank groups.
-// (the packed prefill layout stores its blocks in this same order)
-__device__ __forceinline__ int swz_a(int r) { return prefill_swz(r); }
+// Row-major operand: 16-byte chunk c of row r of the sparse-value tile sits
+// at chunk c ^ swz_a(r) of the row's 64 bytes, so the 16 consecutive rows
+// that a ds_read_b128 serves together fall on distinct 16-byte bank
+// windows.  (The packed prefill operand instead arrives in the lane order
+// of the reads, prefill_vals_unit, and each read is lane-contiguous.)
+__device__ __forceinline__ int swz_a(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
 
 template <int DT, int BN = kBN> __device__ __forceinline__ int swz(int r) {
     // a permutation of the row's 16-byte chunks (8-bit rows of 128 columns
@@ -404,8 +404,11 @@ __device__ __forceinline__ void spmm_tile(const SpmmArgs& a, int tm, int tn, uin
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int row = 32 * (wm * 4 + i) + rl;
-            o.av[i] = *reinterpret_cast<const uint4*>(st + L::B_BYTES + row * L::A_ROWB +
-                                                      (((2 * s + q) ^ swz_a(row)) << 4));
+            if constexpr (PK)
+                o.av[i] = *reinterpret_cast<const uint4*>(st + L::B_BYTES + (((wm * 4 + i) * 2 + s) << 10) + lane * 16);
+            else
+                o.av[i] = *reinterpret_cast<const uint4*>(st + L::B_BYTES + row * L::A_ROWB +
+                                                          (((2 * s + q) ^ swz_a(row)) << 4));
         }
 #pragma unroll
         for (int j = 0; j < NJ; ++j) {
@@ -523,8 +526,7 @@ __device__ __forceinline__ void spmm_tile(const SpmmArgs& a, int tm, int tn, uin
             constexpr int BPJ = L::B_LOADS / NJ;        // B loads placed after each column tile's reads
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int row = 32 * (wm * 4 + i) + rl;
-                o0.av[i] = *reinterpret_cast<const uint4*>(nx + L::B_BYTES + row * L::A_ROWB + ((q ^ swz_a(row)) << 4));
+                o0.av[i] = *reinterpret_cast<const uint4*>(nx + L::B_BYTES + ((wm * 4 + i) << 11) + lane * 16);
                 dma<16>(ra, dst + L::B_BYTES + (wave * L::A_LOADS + i) * 1024, x.aoff[i]);
             }
 #pragma unroll
@@ -647,12 +649,13 @@ __global__ void __launch_bounds__(256) k_pack_prefill(int64_t M, int64_t K, cons
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < vchunks + mwords; i += stride) {
         if (i < vchunks) {
-            // chunk position p of row r in block (t, s)
+            // 16-byte unit u of block (t, s): chunk c of the stage's bytes of row r
             const int64_t blk = i >> 10, t = blk / stages, st = blk - t * stages;
-            const int r = (int)((i >> 2) & 255), p = (int)(i & 3);
+            int r, c;
+            prefill_vals_unit_inv((int)(i & 1023), &r, &c);
             const int64_t m = t * 256 + r;
             uint4 w = make_uint4(0, 0, 0, 0);
-            if (m < M) w = *reinterpret_cast<const uint4*>(vals + m * ldv_bytes + st * 64 + ((p ^ prefill_swz(r)) << 4));
+            if (m < M) w = *reinterpret_cast<const uint4*>(vals + m * ldv_bytes + st * 64 + (c << 4));
             *reinterpret_cast<uint4*>(pvals + (i << 4)) = w;
         } else {
             const int64_t k = i - vchunks;     // 4-byte word k of pmeta

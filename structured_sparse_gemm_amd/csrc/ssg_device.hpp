@@ -63,8 +63,12 @@ __device__ __forceinline__ bool nibble_valid(uint32_t nib) { return (nib & 3u) <
 // it is the same for every element type: a stage is 64 stored-value bytes of
 // every row (64 dense k for fp16/bf16, 128 for 8-bit types) and a metadata
 // block 32 metadata bytes of every row (256 dense k).
-// * pvals: tile t, stage s -> 16 KiB block (t * stages + s); row r of the tile
-//   at r * 64 in it, its 16-byte chunk c at chunk position c ^ prefill_swz(r).
+// * pvals: tile t, stage s -> 16 KiB block (t * stages + s) of 16-byte lane
+//   chunks in the order of the kernel's sparse-operand reads: 1 KiB piece
+//   (32-row group rt, MFMA k-step s2 of the stage) holds, at lane
+//   position 32 q + rl, 16-byte chunk 2 s2 + q of the stage's 64 bytes of
+//   row 32 rt + rl (prefill_vals_unit).  One lane-contiguous 16-byte read
+//   then gives every lane of a wave its sparse operand.
 // * pmeta: tile t, block g -> 8 KiB block (t * mblocks + g) of 16-byte lane
 //   chunks, one per (MFMA k-step group, 128-row half, lane) of the kernel:
 //   chunk u = (hq * 2 + wm) * 64 + 32 q + rl holds the index words of rows
@@ -77,12 +81,14 @@ __device__ __forceinline__ bool nibble_valid(uint32_t nib) { return (nib & 3u) <
 //   k-steps.
 // Rows past M and metadata bytes past K / 8 hold zeros.
 // ---------------------------------------------------------------------------
-__host__ __device__ __forceinline__ int prefill_swz(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
-
-// Offset in pvals of stored-value byte b of row m.
-__host__ __device__ __forceinline__ int64_t prefill_vals_offset(int64_t m, int64_t b, int64_t stages) {
-    const int r = (int)(m & 255);
-    return (((m >> 8) * stages + (b >> 6)) << 14) + r * 64 + ((((int)(b >> 4) & 3) ^ prefill_swz(r)) << 4) + (b & 15);
+// 16-byte unit of a pvals stage block that holds chunk c (0..3) of the
+// stage's 64 bytes of tile row r (0..255), and the inverse.
+__host__ __device__ __forceinline__ int prefill_vals_unit(int r, int c) {
+    return ((((r >> 5) << 1) + (c >> 1)) << 6) + ((c & 1) << 5) + (r & 31);
+}
+__host__ __device__ __forceinline__ void prefill_vals_unit_inv(int u, int* r, int* c) {
+    *r = ((u >> 7) << 5) + (u & 31);
+    *c = (((u >> 6) & 1) << 1) + ((u >> 5) & 1);
 }
 
 // Position in its 8 KiB metadata block of byte j (0..31) of row r (0..255)

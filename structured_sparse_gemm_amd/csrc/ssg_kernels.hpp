@@ -140,4 +140,14 @@ const char* mfma_probe_name(int form);
 int64_t mfma_probe_ops(int form, int64_t workgroups, int64_t iters);
 hipError_t launch_mfma_probe(int form, int64_t workgroups, int64_t iters, uint32_t* sink, hipStream_t s);
 
+// The LDS read probe: lane l of every wave reads 16 bytes at LDS byte
+// off[l] + 4096 j, j < 8 (off[l] a multiple of 16, at most
+// kLdsProbeMaxOffset), `iters` times; 4 waves per workgroup.
+constexpr uint32_t kLdsProbeMaxOffset = 65536 - 7 * 4096 - 16;
+struct LdsPattern {
+    uint32_t off[64];
+};
+hipError_t launch_lds_read_probe(const LdsPattern& pat, int64_t workgroups, int64_t iters, uint32_t* sink,
+                                 hipStream_t s);
+
 }  // namespace ssg

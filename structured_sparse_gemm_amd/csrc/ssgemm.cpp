@@ -784,6 +784,22 @@ int ssg_mfma_probe(int form, int64_t workgroups, int64_t iters, uint32_t* sink, 
     return e == hipSuccess ? SSG_OK : hip_fail(e, "matrix-instruction probe launch");
 }
 
+int ssg_lds_read_probe(const uint32_t* offsets, int64_t workgroups, int64_t iters, uint32_t* sink, void* stream) {
+    if (!offsets || !sink) return fail(SSG_ERR_NULL, "offsets or sink is NULL");
+    ssg::LdsPattern pat;
+    for (int l = 0; l < 64; ++l) {
+        if (offsets[l] % 16 || offsets[l] > ssg::kLdsProbeMaxOffset)
+            return fail(SSG_ERR_SHAPE, "offsets[%d]=%u is not a multiple of 16 in [0, %u]", l, offsets[l],
+                        ssg::kLdsProbeMaxOffset);
+        pat.off[l] = offsets[l];
+    }
+    if (workgroups <= 0 || workgroups > 0x7fffffff || iters <= 0)
+        return fail(SSG_ERR_SHAPE, "workgroups=%lld and iters=%lld must be positive (workgroups below 2^31)",
+                    (long long)workgroups, (long long)iters);
+    hipError_t e = ssg::launch_lds_read_probe(pat, workgroups, iters, sink, (hipStream_t)stream);
+    return e == hipSuccess ? SSG_OK : hip_fail(e, "LDS read probe launch");
+}
+
 int64_t ssg_nm_vals_cols(int nm_n, int nm_m, int64_t K) {
     return nm_m > 0 && nm_n >= 0 ? K / nm_m * nm_n : 0;
 }

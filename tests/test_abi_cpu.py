@@ -322,6 +322,23 @@ def test_mfma_probe_description_and_argument_errors(lib):
     assert lib.ssg_mfma_probe(0, 1, 1, None, None) == _abi.SSG_ERR_NULL
 
 
+def test_lds_read_probe_argument_errors(lib):
+    good = (ctypes.c_uint32 * 64)(*[16 * l for l in range(64)])
+    bad_align = (ctypes.c_uint32 * 64)(*([16 * l for l in range(63)] + [8]))
+    too_far = (ctypes.c_uint32 * 64)(*([16 * l for l in range(63)] + [65536 - 7 * 4096]))
+    last_ok = (ctypes.c_uint32 * 64)(*([16 * l for l in range(63)] + [65536 - 7 * 4096 - 16]))
+    f = lib.ssg_lds_read_probe
+    cast = lambda a: ctypes.cast(a, ctypes.c_void_p)
+    assert f(None, 1, 1, FAKE, None) == _abi.SSG_ERR_NULL
+    assert f(cast(good), 1, 1, None, None) == _abi.SSG_ERR_NULL
+    assert f(cast(good), 0, 1, FAKE, None) == _abi.SSG_ERR_SHAPE
+    assert f(cast(good), 1, 0, FAKE, None) == _abi.SSG_ERR_SHAPE
+    assert f(cast(bad_align), 1, 1, FAKE, None) == _abi.SSG_ERR_SHAPE
+    assert f(cast(too_far), 1, 1, FAKE, None) == _abi.SSG_ERR_SHAPE
+    assert f(cast(last_ok), 0, 1, FAKE, None) == _abi.SSG_ERR_SHAPE      # only the count is wrong
+    assert b"workgroups" in lib.ssg_last_error()
+
+
 def test_prefill_bt_argument_errors(lib):
     f = lib.ssg_spmm_2to4_prefill_bt
     assert f(BF16, F32, 64, 16, 128, FAKE, FAKE, FAKE, 100, FAKE, 16, None) == _abi.SSG_ERR_STRIDE   # ldbt < K

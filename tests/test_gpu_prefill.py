@@ -31,10 +31,6 @@ def device():
     return torch.device("cuda:0")
 
 
-def swz(r):
-    return ((r >> 1) ^ (r >> 3)) & 3
-
-
 def expected_prefill(dt, vals_bits, meta, M, K):
     """The packed prefill layout written out from its definition."""
     es = 2 if dt in ("f16", "bf16") else 1
@@ -43,18 +39,16 @@ def expected_prefill(dt, vals_bits, meta, M, K):
     vb[:M] = np.ascontiguousarray(vals_bits).view(np.uint8).reshape(M, -1)
     mb = np.zeros((tiles * 256, mblocks * 32), np.uint8)
     mb[:M, :K // 8] = meta[:, :K // 8]
-    src = vb.reshape(tiles, 256, stages, 4, 16)
-    pv = np.zeros((tiles, stages, 256, 4, 16), np.uint8)
-    for r in range(256):
-        for c in range(4):
-            pv[:, :, r, c ^ swz(r)] = src[:, r, :, c]
+    # values in lane order: row r = 32 rt + rl of the tile, stage st, chunk
+    # c = 2 s2 + q of the stage's 64 bytes; order [tile][stage][rt][s2][q][rl]
+    pv = vb.reshape(tiles, 8, 32, stages, 2, 2, 16).transpose(0, 3, 1, 4, 5, 2, 6)
     # metadata blocks in 16-byte lane chunks: row r = 128 wm + 32 i + rl, block
     # byte j = ((hq * kpc + hs) * 2 + q) * iw + e (k-step h = hq * kpc + hs,
     # lane half q, index-word byte e); order [tile][block][hq][wm][q][rl][hs][i][e]
     iw = 4 if es == 1 else 2
     kpc = 4 // iw
     pm = mb.reshape(tiles, 2, 4, 32, mblocks, 4, kpc, 2, iw).transpose(0, 4, 5, 1, 7, 3, 6, 2, 8)
-    return pv.reshape(-1), np.ascontiguousarray(pm).reshape(-1)
+    return np.ascontiguousarray(pv).reshape(-1), np.ascontiguousarray(pm).reshape(-1)
 
 
 def shapes_for(dt):

@@ -1,6 +1,7 @@
-"""The measurement probes through the C ABI: the streaming read and the
-matrix-instruction issue-rate probe launch, finish and leave their sinks
-alone (a sink word is written only when a fold hits one fixed value)."""
+"""The measurement probes through the C ABI: the streaming read, the
+matrix-instruction issue-rate probe and the LDS read probe launch, finish
+and leave their sinks alone (a sink word is written only when a fold hits
+one fixed value)."""
 import pytest
 import torch
 
@@ -35,3 +36,22 @@ def test_mfma_probe_runs_every_form(form):
     ssg.ssg_mfma_probe(form, 3, 1, sink)                    # fewer workgroups than CUs
     torch.cuda.synchronize()
     assert int(sink.abs().sum()) == 0
+
+
+def test_lds_read_probe_runs_and_sees_bank_conflicts():
+    import bench
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    sink = torch.zeros(cus, dtype=torch.int32, device="cuda")
+    pats = dict(bench.lds_patterns())
+    for offs in pats.values():
+        ssg.ssg_lds_read_probe(offs, 3, 2, sink)
+    torch.cuda.synchronize()
+    assert int(sink.ne(0).sum()) == 0 or int(sink.ne(0).sum()) == int(sink.eq(-1640531527).sum())
+    # sixteen lanes on one bank take many times longer than a contiguous read
+    stream = torch.cuda.current_stream()
+    t = {}
+    for name in ("contiguous (lane l at 16 l)", "the 16 lanes of each group on one bank, 256 B apart"):
+        ssg.ssg_lds_read_probe(pats[name], cus, 10, sink)
+        t[name] = min(bench.time_kernel(lambda i: ssg.ssg_lds_read_probe(pats[name], cus, 500, sink), 1, stream)
+                      for _ in range(3))
+    assert t["the 16 lanes of each group on one bank, 256 B apart"] > 3 * t["contiguous (lane l at 16 l)"]
