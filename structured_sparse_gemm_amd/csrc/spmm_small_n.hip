@@ -1090,7 +1090,10 @@ template <int DT> struct Cbm {
     static constexpr int LX = 4;                           // k-steps of fragments, masks, offsets and B in flight
     static constexpr int LY = 2;                           // k-steps of residual value windows in flight
     static constexpr int YWIN = 2048;                      // a block's values: at most 1 KiB plus alignment
-    template <int TM> static constexpr int wave_lds() { return LX * BSTEP + LY * TM * YWIN + 16; }
+    // LDS per wave: B slots (row-major B only), value windows, 16 zero bytes
+    template <int TM, bool BT> static constexpr int wave_lds() {
+        return (BT ? 0 : LX * BSTEP) + LY * TM * YWIN + 16;
+    }
 };
 
 // Residual operand of a lane from its block's value window in LDS: slot s
@@ -1164,7 +1167,7 @@ __global__ void __launch_bounds__(W * 64) k_spmm_packed_cbm(SpmmArgs a, const ui
     // load makes a wait stricter (loads complete in issue order), never
     // looser.
     constexpr int GY = TM;
-    constexpr int WL = C::template wave_lds<TM>();
+    constexpr int WL = C::template wave_lds<TM, BT>();
     static_assert(LX % LY == 0 && GX + GY < 64, "ring");
     static_assert(W * WL <= 160 * 1024 && W * kTMax * 1024 <= W * WL, "LDS");
     extern __shared__ __attribute__((aligned(1024))) uint8_t lds[];
@@ -1176,7 +1179,7 @@ __global__ void __launch_bounds__(W * 64) k_spmm_packed_cbm(SpmmArgs a, const ui
     const int nt = (int)min<int64_t>(TM, tiles - t0);
     const int64_t ksteps = a.K / T::KS;
     const uint32_t wbase = (uint32_t)(wave * WL);                 // this wave's LDS region
-    const uint32_t ybase = wbase + LX * C::BSTEP;                 // its value windows
+    const uint32_t ybase = wbase + (BT ? 0 : LX * C::BSTEP);     // its value windows
     const uint32_t zpad = ybase + LY * TM * C::YWIN;              // 16 zero bytes
     if (lane == 0) *reinterpret_cast<uint4*>(lds + zpad) = make_uint4(0, 0, 0, 0);
 
@@ -1354,7 +1357,7 @@ template <int DT, int TM, int W, bool BT>
 void launch_packed_cbm_w(const SpmmArgs& a, const uint8_t* pv, const uint8_t* pm, const uint8_t* rmask,
                          const int32_t* roff, const uint8_t* cvals, int64_t nvals, int64_t tiles, hipStream_t s) {
     hipLaunchKernelGGL((k_spmm_packed_cbm<DT, TM, W, BT>), dim3((unsigned)((tiles + TM - 1) / TM)), dim3(64 * W),
-                       W * Cbm<DT>::template wave_lds<TM>(), s, a, pv, pm, rmask, roff, cvals, nvals, tiles);
+                       (W * Cbm<DT>::template wave_lds<TM, BT>()), s, a, pv, pm, rmask, roff, cvals, nvals, tiles);
 }
 
 template <int DT, bool BT = false>
