@@ -239,8 +239,8 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const uint8_t* base, int6
 // s_nop is the wait state GFX9 needs between an SALU write of M0 and an
 // LDS-DMA load that reads it.
 template <int BYTES>
-__device__ __forceinline__ void dma(__amdgpu_buffer_rsrc_t r, const uint8_t* lds_dst, uint32_t voff) {
-    const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(const lds_void*)lds_dst);
+__device__ __forceinline__ void dma(__amdgpu_buffer_rsrc_t r, uint32_t lds_dst, uint32_t voff) {
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_dst);
     if constexpr (BYTES == 16)
         asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(m0), "v"(voff), "s"(r)
                      : "memory", "m0");
@@ -286,7 +286,7 @@ __device__ __forceinline__ void interleave() {
 
 // Issue the direct-to-LDS loads of stage `it` into `st` (this wave's share).
 template <int DT, int BN>
-__device__ __forceinline__ void issue(const Ctx& x, uint8_t* st, int64_t it, int wave) {
+__device__ __forceinline__ void issue(const Ctx& x, uint32_t st, int64_t it, int wave) {
     using L = Lay<DT, BN>;
     using T = PT<DT>;
     const __amdgpu_buffer_rsrc_t rb = rsrc(x.bbase + it * x.bstage, x.bbytes - it * x.bstage);
@@ -300,7 +300,7 @@ __device__ __forceinline__ void issue(const Ctx& x, uint8_t* st, int64_t it, int
 // Issue the direct-to-LDS loads of metadata block `g` (the 32 bytes of each
 // of the tile's rows that cover stages [g * MB, (g + 1) * MB)) into `mt`.
 template <int DT, int BN>
-__device__ __forceinline__ void issue_meta(const Ctx& x, uint8_t* mt, int64_t g, int wave) {
+__device__ __forceinline__ void issue_meta(const Ctx& x, uint32_t mt, int64_t g, int wave) {
     using L = Lay<DT, BN>;
     const __amdgpu_buffer_rsrc_t rm = rsrc(x.mbase + g * x.mstep, x.mbytes - g * x.mstep);
 #pragma unroll
@@ -317,6 +317,10 @@ __device__ __forceinline__ void spmm_tile(const SpmmArgs& a, int tm, int tn, uin
     using S = typename std::conditional<DT == DT_I8, int32_t, float>::type;
     constexpr int NJ = L::NJ;
     uint8_t* const mlds = lds + kStages * L::STAGE;   // two metadata blocks
+    // LDS byte addresses of the same, for the loads' M0 (32-bit arithmetic,
+    // so no generic-pointer conversion per load)
+    const uint32_t lds32 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(const lds_void*)lds);
+    const uint32_t mlds32 = lds32 + kStages * L::STAGE;
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -462,13 +466,13 @@ __device__ __forceinline__ void spmm_tile(const SpmmArgs& a, int tm, int tn, uin
     // after every wave's last read of block g - 2, whose buffer it takes) and
     // is first read MB - 1 iterations later.  The wait of an iteration that
     // follows such an issue leaves the block's loads outstanding too.
-    issue_meta<DT, BN>(x, mlds, 0, wave);
-    issue<DT, BN>(x, lds, 0, wave);
-    issue<DT, BN>(x, lds + L::STAGE, 1, wave);
+    issue_meta<DT, BN>(x, mlds32, 0, wave);
+    issue<DT, BN>(x, lds32, 0, wave);
+    issue<DT, BN>(x, lds32 + L::STAGE, 1, wave);
     wait_vm<L::VM_PER_STAGE>();
     barrier();
-    issue<DT, BN>(x, lds + 2 * L::STAGE, 2, wave);
-    issue_meta<DT, BN>(x, mlds + L::MBLK, 1, wave);
+    issue<DT, BN>(x, lds32 + 2 * L::STAGE, 2, wave);
+    issue_meta<DT, BN>(x, mlds32 + L::MBLK, 1, wave);
 
     // Index words: packed 16-bit -- one chunk per stage (dn: both k-steps'
     // words, two per register); packed 8-bit -- one chunk per k-step;
@@ -511,10 +515,10 @@ __device__ __forceinline__ void spmm_tile(const SpmmArgs& a, int tm, int tn, uin
         else wait_vm<L::VM_PER_STAGE>();
         __builtin_amdgcn_s_waitcnt(0xC07F);
         barrier();
-        uint8_t* const dst = lds + slot * L::STAGE;
+        const uint32_t dst = lds32 + slot * L::STAGE;
         if constexpr (!PK) issue<DT, BN>(x, dst, it + 3, wave);
         if ((it + 1) % T::MB == 0)
-            issue_meta<DT, BN>(x, mlds + (((it + 1) / T::MB + 1) & 1) * L::MBLK, (it + 1) / T::MB + 1, wave);
+            issue_meta<DT, BN>(x, mlds32 + (((it + 1) / T::MB + 1) & 1) * L::MBLK, (it + 1) / T::MB + 1, wave);
         slot = slot == kStages - 1 ? 0 : slot + 1;
         const uint8_t* nx = lds + slot * L::STAGE;
         if constexpr (PK) {
