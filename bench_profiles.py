@@ -55,7 +55,7 @@ COMMANDS = {
     "lds": "mkdir -p $R/gpurun_out && timeout -k 10 120 python3 $R/bench.py --lds-patterns > $R/gpurun_out/lds_patterns.json",
 }
 
-HEADLINE = "k_spmm_pipe<1, true, true>"     # the headline step's product
+HEADLINE = "k_spmm_pipe<1, true, true, 8>"     # the headline step's product
 TIMED = 20                                   # launches bench.py times back to back (--steps 20)
 
 # Kernels the counter passes attribute to a workload line of bench.py:
@@ -63,17 +63,17 @@ TIMED = 20                                   # launches bench.py times back to b
 # The workload line names the bench entry whose algorithmic bytes apply; the
 # family names the sources whose hash marks the counters stale.
 PROFILED = [
-    ("k_spmm_pipe<1, true, true>", "c4", "spmm_large_n",
+    ("k_spmm_pipe<1, true, true, 8>", "c4", "spmm_large_n",
      "bf16 28672x8192x2048 SpMM, packed prefill layout, B activation-major (the headline step's product)"),
     ("k_compress_prefill<1>", "c4", "compress",
      "bf16 28672x8192x2048 prune + compress into the packed prefill layout (the headline step's compress)"),
-    ("k_spmm_pipe<1, true, false>", "c4_bkn", "spmm_large_n",
+    ("k_spmm_pipe<1, true, false, 4>", "c4_bkn", "spmm_large_n",
      "bf16 28672x8192x2048 SpMM, packed prefill layout, B [K, N] row-major"),
-    ("k_spmm_pipe<1, false, false>", "c4_rowmajor", "spmm_large_n", "bf16 28672x8192x2048 SpMM, row-major operand"),
-    ("k_spmm_pipe<2, true, true>", "c2_prefill_bt", "spmm_large_n",
+    ("k_spmm_pipe<1, false, false, 4>", "c4_rowmajor", "spmm_large_n", "bf16 28672x8192x2048 SpMM, row-major operand"),
+    ("k_spmm_pipe<2, true, true, 8>", "c2_prefill_bt", "spmm_large_n",
      "int8 4096^3 SpMM, packed prefill layout, B activation-major"),
-    ("k_spmm_pipe<2, true, false>", "c2_prefill", "spmm_large_n", "int8 4096^3 SpMM, packed prefill layout"),
-    ("k_spmm_pipe<2, false, false>", "c2", "spmm_large_n", "int8 4096^3 SpMM, row-major operand"),
+    ("k_spmm_pipe<2, true, false, 4>", "c2_prefill", "spmm_large_n", "int8 4096^3 SpMM, packed prefill layout"),
+    ("k_spmm_pipe<2, false, false, 4>", "c2", "spmm_large_n", "int8 4096^3 SpMM, row-major operand"),
     (re.compile(r"k_spmm_small_n_ring<0, \d+, \d+, false, false>"), "c3", "spmm_small_n",
      "fp16 11008x4096x16 SpMM, row-major operand"),
     (re.compile(r"k_spmm_packed<0, \d+, \d+, false, false, false>"), "c3_packed", "spmm_small_n",

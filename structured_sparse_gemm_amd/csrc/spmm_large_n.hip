@@ -12,7 +12,10 @@
 // * Workgroup tile 256 x 256, 4 waves (one per SIMD) in 2 x 2, each wave a
 //   4 x 4 grid of 32 x 32 sparse MFMA tiles: v_smfmac_f32_32x32x32_{f16,bf16}
 //   (32 dense k) or v_smfmac_i32_32x32x64_i8 (64 dense k); two of them per
-//   k-block (BK = 64 dense k for 16-bit, 128 for int8).
+//   k-block (BK = 64 dense k for 16-bit, 128 for int8).  The packed operand
+//   with activation-major B runs 8 waves (two per SIMD) in 2 x 4, each a
+//   4 x 2 grid: with one wave per SIMD every non-MFMA instruction of the
+//   wave delays its next MFMA, and a second wave fills those gaps.
 // * Every operand reaches LDS through direct-to-LDS buffer loads
 //   (buffer_load ... lds): no register staging, and a row or column beyond
 //   the matrix is an out-of-range buffer offset that reads as zero, so edge
@@ -57,7 +60,7 @@ namespace ssg {
 
 namespace {
 
-constexpr int kBM = 256, kBN = 256, kStages = 3, kThreads = 256;
+constexpr int kBM = 256, kBN = 256, kStages = 3;
 constexpr int kGroupM = 8;             // row tiles walked together per XCD
 constexpr uint32_t kOob = 0x80000000u; // buffer offset that reads as zero
 
@@ -84,10 +87,12 @@ template <> struct PT<DT_I8> {
 template <> struct PT<DT_E4M3> : PT<DT_I8> {};   // 8-bit floats: the int8 shapes
 template <> struct PT<DT_E5M2> : PT<DT_I8> {};
 
-template <int DT, int BN = kBN>
+// NW waves per workgroup: two along M (128 rows each), NW / 2 along N
+template <int DT, int BN = kBN, int NW = 4>
 struct Lay {
     using T = PT<DT>;
-    static constexpr int NJ = BN / 64;                     // 32-column MFMA tiles per wave
+    static constexpr int WN = NW / 2;                      // waves along N
+    static constexpr int NJ = BN / (32 * WN);              // 32-column MFMA tiles per wave
     static constexpr int ROWB = BN * T::ES;                // B tile row bytes
     static constexpr int CPR = ROWB / 16;                  // 16-byte chunks per row
     static constexpr int B_BYTES = T::BK * ROWB;           // 32 KiB
@@ -97,13 +102,15 @@ struct Lay {
     static constexpr int MBLK_ROWB = T::MB * T::MSTAGE;    // metadata bytes per row per block (32)
     static constexpr int MBLK = kBM * MBLK_ROWB;           // 8 KiB, two blocks resident
     static constexpr int LDS = kStages * STAGE + 2 * MBLK;
-    static constexpr int B_LOADS = B_BYTES / 1024 / 4;     // per wave per stage (1 KiB each)
-    static constexpr int A_LOADS = A_BYTES / 1024 / 4;
-    static constexpr int M_LOADS = MBLK / 256 / 4;         // per wave per block (256 B each)
+    static constexpr int B_LOADS = B_BYTES / 1024 / NW;    // per wave per stage (1 KiB each)
+    static constexpr int A_LOADS = A_BYTES / 1024 / NW;
+    static constexpr int M_LOADS = MBLK / 256 / NW;        // per wave per block (256 B each)
     static constexpr int VM_PER_STAGE = B_LOADS + A_LOADS;
     static_assert(A_ROWB == 64 && MBLK_ROWB == 32, "layout");
     static_assert(LDS <= 160 * 1024, "LDS");
-    static_assert(B_LOADS % NJ == 0 && B_LOADS >= 1, "B loads per wave per stage");
+    static_assert((NW == 4 || NW == 8) && NJ >= 1, "waves");
+    static_assert(B_LOADS % NJ == 0 && B_LOADS >= 1 && A_LOADS >= 1 && A_LOADS <= 4 && M_LOADS >= 1,
+                  "loads per wave per stage");
 };
 
 // Row-major operand: 16-byte chunk c of row r of the sparse-value tile sits
@@ -285,9 +292,9 @@ __device__ __forceinline__ void interleave() {
 // reads of B and 4 index words
 
 // Issue the direct-to-LDS loads of stage `it` into `st` (this wave's share).
-template <int DT, int BN>
+template <int DT, int BN, int NW>
 __device__ __forceinline__ void issue(const Ctx& x, uint32_t st, int64_t it, int wave) {
-    using L = Lay<DT, BN>;
+    using L = Lay<DT, BN, NW>;
     using T = PT<DT>;
     const __amdgpu_buffer_rsrc_t rb = rsrc(x.bbase + it * x.bstage, x.bbytes - it * x.bstage);
     const __amdgpu_buffer_rsrc_t ra = rsrc(x.vbase + it * x.vstage, x.vbytes - it * x.vstage);
@@ -299,9 +306,9 @@ __device__ __forceinline__ void issue(const Ctx& x, uint32_t st, int64_t it, int
 
 // Issue the direct-to-LDS loads of metadata block `g` (the 32 bytes of each
 // of the tile's rows that cover stages [g * MB, (g + 1) * MB)) into `mt`.
-template <int DT, int BN>
+template <int DT, int BN, int NW>
 __device__ __forceinline__ void issue_meta(const Ctx& x, uint32_t mt, int64_t g, int wave) {
-    using L = Lay<DT, BN>;
+    using L = Lay<DT, BN, NW>;
     const __amdgpu_buffer_rsrc_t rm = rsrc(x.mbase + g * x.mstep, x.mbytes - g * x.mstep);
 #pragma unroll
     for (int j = 0; j < L::M_LOADS; ++j) dma<4>(rm, mt + (wave * L::M_LOADS + j) * 256, x.moff[j]);
@@ -309,10 +316,10 @@ __device__ __forceinline__ void issue_meta(const Ctx& x, uint32_t mt, int64_t g,
 
 // Tile (tm, tn) of width BN (256, or 128 for the half-width tiles that fill
 // the last wave of a launch): rows [256 tm, +256), columns [BN tn, +BN).
-template <int DT, bool PK, int BN, bool BT>
+template <int DT, bool PK, int BN, bool BT, int NW>
 __device__ __forceinline__ void spmm_tile(const SpmmArgs& a, int tm, int tn, uint8_t* lds) {
     using T = PT<DT>;
-    using L = Lay<DT, BN>;
+    using L = Lay<DT, BN, NW>;
     using Acc = Acc16<DT>;
     using S = typename std::conditional<DT == DT_I8, int32_t, float>::type;
     constexpr int NJ = L::NJ;
@@ -324,7 +331,8 @@ __device__ __forceinline__ void spmm_tile(const SpmmArgs& a, int tm, int tn, uin
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave / L::WN, wn = wave % L::WN;     // rows [128 wm, +128), columns [32 NJ wn, +32 NJ)
+    constexpr int WCOLS = 32 * NJ;
     const int64_t m0 = (int64_t)tm * kBM, n0 = (int64_t)tn * BN;
 
     // per-lane load offsets (constant across stages)
@@ -416,8 +424,8 @@ __device__ __forceinline__ void spmm_tile(const SpmmArgs& a, int tm, int tn, uin
         }
 #pragma unroll
         for (int j = 0; j < NJ; ++j) {
-            if constexpr (BT) b_frag_bt<DT>(st, s, wn * (BN / 2) + 32 * j, lane, o.b[j]);
-            else b_frag<DT, BN>(st, s, wn * (BN / 2) + 32 * j, lane, o.b[j]);
+            if constexpr (BT) b_frag_bt<DT>(st, s, wn * WCOLS + 32 * j, lane, o.b[j]);
+            else b_frag<DT, BN>(st, s, wn * WCOLS + 32 * j, lane, o.b[j]);
         }
     };
     // Index words of sub-step s of stage t for this lane, read so that no
@@ -466,13 +474,13 @@ __device__ __forceinline__ void spmm_tile(const SpmmArgs& a, int tm, int tn, uin
     // after every wave's last read of block g - 2, whose buffer it takes) and
     // is first read MB - 1 iterations later.  The wait of an iteration that
     // follows such an issue leaves the block's loads outstanding too.
-    issue_meta<DT, BN>(x, mlds32, 0, wave);
-    issue<DT, BN>(x, lds32, 0, wave);
-    issue<DT, BN>(x, lds32 + L::STAGE, 1, wave);
+    issue_meta<DT, BN, NW>(x, mlds32, 0, wave);
+    issue<DT, BN, NW>(x, lds32, 0, wave);
+    issue<DT, BN, NW>(x, lds32 + L::STAGE, 1, wave);
     wait_vm<L::VM_PER_STAGE>();
     barrier();
-    issue<DT, BN>(x, lds32 + 2 * L::STAGE, 2, wave);
-    issue_meta<DT, BN>(x, mlds32 + L::MBLK, 1, wave);
+    issue<DT, BN, NW>(x, lds32 + 2 * L::STAGE, 2, wave);
+    issue_meta<DT, BN, NW>(x, mlds32 + L::MBLK, 1, wave);
 
     // Index words: packed 16-bit -- one chunk per stage (dn: both k-steps'
     // words, two per register); packed 8-bit -- one chunk per k-step;
@@ -516,9 +524,9 @@ __device__ __forceinline__ void spmm_tile(const SpmmArgs& a, int tm, int tn, uin
         __builtin_amdgcn_s_waitcnt(0xC07F);
         barrier();
         const uint32_t dst = lds32 + slot * L::STAGE;
-        if constexpr (!PK) issue<DT, BN>(x, dst, it + 3, wave);
+        if constexpr (!PK) issue<DT, BN, NW>(x, dst, it + 3, wave);
         if ((it + 1) % T::MB == 0)
-            issue_meta<DT, BN>(x, mlds32 + (((it + 1) / T::MB + 1) & 1) * L::MBLK, (it + 1) / T::MB + 1, wave);
+            issue_meta<DT, BN, NW>(x, mlds32 + (((it + 1) / T::MB + 1) & 1) * L::MBLK, (it + 1) / T::MB + 1, wave);
         slot = slot == kStages - 1 ? 0 : slot + 1;
         const uint8_t* nx = lds + slot * L::STAGE;
         if constexpr (PK) {
@@ -526,17 +534,17 @@ __device__ __forceinline__ void spmm_tile(const SpmmArgs& a, int tm, int tn, uin
             // of the next k-step so they leave the wave between its MFMAs
             const __amdgpu_buffer_rsrc_t rb = rsrc(x.bbase + (it + 3) * x.bstage, x.bbytes - (it + 3) * x.bstage);
             const __amdgpu_buffer_rsrc_t ra = rsrc(x.vbase + (it + 3) * x.vstage, x.vbytes - (it + 3) * x.vstage);
-            static_assert(L::A_LOADS == 4, "spread issue assumes 4 loads of values per stage");
+            // the A_LOADS (at most 4) loads of values follow the first reads
             constexpr int BPJ = L::B_LOADS / NJ;        // B loads placed after each column tile's reads
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 o0.av[i] = *reinterpret_cast<const uint4*>(nx + L::B_BYTES + ((wm * 4 + i) << 11) + lane * 16);
-                dma<16>(ra, dst + L::B_BYTES + (wave * L::A_LOADS + i) * 1024, x.aoff[i]);
+                if (i < L::A_LOADS) dma<16>(ra, dst + L::B_BYTES + (wave * L::A_LOADS + i) * 1024, x.aoff[i]);
             }
 #pragma unroll
             for (int j = 0; j < NJ; ++j) {
-                if constexpr (BT) b_frag_bt<DT>(nx, 0, wn * (BN / 2) + 32 * j, lane, o0.b[j]);
-                else b_frag<DT, BN>(nx, 0, wn * (BN / 2) + 32 * j, lane, o0.b[j]);
+                if constexpr (BT) b_frag_bt<DT>(nx, 0, wn * WCOLS + 32 * j, lane, o0.b[j]);
+                else b_frag<DT, BN>(nx, 0, wn * WCOLS + 32 * j, lane, o0.b[j]);
 #pragma unroll
                 for (int u = 0; u < BPJ; ++u)
                     dma<16>(rb, dst + (wave * L::B_LOADS + BPJ * j + u) * 1024, x.boff[BPJ * j + u]);
@@ -559,7 +567,7 @@ __device__ __forceinline__ void spmm_tile(const SpmmArgs& a, int tm, int tn, uin
     for (int i = 0; i < 4; ++i) {
 #pragma unroll
         for (int j = 0; j < NJ; ++j) {
-            const int64_t col = n0 + wn * (BN / 2) + 32 * j + rl;
+            const int64_t col = n0 + wn * WCOLS + 32 * j + rl;
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
                 const int64_t row = m0 + wm * 128 + 32 * i + 8 * (e >> 2) + 4 * q + (e & 3);
@@ -592,17 +600,17 @@ __device__ __forceinline__ void xcd_order(int bid, int tiles_m, int tiles_n, int
     *tn = in_group / gm;
 }
 
-template <int DT, bool PK, bool BT = false>
-__global__ void __launch_bounds__(kThreads) k_spmm_pipe(SpmmArgs a, int tiles_m, int tiles_n, int full_rows) {
+template <int DT, bool PK, bool BT = false, int NW = 4>
+__global__ void __launch_bounds__(NW * 64) k_spmm_pipe(SpmmArgs a, int tiles_m, int tiles_n, int full_rows) {
     __shared__ __attribute__((aligned(1024))) uint8_t lds[Lay<DT>::LDS];
     const int nfull = full_rows * tiles_n;
     int tm, tn;
     if ((int)blockIdx.x < nfull) {
         xcd_order(blockIdx.x, full_rows, tiles_n, &tm, &tn);
-        spmm_tile<DT, PK, kBN, BT>(a, tm, tn, lds);
+        spmm_tile<DT, PK, kBN, BT, NW>(a, tm, tn, lds);
     } else {
         xcd_order(blockIdx.x - nfull, tiles_m - full_rows, 2 * tiles_n, &tm, &tn);
-        spmm_tile<DT, PK, kBN / 2, BT>(a, full_rows + tm, tn, lds);
+        spmm_tile<DT, PK, kBN / 2, BT, NW>(a, full_rows + tm, tn, lds);
     }
 }
 
@@ -633,12 +641,12 @@ int full_row_tiles(int tiles_m, int tiles_n) {
     return conv <= kCUs - rem ? tiles_m - half_rows : tiles_m;
 }
 
-template <int DT, bool PK = false, bool BT = false>
+template <int DT, bool PK = false, bool BT = false, int NW = 4>
 hipError_t pipe_launch(const SpmmArgs& a, hipStream_t s) {
     const int tm = (int)((a.M + kBM - 1) / kBM), tn = (int)((a.N + kBN - 1) / kBN);
     const int full = full_row_tiles(tm, tn);
     const unsigned grid = (unsigned)(full * tn + 2 * (tm - full) * tn);
-    hipLaunchKernelGGL((k_spmm_pipe<DT, PK, BT>), dim3(grid), dim3(kThreads), 0, s, a, tm, tn, full);
+    hipLaunchKernelGGL((k_spmm_pipe<DT, PK, BT, NW>), dim3(grid), dim3(NW * 64), 0, s, a, tm, tn, full);
     return hipGetLastError();
 }
 
@@ -746,11 +754,11 @@ bool supported_prefill_packed_bt(const SpmmArgs& a) {
 
 hipError_t launch_spmm_prefill_packed_bt(const SpmmArgs& a, hipStream_t s) {
     switch (a.dt) {
-        case DT_F16: return pipe_launch<DT_F16, true, true>(a, s);
-        case DT_BF16: return pipe_launch<DT_BF16, true, true>(a, s);
-        case DT_I8: return pipe_launch<DT_I8, true, true>(a, s);
-        case DT_E4M3: return pipe_launch<DT_E4M3, true, true>(a, s);
-        case DT_E5M2: return pipe_launch<DT_E5M2, true, true>(a, s);
+        case DT_F16: return pipe_launch<DT_F16, true, true, 8>(a, s);
+        case DT_BF16: return pipe_launch<DT_BF16, true, true, 8>(a, s);
+        case DT_I8: return pipe_launch<DT_I8, true, true, 8>(a, s);
+        case DT_E4M3: return pipe_launch<DT_E4M3, true, true, 8>(a, s);
+        case DT_E5M2: return pipe_launch<DT_E5M2, true, true, 8>(a, s);
         default: return hipErrorInvalidValue;
     }
 }
