@@ -407,7 +407,7 @@ __device__ __forceinline__ void spmm_tile(const SpmmArgs& a, int tm, int tn, uin
     const int q = lane >> 5, rl = lane & 31;
 
     // Operands of one MFMA k-step (sub-step) from an LDS stage: 4 sparse
-    // fragments of this wave's row tiles and 4 B fragments of its columns.
+    // fragments of this wave's row tiles and NJ B fragments of its columns.
     struct Ops {
         uint4 av[4];
         uint4 b[NJ][2];
