@@ -114,11 +114,13 @@ struct Lay {
 };
 
 // Row-major operand: 16-byte chunk c of row r of the sparse-value tile sits
-// at chunk c ^ swz_a(r) of the row's 64 bytes, so the 16 consecutive rows
-// that a ds_read_b128 serves together fall on distinct 16-byte bank
-// windows.  (The packed prefill operand instead arrives in the lane order
-// of the reads, prefill_vals_unit, and each read is lane-contiguous.)
-__device__ __forceinline__ int swz_a(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
+// at chunk c ^ swz_a(r) of the row's 64 bytes.  The permutation was chosen
+// by measurement (the LDS read probe over every pair of row-bit parities):
+// with it a sparse-operand read (32 rows, two chunks each) runs at the rate
+// of a lane-contiguous read, where the XOR of row bits 1 and 3 ran at 0.6
+// of it.  (The packed prefill operand instead arrives in the lane order of
+// the reads, prefill_vals_unit, and each read is lane-contiguous.)
+__device__ __forceinline__ int swz_a(int r) { return ((r >> 2) & 1) | (((r ^ (r >> 4)) & 1) << 1); }
 
 template <int DT, int BN = kBN> __device__ __forceinline__ int swz(int r) {
     // a permutation of the row's 16-byte chunks (8-bit rows of 128 columns
