@@ -256,6 +256,9 @@ def lds_patterns() -> list:
     pats.append(("the same, lanes 0-15 only (the rest contiguous, 8 KiB on)",
                  [(l & 31) * 64 + (((l >> 5) ^ swz_rows(l & 31)) << 4) if l < 16 else 8192 + 16 * l
                   for l in range(64)]))
+    pats.append(("sparse values, rows of 64 B, chunks swizzled by (r/4)%2 + 2((r^r/16)%2) (row-major operand)",
+                 [(l & 31) * 64 + (((l >> 5) ^ (((l & 31) >> 2) & 1) ^ ((((l & 31) ^ ((l & 31) >> 4)) & 1) << 1)) << 4)
+                  for l in range(64)]))
     pats.append(("sparse values, rows of 64 B, unswizzled", [(l & 31) * 64 + ((l >> 5) << 4) for l in range(64)]))
     pats.append(("sparse values, packed prefill layout (lane order)", [16 * l for l in range(64)]))
     pats.append(("activation-major B, rows of 128 B, chunks swizzled by (n/2)%8",
